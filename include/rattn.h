@@ -1,0 +1,136 @@
+/*
+ * rattn.h -- relative-bias grouped-query attention for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (vLLM recipes page "thinkingmachines/Inkling", Overview > Architectural
+ * highlights > Attention): grouped-query attention with head size 128 in which RoPE is
+ * replaced by a learned relative-position term added to the logits before the softmax.
+ * The term is a per-query-head table r indexed by the clamped distance, so for a query at
+ * absolute position i and a key at position j:
+ *
+ *     logit[i, j] = (q_i . k_j) / sqrt(128) + r[h, min(i - j, R - 1)]
+ *     out_i       = sum_j softmax_j(logit[i, :]) v_j,   lse_i = log sum_j exp(logit[i, j])
+ *
+ * over the visible keys: 0 <= i - j (causal) and, for a sliding-window layer with window
+ * W > 0, i - j <= W - 1 (W keys including the query itself).  The page names both full and
+ * sliding-window layers, multi-token (MTP) verification of up to 9 tokens per step
+ * (Overview > MTP), and a paged KV cache with 128-token blocks (Client Usage,
+ * "--block-size 128").
+ *
+ * Conventions shared by every entry point
+ *   - All tensors are dense, row-major, innermost dimension last; the head dimension is 128.
+ *   - Query head h reads KV head h / (Hq / Hkv) (contiguous groups); Hq % Hkv == 0.
+ *   - bf16 data is IEEE bfloat16 bit patterns.  Accumulation is fp32.  bf16 outputs are
+ *     rounded to nearest even from fp32.
+ *   - lse is fp32, natural logarithm.
+ *   - Device pointers must be valid on the current HIP device; `stream` is a hipStream_t
+ *     passed as void* (NULL = the null stream).  Calls only enqueue work: they neither
+ *     allocate nor synchronise, and the caller owns every buffer.
+ *   - Status: RATTN_OK or an error code; on error rattn_last_error() returns a
+ *     thread-local message.  Argument errors are detected on the host before any HIP call,
+ *     so nothing is enqueued and no output is written.
+ *   - Results are deterministic: fixed arguments give bitwise-identical outputs.
+ */
+#ifndef RATTN_H
+#define RATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RATTN_ABI_VERSION 1
+
+enum rattn_status {
+  RATTN_OK = 0,
+  RATTN_ERR_INVALID_ARG = 1, /* null pointer, inconsistent sizes */
+  RATTN_ERR_UNSUPPORTED = 2, /* head_dim != 128, block_size != 128, dtype not handled */
+  RATTN_ERR_WORKSPACE = 3,   /* decode workspace missing or too small */
+  RATTN_ERR_HIP = 4          /* a HIP launch failed; message holds hipGetErrorString */
+};
+
+enum rattn_dtype { RATTN_BF16 = 0, RATTN_FP32 = 1 };
+
+/*
+ * Prefill / chunked prefill over contiguous K/V.
+ *
+ *   q    [B, Lq, Hq, 128]   dtype    device, read
+ *   k    [B, Lk, Hkv, 128]  dtype    device, read
+ *   v    [B, Lk, Hkv, 128]  dtype    device, read
+ *   bias [Hq, R]            fp32     device, read   (r above; R >= 1)
+ *   out  [B, Lq, Hq, 128]   dtype    device, written
+ *   lse  [B, Lq, Hq]        fp32     device, written; may be NULL
+ *
+ * Query t of every sequence sits at absolute position Lk - Lq + t (bottom-right alignment:
+ * a chunk of Lq new tokens whose own keys are the last Lq of the Lk keys), so Lq <= Lk.
+ * window <= 0 selects full causal attention; window > 0 a sliding window of that many keys.
+ * dtype RATTN_BF16: bf16 in/out.  RATTN_FP32: fp32 in/out; q.k is formed without rounding
+ * the inputs to bf16 (three-term bf16 split), likewise p.v.
+ * B == 0 or Lq == 0 is a no-op returning RATTN_OK (pointers may then be NULL).
+ * Status: INVALID_ARG for a null required pointer, negative sizes, Hq % Hkv != 0, Lq > Lk,
+ * R < 1; UNSUPPORTED for head_dim != 128 or an unknown dtype; HIP if the launch fails.
+ */
+int rattn_prefill(const void* q, const void* k, const void* v, const float* bias, void* out,
+                  float* lse, int B, int Lq, int Lk, int Hq, int Hkv, int head_dim, int R,
+                  int window, int dtype, void* stream);
+
+/*
+ * Number of KV splits per (sequence, KV head) that rattn_decode_paged will use for these
+ * arguments.  num_splits > 0 requests at most that many splits; 0 lets the library choose
+ * from the sizes alone (no device query).  Returns 0 for invalid sizes.
+ */
+int rattn_decode_num_splits(int B, int n_q, int Hq, int Hkv, int max_ctx_len, int num_splits);
+
+/*
+ * Device workspace, in bytes, that rattn_decode_paged needs for these arguments (partial
+ * outputs and log-sum-exps of every split).  Returns 0 for invalid sizes.
+ */
+size_t rattn_decode_workspace_bytes(int B, int n_q, int Hq, int Hkv, int max_ctx_len,
+                                    int num_splits);
+
+/*
+ * Paged decode with multi-query (MTP) verification: n_q query tokens per sequence attend
+ * to the sequence's paged KV cache, split over the context and merged by log-sum-exp.
+ *
+ *   q           [B, n_q, Hq, 128]                 bf16   device, read
+ *   k_cache     [num_blocks, 128, Hkv, 128]       bf16   device, read
+ *   v_cache     [num_blocks, 128, Hkv, 128]       bf16   device, read
+ *   block_table [B, max_blocks_per_seq]           int32  device, read (physical block ids)
+ *   ctx_lens    [B]                               int32  device, read; keys in the cache
+ *               for the sequence INCLUDING its n_q query tokens; 1 <= n_q <= ctx_lens[b]
+ *               <= min(max_ctx_len, 128 * max_blocks_per_seq) is the caller's guarantee
+ *   windows     [B]                               int32  device, read; <= 0 full causal,
+ *               > 0 sliding window; NULL means every sequence is full causal
+ *   bias        [Hq, R]                           fp32   device, read
+ *   out         [B, n_q, Hq, 128]                 bf16   device, written
+ *   lse         [B, n_q, Hq]                      fp32   device, written; may be NULL
+ *   workspace   device scratch of at least rattn_decode_workspace_bytes(...) bytes
+ *
+ * Query t of sequence b sits at position ctx_lens[b] - n_q + t and sees keys per the
+ * causal / window rule above (the n_q queries are causal among themselves).
+ * Only blocks holding a key visible to some query of the sequence are read; other
+ * block-table entries are never dereferenced and may hold anything.  Cache slots outside
+ * [max(0, ctx - n_q - W + 1), ctx) (W the window, 0 if full) may hold anything, NaN
+ * included: they are zero-filled on load and never reach an output.
+ * block_size and head_dim must be 128.  num_splits: 0 = automatic, else the maximum.
+ * B == 0 is a no-op.  Status: INVALID_ARG (null pointer, sizes, Hq % Hkv, n_q < 1, R < 1,
+ * num_blocks < 1), UNSUPPORTED (head_dim, block_size, n_q > 128),
+ * WORKSPACE (workspace NULL or smaller than required), HIP (launch failure).
+ */
+int rattn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                       const int* block_table, const int* ctx_lens, const int* windows,
+                       const float* bias, void* out, float* lse, int B, int n_q, int Hq,
+                       int Hkv, int head_dim, int block_size, int R, int num_blocks,
+                       int max_blocks_per_seq, int max_ctx_len, int num_splits,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Message describing the last non-OK status returned on this thread ("" if none). */
+const char* rattn_last_error(void);
+
+/* RATTN_ABI_VERSION of the loaded library. */
+int rattn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RATTN_H */

@@ -1,0 +1,251 @@
+"""Seeded synthetic inputs for relative-bias GQA attention.
+
+This module only draws random numbers and lays them out in memory; it holds
+none of the attention arithmetic.  Both the CPU oracle and the HIP path are
+fed from here so that they see identical bytes.
+
+Conventions (one fresh ``numpy.random.default_rng(seed)`` per workload, draws in
+the order listed by each function):
+
+* bf16 tensors are drawn as float32 ``standard_normal`` and rounded to
+  bfloat16 with round-to-nearest-even; they are returned as ``uint16`` bit
+  patterns (``to_float`` widens them back exactly).
+* The relative-bias table ``r[Hq, R]`` is float32 ``0.5 * standard_normal``
+  (standard deviation 0.5).
+* Layouts: Q ``[B, L, Hq, 128]``, K/V ``[B, L, Hkv, 128]`` token-major; paged
+  caches ``[num_blocks, 128, Hkv, 128]``; block table ``int32 [B, max_blocks]``.
+
+The workload shapes follow the Inkling recipe page (vLLM recipes,
+"thinkingmachines/Inkling", Overview > Architectural highlights: grouped-query
+attention with head size 128, full and sliding-window layers, 9 tokens per
+step with MTP; Client Usage: ``--block-size 128``; TP4 on MI355X, so one GPU
+holds 16 of 64 query heads and 2 of 8 KV heads).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+
+HEAD_DIM = 128
+BLOCK_SIZE = 128
+
+
+# ----------------------------------------------------------------------------
+# bf16 helpers (bit-level, no arithmetic of the method)
+# ----------------------------------------------------------------------------
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns (uint16), round-to-nearest-even.
+
+    NaN inputs stay NaN (quiet bit forced)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32)
+    nan = np.isnan(x)
+    rounded = ((u.astype(np.uint64) + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    if nan.any():
+        rounded[nan] = ((u[nan] >> 16) | 0x0040).astype(np.uint16)
+    return rounded
+
+
+def to_float(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) -> float32, exact."""
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def _normal_bf16(rng: np.random.Generator, shape, chunk: int = 1 << 26) -> np.ndarray:
+    """N(0,1) float32 draws rounded to bf16, generated in chunks to bound memory."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.uint16)
+    for s in range(0, n, chunk):
+        e = min(n, s + chunk)
+        out[s:e] = bf16_round(rng.standard_normal(e - s, dtype=np.float32))
+    return out.reshape(shape)
+
+
+def _normal(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
+    if dtype == "bf16":
+        return _normal_bf16(rng, shape)
+    if dtype == "fp32":
+        return rng.standard_normal(shape, dtype=np.float32)
+    raise ValueError(f"unknown dtype {dtype}")
+
+
+def _bias(rng: np.random.Generator, hq: int, r: int) -> np.ndarray:
+    return (0.5 * rng.standard_normal((hq, r), dtype=np.float32)).astype(np.float32)
+
+
+# ----------------------------------------------------------------------------
+# Prefill (contiguous K/V)
+# ----------------------------------------------------------------------------
+@dataclass
+class PrefillCase:
+    q: np.ndarray            # [B, Lq, Hq, 128] uint16 (bf16 bits) or float32
+    k: np.ndarray            # [B, Lk, Hkv, 128]
+    v: np.ndarray            # [B, Lk, Hkv, 128]
+    bias: np.ndarray         # [Hq, R] float32
+    window: int              # <= 0: full causal
+    dtype: str               # "bf16" | "fp32"
+    name: str = ""
+
+    @property
+    def B(self): return self.q.shape[0]
+    @property
+    def Lq(self): return self.q.shape[1]
+    @property
+    def Lk(self): return self.k.shape[1]
+    @property
+    def Hq(self): return self.q.shape[2]
+    @property
+    def Hkv(self): return self.k.shape[2]
+    @property
+    def R(self): return self.bias.shape[1]
+
+
+def make_prefill(seed: int, B: int, Lq: int, Lk: int, Hq: int, Hkv: int, R: int,
+                 window: int, dtype: str = "bf16", name: str = "") -> PrefillCase:
+    """Draw order: Q, K, V, r."""
+    rng = np.random.default_rng(seed)
+    q = _normal(rng, (B, Lq, Hq, HEAD_DIM), dtype)
+    k = _normal(rng, (B, Lk, Hkv, HEAD_DIM), dtype)
+    v = _normal(rng, (B, Lk, Hkv, HEAD_DIM), dtype)
+    bias = _bias(rng, Hq, R)
+    return PrefillCase(q, k, v, bias, window, dtype, name)
+
+
+# ----------------------------------------------------------------------------
+# Paged decode
+# ----------------------------------------------------------------------------
+@dataclass
+class DecodeCase:
+    q: np.ndarray             # [B, n_q, Hq, 128] uint16 (bf16 bits)
+    k_cache: np.ndarray       # [num_blocks, 128, Hkv, 128] uint16
+    v_cache: np.ndarray       # [num_blocks, 128, Hkv, 128] uint16
+    block_table: np.ndarray   # [B, max_blocks_per_seq] int32
+    ctx_lens: np.ndarray      # [B] int32, tokens in cache including the n_q queries
+    windows: np.ndarray       # [B] int32, <= 0 full
+    bias: np.ndarray          # [Hq, R] float32
+    name: str = ""
+    poison_block: Optional[int] = None
+
+    @property
+    def B(self): return self.q.shape[0]
+    @property
+    def n_q(self): return self.q.shape[1]
+    @property
+    def Hq(self): return self.q.shape[2]
+    @property
+    def Hkv(self): return self.k_cache.shape[2]
+    @property
+    def R(self): return self.bias.shape[1]
+    @property
+    def num_blocks(self): return self.k_cache.shape[0]
+    @property
+    def max_blocks_per_seq(self): return self.block_table.shape[1]
+    @property
+    def max_ctx_len(self): return int(self.ctx_lens.max()) if self.B else 0
+
+
+def resident_block_range(ctx: int, n_q: int, window: int, block_size: int = BLOCK_SIZE):
+    """Logical blocks a serving engine keeps resident for one sequence.
+
+    Full-attention sequences keep every block; a sliding-window sequence keeps
+    the blocks overlapping the last ``window + n_q - 1`` positions (a
+    conservative superset of what its queries can see).  Other block-table
+    entries point at a poison block."""
+    nblk = (ctx + block_size - 1) // block_size
+    if window <= 0:
+        return 0, nblk
+    first_pos = max(0, ctx - n_q - window + 1)
+    return first_pos // block_size, nblk
+
+
+def make_decode(seed: int, ctx_lens, windows, n_q: int, Hq: int, Hkv: int, R: int,
+                name: str = "", poison: bool = True, draw_ctx=None) -> DecodeCase:
+    """Build a paged-KV decode case.
+
+    Draw order: (optional ``draw_ctx(rng)`` for the context lengths), physical
+    block permutation, K cache, V cache, Q, r.  Resident blocks get physical
+    ids from one random permutation; if ``poison`` is set one extra block of
+    NaNs sits at the end and every non-resident block-table entry, as well as
+    every cache slot at or beyond a sequence's context length, holds NaN.
+    """
+    rng = np.random.default_rng(seed)
+    if draw_ctx is not None:
+        ctx_lens = draw_ctx(rng)
+    ctx_lens = np.asarray(ctx_lens, dtype=np.int32)
+    windows = np.asarray(windows, dtype=np.int32)
+    B = len(ctx_lens)
+    ranges = [resident_block_range(int(c), n_q, int(w)) for c, w in zip(ctx_lens, windows)]
+    max_blocks = max((e for _, e in ranges), default=1)
+    total = sum(e - s for s, e in ranges)
+    perm = rng.permutation(total).astype(np.int32)
+    num_blocks = total + (1 if poison else 0)
+    poison_id = total if poison else 0
+    bt = np.full((B, max(1, max_blocks)), poison_id, dtype=np.int32)
+    pos = 0
+    for b, (s, e) in enumerate(ranges):
+        bt[b, s:e] = perm[pos:pos + e - s]
+        pos += e - s
+    shape = (num_blocks, BLOCK_SIZE, Hkv, HEAD_DIM)
+    kc = _normal_bf16(rng, shape)
+    vc = _normal_bf16(rng, shape)
+    nan16 = np.uint16(0x7FC0)
+    if poison:
+        kc[poison_id] = nan16
+        vc[poison_id] = nan16
+        for b, c in enumerate(ctx_lens):
+            c = int(c)
+            last = (c - 1) // BLOCK_SIZE
+            off = c - last * BLOCK_SIZE
+            if off < BLOCK_SIZE:
+                kc[bt[b, last], off:] = nan16
+                vc[bt[b, last], off:] = nan16
+    q = _normal_bf16(rng, (B, n_q, Hq, HEAD_DIM))
+    bias = _bias(rng, Hq, R)
+    return DecodeCase(q, kc, vc, bt, ctx_lens, windows, bias, name, poison_id if poison else None)
+
+
+# ----------------------------------------------------------------------------
+# The five named workloads
+# ----------------------------------------------------------------------------
+WORKLOADS = {
+    "tiny_prefill_fp32": "batch 1, L=256, 4 q / 1 kv heads, fp32, full causal, R=256",
+    "swa_prefill_8k": "batch 1, L=8192, 16 q / 2 kv heads, bf16, window 4096, R=4096",
+    "chunked_prefill_32k": "batch 1, 8192 queries at 24576..32767 over 32768 keys, 16/2 heads, bf16, full, R=8192",
+    "paged_decode_b64": "batch 64, 1 query, ctx U[4096,131072], odd b window 4096, 16/2 heads, bf16, R=8192",
+    "mtp_verify_1m": "batch 1, 9 queries at the tail of 1,048,576 keys, 16/2 heads, bf16, full, R=8192",
+}
+
+
+def tiny_prefill_fp32(seed: int = 0) -> PrefillCase:
+    return make_prefill(seed, 1, 256, 256, 4, 1, 256, 0, "fp32", "tiny_prefill_fp32")
+
+
+def swa_prefill_8k(seed: int = 0) -> PrefillCase:
+    return make_prefill(seed, 1, 8192, 8192, 16, 2, 4096, 4096, "bf16", "swa_prefill_8k")
+
+
+def chunked_prefill_32k(seed: int = 0) -> PrefillCase:
+    return make_prefill(seed, 1, 8192, 32768, 16, 2, 8192, 0, "bf16", "chunked_prefill_32k")
+
+
+def paged_decode_b64(seed: int = 0) -> DecodeCase:
+    B = 64
+    windows = np.where(np.arange(B) % 2 == 1, 4096, 0).astype(np.int32)
+    draw = lambda rng: rng.integers(4096, 131072, size=B, endpoint=True).astype(np.int32)
+    return make_decode(seed, None, windows, 1, 16, 2, 8192, "paged_decode_b64", True, draw)
+
+
+def mtp_verify_1m(seed: int = 0) -> DecodeCase:
+    return make_decode(seed, [1 << 20], [0], 9, 16, 2, 8192, "mtp_verify_1m", poison=False)
+
+
+WORKLOAD_FNS = {
+    "tiny_prefill_fp32": tiny_prefill_fp32,
+    "swa_prefill_8k": swa_prefill_8k,
+    "chunked_prefill_32k": chunked_prefill_32k,
+    "paged_decode_b64": paged_decode_b64,
+    "mtp_verify_1m": mtp_verify_1m,
+}
