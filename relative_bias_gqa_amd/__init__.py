@@ -1,1 +1,171 @@
-"""relative_bias_gqa_amd: relative-bias GQA attention for MI355X (placeholder; binding lands with the HIP library)."""
+"""relative_bias_gqa_amd -- relative-bias grouped-query attention for MI355X (gfx950).
+
+Thin ctypes binding over ``librattn.so`` (C ABI in ``include/rattn.h``).  The
+functions named like the C entry points only marshal arguments: they read
+shapes and device pointers off torch tensors and call the library on the
+current (or given) HIP stream.  Every step of the computation runs in the HIP
+kernels; there is no fallback.  If the library is missing or fails to load,
+every call raises.
+
+Operation (vLLM recipes page "thinkingmachines/Inkling", Overview >
+Architectural highlights > Attention): GQA with head size 128 and a learned
+relative-position term on the pre-softmax logits, fixed here as
+``logit[i,j] = q_i.k_j/sqrt(128) + r[h, min(i-j, R-1)]``; causal full or
+sliding-window; prefill over contiguous K/V and paged (block 128) decode with
+multi-query (MTP) verification.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librattn.so")
+
+RATTN_OK, RATTN_ERR_INVALID_ARG, RATTN_ERR_UNSUPPORTED, RATTN_ERR_WORKSPACE, RATTN_ERR_HIP = 0, 1, 2, 3, 4
+RATTN_BF16, RATTN_FP32 = 0, 1
+ABI_VERSION = 1
+
+EXPORTED = ("rattn_prefill", "rattn_decode_num_splits", "rattn_decode_workspace_bytes", "rattn_decode_paged",
+            "rattn_last_error", "rattn_abi_version")
+
+_lib = None
+
+
+class RattnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"status {status}: {message}")
+        self.status = status
+
+
+def load(path: Optional[str] = None):
+    """Load (once) and return the ctypes handle of librattn.so."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is not built: run `python -m relative_bias_gqa_amd.build` "
+                           "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(p)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.rattn_prefill.restype = i32
+    lib.rattn_prefill.argtypes = [vp] * 6 + [i32] * 9 + [vp]
+    lib.rattn_decode_num_splits.restype = i32
+    lib.rattn_decode_num_splits.argtypes = [i32] * 6
+    lib.rattn_decode_workspace_bytes.restype = sz
+    lib.rattn_decode_workspace_bytes.argtypes = [i32] * 6
+    lib.rattn_decode_paged.restype = i32
+    lib.rattn_decode_paged.argtypes = [vp] * 9 + [i32] * 11 + [vp, sz, vp]
+    lib.rattn_last_error.restype = ctypes.c_char_p
+    lib.rattn_last_error.argtypes = []
+    lib.rattn_abi_version.restype = i32
+    lib.rattn_abi_version.argtypes = []
+    if lib.rattn_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"{p}: ABI version {lib.rattn_abi_version()} != {ABI_VERSION}")
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def rattn_last_error() -> str:
+    return load().rattn_last_error().decode()
+
+
+def rattn_abi_version() -> int:
+    return load().rattn_abi_version()
+
+
+def _check(status: int):
+    if status != RATTN_OK:
+        raise RattnError(status, rattn_last_error())
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to librattn must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return RATTN_BF16
+    if t.dtype == torch.float32:
+        return RATTN_FP32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def rattn_prefill(q, k, v, bias, out, lse=None, window: int = 0, stream=None) -> None:
+    """q [B,Lq,Hq,128], k/v [B,Lk,Hkv,128] (bf16 or fp32), bias [Hq,R] fp32,
+    out like q, lse [B,Lq,Hq] fp32 or None.  Query t sits at position Lk-Lq+t."""
+    B, Lq, Hq, D = q.shape
+    Lk, Hkv = k.shape[1], k.shape[2]
+    R = bias.shape[1]
+    _check(load().rattn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(out), _ptr(lse),
+                                B, Lq, Lk, Hq, Hkv, D, R, int(window), _dtype_code(q), _stream(stream)))
+
+
+def rattn_decode_num_splits(B: int, n_q: int, Hq: int, Hkv: int, max_ctx_len: int, num_splits: int = 0) -> int:
+    return load().rattn_decode_num_splits(B, n_q, Hq, Hkv, max_ctx_len, num_splits)
+
+
+def rattn_decode_workspace_bytes(B: int, n_q: int, Hq: int, Hkv: int, max_ctx_len: int,
+                                 num_splits: int = 0) -> int:
+    return load().rattn_decode_workspace_bytes(B, n_q, Hq, Hkv, max_ctx_len, num_splits)
+
+
+def rattn_decode_paged(q, k_cache, v_cache, block_table, ctx_lens, windows, bias, out, lse,
+                       max_ctx_len: int, num_splits: int = 0, workspace=None, stream=None) -> None:
+    """q [B,n_q,Hq,128] bf16; caches [num_blocks,128,Hkv,128] bf16; block_table [B,mb] int32;
+    ctx_lens [B] int32 (including the n_q queries); windows [B] int32 or None; bias [Hq,R]
+    fp32; out like q; lse [B,n_q,Hq] fp32 or None; workspace a uint8 device tensor of at
+    least rattn_decode_workspace_bytes(...) bytes."""
+    B, n_q, Hq, D = q.shape
+    num_blocks, bs, Hkv = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+    mb = block_table.shape[1]
+    R = bias.shape[1]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().rattn_decode_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(ctx_lens),
+                                     _ptr(windows), _ptr(bias), _ptr(out), _ptr(lse), B, n_q, Hq, Hkv, D, bs, R,
+                                     num_blocks, mb, int(max_ctx_len), int(num_splits), _ptr(workspace), ws_bytes,
+                                     _stream(stream)))
+
+
+# ---- conveniences that allocate the outputs (torch device memory) and call the above ----
+def prefill(q, k, v, bias, window: int = 0, want_lse: bool = True, stream=None) -> Tuple:
+    import torch
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if want_lse else None
+    rattn_prefill(q, k, v, bias, out, lse, window, stream)
+    return out, lse
+
+
+def decode_workspace(B, n_q, Hq, Hkv, max_ctx_len, num_splits=0, device="cuda"):
+    import torch
+    n = rattn_decode_workspace_bytes(B, n_q, Hq, Hkv, max_ctx_len, num_splits)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+
+
+def decode_paged(q, k_cache, v_cache, block_table, ctx_lens, windows, bias, max_ctx_len: int,
+                 num_splits: int = 0, want_lse: bool = True, workspace=None, stream=None) -> Tuple:
+    import torch
+    B, n_q, Hq, _ = q.shape
+    Hkv = k_cache.shape[2]
+    if workspace is None:
+        workspace = decode_workspace(B, n_q, Hq, Hkv, max_ctx_len, num_splits, q.device)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if want_lse else None
+    rattn_decode_paged(q, k_cache, v_cache, block_table, ctx_lens, windows, bias, out, lse, max_ctx_len,
+                       num_splits, workspace, stream)
+    return out, lse

@@ -1,0 +1,113 @@
+// device_common.hpp -- gfx950 building blocks shared by the attention kernels.
+//
+// MFMA operand layouts (v_mfma_f32_32x32x16_bf16, wave64), as used throughout:
+//   A (32 x 16):  lane l holds A[l % 32][8 * (l / 32) + e],  e = 0..7
+//   B (16 x 32):  lane l holds B[8 * (l / 32) + e][l % 32]
+//   C (32 x 32):  lane l, register r holds C[8 * (r / 4) + 4 * (l / 32) + r % 4][l % 32]
+// The kernels compute S^T = K Q^T and O^T = V^T P^T, so a lane's accumulator column
+// is one query row and the softmax statistics of that row live in the lane and its
+// partner lane l ^ 32.
+//
+// ds_read_b64_tr_b16 (LDS transpose read): within each group of 16 lanes, if lane m
+// supplies the address of four consecutive 16-bit elements M[m][0..3], lane i receives
+// M[4 e + i / 4][i % 4] for e = 0..3.  With lane m pointing at V[row0 + m / 4][col0 +
+// 4 (m % 4)] this hands lane i the column V[row0 + 0..3][col0 + i] of a row-major tile,
+// which is the V^T operand of the P.V product without any transposed store.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rattn {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kHeadDim = 128;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+__device__ __forceinline__ f32x16_t mfma_32x32x16(u32x4_t a, u32x4_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// Two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2_t v;
+  v[0] = (__bf16)lo;
+  v[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float bf16_lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Combine a value with the one held by lane l ^ 32 (v_permlane32_swap: lane l < 32 gets
+// its partner's value in the second result, lane l >= 32 in the first).
+__device__ __forceinline__ float half_swap_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_swap_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// V^T operand (32 d-rows x 16 keys) of one MFMA from a row-major bf16 V tile in LDS.
+// Key order within the 16-key step: lane half hf supplies keys kbase + 4 hf + 0..3 and
+// kbase + 8 + 4 hf + 0..3, matching the register order of the S^T accumulator.
+__device__ __forceinline__ u32x4_t load_vt_operand(const uint16_t* v_tile, int stride, int kbase,
+                                                   int dcol0, int lane) {
+  const int m = lane & 15;
+  const int hf = lane >> 5;
+  const int row = kbase + 4 * hf + (m >> 2);
+  const int col = dcol0 + 16 * ((lane >> 4) & 1) + 4 * (m & 3);
+  const s16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(v_tile + row * stride + col));
+  const s16x4_t b =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(v_tile + (row + 8) * stride + col));
+  const u32x2_t ua = __builtin_bit_cast(u32x2_t, a);
+  const u32x2_t ub = __builtin_bit_cast(u32x2_t, b);
+  u32x4_t r;
+  r[0] = ua[0];
+  r[1] = ua[1];
+  r[2] = ub[0];
+  r[3] = ub[1];
+  return r;
+}
+
+// P^T operand for one 16-key step from eight probabilities (accumulator registers
+// 8*half .. 8*half+7 of a 32-key block), packed to bf16.
+__device__ __forceinline__ u32x4_t pack_p_operand(const float* p8) {
+  u32x4_t r;
+  r[0] = pack_bf16x2(p8[0], p8[1]);
+  r[1] = pack_bf16x2(p8[2], p8[3]);
+  r[2] = pack_bf16x2(p8[4], p8[5]);
+  r[3] = pack_bf16x2(p8[6], p8[7]);
+  return r;
+}
+
+__device__ __forceinline__ u32x4_t zero_u32x4() {
+  u32x4_t z;
+  z[0] = z[1] = z[2] = z[3] = 0u;
+  return z;
+}
+
+__device__ __forceinline__ f32x16_t zero_f32x16() {
+  f32x16_t z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+}  // namespace rattn

@@ -1,0 +1,130 @@
+"""The C-ABI library on the CPU: it loads, exports what include/rattn.h declares, and
+rejects bad arguments with the documented status before touching a device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import relative_bias_gqa_amd as rb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rattn.h")
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation or is a no-op
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(rb.LIB_PATH):
+        rb_build = __import__("relative_bias_gqa_amd.build", fromlist=["build"])
+        rb_build.build()
+    return rb.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rattn_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_names():
+    assert declared_functions() == sorted(rb.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_abi_version(lib):
+    assert lib.rattn_abi_version() == rb.ABI_VERSION == 1
+
+
+def _prefill(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, bias=FAKE, out=FAKE, lse=None, B=1, Lq=4, Lk=4, Hq=4, Hkv=2, D=128, R=8,
+             window=0, dtype=0, stream=None)
+    a.update(kw)
+    return lib.rattn_prefill(a["q"], a["k"], a["v"], a["bias"], a["out"], a["lse"], a["B"], a["Lq"], a["Lk"],
+                             a["Hq"], a["Hkv"], a["D"], a["R"], a["window"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(q=None), rb.RATTN_ERR_INVALID_ARG, "null"),
+    (dict(bias=None), rb.RATTN_ERR_INVALID_ARG, "null"),
+    (dict(out=None), rb.RATTN_ERR_INVALID_ARG, "null"),
+    (dict(Hq=6, Hkv=4), rb.RATTN_ERR_INVALID_ARG, "multiple"),
+    (dict(Hkv=0), rb.RATTN_ERR_INVALID_ARG, "multiple"),
+    (dict(Lq=5, Lk=4), rb.RATTN_ERR_INVALID_ARG, "Lq"),
+    (dict(R=0), rb.RATTN_ERR_INVALID_ARG, "R="),
+    (dict(B=-1), rb.RATTN_ERR_INVALID_ARG, "negative"),
+    (dict(D=64), rb.RATTN_ERR_UNSUPPORTED, "head_dim"),
+    (dict(dtype=7), rb.RATTN_ERR_UNSUPPORTED, "dtype"),
+])
+def test_prefill_validation(lib, kw, status, needle):
+    assert _prefill(lib, **kw) == status
+    assert needle in rb.rattn_last_error()
+
+
+def test_prefill_empty_is_noop(lib):
+    assert _prefill(lib, B=0, q=None, k=None, v=None, bias=None, out=None) == rb.RATTN_OK
+    assert _prefill(lib, Lq=0, q=None, out=None) == rb.RATTN_OK
+    assert rb.rattn_last_error() == ""
+
+
+def _decode(lib, **kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, ctx=FAKE, win=None, bias=FAKE, out=FAKE, lse=None, B=2, n_q=1,
+             Hq=16, Hkv=2, D=128, bs=128, R=8, nb=4, mb=2, max_ctx=200, ns=0, ws=FAKE, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return lib.rattn_decode_paged(a["q"], a["kc"], a["vc"], a["bt"], a["ctx"], a["win"], a["bias"], a["out"],
+                                  a["lse"], a["B"], a["n_q"], a["Hq"], a["Hkv"], a["D"], a["bs"], a["R"], a["nb"],
+                                  a["mb"], a["max_ctx"], a["ns"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(q=None), rb.RATTN_ERR_INVALID_ARG, "null"),
+    (dict(bt=None), rb.RATTN_ERR_INVALID_ARG, "null"),
+    (dict(ctx=None), rb.RATTN_ERR_INVALID_ARG, "null"),
+    (dict(Hq=15), rb.RATTN_ERR_INVALID_ARG, "multiple"),
+    (dict(n_q=0), rb.RATTN_ERR_INVALID_ARG, "n_q"),
+    (dict(R=0), rb.RATTN_ERR_INVALID_ARG, "R="),
+    (dict(nb=0), rb.RATTN_ERR_INVALID_ARG, "num_blocks"),
+    (dict(max_ctx=0), rb.RATTN_ERR_INVALID_ARG, "max_ctx_len"),
+    (dict(max_ctx=257, mb=2), rb.RATTN_ERR_INVALID_ARG, "block table"),
+    (dict(D=96), rb.RATTN_ERR_UNSUPPORTED, "head_dim"),
+    (dict(bs=16), rb.RATTN_ERR_UNSUPPORTED, "block_size"),
+    (dict(n_q=129, max_ctx=256), rb.RATTN_ERR_UNSUPPORTED, "n_q"),
+    (dict(ws=None), rb.RATTN_ERR_WORKSPACE, "workspace"),
+    (dict(wsb=16), rb.RATTN_ERR_WORKSPACE, "workspace"),
+])
+def test_decode_validation(lib, kw, status, needle):
+    assert _decode(lib, **kw) == status
+    assert needle in rb.rattn_last_error()
+
+
+def test_decode_empty_is_noop(lib):
+    assert _decode(lib, B=0, q=None, kc=None) == rb.RATTN_OK
+
+
+def test_workspace_and_split_plan(lib):
+    # the workspace holds a partial output (128 fp32) and a log-sum-exp per row and split
+    for (B, n_q, Hq, Hkv, ctx, ns) in [(64, 1, 16, 2, 131072, 0), (1, 9, 16, 2, 1 << 20, 0), (3, 2, 8, 8, 1000, 5)]:
+        S = rb.rattn_decode_num_splits(B, n_q, Hq, Hkv, ctx, ns)
+        assert 1 <= S <= (ctx + 127) // 128
+        if ns:
+            assert S <= ns
+        wsb = rb.rattn_decode_workspace_bytes(B, n_q, Hq, Hkv, ctx, ns)
+        rows = B * n_q * Hq
+        assert wsb >= rows * S * 129 * 4
+        assert wsb <= rows * S * 129 * 4 + 256
+    # more splits requested than blocks: capped at one block per split
+    assert rb.rattn_decode_num_splits(1, 1, 8, 1, 300, 100) == 3
+    assert rb.rattn_decode_workspace_bytes(1, 0, 8, 1, 300, 0) == 0
+    # automatic plan spreads the 1M-token verify over many splits (enough workgroups)
+    S5 = rb.rattn_decode_num_splits(1, 9, 16, 2, 1 << 20, 0)
+    assert S5 * 2 >= 256
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(RuntimeError, match="not built"):
+        rb.load(str(tmp_path / "missing.so"))
