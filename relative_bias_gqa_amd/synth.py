@@ -23,7 +23,9 @@ holds 16 of 64 query heads and 2 of 8 KV heads).
 """
 from __future__ import annotations
 
-from dataclasses import dataclass, field
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass
 from typing import Optional
 
 import numpy as np
@@ -41,8 +43,9 @@ def bf16_round(x: np.ndarray) -> np.ndarray:
     NaN inputs stay NaN (quiet bit forced)."""
     x = np.ascontiguousarray(x, dtype=np.float32)
     u = x.view(np.uint32)
+    # no finite or infinite input can carry past bit 31 here (largest is 0xFF7FFFFF + 0x8000)
+    rounded = ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
     nan = np.isnan(x)
-    rounded = ((u.astype(np.uint64) + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
     if nan.any():
         rounded[nan] = ((u[nan] >> 16) | 0x0040).astype(np.uint16)
     return rounded
@@ -54,13 +57,33 @@ def to_float(bits: np.ndarray) -> np.ndarray:
     return (bits.astype(np.uint32) << 16).view(np.float32)
 
 
-def _normal_bf16(rng: np.random.Generator, shape, chunk: int = 1 << 26) -> np.ndarray:
-    """N(0,1) float32 draws rounded to bf16, generated in chunks to bound memory."""
+_CHUNK = 1 << 22
+
+
+def _normal_bf16(rng: np.random.Generator, shape) -> np.ndarray:
+    """N(0,1) float32 draws rounded to bf16.
+
+    One 63-bit key is drawn from ``rng``; chunk c of ``_CHUNK`` values then comes from
+    its own PCG64 stream seeded with (key, c), so large tensors fill in parallel and the
+    bytes do not depend on the number of threads."""
     n = int(np.prod(shape))
+    key = int(rng.integers(0, 1 << 63))
     out = np.empty(n, dtype=np.uint16)
-    for s in range(0, n, chunk):
-        e = min(n, s + chunk)
-        out[s:e] = bf16_round(rng.standard_normal(e - s, dtype=np.float32))
+
+    def fill(c: int) -> None:
+        s = c * _CHUNK
+        e = min(n, s + _CHUNK)
+        g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([key, c])))
+        out[s:e] = bf16_round(g.standard_normal(e - s, dtype=np.float32))
+
+    nchunks = (n + _CHUNK - 1) // _CHUNK
+    if nchunks <= 1:
+        for c in range(nchunks):
+            fill(c)
+    else:
+        workers = max(1, min(16, len(os.sched_getaffinity(0)), nchunks))
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(fill, range(nchunks)))
     return out.reshape(shape)
 
 
