@@ -233,6 +233,10 @@ def main(argv=None) -> int:
     ap.add_argument("--only-headline", action="store_true", help="time only the headline workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-stride", type=int, default=4, help="oracle sample: every n-th query row")
+    ap.add_argument("--only", default=None,
+                    help="time just this workload and print its own result line (for profiler runs)")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="also run 4 device-to-device copies of this many MiB (byte-counter calibration)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -255,6 +259,27 @@ def main(argv=None) -> int:
         if a.dtype == np.uint16:
             return torch.from_numpy(a.view(np.int16)).to("cuda:0").view(torch.bfloat16)
         return torch.from_numpy(a).to("cuda:0")
+
+    if args.copy_calib_mib > 0:
+        n = args.copy_calib_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy calibration: 4 copies of {n} bytes")
+        del src, dst
+    if args.only:
+        if args.only not in ALL_WORKLOADS:
+            raise SystemExit(f"unknown workload {args.only}")
+        cls = DecodeRun if args.only in ("paged_decode_b64", "mtp_verify_1m") else PrefillRun
+        run = cls(args.only, torch, rb, synth, dev)
+        torch.cuda.synchronize()
+        sec = time_steps(run, torch, args.steps, args.warmup)
+        res = result_of(run, sec)
+        log(f"[bench] {args.only}: {res['ms_per_step']:.4f} ms/step, {res['value']} {run.unit}")
+        print(json.dumps(res), flush=True)
+        return 0
 
     names = [HEADLINE] if args.only_headline else [w for w in args.workloads.split(",") if w]
     if HEADLINE not in names:
