@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define RATTN_ABI_VERSION 1
+#define RATTN_ABI_VERSION 2
 
 enum rattn_status {
   RATTN_OK = 0,
@@ -75,22 +75,26 @@ int rattn_prefill(const void* q, const void* k, const void* v, const float* bias
                   int window, int dtype, void* stream);
 
 /*
- * Number of KV splits per (sequence, KV head) that rattn_decode_paged will use for these
- * arguments.  num_splits > 0 requests at most that many splits; 0 lets the library choose
- * from the sizes alone (no device query).  Returns 0 for invalid sizes.
+ * Number of split workgroups rattn_decode_paged will use for these arguments.  The
+ * visible keys of the whole batch form one stream of 64-token units that is divided
+ * evenly among them.  num_splits > 0 asks for exactly that many (fewer when the batch has
+ * fewer units); 0 selects the default, one per compute unit of an MI355X (256).  Returns
+ * 0 for invalid sizes.  The choice changes only the summation order of the result.
  */
 int rattn_decode_num_splits(int B, int n_q, int Hq, int Hkv, int max_ctx_len, int num_splits);
 
 /*
- * Device workspace, in bytes, that rattn_decode_paged needs for these arguments (partial
- * outputs and log-sum-exps of every split).  Returns 0 for invalid sizes.
+ * Device workspace, in bytes, that rattn_decode_paged needs for these arguments (one
+ * partial output and log-sum-exp per split workgroup and per segment it touches).  It is
+ * an upper bound for any max_blocks_per_seq.  Returns 0 for invalid sizes.
  */
 size_t rattn_decode_workspace_bytes(int B, int n_q, int Hq, int Hkv, int max_ctx_len,
                                     int num_splits);
 
 /*
  * Paged decode with multi-query (MTP) verification: n_q query tokens per sequence attend
- * to the sequence's paged KV cache, split over the context and merged by log-sum-exp.
+ * to the sequence's paged KV cache.  The visible keys are split among the workgroups
+ * (rattn_decode_num_splits) and the partial results are merged by log-sum-exp.
  *
  *   q           [B, n_q, Hq, 128]                 bf16   device, read
  *   k_cache     [num_blocks, 128, Hkv, 128]       bf16   device, read
@@ -112,7 +116,8 @@ size_t rattn_decode_workspace_bytes(int B, int n_q, int Hq, int Hkv, int max_ctx
  * block-table entries are never dereferenced and may hold anything.  Cache slots outside
  * [max(0, ctx - n_q - W + 1), ctx) (W the window, 0 if full) may hold anything, NaN
  * included: they are zero-filled on load and never reach an output.
- * block_size and head_dim must be 128.  num_splits: 0 = automatic, else the maximum.
+ * block_size and head_dim must be 128.  num_splits: 0 = automatic, else the number of split
+ * workgroups.  Batches are processed in launches of at most 2048 sequences.
  * B == 0 is a no-op.  Status: INVALID_ARG (null pointer, sizes, Hq % Hkv, n_q < 1, R < 1,
  * num_blocks < 1), UNSUPPORTED (head_dim, block_size, n_q > 128),
  * WORKSPACE (workspace NULL or smaller than required), HIP (launch failure).

@@ -36,54 +36,60 @@ int largest_divisor_at_most(int n, int cap) {
 constexpr int kMaxPosition = (1 << 30) - 1;  // positions stay clear of the kernels' window sentinel
 constexpr float kScaleLog2 = 1.4426950408889634f * 0.08838834764831845f;  // log2(e) / sqrt(128)
 
-// ---- paged-decode split plan ---------------------------------------------------------
+// ---- paged-decode plan ---------------------------------------------------------------
+// Segment = (sequence, KV head, subgroup of gs query heads); rows = n_q * gs.  The unit
+// stream (64-token units of every segment) is divided among P workgroups; sequences are
+// processed in launches of at most `batch` sequences, each reusing the same workspace.
+constexpr int kAutoWorkgroups = 256;  // one per compute unit of an MI355X
+
 struct DecodePlan {
-  int gs, n_hs, rows, S, SB;
-  size_t o_bytes, lse_off, total;
+  int gs, n_hs, KH, rows, SL, P, batch, KS;
+  size_t lse_off, total;
 };
 
-bool plan_decode(int B, int n_q, int Hq, int Hkv, int max_ctx_len, int num_splits, DecodePlan* pl) {
-  if (B < 0 || n_q < 1 || n_q > rattn::kDecodeMaxRows || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 ||
-      max_ctx_len < 1 || max_ctx_len > kMaxPosition || num_splits < 0)
+bool plan_decode(int B, int n_q, int Hq, int Hkv, int max_ctx_len, int max_blocks, int num_splits, DecodePlan* pl) {
+  if (B < 1 || n_q < 1 || n_q > rattn::kDecodeMaxRows || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 ||
+      max_ctx_len < 1 || max_ctx_len > kMaxPosition || max_blocks < 1 || num_splits < 0)
     return false;
   const int G = Hq / Hkv;
-  // query heads per workgroup: as many of the group as fit the row and bias-slice limits
-  int gs = 1;
+  const int SL = rattn::kDecodeUnit - 1 + n_q;
+  // query heads per segment: the largest divisor of G whose rows fit four waves and whose
+  // bias slices fit the per-unit staging buffer
+  int gs = 0;
   for (int d = G; d >= 1; --d) {
-    if (G % d != 0) continue;
-    if (n_q * d <= rattn::kDecodeMaxRows && d * (127 + n_q) <= rattn::kDecodeBiasFloats) {
+    if (G % d == 0 && n_q * d <= rattn::kDecodeMaxRows && d * SL <= rattn::kDecodeBiasFloats) {
       gs = d;
       break;
     }
   }
-  const int rows = n_q * gs;
+  if (gs == 0) return false;
   const int n_hs = G / gs;
-  const long long max_blocks = (max_ctx_len + 127) / 128;
-  long long SB;
-  if (num_splits > 0) {
-    const long long S = num_splits < max_blocks ? num_splits : max_blocks;
-    SB = (max_blocks + S - 1) / S;
-  } else {
-    // (a) each split reads at least 64x the bytes of partial results it writes
-    //     (rows x 129 floats against SB blocks of 32 KB K + 32 KB V);
-    // (b) the grid offers about 8192 workgroups at the longest context.
-    const long long min_sb = ((long long)rows * 129 * 4 * 64 + 65535) / 65536;
-    const long long fill_sb = ((long long)B * Hkv * n_hs * max_blocks + 8191) / 8192;
-    SB = min_sb > fill_sb ? min_sb : fill_sb;
-    if (SB < 1) SB = 1;
-  }
-  const long long S = (max_blocks + SB - 1) / SB;
-  const long long nrows = (long long)B * n_q * Hq;
-  const long long grid = (long long)B * Hkv * n_hs * S;
-  if (grid > 0x7fffffffLL || nrows > 0x7fffffffLL) return false;
+  const long long KH = (long long)Hkv * n_hs;
+  // units per launch must stay below 2^31 (a sequence has at most 2 units per block-table
+  // entry, whatever ctx_lens holds: the kernels clamp it to the table)
+  (void)max_ctx_len;
+  const long long max_units_per_seq = 2LL * max_blocks + 1;
+  long long batch = B < rattn::kDecodeMaxBatch ? B : rattn::kDecodeMaxBatch;
+  const long long cap = 0x7fffffffLL / (max_units_per_seq * KH);
+  if (cap < 1) return false;
+  if (batch > cap) batch = cap;
+  const int P = num_splits > 0 ? num_splits : kAutoWorkgroups;
+  const long long rows = (long long)n_q * gs;
+  // up to two row blocks of 32: the two 32-key halves of a unit go to different waves
+  const int KS = rows <= 64 ? 2 : 1;
+  const long long slots = (P + batch * KH) * KS;
+  if (batch * KH * rows > 0x7fffffffLL) return false;
   pl->gs = gs;
   pl->n_hs = n_hs;
-  pl->rows = rows;
-  pl->S = (int)S;
-  pl->SB = (int)SB;
-  pl->o_bytes = (size_t)nrows * (size_t)S * 128 * sizeof(float);
-  pl->lse_off = (pl->o_bytes + 255) & ~(size_t)255;
-  pl->total = pl->lse_off + (size_t)nrows * (size_t)S * sizeof(float);
+  pl->KH = (int)KH;
+  pl->rows = (int)rows;
+  pl->SL = SL;
+  pl->P = P;
+  pl->batch = (int)batch;
+  pl->KS = KS;
+  const size_t o_bytes = (size_t)slots * (size_t)rows * 128 * sizeof(float);
+  pl->lse_off = (o_bytes + 255) & ~(size_t)255;
+  pl->total = pl->lse_off + (size_t)slots * (size_t)rows * sizeof(float);
   return true;
 }
 
@@ -144,13 +150,13 @@ int rattn_prefill(const void* q, const void* k, const void* v, const float* bias
 
 int rattn_decode_num_splits(int B, int n_q, int Hq, int Hkv, int max_ctx_len, int num_splits) {
   DecodePlan pl;
-  if (!plan_decode(B, n_q, Hq, Hkv, max_ctx_len, num_splits, &pl)) return 0;
-  return pl.S;
+  if (!plan_decode(B, n_q, Hq, Hkv, max_ctx_len, (max_ctx_len + 127) / 128, num_splits, &pl)) return 0;
+  return pl.P;
 }
 
 size_t rattn_decode_workspace_bytes(int B, int n_q, int Hq, int Hkv, int max_ctx_len, int num_splits) {
   DecodePlan pl;
-  if (!plan_decode(B, n_q, Hq, Hkv, max_ctx_len, num_splits, &pl)) return 0;
+  if (!plan_decode(B, n_q, Hq, Hkv, max_ctx_len, (max_ctx_len + 127) / 128, num_splits, &pl)) return 0;
   return pl.total;
 }
 
@@ -182,25 +188,18 @@ int rattn_decode_paged(const void* q, const void* k_cache, const void* v_cache, 
     return fail(RATTN_ERR_INVALID_ARG, "rattn_decode_paged: max_ctx_len=%d exceeds the block table (%d blocks)",
                 max_ctx_len, max_blocks_per_seq);
   DecodePlan pl;
-  if (!plan_decode(B, n_q, Hq, Hkv, max_ctx_len, num_splits, &pl))
+  if (!plan_decode(B, n_q, Hq, Hkv, max_ctx_len, max_blocks_per_seq, num_splits, &pl))
     return fail(RATTN_ERR_INVALID_ARG, "rattn_decode_paged: problem too large for one launch");
   if (!workspace || workspace_bytes < pl.total)
     return fail(RATTN_ERR_WORKSPACE, "rattn_decode_paged: workspace %zu bytes at %p, need %zu", workspace_bytes,
                 workspace, pl.total);
 
   rattn::DecodeParams p;
-  p.q = (const uint16_t*)q;
   p.k_cache = (const uint16_t*)k_cache;
   p.v_cache = (const uint16_t*)v_cache;
-  p.block_table = block_table;
-  p.ctx_lens = ctx_lens;
-  p.windows = windows;
   p.bias = bias;
-  p.out = (uint16_t*)out;
-  p.lse = lse;
   p.ws_o = (float*)workspace;
   p.ws_lse = (float*)((char*)workspace + pl.lse_off);
-  p.B = B;
   p.n_q = n_q;
   p.Hq = Hq;
   p.Hkv = Hkv;
@@ -210,12 +209,24 @@ int rattn_decode_paged(const void* q, const void* k_cache, const void* v_cache, 
   p.G = Hq / Hkv;
   p.gs = pl.gs;
   p.n_hs = pl.n_hs;
+  p.KH = pl.KH;
   p.rows = pl.rows;
-  p.S = pl.S;
-  p.SB = pl.SB;
+  p.SL = pl.SL;
+  p.KS = pl.KS;
+  p.P = pl.P;
   p.scale_log2 = kScaleLog2;
-  hipError_t e = rattn::launch_decode(p, (hipStream_t)stream);
-  if (e != hipSuccess) return fail(RATTN_ERR_HIP, "rattn_decode_paged: launch failed: %s", hipGetErrorString(e));
+  const size_t q_rows = (size_t)n_q * Hq;
+  for (int b0 = 0; b0 < B; b0 += pl.batch) {
+    p.B = B - b0 < pl.batch ? B - b0 : pl.batch;
+    p.q = (const uint16_t*)q + (size_t)b0 * q_rows * 128;
+    p.out = (uint16_t*)out + (size_t)b0 * q_rows * 128;
+    p.lse = lse ? lse + (size_t)b0 * q_rows : nullptr;
+    p.block_table = block_table + (size_t)b0 * max_blocks_per_seq;
+    p.ctx_lens = ctx_lens + b0;
+    p.windows = windows ? windows + b0 : nullptr;
+    hipError_t e = rattn::launch_decode(p, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(RATTN_ERR_HIP, "rattn_decode_paged: launch failed: %s", hipGetErrorString(e));
+  }
   return ok();
 }
 

@@ -1,4 +1,4 @@
-// decode.hip -- paged split-KV decode with multi-query (MTP) verification for gfx950.
+// decode.hip -- paged decode with multi-query (MTP) verification for gfx950.
 //
 // Each sequence b has ctx_lens[b] keys in a paged cache of 128-token blocks (vLLM recipes
 // page "thinkingmachines/Inkling", Client Usage: "--block-size 128") and n_q query tokens
@@ -8,322 +8,573 @@
 //   softmax_j(q.k_j / sqrt(128) + r[h, min(p - j, R - 1)]) . V over the causal (and, for a
 //   sliding-window sequence, windowed) keys.
 //
-// Pass 1 (split kernel): workgroup = (sequence, KV head, query-head subgroup, split of SB
-// consecutive cache blocks).  Its query rows are the n_q tokens x gs query heads that
-// share the KV head (GQA packing: every K/V block is read from HBM once for all of them).
-// Waves own 32 rows each.  Per cache block the workgroup gathers K and V (32 KB each per KV
-// head) through the block table into LDS -- the next block's loads are in flight while the
-// current one is computed -- and each wave does S^T = K Q^T, bias + mask, an online
-// softmax and O^T += V^T P^T.  Slots outside the sequence's visible range are zero-filled
-// on load, so poisoned (NaN) cache contents never reach the arithmetic.  The split writes
-// its normalised partial output and log2-sum-exp to the workspace.
-// Pass 2 (merge kernel): per query row, LSE = log sum_s exp(LSE_s) and
-// O = sum_s exp(LSE_s - LSE) O_s, written as bf16 (+ natural-log lse).
+// The operation streams the visible K/V of the batch once, so it is bound by HBM bytes.
+// Work decomposition: a segment is (sequence, KV head, query-head subgroup); its rows are
+// the n_q tokens x gs query heads that share the KV head (GQA packing: each K/V byte is
+// read from HBM once for all of them).  A segment's visible keys are cut into 64-token
+// units; the units of all segments, in order, form one stream that is divided evenly
+// among P workgroups (one per CU), so every CU moves the same number of bytes whatever
+// the context lengths.  A workgroup walks its units in order and writes one normalised
+// partial output and log2-sum-exp per segment it touches (slot = workgroup + segment);
+// the merge kernel combines the pieces of each segment.
+//
+// Split kernel pipeline (4 waves): K and V rows of a unit are gathered through the block
+// table straight into LDS (global_load_lds_dwordx4, no register staging) into a ring of
+// four stages, three units ahead of the one being computed, so about 96 KB per CU are
+// always in flight.  Slots outside a sequence's visible range are loaded from a zero row
+// instead of the cache, so poisoned (NaN) cache contents never reach the arithmetic and
+// invisible block-table entries are never dereferenced.  K and V rows are stored with a
+// 16-byte-chunk XOR swizzle (LDS rows are 256 B, no padding) so the MFMA operand reads
+// are bank-conflict free.  The relative-bias slice of every unit (63 + n_q distances per
+// head) is staged the same way.  Per unit, each computing wave (32 query rows) does
+// S^T = K Q^T on MFMA, bias + mask, an online softmax and O^T += V^T P^T.
 #include "device_common.hpp"
 #include "launch.hpp"
+
+#include <type_traits>
 
 namespace rattn {
 namespace {
 
-constexpr int kThreads = 256;   // 4 waves
-constexpr int kBlock = 128;     // tokens per cache block
-constexpr int kKStride = 136;   // bf16 per K row in LDS
-constexpr int kVStride = 160;   // bf16 per V row in LDS
+constexpr int kThreads = 256;  // 4 waves
+constexpr int kUnit = kDecodeUnit;  // 64 tokens per unit / pipeline stage
+constexpr int kStages = 4;
+constexpr int kKVBytes = kUnit * kHeadDim * 2;           // 16 KB of K (or V) per stage
+constexpr int kBiasBytes = kDecodeBiasFloats * 4;        // 4 KB of bias per stage
+constexpr int kStageBytes = 2 * kKVBytes + kBiasBytes;   // 36 KB
 constexpr float kRescaleSlack = 8.0f;
 
-struct SeqRange {
-  int ctx, Weff, blk_lo, blk_hi, vis_lo;
+// 256 bytes of zeros: the source of every invisible K/V row.
+__device__ __attribute__((aligned(256))) const uint32_t kZeroRow[64] = {0};
+
+struct SeqInfo {
+  int ctx;     // keys in the cache (clamped into [1, 128 * max_blocks_per_seq])
+  int weff;    // window, or a huge value for full attention
+  int vis_lo;  // first key any query of the sequence can see
+  int clo;     // first unit (64-token chunk index) of the visible range
+  int nch;     // units of the visible range
 };
 
-__device__ __forceinline__ SeqRange seq_range(const DecodeParams& p, int b) {
-  SeqRange r;
-  r.ctx = p.ctx_lens[b];
-  const int W = p.windows ? p.windows[b] : 0;
-  r.Weff = W > 0 ? W : 0x40000000;
-  r.vis_lo = W > 0 ? max(0, r.ctx - p.n_q - W + 1) : 0;
-  r.blk_lo = r.vis_lo / kBlock;
-  // never index past the sequence's block-table row or the planned splits, whatever
-  // ctx_lens holds
-  r.blk_hi = min(min((r.ctx - 1) / kBlock + 1, p.mbps), p.S * p.SB);
-  return r;
+// Wave-uniform 32-bit load through the scalar cache (lgkmcnt), so that it does not wait
+// behind the LDS-bound loads in flight.
+__device__ __forceinline__ int uniform_load_i32(const int* ptr) {
+  // readfirstlane returns a signed int: widen each half as unsigned
+  const uint64_t a = (uint64_t)(uintptr_t)ptr;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const uint64_t ua = ((uint64_t)hi << 32) | (uint64_t)lo;
+  int v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=&s"(v) : "s"(ua) : "memory");
+  return v;
 }
 
-__device__ __forceinline__ u32x4_t ld16(const void* p) { return *(const u32x4_t*)p; }
+__device__ __forceinline__ SeqInfo seq_info(const DecodeParams& p, int b) {
+  SeqInfo s;
+  s.ctx = min(max(p.ctx_lens[b], 1), p.mbps * 128);
+  const int W = p.windows ? p.windows[b] : 0;
+  s.weff = W > 0 ? W : 0x40000000;
+  s.vis_lo = W > 0 ? max(0, s.ctx - p.n_q - W + 1) : 0;
+  s.clo = s.vis_lo / kUnit;
+  s.nch = (s.ctx - 1) / kUnit + 1 - s.clo;
+  return s;
+}
 
+// Exclusive prefix of visible units over the sequences, pre[0..B], computed by the whole
+// workgroup into LDS.  Returns pre[B].
+__device__ int batch_prefix(const DecodeParams& p, int* pre, int* scratch) {
+  const int tid = threadIdx.x;
+  const int per = (p.B + kThreads - 1) / kThreads;
+  int local = 0;
+  for (int i = 0; i < per; ++i) {
+    const int b = tid * per + i;
+    if (b < p.B) local += seq_info(p, b).nch;
+  }
+  scratch[tid] = local;
+  __syncthreads();
+  for (int off = 1; off < kThreads; off <<= 1) {
+    const int v = tid >= off ? scratch[tid - off] : 0;
+    __syncthreads();
+    scratch[tid] += v;
+    __syncthreads();
+  }
+  int run = scratch[tid] - local;
+  for (int i = 0; i < per; ++i) {
+    const int b = tid * per + i;
+    if (b < p.B) {
+      pre[b] = run;
+      run += seq_info(p, b).nch;
+    }
+  }
+  if (tid == kThreads - 1) pre[p.B] = scratch[tid];
+  __syncthreads();
+  return pre[p.B];
+}
+
+// Position in the unit stream: sequence, segment within the sequence, absolute chunk.
+struct Cursor {
+  int b, kh, c;
+  SeqInfo si;
+};
+
+__device__ __forceinline__ Cursor cursor_at(const DecodeParams& p, const int* pre, int u) {
+  // last b with pre[b] * KH <= u
+  int lo = 0, hi = p.B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (pre[mid] * p.KH <= u) lo = mid;
+    else hi = mid - 1;
+  }
+  Cursor c;
+  c.b = lo;
+  c.si = seq_info(p, lo);
+  const int r = u - pre[lo] * p.KH;
+  c.kh = r / c.si.nch;
+  c.c = c.si.clo + (r - c.kh * c.si.nch);
+  return c;
+}
+
+__device__ __forceinline__ void cursor_next(const DecodeParams& p, Cursor& c) {
+  if (++c.c == c.si.clo + c.si.nch) {
+    if (++c.kh == p.KH) {
+      c.kh = 0;
+      if (c.b + 1 < p.B) {
+        ++c.b;
+        c.si = seq_info(p, c.b);
+      }
+    }
+    c.c = c.si.clo;
+  }
+}
+
+// V^T operand (32 d-rows x 16 keys) from a swizzled V stage: LDS row = key, 256 B, the
+// 16-byte chunk k of row r stored at chunk k ^ (2 (r & 7)).  Same lane/key order as
+// load_vt_operand.
+__device__ __forceinline__ u32x4_t load_vt_swz(const unsigned char* v_stage, int kbase, int dcol0, int lane) {
+  const int m = lane & 15;
+  const int hf = lane >> 5;
+  const int row = kbase + 4 * hf + (m >> 2);
+  const int col = dcol0 + 16 * ((lane >> 4) & 1) + 4 * (m & 3);
+  const int off = (((col >> 3) ^ ((row & 7) << 1)) << 4) + ((col & 7) << 1);
+  const s16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(v_stage + row * 256 + off));
+  const s16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(v_stage + (row + 8) * 256 + off));
+  const u32x2_t ua = __builtin_bit_cast(u32x2_t, a);
+  const u32x2_t ub = __builtin_bit_cast(u32x2_t, b);
+  return u32x4_t{ua[0], ua[1], ub[0], ub[1]};
+}
+
+// KS: waves sharing the keys of a unit (2: one 32-key half each; 1: a wave takes both).
+// NB: bias loads per wave and unit (64 floats each), NB * 256 >= gs * SL.
+template <int KS, int NB>
 __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[kBlock * kKStride];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[kBlock * kVStride];
-  __shared__ __attribute__((aligned(16))) float b_lds[kDecodeBiasFloats];
+  constexpr int KB = 2 / KS;  // 32-key blocks per computing wave and unit
+  constexpr int kLoadsPerStage = 8 + NB;
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[kStages * kStageBytes];
+  __shared__ int pre[kDecodeMaxBatch + 1];
+  __shared__ int scratch[kThreads];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31;
   const int hf = lane >> 5;
 
-  // ---- job --------------------------------------------------------------------------
-  const int s = (int)blockIdx.x % p.S;
-  const int rest = (int)blockIdx.x / p.S;
-  const int hs = rest % p.n_hs;
-  const int hk = (rest / p.n_hs) % p.Hkv;
-  const int b = rest / (p.n_hs * p.Hkv);
+  const int units = batch_prefix(p, pre, scratch) * p.KH;
+  const int P = min(p.P, units);
+  const int w = blockIdx.x;
+  if (w >= P) return;  // uniform
+  const int u0 = (int)((long long)w * units / P);
+  const int n_units = (int)((long long)(w + 1) * units / P) - u0;
 
-  const SeqRange sr = seq_range(p, b);
-  const int blk_begin = max(s * p.SB, sr.blk_lo);
-  const int blk_end = min((s + 1) * p.SB, sr.blk_hi);
-  if (blk_begin >= blk_end) return;  // no visible key in this split (uniform exit)
-
-  const int p0 = sr.ctx - p.n_q;     // position of query 0
-  const int p_last = sr.ctx - 1;
-  const int SL = kBlock - 1 + p.n_q; // bias slice length per head and block
-
-  // ---- this lane's query row ---------------------------------------------------------
-  const int c = 32 * wave + col;
-  const bool wave_active = 32 * wave < p.rows;
-  const bool row_ok = c < p.rows;
-  const int tq = row_ok ? c / p.gs : 0;
-  const int gi = row_ok ? c % p.gs : 0;
-  const int h = hk * p.G + hs * p.gs + gi;
-  u32x4_t qr[8];
-  {
-    const size_t qbase = (((size_t)b * p.n_q + tq) * p.Hq + h) * kHeadDim;
+  // ---- loads of one unit into a stage -------------------------------------------------
+  // K/V: wave `wave` issues tokens 16 wave .. 16 wave + 15 of the 64-token unit, four
+  // tokens (1 KB) per instruction; lane i of instruction m fetches 16-byte chunk
+  // (i & 15) ^ swz(tok) of token tok = 4 m + i / 16, which lands at LDS chunk i & 15.
+  // Per-lane byte offsets are fixed; a unit only adds its block base.
+  uint32_t koff[4], voff[4], kz[4], vz[4];
+  int ktok[4];
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) qr[ks] = row_ok ? ld16(p.q + qbase + 16 * ks + 8 * hf) : zero_u32x4();
+  for (int i = 0; i < 4; ++i) {
+    const int tok = 16 * wave + 4 * i + (lane >> 4);
+    const int slot = lane & 15;
+    const int ck = slot ^ (tok & 15);
+    const int cv = slot ^ ((tok & 7) << 1);
+    ktok[i] = tok;
+    koff[i] = (uint32_t)(tok * p.Hkv) * 256u + ck * 16;
+    voff[i] = (uint32_t)(tok * p.Hkv) * 256u + cv * 16;
+    kz[i] = ck * 16;
+    vz[i] = cv * 16;
   }
-  const float bias_sat = p.bias[(size_t)h * p.R + (p.R - 1)] * kLog2e;
+  // Bias: NB * 256 floats per stage; entry g * SL + x = r[h_g, clamp(d0 + x, 0, R - 1)].
+  int bias_g[NB], bias_x[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int idx = 64 * (NB * wave + i) + lane;
+    bias_g[i] = idx / p.SL;
+    bias_x[i] = idx - bias_g[i] * p.SL;
+  }
+  const unsigned char* kc_bytes = (const unsigned char*)p.k_cache;
+  const unsigned char* vc_bytes = (const unsigned char*)p.v_cache;
+  const unsigned char* zero_bytes = (const unsigned char*)kZeroRow;
+  const uint32_t ring_base = lds_addr(ring);
 
-  // ---- block loads (gather through the block table, zero-fill invisible slots) --------
-  u32x4_t kreg[8], vreg[8];
-  float breg[(kDecodeBiasFloats + kThreads - 1) / kThreads];
-  const int* bt_row = p.block_table + (size_t)b * p.mbps;
-  auto issue_block = [&](int blk) {
-    // ids outside [0, num_blocks) are clamped so a bad table entry cannot address memory
-    // beyond the caches
-    const int phys = min(max(bt_row[blk], 0), p.num_blocks - 1);
-    const int r0 = tid >> 4, chunk = tid & 15;
+  auto issue_unit = [&](const Cursor& ic, int st) {
+    const int kvh = ic.kh / p.n_hs;
+    const int hs = ic.kh - kvh * p.n_hs;
+    const int j0 = ic.c * kUnit;
+    int phys = uniform_load_i32(p.block_table + (size_t)ic.b * p.mbps + (ic.c >> 1));
+    phys = min(max(phys, 0), p.num_blocks - 1);
+    const size_t base = (((size_t)phys * 128 + (ic.c & 1) * kUnit) * p.Hkv + kvh) * 256;
+    const unsigned char* kb_ = kc_bytes + base;
+    const unsigned char* vb_ = vc_bytes + base;
+    const uint32_t kdst = ring_base + st * kStageBytes + wave * 4096;
+    const uint32_t vdst = kdst + kKVBytes;
+    const uint32_t bdst = ring_base + st * kStageBytes + 2 * kKVBytes + wave * (NB * 256);
+    const bool interior = j0 >= ic.si.vis_lo && j0 + kUnit <= ic.si.ctx;
 #pragma unroll
-    for (int cc = 0; cc < 8; ++cc) {
-      const int row = r0 + 16 * cc;
-      const int j = blk * kBlock + row;
-      if (j >= sr.vis_lo && j < sr.ctx) {
-        const size_t a = (((size_t)phys * kBlock + row) * p.Hkv + hk) * kHeadDim + chunk * 8;
-        kreg[cc] = ld16(p.k_cache + a);
-        vreg[cc] = ld16(p.v_cache + a);
-      } else {
-        kreg[cc] = zero_u32x4();
-        vreg[cc] = zero_u32x4();
+    for (int i = 0; i < 4; ++i) {
+      const unsigned char* gk = kb_ + koff[i];
+      const unsigned char* gv = vb_ + voff[i];
+      if (!interior) {
+        const int j = j0 + ktok[i];
+        const bool vis = j >= ic.si.vis_lo && j < ic.si.ctx;
+        gk = vis ? gk : zero_bytes + kz[i];
+        gv = vis ? gv : zero_bytes + vz[i];
       }
+      dma16(gk, kdst + i * 1024);
+      dma16(gv, vdst + i * 1024);
     }
-    const int j0 = blk * kBlock;
-    if (p0 - (j0 + kBlock - 1) < p.R - 1) {  // block not entirely beyond R - 1: stage slices
-      const int d0 = p0 - j0 - (kBlock - 1);
+    const int p0 = ic.si.ctx - p.n_q;
+    const bool saturated = p0 - (j0 + kUnit - 1) >= p.R - 1;
+    const int d0 = p0 - j0 - (kUnit - 1);
+    const int hbase = kvh * p.G + hs * p.gs;
 #pragma unroll
-      for (int i = 0; i < (kDecodeBiasFloats + kThreads - 1) / kThreads; ++i) {
-        const int idx = tid + kThreads * i;
-        float val = 0.f;
-        if (idx < p.gs * SL) {
-          const int g = idx / SL, x = idx % SL;
-          const int d = min(max(d0 + x, 0), p.R - 1);
-          val = p.bias[(size_t)(hk * p.G + hs * p.gs + g) * p.R + d] * kLog2e;
-        }
-        breg[i] = val;
+    for (int i = 0; i < NB; ++i) {
+      const float* src = p.bias;
+      if (!saturated && bias_g[i] < p.gs) {
+        const int d = min(max(d0 + bias_x[i], 0), p.R - 1);
+        src = p.bias + (size_t)(hbase + bias_g[i]) * p.R + d;
       }
-    }
-  };
-  auto store_block = [&](int blk) {
-    const int r0 = tid >> 4, chunk = tid & 15;
-#pragma unroll
-    for (int cc = 0; cc < 8; ++cc) {
-      *(u32x4_t*)&k_lds[(r0 + 16 * cc) * kKStride + chunk * 8] = kreg[cc];
-      *(u32x4_t*)&v_lds[(r0 + 16 * cc) * kVStride + chunk * 8] = vreg[cc];
-    }
-    const int j0 = blk * kBlock;
-    if (p0 - (j0 + kBlock - 1) < p.R - 1) {
-#pragma unroll
-      for (int i = 0; i < (kDecodeBiasFloats + kThreads - 1) / kThreads; ++i) {
-        const int idx = tid + kThreads * i;
-        if (idx < p.gs * SL) b_lds[idx] = breg[i];
-      }
+      dma4(src, bdst + i * 256);
     }
   };
 
-  // ---- running state ---------------------------------------------------------------
+  // ---- this wave's role: row block rb (32 rows) and key half ks of every unit ----------
+  // With at most two row blocks the two 32-key halves of a unit go to different waves,
+  // which keep separate online-softmax states (separate pieces for the merge kernel).
+  const int n_rb = (p.rows + 31) / 32;
+  const int rb_span = KS == 2 ? n_rb : 4;
+  const int rb = wave % rb_span;
+  const int ks_w = wave / rb_span;
+  const bool wave_active = rb < n_rb && ks_w < KS;
+  const int kb_lo = KS == 2 ? ks_w : 0;
+  const int r_row = 32 * rb + col;
+  const bool row_ok = r_row < p.rows;
+  const int tq = row_ok ? r_row / p.gs : 0;
+  const int gq = row_ok ? r_row - tq * p.gs : 0;
+  // bias entry of key kk for this lane: bs[bias_lane + 59 - (kk - 4 hf - 32 kb_lo)]
+  const int bias_lane = gq * p.SL + tq + 4 - 4 * hf - 32 * kb_lo;
+
   f32x16_t o[4];
-#pragma unroll
-  for (int db = 0; db < 4; ++db) o[db] = zero_f32x16();
-  float m_run = kNegInf;
-  float l_run = 0.f;
+  u32x4_t qr[8];
+  float m_run = kNegInf, l_run = 0.f, bias_sat = 0.f;
 
-  auto compute_block = [&](int blk) {
+  auto begin_segment = [&](const Cursor& cc) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db) o[db] = zero_f32x16();
+    m_run = kNegInf;
+    l_run = 0.f;
     if (!wave_active) return;
-    const int j0 = blk * kBlock;
-    const bool saturated = p0 - (j0 + kBlock - 1) >= p.R - 1;
-    const bool need_mask = (j0 + kBlock - 1 > p0) || (j0 < p_last - sr.Weff + 1);
+    const int kvh = cc.kh / p.n_hs;
+    const int hs = cc.kh - kvh * p.n_hs;
+    const int h = kvh * p.G + hs * p.gs + gq;
+    const size_t qbase = (((size_t)cc.b * p.n_q + tq) * p.Hq + h) * kHeadDim;
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {  // two halves of 64 keys
-      f32x16_t sacc[2];
+    for (int ks = 0; ks < 8; ++ks)
+      qr[ks] = row_ok ? *(const u32x4_t*)(p.q + qbase + 16 * ks + 8 * hf) : zero_u32x4();
+    bias_sat = p.bias[(size_t)h * p.R + (p.R - 1)] * kLog2e;
+    // take the loaded values through an opaque definition here, so the compiler's wait for
+    // them sits at this point and not in front of the first MFMA, behind later LDS loads
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        sacc[kb] = zero_f32x16();
-        const uint16_t* krow = &k_lds[(64 * kh + 32 * kb + col) * kKStride + 8 * hf];
+    for (int ks = 0; ks < 8; ++ks) asm volatile("" : "+v"(qr[ks]));
+    asm volatile("" : "+v"(bias_sat));
+  };
+
+  auto flush_segment = [&](int seg) {
+    if (!wave_active) return;
+    const float l_tot = half_swap_sum(l_run);
+    if (!row_ok) return;
+    const size_t slot_row = ((size_t)(w + seg) * KS + ks_w) * p.rows + r_row;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    float* dst = p.ws_o + slot_row * kHeadDim;
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) sacc[kb] = mfma_32x32x16(*(const u32x4_t*)(krow + 16 * ks), qr[ks], sacc[kb]);
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int d = 32 * db + 8 * q + 4 * hf;
+        *(f32x4_t*)(dst + d) = f32x4_t{o[db][4 * q] * inv, o[db][4 * q + 1] * inv, o[db][4 * q + 2] * inv,
+                                       o[db][4 * q + 3] * inv};
       }
-      float t[2][16];
+    if (hf == 0) p.ws_lse[slot_row] = l_tot > 0.f ? m_run + __log2f(l_tot) : kNegInf;
+  };
+
+  // logits of this wave's 32-key blocks (log2 units) into t; returns the row maximum
+  auto logits = [&](auto sat_c, auto mask_c, const f32x16_t* sacc, const float* bs_lds, float (*t)[16],
+                    int dl, int weff) {
+    constexpr bool SAT = decltype(sat_c)::value;
+    constexpr bool MASK = decltype(mask_c)::value;
+    float mx = kNegInf;
+    float bb[KB][16];
+    if constexpr (!SAT) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int i = 0; i < KB; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kk = 64 * kh + 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);  // key offset in block
-          const float bv = saturated ? bias_sat : b_lds[gi * SL + (tq + kBlock - 1 - kk)];
-          t[kb][r] = sacc[kb][r] * p.scale_log2 + bv;
+        for (int r = 0; r < 16; ++r) bb[i][r] = bs_lds[bias_lane + 59 - (32 * i + 8 * (r >> 2) + (r & 3))];
+    }
+#pragma unroll
+    for (int i = 0; i < KB; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float x;
+        if constexpr (SAT) x = fmaf(sacc[i][r], p.scale_log2, bias_sat);
+        else x = fmaf(bb[i][r], kLog2e, sacc[i][r] * p.scale_log2);
+        if constexpr (MASK) {
+          // distance of this key from the lane's query; visible iff 0 <= d < weff
+          const int d = dl - (32 * i + 8 * (r >> 2) + (r & 3));
+          x = (uint32_t)d < (uint32_t)weff ? x : kNegInf;
         }
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int kk = 64 * kh + 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
-            const int d = p0 + tq - j0 - kk;
-            t[kb][r] = (d >= 0 && d < sr.Weff) ? t[kb][r] : kNegInf;
-          }
+        t[i][r] = x;
+        mx = fmaxf(mx, x);
       }
-      float mx = t[0][0];
+    return mx;
+  };
+
+  auto compute_unit = [&](const Cursor& cc, int st) {
+    if (!wave_active) return;
+    const unsigned char* ks_lds = ring + st * kStageBytes;
+    const unsigned char* vs_lds = ks_lds + kKVBytes;
+    const float* bs_lds = (const float*)(vs_lds + kKVBytes);
+    const int j0 = cc.c * kUnit;
+    const int p0 = cc.si.ctx - p.n_q;  // position of query 0
+    const bool saturated = p0 - (j0 + kUnit - 1) >= p.R - 1;
+    const bool need_mask = (j0 + kUnit - 1 > p0) || (j0 < cc.si.ctx - cc.si.weff);
+
+    // every LDS operand of this wave's 32-key blocks first, so their latency overlaps
+    u32x4_t ka[KB][8];
+    u32x4_t va[KB][4][2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int i = 0; i < KB; ++i) {
+      const int krow = 32 * (kb_lo + i) + col;
+      const unsigned char* kr = ks_lds + krow * 256;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, t[kb][r]);
-      mx = half_swap_max(mx);
-      const bool raise = mx > m_run + kRescaleSlack;
-      if (__builtin_amdgcn_ballot_w64(raise)) {
-        const float alpha = raise ? fast_exp2(m_run - mx) : 1.f;
-        m_run = raise ? mx : m_run;
-        l_run *= alpha;
+      for (int k8 = 0; k8 < 8; ++k8) ka[i][k8] = *(const u32x4_t*)(kr + (((2 * k8 + hf) ^ (krow & 15)) << 4));
+    }
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-      }
-      const float msub = (m_run == kNegInf) ? 0.f : m_run;
-      float lsum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          t[kb][r] = fast_exp2(t[kb][r] - msub);
-          lsum += t[kb][r];
-        }
-      l_run += lsum;
-      u32x4_t pk[2][2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int half = 0; half < 2; ++half) pk[kb][half] = pack_p_operand(&t[kb][8 * half]);
+    for (int i = 0; i < KB; ++i)
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int half = 0; half < 2; ++half)
+          va[i][db][half] = load_vt_swz(vs_lds, 32 * (kb_lo + i) + 16 * half, 32 * db, lane);
+    // S^T = K Q^T
+    f32x16_t sacc[KB];
 #pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            const u32x4_t a = load_vt_operand(v_lds, kVStride, 64 * kh + 32 * kb + 16 * half, 32 * db, lane);
-            o[db] = mfma_32x32x16(a, pk[kb][half], o[db]);
-          }
+    for (int i = 0; i < KB; ++i) {
+      sacc[i] = zero_f32x16();
+#pragma unroll
+      for (int k8 = 0; k8 < 8; ++k8) sacc[i] = mfma_32x32x16(ka[i][k8], qr[k8], sacc[i]);
     }
+    float t[KB][16];
+    const int dl = p0 + tq - j0 - 4 * hf - 32 * kb_lo;  // distance of this lane's first key
+    const int weff = cc.si.weff;
+    float mx;
+    if (saturated) {
+      mx = need_mask ? logits(std::true_type{}, std::true_type{}, sacc, bs_lds, t, dl, weff)
+                     : logits(std::true_type{}, std::false_type{}, sacc, bs_lds, t, dl, weff);
+    } else {
+      mx = need_mask ? logits(std::false_type{}, std::true_type{}, sacc, bs_lds, t, dl, weff)
+                     : logits(std::false_type{}, std::false_type{}, sacc, bs_lds, t, dl, weff);
+    }
+    // online softmax, maximum raised lazily
+    mx = half_swap_max(mx);
+    const bool raise = mx > m_run + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(raise)) {
+      const float alpha = raise ? fast_exp2(m_run - mx) : 1.f;
+      m_run = raise ? mx : m_run;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+    }
+    const float msub = (m_run == kNegInf) ? 0.f : m_run;
+    float lsum = 0.f;
+    u32x4_t pk[KB][2];
+#pragma unroll
+    for (int i = 0; i < KB; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        t[i][r] = fast_exp2(t[i][r] - msub);
+        lsum += t[i][r];
+      }
+#pragma unroll
+      for (int half = 0; half < 2; ++half) pk[i][half] = pack_p_operand(&t[i][8 * half]);
+    }
+    l_run += lsum;
+    // O^T += V^T P^T
+#pragma unroll
+    for (int i = 0; i < KB; ++i)
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) o[db] = mfma_32x32x16(va[i][db][half], pk[i][half], o[db]);
   };
 
-  // ---- block loop ------------------------------------------------------------------
-  issue_block(blk_begin);
-  store_block(blk_begin);
-  __syncthreads();
-  for (int blk = blk_begin; blk < blk_end; ++blk) {
-    const bool has_next = blk + 1 < blk_end;
-    if (has_next) issue_block(blk + 1);
-    compute_block(blk);
-    __syncthreads();
-    if (has_next) {
-      store_block(blk + 1);
-      __syncthreads();
-    }
+  // ---- main loop: unit t computed from stage t % 4 while units t+1..t+3 load ------------
+  Cursor cc = cursor_at(p, pre, u0);
+  Cursor ic = cc;
+  begin_segment(cc);  // before any LDS load is in flight
+  const int prologue = min(kStages - 1, n_units);
+  for (int i = 0; i < prologue; ++i) {
+    issue_unit(ic, i);
+    cursor_next(p, ic);
   }
-
-  // ---- partial result of this split ------------------------------------------------
-  const float l_tot = half_swap_sum(l_run);
-  if (!row_ok) return;
-  const size_t row_id = ((size_t)b * p.n_q + tq) * p.Hq + h;
-  const size_t slot = row_id * p.S + s;
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  float* dst = p.ws_o + slot * kHeadDim;
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int d = 32 * db + 8 * q + 4 * hf;
-      *(f32x4_t*)(dst + d) = f32x4_t{o[db][4 * q] * inv, o[db][4 * q + 1] * inv, o[db][4 * q + 2] * inv,
-                                     o[db][4 * q + 3] * inv};
+  int seg = cc.b * p.KH + cc.kh;
+  for (int t = 0; t < n_units; ++t) {
+    const int ahead = min(kStages - 2, n_units - 1 - t);  // units issued after this one
+    if (ahead >= 2) vm_wait<2 * kLoadsPerStage>();
+    else if (ahead == 1) vm_wait<kLoadsPerStage>();
+    else vm_wait<0>();
+    wg_barrier();  // unit t is in LDS; every wave is done with unit t - 1
+    if (t + kStages - 1 < n_units) {
+      issue_unit(ic, (t + kStages - 1) % kStages);
+      cursor_next(p, ic);
     }
-  if (hf == 0) p.ws_lse[slot] = l_tot > 0.f ? m_run + __log2f(l_tot) : kNegInf;
+    const int cseg = cc.b * p.KH + cc.kh;
+    if (cseg != seg) {
+      flush_segment(seg);
+      begin_segment(cc);
+      seg = cseg;
+    }
+    compute_unit(cc, t % kStages);
+    cursor_next(p, cc);
+  }
+  flush_segment(seg);
 }
 
-// One workgroup per query row: merge the partial results of its sequence's splits.
+// One workgroup per (segment, row): merge the pieces of the segment.
 __global__ __launch_bounds__(kThreads) void decode_merge_kernel(DecodeParams p) {
   __shared__ float red[kThreads];
+  __shared__ int ired[2][kThreads];
   __shared__ f32x4_t acc_lds[8][32];
   const int tid = threadIdx.x;
-  const size_t row_id = blockIdx.x;
-  const int b = (int)(row_id / ((size_t)p.n_q * p.Hq));
-  const SeqRange sr = seq_range(p, b);
-  const int s_lo = sr.blk_lo / p.SB;
-  const int s_hi = (sr.blk_hi - 1) / p.SB + 1;
-  const float* lse_s = p.ws_lse + row_id * p.S;
+  const int seg = blockIdx.x / p.rows;
+  const int r_row = blockIdx.x - seg * p.rows;
+  const int b = seg / p.KH;
+  const int kh = seg - b * p.KH;
+
+  // units before sequence b, and in total
+  int before = 0, total = 0;
+  for (int bb = tid; bb < p.B; bb += kThreads) {
+    const int n = seq_info(p, bb).nch;
+    total += n;
+    if (bb < b) before += n;
+  }
+  ired[0][tid] = before;
+  ired[1][tid] = total;
+  __syncthreads();
+  for (int s = kThreads / 2; s > 0; s >>= 1) {
+    if (tid < s) {
+      ired[0][tid] += ired[0][tid + s];
+      ired[1][tid] += ired[1][tid + s];
+    }
+    __syncthreads();
+  }
+  const long long units = (long long)ired[1][0] * p.KH;
+  const long long P = min((long long)p.P, units);
+  const int nch = seq_info(p, b).nch;
+  const long long us = (long long)ired[0][0] * p.KH + (long long)kh * nch;
+  const long long ue = us + nch;
+  // workgroup w covers units [w units / P, (w + 1) units / P)
+  const int w_first = (int)(((us + 1) * P + units - 1) / units) - 1;
+  const int w_last = (int)((ue * P + units - 1) / units) - 1;
+  // piece i = (workgroup w_first + i / KS, key half i % KS)
+  const int n_pieces = (w_last - w_first + 1) * p.KS;
+  auto slot_row = [&](int i) {
+    return ((size_t)(w_first + i / p.KS + seg) * p.KS + (i % p.KS)) * p.rows + r_row;
+  };
 
   float m = kNegInf;
-  for (int s = s_lo + tid; s < s_hi; s += kThreads) m = fmaxf(m, lse_s[s]);
+  for (int i = tid; i < n_pieces; i += kThreads) m = fmaxf(m, p.ws_lse[slot_row(i)]);
   red[tid] = m;
   __syncthreads();
-  for (int w = kThreads / 2; w > 0; w >>= 1) {
-    if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
+  for (int s = kThreads / 2; s > 0; s >>= 1) {
+    if (tid < s) red[tid] = fmaxf(red[tid], red[tid + s]);
     __syncthreads();
   }
   const float M = red[0];
   __syncthreads();
   float z = 0.f;
-  for (int s = s_lo + tid; s < s_hi; s += kThreads) z += fast_exp2(lse_s[s] - M);
+  for (int i = tid; i < n_pieces; i += kThreads) z += fast_exp2(p.ws_lse[slot_row(i)] - M);
   red[tid] = z;
   __syncthreads();
-  for (int w = kThreads / 2; w > 0; w >>= 1) {
-    if (tid < w) red[tid] += red[tid + w];
+  for (int s = kThreads / 2; s > 0; s >>= 1) {
+    if (tid < s) red[tid] += red[tid + s];
     __syncthreads();
   }
   const float Z = red[0];
 
   const int d4 = tid & 31, grp = tid >> 5;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s = s_lo + grp; s < s_hi; s += 8) {
-    const float w = fast_exp2(lse_s[s] - M);
-    const f32x4_t x = *(const f32x4_t*)(p.ws_o + (row_id * p.S + s) * kHeadDim + 4 * d4);
-    acc += w * x;
+  for (int i = grp; i < n_pieces; i += 8) {
+    const size_t sr = slot_row(i);
+    const float wgt = fast_exp2(p.ws_lse[sr] - M);
+    const f32x4_t x = *(const f32x4_t*)(p.ws_o + sr * kHeadDim + 4 * d4);
+    acc += wgt * x;
   }
   acc_lds[grp][d4] = acc;
   __syncthreads();
+  const int kvh = kh / p.n_hs;
+  const int hs = kh - kvh * p.n_hs;
+  const int tq = r_row / p.gs;
+  const int h = kvh * p.G + hs * p.gs + (r_row - tq * p.gs);
+  const size_t out_row = ((size_t)b * p.n_q + tq) * p.Hq + h;
   if (grp == 0) {
     f32x4_t tot = acc_lds[0][d4];
 #pragma unroll
     for (int g = 1; g < 8; ++g) tot += acc_lds[g][d4];
     const float inv = 1.f / Z;
-    *(u32x2_t*)(p.out + row_id * kHeadDim + 4 * d4) =
+    *(u32x2_t*)(p.out + out_row * kHeadDim + 4 * d4) =
         u32x2_t{pack_bf16x2(tot[0] * inv, tot[1] * inv), pack_bf16x2(tot[2] * inv, tot[3] * inv)};
   }
-  if (tid == 0 && p.lse != nullptr) p.lse[row_id] = (M + __log2f(Z)) * kLn2;
+  if (tid == 0 && p.lse != nullptr) p.lse[out_row] = (M + __log2f(Z)) * kLn2;
 }
 
 }  // namespace
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
-  const long long grid1 = (long long)p.B * p.Hkv * p.n_hs * p.S;
-  const long long grid2 = (long long)p.B * p.n_q * p.Hq;
-  if (grid1 <= 0) return hipSuccess;
-  if (grid1 > 0x7fffffffLL || grid2 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(decode_split_kernel, dim3((unsigned)grid1), dim3(kThreads), 0, stream, p);
+  const long long grid2 = (long long)p.B * p.KH * p.rows;
+  if (p.B <= 0) return hipSuccess;
+  if (grid2 > 0x7fffffffLL || p.P < 1) return hipErrorInvalidConfiguration;
+  const int nb = (p.gs * p.SL + 255) / 256;  // bias loads per wave and unit
+  if (nb < 1 || nb > 4 || (p.KS != 1 && p.KS != 2)) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)p.P), block(kThreads);
+#define RATTN_SPLIT(KS_, NB_) hipLaunchKernelGGL((decode_split_kernel<KS_, NB_>), grid, block, 0, stream, p)
+  if (p.KS == 2) {
+    switch (nb) {
+      case 1: RATTN_SPLIT(2, 1); break;
+      case 2: RATTN_SPLIT(2, 2); break;
+      case 3: RATTN_SPLIT(2, 3); break;
+      default: RATTN_SPLIT(2, 4); break;
+    }
+  } else {
+    switch (nb) {
+      case 1: RATTN_SPLIT(1, 1); break;
+      case 2: RATTN_SPLIT(1, 2); break;
+      case 3: RATTN_SPLIT(1, 3); break;
+      default: RATTN_SPLIT(1, 4); break;
+    }
+  }
+#undef RATTN_SPLIT
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_merge_kernel, dim3((unsigned)grid2), dim3(kThreads), 0, stream, p);

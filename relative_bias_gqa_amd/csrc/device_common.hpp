@@ -97,6 +97,60 @@ __device__ __forceinline__ u32x4_t pack_p_operand(const float* p8) {
   return r;
 }
 
+// ---- direct global -> LDS loads (global_load_lds_dword{,x4}) --------------------------
+// Lane i of the issuing wave writes its 4 (or 16) bytes at LDS byte address
+// M0 + 4 i (or 16 i); lanes that are switched off write nothing.  The loads are issued
+// from inline assembly so that the compiler does not pair every later LDS read with a
+// wait for all of them; the caller orders them explicitly with vm_wait<n>() (they count
+// in vmcnt like any vector-memory load) and a workgroup barrier.  M0 is saved and restored
+// around each load, and one wait state separates the M0 write from the load.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_byte_addr) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_byte_addr);
+  uint32_t save;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "v"(g), "s"(m0v)
+      : "memory");
+}
+
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds_byte_addr) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_byte_addr);
+  uint32_t save;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "v"(g), "s"(m0v)
+      : "memory");
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier that is also a compiler fence for memory operations.  The wave's own
+// LDS accesses complete first (lgkmcnt 0); outstanding global loads are not waited for.
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ u32x4_t zero_u32x4() {
   u32x4_t z;
   z[0] = z[1] = z[2] = z[3] = 0u;

@@ -27,7 +27,10 @@ struct PrefillParams {
 hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream);
 hipError_t launch_prefill_fp32(const PrefillParams& p, hipStream_t stream);
 
-// Paged split-KV decode (sizes validated, split plan fixed by the host).
+// Paged decode (sizes validated by the host).  The visible keys of every (sequence, KV
+// head, query-head subgroup) "segment" are cut into 64-token units; the concatenated unit
+// stream of the whole batch is divided evenly among P workgroups, each of which writes
+// one partial result per segment it touches (slot = workgroup + segment).
 struct DecodeParams {
   const uint16_t* q;
   const uint16_t* k_cache;
@@ -38,23 +41,27 @@ struct DecodeParams {
   const float* bias;
   uint16_t* out;
   float* lse;
-  float* ws_o;    // [B, n_q, Hq, S, 128] partial outputs (normalised per split)
-  float* ws_lse;  // [B, n_q, Hq, S] partial log2-sum-exp
+  float* ws_o;    // [P + B * KH, KS, rows, 128] partial outputs (normalised per piece)
+  float* ws_lse;  // [P + B * KH, KS, rows] partial log2-sum-exp
   int B, n_q, Hq, Hkv, R, mbps;
   int num_blocks; // physical blocks in each cache
   int G;          // Hq / Hkv
-  int gs;         // query heads per workgroup
+  int gs;         // query heads per segment
   int n_hs;       // G / gs
-  int rows;       // n_q * gs query rows per workgroup
-  int S;          // splits per sequence
-  int SB;         // cache blocks per split
+  int KH;         // Hkv * n_hs segments per sequence
+  int rows;       // n_q * gs query rows per segment
+  int SL;         // bias entries per head staged for one unit: 63 + n_q
+  int KS;         // waves sharing a unit's keys (2 when rows <= 64, else 1)
+  int P;          // split workgroups
   float scale_log2;
 };
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 
 // Decode limits the host must respect.
-constexpr int kDecodeMaxRows = 128;       // n_q * gs
-constexpr int kDecodeBiasFloats = 1152;   // gs * (127 + n_q)
+constexpr int kDecodeMaxRows = 128;       // n_q * gs (four waves of 32 rows)
+constexpr int kDecodeBiasFloats = 1024;   // gs * (63 + n_q) per unit
+constexpr int kDecodeMaxBatch = 2048;     // sequences per launch (prefix table in LDS)
+constexpr int kDecodeUnit = 64;           // tokens per unit
 
 }  // namespace rattn

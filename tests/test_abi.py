@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.rattn_abi_version() == rb.ABI_VERSION == 1
+    assert lib.rattn_abi_version() == rb.ABI_VERSION == 2
 
 
 def _prefill(lib, **kw):
@@ -107,22 +107,26 @@ def test_decode_empty_is_noop(lib):
 
 
 def test_workspace_and_split_plan(lib):
-    # the workspace holds a partial output (128 fp32) and a log-sum-exp per row and split
-    for (B, n_q, Hq, Hkv, ctx, ns) in [(64, 1, 16, 2, 131072, 0), (1, 9, 16, 2, 1 << 20, 0), (3, 2, 8, 8, 1000, 5)]:
-        S = rb.rattn_decode_num_splits(B, n_q, Hq, Hkv, ctx, ns)
-        assert 1 <= S <= (ctx + 127) // 128
-        if ns:
-            assert S <= ns
+    # the KV stream of the batch is split among P workgroups (256 by default); the workspace
+    # holds a partial output (128 fp32) and a log-sum-exp per (workgroup + segment) slot, key
+    # half and row of a segment, a segment being (sequence, KV head, query-head subgroup)
+    for (B, n_q, Hq, Hkv, ctx, ns, gs) in [(64, 1, 16, 2, 131072, 0, 8), (1, 9, 16, 2, 1 << 20, 0, 8),
+                                           (3, 2, 8, 8, 1000, 5, 1), (2, 9, 32, 2, 4000, 7, 8),
+                                           (5, 100, 4, 1, 5000, 0, 1)]:
+        P = rb.rattn_decode_num_splits(B, n_q, Hq, Hkv, ctx, ns)
+        assert P == (ns if ns else 256)
+        G = Hq // Hkv
+        KH = Hkv * (G // gs)
+        rows = n_q * gs
+        KS = 2 if rows <= 64 else 1   # key halves of a unit on separate waves for small row counts
+        slots = (P + B * KH) * KS
         wsb = rb.rattn_decode_workspace_bytes(B, n_q, Hq, Hkv, ctx, ns)
-        rows = B * n_q * Hq
-        assert wsb >= rows * S * 129 * 4
-        assert wsb <= rows * S * 129 * 4 + 256
-    # more splits requested than blocks: capped at one block per split
-    assert rb.rattn_decode_num_splits(1, 1, 8, 1, 300, 100) == 3
+        assert slots * rows * 129 * 4 <= wsb <= slots * rows * 129 * 4 + 256
     assert rb.rattn_decode_workspace_bytes(1, 0, 8, 1, 300, 0) == 0
-    # automatic plan spreads the 1M-token verify over many splits (enough workgroups)
-    S5 = rb.rattn_decode_num_splits(1, 9, 16, 2, 1 << 20, 0)
-    assert S5 * 2 >= 256
+    assert rb.rattn_decode_num_splits(1, 129, 8, 1, 300, 0) == 0
+    # large batches run in launches of at most 2048 sequences sharing one workspace
+    big = rb.rattn_decode_workspace_bytes(5000, 1, 16, 2, 4096, 0)
+    assert big == rb.rattn_decode_workspace_bytes(2048, 1, 16, 2, 4096, 0)
 
 
 def test_binding_fails_loudly_without_library(tmp_path):

@@ -105,7 +105,9 @@ def test_decode_small(name, seed, ctx, windows, n_q, Hq, Hkv, R):
     print(f"case {name}", flush=True)
     case = synth.make_decode(seed, ctx, windows, n_q, Hq, Hkv, R)
     ref_o, ref_l, _ = oracle.ref_decode(case)
-    for ns in (0, 1, 3):
+    # the KV stream is split among 256 (default), 1, 3, 7 or 5000 workgroups; 5000 exceeds
+    # the number of 64-token units, so some workgroups get none
+    for ns in (0, 1, 3, 7, 5000):
         out, lse = run_decode(case, ns)
         compare(out, lse, ref_o, ref_l, f"{name} splits={ns}")
 
