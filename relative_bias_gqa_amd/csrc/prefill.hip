@@ -1,4 +1,5 @@
-// prefill.hip -- relative-bias GQA prefill / chunked prefill for gfx950.
+// prefill.hip -- relative-bias GQA prefill / chunked prefill for gfx950, fp32 inputs.
+// (bf16 inputs use prefill_bf16.hip.)
 //
 // Computes, for every query row (b, t, h) at absolute position p = Lk - Lq + t,
 //   out = softmax_j(q.k_j / sqrt(128) + r[h, min(p - j, R - 1)]) . V,  lse = log-sum-exp,
@@ -394,7 +395,6 @@ hipError_t launch(const PrefillParams& p, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream) { return launch<false>(p, stream); }
 hipError_t launch_prefill_fp32(const PrefillParams& p, hipStream_t stream) { return launch<true>(p, stream); }
 
 }  // namespace rattn
