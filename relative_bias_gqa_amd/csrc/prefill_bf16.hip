@@ -20,10 +20,10 @@
 //     workgroup's query heads (GQA packing: one K/V read per head group).  K/V rows are
 //     stored with a 16-byte-chunk XOR swizzle so the MFMA operand reads are conflict free;
 //   - each wave also loads its own 95-entry diagonal slice of r for the tile into the
-//     stage and scales it by log2(e) in place; a tile entirely beyond distance R - 1 uses
-//     one scalar instead;
-//   - per tile and wave: S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (Q resident in
-//     registers), logits in log2 units with the running maximum folded into the same FMA,
+//     stage, scales it by sqrt(128) in place and seeds its S accumulators with it, so the
+//     MFMA adds q.k onto the bias; a tile entirely beyond distance R - 1 seeds one scalar;
+//   - per tile and wave: S^T = sqrt(128) r + K Q^T on v_mfma_f32_32x32x16_bf16 (Q resident
+//     in registers), logits in log2 units with the running maximum in the same FMA,
 //     the causal / window mask only on edge tiles, an online softmax whose maximum is only
 //     raised when a row's maximum grows by more than 8 (log2 units), and O^T += V^T P^T
 //     with P rounded to bf16 and V read transposed from LDS (ds_read_b64_tr_b16).
@@ -45,6 +45,7 @@ constexpr int kBiasBytes = kWaves * kSliceFloats * 4;
 constexpr int kStageBytes = 2 * kKVBytes + kBiasBytes;  // 36 KB
 constexpr int kLoadsPerStage = 6;                 // per wave: 2 K + 2 V + 2 bias
 constexpr float kRescaleSlack = 8.0f;             // log2 units: P entries stay below 2^8
+constexpr float kSqrtD = 11.313708498984761f;     // sqrt(128)
 
 // 256 bytes of zeros: the source of every K/V row past the end of the sequence.
 __device__ __attribute__((aligned(256))) const uint32_t kZeroRowP[64] = {0};
@@ -110,11 +111,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
     for (int ks = 0; ks < 8; ++ks)
       qr[ks] = ok ? *(const u32x4_t*)((const uint16_t*)p.q + qbase + 16 * ks + 8 * hf) : zero_u32x4();
   }
-  const float bias_sat = p.bias[(size_t)h * p.R + (p.R - 1)] * kLog2e;
+  // bias in score units (multiplied by sqrt(128)), so that it can seed the S accumulator:
+  // (q.k + sqrt(128) r) * log2(e) / sqrt(128) = q.k * log2(e) / sqrt(128) + r * log2(e)
+  float bias_sat_v = p.bias[(size_t)h * p.R + (p.R - 1)] * kSqrtD;
   // pin the waits for these loads here, before any LDS-bound load is in flight
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) asm volatile("" : "+v"(qr[ks]));
-  float bias_sat_v = bias_sat;
   asm volatile("" : "+v"(bias_sat_v));
 
   // ---- tile loads -------------------------------------------------------------------
@@ -177,74 +179,81 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   // bias entry of key kk (0..63) for this lane's column: slice[63 + col - kk]
   const int bias_lane = col - 4 * hf + 4;  // slice[bias_lane + 59 - (kk - 4 hf)]
 
-  auto compute_tile = [&](int kt, int st) {
+  auto wave_sees = [&](int kt) {
     const int j0 = kt * kBK;
-    if (!wave_active || j0 > wkmax || j0 + kBK - 1 < wkmin) return;
-    const unsigned char* k_st = ring + st * kStageBytes;
-    const unsigned char* v_st = k_st + kKVBytes;
-    float* b_st = (float*)(k_st + 2 * kKVBytes + wave * (kSliceFloats * 4));
-    const bool need_mask = (j0 + kBK - 1 > pw0) || (j0 < pw_last - Weff + 1);
-    const bool saturated = pw0 - (j0 + kBK - 1) >= p.R - 1;
+    return wave_active && j0 <= wkmax && j0 + kBK - 1 >= wkmin;
+  };
 
-    // S^T = K Q^T : two 32-key blocks
-    f32x16_t s[2];
+  // S^T = sqrt(128) r + K Q^T for the two 32-key blocks of tile kt (stage st): the
+  // accumulators start from this wave's bias slice (or the saturated scalar)
+  auto score_tile = [&](int kt, int st, f32x16_t* s) {
+    const int j0 = kt * kBK;
+    const unsigned char* k_st = ring + st * kStageBytes;
+    float* b_st = (float*)(k_st + 2 * kKVBytes + wave * (kSliceFloats * 4));
+    if (pw0 - (j0 + kBK - 1) >= p.R - 1) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] = bias_sat_v;
+    } else {
+      // scale the slice to score units in place (only this wave reads it)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) b_st[64 * i + lane] *= kSqrtD;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] = b_st[bias_lane + 59 - (32 * kb + 8 * (r >> 2) + (r & 3))];
+    }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int krow = 32 * kb + col;
       const unsigned char* kr = k_st + krow * 256;
-      u32x4_t ka[8];
 #pragma unroll
-      for (int k8 = 0; k8 < 8; ++k8) ka[k8] = *(const u32x4_t*)(kr + (((2 * k8 + hf) ^ (krow & 15)) << 4));
-      s[kb] = zero_f32x16();
+      for (int g = 0; g < 2; ++g) {
+        u32x4_t ka[4];
 #pragma unroll
-      for (int k8 = 0; k8 < 8; ++k8) s[kb] = mfma_32x32x16(ka[k8], qr[k8], s[kb]);
+        for (int i = 0; i < 4; ++i) {
+          ka[i] = *(const u32x4_t*)(kr + (((2 * (4 * g + i) + hf) ^ (krow & 15)) << 4));
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          s[kb] = mfma_32x32x16(ka[i], qr[4 * g + i], s[kb]);
+        }
+      }
     }
+  };
+
+  // mask and online softmax of tile kt from its scores: P as bf16
+  auto softmax = [&](int kt, f32x16_t* s, u32x4_t (*pk)[2]) {
+    const int j0 = kt * kBK;
+    const bool need_mask = (j0 + kBK - 1 > pw0) || (j0 < pw_last - Weff + 1);
 
     // logits relative to the running maximum, in log2 units
     const bool fresh = m_run == kNegInf;
     const float m_ref = fresh ? 0.f : m_run;
-    float t[2][16];
-    float mx = kNegInf;
-    auto logits = [&](auto sat_c, auto mask_c) {
-      constexpr bool SAT = decltype(sat_c)::value;
-      constexpr bool MASK = decltype(mask_c)::value;
-      float bb[2][16];
-      if constexpr (!SAT) {
+    f32x16_t* t = s;  // the logits overwrite the scores
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) bb[kb][r] = b_st[bias_lane + 59 - (32 * kb + 8 * (r >> 2) + (r & 3))];
-      }
-      const float csat = bias_sat_v - m_ref;
+      for (int r = 0; r < 16; ++r) t[kb][r] = fmaf(s[kb][r], p.scale_log2, -m_ref);
+    if (need_mask) {
       const int dl = pw0 + col - j0 - 4 * hf;  // distance of this lane's first key
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float x;
-          if constexpr (SAT) x = fmaf(s[kb][r], p.scale_log2, csat);
-          else x = fmaf(s[kb][r], p.scale_log2, bb[kb][r]) - m_ref;
-          if constexpr (MASK) {
-            const int d = dl - (32 * kb + 8 * (r >> 2) + (r & 3));
-            x = (uint32_t)d < (uint32_t)Weff ? x : kNegInf;
-          }
-          t[kb][r] = x;
+          const int d = dl - (32 * kb + 8 * (r >> 2) + (r & 3));
+          t[kb][r] = (uint32_t)d < (uint32_t)Weff ? t[kb][r] : kNegInf;
         }
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(t[kb][r], t[kb][r + 1]));
-    };
-    if (saturated) {
-      if (need_mask) logits(std::true_type{}, std::true_type{});
-      else logits(std::true_type{}, std::false_type{});
-    } else {
-      // scale this wave's slice by log2(e) in place (it is read only by this wave)
-#pragma unroll
-      for (int i = 0; i < 2; ++i) b_st[64 * i + lane] *= kLog2e;
-      if (need_mask) logits(std::false_type{}, std::true_type{});
-      else logits(std::false_type{}, std::false_type{});
     }
+    // row maximum: a tree of three-input maxima over the 32 values, then the lane pair
+    float m8[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int kb = i >> 2, r = (i & 3) * 4;
+      m8[i] = fmaxf(fmaxf(t[kb][r], t[kb][r + 1]), fmaxf(t[kb][r + 2], t[kb][r + 3]));
+    }
+    float mx = fmaxf(fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3])), fmaxf(fmaxf(m8[4], m8[5]), fmaxf(m8[6], m8[7])));
     mx = half_swap_max(mx);
 
     // raise the running maximum when a row's new maximum exceeds it by the slack
@@ -267,7 +276,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
 
     // P = exp2(t); the normaliser sums it in fp32 (the log-sum-exp needs that accuracy),
     // the P.V product takes it rounded to bf16
-    u32x4_t pk[2][2];
     float lsum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -284,21 +292,28 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
         pk[kb][half] = w;
       }
     l_run += lsum;
+  };
 
-    // O^T += V^T P^T
+  // O^T += V^T P^T for tile kt (stage st)
+  auto pv = [&](int st, const u32x4_t (*pk)[2]) {
+    const unsigned char* v_st = ring + st * kStageBytes + kKVBytes;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         u32x4_t va[4];
 #pragma unroll
-        for (int db = 0; db < 4; ++db) va[db] = vt_operand(v_st, 32 * kb + 16 * half, 32 * db, lane);
+        for (int db = 0; db < 4; ++db) {
+          va[db] = vt_operand(v_st, 32 * kb + 16 * half, 32 * db, lane);
+        }
 #pragma unroll
         for (int db = 0; db < 4; ++db) o[db] = mfma_32x32x16(va[db], pk[kb][half], o[db]);
       }
   };
 
   // ---- key loop: tile t computed from stage t % 4 while tiles t+1..t+3 load -------------
+  f32x16_t s_cur[2];
+  u32x4_t pk[2][2];
   const int prologue = min(kStages - 1, n_tiles);
   for (int i = 0; i < prologue; ++i) issue_tile(kt_begin + i, i);
   for (int t = 0; t < n_tiles; ++t) {
@@ -308,7 +323,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
     else vm_wait<0>();
     wg_barrier();  // tile t is in LDS; every wave is done with tile t - 1
     if (t + kStages - 1 < n_tiles) issue_tile(kt_begin + t + kStages - 1, (t + kStages - 1) % kStages);
-    compute_tile(kt_begin + t, t % kStages);
+    if (wave_sees(kt_begin + t)) {
+      score_tile(kt_begin + t, t % kStages, s_cur);
+      softmax(kt_begin + t, s_cur, pk);
+      pv(t % kStages, pk);
+    }
   }
 
   // ---- epilogue --------------------------------------------------------------------
