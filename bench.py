@@ -38,8 +38,8 @@ HEADLINE = "swa_prefill_8k"
 ALL_WORKLOADS = ["tiny_prefill_fp32", "swa_prefill_8k", "chunked_prefill_32k", "paged_decode_b64", "mtp_verify_1m"]
 HEAD_DIM = 128
 KERNEL_SOURCES = {
-    "prefill": ["relative_bias_gqa_amd/csrc/prefill.hip", "relative_bias_gqa_amd/csrc/device_common.hpp",
-                "relative_bias_gqa_amd/csrc/launch.hpp"],
+    "prefill": ["relative_bias_gqa_amd/csrc/prefill.hip", "relative_bias_gqa_amd/csrc/prefill_bf16.hip",
+                "relative_bias_gqa_amd/csrc/device_common.hpp", "relative_bias_gqa_amd/csrc/launch.hpp"],
     "decode": ["relative_bias_gqa_amd/csrc/decode.hip", "relative_bias_gqa_amd/csrc/device_common.hpp",
                "relative_bias_gqa_amd/csrc/launch.hpp"],
 }
@@ -232,7 +232,7 @@ def main(argv=None) -> int:
                     help="comma-separated workloads to time besides the headline")
     ap.add_argument("--only-headline", action="store_true", help="time only the headline workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-stride", type=int, default=4, help="oracle sample: every n-th query row")
+    ap.add_argument("--cpu-stride", type=int, default=1, help="oracle sample: every n-th query row")
     ap.add_argument("--only", default=None,
                     help="time just this workload and print its own result line (for profiler runs)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
