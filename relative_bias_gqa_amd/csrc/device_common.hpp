@@ -57,6 +57,24 @@ __device__ __forceinline__ float half_swap_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
+// Maxima on v_max3_f32 / v_max_f32 directly: the operands here are results of FMAs or
+// -inf, never signalling NaNs, so the quieting that fmaxf adds in IEEE mode is not needed.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float max2f(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+// max(x, y) over this lane and lane l ^ 32
+__device__ __forceinline__ float half_swap_max3(float x, float y) {
+  const float m = max2f(x, y);
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return max2f(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 __device__ __forceinline__ float half_swap_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
@@ -147,6 +165,16 @@ __device__ __forceinline__ void vm_wait() {
 // LDS accesses complete first (lgkmcnt 0); outstanding global loads are not waited for.
 __device__ __forceinline__ void wg_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Workgroup barrier that leaves the wave's own LDS reads in flight: for loops whose LDS
+// reads all complete before their results are used (the compiler waits for them there),
+// so that a wave never reaches a barrier that precedes a refill of the data it reads
+// with such a read still pending.  Global -> LDS loads are ordered separately (vm_wait).
+__device__ __forceinline__ void wg_barrier_reads_in_flight() {
+  asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }

@@ -16,17 +16,21 @@
 //   - it walks 64-key tiles from the first key any of its rows can see to the last, so
 //     tiles before the window or after the diagonal are never loaded;
 //   - K and V tiles go from global memory straight into LDS (global_load_lds_dwordx4) in a
-//     ring of four stages, three tiles ahead of the one computed, and serve all of the
-//     workgroup's query heads (GQA packing: one K/V read per head group).  K/V rows are
-//     stored with a 16-byte-chunk XOR swizzle so the MFMA operand reads are conflict free;
-//   - each wave also loads its own 95-entry diagonal slice of r for the tile into the
-//     stage, scales it by sqrt(128) in place and seeds its S accumulators with it, so the
-//     MFMA adds q.k onto the bias; a tile entirely beyond distance R - 1 seeds one scalar;
-//   - per tile and wave: S^T = sqrt(128) r + K Q^T on v_mfma_f32_32x32x16_bf16 (Q resident
-//     in registers), logits in log2 units with the running maximum in the same FMA,
-//     the causal / window mask only on edge tiles, an online softmax whose maximum is only
-//     raised when a row's maximum grows by more than 8 (log2 units), and O^T += V^T P^T
-//     with P rounded to bf16 and V read transposed from LDS (ds_read_b64_tr_b16).
+//     ring of four stages, two tiles ahead, and serve all of the workgroup's query heads
+//     (GQA packing: one K/V read per head group).  K/V rows carry a 16-byte-chunk XOR
+//     swizzle so the MFMA operand reads are conflict free, and every operand address is
+//     one register XORed with a constant;
+//   - each wave also loads its own diagonal slice of r for the tile (distances clamped to
+//     R - 1) into the stage and seeds its S accumulators with it, scaled by sqrt(128), so
+//     the MFMA adds q.k onto the bias;
+//   - the two halves of the workgroup (one wave of each on every SIMD) run in ping-pong,
+//     half a tile apart: while one wave of a SIMD runs its MFMA half-step (O^T += V^T P^T
+//     of the previous tile, then S^T = sqrt(128) r + K Q^T on v_mfma_f32_32x32x16_bf16,
+//     Q resident in registers), the other runs its softmax half-step on the vector ALU:
+//     logits in log2 units with the running maximum in the same FMA, the causal / window
+//     mask only on edge tiles, an online softmax whose maximum is only raised when a row's
+//     maximum grows by more than 8 (log2 units), P rounded to bf16, and the next tile's
+//     bias seeds.  V is read transposed from LDS (ds_read_b64_tr_b16).
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -50,20 +54,16 @@ constexpr float kSqrtD = 11.313708498984761f;     // sqrt(128)
 // 256 bytes of zeros: the source of every K/V row past the end of the sequence.
 __device__ __attribute__((aligned(256))) const uint32_t kZeroRowP[64] = {0};
 
-// V^T operand (32 d-rows x 16 keys) from a swizzled V tile: LDS row = key, 256 B, the
-// 16-byte chunk c of row r stored at chunk c ^ (2 (r & 7)).  Lane half hf supplies keys
-// kbase + 4 hf + 0..3 and kbase + 8 + 4 hf + 0..3, the register order of the S^T block.
-__device__ __forceinline__ u32x4_t vt_operand(const unsigned char* v_stage, int kbase, int dcol0, int lane) {
-  const int m = lane & 15;
-  const int hf = lane >> 5;
-  const int row = kbase + 4 * hf + (m >> 2);
-  const int col = dcol0 + 16 * ((lane >> 4) & 1) + 4 * (m & 3);
-  const int off = (((col >> 3) ^ ((row & 7) << 1)) << 4) + ((col & 7) << 1);
-  const s16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(v_stage + row * 256 + off));
-  const s16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(v_stage + (row + 8) * 256 + off));
-  const u32x2_t ua = __builtin_bit_cast(u32x2_t, a);
-  const u32x2_t ub = __builtin_bit_cast(u32x2_t, b);
-  return u32x4_t{ua[0], ua[1], ub[0], ub[1]};
+// LDS accesses through plain 32-bit byte addresses, so that the per-lane part of every
+// operand address is one register and the rest is an immediate offset or an XOR with a
+// constant (see the swizzles below).
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
+typedef __attribute__((address_space(3))) float lds_f32_t;
+__device__ __forceinline__ u32x4_t lds_ld16(uint32_t a) { return *(const lds_u32x4_t*)(size_t)a; }
+__device__ __forceinline__ float lds_ldf(uint32_t a) { return *(const lds_f32_t*)(size_t)a; }
+__device__ __forceinline__ void lds_stf(uint32_t a, float v) { *(lds_f32_t*)(size_t)a = v; }
+__device__ __forceinline__ u32x2_t lds_tr8(uint32_t a) {
+  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(size_t)a));
 }
 
 __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams p) {
@@ -98,8 +98,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   const int kt_begin = max(0, off + T0 - Weff + 1) / kBK;
   const int kt_end = (off + T1 - 1) / kBK + 1;
   const int n_tiles = kt_end - kt_begin;
-  const int wkmin = max(0, pw0 - Weff + 1);
-  const int wkmax = pw_last;
 
   // ---- Q^T operand, resident for the whole key loop -------------------------------
   u32x4_t qr[8];
@@ -111,13 +109,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
     for (int ks = 0; ks < 8; ++ks)
       qr[ks] = ok ? *(const u32x4_t*)((const uint16_t*)p.q + qbase + 16 * ks + 8 * hf) : zero_u32x4();
   }
-  // bias in score units (multiplied by sqrt(128)), so that it can seed the S accumulator:
-  // (q.k + sqrt(128) r) * log2(e) / sqrt(128) = q.k * log2(e) / sqrt(128) + r * log2(e)
-  float bias_sat_v = p.bias[(size_t)h * p.R + (p.R - 1)] * kSqrtD;
   // pin the waits for these loads here, before any LDS-bound load is in flight
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) asm volatile("" : "+v"(qr[ks]));
-  asm volatile("" : "+v"(bias_sat_v));
 
   // ---- tile loads -------------------------------------------------------------------
   // K/V: wave w issues keys 8 w .. 8 w + 7 of the tile, four keys (1 KB) per instruction;
@@ -160,14 +154,35 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
       dma16(gk, kdst + i * 1024);
       dma16(gv, vdst + i * 1024);
     }
-    // this wave's bias slice: entry x = r[h, clamp(pw0 - j0 - 63 + x, 0, R - 1)]
-    const int d0 = pw0 - j0 - (kBK - 1);
+    // this wave's bias slice, stored by decreasing distance:
+    // entry y = r[h, clamp(pw0 - j0 + 31 - y, 0, R - 1)]
+    const int d0 = pw0 - j0 + 31;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int d = min(max(d0 + 64 * i + lane, 0), p.R - 1);
+      const int d = min(max(d0 - 64 * i - lane, 0), p.R - 1);
       dma4(bias_row + d, bdst + i * 256);
     }
   };
+
+  // ---- per-lane LDS operand addresses (stage 0) ----------------------------------------
+  // K tile rows are 256 B with 16-byte chunk c of key j stored at chunk c ^ (j & 15).  The
+  // A operand of k-step i (key row 32 kb + col, chunk 2 i + hf) then sits at byte
+  //   row base + ((32 i) ^ L),  L = 32 ((col & 15) >> 1) + 16 (hf ^ (col & 1)),
+  // i.e. at kx0 ^ (32 i) (+ 8192 for kb = 1), the row base being 256-byte aligned.
+  const uint32_t kx0 = ring_base + col * 256 + 32 * ((col & 15) >> 1) + 16 * (hf ^ (col & 1));
+  // V tile rows are 256 B with chunk c of key j at chunk c ^ (2 (j & 7)).  Lane (m = lane
+  // & 15, u = bit 4, hf) of the transposed read for d block db, keys kbase.. reads key row
+  // kbase + 4 hf + (m >> 2) (and 8 rows on) at column 32 db + 16 u + 4 (m & 3): with
+  // Y = (2 u + ((m & 3) >> 1)) ^ (2 (row & 7)) that is vz0 ^ (64 db) + 256 kbase.
+  uint32_t vz0;
+  {
+    const int m = lane & 15, u = (lane >> 4) & 1;
+    const int vrow = 4 * hf + (m >> 2);
+    const int y = (2 * u + ((m & 3) >> 1)) ^ (2 * (vrow & 7));
+    vz0 = ring_base + kKVBytes + vrow * 256 + 16 * y + 8 * (m & 1);
+  }
+  // this wave's bias slice: seeds at sb0 + 4 (32 kb + 8 (r >> 2) + (r & 3))
+  const uint32_t sb0 = ring_base + 2 * kKVBytes + wave * (kSliceFloats * 4) + 4 * (31 - col + 4 * hf);
 
   // ---- running state ---------------------------------------------------------------
   f32x16_t o[4];
@@ -175,88 +190,115 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   for (int db = 0; db < 4; ++db) o[db] = zero_f32x16();
   float m_run = kNegInf;  // running max (log2 units), identical in both lane halves
   float l_run = 0.f;      // this lane's share of the running normaliser
+  f32x16_t s[2];          // S^T of the tile in flight (two 32-key blocks)
+  u32x4_t pk[2][2];       // its P^T as bf16 MFMA operands
 
-  // bias entry of key kk (0..63) for this lane's column: slice[63 + col - kk]
-  const int bias_lane = col - 4 * hf + 4;  // slice[bias_lane + 59 - (kk - 4 hf)]
-
-  auto wave_sees = [&](int kt) {
-    const int j0 = kt * kBK;
-    return wave_active && j0 <= wkmax && j0 + kBK - 1 >= wkmin;
-  };
-
-  // S^T = sqrt(128) r + K Q^T for the two 32-key blocks of tile kt (stage st): the
-  // accumulators start from this wave's bias slice (or the saturated scalar)
-  auto score_tile = [&](int kt, int st, f32x16_t* s) {
-    const int j0 = kt * kBK;
-    const unsigned char* k_st = ring + st * kStageBytes;
-    float* b_st = (float*)(k_st + 2 * kKVBytes + wave * (kSliceFloats * 4));
-    if (pw0 - (j0 + kBK - 1) >= p.R - 1) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][r] = bias_sat_v;
-    } else {
-      // scale the slice to score units in place (only this wave reads it)
-#pragma unroll
-      for (int i = 0; i < 2; ++i) b_st[64 * i + lane] *= kSqrtD;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][r] = b_st[bias_lane + 59 - (32 * kb + 8 * (r >> 2) + (r & 3))];
-    }
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int krow = 32 * kb + col;
-      const unsigned char* kr = k_st + krow * 256;
-#pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        u32x4_t ka[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          ka[i] = *(const u32x4_t*)(kr + (((2 * (4 * g + i) + hf) ^ (krow & 15)) << 4));
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          s[kb] = mfma_32x32x16(ka[i], qr[4 * g + i], s[kb]);
-        }
-      }
-    }
-  };
-
-  // mask and online softmax of tile kt from its scores: P as bf16
-  auto softmax = [&](int kt, f32x16_t* s, u32x4_t (*pk)[2]) {
-    const int j0 = kt * kBK;
-    const bool need_mask = (j0 + kBK - 1 > pw0) || (j0 < pw_last - Weff + 1);
-
-    // logits relative to the running maximum, in log2 units
-    const bool fresh = m_run == kNegInf;
-    const float m_ref = fresh ? 0.f : m_run;
-    f32x16_t* t = s;  // the logits overwrite the scores
+  // The S accumulators of the tile in stage st start from the wave's bias slice (scaled
+  // to score units in the MFMA half-step).  Distances beyond R - 1 are clamped in the
+  // slice, so a tile entirely past them is seeded with r[h, R - 1] like any other.
+  auto load_seeds = [&](int st) {
+    // one base register per call, the rest immediate offsets (kept from being hoisted
+    // out of the loop as 32 separate addresses)
+    uint32_t base = sb0 + st * kStageBytes;
+    asm volatile("" : "+v"(base));
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) t[kb][r] = fmaf(s[kb][r], p.scale_log2, -m_ref);
-    if (need_mask) {
-      const int dl = pw0 + col - j0 - 4 * hf;  // distance of this lane's first key
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int d = dl - (32 * kb + 8 * (r >> 2) + (r & 3));
-          t[kb][r] = (uint32_t)d < (uint32_t)Weff ? t[kb][r] : kNegInf;
-        }
-    }
-    // row maximum: a tree of three-input maxima over the 32 values, then the lane pair
-    float m8[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int kb = i >> 2, r = (i & 3) * 4;
-      m8[i] = fmaxf(fmaxf(t[kb][r], t[kb][r + 1]), fmaxf(t[kb][r + 2], t[kb][r + 3]));
-    }
-    float mx = fmaxf(fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3])), fmaxf(fmaxf(m8[4], m8[5]), fmaxf(m8[6], m8[7])));
-    mx = half_swap_max(mx);
+      for (int r = 0; r < 16; ++r) s[kb][r] = lds_ldf(base + 4 * (32 * kb + 8 * (r >> 2) + (r & 3)));
+  };
 
-    // raise the running maximum when a row's new maximum exceeds it by the slack
+  // MFMA half-step: O^T += V^T P^T for the previous tile (stage st_prev), then
+  // S^T = sqrt(128) r + K Q^T for the tile in stage st on the seeded accumulators.  The
+  // 32 MFMAs run as eight groups of four (P.V keys 16 G.., then S k-steps in pairs); each
+  // group's operands are read from LDS two groups ahead, and the seeds are scaled to score
+  // units while the P.V groups run.
+  auto mfma_half = [&](int st, int st_prev) {
+    const uint32_t so = st * kStageBytes;
+    const uint32_t kx = kx0 + so;
+    const uint32_t vz = vz0 + st_prev * kStageBytes;
+    // operands of group gi: P.V (gi < 4) keys 16 gi.., or S k-steps 2 (gi - 4) and
+    // 2 (gi - 4) + 1 of both key blocks
+    auto load = [&](int gi, u32x4_t* op) {
+      if (gi < 4) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const uint32_t a = (vz ^ (64u * db)) + 256u * (16 * gi);
+          const u32x2_t lo = lds_tr8(a), hi = lds_tr8(a + 2048u);
+          op[db] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+        }
+      } else {
+        // k-steps 2 (gi - 4) and 2 (gi - 4) + 1 of both key blocks
+#pragma unroll
+        for (int i = 0; i < 4; ++i) op[i] = lds_ld16((kx ^ (32u * (2 * (gi - 4) + (i >> 1)))) + 8192u * (i & 1));
+      }
+    };
+    u32x4_t op[3][4];
+    load(0, op[0]);
+    load(1, op[1]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int gi = 0; gi < 8; ++gi) {
+      if (gi + 2 < 8) load(gi + 2, op[(gi + 2) % 3]);
+      const u32x4_t* cur = op[gi % 3];
+      if (gi < 4) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db) o[db] = mfma_32x32x16(cur[db], pk[gi >> 1][gi & 1], o[db]);
+        if (gi == 2) s[0] *= kSqrtD;
+        if (gi == 3) s[1] *= kSqrtD;
+      } else {
+        // alternate the two key blocks so that consecutive MFMAs are independent
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[i & 1] = mfma_32x32x16(cur[i], qr[2 * (gi - 4) + (i >> 1)], s[i & 1]);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // keep the reads two groups ahead
+    }
+  };
+
+  // Softmax half-step of tile kt: logits in log2 units relative to the running maximum
+  // (the bias and the max in one FMA), the causal / window mask on edge tiles, the row
+  // maximum, a lazy raise of the running maximum (only when a row's maximum grows by
+  // more than the slack, rescaling O and the normaliser), then P = exp2 in fp32 for the
+  // normaliser (the log-sum-exp needs that accuracy) and rounded to bf16 for P.V.
+  auto softmax_half = [&](int kt) {
+    const int j0 = kt * kBK;
+    const bool fresh = m_run == kNegInf;
+    const float m_ref = fresh ? 0.f : m_run;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = fmaf(s[kb][r], p.scale_log2, -m_ref);
+    const bool causal = j0 + kBK - 1 > pw0;
+    const bool window = j0 < pw_last - Weff + 1;
+    if (causal || window) {
+      // the distance of key 32 kb + 8 (r >> 2) + 4 hf + (r & 3) from this lane's query
+      // is dl - c(kb, r)
+      const int dl = pw0 + col - j0 - 4 * hf;
+      if (!window) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int c = 32 * kb + 8 * (r >> 2) + (r & 3);
+            s[kb][r] = c <= dl ? s[kb][r] : kNegInf;
+          }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int c = 32 * kb + 8 * (r >> 2) + (r & 3);
+            s[kb][r] = (uint32_t)(dl - c) < (uint32_t)Weff ? s[kb][r] : kNegInf;
+          }
+      }
+    }
+    float ma = max3f(s[0][0], s[0][1], s[0][2]);
+    float mb = max3f(s[1][0], s[1][1], s[1][2]);
+#pragma unroll
+    for (int r = 3; r < 15; r += 2) {
+      ma = max3f(ma, s[0][r], s[0][r + 1]);
+      mb = max3f(mb, s[1][r], s[1][r + 1]);
+    }
+    const float mx = half_swap_max3(max3f(ma, mb, s[0][15]), s[1][15]);
     const bool raise = fresh ? (mx > kNegInf) : (mx > kRescaleSlack);
     if (__builtin_amdgcn_ballot_w64(raise)) {
       const float delta = raise ? mx : 0.f;
@@ -265,17 +307,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
       m_run = raise ? m_new : m_run;
       l_run *= alpha;
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) t[kb][r] -= delta;
+      for (int db = 0; db < 4; ++db) o[db] *= alpha;
+      s[0] -= delta;
+      s[1] -= delta;
     }
-
-    // P = exp2(t); the normaliser sums it in fp32 (the log-sum-exp needs that accuracy),
-    // the P.V product takes it rounded to bf16
     float lsum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -285,7 +320,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 8 * half + 2 * e;
-          const float e0 = fast_exp2(t[kb][r]), e1 = fast_exp2(t[kb][r + 1]);
+          const float e0 = fast_exp2(s[kb][r]), e1 = fast_exp2(s[kb][r + 1]);
           lsum += e0 + e1;
           w[e] = pack_bf16x2(e0, e1);
         }
@@ -294,39 +329,77 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
     l_run += lsum;
   };
 
-  // O^T += V^T P^T for tile kt (stage st)
-  auto pv = [&](int st, const u32x4_t (*pk)[2]) {
-    const unsigned char* v_st = ring + st * kStageBytes + kKVBytes;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        u32x4_t va[4];
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          va[db] = vt_operand(v_st, 32 * kb + 16 * half, 32 * db, lane);
-        }
-#pragma unroll
-        for (int db = 0; db < 4; ++db) o[db] = mfma_32x32x16(va[db], pk[kb][half], o[db]);
-      }
-  };
-
-  // ---- key loop: tile t computed from stage t % 4 while tiles t+1..t+3 load -------------
-  f32x16_t s_cur[2];
-  u32x4_t pk[2][2];
-  const int prologue = min(kStages - 1, n_tiles);
+  // ---- key loop: two wave groups in ping-pong -------------------------------------
+  // Waves 0-3 and 4-7 (one of each on every SIMD) run the same code: per tile t, an MFMA
+  // half-step (P.V of tile t - 1, then S of tile t) and a softmax half-step (tile t, then
+  // the seeds of tile t + 1), each after a workgroup barrier.  Group 1 passes one extra
+  // barrier first, so it runs one half-step behind: while one wave of a SIMD feeds the
+  // matrix cores, the other runs the softmax on the vector ALU and its LDS reads.
+  // Barrier k: group 0 starts its MFMA half of tile k / 2 after even k, group 1 after odd
+  // k.  Tile t + 1 must be whole in LDS at barrier 2 t + 1 (its seeds are read after it):
+  // group 0 waits for its share before its barrier after MFMA half t, group 1 before its
+  // barrier ahead of MFMA half t.  The stage of tile t - 2 (last read by group 1's P.V
+  // of it, before barrier 2 t) is refilled with tile t + 2 right after barrier 2 t: by
+  // group 0 after its barrier ahead of MFMA half t, by group 1 after its barrier ahead
+  // of softmax half t - 1.
+  const bool g1 = wave >= kWaves / 2;
+  const int prologue = min(g1 ? 3 : 2, n_tiles);
   for (int i = 0; i < prologue; ++i) issue_tile(kt_begin + i, i);
-  for (int t = 0; t < n_tiles; ++t) {
-    const int ahead = min(kStages - 2, n_tiles - 1 - t);  // tiles issued after this one
-    if (ahead >= 2) vm_wait<2 * kLoadsPerStage>();
-    else if (ahead == 1) vm_wait<kLoadsPerStage>();
+  // P of "tile -1" is zero and the V rows of the last stage are zeroed, so that the first
+  // MFMA half-step can run its P.V like every other (it adds nothing)
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int half = 0; half < 2; ++half) pk[kb][half] = zero_u32x4();
+  {
+    u32x4_t* vlast = (u32x4_t*)(ring + (kStages - 1) * kStageBytes + kKVBytes);
+    vlast[tid] = zero_u32x4();
+    vlast[tid + kThreads] = zero_u32x4();
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // before the first barrier
+  }
+  if (g1) {
+    if (n_tiles >= 3) vm_wait<2 * kLoadsPerStage>();  // tile 0
+    else if (n_tiles == 2) vm_wait<kLoadsPerStage>();
     else vm_wait<0>();
-    wg_barrier();  // tile t is in LDS; every wave is done with tile t - 1
-    if (t + kStages - 1 < n_tiles) issue_tile(kt_begin + t + kStages - 1, (t + kStages - 1) % kStages);
-    if (wave_sees(kt_begin + t)) {
-      score_tile(kt_begin + t, t % kStages, s_cur);
-      softmax(kt_begin + t, s_cur, pk);
-      pv(t % kStages, pk);
+    wg_barrier();
+    load_seeds(0);
+  } else {
+    if (n_tiles >= 2) vm_wait<kLoadsPerStage>();  // tile 0
+    else vm_wait<0>();
+  }
+  for (int t = 0; t < n_tiles; ++t) {
+    if (g1) {
+      if (t + 2 < n_tiles) vm_wait<kLoadsPerStage>();  // tile t + 1; t + 2 may still be loading
+      else vm_wait<0>();
+    }
+    wg_barrier_reads_in_flight();
+    if (!g1 && t + 2 < n_tiles) issue_tile(kt_begin + t + 2, (t + 2) % kStages);
+    if (!g1 && t == 0) load_seeds(0);
+    mfma_half(t % kStages, (t + kStages - 1) % kStages);
+    if (!g1) {
+      if (t + 2 < n_tiles) vm_wait<kLoadsPerStage>();  // tile t + 1; t + 2 may still be loading
+      else vm_wait<0>();
+    }
+    wg_barrier_reads_in_flight();
+    if (g1 && t + 3 < n_tiles) issue_tile(kt_begin + t + 3, (t + 3) % kStages);
+    softmax_half(kt_begin + t);
+    load_seeds((t + 1) % kStages);  // (unused after the last tile)
+  }
+  if (!g1) wg_barrier();
+  if (n_tiles > 0) {
+    // P.V of the last tile
+    const uint32_t vz = vz0 + ((n_tiles - 1) % kStages) * kStageBytes;
+#pragma unroll
+    for (int G = 0; G < 4; ++G) {
+      u32x4_t va[4];
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const uint32_t a = (vz ^ (64u * db)) + 256u * (16 * G);
+        const u32x2_t lo = lds_tr8(a), hi = lds_tr8(a + 2048u);
+        va[db] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+      }
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[db] = mfma_32x32x16(va[db], pk[G >> 1][G & 1], o[db]);
     }
   }
 
