@@ -128,9 +128,16 @@ class PrefillRun:
                        "kv_heads": c.Hkv, "head_dim": HEAD_DIM, "window": c.window, "bias_len": c.R,
                        "dtype": c.dtype}
         self.dtype = "bf16" if c.dtype == "bf16" else "f32"
+        # the library's key-range split plan, with its (zero-filled) workspace allocated here,
+        # outside the timed region
+        nbytes = rb.rattn_prefill_workspace_bytes(c.B, c.Lq, c.Lk, c.Hq, c.Hkv, c.window,
+                                                  rb.RATTN_BF16 if c.dtype == "bf16" else rb.RATTN_FP32)
+        self.ws = torch.zeros(nbytes, dtype=torch.uint8, device=self.q.device) if nbytes else None
+        self.config["kv_split_workspace_bytes"] = nbytes
 
     def step(self, stream):
-        self.rb.rattn_prefill(self.q, self.k, self.v, self.bias, self.out, self.lse, self.case.window, stream)
+        self.rb.rattn_prefill(self.q, self.k, self.v, self.bias, self.out, self.lse, self.case.window, 0, self.ws,
+                              stream)
 
     def rate(self, seconds):
         return self.work / seconds / 1e12
@@ -140,7 +147,7 @@ class PrefillRun:
         return bool(torch.isfinite(self.out.float()).all()) and bool(torch.isfinite(self.lse).all())
 
     def free(self):
-        del self.q, self.k, self.v, self.bias, self.out, self.lse
+        del self.q, self.k, self.v, self.bias, self.out, self.lse, self.ws
 
 
 class DecodeRun:

@@ -39,17 +39,32 @@
 extern "C" {
 #endif
 
-#define RATTN_ABI_VERSION 2
+#define RATTN_ABI_VERSION 3
 
 enum rattn_status {
   RATTN_OK = 0,
   RATTN_ERR_INVALID_ARG = 1, /* null pointer, inconsistent sizes */
   RATTN_ERR_UNSUPPORTED = 2, /* head_dim != 128, block_size != 128, dtype not handled */
-  RATTN_ERR_WORKSPACE = 3,   /* decode workspace missing or too small */
+  RATTN_ERR_WORKSPACE = 3,   /* workspace missing or too small */
   RATTN_ERR_HIP = 4          /* a HIP launch failed; message holds hipGetErrorString */
 };
 
 enum rattn_dtype { RATTN_BF16 = 0, RATTN_FP32 = 1 };
+
+/*
+ * Device workspace, in bytes, that rattn_prefill needs to split the key range of its
+ * heaviest query tiles (0: these arguments never split; then rattn_prefill may be given
+ * no workspace).  kv_splits as for rattn_prefill.  The plan is a pure function of the
+ * arguments.  Returns 0 for invalid sizes.
+ *
+ * Why a split: the query tiles of a long sliding-window (or long causal) prefill all walk
+ * about as many keys as the longest one, and with about two tiles per compute unit the
+ * last ones to start finish late.  Splitting the keys of the heaviest tiles into pieces
+ * that merge by log-sum-exp evens the work out (the key-range split the decode path uses
+ * for every sequence, applied to prefill tiles).
+ */
+size_t rattn_prefill_workspace_bytes(int B, int Lq, int Lk, int Hq, int Hkv, int window, int dtype,
+                                     int kv_splits);
 
 /*
  * Prefill / chunked prefill over contiguous K/V.
@@ -60,19 +75,32 @@ enum rattn_dtype { RATTN_BF16 = 0, RATTN_FP32 = 1 };
  *   bias [Hq, R]            fp32     device, read   (r above; R >= 1)
  *   out  [B, Lq, Hq, 128]   dtype    device, written
  *   lse  [B, Lq, Hq]        fp32     device, written; may be NULL
+ *   workspace               device scratch of workspace_bytes >=
+ *                           rattn_prefill_workspace_bytes(...) bytes, or NULL with
+ *                           workspace_bytes = 0 (then nothing is split)
  *
  * Query t of every sequence sits at absolute position Lk - Lq + t (bottom-right alignment:
  * a chunk of Lq new tokens whose own keys are the last Lq of the Lk keys), so Lq <= Lk.
  * window <= 0 selects full causal attention; window > 0 a sliding window of that many keys.
  * dtype RATTN_BF16: bf16 in/out.  RATTN_FP32: fp32 in/out; q.k is formed without rounding
- * the inputs to bf16 (three-term bf16 split), likewise p.v.
+ * the inputs to bf16 (three-term bf16 split), likewise p.v (never key-split).
+ * kv_splits: 0 = the library's plan (a split only where it shortens the launch), 1 = no
+ * split, n in 2..8 = split every query tile with at least 2n key tiles of 64 into n pieces.
+ * A split changes only the summation order of the result.
+ * Workspace: its first bytes hold per-tile counters that must be zero when the workspace
+ * is first used; every completed call leaves them zero again, so a workspace zero-filled
+ * once can be reused by later calls of any size it is large enough for.  Calls that share
+ * a workspace must not run concurrently.
  * B == 0 or Lq == 0 is a no-op returning RATTN_OK (pointers may then be NULL).
  * Status: INVALID_ARG for a null required pointer, negative sizes, Hq % Hkv != 0, Lq > Lk,
- * R < 1; UNSUPPORTED for head_dim != 128 or an unknown dtype; HIP if the launch fails.
+ * R < 1, kv_splits outside 0..8, workspace_bytes > 0 with a NULL workspace; WORKSPACE if
+ * workspace_bytes is below rattn_prefill_workspace_bytes(...); UNSUPPORTED for head_dim !=
+ * 128 or an unknown dtype; HIP if the launch fails.
  */
 int rattn_prefill(const void* q, const void* k, const void* v, const float* bias, void* out,
                   float* lse, int B, int Lq, int Lk, int Hq, int Hkv, int head_dim, int R,
-                  int window, int dtype, void* stream);
+                  int window, int dtype, int kv_splits, void* workspace, size_t workspace_bytes,
+                  void* stream);
 
 /*
  * Number of split workgroups rattn_decode_paged will use for these arguments.  The

@@ -25,9 +25,9 @@ LIB_PATH = os.path.join(_HERE, "librattn.so")
 
 RATTN_OK, RATTN_ERR_INVALID_ARG, RATTN_ERR_UNSUPPORTED, RATTN_ERR_WORKSPACE, RATTN_ERR_HIP = 0, 1, 2, 3, 4
 RATTN_BF16, RATTN_FP32 = 0, 1
-ABI_VERSION = 2
+ABI_VERSION = 3
 
-EXPORTED = ("rattn_prefill", "rattn_decode_num_splits", "rattn_decode_workspace_bytes", "rattn_decode_paged",
+EXPORTED = ("rattn_prefill_workspace_bytes", "rattn_prefill", "rattn_decode_num_splits", "rattn_decode_workspace_bytes", "rattn_decode_paged",
             "rattn_last_error", "rattn_abi_version")
 
 _lib = None
@@ -50,8 +50,10 @@ def load(path: Optional[str] = None):
                            "(or __graft_entry__.build()) first")
     lib = ctypes.CDLL(p)
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.rattn_prefill_workspace_bytes.restype = sz
+    lib.rattn_prefill_workspace_bytes.argtypes = [i32] * 8
     lib.rattn_prefill.restype = i32
-    lib.rattn_prefill.argtypes = [vp] * 6 + [i32] * 9 + [vp]
+    lib.rattn_prefill.argtypes = [vp] * 6 + [i32] * 10 + [vp, sz, vp]
     lib.rattn_decode_num_splits.restype = i32
     lib.rattn_decode_num_splits.argtypes = [i32] * 6
     lib.rattn_decode_workspace_bytes.restype = sz
@@ -106,14 +108,24 @@ def _dtype_code(t) -> int:
     raise ValueError(f"unsupported dtype {t.dtype}")
 
 
-def rattn_prefill(q, k, v, bias, out, lse=None, window: int = 0, stream=None) -> None:
+def rattn_prefill_workspace_bytes(B: int, Lq: int, Lk: int, Hq: int, Hkv: int, window: int = 0,
+                                  dtype: int = RATTN_BF16, kv_splits: int = 0) -> int:
+    return load().rattn_prefill_workspace_bytes(B, Lq, Lk, Hq, Hkv, int(window), dtype, int(kv_splits))
+
+
+def rattn_prefill(q, k, v, bias, out, lse=None, window: int = 0, kv_splits: int = 0, workspace=None,
+                  stream=None) -> None:
     """q [B,Lq,Hq,128], k/v [B,Lk,Hkv,128] (bf16 or fp32), bias [Hq,R] fp32,
-    out like q, lse [B,Lq,Hq] fp32 or None.  Query t sits at position Lk-Lq+t."""
+    out like q, lse [B,Lq,Hq] fp32 or None.  Query t sits at position Lk-Lq+t.
+    workspace: a uint8 device tensor of at least rattn_prefill_workspace_bytes(...) bytes,
+    zero-filled before its first use (calls leave it so), or None (no key-range split)."""
     B, Lq, Hq, D = q.shape
     Lk, Hkv = k.shape[1], k.shape[2]
     R = bias.shape[1]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load().rattn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(out), _ptr(lse),
-                                B, Lq, Lk, Hq, Hkv, D, R, int(window), _dtype_code(q), _stream(stream)))
+                                B, Lq, Lk, Hq, Hkv, D, R, int(window), _dtype_code(q), int(kv_splits),
+                                _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def rattn_decode_num_splits(B: int, n_q: int, Hq: int, Hkv: int, max_ctx_len: int, num_splits: int = 0) -> int:
@@ -143,11 +155,31 @@ def rattn_decode_paged(q, k_cache, v_cache, block_table, ctx_lens, windows, bias
 
 
 # ---- conveniences that allocate the outputs (torch device memory) and call the above ----
-def prefill(q, k, v, bias, window: int = 0, want_lse: bool = True, stream=None) -> Tuple:
+_prefill_ws = {}
+
+
+def prefill_workspace(nbytes: int, device):
+    """A zero-filled workspace of at least nbytes on `device`, kept and reused by later
+    calls (prefill calls leave it zero-filled).  Not for calls running concurrently."""
+    import torch
+    key = str(torch.device(device))
+    ws = _prefill_ws.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=device)
+        _prefill_ws[key] = ws
+    return ws
+
+
+def prefill(q, k, v, bias, window: int = 0, want_lse: bool = True, kv_splits: int = 0, workspace=None,
+            stream=None) -> Tuple:
     import torch
     out = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if want_lse else None
-    rattn_prefill(q, k, v, bias, out, lse, window, stream)
+    if workspace is None:
+        n = rattn_prefill_workspace_bytes(q.shape[0], q.shape[1], k.shape[1], q.shape[2], k.shape[2], window,
+                                          _dtype_code(q), kv_splits)
+        workspace = prefill_workspace(n, q.device) if n > 0 else None
+    rattn_prefill(q, k, v, bias, out, lse, window, kv_splits, workspace, stream)
     return out, lse
 
 

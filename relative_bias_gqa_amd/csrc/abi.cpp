@@ -7,6 +7,11 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <algorithm>
+#include <functional>
+#include <queue>
+#include <vector>
+
 #include "launch.hpp"
 #include "rattn.h"
 
@@ -93,6 +98,149 @@ bool plan_decode(int B, int n_q, int Hq, int Hkv, int max_ctx_len, int max_block
   return true;
 }
 
+// ---- prefill work decomposition and key-range split plan -----------------------------
+// A workgroup takes one KV head, hpw of its query heads and 32 * tsub tokens (hpw * tsub
+// = 8 waves).  Workgroups go to compute units in index order as units free up, heaviest
+// token tiles first.  When the heaviest tiles are long compared with a unit's share of the
+// work (a sliding window: every tile past the window costs the same), the last ones to
+// start finish late; splitting the key range of the heaviest tiles into `parts` pieces,
+// merged through the workspace, evens this out.  The plan simulates the in-order dispatch
+// for the grid without a split and for a few splits and keeps the fastest.
+void prefill_shape(int B, int Lq, int Lk, int Hq, int Hkv, int window, rattn::PrefillParams* p) {
+  p->B = B;
+  p->Lq = Lq;
+  p->Lk = Lk;
+  p->Hq = Hq;
+  p->Hkv = Hkv;
+  p->window = window > 0 ? window : 0;
+  p->G = Hq / Hkv;
+  p->hpw = largest_divisor_at_most(p->G, 8);
+  while (8 % p->hpw != 0) p->hpw = largest_divisor_at_most(p->G, p->hpw - 1);
+  p->tsub = 8 / p->hpw;
+  p->n_hg = p->G / p->hpw;
+  p->n_tok_tiles = (Lq + 32 * p->tsub - 1) / (32 * p->tsub);
+  p->n_split = 0;
+  p->parts = 1;
+  p->ws_o = nullptr;
+  p->ws_lse = nullptr;
+  p->ws_cnt = nullptr;
+}
+
+// 64-key tiles walked by token tile `tile` (the same range as the kernel computes)
+int prefill_tile_keys(const rattn::PrefillParams& p, int tile) {
+  const long long rows = 32LL * p.tsub, off = (long long)p.Lk - p.Lq;
+  const long long T0 = tile * rows, T1 = std::min<long long>(p.Lq, T0 + rows);
+  const long long weff = p.window > 0 ? p.window : (1LL << 30);
+  const long long kb = std::max(0LL, off + T0 - weff + 1) / 64, ke = (off + T1 - 1) / 64 + 1;
+  return (int)(ke - kb);
+}
+
+struct PrefillSplit {
+  int n_split = 0, parts = 1;
+  size_t lse_off = 0, o_off = 0, ws_bytes = 0;
+};
+
+constexpr int kDispatchUnits = 256;      // compute units of an MI355X
+// fixed costs in key-tile times: a workgroup's prologue and epilogue; a piece's, including
+// writing its partial and its share of the merge (fitted to sliding-window prefill timings
+// of 2-, 3- and 4-way splits on an MI355X)
+constexpr double kWgOverhead = 1.0;
+constexpr double kPieceOverhead = 4.5;
+
+// finish time of the last workgroup, jobs started in order on the least-loaded unit
+double simulate_dispatch(const std::vector<double>& jobs) {
+  std::priority_queue<double, std::vector<double>, std::greater<double>> units;
+  for (int i = 0; i < kDispatchUnits; ++i) units.push(0.0);
+  double end = 0.0;
+  for (double j : jobs) {
+    const double t = units.top() + j;
+    units.pop();
+    units.push(t);
+    end = std::max(end, t);
+  }
+  return end;
+}
+
+PrefillSplit split_layout(const rattn::PrefillParams& p, int n_split, int parts) {
+  PrefillSplit sp;
+  if (n_split <= 0 || parts < 2) return sp;
+  sp.n_split = n_split;
+  sp.parts = parts;
+  const size_t per_tile = (size_t)p.B * p.Hkv * p.n_hg;
+  const size_t jobs = (size_t)n_split * per_tile, pieces = jobs * parts;
+  sp.lse_off = (jobs * sizeof(int) + 255) & ~(size_t)255;
+  sp.o_off = (sp.lse_off + pieces * 256 * sizeof(float) + 255) & ~(size_t)255;
+  sp.ws_bytes = sp.o_off + pieces * 256 * 128 * sizeof(float);
+  return sp;
+}
+
+PrefillSplit plan_prefill_split_uncached(const rattn::PrefillParams& p, int dtype, int kv_splits) {
+  if (dtype != RATTN_BF16 || kv_splits == 1) return PrefillSplit{};
+  const int nt = p.n_tok_tiles;
+  std::vector<int> keys(nt);
+  for (int t = 0; t < nt; ++t) keys[t] = prefill_tile_keys(p, t);  // non-decreasing in t
+  if (kv_splits >= 2) {
+    // split every token tile with at least 2 * kv_splits key tiles
+    int n_split = 0;
+    while (n_split < nt && keys[nt - 1 - n_split] >= 2 * kv_splits) ++n_split;
+    return split_layout(p, n_split, kv_splits);
+  }
+  const long long per_tile = (long long)p.B * p.Hkv * p.n_hg;
+  if ((long long)nt * per_tile * rattn::kMaxPieces > 0x7fffffffLL) return PrefillSplit{};
+  auto jobs_of = [&](int n_split, int parts) {
+    std::vector<double> jobs;
+    for (int t = nt - 1; t >= nt - n_split; --t)
+      for (long long r = 0; r < per_tile; ++r)
+        for (int q = 0; q < parts; ++q) {
+          const int lo = keys[t] * q / parts, hi = keys[t] * (q + 1) / parts;
+          jobs.push_back(hi - lo + kPieceOverhead);
+        }
+    for (int t = nt - 1 - n_split; t >= 0; --t)
+      for (long long r = 0; r < per_tile; ++r) jobs.push_back(keys[t] + kWgOverhead);
+    return jobs;
+  };
+  double total = 0.0;
+  for (int t = 0; t < nt; ++t) total += (keys[t] + kWgOverhead) * per_tile;
+  double best = simulate_dispatch(jobs_of(0, 1));
+  // a grid that already finishes within 5 % of an even spread is left alone
+  if (best <= 1.05 * total / kDispatchUnits) return PrefillSplit{};
+  int best_split = 0, best_parts = 1;
+  const int kmax = keys[nt - 1];
+  for (int parts = 2; parts <= 4; ++parts)
+    for (int frac = 0; frac <= 3; ++frac) {
+      const int thr = std::max(2 * parts, kmax * frac / 4);
+      int n_split = 0;
+      while (n_split < nt && keys[nt - 1 - n_split] >= thr) ++n_split;
+      if (n_split == 0) continue;
+      const double m = simulate_dispatch(jobs_of(n_split, parts));
+      if (m < 0.97 * best) {
+        best = m;
+        best_split = n_split;
+        best_parts = parts;
+      }
+    }
+  return split_layout(p, best_split, best_parts);
+}
+
+// the plan of the last few shapes (calls repeat their shapes)
+PrefillSplit plan_prefill_split(const rattn::PrefillParams& p, int dtype, int kv_splits) {
+  struct Entry {
+    int key[8];
+    PrefillSplit plan;
+  };
+  thread_local Entry cache[8];
+  thread_local int filled = 0, next = 0;
+  const int key[8] = {p.B, p.Lq, p.Lk, p.Hq, p.Hkv, p.window, dtype, kv_splits};
+  for (int i = 0; i < filled; ++i)
+    if (std::equal(key, key + 8, cache[i].key)) return cache[i].plan;
+  const PrefillSplit sp = plan_prefill_split_uncached(p, dtype, kv_splits);
+  std::copy(key, key + 8, cache[next].key);
+  cache[next].plan = sp;
+  next = (next + 1) % 8;
+  filled = std::min(filled + 1, 8);
+  return sp;
+}
+
 }  // namespace
 
 extern "C" {
@@ -103,13 +251,16 @@ int rattn_abi_version(void) { return RATTN_ABI_VERSION; }
 
 int rattn_prefill(const void* q, const void* k, const void* v, const float* bias, void* out,
                   float* lse, int B, int Lq, int Lk, int Hq, int Hkv, int head_dim, int R,
-                  int window, int dtype, void* stream) {
+                  int window, int dtype, int kv_splits, void* workspace, size_t workspace_bytes,
+                  void* stream) {
   if (B < 0 || Lq < 0 || Lk < 0 || Hq < 0 || Hkv < 0)
     return fail(RATTN_ERR_INVALID_ARG, "rattn_prefill: negative size (B=%d Lq=%d Lk=%d Hq=%d Hkv=%d)", B, Lq,
                 Lk, Hq, Hkv);
   if (head_dim != 128) return fail(RATTN_ERR_UNSUPPORTED, "rattn_prefill: head_dim %d (only 128)", head_dim);
   if (dtype != RATTN_BF16 && dtype != RATTN_FP32)
     return fail(RATTN_ERR_UNSUPPORTED, "rattn_prefill: unknown dtype %d", dtype);
+  if (kv_splits < 0 || kv_splits > rattn::kMaxPieces)
+    return fail(RATTN_ERR_INVALID_ARG, "rattn_prefill: kv_splits=%d outside 0..%d", kv_splits, rattn::kMaxPieces);
   if (B == 0 || Lq == 0) return ok();
   if (!q || !k || !v || !bias || !out) return fail(RATTN_ERR_INVALID_ARG, "rattn_prefill: null pointer argument");
   if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0)
@@ -117,6 +268,8 @@ int rattn_prefill(const void* q, const void* k, const void* v, const float* bias
   if (Lq > Lk) return fail(RATTN_ERR_INVALID_ARG, "rattn_prefill: Lq=%d > Lk=%d", Lq, Lk);
   if (Lk > kMaxPosition) return fail(RATTN_ERR_INVALID_ARG, "rattn_prefill: Lk=%d too large", Lk);
   if (R < 1) return fail(RATTN_ERR_INVALID_ARG, "rattn_prefill: R=%d < 1", R);
+  if (workspace == nullptr && workspace_bytes != 0)
+    return fail(RATTN_ERR_INVALID_ARG, "rattn_prefill: workspace_bytes=%zu with a null workspace", workspace_bytes);
 
   rattn::PrefillParams p;
   p.q = q;
@@ -125,27 +278,37 @@ int rattn_prefill(const void* q, const void* k, const void* v, const float* bias
   p.bias = bias;
   p.out = out;
   p.lse = lse;
-  p.B = B;
-  p.Lq = Lq;
-  p.Lk = Lk;
-  p.Hq = Hq;
-  p.Hkv = Hkv;
   p.R = R;
-  p.window = window > 0 ? window : 0;
-  p.G = Hq / Hkv;
-  p.hpw = largest_divisor_at_most(p.G, 8);
-  while (8 % p.hpw != 0) p.hpw = largest_divisor_at_most(p.G, p.hpw - 1);
-  p.tsub = 8 / p.hpw;
-  p.n_hg = p.G / p.hpw;
-  p.n_tok_tiles = (Lq + 32 * p.tsub - 1) / (32 * p.tsub);
+  prefill_shape(B, Lq, Lk, Hq, Hkv, window, &p);
   p.scale_log2 = kScaleLog2;
-  const long long grid = (long long)p.n_tok_tiles * B * Hkv * p.n_hg;
+  // no workspace: never split
+  const PrefillSplit sp = workspace == nullptr ? PrefillSplit{} : plan_prefill_split(p, dtype, kv_splits);
+  if (sp.ws_bytes > workspace_bytes)
+    return fail(RATTN_ERR_WORKSPACE, "rattn_prefill: workspace of %zu bytes, %zu needed", workspace_bytes,
+                sp.ws_bytes);
+  p.n_split = sp.n_split;
+  p.parts = sp.parts;
+  p.ws_cnt = (int*)workspace;
+  p.ws_lse = sp.ws_bytes ? (float*)((char*)workspace + sp.lse_off) : nullptr;
+  p.ws_o = sp.ws_bytes ? (float*)((char*)workspace + sp.o_off) : nullptr;
+  const long long per_tile = (long long)B * Hkv * p.n_hg;
+  const long long grid = ((long long)p.n_tok_tiles - p.n_split) * per_tile + (long long)p.n_split * per_tile * p.parts;
   if (grid > 0x7fffffffLL) return fail(RATTN_ERR_INVALID_ARG, "rattn_prefill: problem too large for one launch");
 
   hipError_t e = dtype == RATTN_BF16 ? rattn::launch_prefill_bf16(p, (hipStream_t)stream)
                                      : rattn::launch_prefill_fp32(p, (hipStream_t)stream);
   if (e != hipSuccess) return fail(RATTN_ERR_HIP, "rattn_prefill: launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+size_t rattn_prefill_workspace_bytes(int B, int Lq, int Lk, int Hq, int Hkv, int window, int dtype,
+                                     int kv_splits) {
+  if (B < 1 || Lq < 1 || Lk < Lq || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || Lk > kMaxPosition ||
+      (dtype != RATTN_BF16 && dtype != RATTN_FP32) || kv_splits < 0 || kv_splits > rattn::kMaxPieces)
+    return 0;
+  rattn::PrefillParams p;
+  prefill_shape(B, Lq, Lk, Hq, Hkv, window, &p);
+  return plan_prefill_split(p, dtype, kv_splits).ws_bytes;
 }
 
 int rattn_decode_num_splits(int B, int n_q, int Hq, int Hkv, int max_ctx_len, int num_splits) {

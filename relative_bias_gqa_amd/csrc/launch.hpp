@@ -22,7 +22,17 @@ struct PrefillParams {
   int n_tok_tiles;  // ceil(Lq / (32 * tsub))
   int n_hg;         // G / hpw head groups per KV head
   float scale_log2; // log2(e) / sqrt(128)
+  // Key-range split of the heaviest token tiles (bf16 path): the last n_split token tiles
+  // are each computed by `parts` workgroups over consecutive shares of their key tiles,
+  // which merge through the workspace (n_split = 0, parts = 1: no split).
+  int n_split;
+  int parts;
+  float* ws_o;    // [n_split * B * Hkv * n_hg * parts, 256 rows, 128] normalised partials
+  float* ws_lse;  // [same, 256 rows] log2-sum-exp of each partial
+  int* ws_cnt;    // [n_split * B * Hkv * n_hg] finished pieces; zero between calls
 };
+
+constexpr int kMaxPieces = 8;  // largest `parts` of a prefill key-range split
 
 hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream);
 hipError_t launch_prefill_fp32(const PrefillParams& p, hipStream_t stream);

@@ -48,6 +48,7 @@ constexpr int kSliceFloats = 128;                 // per wave: 95 distances used
 constexpr int kBiasBytes = kWaves * kSliceFloats * 4;
 constexpr int kStageBytes = 2 * kKVBytes + kBiasBytes;  // 36 KB
 constexpr int kLoadsPerStage = 6;                 // per wave: 2 K + 2 V + 2 bias
+constexpr int kWgRows = 32 * kWaves;              // query rows of a workgroup
 constexpr float kRescaleSlack = 8.0f;             // log2 units: P entries stay below 2^8
 constexpr float kSqrtD = 11.313708498984761f;     // sqrt(128)
 
@@ -68,6 +69,7 @@ __device__ __forceinline__ u32x2_t lds_tr8(uint32_t a) {
 
 __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams p) {
   __shared__ __attribute__((aligned(1024))) unsigned char ring[kStages * kStageBytes];
+  __shared__ int last_piece;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -76,9 +78,16 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   const int hf = lane >> 5;   // which half of the key rows this lane holds
 
   // ---- job: heaviest (last) token tiles first ---------------------------------------
+  // The first n_split * per_tile * parts workgroups each take one of `parts` pieces of the
+  // key range of the n_split heaviest token tiles (the pieces of a tile adjacent); the
+  // others take whole token tiles.  Both lists run from the heaviest tile down.
   const int per_tile = p.B * p.Hkv * p.n_hg;
-  const int tile = p.n_tok_tiles - 1 - (int)blockIdx.x / per_tile;
-  const int rem = (int)blockIdx.x % per_tile;
+  const int n_piece_wgs = p.n_split * per_tile * p.parts;
+  const bool is_piece = (int)blockIdx.x < n_piece_wgs;
+  const int job = is_piece ? (int)blockIdx.x / p.parts : (int)blockIdx.x - n_piece_wgs + p.n_split * per_tile;
+  const int piece = is_piece ? (int)blockIdx.x % p.parts : 0;
+  const int tile = p.n_tok_tiles - 1 - job / per_tile;
+  const int rem = job % per_tile;
   const int hg = rem % p.n_hg;
   const int hk = (rem / p.n_hg) % p.Hkv;
   const int b = rem / (p.n_hg * p.Hkv);
@@ -94,9 +103,15 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   const int pw_last = pw0 + max(wvalid, 1) - 1;
   const int Weff = p.window > 0 ? p.window : 0x40000000;
 
-  // keys the workgroup needs, in whole tiles, and the keys this wave needs
-  const int kt_begin = max(0, off + T0 - Weff + 1) / kBK;
-  const int kt_end = (off + T1 - 1) / kBK + 1;
+  // keys the workgroup needs, in whole tiles (a piece: its share of them)
+  int kt_begin = max(0, off + T0 - Weff + 1) / kBK;
+  int kt_end = (off + T1 - 1) / kBK + 1;
+  if (is_piece) {
+    const int nt = kt_end - kt_begin;
+    const int first = kt_begin;
+    kt_begin = first + (nt * piece) / p.parts;
+    kt_end = first + (nt * (piece + 1)) / p.parts;
+  }
   const int n_tiles = kt_end - kt_begin;
 
   // ---- Q^T operand, resident for the whole key loop -------------------------------
@@ -406,26 +421,106 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   // ---- epilogue --------------------------------------------------------------------
   const float l_tot = half_swap_sum(l_run);
   const int tq = tw0 + col;
-  if (!wave_active || tq >= p.Lq) return;
-  const float inv = 1.f / l_tot;
-  const size_t obase = (((size_t)b * p.Lq + tq) * p.Hq + h) * kHeadDim;
+  const bool row_ok = wave_active && tq < p.Lq;
+  const size_t obase = (((size_t)b * p.Lq + (row_ok ? tq : 0)) * p.Hq + h) * kHeadDim;
+  if (!is_piece) {
+    if (!row_ok) return;
+    const float inv = 1.f / l_tot;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int d = 32 * db + 8 * q + 4 * hf;
+        const float x0 = o[db][4 * q + 0] * inv, x1 = o[db][4 * q + 1] * inv;
+        const float x2 = o[db][4 * q + 2] * inv, x3 = o[db][4 * q + 3] * inv;
+        *(u32x2_t*)((uint16_t*)p.out + obase + d) = u32x2_t{pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
+      }
+    if (hf == 0 && p.lse != nullptr)
+      p.lse[((size_t)b * p.Lq + tq) * p.Hq + h] = (m_run + __log2f(l_tot)) * kLn2;
+    return;
+  }
+
+  // A piece: its normalised output and log2-sum-exp per row go to the workspace (a row
+  // that saw no key of this piece: zeros and -inf).  The piece that finishes last merges
+  // all pieces of the tile from the workspace, in piece order (so the result does not
+  // depend on which one that is), and writes the output.
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const float lse2 = l_tot > 0.f ? m_run + __log2f(l_tot) : kNegInf;
+  // Partial layout (per piece, per wave): register r of block db, then the lane -- each
+  // dword store or load of a wave covers 256 consecutive bytes.
+  const int wrow = wave * 32 + col;  // row of the workgroup, 0..255
+  auto part_o = [&](size_t slot) { return p.ws_o + ((slot * kWaves + wave) * 32 * kHeadDim + lane); };
+  // The partials are written and read with device-coherent (agent-scope) accesses, which
+  // go to the coherence point directly: a device-scope fence instead would write back and
+  // invalidate this XCD's whole L2, and with it the K/V tiles of every other workgroup.
+  auto st_dev = [](float* a, float v) { __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+  auto ld_dev = [](const float* a) { return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+  {
+    float* wo = part_o(blockIdx.x);
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st_dev(wo + (16 * db + 4 * q + i) * 64, o[db][4 * q + i] * inv);
+    if (hf == 0) st_dev(p.ws_lse + (size_t)blockIdx.x * kWgRows + wrow, lse2);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's partials have landed
+  __syncthreads();
+  if (tid == 0) {
+    const int old = __hip_atomic_fetch_add(p.ws_cnt + job, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last_piece = old == p.parts - 1;
+    // every piece of this tile has counted: leave the counter at zero for the next call
+    if (last_piece) __hip_atomic_store(p.ws_cnt + job, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (!last_piece) return;
+  if (!row_ok) return;
+  const size_t slot0 = (size_t)job * p.parts;  // workgroup index of piece 0 of this tile
+  float lse_j[kMaxPieces];
+  float mmax = kNegInf;
+#pragma unroll
+  for (int j = 0; j < kMaxPieces; ++j) {
+    lse_j[j] = j >= p.parts ? kNegInf : ld_dev(p.ws_lse + (slot0 + j) * kWgRows + wrow);
+    mmax = fmaxf(mmax, lse_j[j]);
+  }
+  f32x16_t acc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) acc[db] = zero_f32x16();
+  float wsum = 0.f;
+#pragma unroll
+  for (int j = 0; j < kMaxPieces; ++j) {
+    if (j >= p.parts) break;
+    const float w = lse_j[j] == kNegInf ? 0.f : fast_exp2(lse_j[j] - mmax);
+    wsum += w;
+    const float* src = part_o(slot0 + j);
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          acc[db][4 * q + i] = fmaf(w, ld_dev(src + (16 * db + 4 * q + i) * 64), acc[db][4 * q + i]);
+  }
+  const float winv = 1.f / wsum;
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int d = 32 * db + 8 * q + 4 * hf;
-      const float x0 = o[db][4 * q + 0] * inv, x1 = o[db][4 * q + 1] * inv;
-      const float x2 = o[db][4 * q + 2] * inv, x3 = o[db][4 * q + 3] * inv;
+      const float x0 = acc[db][4 * q + 0] * winv, x1 = acc[db][4 * q + 1] * winv;
+      const float x2 = acc[db][4 * q + 2] * winv, x3 = acc[db][4 * q + 3] * winv;
       *(u32x2_t*)((uint16_t*)p.out + obase + d) = u32x2_t{pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
     }
   if (hf == 0 && p.lse != nullptr)
-    p.lse[((size_t)b * p.Lq + tq) * p.Hq + h] = (m_run + __log2f(l_tot)) * kLn2;
+    p.lse[((size_t)b * p.Lq + tq) * p.Hq + h] = (mmax + __log2f(wsum)) * kLn2;
 }
 
 }  // namespace
 
 hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream) {
-  const long long grid = (long long)p.n_tok_tiles * p.B * p.Hkv * p.n_hg;
+  const long long per_tile = (long long)p.B * p.Hkv * p.n_hg;
+  const long long grid = ((long long)p.n_tok_tiles - p.n_split) * per_tile + (long long)p.n_split * per_tile * p.parts;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(prefill_bf16_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, p);

@@ -38,15 +38,16 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.rattn_abi_version() == rb.ABI_VERSION == 2
+    assert lib.rattn_abi_version() == rb.ABI_VERSION == 3
 
 
 def _prefill(lib, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, bias=FAKE, out=FAKE, lse=None, B=1, Lq=4, Lk=4, Hq=4, Hkv=2, D=128, R=8,
-             window=0, dtype=0, stream=None)
+             window=0, dtype=0, kv_splits=0, ws=None, wsb=0, stream=None)
     a.update(kw)
     return lib.rattn_prefill(a["q"], a["k"], a["v"], a["bias"], a["out"], a["lse"], a["B"], a["Lq"], a["Lk"],
-                             a["Hq"], a["Hkv"], a["D"], a["R"], a["window"], a["dtype"], a["stream"])
+                             a["Hq"], a["Hkv"], a["D"], a["R"], a["window"], a["dtype"], a["kv_splits"], a["ws"],
+                             a["wsb"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,status,needle", [
@@ -60,6 +61,10 @@ def _prefill(lib, **kw):
     (dict(B=-1), rb.RATTN_ERR_INVALID_ARG, "negative"),
     (dict(D=64), rb.RATTN_ERR_UNSUPPORTED, "head_dim"),
     (dict(dtype=7), rb.RATTN_ERR_UNSUPPORTED, "dtype"),
+    (dict(kv_splits=9), rb.RATTN_ERR_INVALID_ARG, "kv_splits"),
+    (dict(kv_splits=-1), rb.RATTN_ERR_INVALID_ARG, "kv_splits"),
+    (dict(wsb=64), rb.RATTN_ERR_INVALID_ARG, "workspace"),
+    (dict(Lq=4096, Lk=4096, kv_splits=2, ws=FAKE, wsb=64), rb.RATTN_ERR_WORKSPACE, "workspace"),
 ])
 def test_prefill_validation(lib, kw, status, needle):
     assert _prefill(lib, **kw) == status
@@ -127,6 +132,41 @@ def test_workspace_and_split_plan(lib):
     # large batches run in launches of at most 2048 sequences sharing one workspace
     big = rb.rattn_decode_workspace_bytes(5000, 1, 16, 2, 4096, 0)
     assert big == rb.rattn_decode_workspace_bytes(2048, 1, 16, 2, 4096, 0)
+
+
+def _tile_keys(Lq, Lk, window, rows, tile):
+    off, T0 = Lk - Lq, tile * rows
+    T1 = min(Lq, T0 + rows)
+    weff = window if window > 0 else 1 << 30
+    return (off + T1 - 1) // 64 + 1 - max(0, off + T0 - weff + 1) // 64
+
+
+def _split_bytes(jobs, parts):
+    align = lambda n: (n + 255) // 256 * 256  # noqa: E731
+    pieces = jobs * parts
+    return align(align(jobs * 4) + pieces * 256 * 4) + pieces * 256 * 128 * 4
+
+
+def test_prefill_split_plan(lib):
+    # forced split: every 256-row tile (32 tokens x 8 heads) with >= 2n key tiles -> n pieces,
+    # workspace = per-tile counters + a log2-sum-exp and a 128-float partial per piece row
+    for (B, Lq, Lk, Hq, Hkv, W, n) in [(1, 1000, 1000, 16, 2, 0, 2), (2, 300, 5000, 8, 1, 0, 3),
+                                       (1, 4096, 4096, 16, 2, 1024, 4)]:
+        G = Hq // Hkv
+        hpw = max(d for d in range(1, 9) if G % d == 0 and 8 % d == 0)
+        rows = 32 * (8 // hpw)
+        n_tiles = -(-Lq // rows)
+        n_split = sum(1 for t in range(n_tiles) if _tile_keys(Lq, Lk, W, rows, t) >= 2 * n)
+        jobs = n_split * B * Hkv * (G // hpw)
+        want = _split_bytes(jobs, n) if n_split else 0
+        assert rb.rattn_prefill_workspace_bytes(B, Lq, Lk, Hq, Hkv, W, rb.RATTN_BF16, n) == want
+    # the library's own plan: a long sliding-window prefill is split, a long chunked prefill
+    # (whose tiles differ in length and balance by themselves) and fp32 inputs are not
+    assert rb.rattn_prefill_workspace_bytes(1, 8192, 8192, 16, 2, 4096, rb.RATTN_BF16, 0) > 0
+    assert rb.rattn_prefill_workspace_bytes(1, 8192, 32768, 16, 2, 0, rb.RATTN_BF16, 0) == 0
+    assert rb.rattn_prefill_workspace_bytes(1, 8192, 8192, 16, 2, 4096, rb.RATTN_FP32, 0) == 0
+    assert rb.rattn_prefill_workspace_bytes(1, 8192, 8192, 16, 2, 4096, rb.RATTN_BF16, 1) == 0
+    assert rb.rattn_prefill_workspace_bytes(1, 0, 8, 16, 2, 0, rb.RATTN_BF16, 0) == 0
 
 
 def test_binding_fails_loudly_without_library(tmp_path):

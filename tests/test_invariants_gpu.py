@@ -119,6 +119,27 @@ def test_chunk_equals_full_prefill(window):
     assert (lse_c - lse_f[:, L - Lq:]).abs().max().item() <= 1e-4
 
 
+def test_key_split_only_reorders_sums():
+    """Any key-range split of the query tiles gives the unsplit result up to summation order,
+    and a split call repeated is bitwise identical (the merge runs in piece order whichever
+    piece finishes last)."""
+    print("case key split", flush=True)
+    L, Hq, Hkv, R, W = 2000, 16, 2, 900, 700
+    case = synth.make_prefill(50, 1, L, L, Hq, Hkv, R, W, "bf16")
+    q, k, v, r = dev(case.q), dev(case.k), dev(case.v), dev(case.bias)
+    ref_o, ref_l = rb.prefill(q, k, v, r, W, kv_splits=1)
+    for ns in (0, 2, 3, 5, 8):
+        n = rb.rattn_prefill_workspace_bytes(1, L, L, Hq, Hkv, W, rb.RATTN_BF16, ns)
+        ws = torch.zeros(max(n, 1), dtype=torch.uint8, device="cuda")
+        o1, l1 = rb.prefill(q, k, v, r, W, kv_splits=ns, workspace=ws)
+        o2, l2 = rb.prefill(q, k, v, r, W, kv_splits=ns, workspace=ws)
+        torch.cuda.synchronize()
+        assert _bitwise_equal(o1, o2) and _bitwise_equal(l1, l2)
+        assert (o1.float() - ref_o.float()).abs().max().item() <= 8e-3  # one bf16 ulp near 1
+        assert (l1 - ref_l).abs().max().item() <= 1e-5
+        assert int(ws[:256].count_nonzero()) == 0
+
+
 def test_one_hot_values_expose_the_weights():
     print("case one-hot V", flush=True)
     # 256 keys, one KV head: two runs with V_j = e_j (j < 128) and V_j = e_(j-128) (j >= 128)
@@ -166,10 +187,10 @@ def test_empty_calls_are_noops():
     lib = rb.load()
     sentinel = torch.full((4,), 7.0, device="cuda")
     # B = 0 and Lq = 0 prefill, B = 0 decode: status OK, nothing written
-    assert lib.rattn_prefill(None, None, None, None, None, sentinel.data_ptr(), 0, 5, 5, 4, 1, 128, 8, 0, 0,
-                             None) == rb.RATTN_OK
-    assert lib.rattn_prefill(None, None, None, None, None, sentinel.data_ptr(), 1, 0, 5, 4, 1, 128, 8, 0, 0,
-                             None) == rb.RATTN_OK
+    assert lib.rattn_prefill(None, None, None, None, None, sentinel.data_ptr(), 0, 5, 5, 4, 1, 128, 8, 0, 0, 0,
+                             None, 0, None) == rb.RATTN_OK
+    assert lib.rattn_prefill(None, None, None, None, None, sentinel.data_ptr(), 1, 0, 5, 4, 1, 128, 8, 0, 0, 0,
+                             None, 0, None) == rb.RATTN_OK
     assert lib.rattn_decode_paged(None, None, None, None, None, None, None, None, sentinel.data_ptr(), 0, 1, 16,
                                   2, 128, 128, 8, 4, 2, 200, 0, None, 0, None) == rb.RATTN_OK
     torch.cuda.synchronize()
