@@ -29,8 +29,10 @@ def _hipcc() -> str:
 
 
 # Packed fp32 VALU instructions are disabled for all device code; hipcc -O3 would otherwise
-# form v_pk_{add,mul,fma}_f32 from ordinary float code.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# form v_pk_{add,mul,fma}_f32 from ordinary float code.  MFMA results stay in VGPRs: the
+# kernels touch their accumulators with vector instructions (softmax, rescale), and with
+# AGPR accumulators the compiler copied them between the register files on every unit.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function",
           "-I", INCLUDE, "-I", CSRC]
 

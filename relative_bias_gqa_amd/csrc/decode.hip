@@ -146,22 +146,6 @@ __device__ __forceinline__ void cursor_next(const DecodeParams& p, Cursor& c) {
   }
 }
 
-// V^T operand (32 d-rows x 16 keys) from a swizzled V stage: LDS row = key, 256 B, the
-// 16-byte chunk k of row r stored at chunk k ^ (2 (r & 7)).  Same lane/key order as
-// load_vt_operand.
-__device__ __forceinline__ u32x4_t load_vt_swz(const unsigned char* v_stage, int kbase, int dcol0, int lane) {
-  const int m = lane & 15;
-  const int hf = lane >> 5;
-  const int row = kbase + 4 * hf + (m >> 2);
-  const int col = dcol0 + 16 * ((lane >> 4) & 1) + 4 * (m & 3);
-  const int off = (((col >> 3) ^ ((row & 7) << 1)) << 4) + ((col & 7) << 1);
-  const s16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(v_stage + row * 256 + off));
-  const s16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(v_stage + (row + 8) * 256 + off));
-  const u32x2_t ua = __builtin_bit_cast(u32x2_t, a);
-  const u32x2_t ub = __builtin_bit_cast(u32x2_t, b);
-  return u32x4_t{ua[0], ua[1], ub[0], ub[1]};
-}
-
 // KS: waves sharing the keys of a unit (2: one 32-key half each; 1: a wave takes both).
 // NB: bias loads per wave and unit (64 floats each), NB * 256 >= gs * SL.
 template <int KS, int NB>
@@ -267,6 +251,18 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeParams 
   const int ks_w = wave / rb_span;
   const bool wave_active = rb < n_rb && ks_w < KS;
   const int kb_lo = KS == 2 ? ks_w : 0;
+  // LDS operand bases (stage 0).  K rows are 256 B with 16-byte chunk c of key j at chunk
+  // c ^ (j & 15): the A operand of k-step k8 (key 32 kb + col, chunk 2 k8 + hf) sits at
+  // kx0 ^ (32 k8).  V rows have chunk c of key j at c ^ (2 (j & 7)): the transposed read
+  // of d block db, keys kbase.. is at vz0 ^ (64 db) + 256 kbase (and 8 rows on).
+  const uint32_t kx0 = ring_base + 8192u * kb_lo + col * 256 + 32 * ((col & 15) >> 1) + 16 * (hf ^ (col & 1));
+  uint32_t vz0;
+  {
+    const int m = lane & 15, u = (lane >> 4) & 1;
+    const int vrow = 4 * hf + (m >> 2);
+    const int y = (2 * u + ((m & 3) >> 1)) ^ (2 * (vrow & 7));
+    vz0 = ring_base + kKVBytes + 8192u * kb_lo + vrow * 256 + 16 * y + 8 * (m & 1);
+  }
   const int r_row = 32 * rb + col;
   const bool row_ok = r_row < p.rows;
   const int tq = row_ok ? r_row / p.gs : 0;
@@ -353,29 +349,25 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeParams 
     const unsigned char* ks_lds = ring + st * kStageBytes;
     const unsigned char* vs_lds = ks_lds + kKVBytes;
     const float* bs_lds = (const float*)(vs_lds + kKVBytes);
+    // this unit's operand bases: one register each, the reads differ by an XOR with a
+    // constant and an immediate offset (kept opaque so the compiler does not precompute
+    // every read address of every stage)
+    uint32_t kx = kx0 + st * kStageBytes, vz = vz0 + st * kStageBytes;
+    asm volatile("" : "+v"(kx), "+v"(vz));
     const int j0 = cc.c * kUnit;
     const int p0 = cc.si.ctx - p.n_q;  // position of query 0
     const bool saturated = p0 - (j0 + kUnit - 1) >= p.R - 1;
     const bool need_mask = (j0 + kUnit - 1 > p0) || (j0 < cc.si.ctx - cc.si.weff);
 
-    // every LDS operand of this wave's 32-key blocks first, so their latency overlaps
+    // the K operands of this wave's 32-key blocks first, then S^T = K Q^T; the V operands
+    // are read after the score MFMAs are issued, so that their latency overlaps the
+    // softmax and the K and V operands are never live together (which would push the
+    // wave past 256 VGPRs into AGPR accumulators and copies)
     u32x4_t ka[KB][8];
-    u32x4_t va[KB][4][2];
-#pragma unroll
-    for (int i = 0; i < KB; ++i) {
-      const int krow = 32 * (kb_lo + i) + col;
-      const unsigned char* kr = ks_lds + krow * 256;
-#pragma unroll
-      for (int k8 = 0; k8 < 8; ++k8) ka[i][k8] = *(const u32x4_t*)(kr + (((2 * k8 + hf) ^ (krow & 15)) << 4));
-    }
 #pragma unroll
     for (int i = 0; i < KB; ++i)
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int half = 0; half < 2; ++half)
-          va[i][db][half] = load_vt_swz(vs_lds, 32 * (kb_lo + i) + 16 * half, 32 * db, lane);
-    // S^T = K Q^T
+      for (int k8 = 0; k8 < 8; ++k8) ka[i][k8] = lds_ld16((kx ^ (32u * k8)) + 8192u * i);
     f32x16_t sacc[KB];
 #pragma unroll
     for (int i = 0; i < KB; ++i) {
@@ -383,6 +375,21 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeParams 
 #pragma unroll
       for (int k8 = 0; k8 < 8; ++k8) sacc[i] = mfma_32x32x16(ka[i][k8], qr[k8], sacc[i]);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    // V^T operands of 32-key block i (the first block's are read now, overlapping the
+    // softmax; a second block's while the first block's P.V MFMAs run)
+    u32x4_t va[4][2];
+    auto load_v = [&](int i) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const uint32_t a = (vz ^ (64u * db)) + 256u * (32 * i + 16 * half);
+          const u32x2_t lo = lds_tr8(a), hi = lds_tr8(a + 2048u);
+          va[db][half] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+        }
+    };
+    load_v(0);
     float t[KB][16];
     const int dl = p0 + tq - j0 - 4 * hf - 32 * kb_lo;  // distance of this lane's first key
     const int weff = cc.si.weff;
@@ -422,11 +429,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeParams 
     l_run += lsum;
     // O^T += V^T P^T
 #pragma unroll
-    for (int i = 0; i < KB; ++i)
+    for (int i = 0; i < KB; ++i) {
+      if (i > 0) load_v(i);
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int half = 0; half < 2; ++half) o[db] = mfma_32x32x16(va[i][db][half], pk[i][half], o[db]);
+        for (int half = 0; half < 2; ++half) o[db] = mfma_32x32x16(va[db][half], pk[i][half], o[db]);
+    }
   };
 
   // ---- main loop: unit t computed from stage t % 4 while units t+1..t+3 load ------------

@@ -115,6 +115,17 @@ __device__ __forceinline__ u32x4_t pack_p_operand(const float* p8) {
   return r;
 }
 
+// LDS accesses through plain 32-bit byte addresses, so that the per-lane part of every
+// operand address is one register and the rest is an immediate offset or an XOR with a
+// constant (the K/V tile swizzles of the kernels are chosen to allow this).
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
+typedef __attribute__((address_space(3))) float lds_f32_t;
+__device__ __forceinline__ u32x4_t lds_ld16(uint32_t a) { return *(const lds_u32x4_t*)(size_t)a; }
+__device__ __forceinline__ float lds_ldf(uint32_t a) { return *(const lds_f32_t*)(size_t)a; }
+__device__ __forceinline__ u32x2_t lds_tr8(uint32_t a) {
+  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(size_t)a));
+}
+
 // ---- direct global -> LDS loads (global_load_lds_dword{,x4}) --------------------------
 // Lane i of the issuing wave writes its 4 (or 16) bytes at LDS byte address
 // M0 + 4 i (or 16 i); lanes that are switched off write nothing.  The loads are issued

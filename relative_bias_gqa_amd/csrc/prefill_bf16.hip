@@ -55,18 +55,6 @@ constexpr float kSqrtD = 11.313708498984761f;     // sqrt(128)
 // 256 bytes of zeros: the source of every K/V row past the end of the sequence.
 __device__ __attribute__((aligned(256))) const uint32_t kZeroRowP[64] = {0};
 
-// LDS accesses through plain 32-bit byte addresses, so that the per-lane part of every
-// operand address is one register and the rest is an immediate offset or an XOR with a
-// constant (see the swizzles below).
-typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
-typedef __attribute__((address_space(3))) float lds_f32_t;
-__device__ __forceinline__ u32x4_t lds_ld16(uint32_t a) { return *(const lds_u32x4_t*)(size_t)a; }
-__device__ __forceinline__ float lds_ldf(uint32_t a) { return *(const lds_f32_t*)(size_t)a; }
-__device__ __forceinline__ void lds_stf(uint32_t a, float v) { *(lds_f32_t*)(size_t)a = v; }
-__device__ __forceinline__ u32x2_t lds_tr8(uint32_t a) {
-  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(size_t)a));
-}
-
 __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams p) {
   __shared__ __attribute__((aligned(1024))) unsigned char ring[kStages * kStageBytes];
   __shared__ int last_piece;
