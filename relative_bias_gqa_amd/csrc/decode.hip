@@ -313,12 +313,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeParams 
     if (hf == 0) p.ws_lse[slot_row] = l_tot > 0.f ? m_run + __log2f(l_tot) : kNegInf;
   };
 
-  // logits of this wave's 32-key blocks (log2 units) into t; returns the row maximum
+  // logits of this wave's 32-key blocks into t, in log2 units relative to m_ref (the
+  // running maximum, or 0 before the row's first visible key): the bias and the
+  // reference in one FMA.  Returns the row maximum over this lane and its partner.
   auto logits = [&](auto sat_c, auto mask_c, const f32x16_t* sacc, const float* bs_lds, float (*t)[16],
-                    int dl, int weff) {
+                    int dl, int weff, float m_ref) {
     constexpr bool SAT = decltype(sat_c)::value;
     constexpr bool MASK = decltype(mask_c)::value;
-    float mx = kNegInf;
     float bb[KB][16];
     if constexpr (!SAT) {
 #pragma unroll
@@ -326,22 +327,31 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeParams 
 #pragma unroll
         for (int r = 0; r < 16; ++r) bb[i][r] = bs_lds[bias_lane + 59 - (32 * i + 8 * (r >> 2) + (r & 3))];
     }
+    const float c_sat = bias_sat - m_ref;
 #pragma unroll
     for (int i = 0; i < KB; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float x;
-        if constexpr (SAT) x = fmaf(sacc[i][r], p.scale_log2, bias_sat);
-        else x = fmaf(bb[i][r], kLog2e, sacc[i][r] * p.scale_log2);
+        if constexpr (SAT) x = fmaf(sacc[i][r], p.scale_log2, c_sat);
+        else x = fmaf(bb[i][r], kLog2e, fmaf(sacc[i][r], p.scale_log2, -m_ref));
         if constexpr (MASK) {
           // distance of this key from the lane's query; visible iff 0 <= d < weff
           const int d = dl - (32 * i + 8 * (r >> 2) + (r & 3));
           x = (uint32_t)d < (uint32_t)weff ? x : kNegInf;
         }
         t[i][r] = x;
-        mx = fmaxf(mx, x);
       }
-    return mx;
+    float mb[KB];
+#pragma unroll
+    for (int i = 0; i < KB; ++i) {
+      float m = max3f(t[i][0], t[i][1], t[i][2]);
+#pragma unroll
+      for (int r = 3; r < 15; r += 2) m = max3f(m, t[i][r], t[i][r + 1]);
+      mb[i] = m;
+    }
+    if constexpr (KB == 1) return half_swap_max3(mb[0], t[0][15]);
+    else return half_swap_max3(max3f(mb[0], mb[1], t[0][15]), t[1][15]);
   };
 
   auto compute_unit = [&](const Cursor& cc, int st) {
@@ -393,34 +403,42 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeParams 
     float t[KB][16];
     const int dl = p0 + tq - j0 - 4 * hf - 32 * kb_lo;  // distance of this lane's first key
     const int weff = cc.si.weff;
+    const bool fresh = m_run == kNegInf;
+    const float m_ref = fresh ? 0.f : m_run;
     float mx;
     if (saturated) {
-      mx = need_mask ? logits(std::true_type{}, std::true_type{}, sacc, bs_lds, t, dl, weff)
-                     : logits(std::true_type{}, std::false_type{}, sacc, bs_lds, t, dl, weff);
+      mx = need_mask ? logits(std::true_type{}, std::true_type{}, sacc, bs_lds, t, dl, weff, m_ref)
+                     : logits(std::true_type{}, std::false_type{}, sacc, bs_lds, t, dl, weff, m_ref);
     } else {
-      mx = need_mask ? logits(std::false_type{}, std::true_type{}, sacc, bs_lds, t, dl, weff)
-                     : logits(std::false_type{}, std::false_type{}, sacc, bs_lds, t, dl, weff);
+      mx = need_mask ? logits(std::false_type{}, std::true_type{}, sacc, bs_lds, t, dl, weff, m_ref)
+                     : logits(std::false_type{}, std::false_type{}, sacc, bs_lds, t, dl, weff, m_ref);
     }
-    // online softmax, maximum raised lazily
-    mx = half_swap_max(mx);
-    const bool raise = mx > m_run + kRescaleSlack;
+    // online softmax: the running maximum is raised only when a row's maximum exceeds it
+    // by more than the slack (or on the row's first visible key), rescaling O, the
+    // normaliser and this unit's logits
+    const bool raise = fresh ? (mx > kNegInf) : (mx > kRescaleSlack);
     if (__builtin_amdgcn_ballot_w64(raise)) {
-      const float alpha = raise ? fast_exp2(m_run - mx) : 1.f;
-      m_run = raise ? mx : m_run;
+      const float delta = raise ? mx : 0.f;
+      const float m_new = m_ref + delta;
+      const float alpha = raise ? fast_exp2(m_run - m_new) : 1.f;
+      m_run = raise ? m_new : m_run;
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+#pragma unroll
+      for (int i = 0; i < KB; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) t[i][r] -= delta;
     }
-    const float msub = (m_run == kNegInf) ? 0.f : m_run;
     float lsum = 0.f;
     u32x4_t pk[KB][2];
 #pragma unroll
     for (int i = 0; i < KB; ++i) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        t[i][r] = fast_exp2(t[i][r] - msub);
+        t[i][r] = fast_exp2(t[i][r]);
         lsum += t[i][r];
       }
 #pragma unroll
