@@ -8,11 +8,13 @@ other workloads (fp32 tiny prefill, 32k chunked prefill, batch-64 paged decode, 
 9-query verify), each timed the same way: prefill in TFLOP/s against the bf16 MFMA peak,
 decode in KV GB/s (bytes the method must move) against the HBM peak.
 
-Timing: W untimed warm-up steps, then exactly K steps between two hipEvents recorded on
-the stream the kernels are launched on, with a device synchronisation on both sides.
+Timing: the step repeated, untimed, for at least S ms of wall clock (the GPU raises its
+clock over its first tens of milliseconds under load; S 0 skips this), then W untimed
+warm-up steps, then exactly K steps between two hipEvents recorded on the stream the
+kernels are launched on, with a device synchronisation on both sides.
 The CPU oracle (fp64) is timed on a bounded sample of the headline workload.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads a,b,...]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-ms S] [--workloads a,b,...]
                        [--no-cpu-baseline] [--only HEADLINE]
 """
 from __future__ import annotations
@@ -189,9 +191,23 @@ class DecodeRun:
         del self.q, self.kc, self.vc, self.bt, self.ctx, self.win, self.bias, self.out, self.lse, self.ws
 
 
-def time_steps(run, torch, steps: int, warmup: int):
+def settle_clock(run, torch, stream, ms: float) -> int:
+    """Repeat the step, untimed, for at least `ms` milliseconds of wall clock."""
+    if ms <= 0:
+        return 0
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < ms / 1e3:
+        for _ in range(8):
+            run.step(stream)
+        n += 8
+        torch.cuda.synchronize()
+    return n
+
+
+def time_steps(run, torch, steps: int, warmup: int, settle_ms: float = 0.0):
     """Average seconds per step over exactly `steps` steps, hipEvents on the launch stream."""
     stream = torch.cuda.current_stream()
+    settle_clock(run, torch, stream, settle_ms)
     for _ in range(warmup):
         run.step(stream)
     torch.cuda.synchronize()
@@ -235,6 +251,8 @@ def main(argv=None) -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle-ms", type=float, default=200.0,
+                    help="untimed repetition of the step before the warm-up, in ms of wall clock")
     ap.add_argument("--workloads", default=",".join(ALL_WORKLOADS),
                     help="comma-separated workloads to time besides the headline")
     ap.add_argument("--only-headline", action="store_true", help="time only the headline workload")
@@ -282,7 +300,7 @@ def main(argv=None) -> int:
         cls = DecodeRun if args.only in ("paged_decode_b64", "mtp_verify_1m") else PrefillRun
         run = cls(args.only, torch, rb, synth, dev)
         torch.cuda.synchronize()
-        sec = time_steps(run, torch, args.steps, args.warmup)
+        sec = time_steps(run, torch, args.steps, args.warmup, args.settle_ms)
         res = result_of(run, sec)
         log(f"[bench] {args.only}: {res['ms_per_step']:.4f} ms/step, {res['value']} {run.unit}")
         print(json.dumps(res), flush=True)
@@ -299,7 +317,7 @@ def main(argv=None) -> int:
         run = cls(name, torch, rb, synth, dev)
         log(f"[bench] {name}: inputs on device in {time.time() - t0:.1f} s; timing {args.steps} steps")
         torch.cuda.synchronize()
-        sec = time_steps(run, torch, args.steps, args.warmup)
+        sec = time_steps(run, torch, args.steps, args.warmup, args.settle_ms)
         if not run.finite():
             raise RuntimeError(f"{name}: non-finite output")
         res = result_of(run, sec)
@@ -324,6 +342,7 @@ def main(argv=None) -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "clock_settle_ms": args.settle_ms,
         "ms_per_step": h["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",

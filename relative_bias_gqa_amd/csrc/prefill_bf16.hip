@@ -29,8 +29,8 @@
 //     Q resident in registers), the other runs its softmax half-step on the vector ALU:
 //     logits in log2 units with the running maximum in the same FMA, the causal / window
 //     mask only on edge tiles, an online softmax whose maximum is only raised when a row's
-//     maximum grows by more than 8 (log2 units), P rounded to bf16, and the next tile's
-//     bias seeds.  V is read transposed from LDS (ds_read_b64_tr_b16).
+//     maximum grows by more than 8 (log2 units), P rounded to bf16; one workgroup
+//     barrier per tile.  V is read transposed from LDS (ds_read_b64_tr_b16).
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -333,20 +333,18 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   };
 
   // ---- key loop: two wave groups in ping-pong -------------------------------------
-  // Waves 0-3 and 4-7 (one of each on every SIMD) run the same code: per tile t, an MFMA
-  // half-step (P.V of tile t - 1, then S of tile t) and a softmax half-step (tile t, then
-  // the seeds of tile t + 1), each after a workgroup barrier.  Group 1 passes one extra
-  // barrier first, so it runs one half-step behind: while one wave of a SIMD feeds the
-  // matrix cores, the other runs the softmax on the vector ALU and its LDS reads.
-  // Barrier k: group 0 starts its MFMA half of tile k / 2 after even k, group 1 after odd
-  // k.  Tile t + 1 must be whole in LDS at barrier 2 t + 1 (its seeds are read after it):
-  // group 0 waits for its share before its barrier after MFMA half t, group 1 before its
-  // barrier ahead of MFMA half t.  The stage of tile t - 2 (last read by group 1's P.V
-  // of it, before barrier 2 t) is refilled with tile t + 2 right after barrier 2 t: by
-  // group 0 after its barrier ahead of MFMA half t, by group 1 after its barrier ahead
-  // of softmax half t - 1.
+  // Waves 0-3 and 4-7 (one of each on every SIMD) run the same code per tile t: read the
+  // seeds of tile t, an MFMA half-step (P.V of tile t - 1, then S of tile t), a softmax
+  // half-step (tile t).  There is one workgroup barrier per tile; barrier t means "tile t
+  // is whole in LDS" (every wave waited for its share of it first), and right after it
+  // each wave starts its share of tile t + 2, into the stage of tile t - 2.  Group 0
+  // passes barrier t before its MFMA half of tile t, group 1 after it (and barrier 0 ahead
+  // of everything), so between barriers t and t + 1 group 0 runs MFMA(t) then softmax(t)
+  // while group 1 runs softmax(t - 1) then MFMA(t): the two waves of a SIMD take turns on
+  // the matrix cores and the vector ALU.  Every read of a stage falls between the barrier
+  // that completes its tile and the barrier that refills it, two tiles later.
   const bool g1 = wave >= kWaves / 2;
-  const int prologue = min(g1 ? 3 : 2, n_tiles);
+  const int prologue = min(2, n_tiles);
   for (int i = 0; i < prologue; ++i) issue_tile(kt_begin + i, i);
   // P of "tile -1" is zero and the V rows of the last stage are zeroed, so that the first
   // MFMA half-step can run its P.V like every other (it adds nothing)
@@ -360,35 +358,20 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
     vlast[tid + kThreads] = zero_u32x4();
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // before the first barrier
   }
-  if (g1) {
-    if (n_tiles >= 3) vm_wait<2 * kLoadsPerStage>();  // tile 0
-    else if (n_tiles == 2) vm_wait<kLoadsPerStage>();
+  auto tile_barrier = [&](int j) {
+    if (j + 1 < n_tiles) vm_wait<kLoadsPerStage>();  // tile j; tile j + 1 may still be loading
     else vm_wait<0>();
-    wg_barrier();
-    load_seeds(0);
-  } else {
-    if (n_tiles >= 2) vm_wait<kLoadsPerStage>();  // tile 0
-    else vm_wait<0>();
-  }
+    wg_barrier_reads_in_flight();
+    if (j + 2 < n_tiles) issue_tile(kt_begin + j + 2, (j + 2) % kStages);
+  };
+  if (g1 && n_tiles > 0) tile_barrier(0);
   for (int t = 0; t < n_tiles; ++t) {
-    if (g1) {
-      if (t + 2 < n_tiles) vm_wait<kLoadsPerStage>();  // tile t + 1; t + 2 may still be loading
-      else vm_wait<0>();
-    }
-    wg_barrier_reads_in_flight();
-    if (!g1 && t + 2 < n_tiles) issue_tile(kt_begin + t + 2, (t + 2) % kStages);
-    if (!g1 && t == 0) load_seeds(0);
+    if (!g1) tile_barrier(t);
+    load_seeds(t % kStages);
     mfma_half(t % kStages, (t + kStages - 1) % kStages);
-    if (!g1) {
-      if (t + 2 < n_tiles) vm_wait<kLoadsPerStage>();  // tile t + 1; t + 2 may still be loading
-      else vm_wait<0>();
-    }
-    wg_barrier_reads_in_flight();
-    if (g1 && t + 3 < n_tiles) issue_tile(kt_begin + t + 3, (t + 3) % kStages);
+    if (g1 && t + 1 < n_tiles) tile_barrier(t + 1);
     softmax_half(kt_begin + t);
-    load_seeds((t + 1) % kStages);  // (unused after the last tile)
   }
-  if (!g1) wg_barrier();
   if (n_tiles > 0) {
     // P.V of the last tile
     const uint32_t vz = vz0 + ((n_tiles - 1) % kStages) * kStageBytes;
