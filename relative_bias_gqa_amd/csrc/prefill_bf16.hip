@@ -34,8 +34,6 @@
 #include "device_common.hpp"
 #include "launch.hpp"
 
-#include <type_traits>
-
 namespace rattn {
 namespace {
 
@@ -186,6 +184,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   }
   // this wave's bias slice: seeds at sb0 + 4 (32 kb + 8 (r >> 2) + (r & 3))
   const uint32_t sb0 = ring_base + 2 * kKVBytes + wave * (kSliceFloats * 4) + 4 * (31 - col + 4 * hf);
+  const uint32_t sl0 = ring_base + 2 * kKVBytes + wave * (kSliceFloats * 4) + 8 * lane;
 
   // ---- running state ---------------------------------------------------------------
   f32x16_t o[4];
@@ -199,7 +198,24 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   // The S accumulators of the tile in stage st start from the wave's bias slice (scaled
   // to score units in the MFMA half-step).  Distances beyond R - 1 are clamped in the
   // slice, so a tile entirely past them is seeded with r[h, R - 1] like any other.
-  auto load_seeds = [&](int st) {
+  // The seeds of the tile in stage st: this wave's whole slice is first scaled by sqrt(128)
+  // in place (two entries per lane: two multiplies instead of one per seed), then the 32
+  // seeds are read; the LDS serves one wave's requests in order, so the reads see the
+  // scaled entries.  Runs once per tile, inside the MFMA half-step: the slice read goes
+  // out before the first operand reads, the rest after the second group of MFMAs.
+  float sl_e0, sl_e1;
+  uint32_t sl_addr;
+  auto seeds_begin = [&](int st) {
+    sl_addr = sl0 + st * kStageBytes;
+    asm volatile("" : "+v"(sl_addr));
+    const lds_f32_t* ps = (const lds_f32_t*)(size_t)sl_addr;
+    sl_e0 = ps[0];
+    sl_e1 = ps[1];
+  };
+  auto seeds_end = [&](int st) {
+    lds_f32_t* ps = (lds_f32_t*)(size_t)sl_addr;
+    ps[0] = sl_e0 * kSqrtD;
+    ps[1] = sl_e1 * kSqrtD;
     // one base register per call, the rest immediate offsets (kept from being hoisted
     // out of the loop as 32 separate addresses)
     uint32_t base = sb0 + st * kStageBytes;
@@ -213,8 +229,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   // MFMA half-step: O^T += V^T P^T for the previous tile (stage st_prev), then
   // S^T = sqrt(128) r + K Q^T for the tile in stage st on the seeded accumulators.  The
   // 32 MFMAs run as eight groups of four (P.V keys 16 G.., then S k-steps in pairs); each
-  // group's operands are read from LDS two groups ahead, and the seeds are scaled to score
-  // units while the P.V groups run.
+  // group's operands are read from LDS two groups ahead.
   auto mfma_half = [&](int st, int st_prev) {
     const uint32_t so = st * kStageBytes;
     const uint32_t kx = kx0 + so;
@@ -236,6 +251,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
       }
     };
     u32x4_t op[3][4];
+    seeds_begin(st);
+    __builtin_amdgcn_sched_barrier(0);
     load(0, op[0]);
     load(1, op[1]);
     __builtin_amdgcn_sched_barrier(0);
@@ -246,8 +263,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
       if (gi < 4) {
 #pragma unroll
         for (int db = 0; db < 4; ++db) o[db] = mfma_32x32x16(cur[db], pk[gi >> 1][gi & 1], o[db]);
-        if (gi == 2) s[0] *= kSqrtD;
-        if (gi == 3) s[1] *= kSqrtD;
+        // the seeds (needed from group 4 on); the slice read went out before the operands
+        // of groups 0 and 1, so it has arrived
+        if (gi == 1) seeds_end(st);
       } else {
         // alternate the two key blocks so that consecutive MFMAs are independent
 #pragma unroll
@@ -264,36 +282,26 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   // normaliser (the log-sum-exp needs that accuracy) and rounded to bf16 for P.V.
   auto softmax_half = [&](int kt) {
     const int j0 = kt * kBK;
+    if (j0 + kBK - 1 > pw0 || j0 < pw_last - Weff + 1) {
+      // edge tile: mask the raw scores (in place; -inf stays -inf through the logit FMA).
+      // Key 32 kb + 8 (r >> 2) + 4 hf + (r & 3) is at distance dl - c(kb, r) from this
+      // lane's query; visible iff 0 <= distance < Weff (Weff is huge without a window).
+      const int dl = pw0 + col - j0 - 4 * hf;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int c = 32 * kb + 8 * (r >> 2) + (r & 3);
+          s[kb][r] = (uint32_t)(dl - c) < (uint32_t)Weff ? s[kb][r] : kNegInf;
+        }
+    }
     const bool fresh = m_run == kNegInf;
     const float m_ref = fresh ? 0.f : m_run;
+    const float raise_above = fresh ? kNegInf : kRescaleSlack;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][r] = fmaf(s[kb][r], p.scale_log2, -m_ref);
-    const bool causal = j0 + kBK - 1 > pw0;
-    const bool window = j0 < pw_last - Weff + 1;
-    if (causal || window) {
-      // the distance of key 32 kb + 8 (r >> 2) + 4 hf + (r & 3) from this lane's query
-      // is dl - c(kb, r)
-      const int dl = pw0 + col - j0 - 4 * hf;
-      if (!window) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int c = 32 * kb + 8 * (r >> 2) + (r & 3);
-            s[kb][r] = c <= dl ? s[kb][r] : kNegInf;
-          }
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int c = 32 * kb + 8 * (r >> 2) + (r & 3);
-            s[kb][r] = (uint32_t)(dl - c) < (uint32_t)Weff ? s[kb][r] : kNegInf;
-          }
-      }
-    }
     float ma = max3f(s[0][0], s[0][1], s[0][2]);
     float mb = max3f(s[1][0], s[1][1], s[1][2]);
 #pragma unroll
@@ -302,7 +310,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
       mb = max3f(mb, s[1][r], s[1][r + 1]);
     }
     const float mx = half_swap_max3(max3f(ma, mb, s[0][15]), s[1][15]);
-    const bool raise = fresh ? (mx > kNegInf) : (mx > kRescaleSlack);
+    const bool raise = mx > raise_above;
     if (__builtin_amdgcn_ballot_w64(raise)) {
       const float delta = raise ? mx : 0.f;
       const float m_new = m_ref + delta;
@@ -314,7 +322,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
       s[0] -= delta;
       s[1] -= delta;
     }
-    float lsum = 0.f;
+    float lsum;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -324,7 +332,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
         for (int e = 0; e < 4; ++e) {
           const int r = 8 * half + 2 * e;
           const float e0 = fast_exp2(s[kb][r]), e1 = fast_exp2(s[kb][r + 1]);
-          lsum += e0 + e1;
+          lsum = (kb | half | e) ? lsum + (e0 + e1) : e0 + e1;
           w[e] = pack_bf16x2(e0, e1);
         }
         pk[kb][half] = w;
@@ -367,7 +375,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   if (g1 && n_tiles > 0) tile_barrier(0);
   for (int t = 0; t < n_tiles; ++t) {
     if (!g1) tile_barrier(t);
-    load_seeds(t % kStages);
     mfma_half(t % kStages, (t + kStages - 1) % kStages);
     if (g1 && t + 1 < n_tiles) tile_barrier(t + 1);
     softmax_half(kt_begin + t);
