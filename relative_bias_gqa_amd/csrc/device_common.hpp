@@ -165,6 +165,36 @@ __device__ __forceinline__ void dma4(const void* g, uint32_t lds_byte_addr) {
       : "memory");
 }
 
+// The same with a wave-uniform base address in SGPRs and a 32-bit per-lane byte offset,
+// so that issuing a load needs no vector ALU work.
+__device__ __forceinline__ void dma16s(const void* base, uint32_t off, uint32_t lds_byte_addr) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_byte_addr);
+  uint32_t save;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "v"(off), "s"(base), "s"(m0v)
+      : "memory");
+}
+
+__device__ __forceinline__ void dma4s(const void* base, uint32_t off, uint32_t lds_byte_addr) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_byte_addr);
+  uint32_t save;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "v"(off), "s"(base), "s"(m0v)
+      : "memory");
+}
+
 // Wait until at most N vector-memory operations of this wave are outstanding.
 template <int N>
 __device__ __forceinline__ void vm_wait() {

@@ -137,31 +137,50 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   const float* bias_row = p.bias + (size_t)h * p.R;
   const uint32_t ring_base = lds_addr(ring);
 
+  // Interior tiles issue from a scalar base plus fixed per-lane offsets (no vector ALU
+  // work); the last tile (keys past Lk read a zero row) and bias halves that are only
+  // partly clamped compute per-lane addresses.
+  const uint32_t boff = 4u * (63 - lane);  // bias entry lo + 63 - lane of a 64-entry half
+  const uint32_t zoff = 0;
   auto issue_tile = [&](int kt, int st) {
     const int j0 = kt * kBK;
     const size_t base = (size_t)j0 * p.Hkv * 256;
     const uint32_t kdst = ring_base + st * kStageBytes + wave * 2048;
     const uint32_t vdst = kdst + kKVBytes;
     const uint32_t bdst = ring_base + st * kStageBytes + 2 * kKVBytes + wave * (kSliceFloats * 4);
-    const bool tail = j0 + kBK > p.Lk;
+    if (j0 + kBK <= p.Lk) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const unsigned char* gk = kc_bytes + base + koff[i];
-      const unsigned char* gv = vc_bytes + base + voff[i];
-      if (tail && j0 + ktok[i] >= p.Lk) {
-        gk = zero_bytes + kz[i];
-        gv = zero_bytes + vz[i];
+      for (int i = 0; i < 2; ++i) {
+        dma16s(kc_bytes + base, koff[i], kdst + i * 1024);
+        dma16s(vc_bytes + base, voff[i], vdst + i * 1024);
       }
-      dma16(gk, kdst + i * 1024);
-      dma16(gv, vdst + i * 1024);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const unsigned char* gk = kc_bytes + base + koff[i];
+        const unsigned char* gv = vc_bytes + base + voff[i];
+        if (j0 + ktok[i] >= p.Lk) {
+          gk = zero_bytes + kz[i];
+          gv = zero_bytes + vz[i];
+        }
+        dma16(gk, kdst + i * 1024);
+        dma16(gv, vdst + i * 1024);
+      }
     }
     // this wave's bias slice, stored by decreasing distance:
-    // entry y = r[h, clamp(pw0 - j0 + 31 - y, 0, R - 1)]
-    const int d0 = pw0 - j0 + 31;
+    // entry y = r[h, clamp(pw0 - j0 + 31 - y, 0, R - 1)]; half i holds y = 64 i + lane,
+    // distances lo + 63 - lane with lo = pw0 - j0 - 32 - 64 i
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int d = min(max(d0 - 64 * i - lane, 0), p.R - 1);
-      dma4(bias_row + d, bdst + i * 256);
+      const int lo = pw0 - j0 - 32 - 64 * i;
+      if (lo >= 0 && lo + 63 <= p.R - 1) {
+        dma4s(bias_row + lo, boff, bdst + i * 256);
+      } else if (lo >= p.R - 1) {
+        dma4s(bias_row + (p.R - 1), zoff, bdst + i * 256);
+      } else {
+        const int d = min(max(lo + 63 - lane, 0), p.R - 1);
+        dma4(bias_row + d, bdst + i * 256);
+      }
     }
   };
 
