@@ -140,20 +140,26 @@ struct PrefillSplit {
   size_t lse_off = 0, o_off = 0, ws_bytes = 0;
 };
 
-constexpr int kDispatchUnits = 256;      // compute units of an MI355X
-// fixed costs in key-tile times: a workgroup's prologue and epilogue; a piece's, including
-// writing its partial and its share of the merge (fitted to sliding-window prefill timings
-// of 2-, 3- and 4-way splits on an MI355X)
-constexpr double kWgOverhead = 1.0;
-constexpr double kPieceOverhead = 4.5;
+// Workgroup i of a launch runs on XCD i % 8 of an MI355X, each XCD filling its 32 compute
+// units from its own share of the grid in order.
+constexpr int kXcds = 8;
+constexpr int kUnitsPerXcd = 32;
+// fixed costs in key-tile times: a workgroup's prologue, epilogue and the gap before the
+// next workgroup on its unit; a piece's, including writing its partial and its share of
+// the merge (measured per workgroup on sliding-window prefill on an MI355X)
+constexpr double kWgOverhead = 2.5;
+constexpr double kPieceOverhead = 5.0;
 
-// finish time of the last workgroup, jobs started in order on the least-loaded unit
+// finish time of the last workgroup: the jobs, in grid order, go to XCDs round robin and
+// within an XCD to the least-loaded unit
 double simulate_dispatch(const std::vector<double>& jobs) {
-  std::priority_queue<double, std::vector<double>, std::greater<double>> units;
-  for (int i = 0; i < kDispatchUnits; ++i) units.push(0.0);
+  std::vector<std::priority_queue<double, std::vector<double>, std::greater<double>>> xcd(kXcds);
+  for (auto& units : xcd)
+    for (int i = 0; i < kUnitsPerXcd; ++i) units.push(0.0);
   double end = 0.0;
-  for (double j : jobs) {
-    const double t = units.top() + j;
+  for (size_t i = 0; i < jobs.size(); ++i) {
+    auto& units = xcd[i % kXcds];
+    const double t = units.top() + jobs[i];
     units.pop();
     units.push(t);
     end = std::max(end, t);
@@ -187,14 +193,16 @@ PrefillSplit plan_prefill_split_uncached(const rattn::PrefillParams& p, int dtyp
   }
   const long long per_tile = (long long)p.B * p.Hkv * p.n_hg;
   if ((long long)nt * per_tile * rattn::kMaxPieces > 0x7fffffffLL) return PrefillSplit{};
+  // job sizes in grid order, pieces mapped to workgroups as the kernel does
   auto jobs_of = [&](int n_split, int parts) {
     std::vector<double> jobs;
-    for (int t = nt - 1; t >= nt - n_split; --t)
-      for (long long r = 0; r < per_tile; ++r)
-        for (int q = 0; q < parts; ++q) {
-          const int lo = keys[t] * q / parts, hi = keys[t] * (q + 1) / parts;
-          jobs.push_back(hi - lo + kPieceOverhead);
-        }
+    const long long n_jobs = (long long)n_split * per_tile;
+    for (long long w = 0; w < n_jobs * parts; ++w) {
+      int job, piece;
+      rattn::prefill_piece_of(w, n_jobs, parts, &job, &piece);
+      const int k = keys[nt - 1 - (int)(job / per_tile)];
+      jobs.push_back(k * (piece + 1) / parts - k * piece / parts + kPieceOverhead);
+    }
     for (int t = nt - 1 - n_split; t >= 0; --t)
       for (long long r = 0; r < per_tile; ++r) jobs.push_back(keys[t] + kWgOverhead);
     return jobs;
@@ -203,7 +211,7 @@ PrefillSplit plan_prefill_split_uncached(const rattn::PrefillParams& p, int dtyp
   for (int t = 0; t < nt; ++t) total += (keys[t] + kWgOverhead) * per_tile;
   double best = simulate_dispatch(jobs_of(0, 1));
   // a grid that already finishes within 5 % of an even spread is left alone
-  if (best <= 1.05 * total / kDispatchUnits) return PrefillSplit{};
+  if (best <= 1.05 * total / (kXcds * kUnitsPerXcd)) return PrefillSplit{};
   int best_split = 0, best_parts = 1;
   const int kmax = keys[nt - 1];
   for (int parts = 2; parts <= 4; ++parts)

@@ -32,7 +32,26 @@ struct PrefillParams {
   int* ws_cnt;    // [n_split * B * Hkv * n_hg] finished pieces; zero between calls
 };
 
-constexpr int kMaxPieces = 8;  // largest `parts` of a prefill key-range split
+constexpr int kMaxPieces = 8;
+
+// Workgroup w (< n_jobs * parts) of a split prefill grid takes piece *piece of job *job.
+// Workgroup w runs on XCD w % 8, so in each group of 8 * parts workgroups (8 jobs),
+// workgroup x + 8 k takes piece k of job x: the pieces of a job share an XCD, and the
+// merges (done by whichever piece of a job finishes last) spread over all XCDs.  A last,
+// partial group keeps the pieces of a job adjacent.
+__host__ __device__ inline void prefill_piece_of(long long w, long long n_jobs, int parts, int* job, int* piece) {
+  const long long full = n_jobs / 8 * 8 * parts;
+  if (w < full) {
+    const long long g = w / (8 * parts);
+    const int r = (int)(w - g * 8 * parts);
+    *job = (int)(g * 8 + r % 8);
+    *piece = r / 8;
+  } else {
+    const long long r = w - full;
+    *job = (int)(n_jobs / 8 * 8 + r / parts);
+    *piece = (int)(r % parts);
+  }
+}  // largest `parts` of a prefill key-range split
 
 hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream);
 hipError_t launch_prefill_fp32(const PrefillParams& p, hipStream_t stream);

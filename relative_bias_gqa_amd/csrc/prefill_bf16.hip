@@ -70,8 +70,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   const int per_tile = p.B * p.Hkv * p.n_hg;
   const int n_piece_wgs = p.n_split * per_tile * p.parts;
   const bool is_piece = (int)blockIdx.x < n_piece_wgs;
-  const int job = is_piece ? (int)blockIdx.x / p.parts : (int)blockIdx.x - n_piece_wgs + p.n_split * per_tile;
-  const int piece = is_piece ? (int)blockIdx.x % p.parts : 0;
+  int job = (int)blockIdx.x - n_piece_wgs + p.n_split * per_tile, piece = 0;
+  if (is_piece) prefill_piece_of(blockIdx.x, (long long)p.n_split * per_tile, p.parts, &job, &piece);
   const int tile = p.n_tok_tiles - 1 - job / per_tile;
   const int rem = job % per_tile;
   const int hg = rem % p.n_hg;
@@ -443,24 +443,27 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   // depend on which one that is), and writes the output.
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const float lse2 = l_tot > 0.f ? m_run + __log2f(l_tot) : kNegInf;
-  // Partial layout (per piece, per wave): register r of block db, then the lane -- each
-  // dword store or load of a wave covers 256 consecutive bytes.
+  // Partial layout (per piece, per wave): 16-byte chunk c = 4 db + q of every lane, then
+  // the lane -- each 16-byte store or load of a wave covers 1 KB of consecutive bytes.
   const int wrow = wave * 32 + col;  // row of the workgroup, 0..255
-  auto part_o = [&](size_t slot) { return p.ws_o + ((slot * kWaves + wave) * 32 * kHeadDim + lane); };
-  // The partials are written and read with device-coherent (agent-scope) accesses, which
-  // go to the coherence point directly: a device-scope fence instead would write back and
-  // invalidate this XCD's whole L2, and with it the K/V tiles of every other workgroup.
+  const size_t my_slot = (size_t)job * p.parts + piece;  // piece j of a job: slot job * parts + j
+  auto part_o = [&](size_t slot) { return p.ws_o + ((slot * kWaves + wave) * 32 * kHeadDim + 4 * lane); };
+  // The partials are written and read with device-coherent accesses (the sc1 bit, as a
+  // relaxed agent-scope atomic access of this target has it), which go to the coherence
+  // point directly: a device-scope fence instead would write back and invalidate this
+  // XCD's whole L2, and with it the K/V tiles of every other workgroup.
   auto st_dev = [](float* a, float v) { __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
   auto ld_dev = [](const float* a) { return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
   {
-    float* wo = part_o(blockIdx.x);
+    float* wo = part_o(my_slot);
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) st_dev(wo + (16 * db + 4 * q + i) * 64, o[db][4 * q + i] * inv);
-    if (hf == 0) st_dev(p.ws_lse + (size_t)blockIdx.x * kWgRows + wrow, lse2);
+      for (int q = 0; q < 4; ++q) {
+        const f32x4_t v = {o[db][4 * q] * inv, o[db][4 * q + 1] * inv, o[db][4 * q + 2] * inv, o[db][4 * q + 3] * inv};
+        asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(wo + (4 * db + q) * 256), "v"(v) : "memory");
+      }
+    if (hf == 0) st_dev(p.ws_lse + my_slot * kWgRows + wrow, lse2);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's partials have landed
   __syncthreads();
@@ -490,14 +493,30 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
     if (j >= p.parts) break;
     const float w = lse_j[j] == kNegInf ? 0.f : fast_exp2(lse_j[j] - mmax);
     wsum += w;
-    const float* src = part_o(slot0 + j);
+    if (j == piece) {
+      // this workgroup's own piece, from registers: the same values it stored
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
+        for (int r = 0; r < 16; ++r) acc[db][r] = fmaf(w, o[db][r] * inv, acc[db][r]);
+    } else {
+      const float* src = part_o(slot0 + j);
+      f32x4_t x[16];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          acc[db][4 * q + i] = fmaf(w, ld_dev(src + (16 * db + 4 * q + i) * 64), acc[db][4 * q + i]);
+      for (int c = 0; c < 16; ++c)
+        asm volatile("global_load_dwordx4 %0, %1, off sc1" : "=v"(x[c]) : "v"(src + c * 256) : "memory");
+      asm volatile("s_waitcnt vmcnt(0)"
+                   : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]), "+v"(x[7]),
+                     "+v"(x[8]), "+v"(x[9]), "+v"(x[10]), "+v"(x[11]), "+v"(x[12]), "+v"(x[13]), "+v"(x[14]), "+v"(x[15])
+                   :
+                   : "memory");
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[db][4 * q + i] = fmaf(w, x[4 * db + q][i], acc[db][4 * q + i]);
+    }
   }
   const float winv = 1.f / wsum;
 #pragma unroll
