@@ -488,12 +488,26 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeParams 
   flush_segment(seg);
 }
 
-// One workgroup per (segment, row): merge the pieces of the segment.
+// (max, sum of 2^(x - max)) pairs: the combination of two partial log2-sum-exps.
+__device__ __forceinline__ void lse_combine(float& m, float& z, float m2, float z2) {
+  const float mm = fmaxf(m, m2);
+  if (mm == kNegInf) return;  // both empty
+  z = (m == kNegInf ? 0.f : z * fast_exp2(m - mm)) + (m2 == kNegInf ? 0.f : z2 * fast_exp2(m2 - mm));
+  m = mm;
+}
+
+constexpr int kMergeLse = 2048;  // log2-sum-exps of a segment kept in LDS for the second pass
+
+// One workgroup per (segment, row): merge the pieces of the segment.  One pass over the
+// pieces' log2-sum-exps (an online maximum and sum, combined across lanes and waves), then
+// one over their outputs with eight pieces' loads in flight per thread.
 __global__ __launch_bounds__(kThreads) void decode_merge_kernel(DecodeParams p) {
-  __shared__ float red[kThreads];
-  __shared__ int ired[2][kThreads];
+  __shared__ float lse_s[kMergeLse];
+  __shared__ float red[2][kThreads / 64];
+  __shared__ int ired[2][kThreads / 64];
   __shared__ f32x4_t acc_lds[8][32];
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int seg = blockIdx.x / p.rows;
   const int r_row = blockIdx.x - seg * p.rows;
   const int b = seg / p.KH;
@@ -506,20 +520,27 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(DecodeParams p) 
     total += n;
     if (bb < b) before += n;
   }
-  ired[0][tid] = before;
-  ired[1][tid] = total;
-  __syncthreads();
-  for (int s = kThreads / 2; s > 0; s >>= 1) {
-    if (tid < s) {
-      ired[0][tid] += ired[0][tid + s];
-      ired[1][tid] += ired[1][tid + s];
-    }
-    __syncthreads();
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    before += __shfl_xor(before, off);
+    total += __shfl_xor(total, off);
   }
-  const long long units = (long long)ired[1][0] * p.KH;
+  if (lane == 0) {
+    ired[0][wave] = before;
+    ired[1][wave] = total;
+  }
+  __syncthreads();
+  before = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < kThreads / 64; ++w) {
+    before += ired[0][w];
+    total += ired[1][w];
+  }
+  const long long units = (long long)total * p.KH;
   const long long P = min((long long)p.P, units);
   const int nch = seq_info(p, b).nch;
-  const long long us = (long long)ired[0][0] * p.KH + (long long)kh * nch;
+  const long long us = (long long)before * p.KH + (long long)kh * nch;
   const long long ue = us + nch;
   // workgroup w covers units [w units / P, (w + 1) units / P)
   const int w_first = (int)(((us + 1) * P + units - 1) / units) - 1;
@@ -530,33 +551,45 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(DecodeParams p) 
     return ((size_t)(w_first + i / p.KS + seg) * p.KS + (i % p.KS)) * p.rows + r_row;
   };
 
-  float m = kNegInf;
-  for (int i = tid; i < n_pieces; i += kThreads) m = fmaxf(m, p.ws_lse[slot_row(i)]);
-  red[tid] = m;
-  __syncthreads();
-  for (int s = kThreads / 2; s > 0; s >>= 1) {
-    if (tid < s) red[tid] = fmaxf(red[tid], red[tid + s]);
-    __syncthreads();
+  float m = kNegInf, z = 0.f;
+  for (int i = tid; i < n_pieces; i += kThreads) {
+    const float l = p.ws_lse[slot_row(i)];
+    if (i < kMergeLse) lse_s[i] = l;
+    lse_combine(m, z, l, 1.f);
   }
-  const float M = red[0];
-  __syncthreads();
-  float z = 0.f;
-  for (int i = tid; i < n_pieces; i += kThreads) z += fast_exp2(p.ws_lse[slot_row(i)] - M);
-  red[tid] = z;
-  __syncthreads();
-  for (int s = kThreads / 2; s > 0; s >>= 1) {
-    if (tid < s) red[tid] += red[tid + s];
-    __syncthreads();
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const float m2 = __shfl_xor(m, off), z2 = __shfl_xor(z, off);
+    lse_combine(m, z, m2, z2);
   }
-  const float Z = red[0];
+  if (lane == 0) {
+    red[0][wave] = m;
+    red[1][wave] = z;
+  }
+  __syncthreads();
+  float M = red[0][0], Z = red[1][0];
+#pragma unroll
+  for (int w = 1; w < kThreads / 64; ++w) lse_combine(M, Z, red[0][w], red[1][w]);
+  auto lse_of = [&](int i) { return i < kMergeLse ? lse_s[i] : p.ws_lse[slot_row(i)]; };
 
   const int d4 = tid & 31, grp = tid >> 5;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  for (int i = grp; i < n_pieces; i += 8) {
+  int i = grp;
+  for (; i + 8 * 7 < n_pieces; i += 64) {
+    f32x4_t x[8];
+    float wt[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const size_t sr = slot_row(i + 8 * u);
+      x[u] = *(const f32x4_t*)(p.ws_o + sr * kHeadDim + 4 * d4);
+      wt[u] = fast_exp2(lse_of(i + 8 * u) - M);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc += wt[u] * x[u];
+  }
+  for (; i < n_pieces; i += 8) {
     const size_t sr = slot_row(i);
-    const float wgt = fast_exp2(p.ws_lse[sr] - M);
-    const f32x4_t x = *(const f32x4_t*)(p.ws_o + sr * kHeadDim + 4 * d4);
-    acc += wgt * x;
+    acc += fast_exp2(lse_of(i) - M) * *(const f32x4_t*)(p.ws_o + sr * kHeadDim + 4 * d4);
   }
   acc_lds[grp][d4] = acc;
   __syncthreads();
