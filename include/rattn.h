@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define RATTN_ABI_VERSION 3
+#define RATTN_ABI_VERSION 4
 
 enum rattn_status {
   RATTN_OK = 0,
@@ -52,11 +52,17 @@ enum rattn_status {
 enum rattn_dtype { RATTN_BF16 = 0, RATTN_FP32 = 1 };
 
 /*
- * Device workspace, in bytes, that rattn_prefill needs to split the key range of its
- * heaviest query tiles (0: these arguments never split; then rattn_prefill may be given
- * no workspace).  kv_splits as for rattn_prefill.  The plan is a pure function of the
- * arguments.  Returns 0 for invalid sizes.
+ * Device workspace, in bytes, that rattn_prefill uses for these arguments: for bf16, a
+ * 256-byte job queue, plus, where the plan splits the key range of its heaviest query
+ * tiles, per-tile counters and the pieces' partial results; for fp32, 0.  kv_splits as
+ * for rattn_prefill.  The plan is a pure function of the arguments.  Returns 0 for
+ * invalid sizes.
  *
+ * Why a queue: one workgroup fits on a compute unit (its K/V ring fills the LDS), so a
+ * grid of one workgroup per query tile leaves each unit idle while a finished workgroup's
+ * stores drain and the next one starts (~6 us per hand-over, measured).  With the queue
+ * the launch has one workgroup per compute unit, each taking the next query tile (or
+ * piece) as it finishes one.
  * Why a split: the query tiles of a long sliding-window (or long causal) prefill all walk
  * about as many keys as the longest one, and with about two tiles per compute unit the
  * last ones to start finish late.  Splitting the keys of the heaviest tiles into pieces
@@ -77,7 +83,8 @@ size_t rattn_prefill_workspace_bytes(int B, int Lq, int Lk, int Hq, int Hkv, int
  *   lse  [B, Lq, Hq]        fp32     device, written; may be NULL
  *   workspace               device scratch of workspace_bytes >=
  *                           rattn_prefill_workspace_bytes(...) bytes, or NULL with
- *                           workspace_bytes = 0 (then nothing is split)
+ *                           workspace_bytes = 0 (then one workgroup per query tile,
+ *                           nothing split: slower, same result)
  *
  * Query t of every sequence sits at absolute position Lk - Lq + t (bottom-right alignment:
  * a chunk of Lq new tokens whose own keys are the last Lq of the Lk keys), so Lq <= Lk.
@@ -87,10 +94,12 @@ size_t rattn_prefill_workspace_bytes(int B, int Lq, int Lk, int Hq, int Hkv, int
  * kv_splits: 0 = the library's plan (a split only where it shortens the launch), 1 = no
  * split, n in 2..8 = split every query tile with at least 2n key tiles of 64 into n pieces.
  * A split changes only the summation order of the result.
- * Workspace: its first bytes hold per-tile counters that must be zero when the workspace
- * is first used; every completed call leaves them zero again, so a workspace zero-filled
- * once can be reused by later calls of any size it is large enough for.  Calls that share
- * a workspace must not run concurrently.
+ * Workspace: its first bytes hold the job queue and per-tile counters, which must be zero
+ * when the workspace is first used; every completed call leaves them zero again, so a
+ * workspace zero-filled once can be reused by later calls of any size it is large enough
+ * for.  Calls that share a workspace must not run concurrently.  With or without a
+ * workspace, and whichever workgroup runs which tile, the result is the same bit for bit
+ * for a given plan.
  * B == 0 or Lq == 0 is a no-op returning RATTN_OK (pointers may then be NULL).
  * Status: INVALID_ARG for a null required pointer, negative sizes, Hq % Hkv != 0, Lq > Lk,
  * R < 1, kv_splits outside 0..8, workspace_bytes > 0 with a NULL workspace; WORKSPACE if

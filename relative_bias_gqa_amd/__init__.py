@@ -25,7 +25,7 @@ LIB_PATH = os.path.join(_HERE, "librattn.so")
 
 RATTN_OK, RATTN_ERR_INVALID_ARG, RATTN_ERR_UNSUPPORTED, RATTN_ERR_WORKSPACE, RATTN_ERR_HIP = 0, 1, 2, 3, 4
 RATTN_BF16, RATTN_FP32 = 0, 1
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 EXPORTED = ("rattn_prefill_workspace_bytes", "rattn_prefill", "rattn_decode_num_splits", "rattn_decode_workspace_bytes", "rattn_decode_paged",
             "rattn_last_error", "rattn_abi_version")

@@ -8,6 +8,7 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <atomic>
 #include <functional>
 #include <queue>
 #include <vector>
@@ -135,31 +136,29 @@ int prefill_tile_keys(const rattn::PrefillParams& p, int tile) {
   return (int)(ke - kb);
 }
 
+// Workspace of a bf16 prefill: [256 B: job queue] [split counters] [partial lse] [partial O]
 struct PrefillSplit {
   int n_split = 0, parts = 1;
-  size_t lse_off = 0, o_off = 0, ws_bytes = 0;
+  size_t cnt_off = 0, lse_off = 0, o_off = 0, ws_bytes = 0;
 };
+constexpr size_t kQueueBytes = 256;
 
-// Workgroup i of a launch runs on XCD i % 8 of an MI355X, each XCD filling its 32 compute
-// units from its own share of the grid in order.
-constexpr int kXcds = 8;
-constexpr int kUnitsPerXcd = 32;
-// fixed costs in key-tile times: a workgroup's prologue, epilogue and the gap before the
-// next workgroup on its unit; a piece's, including writing its partial and its share of
-// the merge (measured per workgroup on sliding-window prefill on an MI355X)
-constexpr double kWgOverhead = 2.5;
-constexpr double kPieceOverhead = 5.0;
+// With a queue, a launch has one workgroup per compute unit and each takes the next job
+// slot when it finishes one: the plan simulates that on the 256 compute units of an MI355X.
+constexpr int kDispatchUnits = 256;
+// fixed costs in key-tile times: a job's start (Q and the first tiles in flight) and
+// output; a piece's, including writing its partial and its share of the merge (measured
+// per workgroup on sliding-window prefill on an MI355X)
+constexpr double kWgOverhead = 1.5;
+constexpr double kPieceOverhead = 4.0;
 
-// finish time of the last workgroup: the jobs, in grid order, go to XCDs round robin and
-// within an XCD to the least-loaded unit
+// finish time of the last job, jobs started in order on the least-loaded unit
 double simulate_dispatch(const std::vector<double>& jobs) {
-  std::vector<std::priority_queue<double, std::vector<double>, std::greater<double>>> xcd(kXcds);
-  for (auto& units : xcd)
-    for (int i = 0; i < kUnitsPerXcd; ++i) units.push(0.0);
+  std::priority_queue<double, std::vector<double>, std::greater<double>> units;
+  for (int i = 0; i < kDispatchUnits; ++i) units.push(0.0);
   double end = 0.0;
-  for (size_t i = 0; i < jobs.size(); ++i) {
-    auto& units = xcd[i % kXcds];
-    const double t = units.top() + jobs[i];
+  for (double j : jobs) {
+    const double t = units.top() + j;
     units.pop();
     units.push(t);
     end = std::max(end, t);
@@ -169,19 +168,22 @@ double simulate_dispatch(const std::vector<double>& jobs) {
 
 PrefillSplit split_layout(const rattn::PrefillParams& p, int n_split, int parts) {
   PrefillSplit sp;
+  sp.cnt_off = kQueueBytes;
+  sp.ws_bytes = kQueueBytes;
   if (n_split <= 0 || parts < 2) return sp;
   sp.n_split = n_split;
   sp.parts = parts;
   const size_t per_tile = (size_t)p.B * p.Hkv * p.n_hg;
   const size_t jobs = (size_t)n_split * per_tile, pieces = jobs * parts;
-  sp.lse_off = (jobs * sizeof(int) + 255) & ~(size_t)255;
+  sp.lse_off = (sp.cnt_off + jobs * sizeof(int) + 255) & ~(size_t)255;
   sp.o_off = (sp.lse_off + pieces * 256 * sizeof(float) + 255) & ~(size_t)255;
   sp.ws_bytes = sp.o_off + pieces * 256 * 128 * sizeof(float);
   return sp;
 }
 
 PrefillSplit plan_prefill_split_uncached(const rattn::PrefillParams& p, int dtype, int kv_splits) {
-  if (dtype != RATTN_BF16 || kv_splits == 1) return PrefillSplit{};
+  if (dtype != RATTN_BF16) return PrefillSplit{};
+  if (kv_splits == 1) return split_layout(p, 0, 1);
   const int nt = p.n_tok_tiles;
   std::vector<int> keys(nt);
   for (int t = 0; t < nt; ++t) keys[t] = prefill_tile_keys(p, t);  // non-decreasing in t
@@ -192,7 +194,7 @@ PrefillSplit plan_prefill_split_uncached(const rattn::PrefillParams& p, int dtyp
     return split_layout(p, n_split, kv_splits);
   }
   const long long per_tile = (long long)p.B * p.Hkv * p.n_hg;
-  if ((long long)nt * per_tile * rattn::kMaxPieces > 0x7fffffffLL) return PrefillSplit{};
+  if ((long long)nt * per_tile * rattn::kMaxPieces > 0x7fffffffLL) return split_layout(p, 0, 1);
   // job sizes in grid order, pieces mapped to workgroups as the kernel does
   auto jobs_of = [&](int n_split, int parts) {
     std::vector<double> jobs;
@@ -211,7 +213,7 @@ PrefillSplit plan_prefill_split_uncached(const rattn::PrefillParams& p, int dtyp
   for (int t = 0; t < nt; ++t) total += (keys[t] + kWgOverhead) * per_tile;
   double best = simulate_dispatch(jobs_of(0, 1));
   // a grid that already finishes within 5 % of an even spread is left alone
-  if (best <= 1.05 * total / (kXcds * kUnitsPerXcd)) return PrefillSplit{};
+  if (best <= 1.05 * total / kDispatchUnits) return split_layout(p, 0, 1);
   int best_split = 0, best_parts = 1;
   const int kmax = keys[nt - 1];
   for (int parts = 2; parts <= 4; ++parts)
@@ -228,6 +230,19 @@ PrefillSplit plan_prefill_split_uncached(const rattn::PrefillParams& p, int dtyp
       }
     }
   return split_layout(p, best_split, best_parts);
+}
+
+// compute units of the current device (queried once per device)
+int compute_units() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
 }
 
 // the plan of the last few shapes (calls repeat their shapes)
@@ -289,16 +304,18 @@ int rattn_prefill(const void* q, const void* k, const void* v, const float* bias
   p.R = R;
   prefill_shape(B, Lq, Lk, Hq, Hkv, window, &p);
   p.scale_log2 = kScaleLog2;
-  // no workspace: never split
+  // no workspace: one workgroup per job, never split
   const PrefillSplit sp = workspace == nullptr ? PrefillSplit{} : plan_prefill_split(p, dtype, kv_splits);
   if (sp.ws_bytes > workspace_bytes)
     return fail(RATTN_ERR_WORKSPACE, "rattn_prefill: workspace of %zu bytes, %zu needed", workspace_bytes,
                 sp.ws_bytes);
   p.n_split = sp.n_split;
   p.parts = sp.parts;
-  p.ws_cnt = (int*)workspace;
-  p.ws_lse = sp.ws_bytes ? (float*)((char*)workspace + sp.lse_off) : nullptr;
-  p.ws_o = sp.ws_bytes ? (float*)((char*)workspace + sp.o_off) : nullptr;
+  p.queue = sp.ws_bytes ? (int*)workspace : nullptr;
+  p.queue_workgroups = p.queue ? compute_units() : 0;
+  p.ws_cnt = sp.ws_bytes ? (int*)((char*)workspace + sp.cnt_off) : nullptr;
+  p.ws_lse = sp.n_split ? (float*)((char*)workspace + sp.lse_off) : nullptr;
+  p.ws_o = sp.n_split ? (float*)((char*)workspace + sp.o_off) : nullptr;
   const long long per_tile = (long long)B * Hkv * p.n_hg;
   const long long grid = ((long long)p.n_tok_tiles - p.n_split) * per_tile + (long long)p.n_split * per_tile * p.parts;
   if (grid > 0x7fffffffLL) return fail(RATTN_ERR_INVALID_ARG, "rattn_prefill: problem too large for one launch");

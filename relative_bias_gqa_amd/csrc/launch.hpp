@@ -30,6 +30,8 @@ struct PrefillParams {
   float* ws_o;    // [n_split * B * Hkv * n_hg * parts, 256 rows, 128] normalised partials
   float* ws_lse;  // [same, 256 rows] log2-sum-exp of each partial
   int* ws_cnt;    // [n_split * B * Hkv * n_hg] finished pieces; zero between calls
+  int* queue;            // [2] job queue and done counter (zero before and after a call), or null
+  int queue_workgroups;  // workgroups of a launch with a queue
 };
 
 constexpr int kMaxPieces = 8;

@@ -56,6 +56,7 @@ __device__ __attribute__((aligned(256))) const uint32_t kZeroRowP[64] = {0};
 __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams p) {
   __shared__ __attribute__((aligned(1024))) unsigned char ring[kStages * kStageBytes];
   __shared__ int last_piece;
+  __shared__ int next_slot;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -63,482 +64,511 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   const int col = lane & 31;  // accumulator column = query token within the wave
   const int hf = lane >> 5;   // which half of the key rows this lane holds
 
-  // ---- job: heaviest (last) token tiles first ---------------------------------------
-  // The first n_split * per_tile * parts workgroups each take one of `parts` pieces of the
-  // key range of the n_split heaviest token tiles (the pieces of a tile adjacent); the
-  // others take whole token tiles.  Both lists run from the heaviest tile down.
+  // ---- jobs: heaviest (last) token tiles first ---------------------------------------
+  // Job slot s < n_piece_slots takes one of `parts` pieces of the key range of one of the
+  // n_split heaviest token tiles; the others take whole token tiles.  Both lists run from
+  // the heaviest tile down.  A workgroup runs slot blockIdx.x, then (with a queue) the
+  // next unclaimed slot, until none is left: the output stores of one job drain while
+  // the next one runs.
   const int per_tile = p.B * p.Hkv * p.n_hg;
-  const int n_piece_wgs = p.n_split * per_tile * p.parts;
-  const bool is_piece = (int)blockIdx.x < n_piece_wgs;
-  int job = (int)blockIdx.x - n_piece_wgs + p.n_split * per_tile, piece = 0;
-  if (is_piece) prefill_piece_of(blockIdx.x, (long long)p.n_split * per_tile, p.parts, &job, &piece);
-  const int tile = p.n_tok_tiles - 1 - job / per_tile;
-  const int rem = job % per_tile;
-  const int hg = rem % p.n_hg;
-  const int hk = (rem / p.n_hg) % p.Hkv;
-  const int b = rem / (p.n_hg * p.Hkv);
+  const int n_piece_slots = p.n_split * per_tile * p.parts;
+  const int n_slots = n_piece_slots + (p.n_tok_tiles - p.n_split) * per_tile;
+  for (int slot = blockIdx.x; slot < n_slots;) {
+    const bool is_piece = slot < n_piece_slots;
+    int job = slot - n_piece_slots + p.n_split * per_tile, piece = 0;
+    if (is_piece) prefill_piece_of(slot, (long long)p.n_split * per_tile, p.parts, &job, &piece);
+    const int tile = p.n_tok_tiles - 1 - job / per_tile;
+    const int rem = job % per_tile;
+    const int hg = rem % p.n_hg;
+    const int hk = (rem / p.n_hg) % p.Hkv;
+    const int b = rem / (p.n_hg * p.Hkv);
 
-  const int h = hk * p.G + hg * p.hpw + (wave % p.hpw);
-  const int T0 = tile * 32 * p.tsub;
-  const int T1 = min(p.Lq, T0 + 32 * p.tsub);
-  const int tw0 = T0 + (wave / p.hpw) * 32;  // first token of this wave
-  const int off = p.Lk - p.Lq;               // position of token 0
-  const int pw0 = off + tw0;                 // position of this wave's column 0
-  const int wvalid = min(32, p.Lq - tw0);    // valid columns of this wave (may be <= 0)
-  const bool wave_active = wvalid > 0;
-  const int pw_last = pw0 + max(wvalid, 1) - 1;
-  const int Weff = p.window > 0 ? p.window : 0x40000000;
+    const int h = hk * p.G + hg * p.hpw + (wave % p.hpw);
+    const int T0 = tile * 32 * p.tsub;
+    const int T1 = min(p.Lq, T0 + 32 * p.tsub);
+    const int tw0 = T0 + (wave / p.hpw) * 32;  // first token of this wave
+    const int off = p.Lk - p.Lq;               // position of token 0
+    const int pw0 = off + tw0;                 // position of this wave's column 0
+    const int wvalid = min(32, p.Lq - tw0);    // valid columns of this wave (may be <= 0)
+    const bool wave_active = wvalid > 0;
+    const int pw_last = pw0 + max(wvalid, 1) - 1;
+    const int Weff = p.window > 0 ? p.window : 0x40000000;
 
-  // keys the workgroup needs, in whole tiles (a piece: its share of them)
-  int kt_begin = max(0, off + T0 - Weff + 1) / kBK;
-  int kt_end = (off + T1 - 1) / kBK + 1;
-  if (is_piece) {
-    const int nt = kt_end - kt_begin;
-    const int first = kt_begin;
-    kt_begin = first + (nt * piece) / p.parts;
-    kt_end = first + (nt * (piece + 1)) / p.parts;
-  }
-  const int n_tiles = kt_end - kt_begin;
-
-  // ---- Q^T operand, resident for the whole key loop -------------------------------
-  u32x4_t qr[8];
-  {
-    const int tq = tw0 + col;
-    const bool ok = wave_active && tq < p.Lq;
-    const size_t qbase = (((size_t)b * p.Lq + (ok ? tq : 0)) * p.Hq + h) * kHeadDim;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-      qr[ks] = ok ? *(const u32x4_t*)((const uint16_t*)p.q + qbase + 16 * ks + 8 * hf) : zero_u32x4();
-  }
-  // pin the waits for these loads here, before any LDS-bound load is in flight
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks) asm volatile("" : "+v"(qr[ks]));
-
-  // ---- tile loads -------------------------------------------------------------------
-  // K/V: wave w issues keys 8 w .. 8 w + 7 of the tile, four keys (1 KB) per instruction;
-  // lane i fetches 16-byte chunk (i & 15) ^ swz(key) of key 4 m + i / 16.
-  uint32_t koff[2], voff[2], kz[2], vz[2];
-  int ktok[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int tok = 8 * wave + 4 * i + (lane >> 4);
-    const int slot = lane & 15;
-    const int ck = slot ^ (tok & 15);
-    const int cv = slot ^ ((tok & 7) << 1);
-    ktok[i] = tok;
-    koff[i] = (uint32_t)(tok * p.Hkv) * 256u + ck * 16;
-    voff[i] = (uint32_t)(tok * p.Hkv) * 256u + cv * 16;
-    kz[i] = ck * 16;
-    vz[i] = cv * 16;
-  }
-  const unsigned char* kc_bytes = (const unsigned char*)p.k + ((size_t)b * p.Lk * p.Hkv + hk) * 256;
-  const unsigned char* vc_bytes = (const unsigned char*)p.v + ((size_t)b * p.Lk * p.Hkv + hk) * 256;
-  const unsigned char* zero_bytes = (const unsigned char*)kZeroRowP;
-  const float* bias_row = p.bias + (size_t)h * p.R;
-  const uint32_t ring_base = lds_addr(ring);
-
-  // Interior tiles issue from a scalar base plus fixed per-lane offsets (no vector ALU
-  // work); the last tile (keys past Lk read a zero row) and bias halves that are only
-  // partly clamped compute per-lane addresses.
-  const uint32_t boff = 4u * (63 - lane);  // bias entry lo + 63 - lane of a 64-entry half
-  const uint32_t zoff = 0;
-  auto issue_tile = [&](int kt, int st) {
-    const int j0 = kt * kBK;
-    const size_t base = (size_t)j0 * p.Hkv * 256;
-    const uint32_t kdst = ring_base + st * kStageBytes + wave * 2048;
-    const uint32_t vdst = kdst + kKVBytes;
-    const uint32_t bdst = ring_base + st * kStageBytes + 2 * kKVBytes + wave * (kSliceFloats * 4);
-    if (j0 + kBK <= p.Lk) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        dma16s(kc_bytes + base, koff[i], kdst + i * 1024);
-        dma16s(vc_bytes + base, voff[i], vdst + i * 1024);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const unsigned char* gk = kc_bytes + base + koff[i];
-        const unsigned char* gv = vc_bytes + base + voff[i];
-        if (j0 + ktok[i] >= p.Lk) {
-          gk = zero_bytes + kz[i];
-          gv = zero_bytes + vz[i];
-        }
-        dma16(gk, kdst + i * 1024);
-        dma16(gv, vdst + i * 1024);
-      }
+    // keys the workgroup needs, in whole tiles (a piece: its share of them)
+    int kt_begin = max(0, off + T0 - Weff + 1) / kBK;
+    int kt_end = (off + T1 - 1) / kBK + 1;
+    if (is_piece) {
+      const int nt = kt_end - kt_begin;
+      const int first = kt_begin;
+      kt_begin = first + (nt * piece) / p.parts;
+      kt_end = first + (nt * (piece + 1)) / p.parts;
     }
-    // this wave's bias slice, stored by decreasing distance:
-    // entry y = r[h, clamp(pw0 - j0 + 31 - y, 0, R - 1)]; half i holds y = 64 i + lane,
-    // distances lo + 63 - lane with lo = pw0 - j0 - 32 - 64 i
+    const int n_tiles = kt_end - kt_begin;
+
+    // ---- Q^T operand, resident for the whole key loop -------------------------------
+    u32x4_t qr[8];
+    {
+      const int tq = tw0 + col;
+      const bool ok = wave_active && tq < p.Lq;
+      const size_t qbase = (((size_t)b * p.Lq + (ok ? tq : 0)) * p.Hq + h) * kHeadDim;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+        qr[ks] = ok ? *(const u32x4_t*)((const uint16_t*)p.q + qbase + 16 * ks + 8 * hf) : zero_u32x4();
+    }
+    // pin the waits for these loads here, before any LDS-bound load is in flight
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) asm volatile("" : "+v"(qr[ks]));
+
+    // ---- tile loads -------------------------------------------------------------------
+    // K/V: wave w issues keys 8 w .. 8 w + 7 of the tile, four keys (1 KB) per instruction;
+    // lane i fetches 16-byte chunk (i & 15) ^ swz(key) of key 4 m + i / 16.
+    uint32_t koff[2], voff[2], kz[2], vz[2];
+    int ktok[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int lo = pw0 - j0 - 32 - 64 * i;
-      if (lo >= 0 && lo + 63 <= p.R - 1) {
-        dma4s(bias_row + lo, boff, bdst + i * 256);
-      } else if (lo >= p.R - 1) {
-        dma4s(bias_row + (p.R - 1), zoff, bdst + i * 256);
-      } else {
-        const int d = min(max(lo + 63 - lane, 0), p.R - 1);
-        dma4(bias_row + d, bdst + i * 256);
-      }
+      const int tok = 8 * wave + 4 * i + (lane >> 4);
+      const int slot = lane & 15;
+      const int ck = slot ^ (tok & 15);
+      const int cv = slot ^ ((tok & 7) << 1);
+      ktok[i] = tok;
+      koff[i] = (uint32_t)(tok * p.Hkv) * 256u + ck * 16;
+      voff[i] = (uint32_t)(tok * p.Hkv) * 256u + cv * 16;
+      kz[i] = ck * 16;
+      vz[i] = cv * 16;
     }
-  };
+    const unsigned char* kc_bytes = (const unsigned char*)p.k + ((size_t)b * p.Lk * p.Hkv + hk) * 256;
+    const unsigned char* vc_bytes = (const unsigned char*)p.v + ((size_t)b * p.Lk * p.Hkv + hk) * 256;
+    const unsigned char* zero_bytes = (const unsigned char*)kZeroRowP;
+    const float* bias_row = p.bias + (size_t)h * p.R;
+    const uint32_t ring_base = lds_addr(ring);
 
-  // ---- per-lane LDS operand addresses (stage 0) ----------------------------------------
-  // K tile rows are 256 B with 16-byte chunk c of key j stored at chunk c ^ (j & 15).  The
-  // A operand of k-step i (key row 32 kb + col, chunk 2 i + hf) then sits at byte
-  //   row base + ((32 i) ^ L),  L = 32 ((col & 15) >> 1) + 16 (hf ^ (col & 1)),
-  // i.e. at kx0 ^ (32 i) (+ 8192 for kb = 1), the row base being 256-byte aligned.
-  const uint32_t kx0 = ring_base + col * 256 + 32 * ((col & 15) >> 1) + 16 * (hf ^ (col & 1));
-  // V tile rows are 256 B with chunk c of key j at chunk c ^ (2 (j & 7)).  Lane (m = lane
-  // & 15, u = bit 4, hf) of the transposed read for d block db, keys kbase.. reads key row
-  // kbase + 4 hf + (m >> 2) (and 8 rows on) at column 32 db + 16 u + 4 (m & 3): with
-  // Y = (2 u + ((m & 3) >> 1)) ^ (2 (row & 7)) that is vz0 ^ (64 db) + 256 kbase.
-  uint32_t vz0;
-  {
-    const int m = lane & 15, u = (lane >> 4) & 1;
-    const int vrow = 4 * hf + (m >> 2);
-    const int y = (2 * u + ((m & 3) >> 1)) ^ (2 * (vrow & 7));
-    vz0 = ring_base + kKVBytes + vrow * 256 + 16 * y + 8 * (m & 1);
-  }
-  // this wave's bias slice: seeds at sb0 + 4 (32 kb + 8 (r >> 2) + (r & 3))
-  const uint32_t sb0 = ring_base + 2 * kKVBytes + wave * (kSliceFloats * 4) + 4 * (31 - col + 4 * hf);
-  const uint32_t sl0 = ring_base + 2 * kKVBytes + wave * (kSliceFloats * 4) + 8 * lane;
-
-  // ---- running state ---------------------------------------------------------------
-  f32x16_t o[4];
+    // Interior tiles issue from a scalar base plus fixed per-lane offsets (no vector ALU
+    // work); the last tile (keys past Lk read a zero row) and bias halves that are only
+    // partly clamped compute per-lane addresses.
+    const uint32_t boff = 4u * (63 - lane);  // bias entry lo + 63 - lane of a 64-entry half
+    const uint32_t zoff = 0;
+    auto issue_tile = [&](int kt, int st) {
+      const int j0 = kt * kBK;
+      const size_t base = (size_t)j0 * p.Hkv * 256;
+      const uint32_t kdst = ring_base + st * kStageBytes + wave * 2048;
+      const uint32_t vdst = kdst + kKVBytes;
+      const uint32_t bdst = ring_base + st * kStageBytes + 2 * kKVBytes + wave * (kSliceFloats * 4);
+      if (j0 + kBK <= p.Lk) {
 #pragma unroll
-  for (int db = 0; db < 4; ++db) o[db] = zero_f32x16();
-  float m_run = kNegInf;  // running max (log2 units), identical in both lane halves
-  float l_run = 0.f;      // this lane's share of the running normaliser
-  f32x16_t s[2];          // S^T of the tile in flight (two 32-key blocks)
-  u32x4_t pk[2][2];       // its P^T as bf16 MFMA operands
-
-  // The S accumulators of the tile in stage st start from the wave's bias slice (scaled
-  // to score units in the MFMA half-step).  Distances beyond R - 1 are clamped in the
-  // slice, so a tile entirely past them is seeded with r[h, R - 1] like any other.
-  // The seeds of the tile in stage st: this wave's whole slice is first scaled by sqrt(128)
-  // in place (two entries per lane: two multiplies instead of one per seed), then the 32
-  // seeds are read; the LDS serves one wave's requests in order, so the reads see the
-  // scaled entries.  Runs once per tile, inside the MFMA half-step: the slice read goes
-  // out before the first operand reads, the rest after the second group of MFMAs.
-  float sl_e0, sl_e1;
-  uint32_t sl_addr;
-  auto seeds_begin = [&](int st) {
-    sl_addr = sl0 + st * kStageBytes;
-    asm volatile("" : "+v"(sl_addr));
-    const lds_f32_t* ps = (const lds_f32_t*)(size_t)sl_addr;
-    sl_e0 = ps[0];
-    sl_e1 = ps[1];
-  };
-  auto seeds_end = [&](int st) {
-    lds_f32_t* ps = (lds_f32_t*)(size_t)sl_addr;
-    ps[0] = sl_e0 * kSqrtD;
-    ps[1] = sl_e1 * kSqrtD;
-    // one base register per call, the rest immediate offsets (kept from being hoisted
-    // out of the loop as 32 separate addresses)
-    uint32_t base = sb0 + st * kStageBytes;
-    asm volatile("" : "+v"(base));
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = lds_ldf(base + 4 * (32 * kb + 8 * (r >> 2) + (r & 3)));
-  };
-
-  // MFMA half-step: O^T += V^T P^T for the previous tile (stage st_prev), then
-  // S^T = sqrt(128) r + K Q^T for the tile in stage st on the seeded accumulators.  The
-  // 32 MFMAs run as eight groups of four (P.V keys 16 G.., then S k-steps in pairs); each
-  // group's operands are read from LDS two groups ahead.
-  auto mfma_half = [&](int st, int st_prev) {
-    const uint32_t so = st * kStageBytes;
-    const uint32_t kx = kx0 + so;
-    const uint32_t vz = vz0 + st_prev * kStageBytes;
-    // operands of group gi: P.V (gi < 4) keys 16 gi.., or S k-steps 2 (gi - 4) and
-    // 2 (gi - 4) + 1 of both key blocks
-    auto load = [&](int gi, u32x4_t* op) {
-      if (gi < 4) {
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const uint32_t a = (vz ^ (64u * db)) + 256u * (16 * gi);
-          const u32x2_t lo = lds_tr8(a), hi = lds_tr8(a + 2048u);
-          op[db] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+        for (int i = 0; i < 2; ++i) {
+          dma16s(kc_bytes + base, koff[i], kdst + i * 1024);
+          dma16s(vc_bytes + base, voff[i], vdst + i * 1024);
         }
       } else {
-        // k-steps 2 (gi - 4) and 2 (gi - 4) + 1 of both key blocks
 #pragma unroll
-        for (int i = 0; i < 4; ++i) op[i] = lds_ld16((kx ^ (32u * (2 * (gi - 4) + (i >> 1)))) + 8192u * (i & 1));
+        for (int i = 0; i < 2; ++i) {
+          const unsigned char* gk = kc_bytes + base + koff[i];
+          const unsigned char* gv = vc_bytes + base + voff[i];
+          if (j0 + ktok[i] >= p.Lk) {
+            gk = zero_bytes + kz[i];
+            gv = zero_bytes + vz[i];
+          }
+          dma16(gk, kdst + i * 1024);
+          dma16(gv, vdst + i * 1024);
+        }
+      }
+      // this wave's bias slice, stored by decreasing distance:
+      // entry y = r[h, clamp(pw0 - j0 + 31 - y, 0, R - 1)]; half i holds y = 64 i + lane,
+      // distances lo + 63 - lane with lo = pw0 - j0 - 32 - 64 i
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int lo = pw0 - j0 - 32 - 64 * i;
+        if (lo >= 0 && lo + 63 <= p.R - 1) {
+          dma4s(bias_row + lo, boff, bdst + i * 256);
+        } else if (lo >= p.R - 1) {
+          dma4s(bias_row + (p.R - 1), zoff, bdst + i * 256);
+        } else {
+          const int d = min(max(lo + 63 - lane, 0), p.R - 1);
+          dma4(bias_row + d, bdst + i * 256);
+        }
       }
     };
-    u32x4_t op[3][4];
-    seeds_begin(st);
-    __builtin_amdgcn_sched_barrier(0);
-    load(0, op[0]);
-    load(1, op[1]);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int gi = 0; gi < 8; ++gi) {
-      if (gi + 2 < 8) load(gi + 2, op[(gi + 2) % 3]);
-      const u32x4_t* cur = op[gi % 3];
-      if (gi < 4) {
-#pragma unroll
-        for (int db = 0; db < 4; ++db) o[db] = mfma_32x32x16(cur[db], pk[gi >> 1][gi & 1], o[db]);
-        // the seeds (needed from group 4 on); the slice read went out before the operands
-        // of groups 0 and 1, so it has arrived
-        if (gi == 1) seeds_end(st);
-      } else {
-        // alternate the two key blocks so that consecutive MFMAs are independent
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s[i & 1] = mfma_32x32x16(cur[i], qr[2 * (gi - 4) + (i >> 1)], s[i & 1]);
-      }
-      __builtin_amdgcn_sched_barrier(0);  // keep the reads two groups ahead
-    }
-  };
 
-  // Softmax half-step of tile kt: logits in log2 units relative to the running maximum
-  // (the bias and the max in one FMA), the causal / window mask on edge tiles, the row
-  // maximum, a lazy raise of the running maximum (only when a row's maximum grows by
-  // more than the slack, rescaling O and the normaliser), then P = exp2 in fp32 for the
-  // normaliser (the log-sum-exp needs that accuracy) and rounded to bf16 for P.V.
-  auto softmax_half = [&](int kt) {
-    const int j0 = kt * kBK;
-    if (j0 + kBK - 1 > pw0 || j0 < pw_last - Weff + 1) {
-      // edge tile: mask the raw scores (in place; -inf stays -inf through the logit FMA).
-      // Key 32 kb + 8 (r >> 2) + 4 hf + (r & 3) is at distance dl - c(kb, r) from this
-      // lane's query; visible iff 0 <= distance < Weff (Weff is huge without a window).
-      const int dl = pw0 + col - j0 - 4 * hf;
+    // ---- per-lane LDS operand addresses (stage 0) ----------------------------------------
+    // K tile rows are 256 B with 16-byte chunk c of key j stored at chunk c ^ (j & 15).  The
+    // A operand of k-step i (key row 32 kb + col, chunk 2 i + hf) then sits at byte
+    //   row base + ((32 i) ^ L),  L = 32 ((col & 15) >> 1) + 16 (hf ^ (col & 1)),
+    // i.e. at kx0 ^ (32 i) (+ 8192 for kb = 1), the row base being 256-byte aligned.
+    const uint32_t kx0 = ring_base + col * 256 + 32 * ((col & 15) >> 1) + 16 * (hf ^ (col & 1));
+    // V tile rows are 256 B with chunk c of key j at chunk c ^ (2 (j & 7)).  Lane (m = lane
+    // & 15, u = bit 4, hf) of the transposed read for d block db, keys kbase.. reads key row
+    // kbase + 4 hf + (m >> 2) (and 8 rows on) at column 32 db + 16 u + 4 (m & 3): with
+    // Y = (2 u + ((m & 3) >> 1)) ^ (2 (row & 7)) that is vz0 ^ (64 db) + 256 kbase.
+    uint32_t vz0;
+    {
+      const int m = lane & 15, u = (lane >> 4) & 1;
+      const int vrow = 4 * hf + (m >> 2);
+      const int y = (2 * u + ((m & 3) >> 1)) ^ (2 * (vrow & 7));
+      vz0 = ring_base + kKVBytes + vrow * 256 + 16 * y + 8 * (m & 1);
+    }
+    // this wave's bias slice: seeds at sb0 + 4 (32 kb + 8 (r >> 2) + (r & 3))
+    const uint32_t sb0 = ring_base + 2 * kKVBytes + wave * (kSliceFloats * 4) + 4 * (31 - col + 4 * hf);
+    const uint32_t sl0 = ring_base + 2 * kKVBytes + wave * (kSliceFloats * 4) + 8 * lane;
+
+    // ---- running state ---------------------------------------------------------------
+    f32x16_t o[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) o[db] = zero_f32x16();
+    float m_run = kNegInf;  // running max (log2 units), identical in both lane halves
+    float l_run = 0.f;      // this lane's share of the running normaliser
+    f32x16_t s[2];          // S^T of the tile in flight (two 32-key blocks)
+    u32x4_t pk[2][2];       // its P^T as bf16 MFMA operands
+
+    // The S accumulators of the tile in stage st start from the wave's bias slice (scaled
+    // to score units in the MFMA half-step).  Distances beyond R - 1 are clamped in the
+    // slice, so a tile entirely past them is seeded with r[h, R - 1] like any other.
+    // The seeds of the tile in stage st: this wave's whole slice is first scaled by sqrt(128)
+    // in place (two entries per lane: two multiplies instead of one per seed), then the 32
+    // seeds are read; the LDS serves one wave's requests in order, so the reads see the
+    // scaled entries.  Runs once per tile, inside the MFMA half-step: the slice read goes
+    // out before the first operand reads, the rest after the second group of MFMAs.
+    float sl_e0, sl_e1;
+    uint32_t sl_addr;
+    auto seeds_begin = [&](int st) {
+      sl_addr = sl0 + st * kStageBytes;
+      asm volatile("" : "+v"(sl_addr));
+      const lds_f32_t* ps = (const lds_f32_t*)(size_t)sl_addr;
+      sl_e0 = ps[0];
+      sl_e1 = ps[1];
+    };
+    auto seeds_end = [&](int st) {
+      lds_f32_t* ps = (lds_f32_t*)(size_t)sl_addr;
+      ps[0] = sl_e0 * kSqrtD;
+      ps[1] = sl_e1 * kSqrtD;
+      // one base register per call, the rest immediate offsets (kept from being hoisted
+      // out of the loop as 32 separate addresses)
+      uint32_t base = sb0 + st * kStageBytes;
+      asm volatile("" : "+v"(base));
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int c = 32 * kb + 8 * (r >> 2) + (r & 3);
-          s[kb][r] = (uint32_t)(dl - c) < (uint32_t)Weff ? s[kb][r] : kNegInf;
+        for (int r = 0; r < 16; ++r) s[kb][r] = lds_ldf(base + 4 * (32 * kb + 8 * (r >> 2) + (r & 3)));
+    };
+
+    // MFMA half-step: O^T += V^T P^T for the previous tile (stage st_prev), then
+    // S^T = sqrt(128) r + K Q^T for the tile in stage st on the seeded accumulators.  The
+    // 32 MFMAs run as eight groups of four (P.V keys 16 G.., then S k-steps in pairs); each
+    // group's operands are read from LDS two groups ahead.
+    auto mfma_half = [&](int st, int st_prev) {
+      const uint32_t so = st * kStageBytes;
+      const uint32_t kx = kx0 + so;
+      const uint32_t vz = vz0 + st_prev * kStageBytes;
+      // operands of group gi: P.V (gi < 4) keys 16 gi.., or S k-steps 2 (gi - 4) and
+      // 2 (gi - 4) + 1 of both key blocks
+      auto load = [&](int gi, u32x4_t* op) {
+        if (gi < 4) {
+#pragma unroll
+          for (int db = 0; db < 4; ++db) {
+            const uint32_t a = (vz ^ (64u * db)) + 256u * (16 * gi);
+            const u32x2_t lo = lds_tr8(a), hi = lds_tr8(a + 2048u);
+            op[db] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+          }
+        } else {
+          // k-steps 2 (gi - 4) and 2 (gi - 4) + 1 of both key blocks
+#pragma unroll
+          for (int i = 0; i < 4; ++i) op[i] = lds_ld16((kx ^ (32u * (2 * (gi - 4) + (i >> 1)))) + 8192u * (i & 1));
         }
-    }
-    const bool fresh = m_run == kNegInf;
-    const float m_ref = fresh ? 0.f : m_run;
-    const float raise_above = fresh ? kNegInf : kRescaleSlack;
+      };
+      u32x4_t op[3][4];
+      seeds_begin(st);
+      __builtin_amdgcn_sched_barrier(0);
+      load(0, op[0]);
+      load(1, op[1]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int gi = 0; gi < 8; ++gi) {
+        if (gi + 2 < 8) load(gi + 2, op[(gi + 2) % 3]);
+        const u32x4_t* cur = op[gi % 3];
+        if (gi < 4) {
+#pragma unroll
+          for (int db = 0; db < 4; ++db) o[db] = mfma_32x32x16(cur[db], pk[gi >> 1][gi & 1], o[db]);
+          // the seeds (needed from group 4 on); the slice read went out before the operands
+          // of groups 0 and 1, so it has arrived
+          if (gi == 1) seeds_end(st);
+        } else {
+          // alternate the two key blocks so that consecutive MFMAs are independent
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s[i & 1] = mfma_32x32x16(cur[i], qr[2 * (gi - 4) + (i >> 1)], s[i & 1]);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // keep the reads two groups ahead
+      }
+    };
+
+    // Softmax half-step of tile kt: logits in log2 units relative to the running maximum
+    // (the bias and the max in one FMA), the causal / window mask on edge tiles, the row
+    // maximum, a lazy raise of the running maximum (only when a row's maximum grows by
+    // more than the slack, rescaling O and the normaliser), then P = exp2 in fp32 for the
+    // normaliser (the log-sum-exp needs that accuracy) and rounded to bf16 for P.V.
+    auto softmax_half = [&](int kt) {
+      const int j0 = kt * kBK;
+      if (j0 + kBK - 1 > pw0 || j0 < pw_last - Weff + 1) {
+        // edge tile: mask the raw scores (in place; -inf stays -inf through the logit FMA).
+        // Key 32 kb + 8 (r >> 2) + 4 hf + (r & 3) is at distance dl - c(kb, r) from this
+        // lane's query; visible iff 0 <= distance < Weff (Weff is huge without a window).
+        const int dl = pw0 + col - j0 - 4 * hf;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int c = 32 * kb + 8 * (r >> 2) + (r & 3);
+            s[kb][r] = (uint32_t)(dl - c) < (uint32_t)Weff ? s[kb][r] : kNegInf;
+          }
+      }
+      const bool fresh = m_run == kNegInf;
+      const float m_ref = fresh ? 0.f : m_run;
+      const float raise_above = fresh ? kNegInf : kRescaleSlack;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] = fmaf(s[kb][r], p.scale_log2, -m_ref);
+      float ma = max3f(s[0][0], s[0][1], s[0][2]);
+      float mb = max3f(s[1][0], s[1][1], s[1][2]);
+#pragma unroll
+      for (int r = 3; r < 15; r += 2) {
+        ma = max3f(ma, s[0][r], s[0][r + 1]);
+        mb = max3f(mb, s[1][r], s[1][r + 1]);
+      }
+      const float mx = half_swap_max3(max3f(ma, mb, s[0][15]), s[1][15]);
+      const bool raise = mx > raise_above;
+      if (__builtin_amdgcn_ballot_w64(raise)) {
+        const float delta = raise ? mx : 0.f;
+        const float m_new = m_ref + delta;
+        const float alpha = raise ? fast_exp2(m_run - m_new) : 1.f;
+        m_run = raise ? m_new : m_run;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) o[db] *= alpha;
+        s[0] -= delta;
+        s[1] -= delta;
+      }
+      float lsum;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          u32x4_t w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 8 * half + 2 * e;
+            const float e0 = fast_exp2(s[kb][r]), e1 = fast_exp2(s[kb][r + 1]);
+            lsum = (kb | half | e) ? lsum + (e0 + e1) : e0 + e1;
+            w[e] = pack_bf16x2(e0, e1);
+          }
+          pk[kb][half] = w;
+        }
+      l_run += lsum;
+    };
+
+    // ---- key loop: two wave groups in ping-pong -------------------------------------
+    // Waves 0-3 and 4-7 (one of each on every SIMD) run the same code per tile t: read the
+    // seeds of tile t, an MFMA half-step (P.V of tile t - 1, then S of tile t), a softmax
+    // half-step (tile t).  There is one workgroup barrier per tile; barrier t means "tile t
+    // is whole in LDS" (every wave waited for its share of it first), and right after it
+    // each wave starts its share of tile t + 2, into the stage of tile t - 2.  Group 0
+    // passes barrier t before its MFMA half of tile t, group 1 after it (and barrier 0 ahead
+    // of everything), so between barriers t and t + 1 group 0 runs MFMA(t) then softmax(t)
+    // while group 1 runs softmax(t - 1) then MFMA(t): the two waves of a SIMD take turns on
+    // the matrix cores and the vector ALU.  Every read of a stage falls between the barrier
+    // that completes its tile and the barrier that refills it, two tiles later.
+    const bool g1 = wave >= kWaves / 2;
+    const int prologue = min(2, n_tiles);
+    for (int i = 0; i < prologue; ++i) issue_tile(kt_begin + i, i);
+    // P of "tile -1" is zero and the V rows of the last stage are zeroed, so that the first
+    // MFMA half-step can run its P.V like every other (it adds nothing)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = fmaf(s[kb][r], p.scale_log2, -m_ref);
-    float ma = max3f(s[0][0], s[0][1], s[0][2]);
-    float mb = max3f(s[1][0], s[1][1], s[1][2]);
-#pragma unroll
-    for (int r = 3; r < 15; r += 2) {
-      ma = max3f(ma, s[0][r], s[0][r + 1]);
-      mb = max3f(mb, s[1][r], s[1][r + 1]);
+      for (int half = 0; half < 2; ++half) pk[kb][half] = zero_u32x4();
+    {
+      u32x4_t* vlast = (u32x4_t*)(ring + (kStages - 1) * kStageBytes + kKVBytes);
+      vlast[tid] = zero_u32x4();
+      vlast[tid + kThreads] = zero_u32x4();
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // before the first barrier
     }
-    const float mx = half_swap_max3(max3f(ma, mb, s[0][15]), s[1][15]);
-    const bool raise = mx > raise_above;
-    if (__builtin_amdgcn_ballot_w64(raise)) {
-      const float delta = raise ? mx : 0.f;
-      const float m_new = m_ref + delta;
-      const float alpha = raise ? fast_exp2(m_run - m_new) : 1.f;
-      m_run = raise ? m_new : m_run;
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) o[db] *= alpha;
-      s[0] -= delta;
-      s[1] -= delta;
+    auto tile_barrier = [&](int j) {
+      if (j + 1 < n_tiles) vm_wait<kLoadsPerStage>();  // tile j; tile j + 1 may still be loading
+      else vm_wait<0>();
+      wg_barrier_reads_in_flight();
+      if (j + 2 < n_tiles) issue_tile(kt_begin + j + 2, (j + 2) % kStages);
+    };
+    if (g1 && n_tiles > 0) tile_barrier(0);
+    for (int t = 0; t < n_tiles; ++t) {
+      if (!g1) tile_barrier(t);
+      mfma_half(t % kStages, (t + kStages - 1) % kStages);
+      if (g1 && t + 1 < n_tiles) tile_barrier(t + 1);
+      softmax_half(kt_begin + t);
     }
-    float lsum;
+    // claim the next job now: the atomic's round trip overlaps the epilogue
+    int claimed = n_slots;
+    if (tid == 0 && p.queue != nullptr)
+      claimed = (int)gridDim.x + __hip_atomic_fetch_add(p.queue, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (n_tiles > 0) {
+      // P.V of the last tile
+      const uint32_t vz = vz0 + ((n_tiles - 1) % kStages) * kStageBytes;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int G = 0; G < 4; ++G) {
+        u32x4_t va[4];
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        u32x4_t w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 8 * half + 2 * e;
-          const float e0 = fast_exp2(s[kb][r]), e1 = fast_exp2(s[kb][r + 1]);
-          lsum = (kb | half | e) ? lsum + (e0 + e1) : e0 + e1;
-          w[e] = pack_bf16x2(e0, e1);
+        for (int db = 0; db < 4; ++db) {
+          const uint32_t a = (vz ^ (64u * db)) + 256u * (16 * G);
+          const u32x2_t lo = lds_tr8(a), hi = lds_tr8(a + 2048u);
+          va[db] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
         }
-        pk[kb][half] = w;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) o[db] = mfma_32x32x16(va[db], pk[G >> 1][G & 1], o[db]);
       }
-    l_run += lsum;
-  };
-
-  // ---- key loop: two wave groups in ping-pong -------------------------------------
-  // Waves 0-3 and 4-7 (one of each on every SIMD) run the same code per tile t: read the
-  // seeds of tile t, an MFMA half-step (P.V of tile t - 1, then S of tile t), a softmax
-  // half-step (tile t).  There is one workgroup barrier per tile; barrier t means "tile t
-  // is whole in LDS" (every wave waited for its share of it first), and right after it
-  // each wave starts its share of tile t + 2, into the stage of tile t - 2.  Group 0
-  // passes barrier t before its MFMA half of tile t, group 1 after it (and barrier 0 ahead
-  // of everything), so between barriers t and t + 1 group 0 runs MFMA(t) then softmax(t)
-  // while group 1 runs softmax(t - 1) then MFMA(t): the two waves of a SIMD take turns on
-  // the matrix cores and the vector ALU.  Every read of a stage falls between the barrier
-  // that completes its tile and the barrier that refills it, two tiles later.
-  const bool g1 = wave >= kWaves / 2;
-  const int prologue = min(2, n_tiles);
-  for (int i = 0; i < prologue; ++i) issue_tile(kt_begin + i, i);
-  // P of "tile -1" is zero and the V rows of the last stage are zeroed, so that the first
-  // MFMA half-step can run its P.V like every other (it adds nothing)
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int half = 0; half < 2; ++half) pk[kb][half] = zero_u32x4();
-  {
-    u32x4_t* vlast = (u32x4_t*)(ring + (kStages - 1) * kStageBytes + kKVBytes);
-    vlast[tid] = zero_u32x4();
-    vlast[tid + kThreads] = zero_u32x4();
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // before the first barrier
-  }
-  auto tile_barrier = [&](int j) {
-    if (j + 1 < n_tiles) vm_wait<kLoadsPerStage>();  // tile j; tile j + 1 may still be loading
-    else vm_wait<0>();
-    wg_barrier_reads_in_flight();
-    if (j + 2 < n_tiles) issue_tile(kt_begin + j + 2, (j + 2) % kStages);
-  };
-  if (g1 && n_tiles > 0) tile_barrier(0);
-  for (int t = 0; t < n_tiles; ++t) {
-    if (!g1) tile_barrier(t);
-    mfma_half(t % kStages, (t + kStages - 1) % kStages);
-    if (g1 && t + 1 < n_tiles) tile_barrier(t + 1);
-    softmax_half(kt_begin + t);
-  }
-  if (n_tiles > 0) {
-    // P.V of the last tile
-    const uint32_t vz = vz0 + ((n_tiles - 1) % kStages) * kStageBytes;
-#pragma unroll
-    for (int G = 0; G < 4; ++G) {
-      u32x4_t va[4];
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const uint32_t a = (vz ^ (64u * db)) + 256u * (16 * G);
-        const u32x2_t lo = lds_tr8(a), hi = lds_tr8(a + 2048u);
-        va[db] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
-      }
-#pragma unroll
-      for (int db = 0; db < 4; ++db) o[db] = mfma_32x32x16(va[db], pk[G >> 1][G & 1], o[db]);
     }
-  }
 
-  // ---- epilogue --------------------------------------------------------------------
-  const float l_tot = half_swap_sum(l_run);
-  const int tq = tw0 + col;
-  const bool row_ok = wave_active && tq < p.Lq;
-  const size_t obase = (((size_t)b * p.Lq + (row_ok ? tq : 0)) * p.Hq + h) * kHeadDim;
-  if (!is_piece) {
-    if (!row_ok) return;
-    const float inv = 1.f / l_tot;
+    // ---- epilogue --------------------------------------------------------------------
+    const float l_tot = half_swap_sum(l_run);
+    const int tq = tw0 + col;
+    const bool row_ok = wave_active && tq < p.Lq;
+    const size_t obase = (((size_t)b * p.Lq + (row_ok ? tq : 0)) * p.Hq + h) * kHeadDim;
+    if (!is_piece) {
+      if (row_ok) {
+        const float inv = 1.f / l_tot;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+        for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int d = 32 * db + 8 * q + 4 * hf;
-        const float x0 = o[db][4 * q + 0] * inv, x1 = o[db][4 * q + 1] * inv;
-        const float x2 = o[db][4 * q + 2] * inv, x3 = o[db][4 * q + 3] * inv;
-        *(u32x2_t*)((uint16_t*)p.out + obase + d) = u32x2_t{pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
+          for (int q = 0; q < 4; ++q) {
+            const int d = 32 * db + 8 * q + 4 * hf;
+            const float x0 = o[db][4 * q + 0] * inv, x1 = o[db][4 * q + 1] * inv;
+            const float x2 = o[db][4 * q + 2] * inv, x3 = o[db][4 * q + 3] * inv;
+            *(u32x2_t*)((uint16_t*)p.out + obase + d) = u32x2_t{pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
+          }
+        if (hf == 0 && p.lse != nullptr)
+          p.lse[((size_t)b * p.Lq + tq) * p.Hq + h] = (m_run + __log2f(l_tot)) * kLn2;
       }
-    if (hf == 0 && p.lse != nullptr)
-      p.lse[((size_t)b * p.Lq + tq) * p.Hq + h] = (m_run + __log2f(l_tot)) * kLn2;
-    return;
-  }
-
-  // A piece: its normalised output and log2-sum-exp per row go to the workspace (a row
-  // that saw no key of this piece: zeros and -inf).  The piece that finishes last merges
-  // all pieces of the tile from the workspace, in piece order (so the result does not
-  // depend on which one that is), and writes the output.
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  const float lse2 = l_tot > 0.f ? m_run + __log2f(l_tot) : kNegInf;
-  // Partial layout (per piece, per wave): 16-byte chunk c = 4 db + q of every lane, then
-  // the lane -- each 16-byte store or load of a wave covers 1 KB of consecutive bytes.
-  const int wrow = wave * 32 + col;  // row of the workgroup, 0..255
-  const size_t my_slot = (size_t)job * p.parts + piece;  // piece j of a job: slot job * parts + j
-  auto part_o = [&](size_t slot) { return p.ws_o + ((slot * kWaves + wave) * 32 * kHeadDim + 4 * lane); };
-  // The partials are written and read with device-coherent accesses (the sc1 bit, as a
-  // relaxed agent-scope atomic access of this target has it), which go to the coherence
-  // point directly: a device-scope fence instead would write back and invalidate this
-  // XCD's whole L2, and with it the K/V tiles of every other workgroup.
-  auto st_dev = [](float* a, float v) { __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
-  auto ld_dev = [](const float* a) { return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
-  {
-    float* wo = part_o(my_slot);
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x4_t v = {o[db][4 * q] * inv, o[db][4 * q + 1] * inv, o[db][4 * q + 2] * inv, o[db][4 * q + 3] * inv};
-        asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(wo + (4 * db + q) * 256), "v"(v) : "memory");
-      }
-    if (hf == 0) st_dev(p.ws_lse + my_slot * kWgRows + wrow, lse2);
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's partials have landed
-  __syncthreads();
-  if (tid == 0) {
-    const int old = __hip_atomic_fetch_add(p.ws_cnt + job, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    last_piece = old == p.parts - 1;
-    // every piece of this tile has counted: leave the counter at zero for the next call
-    if (last_piece) __hip_atomic_store(p.ws_cnt + job, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __syncthreads();
-  if (!last_piece) return;
-  if (!row_ok) return;
-  const size_t slot0 = (size_t)job * p.parts;  // workgroup index of piece 0 of this tile
-  float lse_j[kMaxPieces];
-  float mmax = kNegInf;
-#pragma unroll
-  for (int j = 0; j < kMaxPieces; ++j) {
-    lse_j[j] = j >= p.parts ? kNegInf : ld_dev(p.ws_lse + (slot0 + j) * kWgRows + wrow);
-    mmax = fmaxf(mmax, lse_j[j]);
-  }
-  f32x16_t acc[4];
-#pragma unroll
-  for (int db = 0; db < 4; ++db) acc[db] = zero_f32x16();
-  float wsum = 0.f;
-#pragma unroll
-  for (int j = 0; j < kMaxPieces; ++j) {
-    if (j >= p.parts) break;
-    const float w = lse_j[j] == kNegInf ? 0.f : fast_exp2(lse_j[j] - mmax);
-    wsum += w;
-    if (j == piece) {
-      // this workgroup's own piece, from registers: the same values it stored
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[db][r] = fmaf(w, o[db][r] * inv, acc[db][r]);
     } else {
-      const float* src = part_o(slot0 + j);
-      f32x4_t x[16];
+
+      // A piece: its normalised output and log2-sum-exp per row go to the workspace (a row
+      // that saw no key of this piece: zeros and -inf).  The piece that finishes last merges
+      // all pieces of the tile from the workspace (its own included), in piece order (so the
+      // result does not depend on which one that is), and writes the output.
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      const float lse2 = l_tot > 0.f ? m_run + __log2f(l_tot) : kNegInf;
+      // Partial layout (per piece, per wave): 16-byte chunk c = 4 db + q of every lane, then
+      // the lane -- each 16-byte store or load of a wave covers 1 KB of consecutive bytes.
+      const int wrow = wave * 32 + col;  // row of the workgroup, 0..255
+      const size_t my_slot = (size_t)job * p.parts + piece;  // piece j of a job: slot job * parts + j
+      auto part_o = [&](size_t sl) { return p.ws_o + ((sl * kWaves + wave) * 32 * kHeadDim + 4 * lane); };
+      // The partials are written and read with device-coherent accesses (the sc1 bit, as a
+      // relaxed agent-scope atomic access of this target has it), which go to the coherence
+      // point directly: a device-scope fence instead would write back and invalidate this
+      // XCD's whole L2, and with it the K/V tiles of every other workgroup.
+      auto st_dev = [](float* a, float v) { __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+      auto ld_dev = [](const float* a) { return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+      {
+        float* wo = part_o(my_slot);
 #pragma unroll
-      for (int c = 0; c < 16; ++c)
-        asm volatile("global_load_dwordx4 %0, %1, off sc1" : "=v"(x[c]) : "v"(src + c * 256) : "memory");
-      asm volatile("s_waitcnt vmcnt(0)"
-                   : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]), "+v"(x[7]),
-                     "+v"(x[8]), "+v"(x[9]), "+v"(x[10]), "+v"(x[11]), "+v"(x[12]), "+v"(x[13]), "+v"(x[14]), "+v"(x[15])
-                   :
-                   : "memory");
+        for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+          for (int q = 0; q < 4; ++q) {
+            const f32x4_t v = {o[db][4 * q] * inv, o[db][4 * q + 1] * inv, o[db][4 * q + 2] * inv,
+                               o[db][4 * q + 3] * inv};
+            // A VALU write to a register that an in-flight store of more than 8 bytes still
+            // reads as data needs wait states; the compiler does not insert them after inline
+            // assembly (without them the partials came out corrupted whenever the next
+            // store's values reused these registers), so the store brings its own.
+            asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 4"
+                         :
+                         : "v"(wo + (4 * db + q) * 256), "v"(v)
+                         : "memory");
+          }
+        if (hf == 0) st_dev(p.ws_lse + my_slot * kWgRows + wrow, lse2);
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's partials have landed
+      __syncthreads();
+      if (tid == 0) {
+        const int old = __hip_atomic_fetch_add(p.ws_cnt + job, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last_piece = old == p.parts - 1;
+        // every piece of this tile has counted: leave the counter at zero for the next call
+        if (last_piece) __hip_atomic_store(p.ws_cnt + job, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      __syncthreads();
+      if (last_piece && row_ok) {
+        const size_t slot0 = (size_t)job * p.parts;  // workgroup index of piece 0 of this tile
+        float lse_j[kMaxPieces];
+        float mmax = kNegInf;
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+        for (int j = 0; j < kMaxPieces; ++j) {
+          lse_j[j] = j >= p.parts ? kNegInf : ld_dev(p.ws_lse + (slot0 + j) * kWgRows + wrow);
+          mmax = fmaxf(mmax, lse_j[j]);
+        }
+        f32x16_t acc[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[db][4 * q + i] = fmaf(w, x[4 * db + q][i], acc[db][4 * q + i]);
+        for (int db = 0; db < 4; ++db) acc[db] = zero_f32x16();
+        float wsum = 0.f;
+#pragma unroll
+        for (int j = 0; j < kMaxPieces; ++j) {
+          if (j >= p.parts) break;
+          const float w = lse_j[j] == kNegInf ? 0.f : fast_exp2(lse_j[j] - mmax);
+          wsum += w;
+          {
+            const float* src = part_o(slot0 + j);
+            f32x4_t x[16];
+#pragma unroll
+            for (int c = 0; c < 16; ++c)
+              asm volatile("global_load_dwordx4 %0, %1, off sc1" : "=v"(x[c]) : "v"(src + c * 256) : "memory");
+            asm volatile("s_waitcnt vmcnt(0)"
+                         : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]),
+                           "+v"(x[7]), "+v"(x[8]), "+v"(x[9]), "+v"(x[10]), "+v"(x[11]), "+v"(x[12]), "+v"(x[13]),
+                           "+v"(x[14]), "+v"(x[15])
+                         :
+                         : "memory");
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[db][4 * q + i] = fmaf(w, x[4 * db + q][i], acc[db][4 * q + i]);
+          }
+        }
+        const float winv = 1.f / wsum;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int d = 32 * db + 8 * q + 4 * hf;
+            const float x0 = acc[db][4 * q + 0] * winv, x1 = acc[db][4 * q + 1] * winv;
+            const float x2 = acc[db][4 * q + 2] * winv, x3 = acc[db][4 * q + 3] * winv;
+            *(u32x2_t*)((uint16_t*)p.out + obase + d) = u32x2_t{pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
+          }
+        if (hf == 0 && p.lse != nullptr)
+          p.lse[((size_t)b * p.Lq + tq) * p.Hq + h] = (mmax + __log2f(wsum)) * kLn2;
+      }  // last piece
+    }  // piece
+    // next job: every wave is done with this one's LDS stages and shared flags
+    if (tid == 0) next_slot = claimed;
+    __syncthreads();
+    slot = next_slot;
+  }  // jobs
+  // The workgroup that finishes last leaves the queue at zero for the next call.  Each
+  // workgroup counts after its last claim has returned, so the last count comes after
+  // every claim.
+  if (tid == 0 && p.queue != nullptr) {
+    const int done = __hip_atomic_fetch_add(p.queue + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (done == (int)gridDim.x - 1) {
+      __hip_atomic_store(p.queue, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(p.queue + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  const float winv = 1.f / wsum;
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int d = 32 * db + 8 * q + 4 * hf;
-      const float x0 = acc[db][4 * q + 0] * winv, x1 = acc[db][4 * q + 1] * winv;
-      const float x2 = acc[db][4 * q + 2] * winv, x3 = acc[db][4 * q + 3] * winv;
-      *(u32x2_t*)((uint16_t*)p.out + obase + d) = u32x2_t{pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
-    }
-  if (hf == 0 && p.lse != nullptr)
-    p.lse[((size_t)b * p.Lq + tq) * p.Hq + h] = (mmax + __log2f(wsum)) * kLn2;
 }
 
 }  // namespace
 
 hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream) {
   const long long per_tile = (long long)p.B * p.Hkv * p.n_hg;
-  const long long grid = ((long long)p.n_tok_tiles - p.n_split) * per_tile + (long long)p.n_split * per_tile * p.parts;
+  long long grid = ((long long)p.n_tok_tiles - p.n_split) * per_tile + (long long)p.n_split * per_tile * p.parts;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  // with a queue: one workgroup per compute unit, each running jobs until none is left
+  if (p.queue != nullptr && grid > p.queue_workgroups) grid = p.queue_workgroups;
   hipLaunchKernelGGL(prefill_bf16_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }

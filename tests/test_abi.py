@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.rattn_abi_version() == rb.ABI_VERSION == 3
+    assert lib.rattn_abi_version() == rb.ABI_VERSION == 4
 
 
 def _prefill(lib, **kw):
@@ -141,15 +141,19 @@ def _tile_keys(Lq, Lk, window, rows, tile):
     return (off + T1 - 1) // 64 + 1 - max(0, off + T0 - weff + 1) // 64
 
 
+QUEUE_BYTES = 256  # the job queue and its done counter, at the start of every bf16 workspace
+
+
 def _split_bytes(jobs, parts):
     align = lambda n: (n + 255) // 256 * 256  # noqa: E731
     pieces = jobs * parts
-    return align(align(jobs * 4) + pieces * 256 * 4) + pieces * 256 * 128 * 4
+    return align(align(QUEUE_BYTES + jobs * 4) + pieces * 256 * 4) + pieces * 256 * 128 * 4
 
 
 def test_prefill_split_plan(lib):
     # forced split: every 256-row tile (32 tokens x 8 heads) with >= 2n key tiles -> n pieces,
-    # workspace = per-tile counters + a log2-sum-exp and a 128-float partial per piece row
+    # workspace = the job queue + per-tile counters + a log2-sum-exp and a 128-float partial
+    # per piece row
     for (B, Lq, Lk, Hq, Hkv, W, n) in [(1, 1000, 1000, 16, 2, 0, 2), (2, 300, 5000, 8, 1, 0, 3),
                                        (1, 4096, 4096, 16, 2, 1024, 4)]:
         G = Hq // Hkv
@@ -158,14 +162,15 @@ def test_prefill_split_plan(lib):
         n_tiles = -(-Lq // rows)
         n_split = sum(1 for t in range(n_tiles) if _tile_keys(Lq, Lk, W, rows, t) >= 2 * n)
         jobs = n_split * B * Hkv * (G // hpw)
-        want = _split_bytes(jobs, n) if n_split else 0
+        want = _split_bytes(jobs, n) if n_split else QUEUE_BYTES
         assert rb.rattn_prefill_workspace_bytes(B, Lq, Lk, Hq, Hkv, W, rb.RATTN_BF16, n) == want
     # the library's own plan: a long sliding-window prefill is split, a long chunked prefill
-    # (whose tiles differ in length and balance by themselves) and fp32 inputs are not
-    assert rb.rattn_prefill_workspace_bytes(1, 8192, 8192, 16, 2, 4096, rb.RATTN_BF16, 0) > 0
-    assert rb.rattn_prefill_workspace_bytes(1, 8192, 32768, 16, 2, 0, rb.RATTN_BF16, 0) == 0
+    # (whose tiles differ in length and balance by themselves) is not; fp32 inputs use no
+    # workspace; an unsplit bf16 plan needs the job queue only
+    assert rb.rattn_prefill_workspace_bytes(1, 8192, 8192, 16, 2, 4096, rb.RATTN_BF16, 0) > QUEUE_BYTES
+    assert rb.rattn_prefill_workspace_bytes(1, 8192, 32768, 16, 2, 0, rb.RATTN_BF16, 0) == QUEUE_BYTES
     assert rb.rattn_prefill_workspace_bytes(1, 8192, 8192, 16, 2, 4096, rb.RATTN_FP32, 0) == 0
-    assert rb.rattn_prefill_workspace_bytes(1, 8192, 8192, 16, 2, 4096, rb.RATTN_BF16, 1) == 0
+    assert rb.rattn_prefill_workspace_bytes(1, 8192, 8192, 16, 2, 4096, rb.RATTN_BF16, 1) == QUEUE_BYTES
     assert rb.rattn_prefill_workspace_bytes(1, 0, 8, 16, 2, 0, rb.RATTN_BF16, 0) == 0
 
 

@@ -8,6 +8,7 @@
 * With one-hot V rows the output is the attention weights: they match the oracle's
   probabilities and every row of weights sums to one.
 * Repeated calls are bitwise identical.
+* The prefill job queue changes nothing, bitwise, and is left at zero.
 * Empty calls are no-ops that touch nothing.
 """
 import numpy as np
@@ -137,7 +138,40 @@ def test_key_split_only_reorders_sums():
         assert _bitwise_equal(o1, o2) and _bitwise_equal(l1, l2)
         assert (o1.float() - ref_o.float()).abs().max().item() <= 8e-3  # one bf16 ulp near 1
         assert (l1 - ref_l).abs().max().item() <= 1e-5
-        assert int(ws[:256].count_nonzero()) == 0
+        # the job queue (first 256 bytes) and the per-tile counters after it (at most
+        # 63 tiles x 2 jobs here) are left at zero
+        assert int(ws[:256 + 4 * 126].count_nonzero()) == 0
+
+
+@pytest.mark.parametrize("B,L,window", [(2, 4096, 0), (1, 6000, 1500)])
+def test_job_queue_matches_one_workgroup_per_tile(B, L, window):
+    """With a workspace the launch has one workgroup per compute unit taking query tiles
+    from a queue (here more tiles than compute units); without one, one workgroup per tile.
+    Unsplit, the two are the same bit for bit, and the queue is left at zero."""
+    print(f"case job queue B={B} L={L} window={window}", flush=True)
+    case = synth.make_prefill(51, B, L, L, 16, 2, 1000, window, "bf16")
+    q, k, v, r = dev(case.q), dev(case.k), dev(case.v), dev(case.bias)
+    lib = rb.load()
+    outs = []
+    for use_ws in (False, True):
+        out = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+        n = rb.rattn_prefill_workspace_bytes(B, L, L, 16, 2, window, rb.RATTN_BF16, 1)
+        assert n == 256
+        ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
+        for _ in range(2):
+            st = lib.rattn_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), r.data_ptr(), out.data_ptr(),
+                                   lse.data_ptr(), B, L, L, 16, 2, 128, 1000, window, rb.RATTN_BF16, 1,
+                                   ws.data_ptr() if use_ws else None, n if use_ws else 0, None)
+            assert st == rb.RATTN_OK
+        torch.cuda.synchronize()
+        assert int(ws.count_nonzero()) == 0
+        outs.append((out, lse))
+    assert _bitwise_equal(outs[0][0], outs[1][0]) and _bitwise_equal(outs[0][1], outs[1][1])
+    ref_o, ref_l = rb.prefill(q, k, v, r, window)  # the library's plan (maybe split), queued
+    torch.cuda.synchronize()
+    assert (ref_o.float() - outs[0][0].float()).abs().max().item() <= 8e-3
+    assert (ref_l - outs[0][1]).abs().max().item() <= 1e-5
 
 
 def test_one_hot_values_expose_the_weights():
