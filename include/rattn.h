@@ -94,10 +94,10 @@ size_t rattn_prefill_workspace_bytes(int B, int Lq, int Lk, int Hq, int Hkv, int
  * kv_splits: 0 = the library's plan (a split only where it shortens the launch), 1 = no
  * split, n in 2..8 = split every query tile with at least 2n key tiles of 64 into n pieces.
  * A split changes only the summation order of the result.
- * Workspace: its first bytes hold the job queue and per-tile counters, which must be zero
- * when the workspace is first used; every completed call leaves them zero again, so a
- * workspace zero-filled once can be reused by later calls of any size it is large enough
- * for.  Calls that share a workspace must not run concurrently.  With or without a
+ * Workspace: its first 256 bytes + 256 KB hold the job queue and the per-tile split
+ * counters (at the same place for every plan), which must be zero when the workspace is
+ * first used; every completed call leaves them zero again, so a workspace zero-filled
+ * once can be reused by later calls of any size and plan it is large enough for.  Calls that share a workspace must not run concurrently.  With or without a
  * workspace, and whichever workgroup runs which tile, the result is the same bit for bit
  * for a given plan.
  * B == 0 or Lq == 0 is a no-op returning RATTN_OK (pointers may then be NULL).

@@ -136,12 +136,17 @@ int prefill_tile_keys(const rattn::PrefillParams& p, int tile) {
   return (int)(ke - kb);
 }
 
-// Workspace of a bf16 prefill: [256 B: job queue] [split counters] [partial lse] [partial O]
+// Workspace of a bf16 prefill: [256 B: job queue] [256 KB: split counters] [partial lse]
+// [partial O].  The counters sit at the same place for every plan, so a workspace reused
+// by calls of different plans never finds one call's partial results under another's
+// counters (which must start at zero; every call leaves the queue and counters at zero).
 struct PrefillSplit {
   int n_split = 0, parts = 1;
   size_t cnt_off = 0, lse_off = 0, o_off = 0, ws_bytes = 0;
 };
 constexpr size_t kQueueBytes = 256;
+constexpr size_t kCounterBytes = 256 * 1024;
+constexpr long long kMaxSplitJobs = kCounterBytes / sizeof(int);
 
 // With a queue, a launch has one workgroup per compute unit and each takes the next job
 // slot when it finishes one: the plan simulates that on the 256 compute units of an MI355X.
@@ -175,7 +180,7 @@ PrefillSplit split_layout(const rattn::PrefillParams& p, int n_split, int parts)
   sp.parts = parts;
   const size_t per_tile = (size_t)p.B * p.Hkv * p.n_hg;
   const size_t jobs = (size_t)n_split * per_tile, pieces = jobs * parts;
-  sp.lse_off = (sp.cnt_off + jobs * sizeof(int) + 255) & ~(size_t)255;
+  sp.lse_off = sp.cnt_off + kCounterBytes;
   sp.o_off = (sp.lse_off + pieces * 256 * sizeof(float) + 255) & ~(size_t)255;
   sp.ws_bytes = sp.o_off + pieces * 256 * 128 * sizeof(float);
   return sp;
@@ -187,13 +192,15 @@ PrefillSplit plan_prefill_split_uncached(const rattn::PrefillParams& p, int dtyp
   const int nt = p.n_tok_tiles;
   std::vector<int> keys(nt);
   for (int t = 0; t < nt; ++t) keys[t] = prefill_tile_keys(p, t);  // non-decreasing in t
+  const long long per_tile = (long long)p.B * p.Hkv * p.n_hg;
+  const int max_split = (int)std::min<long long>(nt, kMaxSplitJobs / per_tile);  // counters
   if (kv_splits >= 2) {
-    // split every token tile with at least 2 * kv_splits key tiles
+    // split every token tile with at least 2 * kv_splits key tiles (the heaviest ones
+    // while the counters last)
     int n_split = 0;
-    while (n_split < nt && keys[nt - 1 - n_split] >= 2 * kv_splits) ++n_split;
+    while (n_split < max_split && keys[nt - 1 - n_split] >= 2 * kv_splits) ++n_split;
     return split_layout(p, n_split, kv_splits);
   }
-  const long long per_tile = (long long)p.B * p.Hkv * p.n_hg;
   if ((long long)nt * per_tile * rattn::kMaxPieces > 0x7fffffffLL) return split_layout(p, 0, 1);
   // job sizes in grid order, pieces mapped to workgroups as the kernel does
   auto jobs_of = [&](int n_split, int parts) {
@@ -215,12 +222,23 @@ PrefillSplit plan_prefill_split_uncached(const rattn::PrefillParams& p, int dtyp
   // a grid that already finishes within 5 % of an even spread is left alone
   if (best <= 1.05 * total / kDispatchUnits) return split_layout(p, 0, 1);
   int best_split = 0, best_parts = 1;
+  // candidates: the tiles with at least some number of key tiles (2 parts, and fractions
+  // of the longest), and the heaviest n tiles for n a multiple of nt / 16 (the tiles of a
+  // sliding-window prefill past its window all have the same length, and splitting only
+  // some of them can balance better than splitting all)
   const int kmax = keys[nt - 1];
+  std::vector<int> counts;
+  for (int frac = 0; frac <= 3; ++frac) {
+    const int thr = std::max(4, kmax * frac / 4);
+    int n_split = 0;
+    while (n_split < nt && keys[nt - 1 - n_split] >= thr) ++n_split;
+    counts.push_back(n_split);
+  }
+  for (int k = 1; k <= 16; ++k) counts.push_back((int)((long long)nt * k / 16));
   for (int parts = 2; parts <= 4; ++parts)
-    for (int frac = 0; frac <= 3; ++frac) {
-      const int thr = std::max(2 * parts, kmax * frac / 4);
-      int n_split = 0;
-      while (n_split < nt && keys[nt - 1 - n_split] >= thr) ++n_split;
+    for (int n_split : counts) {
+      n_split = std::min(n_split, max_split);
+      while (n_split > 0 && keys[nt - n_split] < 2 * parts) --n_split;  // pieces of >= 2 key tiles
       if (n_split == 0) continue;
       const double m = simulate_dispatch(jobs_of(n_split, parts));
       if (m < 0.97 * best) {

@@ -142,12 +142,13 @@ def _tile_keys(Lq, Lk, window, rows, tile):
 
 
 QUEUE_BYTES = 256  # the job queue and its done counter, at the start of every bf16 workspace
+COUNTER_BYTES = 256 * 1024  # split counters, at the same place for every plan
 
 
 def _split_bytes(jobs, parts):
     align = lambda n: (n + 255) // 256 * 256  # noqa: E731
     pieces = jobs * parts
-    return align(align(QUEUE_BYTES + jobs * 4) + pieces * 256 * 4) + pieces * 256 * 128 * 4
+    return align(QUEUE_BYTES + COUNTER_BYTES + pieces * 256 * 4) + pieces * 256 * 128 * 4
 
 
 def test_prefill_split_plan(lib):
