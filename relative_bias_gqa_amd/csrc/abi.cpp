@@ -141,7 +141,7 @@ int prefill_tile_keys(const rattn::PrefillParams& p, int tile) {
 // by calls of different plans never finds one call's partial results under another's
 // counters (which must start at zero; every call leaves the queue and counters at zero).
 struct PrefillSplit {
-  int n_split = 0, parts = 1;
+  int n_split = 0, parts = 1, n_big = 0;
   size_t cnt_off = 0, lse_off = 0, o_off = 0, ws_bytes = 0;
 };
 constexpr size_t kQueueBytes = 256;
@@ -196,17 +196,32 @@ PrefillSplit plan_prefill_split_uncached(const rattn::PrefillParams& p, int dtyp
   for (int t = 0; t < nt; ++t) keys[t] = prefill_tile_keys(p, t);  // non-decreasing in t
   const long long per_tile = (long long)p.B * p.Hkv * p.n_hg;
   const int max_split = (int)std::min<long long>(nt, kMaxSplitJobs / per_tile);  // counters
+  // Job order: the unsplit tiles longer than the longest piece, the pieces, the other
+  // unsplit tiles (each list from the heaviest down), so the queue starts the longest
+  // jobs first.
+  auto big_of = [&](int n_split, int parts) {
+    if (n_split == 0) return 0;
+    const int longest_piece = (keys[nt - 1] + parts - 1) / parts;
+    int n_big = 0;
+    while (n_split + n_big < nt && keys[nt - 1 - n_split - n_big] > longest_piece) ++n_big;
+    return n_big;
+  };
   if (kv_splits >= 2) {
     // split every token tile with at least 2 * kv_splits key tiles (the heaviest ones
     // while the counters last)
     int n_split = 0;
     while (n_split < max_split && keys[nt - 1 - n_split] >= 2 * kv_splits) ++n_split;
-    return split_layout(p, n_split, kv_splits);
+    PrefillSplit sp = split_layout(p, n_split, kv_splits);
+    sp.n_big = big_of(n_split, kv_splits);
+    return sp;
   }
   if ((long long)nt * per_tile * rattn::kMaxPieces > 0x7fffffffLL) return split_layout(p, 0, 1);
-  // job sizes in grid order, pieces mapped to workgroups as the kernel does
+  // job sizes in queue order, pieces mapped to slots as the kernel does
   auto jobs_of = [&](int n_split, int parts) {
     std::vector<double> jobs;
+    const int n_big = big_of(n_split, parts);
+    for (int t = nt - 1 - n_split; t >= nt - n_split - n_big; --t)
+      for (long long r = 0; r < per_tile; ++r) jobs.push_back(keys[t] + kWgOverhead);
     const long long n_jobs = (long long)n_split * per_tile;
     for (long long w = 0; w < n_jobs * parts; ++w) {
       int job, piece;
@@ -214,7 +229,7 @@ PrefillSplit plan_prefill_split_uncached(const rattn::PrefillParams& p, int dtyp
       const int k = keys[nt - 1 - (int)(job / per_tile)];
       jobs.push_back(k * (piece + 1) / parts - k * piece / parts + kPieceOverhead);
     }
-    for (int t = nt - 1 - n_split; t >= 0; --t)
+    for (int t = nt - 1 - n_split - n_big; t >= 0; --t)
       for (long long r = 0; r < per_tile; ++r) jobs.push_back(keys[t] + kWgOverhead);
     return jobs;
   };
@@ -256,6 +271,9 @@ PrefillSplit plan_prefill_split_uncached(const rattn::PrefillParams& p, int dtyp
       }
     }
   if (best_split == 0 || best_m >= 0.97 * best) return split_layout(p, 0, 1);
+  PrefillSplit sp = split_layout(p, best_split, best_parts);
+  sp.n_big = big_of(best_split, best_parts);
+  return sp;
   return split_layout(p, best_split, best_parts);
 }
 
@@ -337,6 +355,7 @@ int rattn_prefill(const void* q, const void* k, const void* v, const float* bias
     return fail(RATTN_ERR_WORKSPACE, "rattn_prefill: workspace of %zu bytes, %zu needed", workspace_bytes,
                 sp.ws_bytes);
   p.n_split = sp.n_split;
+  p.n_big = sp.n_big;
   p.parts = sp.parts;
   p.queue = sp.ws_bytes ? (int*)workspace : nullptr;
   p.queue_workgroups = p.queue ? compute_units() : 0;

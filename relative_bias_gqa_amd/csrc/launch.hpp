@@ -27,6 +27,7 @@ struct PrefillParams {
   // which merge through the workspace (n_split = 0, parts = 1: no split).
   int n_split;
   int parts;
+  int n_big;      // unsplit token tiles (the heaviest ones) scheduled before the pieces
   float* ws_o;    // [n_split * B * Hkv * n_hg * parts, 256 rows, 128] normalised partials
   float* ws_lse;  // [same, 256 rows] log2-sum-exp of each partial
   int* ws_cnt;    // [n_split * B * Hkv * n_hg] finished pieces; zero between calls
@@ -36,11 +37,11 @@ struct PrefillParams {
 
 constexpr int kMaxPieces = 8;
 
-// Workgroup w (< n_jobs * parts) of a split prefill grid takes piece *piece of job *job.
-// Workgroup w runs on XCD w % 8, so in each group of 8 * parts workgroups (8 jobs),
-// workgroup x + 8 k takes piece k of job x: the pieces of a job share an XCD, and the
-// merges (done by whichever piece of a job finishes last) spread over all XCDs.  A last,
-// partial group keeps the pieces of a job adjacent.
+// Piece slot w (< n_jobs * parts) of a split prefill takes piece *piece of job *job.  In
+// each group of 8 * parts slots (8 jobs), slot x + 8 k takes piece k of job x: the pieces
+// of a job are 8 slots apart, so in the first round of workgroups (workgroup i runs on
+// XCD i % 8) they share an XCD, and the merges (done by whichever piece of a job finishes
+// last) spread over all XCDs.  A last, partial group keeps the pieces of a job adjacent.
 __host__ __device__ inline void prefill_piece_of(long long w, long long n_jobs, int parts, int* job, int* piece) {
   const long long full = n_jobs / 8 * 8 * parts;
   if (w < full) {

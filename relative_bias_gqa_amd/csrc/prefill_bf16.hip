@@ -64,19 +64,23 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   const int col = lane & 31;  // accumulator column = query token within the wave
   const int hf = lane >> 5;   // which half of the key rows this lane holds
 
-  // ---- jobs: heaviest (last) token tiles first ---------------------------------------
-  // Job slot s < n_piece_slots takes one of `parts` pieces of the key range of one of the
-  // n_split heaviest token tiles; the others take whole token tiles.  Both lists run from
-  // the heaviest tile down.  A workgroup runs slot blockIdx.x, then (with a queue) the
-  // next unclaimed slot, until none is left: the output stores of one job drain while
-  // the next one runs.
+  // ---- jobs: longest first -------------------------------------------------------------
+  // Slots: the n_big heaviest unsplit token tiles (longer than any piece), then the
+  // `parts` pieces of the key ranges of the n_split heaviest token tiles, then the other
+  // unsplit tiles, each list from the heaviest tile down.  A workgroup runs slot
+  // blockIdx.x, then (with a queue) the next unclaimed slot, until none is left: the
+  // output stores of one job drain while the next one runs.
   const int per_tile = p.B * p.Hkv * p.n_hg;
   const int n_piece_slots = p.n_split * per_tile * p.parts;
   const int n_slots = n_piece_slots + (p.n_tok_tiles - p.n_split) * per_tile;
+  const int n_big_slots = p.n_big * per_tile;
   for (int slot = blockIdx.x; slot < n_slots;) {
-    const bool is_piece = slot < n_piece_slots;
-    int job = slot - n_piece_slots + p.n_split * per_tile, piece = 0;
-    if (is_piece) prefill_piece_of(slot, (long long)p.n_split * per_tile, p.parts, &job, &piece);
+    const bool is_piece = slot >= n_big_slots && slot < n_big_slots + n_piece_slots;
+    int job, piece = 0;
+    if (is_piece)
+      prefill_piece_of(slot - n_big_slots, (long long)p.n_split * per_tile, p.parts, &job, &piece);
+    else
+      job = p.n_split * per_tile + (slot < n_big_slots ? slot : slot - n_piece_slots);
     const int tile = p.n_tok_tiles - 1 - job / per_tile;
     const int rem = job % per_tile;
     const int hg = rem % p.n_hg;
