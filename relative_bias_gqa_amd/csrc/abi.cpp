@@ -49,7 +49,7 @@ constexpr float kScaleLog2 = 1.4426950408889634f * 0.08838834764831845f;  // log
 constexpr int kAutoWorkgroups = 256;  // one per compute unit of an MI355X
 
 struct DecodePlan {
-  int gs, n_hs, KH, rows, SL, P, batch, KS;
+  int gs, n_hs, KH, rows, SL, P, batch, KS, NW;
   size_t lse_off, total;
 };
 
@@ -59,7 +59,7 @@ bool plan_decode(int B, int n_q, int Hq, int Hkv, int max_ctx_len, int max_block
     return false;
   const int G = Hq / Hkv;
   const int SL = rattn::kDecodeUnit - 1 + n_q;
-  // query heads per segment: the largest divisor of G whose rows fit four waves and whose
+  // query heads per segment: the largest divisor of G whose rows fit four 32-row blocks and whose
   // bias slices fit the per-unit staging buffer
   int gs = 0;
   for (int d = G; d >= 1; --d) {
@@ -81,8 +81,10 @@ bool plan_decode(int B, int n_q, int Hq, int Hkv, int max_ctx_len, int max_block
   if (batch > cap) batch = cap;
   const int P = num_splits > 0 ? num_splits : kAutoWorkgroups;
   const long long rows = (long long)n_q * gs;
-  // up to two row blocks of 32: the two 32-key halves of a unit go to different waves
-  const int KS = rows <= 64 ? 2 : 1;
+  // the two 32-key halves of a unit go to different waves, one wave per (32-row block, key
+  // half): four waves up to two row blocks, eight (two per SIMD) up to four
+  const int KS = 2;
+  const int NW = rows <= 64 ? 4 : 8;
   const long long slots = (P + batch * KH) * KS;
   if (batch * KH * rows > 0x7fffffffLL) return false;
   pl->gs = gs;
@@ -93,6 +95,7 @@ bool plan_decode(int B, int n_q, int Hq, int Hkv, int max_ctx_len, int max_block
   pl->P = P;
   pl->batch = (int)batch;
   pl->KS = KS;
+  pl->NW = NW;
   const size_t o_bytes = (size_t)slots * (size_t)rows * 128 * sizeof(float);
   pl->lse_off = (o_bytes + 255) & ~(size_t)255;
   pl->total = pl->lse_off + (size_t)slots * (size_t)rows * sizeof(float);
@@ -447,6 +450,7 @@ int rattn_decode_paged(const void* q, const void* k_cache, const void* v_cache, 
   p.rows = pl.rows;
   p.SL = pl.SL;
   p.KS = pl.KS;
+  p.NW = pl.NW;
   p.P = pl.P;
   p.scale_log2 = kScaleLog2;
   const size_t q_rows = (size_t)n_q * Hq;

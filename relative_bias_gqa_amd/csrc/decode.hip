@@ -36,7 +36,7 @@
 namespace rattn {
 namespace {
 
-constexpr int kThreads = 256;  // 4 waves
+constexpr int kThreads = 256;  // merge kernel: 4 waves
 constexpr int kUnit = kDecodeUnit;  // 64 tokens per unit / pipeline stage
 constexpr int kStages = 4;
 constexpr int kKVBytes = kUnit * kHeadDim * 2;           // 16 KB of K (or V) per stage
@@ -80,10 +80,11 @@ __device__ __forceinline__ SeqInfo seq_info(const DecodeParams& p, int b) {
 }
 
 // Exclusive prefix of visible units over the sequences, pre[0..B], computed by the whole
-// workgroup into LDS.  Returns pre[B].
+// workgroup (NT threads) into LDS.  Returns pre[B].
+template <int NT>
 __device__ int batch_prefix(const DecodeParams& p, int* pre, int* scratch) {
   const int tid = threadIdx.x;
-  const int per = (p.B + kThreads - 1) / kThreads;
+  const int per = (p.B + NT - 1) / NT;
   int local = 0;
   for (int i = 0; i < per; ++i) {
     const int b = tid * per + i;
@@ -91,7 +92,7 @@ __device__ int batch_prefix(const DecodeParams& p, int* pre, int* scratch) {
   }
   scratch[tid] = local;
   __syncthreads();
-  for (int off = 1; off < kThreads; off <<= 1) {
+  for (int off = 1; off < NT; off <<= 1) {
     const int v = tid >= off ? scratch[tid - off] : 0;
     __syncthreads();
     scratch[tid] += v;
@@ -105,7 +106,7 @@ __device__ int batch_prefix(const DecodeParams& p, int* pre, int* scratch) {
       run += seq_info(p, b).nch;
     }
   }
-  if (tid == kThreads - 1) pre[p.B] = scratch[tid];
+  if (tid == NT - 1) pre[p.B] = scratch[tid];
   __syncthreads();
   return pre[p.B];
 }
@@ -146,15 +147,21 @@ __device__ __forceinline__ void cursor_next(const DecodeParams& p, Cursor& c) {
   }
 }
 
-// KS: waves sharing the keys of a unit (2: one 32-key half each; 1: a wave takes both).
-// NB: bias loads per wave and unit (64 floats each), NB * 256 >= gs * SL.
-template <int KS, int NB>
-__global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeParams p) {
-  constexpr int KB = 2 / KS;  // 32-key blocks per computing wave and unit
-  constexpr int kLoadsPerStage = 8 + NB;
+// NW: waves per workgroup (4, or 8 = two per SIMD, so that one wave's softmax overlaps
+// its partner's MFMAs).  KS: waves sharing the keys of a unit (2: one 32-key half each;
+// 1: a wave takes both).  NB: bias loads per wave and unit (64 floats each),
+// NB * 64 * NW >= gs * SL.
+template <int NW, int KS, int NB>
+__global__ __launch_bounds__(64 * NW, 1) void decode_split_kernel(DecodeParams p) {
+  constexpr int NT = 64 * NW;
+  constexpr int KB = 2 / KS;       // 32-key blocks per computing wave and unit
+  constexpr int TPW = kUnit / NW;  // tokens of a unit loaded by one wave
+  constexpr int NI = TPW / 4;      // K (and V) load instructions per wave and unit
+  constexpr int kLoadsPerStage = 2 * NI + NB;
+  static_assert(NI >= 1 && NI * 4 * NW == kUnit, "load split");
   __shared__ __attribute__((aligned(1024))) unsigned char ring[kStages * kStageBytes];
   __shared__ int pre[kDecodeMaxBatch + 1];
-  __shared__ int scratch[kThreads];
+  __shared__ int scratch[NT];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -162,7 +169,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeParams 
   const int col = lane & 31;
   const int hf = lane >> 5;
 
-  const int units = batch_prefix(p, pre, scratch) * p.KH;
+  const int units = batch_prefix<NT>(p, pre, scratch) * p.KH;
   const int P = min(p.P, units);
   const int w = blockIdx.x;
   if (w >= P) return;  // uniform
@@ -170,15 +177,15 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeParams 
   const int n_units = (int)((long long)(w + 1) * units / P) - u0;
 
   // ---- loads of one unit into a stage -------------------------------------------------
-  // K/V: wave `wave` issues tokens 16 wave .. 16 wave + 15 of the 64-token unit, four
-  // tokens (1 KB) per instruction; lane i of instruction m fetches 16-byte chunk
+  // K/V: wave `wave` issues tokens TPW wave .. TPW wave + TPW - 1 of the 64-token unit,
+  // four tokens (1 KB) per instruction; lane i of instruction m fetches 16-byte chunk
   // (i & 15) ^ swz(tok) of token tok = 4 m + i / 16, which lands at LDS chunk i & 15.
   // Per-lane byte offsets are fixed; a unit only adds its block base.
-  uint32_t koff[4], voff[4], kz[4], vz[4];
-  int ktok[4];
+  uint32_t koff[NI], voff[NI], kz[NI], vz[NI];
+  int ktok[NI];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int tok = 16 * wave + 4 * i + (lane >> 4);
+  for (int i = 0; i < NI; ++i) {
+    const int tok = TPW * wave + 4 * i + (lane >> 4);
     const int slot = lane & 15;
     const int ck = slot ^ (tok & 15);
     const int cv = slot ^ ((tok & 7) << 1);
@@ -188,7 +195,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeParams 
     kz[i] = ck * 16;
     vz[i] = cv * 16;
   }
-  // Bias: NB * 256 floats per stage; entry g * SL + x = r[h_g, clamp(d0 + x, 0, R - 1)].
+  // Bias: NB * 64 * NW floats per stage; entry g * SL + x = r[h_g, clamp(d0 + x, 0, R - 1)].
   int bias_g[NB], bias_x[NB];
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
@@ -210,12 +217,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeParams 
     const size_t base = (((size_t)phys * 128 + (ic.c & 1) * kUnit) * p.Hkv + kvh) * 256;
     const unsigned char* kb_ = kc_bytes + base;
     const unsigned char* vb_ = vc_bytes + base;
-    const uint32_t kdst = ring_base + st * kStageBytes + wave * 4096;
+    const uint32_t kdst = ring_base + st * kStageBytes + wave * (TPW * 256);
     const uint32_t vdst = kdst + kKVBytes;
     const uint32_t bdst = ring_base + st * kStageBytes + 2 * kKVBytes + wave * (NB * 256);
     const bool interior = j0 >= ic.si.vis_lo && j0 + kUnit <= ic.si.ctx;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < NI; ++i) {
       const unsigned char* gk = kb_ + koff[i];
       const unsigned char* gv = vb_ + voff[i];
       if (!interior) {
@@ -246,7 +253,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeParams 
   // With at most two row blocks the two 32-key halves of a unit go to different waves,
   // which keep separate online-softmax states (separate pieces for the merge kernel).
   const int n_rb = (p.rows + 31) / 32;
-  const int rb_span = KS == 2 ? n_rb : 4;
+  const int rb_span = KS == 2 ? n_rb : NW;
   const int rb = wave % rb_span;
   const int ks_w = wave / rb_span;
   const bool wave_active = rb < n_rb && ks_w < KS;
@@ -615,23 +622,32 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   const long long grid2 = (long long)p.B * p.KH * p.rows;
   if (p.B <= 0) return hipSuccess;
   if (grid2 > 0x7fffffffLL || p.P < 1) return hipErrorInvalidConfiguration;
-  const int nb = (p.gs * p.SL + 255) / 256;  // bias loads per wave and unit
-  if (nb < 1 || nb > 4 || (p.KS != 1 && p.KS != 2)) return hipErrorInvalidConfiguration;
-  const dim3 grid((unsigned)p.P), block(kThreads);
-#define RATTN_SPLIT(KS_, NB_) hipLaunchKernelGGL((decode_split_kernel<KS_, NB_>), grid, block, 0, stream, p)
-  if (p.KS == 2) {
+  if ((p.NW != 4 && p.NW != 8) || (p.KS != 1 && p.KS != 2)) return hipErrorInvalidConfiguration;
+  // every computing role (32-row block, key share) needs a wave of its own
+  const int n_rb = (p.rows + 31) / 32;
+  if (p.KS == 2 ? n_rb * 2 > p.NW : n_rb > p.NW) return hipErrorInvalidConfiguration;
+  const int nb = (p.gs * p.SL + 64 * p.NW - 1) / (64 * p.NW);  // bias loads per wave and unit
+  if (nb < 1 || nb * 64 * p.NW > kDecodeBiasFloats) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)p.P);
+#define RATTN_SPLIT(NW_, KS_, NB_) \
+  hipLaunchKernelGGL((decode_split_kernel<NW_, KS_, NB_>), grid, dim3(64 * NW_), 0, stream, p)
+  if (p.NW == 8) {
+    if (p.KS != 2) return hipErrorInvalidConfiguration;
+    if (nb == 1) RATTN_SPLIT(8, 2, 1);
+    else RATTN_SPLIT(8, 2, 2);
+  } else if (p.KS == 2) {
     switch (nb) {
-      case 1: RATTN_SPLIT(2, 1); break;
-      case 2: RATTN_SPLIT(2, 2); break;
-      case 3: RATTN_SPLIT(2, 3); break;
-      default: RATTN_SPLIT(2, 4); break;
+      case 1: RATTN_SPLIT(4, 2, 1); break;
+      case 2: RATTN_SPLIT(4, 2, 2); break;
+      case 3: RATTN_SPLIT(4, 2, 3); break;
+      default: RATTN_SPLIT(4, 2, 4); break;
     }
   } else {
     switch (nb) {
-      case 1: RATTN_SPLIT(1, 1); break;
-      case 2: RATTN_SPLIT(1, 2); break;
-      case 3: RATTN_SPLIT(1, 3); break;
-      default: RATTN_SPLIT(1, 4); break;
+      case 1: RATTN_SPLIT(4, 1, 1); break;
+      case 2: RATTN_SPLIT(4, 1, 2); break;
+      case 3: RATTN_SPLIT(4, 1, 3); break;
+      default: RATTN_SPLIT(4, 1, 4); break;
     }
   }
 #undef RATTN_SPLIT

@@ -83,7 +83,8 @@ struct DecodeParams {
   int KH;         // Hkv * n_hs segments per sequence
   int rows;       // n_q * gs query rows per segment
   int SL;         // bias entries per head staged for one unit: 63 + n_q
-  int KS;         // waves sharing a unit's keys (2 when rows <= 64, else 1)
+  int KS;         // waves sharing a unit's keys (2: one 32-key half each, 1: both halves)
+  int NW;         // waves per split workgroup (4, or 8 when rows > 64)
   int P;          // split workgroups
   float scale_log2;
 };
@@ -91,7 +92,7 @@ struct DecodeParams {
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 
 // Decode limits the host must respect.
-constexpr int kDecodeMaxRows = 128;       // n_q * gs (four waves of 32 rows)
+constexpr int kDecodeMaxRows = 128;       // n_q * gs (four blocks of 32 rows)
 constexpr int kDecodeBiasFloats = 1024;   // gs * (63 + n_q) per unit
 constexpr int kDecodeMaxBatch = 2048;     // sequences per launch (prefix table in LDS)
 constexpr int kDecodeUnit = 64;           // tokens per unit

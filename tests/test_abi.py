@@ -123,8 +123,7 @@ def test_workspace_and_split_plan(lib):
         G = Hq // Hkv
         KH = Hkv * (G // gs)
         rows = n_q * gs
-        KS = 2 if rows <= 64 else 1   # key halves of a unit on separate waves for small row counts
-        slots = (P + B * KH) * KS
+        slots = (P + B * KH) * 2   # the two key halves of a unit run on separate waves
         wsb = rb.rattn_decode_workspace_bytes(B, n_q, Hq, Hkv, ctx, ns)
         assert slots * rows * 129 * 4 <= wsb <= slots * rows * 129 * 4 + 256
     assert rb.rattn_decode_workspace_bytes(1, 0, 8, 1, 300, 0) == 0

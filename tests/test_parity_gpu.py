@@ -124,6 +124,8 @@ DECODE_CASES = [
     ("n9_g8_unsat", 24, [5000, 777], [0, 0], 9, 64, 8, 8192),
     ("n9_g16_subgroups", 25, [400, 1300], [0, 129], 9, 32, 2, 200),
     ("n1_window1", 26, [250, 129], [1, 1], 1, 16, 2, 9),
+    # 16 queries x 8 heads = 128 rows: four 32-row blocks, every wave of the 8-wave split computes
+    ("n16_g8_rows128", 27, [200, 3000, 16], [0, 500, 0], 16, 16, 2, 300),
 ]
 
 
