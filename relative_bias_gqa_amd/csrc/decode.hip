@@ -149,16 +149,19 @@ __device__ __forceinline__ void cursor_next(const DecodeParams& p, Cursor& c) {
 
 // NW: waves per workgroup (4, or 8 = two per SIMD, so that one wave's softmax overlaps
 // its partner's MFMAs).  KS: waves sharing the keys of a unit (2: one 32-key half each;
-// 1: a wave takes both).  NB: bias loads per wave and unit (64 floats each),
-// NB * 64 * NW >= gs * SL.
-template <int NW, int KS, int NB>
+// 1: a wave takes both).  NL: waves that issue the loads, the last NL of the workgroup
+// (NL = NW: every wave; NL < NW: waves without a computing role, so that the computing
+// waves spend no instructions on addresses, block-table reads and load issue).  NB: bias
+// loads per loading wave and unit (64 floats each), NB * 64 * NL >= gs * SL.
+template <int NW, int KS, int NL, int NB>
 __global__ __launch_bounds__(64 * NW, 1) void decode_split_kernel(DecodeParams p) {
   constexpr int NT = 64 * NW;
   constexpr int KB = 2 / KS;       // 32-key blocks per computing wave and unit
-  constexpr int TPW = kUnit / NW;  // tokens of a unit loaded by one wave
-  constexpr int NI = TPW / 4;      // K (and V) load instructions per wave and unit
+  constexpr int TPW = kUnit / NL;  // tokens of a unit loaded by one loading wave
+  constexpr int NI = TPW / 4;      // K (and V) load instructions per loading wave and unit
   constexpr int kLoadsPerStage = 2 * NI + NB;
-  static_assert(NI >= 1 && NI * 4 * NW == kUnit, "load split");
+  static_assert(NL >= 1 && NL <= NW && NI >= 1 && NI * 4 * NL == kUnit, "load split");
+  static_assert(2 * kLoadsPerStage < 64, "vmcnt range");
   __shared__ __attribute__((aligned(1024))) unsigned char ring[kStages * kStageBytes];
   __shared__ int pre[kDecodeMaxBatch + 1];
   __shared__ int scratch[NT];
@@ -168,6 +171,8 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_split_kernel(DecodeParams p
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31;
   const int hf = lane >> 5;
+  const int li = wave - (NW - NL);  // index among the loading waves, < 0 for the others
+  const bool loader = li >= 0;
 
   const int units = batch_prefix<NT>(p, pre, scratch) * p.KH;
   const int P = min(p.P, units);
@@ -177,32 +182,14 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_split_kernel(DecodeParams p
   const int n_units = (int)((long long)(w + 1) * units / P) - u0;
 
   // ---- loads of one unit into a stage -------------------------------------------------
-  // K/V: wave `wave` issues tokens TPW wave .. TPW wave + TPW - 1 of the 64-token unit,
+  // K/V: loading wave li issues tokens TPW li .. TPW li + TPW - 1 of the 64-token unit,
   // four tokens (1 KB) per instruction; lane i of instruction m fetches 16-byte chunk
   // (i & 15) ^ swz(tok) of token tok = 4 m + i / 16, which lands at LDS chunk i & 15.
   // Per-lane byte offsets are fixed; a unit only adds its block base.
-  uint32_t koff[NI], voff[NI], kz[NI], vz[NI];
-  int ktok[NI];
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int tok = TPW * wave + 4 * i + (lane >> 4);
-    const int slot = lane & 15;
-    const int ck = slot ^ (tok & 15);
-    const int cv = slot ^ ((tok & 7) << 1);
-    ktok[i] = tok;
-    koff[i] = (uint32_t)(tok * p.Hkv) * 256u + ck * 16;
-    voff[i] = (uint32_t)(tok * p.Hkv) * 256u + cv * 16;
-    kz[i] = ck * 16;
-    vz[i] = cv * 16;
-  }
-  // Bias: NB * 64 * NW floats per stage; entry g * SL + x = r[h_g, clamp(d0 + x, 0, R - 1)].
-  int bias_g[NB], bias_x[NB];
-#pragma unroll
-  for (int i = 0; i < NB; ++i) {
-    const int idx = 64 * (NB * wave + i) + lane;
-    bias_g[i] = idx / p.SL;
-    bias_x[i] = idx - bias_g[i] * p.SL;
-  }
+  // Per-lane offsets are the same for every unit; they are recomputed inside each issue
+  // (from an opaque copy of the lane index) instead of being kept in registers, so that
+  // they do not occupy registers across the computing waves' code.
+  // Bias: NB * 64 * NL floats per stage; entry g * SL + x = r[h_g, clamp(d0 + x, 0, R - 1)].
   const unsigned char* kc_bytes = (const unsigned char*)p.k_cache;
   const unsigned char* vc_bytes = (const unsigned char*)p.v_cache;
   const unsigned char* zero_bytes = (const unsigned char*)kZeroRow;
@@ -217,19 +204,27 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_split_kernel(DecodeParams p
     const size_t base = (((size_t)phys * 128 + (ic.c & 1) * kUnit) * p.Hkv + kvh) * 256;
     const unsigned char* kb_ = kc_bytes + base;
     const unsigned char* vb_ = vc_bytes + base;
-    const uint32_t kdst = ring_base + st * kStageBytes + wave * (TPW * 256);
+    const uint32_t kdst = ring_base + st * kStageBytes + li * (TPW * 256);
     const uint32_t vdst = kdst + kKVBytes;
-    const uint32_t bdst = ring_base + st * kStageBytes + 2 * kKVBytes + wave * (NB * 256);
+    const uint32_t bdst = ring_base + st * kStageBytes + 2 * kKVBytes + li * (NB * 256);
     const bool interior = j0 >= ic.si.vis_lo && j0 + kUnit <= ic.si.ctx;
+    int lt = lane;
+    asm volatile("" : "+v"(lt));
+    const int slot = lt & 15;
+    const int tok0 = TPW * li + (lt >> 4);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const unsigned char* gk = kb_ + koff[i];
-      const unsigned char* gv = vb_ + voff[i];
+      const int tok = tok0 + 4 * i;
+      const uint32_t ck16 = (uint32_t)(slot ^ (tok & 15)) * 16u;
+      const uint32_t cv16 = (uint32_t)(slot ^ ((tok & 7) << 1)) * 16u;
+      const uint32_t row = (uint32_t)(tok * p.Hkv) * 256u;
+      const unsigned char* gk = kb_ + row + ck16;
+      const unsigned char* gv = vb_ + row + cv16;
       if (!interior) {
-        const int j = j0 + ktok[i];
+        const int j = j0 + tok;
         const bool vis = j >= ic.si.vis_lo && j < ic.si.ctx;
-        gk = vis ? gk : zero_bytes + kz[i];
-        gv = vis ? gv : zero_bytes + vz[i];
+        gk = vis ? gk : zero_bytes + ck16;
+        gv = vis ? gv : zero_bytes + cv16;
       }
       dma16(gk, kdst + i * 1024);
       dma16(gv, vdst + i * 1024);
@@ -238,12 +233,25 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_split_kernel(DecodeParams p
     const bool saturated = p0 - (j0 + kUnit - 1) >= p.R - 1;
     const int d0 = p0 - j0 - (kUnit - 1);
     const int hbase = kvh * p.G + hs * p.gs;
+    // entry 64 (NB li + i) + lane = (head g, distance offset x); x steps by 64 < SL + 1
+    int g = 0, x = 0;
+    if (!saturated) {
+      const int idx0 = 64 * NB * li + lt;
+      g = idx0 / p.SL;
+      x = idx0 - g * p.SL;
+    }
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       const float* src = p.bias;
-      if (!saturated && bias_g[i] < p.gs) {
-        const int d = min(max(d0 + bias_x[i], 0), p.R - 1);
-        src = p.bias + (size_t)(hbase + bias_g[i]) * p.R + d;
+      if (!saturated) {
+        if (i > 0) {
+          x += 64;
+          if (x >= p.SL) {
+            x -= p.SL;
+            ++g;
+          }
+        }
+        if (g < p.gs) src = p.bias + (size_t)(hbase + g) * p.R + min(max(d0 + x, 0), p.R - 1);
       }
       dma4(src, bdst + i * 256);
     }
@@ -468,18 +476,22 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_split_kernel(DecodeParams p
   Cursor ic = cc;
   begin_segment(cc);  // before any LDS load is in flight
   const int prologue = min(kStages - 1, n_units);
-  for (int i = 0; i < prologue; ++i) {
-    issue_unit(ic, i);
-    cursor_next(p, ic);
+  if (loader) {
+    for (int i = 0; i < prologue; ++i) {
+      issue_unit(ic, i);
+      cursor_next(p, ic);
+    }
   }
   int seg = cc.b * p.KH + cc.kh;
   for (int t = 0; t < n_units; ++t) {
-    const int ahead = min(kStages - 2, n_units - 1 - t);  // units issued after this one
-    if (ahead >= 2) vm_wait<2 * kLoadsPerStage>();
-    else if (ahead == 1) vm_wait<kLoadsPerStage>();
-    else vm_wait<0>();
+    if (loader) {
+      const int ahead = min(kStages - 2, n_units - 1 - t);  // units issued after this one
+      if (ahead >= 2) vm_wait<2 * kLoadsPerStage>();
+      else if (ahead == 1) vm_wait<kLoadsPerStage>();
+      else vm_wait<0>();
+    }
     wg_barrier();  // unit t is in LDS; every wave is done with unit t - 1
-    if (t + kStages - 1 < n_units) {
+    if (loader && t + kStages - 1 < n_units) {
       issue_unit(ic, (t + kStages - 1) % kStages);
       cursor_next(p, ic);
     }
@@ -622,32 +634,34 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   const long long grid2 = (long long)p.B * p.KH * p.rows;
   if (p.B <= 0) return hipSuccess;
   if (grid2 > 0x7fffffffLL || p.P < 1) return hipErrorInvalidConfiguration;
-  if ((p.NW != 4 && p.NW != 8) || (p.KS != 1 && p.KS != 2)) return hipErrorInvalidConfiguration;
-  // every computing role (32-row block, key share) needs a wave of its own
-  const int n_rb = (p.rows + 31) / 32;
-  if (p.KS == 2 ? n_rb * 2 > p.NW : n_rb > p.NW) return hipErrorInvalidConfiguration;
-  const int nb = (p.gs * p.SL + 64 * p.NW - 1) / (64 * p.NW);  // bias loads per wave and unit
-  if (nb < 1 || nb * 64 * p.NW > kDecodeBiasFloats) return hipErrorInvalidConfiguration;
+  if ((p.NW != 4 && p.NW != 8) || p.KS != 2) return hipErrorInvalidConfiguration;
+  // every computing role (32-row block, key half) needs a wave of its own; the waves left
+  // over issue the loads (two of them), else every wave does
+  const int roles = (p.rows + 31) / 32 * 2;
+  if (roles > p.NW) return hipErrorInvalidConfiguration;
+  const int NL = p.NW - roles >= 2 ? 2 : p.NW;
+  const int nb = (p.gs * p.SL + 64 * NL - 1) / (64 * NL);  // bias loads per loading wave and unit
+  if (nb < 1 || nb * 64 * NL > kDecodeBiasFloats) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)p.P);
-#define RATTN_SPLIT(NW_, KS_, NB_) \
-  hipLaunchKernelGGL((decode_split_kernel<NW_, KS_, NB_>), grid, dim3(64 * NW_), 0, stream, p)
-  if (p.NW == 8) {
-    if (p.KS != 2) return hipErrorInvalidConfiguration;
-    if (nb == 1) RATTN_SPLIT(8, 2, 1);
-    else RATTN_SPLIT(8, 2, 2);
-  } else if (p.KS == 2) {
+#define RATTN_SPLIT(NW_, NL_, NB_) \
+  hipLaunchKernelGGL((decode_split_kernel<NW_, 2, NL_, NB_>), grid, dim3(64 * NW_), 0, stream, p)
+  if (NL == 2) {
+    // bias loads of up to 1024 floats spread over two waves
     switch (nb) {
-      case 1: RATTN_SPLIT(4, 2, 1); break;
-      case 2: RATTN_SPLIT(4, 2, 2); break;
-      case 3: RATTN_SPLIT(4, 2, 3); break;
-      default: RATTN_SPLIT(4, 2, 4); break;
+      case 1: case 2: if (p.NW == 8) RATTN_SPLIT(8, 2, 2); else RATTN_SPLIT(4, 2, 2); break;
+      case 3: case 4: if (p.NW == 8) RATTN_SPLIT(8, 2, 4); else RATTN_SPLIT(4, 2, 4); break;
+      case 5: case 6: if (p.NW == 8) RATTN_SPLIT(8, 2, 6); else RATTN_SPLIT(4, 2, 6); break;
+      default: if (p.NW == 8) RATTN_SPLIT(8, 2, 8); else RATTN_SPLIT(4, 2, 8); break;
     }
+  } else if (p.NW == 8) {
+    if (nb == 1) RATTN_SPLIT(8, 8, 1);
+    else RATTN_SPLIT(8, 8, 2);
   } else {
     switch (nb) {
-      case 1: RATTN_SPLIT(4, 1, 1); break;
-      case 2: RATTN_SPLIT(4, 1, 2); break;
-      case 3: RATTN_SPLIT(4, 1, 3); break;
-      default: RATTN_SPLIT(4, 1, 4); break;
+      case 1: RATTN_SPLIT(4, 4, 1); break;
+      case 2: RATTN_SPLIT(4, 4, 2); break;
+      case 3: RATTN_SPLIT(4, 4, 3); break;
+      default: RATTN_SPLIT(4, 4, 4); break;
     }
   }
 #undef RATTN_SPLIT
