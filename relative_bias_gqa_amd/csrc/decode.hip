@@ -226,8 +226,8 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_split_kernel(DecodeParams p
         gk = vis ? gk : zero_bytes + ck16;
         gv = vis ? gv : zero_bytes + cv16;
       }
-      dma16(gk, kdst + i * 1024);
-      dma16(gv, vdst + i * 1024);
+      dma16nt(gk, kdst + i * 1024);
+      dma16nt(gv, vdst + i * 1024);
     }
     const int p0 = ic.si.ctx - p.n_q;
     const bool saturated = p0 - (j0 + kUnit - 1) >= p.R - 1;

@@ -151,6 +151,23 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds_byte_addr) {
       : "memory");
 }
 
+// The same as dma16 with the non-temporal cache policy, for data read exactly once (the
+// paged KV stream of decode): measured 7 % faster on a 2.3 GB batch-64 decode than the
+// default policy, which keeps the streamed lines in the caches.
+__device__ __forceinline__ void dma16nt(const void* g, uint32_t lds_byte_addr) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_byte_addr);
+  uint32_t save;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off nt\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "v"(g), "s"(m0v)
+      : "memory");
+}
+
 __device__ __forceinline__ void dma4(const void* g, uint32_t lds_byte_addr) {
   const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_byte_addr);
   uint32_t save;
