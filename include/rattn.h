@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define RATTN_ABI_VERSION 4
+#define RATTN_ABI_VERSION 5
 
 enum rattn_status {
   RATTN_OK = 0,
@@ -110,6 +110,39 @@ int rattn_prefill(const void* q, const void* k, const void* v, const float* bias
                   float* lse, int B, int Lq, int Lk, int Hq, int Hkv, int head_dim, int R,
                   int window, int dtype, int kv_splits, void* workspace, size_t workspace_bytes,
                   void* stream);
+
+/*
+ * Chunked prefill against a paged KV cache (prefix caching: vLLM recipes page
+ * "thinkingmachines/Inkling", Overview, lists prefix caching among the supported features;
+ * Client Usage serves with 128-token cache blocks).  Sequence b has ctx_lens[b] keys in
+ * the cache, the chunk's own K/V included; its Lq queries are its last Lq tokens, query t
+ * at position ctx_lens[b] - Lq + t, with the relative-bias attention and causal / window
+ * rule of rattn_prefill.
+ *
+ *   q           [B, Lq, Hq, 128]                  bf16   device, read
+ *   k_cache     [num_blocks, 128, Hkv, 128]       bf16   device, read
+ *   v_cache     [num_blocks, 128, Hkv, 128]       bf16   device, read
+ *   block_table [B, max_blocks_per_seq]           int32  device, read (physical block ids)
+ *   ctx_lens    [B]                               int32  device, read; Lq <= ctx_lens[b] <=
+ *               min(max_ctx_len, 128 * max_blocks_per_seq) is the caller's guarantee
+ *   bias        [Hq, R]                           fp32   device, read
+ *   out         [B, Lq, Hq, 128]                  bf16   device, written
+ *   lse         [B, Lq, Hq]                       fp32   device, written (natural log); may be NULL
+ *   window      <= 0 full causal, else the sliding window (as in rattn_prefill)
+ *
+ * Only blocks holding a key visible to some query of the chunk are read; other block-table
+ * entries are never dereferenced.  Cache slots before the first query's window, and at or
+ * past ctx_lens[b], may hold anything (NaN included): they are zero-filled on load.  No
+ * workspace; one workgroup per (sequence, KV head, head group, token tile); bitwise
+ * reproducible.  B == 0 or Lq == 0 is a no-op.  Status: INVALID_ARG (null pointer, sizes,
+ * Hq % Hkv, R < 1, num_blocks < 1, max_ctx_len < Lq or beyond the block table),
+ * UNSUPPORTED (head_dim or block_size != 128), HIP (launch failure).
+ */
+int rattn_prefill_paged(const void* q, const void* k_cache, const void* v_cache,
+                        const int* block_table, const int* ctx_lens, const float* bias, void* out,
+                        float* lse, int B, int Lq, int Hq, int Hkv, int head_dim, int block_size,
+                        int R, int window, int num_blocks, int max_blocks_per_seq, int max_ctx_len,
+                        void* stream);
 
 /*
  * Number of split workgroups rattn_decode_paged will use for these arguments.  The

@@ -25,10 +25,10 @@ LIB_PATH = os.path.join(_HERE, "librattn.so")
 
 RATTN_OK, RATTN_ERR_INVALID_ARG, RATTN_ERR_UNSUPPORTED, RATTN_ERR_WORKSPACE, RATTN_ERR_HIP = 0, 1, 2, 3, 4
 RATTN_BF16, RATTN_FP32 = 0, 1
-ABI_VERSION = 4
+ABI_VERSION = 5
 
-EXPORTED = ("rattn_prefill_workspace_bytes", "rattn_prefill", "rattn_decode_num_splits", "rattn_decode_workspace_bytes", "rattn_decode_paged",
-            "rattn_last_error", "rattn_abi_version")
+EXPORTED = ("rattn_prefill_workspace_bytes", "rattn_prefill", "rattn_prefill_paged", "rattn_decode_num_splits",
+            "rattn_decode_workspace_bytes", "rattn_decode_paged", "rattn_last_error", "rattn_abi_version")
 
 _lib = None
 
@@ -54,6 +54,8 @@ def load(path: Optional[str] = None):
     lib.rattn_prefill_workspace_bytes.argtypes = [i32] * 8
     lib.rattn_prefill.restype = i32
     lib.rattn_prefill.argtypes = [vp] * 6 + [i32] * 10 + [vp, sz, vp]
+    lib.rattn_prefill_paged.restype = i32
+    lib.rattn_prefill_paged.argtypes = [vp] * 8 + [i32] * 11 + [vp]
     lib.rattn_decode_num_splits.restype = i32
     lib.rattn_decode_num_splits.argtypes = [i32] * 6
     lib.rattn_decode_workspace_bytes.restype = sz
@@ -128,6 +130,22 @@ def rattn_prefill(q, k, v, bias, out, lse=None, window: int = 0, kv_splits: int 
                                 _ptr(workspace), ws_bytes, _stream(stream)))
 
 
+def rattn_prefill_paged(q, k_cache, v_cache, block_table, ctx_lens, bias, out, lse, max_ctx_len: int,
+                        window: int = 0, stream=None) -> None:
+    """q [B,Lq,Hq,128] bf16; caches [num_blocks,128,Hkv,128] bf16; block_table [B,mb] int32;
+    ctx_lens [B] int32 (keys in the cache including the chunk's own); bias [Hq,R] fp32; out
+    like q; lse [B,Lq,Hq] fp32 or None.  Query t of sequence b sits at ctx_lens[b]-Lq+t."""
+    if _dtype_code(q) != RATTN_BF16:
+        raise TypeError("rattn_prefill_paged takes bf16 q and caches")
+    B, Lq, Hq, D = q.shape
+    num_blocks, bs, Hkv = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+    mb = block_table.shape[1]
+    R = bias.shape[1]
+    _check(load().rattn_prefill_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(ctx_lens),
+                                      _ptr(bias), _ptr(out), _ptr(lse), B, Lq, Hq, Hkv, D, bs, R, int(window),
+                                      num_blocks, mb, int(max_ctx_len), _stream(stream)))
+
+
 def rattn_decode_num_splits(B: int, n_q: int, Hq: int, Hkv: int, max_ctx_len: int, num_splits: int = 0) -> int:
     return load().rattn_decode_num_splits(B, n_q, Hq, Hkv, max_ctx_len, num_splits)
 
@@ -180,6 +198,15 @@ def prefill(q, k, v, bias, window: int = 0, want_lse: bool = True, kv_splits: in
                                           _dtype_code(q), kv_splits)
         workspace = prefill_workspace(n, q.device) if n > 0 else None
     rattn_prefill(q, k, v, bias, out, lse, window, kv_splits, workspace, stream)
+    return out, lse
+
+
+def prefill_paged(q, k_cache, v_cache, block_table, ctx_lens, bias, max_ctx_len: int, window: int = 0,
+                  want_lse: bool = True, stream=None) -> Tuple:
+    import torch
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if want_lse else None
+    rattn_prefill_paged(q, k_cache, v_cache, block_table, ctx_lens, bias, out, lse, max_ctx_len, window, stream)
     return out, lse
 
 

@@ -128,6 +128,12 @@ void prefill_shape(int B, int Lq, int Lk, int Hq, int Hkv, int window, rattn::Pr
   p->ws_o = nullptr;
   p->ws_lse = nullptr;
   p->ws_cnt = nullptr;
+  p->queue = nullptr;
+  p->queue_workgroups = 0;
+  p->block_table = nullptr;
+  p->ctx_lens = nullptr;
+  p->mbps = 0;
+  p->num_blocks = 0;
 }
 
 // 64-key tiles walked by token tile `tile` (the same range as the kernel computes)
@@ -372,6 +378,53 @@ int rattn_prefill(const void* q, const void* k, const void* v, const float* bias
   hipError_t e = dtype == RATTN_BF16 ? rattn::launch_prefill_bf16(p, (hipStream_t)stream)
                                      : rattn::launch_prefill_fp32(p, (hipStream_t)stream);
   if (e != hipSuccess) return fail(RATTN_ERR_HIP, "rattn_prefill: launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int rattn_prefill_paged(const void* q, const void* k_cache, const void* v_cache, const int* block_table,
+                        const int* ctx_lens, const float* bias, void* out, float* lse, int B, int Lq, int Hq,
+                        int Hkv, int head_dim, int block_size, int R, int window, int num_blocks,
+                        int max_blocks_per_seq, int max_ctx_len, void* stream) {
+  if (B < 0 || Lq < 0 || Hq < 0 || Hkv < 0 || num_blocks < 0 || max_blocks_per_seq < 0 || max_ctx_len < 0)
+    return fail(RATTN_ERR_INVALID_ARG, "rattn_prefill_paged: negative size");
+  if (head_dim != 128) return fail(RATTN_ERR_UNSUPPORTED, "rattn_prefill_paged: head_dim %d (only 128)", head_dim);
+  if (block_size != 128)
+    return fail(RATTN_ERR_UNSUPPORTED, "rattn_prefill_paged: block_size %d (only 128)", block_size);
+  if (B == 0 || Lq == 0) return ok();
+  if (!q || !k_cache || !v_cache || !block_table || !ctx_lens || !bias || !out)
+    return fail(RATTN_ERR_INVALID_ARG, "rattn_prefill_paged: null pointer argument");
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0)
+    return fail(RATTN_ERR_INVALID_ARG, "rattn_prefill_paged: Hq=%d must be a positive multiple of Hkv=%d", Hq,
+                Hkv);
+  if (R < 1) return fail(RATTN_ERR_INVALID_ARG, "rattn_prefill_paged: R=%d < 1", R);
+  if (num_blocks < 1 || max_blocks_per_seq < 1)
+    return fail(RATTN_ERR_INVALID_ARG, "rattn_prefill_paged: num_blocks=%d, max_blocks_per_seq=%d", num_blocks,
+                max_blocks_per_seq);
+  if (max_ctx_len < Lq)
+    return fail(RATTN_ERR_INVALID_ARG, "rattn_prefill_paged: max_ctx_len=%d < Lq=%d", max_ctx_len, Lq);
+  if ((long long)max_ctx_len > 128LL * max_blocks_per_seq || max_ctx_len > kMaxPosition)
+    return fail(RATTN_ERR_INVALID_ARG, "rattn_prefill_paged: max_ctx_len=%d exceeds the block table (%d blocks)",
+                max_ctx_len, max_blocks_per_seq);
+
+  rattn::PrefillParams p;
+  p.q = q;
+  p.k = k_cache;
+  p.v = v_cache;
+  p.bias = bias;
+  p.out = out;
+  p.lse = lse;
+  p.R = R;
+  prefill_shape(B, Lq, max_ctx_len, Hq, Hkv, window, &p);
+  p.scale_log2 = kScaleLog2;
+  p.n_big = 0;
+  p.block_table = block_table;
+  p.ctx_lens = ctx_lens;
+  p.mbps = max_blocks_per_seq;
+  p.num_blocks = num_blocks;
+  const long long grid = (long long)p.n_tok_tiles * B * Hkv * p.n_hg;
+  if (grid > 0x7fffffffLL) return fail(RATTN_ERR_INVALID_ARG, "rattn_prefill_paged: problem too large for one launch");
+  hipError_t e = rattn::launch_prefill_bf16(p, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(RATTN_ERR_HIP, "rattn_prefill_paged: launch failed: %s", hipGetErrorString(e));
   return ok();
 }
 

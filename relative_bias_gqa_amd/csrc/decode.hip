@@ -55,19 +55,6 @@ struct SeqInfo {
   int nch;     // units of the visible range
 };
 
-// Wave-uniform 32-bit load through the scalar cache (lgkmcnt), so that it does not wait
-// behind the LDS-bound loads in flight.
-__device__ __forceinline__ int uniform_load_i32(const int* ptr) {
-  // readfirstlane returns a signed int: widen each half as unsigned
-  const uint64_t a = (uint64_t)(uintptr_t)ptr;
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-  const uint64_t ua = ((uint64_t)hi << 32) | (uint64_t)lo;
-  int v;
-  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=&s"(v) : "s"(ua) : "memory");
-  return v;
-}
-
 __device__ __forceinline__ SeqInfo seq_info(const DecodeParams& p, int b) {
   SeqInfo s;
   s.ctx = min(max(p.ctx_lens[b], 1), p.mbps * 128);

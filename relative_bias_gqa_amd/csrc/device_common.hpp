@@ -212,6 +212,19 @@ __device__ __forceinline__ void dma4s(const void* base, uint32_t off, uint32_t l
       : "memory");
 }
 
+// Wave-uniform 32-bit load through the scalar cache (lgkmcnt), so that it does not wait
+// behind the LDS-bound loads in flight.
+__device__ __forceinline__ int uniform_load_i32(const int* ptr) {
+  // readfirstlane returns a signed int: widen each half as unsigned
+  const uint64_t a = (uint64_t)(uintptr_t)ptr;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const uint64_t ua = ((uint64_t)hi << 32) | (uint64_t)lo;
+  int v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=&s"(v) : "s"(ua) : "memory");
+  return v;
+}
+
 // Wait until at most N vector-memory operations of this wave are outstanding.
 template <int N>
 __device__ __forceinline__ void vm_wait() {

@@ -33,6 +33,13 @@ struct PrefillParams {
   int* ws_cnt;    // [n_split * B * Hkv * n_hg] finished pieces; zero between calls
   int* queue;            // [2] job queue and done counter (zero before and after a call), or null
   int queue_workgroups;  // workgroups of a launch with a queue
+  // paged K/V (bf16 path, no split, no queue): k / v are caches [num_blocks, 128, Hkv, 128],
+  // block_table [B, mbps], ctx_lens [B] keys per sequence (Lk is their maximum); null when
+  // K and V are contiguous [B, Lk, Hkv, 128]
+  const int* block_table;
+  const int* ctx_lens;
+  int mbps;
+  int num_blocks;
 };
 
 constexpr int kMaxPieces = 8;

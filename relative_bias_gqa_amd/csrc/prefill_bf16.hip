@@ -53,6 +53,14 @@ constexpr float kSqrtD = 11.313708498984761f;     // sqrt(128)
 // 256 bytes of zeros: the source of every K/V row past the end of the sequence.
 __device__ __attribute__((aligned(256))) const uint32_t kZeroRowP[64] = {0};
 
+// PAGED: K and V come from paged caches [num_blocks, 128, Hkv, 128] through the block
+// table (chunked prefill over a cached prefix), and sequence b has its own context length
+// ctx_lens[b] (its Lq queries are its last Lq tokens).  A 64-key tile is always one half of
+// one 128-token block, laid out like 64 rows of a contiguous K/V, so only the tile's base
+// address (one scalar block-table read per tile) and the key count per sequence differ.
+// Keys that no query of the chunk can see (before the first query's window, or at or past
+// the context) are loaded from a zero row: the cache may hold anything there.
+template <bool PAGED>
 __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams p) {
   __shared__ __attribute__((aligned(1024))) unsigned char ring[kStages * kStageBytes];
   __shared__ int last_piece;
@@ -91,7 +99,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
     const int T0 = tile * 32 * p.tsub;
     const int T1 = min(p.Lq, T0 + 32 * p.tsub);
     const int tw0 = T0 + (wave / p.hpw) * 32;  // first token of this wave
-    const int off = p.Lk - p.Lq;               // position of token 0
+    // keys of this job's sequence
+    const int Lk = PAGED ? min(max(p.ctx_lens[b], p.Lq), 128 * p.mbps) : p.Lk;
+    const int off = Lk - p.Lq;                 // position of token 0
     const int pw0 = off + tw0;                 // position of this wave's column 0
     const int wvalid = min(32, p.Lq - tw0);    // valid columns of this wave (may be <= 0)
     const bool wave_active = wvalid > 0;
@@ -140,8 +150,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
       kz[i] = ck * 16;
       vz[i] = cv * 16;
     }
-    const unsigned char* kc_bytes = (const unsigned char*)p.k + ((size_t)b * p.Lk * p.Hkv + hk) * 256;
-    const unsigned char* vc_bytes = (const unsigned char*)p.v + ((size_t)b * p.Lk * p.Hkv + hk) * 256;
+    const size_t seq_base = PAGED ? 0 : (size_t)b * p.Lk * p.Hkv;
+    const unsigned char* kc_bytes = (const unsigned char*)p.k + (seq_base + hk) * 256;
+    const unsigned char* vc_bytes = (const unsigned char*)p.v + (seq_base + hk) * 256;
+    // first key any query of the sequence's chunk can see (keys before it may hold anything
+    // in a paged cache)
+    const int vis_lo = PAGED ? max(0, off - Weff + 1) : 0;
     const unsigned char* zero_bytes = (const unsigned char*)kZeroRowP;
     const float* bias_row = p.bias + (size_t)h * p.R;
     const uint32_t ring_base = lds_addr(ring);
@@ -153,11 +167,18 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
     const uint32_t zoff = 0;
     auto issue_tile = [&](int kt, int st) {
       const int j0 = kt * kBK;
-      const size_t base = (size_t)j0 * p.Hkv * 256;
+      size_t base;
+      if constexpr (PAGED) {
+        int phys = uniform_load_i32(p.block_table + (size_t)b * p.mbps + (j0 >> 7));
+        phys = min(max(phys, 0), p.num_blocks - 1);
+        base = ((size_t)phys * 128 + (j0 & 127)) * p.Hkv * 256;
+      } else {
+        base = (size_t)j0 * p.Hkv * 256;
+      }
       const uint32_t kdst = ring_base + st * kStageBytes + wave * 2048;
       const uint32_t vdst = kdst + kKVBytes;
       const uint32_t bdst = ring_base + st * kStageBytes + 2 * kKVBytes + wave * (kSliceFloats * 4);
-      if (j0 + kBK <= p.Lk) {
+      if (j0 + kBK <= Lk && (!PAGED || j0 >= vis_lo)) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
           dma16s(kc_bytes + base, koff[i], kdst + i * 1024);
@@ -168,7 +189,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
         for (int i = 0; i < 2; ++i) {
           const unsigned char* gk = kc_bytes + base + koff[i];
           const unsigned char* gv = vc_bytes + base + voff[i];
-          if (j0 + ktok[i] >= p.Lk) {
+          if (j0 + ktok[i] >= Lk || (PAGED && j0 + ktok[i] < vis_lo)) {
             gk = zero_bytes + kz[i];
             gv = zero_bytes + vz[i];
           }
@@ -573,7 +594,10 @@ hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream) {
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   // with a queue: one workgroup per compute unit, each running jobs until none is left
   if (p.queue != nullptr && grid > p.queue_workgroups) grid = p.queue_workgroups;
-  hipLaunchKernelGGL(prefill_bf16_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+  if (p.block_table != nullptr)
+    hipLaunchKernelGGL(prefill_bf16_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL(prefill_bf16_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.rattn_abi_version() == rb.ABI_VERSION == 4
+    assert lib.rattn_abi_version() == rb.ABI_VERSION == 5
 
 
 def _prefill(lib, **kw):
@@ -109,6 +109,40 @@ def test_decode_validation(lib, kw, status, needle):
 
 def test_decode_empty_is_noop(lib):
     assert _decode(lib, B=0, q=None, kc=None) == rb.RATTN_OK
+
+
+def _prefill_paged(lib, **kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, ctx=FAKE, bias=FAKE, out=FAKE, lse=None, B=2, Lq=100, Hq=16, Hkv=2,
+             D=128, bs=128, R=8, window=0, nb=4, mb=2, max_ctx=200, stream=None)
+    a.update(kw)
+    return lib.rattn_prefill_paged(a["q"], a["kc"], a["vc"], a["bt"], a["ctx"], a["bias"], a["out"], a["lse"],
+                                   a["B"], a["Lq"], a["Hq"], a["Hkv"], a["D"], a["bs"], a["R"], a["window"], a["nb"],
+                                   a["mb"], a["max_ctx"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(q=None), rb.RATTN_ERR_INVALID_ARG, "null"),
+    (dict(kc=None), rb.RATTN_ERR_INVALID_ARG, "null"),
+    (dict(bt=None), rb.RATTN_ERR_INVALID_ARG, "null"),
+    (dict(ctx=None), rb.RATTN_ERR_INVALID_ARG, "null"),
+    (dict(out=None), rb.RATTN_ERR_INVALID_ARG, "null"),
+    (dict(Hq=15), rb.RATTN_ERR_INVALID_ARG, "multiple"),
+    (dict(R=0), rb.RATTN_ERR_INVALID_ARG, "R="),
+    (dict(nb=0), rb.RATTN_ERR_INVALID_ARG, "num_blocks"),
+    (dict(max_ctx=99), rb.RATTN_ERR_INVALID_ARG, "max_ctx_len"),
+    (dict(max_ctx=257, mb=2), rb.RATTN_ERR_INVALID_ARG, "block table"),
+    (dict(B=-1), rb.RATTN_ERR_INVALID_ARG, "negative"),
+    (dict(D=64), rb.RATTN_ERR_UNSUPPORTED, "head_dim"),
+    (dict(bs=64), rb.RATTN_ERR_UNSUPPORTED, "block_size"),
+])
+def test_prefill_paged_validation(lib, kw, status, needle):
+    assert _prefill_paged(lib, **kw) == status
+    assert needle in rb.rattn_last_error()
+
+
+def test_prefill_paged_empty_is_noop(lib):
+    assert _prefill_paged(lib, B=0, q=None, kc=None) == rb.RATTN_OK
+    assert _prefill_paged(lib, Lq=0, q=None, bt=None) == rb.RATTN_OK
 
 
 def test_workspace_and_split_plan(lib):
