@@ -37,7 +37,8 @@ METRIC = "prefill attention TFLOP/s (% bf16 MFMA peak); decode KV GB/s (% HBM pe
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 HEADLINE = "swa_prefill_8k"
-ALL_WORKLOADS = ["tiny_prefill_fp32", "swa_prefill_8k", "chunked_prefill_32k", "paged_decode_b64", "mtp_verify_1m"]
+ALL_WORKLOADS = ["tiny_prefill_fp32", "swa_prefill_8k", "chunked_prefill_32k", "paged_decode_b64", "mtp_verify_1m",
+                 "paged_prefill_b4"]
 HEAD_DIM = 128
 KERNEL_SOURCES = {
     "prefill": ["relative_bias_gqa_amd/csrc/prefill.hip", "relative_bias_gqa_amd/csrc/prefill_bf16.hip",
@@ -191,6 +192,46 @@ class DecodeRun:
         del self.q, self.kc, self.vc, self.bt, self.ctx, self.win, self.bias, self.out, self.lse, self.ws
 
 
+class PagedPrefillRun:
+    """Chunked prefill over a paged KV cache: per-sequence contexts, one chunk length."""
+    kind = "prefill"
+
+    def __init__(self, name, torch, rb, synth, dev):
+        self.name = name
+        c = synth.WORKLOAD_FNS[name]()
+        self.case = c
+        self.q, self.kc, self.vc = dev(c.q), dev(c.k_cache), dev(c.v_cache)
+        self.bt, self.ctx, self.bias = dev(c.block_table), dev(c.ctx_lens), dev(c.bias)
+        self.out = torch.empty_like(self.q)
+        self.lse = torch.empty(self.q.shape[:3], dtype=torch.float32, device=self.q.device)
+        self.max_ctx = c.max_ctx_len
+        self.window = int(c.windows[0])
+        self.rb = rb
+        self.work = sum(prefill_flops(1, c.n_q, int(ctx), c.Hq, self.window) for ctx in c.ctx_lens)
+        self.unit, self.peak, self.bound = "TFLOP/s", PEAK_BF16_TFLOPS, "mfma"
+        self.config = {"workload": name, "batch": c.B, "q_len": c.n_q, "ctx_lens": [int(x) for x in c.ctx_lens],
+                       "q_heads": c.Hq, "kv_heads": c.Hkv, "head_dim": HEAD_DIM, "block_size": 128,
+                       "window": self.window, "bias_len": c.R, "dtype": "bf16"}
+        self.dtype = "bf16"
+
+    def step(self, stream):
+        self.rb.rattn_prefill_paged(self.q, self.kc, self.vc, self.bt, self.ctx, self.bias, self.out, self.lse,
+                                    self.max_ctx, self.window, stream)
+
+    def rate(self, seconds):
+        return self.work / seconds / 1e12
+
+    def finite(self):
+        import torch
+        return bool(torch.isfinite(self.out.float()).all()) and bool(torch.isfinite(self.lse).all())
+
+    def free(self):
+        del self.q, self.kc, self.vc, self.bt, self.ctx, self.bias, self.out, self.lse
+
+
+RUN_CLASSES = {"paged_decode_b64": DecodeRun, "mtp_verify_1m": DecodeRun, "paged_prefill_b4": PagedPrefillRun}
+
+
 def settle_clock(run, torch, stream, ms: float) -> int:
     """Repeat the step, untimed, for at least `ms` milliseconds of wall clock."""
     if ms <= 0:
@@ -297,7 +338,7 @@ def main(argv=None) -> int:
     if args.only:
         if args.only not in ALL_WORKLOADS:
             raise SystemExit(f"unknown workload {args.only}")
-        cls = DecodeRun if args.only in ("paged_decode_b64", "mtp_verify_1m") else PrefillRun
+        cls = RUN_CLASSES.get(args.only, PrefillRun)
         run = cls(args.only, torch, rb, synth, dev)
         torch.cuda.synchronize()
         sec = time_steps(run, torch, args.steps, args.warmup, args.settle_ms)
@@ -312,7 +353,7 @@ def main(argv=None) -> int:
     results = {}
     headline = None
     for name in names:
-        cls = DecodeRun if name in ("paged_decode_b64", "mtp_verify_1m") else PrefillRun
+        cls = RUN_CLASSES.get(name, PrefillRun)
         t0 = time.time()
         run = cls(name, torch, rb, synth, dev)
         log(f"[bench] {name}: inputs on device in {time.time() - t0:.1f} s; timing {args.steps} steps")

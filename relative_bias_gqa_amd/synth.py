@@ -239,6 +239,8 @@ WORKLOADS = {
     "chunked_prefill_32k": "batch 1, 8192 queries at 24576..32767 over 32768 keys, 16/2 heads, bf16, full, R=8192",
     "paged_decode_b64": "batch 64, 1 query, ctx U[4096,131072], odd b window 4096, 16/2 heads, bf16, R=8192",
     "mtp_verify_1m": "batch 1, 9 queries at the tail of 1,048,576 keys, 16/2 heads, bf16, full, R=8192",
+    "paged_prefill_b4": "batch 4, 2048-query chunks at the tails of 8192/16384/24576/32768-key paged contexts, "
+                        "16/2 heads, bf16, full causal, R=8192",
 }
 
 
@@ -265,10 +267,17 @@ def mtp_verify_1m(seed: int = 0) -> DecodeCase:
     return make_decode(seed, [1 << 20], [0], 9, 16, 2, 8192, "mtp_verify_1m", poison=False)
 
 
+def paged_prefill_b4(seed: int = 0) -> DecodeCase:
+    """Chunked prefill over a prefix cache: four sequences whose last 2048 tokens are the
+    chunk (their K/V already in the paged cache), contexts 8K..32K."""
+    return make_decode(seed, [8192, 16384, 24576, 32768], [0, 0, 0, 0], 2048, 16, 2, 8192, "paged_prefill_b4")
+
+
 WORKLOAD_FNS = {
     "tiny_prefill_fp32": tiny_prefill_fp32,
     "swa_prefill_8k": swa_prefill_8k,
     "chunked_prefill_32k": chunked_prefill_32k,
     "paged_decode_b64": paged_decode_b64,
     "mtp_verify_1m": mtp_verify_1m,
+    "paged_prefill_b4": paged_prefill_b4,
 }
