@@ -206,6 +206,8 @@ class PagedPrefillRun:
         self.lse = torch.empty(self.q.shape[:3], dtype=torch.float32, device=self.q.device)
         self.max_ctx = c.max_ctx_len
         self.window = int(c.windows[0])
+        # the job queue's (zero-filled) workspace, allocated here, outside the timed region
+        self.ws = torch.zeros(rb.PREFILL_PAGED_WORKSPACE_BYTES, dtype=torch.uint8, device=self.q.device)
         self.rb = rb
         self.work = sum(prefill_flops(1, c.n_q, int(ctx), c.Hq, self.window) for ctx in c.ctx_lens)
         self.unit, self.peak, self.bound = "TFLOP/s", PEAK_BF16_TFLOPS, "mfma"
@@ -216,7 +218,7 @@ class PagedPrefillRun:
 
     def step(self, stream):
         self.rb.rattn_prefill_paged(self.q, self.kc, self.vc, self.bt, self.ctx, self.bias, self.out, self.lse,
-                                    self.max_ctx, self.window, stream)
+                                    self.max_ctx, self.window, self.ws, stream)
 
     def rate(self, seconds):
         return self.work / seconds / 1e12
@@ -226,7 +228,7 @@ class PagedPrefillRun:
         return bool(torch.isfinite(self.out.float()).all()) and bool(torch.isfinite(self.lse).all())
 
     def free(self):
-        del self.q, self.kc, self.vc, self.bt, self.ctx, self.bias, self.out, self.lse
+        del self.q, self.kc, self.vc, self.bt, self.ctx, self.bias, self.out, self.lse, self.ws
 
 
 RUN_CLASSES = {"paged_decode_b64": DecodeRun, "mtp_verify_1m": DecodeRun, "paged_prefill_b4": PagedPrefillRun}

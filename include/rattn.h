@@ -132,17 +132,26 @@ int rattn_prefill(const void* q, const void* k, const void* v, const float* bias
  *
  * Only blocks holding a key visible to some query of the chunk are read; other block-table
  * entries are never dereferenced.  Cache slots before the first query's window, and at or
- * past ctx_lens[b], may hold anything (NaN included): they are zero-filled on load.  No
- * workspace; one workgroup per (sequence, KV head, head group, token tile); bitwise
- * reproducible.  B == 0 or Lq == 0 is a no-op.  Status: INVALID_ARG (null pointer, sizes,
- * Hq % Hkv, R < 1, num_blocks < 1, max_ctx_len < Lq or beyond the block table),
- * UNSUPPORTED (head_dim or block_size != 128), HIP (launch failure).
+ * past ctx_lens[b], may hold anything (NaN included): they are zero-filled on load.
+ * A job is (sequence, KV head, head group, token tile); jobs run sequence by sequence,
+ * longest context first.  workspace: NULL (one workgroup per job) or at least
+ * RATTN_PREFILL_PAGED_WORKSPACE_BYTES of device memory, zero-filled before its first use,
+ * holding a job queue (one workgroup per compute unit takes jobs until none is left); every
+ * completed call leaves it zero, and calls sharing it must not run concurrently (the
+ * first 256 bytes of a rattn_prefill workspace serve as well).  Either way the result is
+ * the same bit for bit.  B == 0 or Lq == 0 is a no-op.  Status: INVALID_ARG (null pointer,
+ * sizes, Hq % Hkv, R < 1, num_blocks < 1, max_ctx_len < Lq or beyond the block table,
+ * workspace_bytes > 0 with a NULL workspace), WORKSPACE (a workspace smaller than
+ * RATTN_PREFILL_PAGED_WORKSPACE_BYTES), UNSUPPORTED (head_dim or block_size != 128), HIP
+ * (launch failure).
  */
+#define RATTN_PREFILL_PAGED_WORKSPACE_BYTES 256
+
 int rattn_prefill_paged(const void* q, const void* k_cache, const void* v_cache,
                         const int* block_table, const int* ctx_lens, const float* bias, void* out,
                         float* lse, int B, int Lq, int Hq, int Hkv, int head_dim, int block_size,
                         int R, int window, int num_blocks, int max_blocks_per_seq, int max_ctx_len,
-                        void* stream);
+                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Number of split workgroups rattn_decode_paged will use for these arguments.  The

@@ -384,7 +384,8 @@ int rattn_prefill(const void* q, const void* k, const void* v, const float* bias
 int rattn_prefill_paged(const void* q, const void* k_cache, const void* v_cache, const int* block_table,
                         const int* ctx_lens, const float* bias, void* out, float* lse, int B, int Lq, int Hq,
                         int Hkv, int head_dim, int block_size, int R, int window, int num_blocks,
-                        int max_blocks_per_seq, int max_ctx_len, void* stream) {
+                        int max_blocks_per_seq, int max_ctx_len, void* workspace, size_t workspace_bytes,
+                        void* stream) {
   if (B < 0 || Lq < 0 || Hq < 0 || Hkv < 0 || num_blocks < 0 || max_blocks_per_seq < 0 || max_ctx_len < 0)
     return fail(RATTN_ERR_INVALID_ARG, "rattn_prefill_paged: negative size");
   if (head_dim != 128) return fail(RATTN_ERR_UNSUPPORTED, "rattn_prefill_paged: head_dim %d (only 128)", head_dim);
@@ -405,6 +406,12 @@ int rattn_prefill_paged(const void* q, const void* k_cache, const void* v_cache,
   if ((long long)max_ctx_len > 128LL * max_blocks_per_seq || max_ctx_len > kMaxPosition)
     return fail(RATTN_ERR_INVALID_ARG, "rattn_prefill_paged: max_ctx_len=%d exceeds the block table (%d blocks)",
                 max_ctx_len, max_blocks_per_seq);
+  if (workspace == nullptr && workspace_bytes != 0)
+    return fail(RATTN_ERR_INVALID_ARG, "rattn_prefill_paged: workspace_bytes=%zu with a null workspace",
+                workspace_bytes);
+  if (workspace != nullptr && workspace_bytes < RATTN_PREFILL_PAGED_WORKSPACE_BYTES)
+    return fail(RATTN_ERR_WORKSPACE, "rattn_prefill_paged: workspace of %zu bytes, %d needed", workspace_bytes,
+                RATTN_PREFILL_PAGED_WORKSPACE_BYTES);
 
   rattn::PrefillParams p;
   p.q = q;
@@ -421,6 +428,9 @@ int rattn_prefill_paged(const void* q, const void* k_cache, const void* v_cache,
   p.ctx_lens = ctx_lens;
   p.mbps = max_blocks_per_seq;
   p.num_blocks = num_blocks;
+  // with a workspace: the job queue (one workgroup per compute unit), else one per job
+  p.queue = workspace != nullptr ? (int*)workspace : nullptr;
+  p.queue_workgroups = p.queue ? compute_units() : 0;
   const long long grid = (long long)p.n_tok_tiles * B * Hkv * p.n_hg;
   if (grid > 0x7fffffffLL) return fail(RATTN_ERR_INVALID_ARG, "rattn_prefill_paged: problem too large for one launch");
   hipError_t e = rattn::launch_prefill_bf16(p, (hipStream_t)stream);

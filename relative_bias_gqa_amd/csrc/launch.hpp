@@ -43,6 +43,7 @@ struct PrefillParams {
 };
 
 constexpr int kMaxPieces = 8;
+constexpr int kMaxSortedSeqs = 1024;  // paged prefill: sequences ordered by context length in LDS
 
 // Piece slot w (< n_jobs * parts) of a split prefill takes piece *piece of job *job.  In
 // each group of 8 * parts slots (8 jobs), slot x + 8 k takes piece k of job x: the pieces

@@ -59,12 +59,17 @@ __device__ __attribute__((aligned(256))) const uint32_t kZeroRowP[64] = {0};
 // one 128-token block, laid out like 64 rows of a contiguous K/V, so only the tile's base
 // address (one scalar block-table read per tile) and the key count per sequence differ.
 // Keys that no query of the chunk can see (before the first query's window, or at or past
-// the context) are loaded from a zero row: the cache may hold anything there.
+// the context) are loaded from a zero row: the cache may hold anything there.  Jobs go
+// sequence by sequence, longest context first (each workgroup ranks the sequences by
+// ctx_lens in LDS, up to kMaxSortedSeqs of them), last token tile first: with the job
+// queue that is close to longest-first whatever the mix of context lengths.
 template <bool PAGED>
 __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams p) {
   __shared__ __attribute__((aligned(1024))) unsigned char ring[kStages * kStageBytes];
   __shared__ int last_piece;
   __shared__ int next_slot;
+  __shared__ int seq_key[PAGED ? kMaxSortedSeqs : 1];    // ctx_lens
+  __shared__ int seq_order[PAGED ? kMaxSortedSeqs : 1];  // sequences, longest context first
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -82,6 +87,21 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
   const int n_piece_slots = p.n_split * per_tile * p.parts;
   const int n_slots = n_piece_slots + (p.n_tok_tiles - p.n_split) * per_tile;
   const int n_big_slots = p.n_big * per_tile;
+  const bool sorted = PAGED && p.B <= kMaxSortedSeqs;
+  if constexpr (PAGED) {
+    if (sorted) {
+      for (int i = tid; i < p.B; i += kThreads) seq_key[i] = p.ctx_lens[i];
+      __syncthreads();
+      // rank of sequence i: the sequences with a longer context, or as long and lower index
+      for (int i = tid; i < p.B; i += kThreads) {
+        const int ki = seq_key[i];
+        int r = 0;
+        for (int j = 0; j < p.B; ++j) r += (seq_key[j] > ki || (seq_key[j] == ki && j < i)) ? 1 : 0;
+        seq_order[r] = i;
+      }
+      __syncthreads();
+    }
+  }
   for (int slot = blockIdx.x; slot < n_slots;) {
     const bool is_piece = slot >= n_big_slots && slot < n_big_slots + n_piece_slots;
     int job, piece = 0;
@@ -89,11 +109,23 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
       prefill_piece_of(slot - n_big_slots, (long long)p.n_split * per_tile, p.parts, &job, &piece);
     else
       job = p.n_split * per_tile + (slot < n_big_slots ? slot : slot - n_piece_slots);
-    const int tile = p.n_tok_tiles - 1 - job / per_tile;
-    const int rem = job % per_tile;
-    const int hg = rem % p.n_hg;
-    const int hk = (rem / p.n_hg) % p.Hkv;
-    const int b = rem / (p.n_hg * p.Hkv);
+    int tile, hg, hk, b;
+    if constexpr (PAGED) {
+      // sequence-major: job = ((rank * n_tok_tiles + (n_tok_tiles - 1 - tile)) * Hkv + hk) * n_hg + hg
+      const int per_seq = p.n_tok_tiles * p.Hkv * p.n_hg;
+      const int r = job / per_seq, within = job - r * per_seq;
+      tile = p.n_tok_tiles - 1 - within / (p.Hkv * p.n_hg);
+      const int rem = within % (p.Hkv * p.n_hg);
+      hg = rem % p.n_hg;
+      hk = rem / p.n_hg;
+      b = sorted ? seq_order[r] : r;
+    } else {
+      tile = p.n_tok_tiles - 1 - job / per_tile;
+      const int rem = job % per_tile;
+      hg = rem % p.n_hg;
+      hk = (rem / p.n_hg) % p.Hkv;
+      b = rem / (p.n_hg * p.Hkv);
+    }
 
     const int h = hk * p.G + hg * p.hpw + (wave % p.hpw);
     const int T0 = tile * 32 * p.tsub;

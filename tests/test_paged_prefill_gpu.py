@@ -6,6 +6,8 @@
   head, a 1024-token chunk; invisible slots and blocks hold NaN.
 * Through a permuted block table it equals the contiguous prefill of the same keys, bitwise.
 * NaN in the slots before the first query's window changes nothing, bitwise.
+* The job queue (with a workspace, sequences taken longest context first) gives the same
+  bits as one workgroup per job, and is left at zero.
 """
 import numpy as np
 import pytest
@@ -100,3 +102,21 @@ def test_paged_prefill_poison_before_window_is_invisible():
     out_b, lse_b = run_paged(case, window, k_cache=dev(kc), v_cache=dev(vc))
     assert torch.isfinite(out_b.float()).all()
     assert _bitwise_equal(out_a, out_b) and _bitwise_equal(lse_a, lse_b)
+
+
+def test_paged_prefill_job_queue_matches_one_workgroup_per_job():
+    print("case paged prefill job queue", flush=True)
+    Lq = 256
+    case = synth.make_decode(67, [700, 5000, 256, 3000, 1200], [0] * 5, Lq, 16, 2, 4096, name="queue")
+    d = decode_to_device(case)
+    args = (d["q"], d["k_cache"], d["v_cache"], d["block_table"], d["ctx_lens"], d["bias"], case.max_ctx_len, 0)
+    out_n, lse_n = rb.prefill_paged(*args, workspace=None)
+    ws = torch.zeros(rb.PREFILL_PAGED_WORKSPACE_BYTES, dtype=torch.uint8, device=d["q"].device)
+    for _ in range(3):
+        out_q, lse_q = rb.prefill_paged(*args, workspace=ws)
+        torch.cuda.synchronize()
+        assert _bitwise_equal(out_n, out_q) and _bitwise_equal(lse_n, lse_q)
+        assert int(ws.sum().item()) == 0
+    ref_o, ref_l, _ = oracle.ref_decode(case)
+    compare(host(out_q), host(lse_q), ref_o, ref_l, "queue")
+
