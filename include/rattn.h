@@ -115,15 +115,21 @@ int rattn_prefill(const void* q, const void* k, const void* v, const float* bias
  * Chunked prefill against a paged KV cache (prefix caching: vLLM recipes page
  * "thinkingmachines/Inkling", Overview, lists prefix caching among the supported features;
  * Client Usage serves with 128-token cache blocks).  Sequence b has ctx_lens[b] keys in
- * the cache, the chunk's own K/V included; its Lq queries are its last Lq tokens, query t
- * at position ctx_lens[b] - Lq + t, with the relative-bias attention and causal / window
+ * the cache, the chunk's own K/V included; its n_b queries (n_b = Lq, or with packed
+ * queries cu_seqlens_q[b + 1] - cu_seqlens_q[b]) are its last n_b tokens, query t at
+ * position ctx_lens[b] - n_b + t, with the relative-bias attention and causal / window
  * rule of rattn_prefill.
  *
- *   q           [B, Lq, Hq, 128]                  bf16   device, read
+ *   q           [B, Lq, Hq, 128]                  bf16   device, read; with cu_seqlens_q,
+ *               packed [cu_seqlens_q[B], Hq, 128]: sequence b's queries are rows
+ *               cu_seqlens_q[b] .. cu_seqlens_q[b + 1] - 1 (out and lse likewise)
+ *   cu_seqlens_q [B + 1]                          int32  device, read, or NULL (Lq queries
+ *               per sequence); non-decreasing from 0, with 0 <= n_b <= Lq the caller's
+ *               guarantee (Lq is then the longest chunk)
  *   k_cache     [num_blocks, 128, Hkv, 128]       bf16   device, read
  *   v_cache     [num_blocks, 128, Hkv, 128]       bf16   device, read
  *   block_table [B, max_blocks_per_seq]           int32  device, read (physical block ids)
- *   ctx_lens    [B]                               int32  device, read; Lq <= ctx_lens[b] <=
+ *   ctx_lens    [B]                               int32  device, read; n_b <= ctx_lens[b] <=
  *               min(max_ctx_len, 128 * max_blocks_per_seq) is the caller's guarantee
  *   bias        [Hq, R]                           fp32   device, read
  *   out         [B, Lq, Hq, 128]                  bf16   device, written
@@ -133,8 +139,8 @@ int rattn_prefill(const void* q, const void* k, const void* v, const float* bias
  * Only blocks holding a key visible to some query of the chunk are read; other block-table
  * entries are never dereferenced.  Cache slots before the first query's window, and at or
  * past ctx_lens[b], may hold anything (NaN included): they are zero-filled on load.
- * A job is (sequence, KV head, head group, token tile); jobs run sequence by sequence,
- * longest context first.  workspace: NULL (one workgroup per job) or at least
+ * A job is (sequence, KV head, head group, 32 (8 / query heads per workgroup) tokens of
+ * the chunk, up to Lq); jobs run sequence by sequence, longest context first.  workspace: NULL (one workgroup per job) or at least
  * RATTN_PREFILL_PAGED_WORKSPACE_BYTES of device memory, zero-filled before its first use,
  * holding a job queue (one workgroup per compute unit takes jobs until none is left); every
  * completed call leaves it zero, and calls sharing it must not run concurrently (the
@@ -148,9 +154,10 @@ int rattn_prefill(const void* q, const void* k, const void* v, const float* bias
 #define RATTN_PREFILL_PAGED_WORKSPACE_BYTES 256
 
 int rattn_prefill_paged(const void* q, const void* k_cache, const void* v_cache,
-                        const int* block_table, const int* ctx_lens, const float* bias, void* out,
-                        float* lse, int B, int Lq, int Hq, int Hkv, int head_dim, int block_size,
-                        int R, int window, int num_blocks, int max_blocks_per_seq, int max_ctx_len,
+                        const int* block_table, const int* ctx_lens, const int* cu_seqlens_q,
+                        const float* bias, void* out, float* lse, int B, int Lq, int Hq, int Hkv,
+                        int head_dim, int block_size, int R, int window, int num_blocks,
+                        int max_blocks_per_seq, int max_ctx_len,
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*

@@ -55,7 +55,7 @@ def load(path: Optional[str] = None):
     lib.rattn_prefill.restype = i32
     lib.rattn_prefill.argtypes = [vp] * 6 + [i32] * 10 + [vp, sz, vp]
     lib.rattn_prefill_paged.restype = i32
-    lib.rattn_prefill_paged.argtypes = [vp] * 8 + [i32] * 11 + [vp, sz, vp]
+    lib.rattn_prefill_paged.argtypes = [vp] * 9 + [i32] * 11 + [vp, sz, vp]
     lib.rattn_decode_num_splits.restype = i32
     lib.rattn_decode_num_splits.argtypes = [i32] * 6
     lib.rattn_decode_workspace_bytes.restype = sz
@@ -134,21 +134,28 @@ PREFILL_PAGED_WORKSPACE_BYTES = 256
 
 
 def rattn_prefill_paged(q, k_cache, v_cache, block_table, ctx_lens, bias, out, lse, max_ctx_len: int,
-                        window: int = 0, workspace=None, stream=None) -> None:
-    """q [B,Lq,Hq,128] bf16; caches [num_blocks,128,Hkv,128] bf16; block_table [B,mb] int32;
+                        window: int = 0, workspace=None, stream=None, cu_seqlens_q=None, max_q_len: int = 0) -> None:
+    """q [B,Lq,Hq,128] bf16, or packed [total,Hq,128] with cu_seqlens_q [B+1] int32 and the
+    longest chunk max_q_len; caches [num_blocks,128,Hkv,128] bf16; block_table [B,mb] int32;
     ctx_lens [B] int32 (keys in the cache including the chunk's own); bias [Hq,R] fp32; out
-    like q; lse [B,Lq,Hq] fp32 or None.  Query t of sequence b sits at ctx_lens[b]-Lq+t.
-    workspace: a zero-filled uint8 device tensor of at least PREFILL_PAGED_WORKSPACE_BYTES
-    (a job queue; calls leave it zero-filled), or None (one workgroup per job)."""
+    like q; lse like q without its last dimension (fp32) or None.  Query t of sequence b
+    (n_b queries) sits at ctx_lens[b]-n_b+t.  workspace: a zero-filled uint8 device tensor of
+    at least PREFILL_PAGED_WORKSPACE_BYTES (a job queue; calls leave it zero-filled), or None
+    (one workgroup per job)."""
     if _dtype_code(q) != RATTN_BF16:
         raise TypeError("rattn_prefill_paged takes bf16 q and caches")
-    B, Lq, Hq, D = q.shape
+    if cu_seqlens_q is None:
+        B, Lq, Hq, D = q.shape
+    else:
+        B, Lq = block_table.shape[0], int(max_q_len)
+        Hq, D = q.shape[1], q.shape[2]
     num_blocks, bs, Hkv = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
     mb = block_table.shape[1]
     R = bias.shape[1]
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load().rattn_prefill_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(ctx_lens),
-                                      _ptr(bias), _ptr(out), _ptr(lse), B, Lq, Hq, Hkv, D, bs, R, int(window),
+                                      _ptr(cu_seqlens_q), _ptr(bias), _ptr(out), _ptr(lse), B, Lq, Hq, Hkv, D, bs, R,
+                                      int(window),
                                       num_blocks, mb, int(max_ctx_len), _ptr(workspace), ws_bytes,
                                       _stream(stream)))
 
@@ -209,16 +216,16 @@ def prefill(q, k, v, bias, window: int = 0, want_lse: bool = True, kv_splits: in
 
 
 def prefill_paged(q, k_cache, v_cache, block_table, ctx_lens, bias, max_ctx_len: int, window: int = 0,
-                  want_lse: bool = True, workspace="auto", stream=None) -> Tuple:
+                  want_lse: bool = True, workspace="auto", stream=None, cu_seqlens_q=None, max_q_len: int = 0) -> Tuple:
     """workspace "auto": the cached zero-filled prefill workspace of q's device (job queue);
     None: one workgroup per job; else a tensor as for rattn_prefill_paged."""
     import torch
     out = torch.empty_like(q)
-    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if want_lse else None
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device) if want_lse else None
     if isinstance(workspace, str):
         workspace = prefill_workspace(PREFILL_PAGED_WORKSPACE_BYTES, q.device)
     rattn_prefill_paged(q, k_cache, v_cache, block_table, ctx_lens, bias, out, lse, max_ctx_len, window, workspace,
-                        stream)
+                        stream, cu_seqlens_q, max_q_len)
     return out, lse
 
 

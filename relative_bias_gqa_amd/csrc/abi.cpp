@@ -132,6 +132,7 @@ void prefill_shape(int B, int Lq, int Lk, int Hq, int Hkv, int window, rattn::Pr
   p->queue_workgroups = 0;
   p->block_table = nullptr;
   p->ctx_lens = nullptr;
+  p->cu_q = nullptr;
   p->mbps = 0;
   p->num_blocks = 0;
 }
@@ -382,8 +383,9 @@ int rattn_prefill(const void* q, const void* k, const void* v, const float* bias
 }
 
 int rattn_prefill_paged(const void* q, const void* k_cache, const void* v_cache, const int* block_table,
-                        const int* ctx_lens, const float* bias, void* out, float* lse, int B, int Lq, int Hq,
-                        int Hkv, int head_dim, int block_size, int R, int window, int num_blocks,
+                        const int* ctx_lens, const int* cu_seqlens_q, const float* bias, void* out, float* lse,
+                        int B, int Lq, int Hq, int Hkv, int head_dim, int block_size, int R, int window,
+                        int num_blocks,
                         int max_blocks_per_seq, int max_ctx_len, void* workspace, size_t workspace_bytes,
                         void* stream) {
   if (B < 0 || Lq < 0 || Hq < 0 || Hkv < 0 || num_blocks < 0 || max_blocks_per_seq < 0 || max_ctx_len < 0)
@@ -426,6 +428,7 @@ int rattn_prefill_paged(const void* q, const void* k_cache, const void* v_cache,
   p.n_big = 0;
   p.block_table = block_table;
   p.ctx_lens = ctx_lens;
+  p.cu_q = cu_seqlens_q;
   p.mbps = max_blocks_per_seq;
   p.num_blocks = num_blocks;
   // with a workspace: the job queue (one workgroup per compute unit), else one per job

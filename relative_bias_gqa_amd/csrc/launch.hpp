@@ -38,6 +38,7 @@ struct PrefillParams {
   // K and V are contiguous [B, Lk, Hkv, 128]
   const int* block_table;
   const int* ctx_lens;
+  const int* cu_q;  // paged: [B + 1] packed query offsets (q, out, lse [total, Hq, ...]), or null: [B, Lq, ...]
   int mbps;
   int num_blocks;
 };

@@ -129,13 +129,17 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
 
     const int h = hk * p.G + hg * p.hpw + (wave % p.hpw);
     const int T0 = tile * 32 * p.tsub;
-    const int T1 = min(p.Lq, T0 + 32 * p.tsub);
+    // this job's sequence: its queries (paged with packed queries: cu_q[b] .. cu_q[b + 1] - 1,
+    // at most Lq) and the row of its first query
+    const int qlen = PAGED && p.cu_q != nullptr ? min(max(p.cu_q[b + 1] - p.cu_q[b], 0), p.Lq) : p.Lq;
+    const size_t qrow0 = PAGED && p.cu_q != nullptr ? (size_t)p.cu_q[b] : (size_t)b * p.Lq;
+    const int T1 = min(qlen, T0 + 32 * p.tsub);
     const int tw0 = T0 + (wave / p.hpw) * 32;  // first token of this wave
     // keys of this job's sequence
-    const int Lk = PAGED ? min(max(p.ctx_lens[b], p.Lq), 128 * p.mbps) : p.Lk;
-    const int off = Lk - p.Lq;                 // position of token 0
+    const int Lk = PAGED ? min(max(p.ctx_lens[b], qlen), 128 * p.mbps) : p.Lk;
+    const int off = Lk - qlen;                 // position of token 0
     const int pw0 = off + tw0;                 // position of this wave's column 0
-    const int wvalid = min(32, p.Lq - tw0);    // valid columns of this wave (may be <= 0)
+    const int wvalid = min(32, qlen - tw0);    // valid columns of this wave (may be <= 0)
     const bool wave_active = wvalid > 0;
     const int pw_last = pw0 + max(wvalid, 1) - 1;
     const int Weff = p.window > 0 ? p.window : 0x40000000;
@@ -149,14 +153,15 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
       kt_begin = first + (nt * piece) / p.parts;
       kt_end = first + (nt * (piece + 1)) / p.parts;
     }
-    const int n_tiles = kt_end - kt_begin;
+    // (a paged job past its sequence's queries has no work)
+    const int n_tiles = PAGED ? (T0 < qlen ? max(kt_end - kt_begin, 0) : 0) : kt_end - kt_begin;
 
     // ---- Q^T operand, resident for the whole key loop -------------------------------
     u32x4_t qr[8];
     {
       const int tq = tw0 + col;
-      const bool ok = wave_active && tq < p.Lq;
-      const size_t qbase = (((size_t)b * p.Lq + (ok ? tq : 0)) * p.Hq + h) * kHeadDim;
+      const bool ok = wave_active && tq < qlen;
+      const size_t qbase = ((qrow0 + (ok ? tq : 0)) * p.Hq + h) * kHeadDim;
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks)
         qr[ks] = ok ? *(const u32x4_t*)((const uint16_t*)p.q + qbase + 16 * ks + 8 * hf) : zero_u32x4();
@@ -484,8 +489,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
     // ---- epilogue --------------------------------------------------------------------
     const float l_tot = half_swap_sum(l_run);
     const int tq = tw0 + col;
-    const bool row_ok = wave_active && tq < p.Lq;
-    const size_t obase = (((size_t)b * p.Lq + (row_ok ? tq : 0)) * p.Hq + h) * kHeadDim;
+    const bool row_ok = wave_active && tq < qlen;
+    const size_t obase = ((qrow0 + (row_ok ? tq : 0)) * p.Hq + h) * kHeadDim;
     if (!is_piece) {
       if (row_ok) {
         const float inv = 1.f / l_tot;
@@ -499,7 +504,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
             *(u32x2_t*)((uint16_t*)p.out + obase + d) = u32x2_t{pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
           }
         if (hf == 0 && p.lse != nullptr)
-          p.lse[((size_t)b * p.Lq + tq) * p.Hq + h] = (m_run + __log2f(l_tot)) * kLn2;
+          p.lse[(qrow0 + tq) * p.Hq + h] = (m_run + __log2f(l_tot)) * kLn2;
       }
     } else {
 
@@ -597,7 +602,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
             *(u32x2_t*)((uint16_t*)p.out + obase + d) = u32x2_t{pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
           }
         if (hf == 0 && p.lse != nullptr)
-          p.lse[((size_t)b * p.Lq + tq) * p.Hq + h] = (mmax + __log2f(wsum)) * kLn2;
+          p.lse[(qrow0 + tq) * p.Hq + h] = (mmax + __log2f(wsum)) * kLn2;
       }  // last piece
     }  // piece
     // next job: every wave is done with this one's LDS stages and shared flags

@@ -112,10 +112,11 @@ def test_decode_empty_is_noop(lib):
 
 
 def _prefill_paged(lib, **kw):
-    a = dict(q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, ctx=FAKE, bias=FAKE, out=FAKE, lse=None, B=2, Lq=100, Hq=16, Hkv=2,
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, ctx=FAKE, cu=None, bias=FAKE, out=FAKE, lse=None, B=2, Lq=100, Hq=16,
+             Hkv=2,
              D=128, bs=128, R=8, window=0, nb=4, mb=2, max_ctx=200, ws=None, wsb=0, stream=None)
     a.update(kw)
-    return lib.rattn_prefill_paged(a["q"], a["kc"], a["vc"], a["bt"], a["ctx"], a["bias"], a["out"], a["lse"],
+    return lib.rattn_prefill_paged(a["q"], a["kc"], a["vc"], a["bt"], a["ctx"], a["cu"], a["bias"], a["out"], a["lse"],
                                    a["B"], a["Lq"], a["Hq"], a["Hkv"], a["D"], a["bs"], a["R"], a["window"], a["nb"],
                                    a["mb"], a["max_ctx"], a["ws"], a["wsb"], a["stream"])
 

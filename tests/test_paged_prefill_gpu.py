@@ -8,6 +8,8 @@
 * NaN in the slots before the first query's window changes nothing, bitwise.
 * The job queue (with a workspace, sequences taken longest context first) gives the same
   bits as one workgroup per job, and is left at zero.
+* Packed queries of different lengths per sequence (cu_seqlens_q; none, one, ragged and the
+  longest chunk) match the oracle's rows for the same positions.
 """
 import numpy as np
 import pytest
@@ -119,4 +121,25 @@ def test_paged_prefill_job_queue_matches_one_workgroup_per_job():
         assert int(ws.sum().item()) == 0
     ref_o, ref_l, _ = oracle.ref_decode(case)
     compare(host(out_q), host(lse_q), ref_o, ref_l, "queue")
+
+
+@pytest.mark.parametrize("window", [0, 200])
+def test_paged_prefill_packed_varlen_queries(window):
+    """Sequence b's chunk is its last n_b queries: the last n_b rows of a fixed-length case at the
+    same context (same positions ctx - n_b + t), so the oracle of that case gives the expected rows."""
+    print(f"case paged prefill packed varlen window={window}", flush=True)
+    max_q = 300
+    ctx = [1000, 300, 2500, 700, 1500]
+    qlens = [300, 0, 1, 129, 77]
+    case = synth.make_decode(68, ctx, [window] * len(ctx), max_q, 16, 2, 1500, name="varlen")
+    ref_o, ref_l, _ = oracle.ref_decode(case)
+    d = decode_to_device(case)
+    qp = np.ascontiguousarray(np.concatenate([case.q[b, max_q - n:] for b, n in enumerate(qlens)], axis=0))
+    cu = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    out, lse = rb.prefill_paged(dev(qp), d["k_cache"], d["v_cache"], d["block_table"], d["ctx_lens"], d["bias"],
+                                case.max_ctx_len, window, cu_seqlens_q=dev(cu), max_q_len=max_q)
+    torch.cuda.synchronize()
+    exp_o = np.concatenate([ref_o[b, max_q - n:] for b, n in enumerate(qlens)], axis=0)
+    exp_l = np.concatenate([ref_l[b, max_q - n:] for b, n in enumerate(qlens)], axis=0)
+    compare(host(out), host(lse), exp_o, exp_l, f"varlen window={window}")
 
