@@ -161,6 +161,39 @@ int rattn_prefill_paged(const void* q, const void* k_cache, const void* v_cache,
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Short convolution of the new keys and values as they enter the paged caches (vLLM recipes
+ * page "thinkingmachines/Inkling", Overview > Architectural highlights > Short convolution:
+ * window-4 sconv modules on the attention keys and values; vLLM keeps their state as the KV
+ * cache of a virtual sliding-window layer).  Read as the causal depthwise convolution over
+ * tokens with four taps and a weight per tap and channel, no bias, no activation:
+ *     y[p, c] = sum_{s=0..3} w[s, c] * x[p - s, c],   x[p] = 0 for p < 0.
+ * Sequence b has n_b = cu_seqlens[b + 1] - cu_seqlens[b] new tokens at positions
+ * ctx_lens[b] - n_b .. ctx_lens[b] - 1: y (rounded to bf16, nearest even) is written to the
+ * attention caches and the raw x to the state caches at those positions; the raw x of up to
+ * three earlier positions is read from the state caches (written by earlier calls).
+ *
+ *   k_new, v_new    [cu_seqlens[B], Hkv, 128]          bf16  device, read (packed new tokens)
+ *   w_k, w_v        [4, Hkv, 128]                      fp32  device, read (tap s multiplies x[p - s])
+ *   k_cache, v_cache [num_blocks, 128, Hkv, 128]       bf16  device, written at the new positions
+ *   k_state, v_state [num_blocks, 128, Hkv, 128]       bf16  device, read before each chunk,
+ *                    written at the new positions (the caches share the block table)
+ *   block_table     [B, max_blocks_per_seq]            int32 device, read
+ *   ctx_lens        [B]                                int32 device, read: keys after the write
+ *   cu_seqlens      [B + 1]                            int32 device, read: non-decreasing from 0
+ *
+ * Caller's guarantees: 0 <= n_b <= max_new, n_b <= ctx_lens[b] <= 128 * max_blocks_per_seq,
+ * block-table entries of the positions written or read are valid, and no two sequences write
+ * the same physical slot.  Only those slots are touched.  Bitwise reproducible.  B == 0 or
+ * max_new == 0 is a no-op.  Status: INVALID_ARG (null pointer, sizes, B > 65535),
+ * UNSUPPORTED (head_dim or block_size != 128, Hkv > 8), HIP (launch failure).
+ */
+int rattn_kv_sconv_write(const void* k_new, const void* v_new, const float* w_k, const float* w_v,
+                         void* k_cache, void* v_cache, void* k_state, void* v_state,
+                         const int* block_table, const int* ctx_lens, const int* cu_seqlens, int B,
+                         int Hkv, int head_dim, int block_size, int num_blocks,
+                         int max_blocks_per_seq, int max_new, void* stream);
+
+/*
  * Number of split workgroups rattn_decode_paged will use for these arguments.  The
  * visible keys of the whole batch form one stream of 64-token units that is divided
  * evenly among them.  num_splits > 0 asks for exactly that many (fewer when the batch has

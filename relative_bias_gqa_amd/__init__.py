@@ -27,8 +27,9 @@ RATTN_OK, RATTN_ERR_INVALID_ARG, RATTN_ERR_UNSUPPORTED, RATTN_ERR_WORKSPACE, RAT
 RATTN_BF16, RATTN_FP32 = 0, 1
 ABI_VERSION = 5
 
-EXPORTED = ("rattn_prefill_workspace_bytes", "rattn_prefill", "rattn_prefill_paged", "rattn_decode_num_splits",
-            "rattn_decode_workspace_bytes", "rattn_decode_paged", "rattn_last_error", "rattn_abi_version")
+EXPORTED = ("rattn_prefill_workspace_bytes", "rattn_prefill", "rattn_prefill_paged", "rattn_kv_sconv_write",
+            "rattn_decode_num_splits", "rattn_decode_workspace_bytes", "rattn_decode_paged", "rattn_last_error",
+            "rattn_abi_version")
 
 _lib = None
 
@@ -56,6 +57,8 @@ def load(path: Optional[str] = None):
     lib.rattn_prefill.argtypes = [vp] * 6 + [i32] * 10 + [vp, sz, vp]
     lib.rattn_prefill_paged.restype = i32
     lib.rattn_prefill_paged.argtypes = [vp] * 9 + [i32] * 11 + [vp, sz, vp]
+    lib.rattn_kv_sconv_write.restype = i32
+    lib.rattn_kv_sconv_write.argtypes = [vp] * 11 + [i32] * 7 + [vp]
     lib.rattn_decode_num_splits.restype = i32
     lib.rattn_decode_num_splits.argtypes = [i32] * 6
     lib.rattn_decode_workspace_bytes.restype = sz
@@ -158,6 +161,20 @@ def rattn_prefill_paged(q, k_cache, v_cache, block_table, ctx_lens, bias, out, l
                                       int(window),
                                       num_blocks, mb, int(max_ctx_len), _ptr(workspace), ws_bytes,
                                       _stream(stream)))
+
+
+def rattn_kv_sconv_write(k_new, v_new, w_k, w_v, k_cache, v_cache, k_state, v_state, block_table, ctx_lens,
+                         cu_seqlens, max_new: int, stream=None) -> None:
+    """k_new/v_new [T,Hkv,128] bf16 packed new tokens; w_k/w_v [4,Hkv,128] fp32; the attention
+    caches and the state caches [num_blocks,128,Hkv,128] bf16 (one block table [B,mb] int32);
+    ctx_lens [B] int32 keys after the write; cu_seqlens [B+1] int32; max_new >= every chunk."""
+    B = block_table.shape[0]
+    num_blocks, bs, Hkv, D = k_cache.shape
+    mb = block_table.shape[1]
+    _check(load().rattn_kv_sconv_write(_ptr(k_new), _ptr(v_new), _ptr(w_k), _ptr(w_v), _ptr(k_cache), _ptr(v_cache),
+                                       _ptr(k_state), _ptr(v_state), _ptr(block_table), _ptr(ctx_lens),
+                                       _ptr(cu_seqlens), B, Hkv, D, bs, num_blocks, mb, int(max_new),
+                                       _stream(stream)))
 
 
 def rattn_decode_num_splits(B: int, n_q: int, Hq: int, Hkv: int, max_ctx_len: int, num_splits: int = 0) -> int:

@@ -441,6 +441,47 @@ int rattn_prefill_paged(const void* q, const void* k_cache, const void* v_cache,
   return ok();
 }
 
+int rattn_kv_sconv_write(const void* k_new, const void* v_new, const float* w_k, const float* w_v, void* k_cache,
+                         void* v_cache, void* k_state, void* v_state, const int* block_table, const int* ctx_lens,
+                         const int* cu_seqlens, int B, int Hkv, int head_dim, int block_size, int num_blocks,
+                         int max_blocks_per_seq, int max_new, void* stream) {
+  if (B < 0 || Hkv < 0 || num_blocks < 0 || max_blocks_per_seq < 0 || max_new < 0)
+    return fail(RATTN_ERR_INVALID_ARG, "rattn_kv_sconv_write: negative size");
+  if (head_dim != 128) return fail(RATTN_ERR_UNSUPPORTED, "rattn_kv_sconv_write: head_dim %d (only 128)", head_dim);
+  if (block_size != 128)
+    return fail(RATTN_ERR_UNSUPPORTED, "rattn_kv_sconv_write: block_size %d (only 128)", block_size);
+  if (Hkv > 8) return fail(RATTN_ERR_UNSUPPORTED, "rattn_kv_sconv_write: Hkv=%d > 8", Hkv);
+  if (B == 0 || max_new == 0) return ok();
+  if (!k_new || !v_new || !w_k || !w_v || !k_cache || !v_cache || !k_state || !v_state || !block_table ||
+      !ctx_lens || !cu_seqlens)
+    return fail(RATTN_ERR_INVALID_ARG, "rattn_kv_sconv_write: null pointer argument");
+  if (Hkv < 1) return fail(RATTN_ERR_INVALID_ARG, "rattn_kv_sconv_write: Hkv=%d < 1", Hkv);
+  if (num_blocks < 1 || max_blocks_per_seq < 1)
+    return fail(RATTN_ERR_INVALID_ARG, "rattn_kv_sconv_write: num_blocks=%d, max_blocks_per_seq=%d", num_blocks,
+                max_blocks_per_seq);
+  if (B > 65535) return fail(RATTN_ERR_INVALID_ARG, "rattn_kv_sconv_write: B=%d > 65535", B);
+  rattn::SconvParams p;
+  p.k_new = (const uint16_t*)k_new;
+  p.v_new = (const uint16_t*)v_new;
+  p.w_k = w_k;
+  p.w_v = w_v;
+  p.k_cache = (uint16_t*)k_cache;
+  p.v_cache = (uint16_t*)v_cache;
+  p.k_state = (uint16_t*)k_state;
+  p.v_state = (uint16_t*)v_state;
+  p.block_table = block_table;
+  p.ctx_lens = ctx_lens;
+  p.cu = cu_seqlens;
+  p.B = B;
+  p.Hkv = Hkv;
+  p.mbps = max_blocks_per_seq;
+  p.num_blocks = num_blocks;
+  p.max_new = max_new;
+  hipError_t e = rattn::launch_sconv_write(p, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(RATTN_ERR_HIP, "rattn_kv_sconv_write: launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 size_t rattn_prefill_workspace_bytes(int B, int Lq, int Lk, int Hq, int Hkv, int window, int dtype,
                                      int kv_splits) {
   if (B < 1 || Lq < 1 || Lk < Lq || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || Lk > kMaxPosition ||

@@ -100,6 +100,24 @@ struct DecodeParams {
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 
+// Short convolution of new K/V tokens written into the paged caches.
+struct SconvParams {
+  const uint16_t* k_new;   // [T, Hkv, 128] bf16, packed new tokens (rows cu[b] .. cu[b + 1] - 1)
+  const uint16_t* v_new;
+  const float* w_k;        // [4, Hkv, 128] fp32: tap s multiplies x[p - s]
+  const float* w_v;
+  uint16_t* k_cache;       // [num_blocks, 128, Hkv, 128] bf16: conv outputs at the new positions
+  uint16_t* v_cache;
+  uint16_t* k_state;       // same layout: raw K/V, read before a chunk, written at its positions
+  uint16_t* v_state;
+  const int* block_table;  // [B, mbps]
+  const int* ctx_lens;     // [B] keys after the write
+  const int* cu;           // [B + 1]
+  int B, Hkv, mbps, num_blocks, max_new;
+};
+
+hipError_t launch_sconv_write(const SconvParams& p, hipStream_t stream);
+
 // Decode limits the host must respect.
 constexpr int kDecodeMaxRows = 128;       // n_q * gs (four blocks of 32 rows)
 constexpr int kDecodeBiasFloats = 1024;   // gs * (63 + n_q) per unit

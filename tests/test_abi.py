@@ -214,3 +214,35 @@ def test_prefill_split_plan(lib):
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(RuntimeError, match="not built"):
         rb.load(str(tmp_path / "missing.so"))
+
+
+def _sconv(lib, **kw):
+    a = dict(kn=FAKE, vn=FAKE, wk=FAKE, wv=FAKE, kc=FAKE, vc=FAKE, ks=FAKE, vs=FAKE, bt=FAKE, ctx=FAKE, cu=FAKE, B=2,
+             Hkv=2, D=128, bs=128, nb=4, mb=2, max_new=10, stream=None)
+    a.update(kw)
+    return lib.rattn_kv_sconv_write(a["kn"], a["vn"], a["wk"], a["wv"], a["kc"], a["vc"], a["ks"], a["vs"], a["bt"],
+                                    a["ctx"], a["cu"], a["B"], a["Hkv"], a["D"], a["bs"], a["nb"], a["mb"],
+                                    a["max_new"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(kn=None), rb.RATTN_ERR_INVALID_ARG, "null"),
+    (dict(ks=None), rb.RATTN_ERR_INVALID_ARG, "null"),
+    (dict(cu=None), rb.RATTN_ERR_INVALID_ARG, "null"),
+    (dict(Hkv=0), rb.RATTN_ERR_INVALID_ARG, "Hkv"),
+    (dict(nb=0), rb.RATTN_ERR_INVALID_ARG, "num_blocks"),
+    (dict(B=70000), rb.RATTN_ERR_INVALID_ARG, "B="),
+    (dict(max_new=-1), rb.RATTN_ERR_INVALID_ARG, "negative"),
+    (dict(D=64), rb.RATTN_ERR_UNSUPPORTED, "head_dim"),
+    (dict(bs=16), rb.RATTN_ERR_UNSUPPORTED, "block_size"),
+    (dict(Hkv=9), rb.RATTN_ERR_UNSUPPORTED, "Hkv"),
+])
+def test_sconv_validation(lib, kw, status, needle):
+    assert _sconv(lib, **kw) == status
+    assert needle in rb.rattn_last_error()
+
+
+def test_sconv_empty_is_noop(lib):
+    assert _sconv(lib, B=0, kn=None) == rb.RATTN_OK
+    assert _sconv(lib, max_new=0, kc=None) == rb.RATTN_OK
+
