@@ -38,13 +38,15 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 HEADLINE = "swa_prefill_8k"
 ALL_WORKLOADS = ["tiny_prefill_fp32", "swa_prefill_8k", "chunked_prefill_32k", "paged_decode_b64", "mtp_verify_1m",
-                 "paged_prefill_b4"]
+                 "paged_prefill_b4", "kv_sconv_32k"]
 HEAD_DIM = 128
 KERNEL_SOURCES = {
     "prefill": ["relative_bias_gqa_amd/csrc/prefill.hip", "relative_bias_gqa_amd/csrc/prefill_bf16.hip",
                 "relative_bias_gqa_amd/csrc/device_common.hpp", "relative_bias_gqa_amd/csrc/launch.hpp"],
     "decode": ["relative_bias_gqa_amd/csrc/decode.hip", "relative_bias_gqa_amd/csrc/device_common.hpp",
                "relative_bias_gqa_amd/csrc/launch.hpp"],
+    "sconv": ["relative_bias_gqa_amd/csrc/sconv.hip", "relative_bias_gqa_amd/csrc/device_common.hpp",
+              "relative_bias_gqa_amd/csrc/launch.hpp"],
 }
 
 
@@ -231,7 +233,48 @@ class PagedPrefillRun:
         del self.q, self.kc, self.vc, self.bt, self.ctx, self.bias, self.out, self.lse, self.ws
 
 
-RUN_CLASSES = {"paged_decode_b64": DecodeRun, "mtp_verify_1m": DecodeRun, "paged_prefill_b4": PagedPrefillRun}
+class SconvRun:
+    """Short convolution of new K/V tokens written into the paged caches (HBM-bound)."""
+    kind = "sconv"
+
+    def __init__(self, name, torch, rb, synth, dev):
+        self.name = name
+        c = synth.WORKLOAD_FNS[name]()
+        self.case = c
+        self.kn, self.vn, self.wk, self.wv = dev(c.k_new), dev(c.v_new), dev(c.w_k), dev(c.w_v)
+        self.kc, self.vc, self.ks, self.vs = dev(c.k_cache), dev(c.v_cache), dev(c.k_state), dev(c.v_state)
+        self.bt, self.ctx, self.cu = dev(c.block_table), dev(c.ctx_lens), dev(c.cu_seqlens)
+        self.max_new = int(c.n_new.max())
+        self.rb = rb
+        Hkv = c.k_new.shape[1]
+        row = Hkv * HEAD_DIM * 2
+        # per new token: its K and V rows read, four cache rows written; per sequence the
+        # state rows of up to three earlier positions read; the weights
+        prior = sum(min(3, int(x) - int(n)) for x, n in zip(c.ctx_lens, c.n_new))
+        self.work = int(6 * row * c.k_new.shape[0] + 2 * row * prior + 2 * 4 * Hkv * HEAD_DIM * 4)
+        self.unit, self.peak, self.bound = "GB/s", PEAK_HBM_GBS, "hbm"
+        self.config = {"workload": name, "batch": len(c.ctx_lens), "new_tokens": [int(x) for x in c.n_new],
+                       "ctx_lens": [int(x) for x in c.ctx_lens], "kv_heads": Hkv, "head_dim": HEAD_DIM,
+                       "block_size": 128, "taps": 4, "dtype": "bf16"}
+        self.dtype = "bf16"
+
+    def step(self, stream):
+        self.rb.rattn_kv_sconv_write(self.kn, self.vn, self.wk, self.wv, self.kc, self.vc, self.ks, self.vs, self.bt,
+                                     self.ctx, self.cu, self.max_new, stream)
+
+    def rate(self, seconds):
+        return self.work / seconds / 1e9
+
+    def finite(self):
+        import torch
+        return bool(torch.isfinite(self.kc.float()).all())
+
+    def free(self):
+        del self.kn, self.vn, self.wk, self.wv, self.kc, self.vc, self.ks, self.vs, self.bt, self.ctx, self.cu
+
+
+RUN_CLASSES = {"paged_decode_b64": DecodeRun, "mtp_verify_1m": DecodeRun, "paged_prefill_b4": PagedPrefillRun,
+               "kv_sconv_32k": SconvRun}
 
 
 def settle_clock(run, torch, stream, ms: float) -> int:

@@ -230,8 +230,45 @@ def make_decode(seed: int, ctx_lens, windows, n_q: int, Hq: int, Hkv: int, R: in
     return DecodeCase(q, kc, vc, bt, ctx_lens, windows, bias, name, poison_id if poison else None)
 
 
+@dataclass
+class SconvCase:
+    k_new: np.ndarray        # [T, Hkv, 128] uint16 (bf16 bits), packed new tokens
+    v_new: np.ndarray
+    w_k: np.ndarray          # [4, Hkv, 128] float32
+    w_v: np.ndarray
+    k_cache: np.ndarray      # [num_blocks, 128, Hkv, 128] uint16
+    v_cache: np.ndarray
+    k_state: np.ndarray
+    v_state: np.ndarray
+    block_table: np.ndarray  # [B, max_blocks_per_seq] int32
+    ctx_lens: np.ndarray     # [B] int32, keys after the write
+    cu_seqlens: np.ndarray   # [B + 1] int32
+    name: str = ""
+
+    @property
+    def n_new(self): return np.diff(self.cu_seqlens)
+
+
+def make_sconv(seed: int, ctx_lens, n_new, Hkv: int, name: str = "") -> SconvCase:
+    """Draw order: block permutation, the four caches, new K, new V, w_k, w_v (N(0,1))."""
+    rng = np.random.default_rng(seed)
+    ctx = np.asarray(ctx_lens, dtype=np.int32)
+    B = len(ctx)
+    nbps = max(1, max((int(c) + BLOCK_SIZE - 1) // BLOCK_SIZE for c in ctx))
+    bt = rng.permutation(B * nbps).astype(np.int32).reshape(B, nbps)
+    shape = (B * nbps, BLOCK_SIZE, Hkv, HEAD_DIM)
+    caches = [_normal_bf16(rng, shape) for _ in range(4)]
+    T = int(np.sum(n_new))
+    k_new = _normal_bf16(rng, (T, Hkv, HEAD_DIM))
+    v_new = _normal_bf16(rng, (T, Hkv, HEAD_DIM))
+    w_k = rng.standard_normal((4, Hkv, HEAD_DIM)).astype(np.float32)
+    w_v = rng.standard_normal((4, Hkv, HEAD_DIM)).astype(np.float32)
+    cu = np.concatenate([[0], np.cumsum(n_new)]).astype(np.int32)
+    return SconvCase(k_new, v_new, w_k, w_v, *caches, bt, ctx, cu, name)
+
+
 # ----------------------------------------------------------------------------
-# The five named workloads
+# The named workloads
 # ----------------------------------------------------------------------------
 WORKLOADS = {
     "tiny_prefill_fp32": "batch 1, L=256, 4 q / 1 kv heads, fp32, full causal, R=256",
@@ -241,6 +278,8 @@ WORKLOADS = {
     "mtp_verify_1m": "batch 1, 9 queries at the tail of 1,048,576 keys, 16/2 heads, bf16, full, R=8192",
     "paged_prefill_b4": "batch 4, 2048-query chunks at the tails of 8192/16384/24576/32768-key paged contexts, "
                         "16/2 heads, bf16, full causal, R=8192",
+    "kv_sconv_32k": "batch 4, 8192 new tokens each after prefixes of 0/8192/16384/24576 tokens, 2 KV heads, "
+                    "bf16, window-4 short convolution into paged caches",
 }
 
 
@@ -273,6 +312,10 @@ def paged_prefill_b4(seed: int = 0) -> DecodeCase:
     return make_decode(seed, [8192, 16384, 24576, 32768], [0, 0, 0, 0], 2048, 16, 2, 8192, "paged_prefill_b4")
 
 
+def kv_sconv_32k(seed: int = 0) -> SconvCase:
+    return make_sconv(seed, [8192, 16384, 24576, 32768], [8192] * 4, 2, "kv_sconv_32k")
+
+
 WORKLOAD_FNS = {
     "tiny_prefill_fp32": tiny_prefill_fp32,
     "swa_prefill_8k": swa_prefill_8k,
@@ -280,4 +323,5 @@ WORKLOAD_FNS = {
     "paged_decode_b64": paged_decode_b64,
     "mtp_verify_1m": mtp_verify_1m,
     "paged_prefill_b4": paged_prefill_b4,
+    "kv_sconv_32k": kv_sconv_32k,
 }
