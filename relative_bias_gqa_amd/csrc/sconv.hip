@@ -24,7 +24,7 @@ namespace rattn {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kTokensPerBlock = 64;
+constexpr int kTokensPerBlock = 16;
 
 __global__ __launch_bounds__(kThreads) void sconv_write_kernel(SconvParams p) {
   const int b = blockIdx.y;
