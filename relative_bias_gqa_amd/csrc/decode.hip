@@ -135,14 +135,16 @@ __device__ __forceinline__ void cursor_next(const DecodeParams& p, Cursor& c) {
 }
 
 // NW: waves per workgroup (4, or 8 = two per SIMD, so that one wave's softmax overlaps
-// its partner's MFMAs).  KS: waves sharing the keys of a unit (2: one 32-key half each;
-// 1: a wave takes both).  NL: waves that issue the loads, the last NL of the workgroup
-// (NL = NW: every wave; NL < NW: waves without a computing role, so that the computing
-// waves spend no instructions on addresses, block-table reads and load issue).  NB: bias
-// loads per loading wave and unit (64 floats each), NB * 64 * NL >= gs * SL.
-template <int NW, int KS, int NL, int NB>
+// its partner's MFMAs).  Every computing wave owns one 32-row block and one 32-key half of
+// each unit (KS = 2 waves share a unit's keys, KB = 1 key block per wave).  NL: waves that
+// issue the loads, the last NL of the workgroup (NL = NW: every wave; NL < NW: waves
+// without a computing role, so that the computing waves spend no instructions on
+// addresses, block-table reads and load issue).  NB: bias loads per loading wave and unit
+// (64 floats each), NB * 64 * NL >= gs * SL.
+template <int NW, int NL, int NB>
 __global__ __launch_bounds__(64 * NW, 1) void decode_split_kernel(DecodeParams p) {
   constexpr int NT = 64 * NW;
+  constexpr int KS = 2;            // waves sharing the keys of a unit
   constexpr int KB = 2 / KS;       // 32-key blocks per computing wave and unit
   constexpr int TPW = kUnit / NL;  // tokens of a unit loaded by one loading wave
   constexpr int NI = TPW / 4;      // K (and V) load instructions per loading wave and unit
@@ -245,14 +247,14 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_split_kernel(DecodeParams p
   };
 
   // ---- this wave's role: row block rb (32 rows) and key half ks of every unit ----------
-  // With at most two row blocks the two 32-key halves of a unit go to different waves,
-  // which keep separate online-softmax states (separate pieces for the merge kernel).
+  // Wave w takes row block w % n_rb and key half w / n_rb (waves past 2 n_rb compute
+  // nothing); the two halves keep separate online-softmax states (separate pieces for the
+  // merge kernel).
   const int n_rb = (p.rows + 31) / 32;
-  const int rb_span = KS == 2 ? n_rb : NW;
-  const int rb = wave % rb_span;
-  const int ks_w = wave / rb_span;
+  const int rb = wave % n_rb;
+  const int ks_w = wave / n_rb;
   const bool wave_active = rb < n_rb && ks_w < KS;
-  const int kb_lo = KS == 2 ? ks_w : 0;
+  const int kb_lo = ks_w;
   // LDS operand bases (stage 0).  K rows are 256 B with 16-byte chunk c of key j at chunk
   // c ^ (j & 15): the A operand of k-step k8 (key 32 kb + col, chunk 2 k8 + hf) sits at
   // kx0 ^ (32 k8).  V rows have chunk c of key j at c ^ (2 (j & 7)): the transposed read
@@ -631,7 +633,7 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   if (nb < 1 || nb * 64 * NL > kDecodeBiasFloats) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)p.P);
 #define RATTN_SPLIT(NW_, NL_, NB_) \
-  hipLaunchKernelGGL((decode_split_kernel<NW_, 2, NL_, NB_>), grid, dim3(64 * NW_), 0, stream, p)
+  hipLaunchKernelGGL((decode_split_kernel<NW_, NL_, NB_>), grid, dim3(64 * NW_), 0, stream, p)
   if (NL == 2) {
     // bias loads of up to 1024 floats spread over two waves
     switch (nb) {

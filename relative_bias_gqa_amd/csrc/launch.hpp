@@ -92,7 +92,7 @@ struct DecodeParams {
   int KH;         // Hkv * n_hs segments per sequence
   int rows;       // n_q * gs query rows per segment
   int SL;         // bias entries per head staged for one unit: 63 + n_q
-  int KS;         // waves sharing a unit's keys (2: one 32-key half each, 1: both halves)
+  int KS;         // waves sharing a unit's keys: 2, one 32-key half each
   int NW;         // waves per split workgroup (4, or 8 when rows > 64)
   int P;          // split workgroups
   float scale_log2;
