@@ -143,3 +143,22 @@ def test_paged_prefill_packed_varlen_queries(window):
     exp_l = np.concatenate([ref_l[b, max_q - n:] for b, n in enumerate(qlens)], axis=0)
     compare(host(out), host(lse), exp_o, exp_l, f"varlen window={window}")
 
+
+def test_paged_prefill_many_sequences():
+    """More sequences than the workgroups rank by context length (1024): jobs go in sequence
+    order; with and without the job queue the result is the same bit for bit and matches the
+    oracle."""
+    print("case paged prefill 1100 sequences", flush=True)
+    rng = np.random.default_rng(69)
+    B, Lq = 1100, 8
+    ctx = rng.integers(Lq, 200, size=B).tolist()
+    case = synth.make_decode(69, ctx, [0] * B, Lq, 16, 2, 64, name="many")
+    d = decode_to_device(case)
+    args = (d["q"], d["k_cache"], d["v_cache"], d["block_table"], d["ctx_lens"], d["bias"], case.max_ctx_len, 0)
+    out_q, lse_q = rb.prefill_paged(*args)
+    out_n, lse_n = rb.prefill_paged(*args, workspace=None)
+    torch.cuda.synchronize()
+    assert _bitwise_equal(out_q, out_n) and _bitwise_equal(lse_q, lse_n)
+    ref_o, ref_l, _ = oracle.ref_decode(case)
+    compare(host(out_q), host(lse_q), ref_o, ref_l, "many sequences")
+

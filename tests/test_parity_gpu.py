@@ -153,3 +153,19 @@ def test_mtp_verify_1m_workload():
     out, lse = run_decode(case)
     ref_o, ref_l, _ = oracle.ref_decode(case)
     compare(out, lse, ref_o, ref_l, case.name)
+
+
+def test_decode_batch_over_one_launch():
+    """2100 sequences: the library runs launches of at most 2048 sequences, one after the
+    other through the same workspace; every sequence still matches the oracle."""
+    print("case decode 2100 sequences", flush=True)
+    rng = np.random.default_rng(29)
+    B = 2100
+    ctx = rng.integers(1, 129, size=B).tolist()
+    windows = [int(w) for w in np.where(np.arange(B) % 3 == 0, 40, 0)]
+    case = synth.make_decode(29, ctx, windows, 1, 16, 2, 64)
+    ref_o, ref_l, _ = oracle.ref_decode(case)
+    for ns in (0, 7):
+        out, lse = run_decode(case, ns)
+        compare(out, lse, ref_o, ref_l, f"decode B=2100 splits={ns}")
+
