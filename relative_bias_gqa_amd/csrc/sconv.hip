@@ -66,6 +66,8 @@ __global__ __launch_bounds__(kThreads) void sconv_write_kernel(SconvParams p) {
     return ((size_t)phys * 128 + (pos & 127)) * row;
   };
   const int t_end = min(n, t_begin + kTokensPerBlock);
+  // two tokens per iteration keep twice the loads in flight (measured 3 % faster; 4 was slower)
+#pragma unroll 2
   for (int t = t_begin + tok_in_pass; t < t_end; t += per_pass) {
     const int pos = start + t;
     float acc[8];
@@ -88,7 +90,9 @@ __global__ __launch_bounds__(kThreads) void sconv_write_kernel(SconvParams p) {
     const size_t dst = slot_of(pos) + ch;
     *(u32x4_t*)(cache + dst) = u32x4_t{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
                                        pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
-    *(u32x4_t*)(state + dst) = x0;
+    // the state row is read again only by a later call (the three rows before its chunk):
+    // stream it past the caches (non-temporal, measured 1.5 % faster)
+    __builtin_nontemporal_store(x0, (u32x4_t*)(state + dst));
   }
 }
 
