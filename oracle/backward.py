@@ -1,0 +1,77 @@
+"""fp64 CPU oracle for the backward pass of relative-bias grouped-query attention.
+
+TEST INFRASTRUCTURE, NOT PRODUCT CODE: only the test suite and the benchmark use it.  It
+shares nothing with the HIP library.
+
+The forward pass is the one of the vLLM recipes page "thinkingmachines/Inkling", Overview >
+Architectural highlights > Attention (a learned relative-position term added to the
+pre-softmax logits of GQA with head size 128), with the term read as r[h, min(i - j, R - 1)]:
+
+    s[i, j] = q_i . k_j / sqrt(D) + r[h, min(p_i - j, R - 1)]   over the visible keys j,
+    P = softmax_j(s),  O = P V,
+
+where query i of a prefill with Lk keys sits at p_i = Lk - Lq + i and key j is visible iff
+0 <= p_i - j (and p_i - j <= W - 1 for a window W > 0).  The page lists training and LoRA
+among what the model is used for; the backward pass is the plain chain rule of that
+definition for a loss whose gradient with respect to O is dO:
+
+    dP = dO V^T,  dS = P * (dP - rowsum(P * dP)),
+    dQ = dS K / sqrt(D),  dK = dS^T Q / sqrt(D),  dV = P^T dO,
+    dr[h, d] = sum of dS[i, j] over the visible (i, j) with min(p_i - j, R - 1) = d,
+
+with dK and dV summed over the query heads that share a KV head.  Every step is a dense
+matrix product or an elementwise operation in float64, one (sequence, head) at a time.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .sconv import bf16_to_f64
+
+
+def _f64(a: np.ndarray) -> np.ndarray:
+    a = np.asarray(a)
+    return bf16_to_f64(a) if a.dtype == np.uint16 else a.astype(np.float64)
+
+
+def prefill_backward(q, k, v, bias, dout, window: int = 0):
+    """Gradients of a prefill (every sequence has Lk keys; query t at Lk - Lq + t).
+
+    q [B, Lq, Hq, D], k and v [B, Lk, Hkv, D], dout [B, Lq, Hq, D]: uint16 (bf16 bits),
+    float32 or float64; bias [Hq, R].  Returns float64 arrays
+    (dq [B, Lq, Hq, D], dk [B, Lk, Hkv, D], dv [B, Lk, Hkv, D], dbias [Hq, R],
+    dbias_abs [Hq, R]); dbias_abs holds the sums of |dS| behind each dbias entry (for error
+    bounds: dbias entries are sums whose terms cancel)."""
+    Q, K, V, dO = _f64(q), _f64(k), _f64(v), _f64(dout)
+    r = np.asarray(bias, dtype=np.float64)
+    B, Lq, Hq, D = Q.shape
+    Lk, Hkv = K.shape[1], K.shape[2]
+    G = Hq // Hkv
+    R = r.shape[1]
+    scale = 1.0 / np.sqrt(D)
+    p = (Lk - Lq) + np.arange(Lq)[:, None]
+    dist = p - np.arange(Lk)[None, :]
+    vis = dist >= 0
+    if window > 0:
+        vis &= dist <= window - 1
+    didx = np.minimum(np.maximum(dist, 0), R - 1)
+    dq = np.zeros_like(Q)
+    dk = np.zeros_like(K)
+    dv = np.zeros_like(V)
+    dbias = np.zeros((Hq, R))
+    dbias_abs = np.zeros((Hq, R))
+    for b in range(B):
+        for h in range(Hq):
+            hk = h // G
+            s = Q[b, :, h] @ K[b, :, hk].T * scale + r[h][didx]
+            s = np.where(vis, s, -np.inf)
+            e = np.exp(s - s.max(axis=1, keepdims=True))
+            P = e / e.sum(axis=1, keepdims=True)
+            dP = dO[b, :, h] @ V[b, :, hk].T
+            dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+            dq[b, :, h] = dS @ K[b, :, hk] * scale
+            dk[b, :, hk] += dS.T @ Q[b, :, h] * scale
+            dv[b, :, hk] += P.T @ dO[b, :, h]
+            dbias[h] += np.bincount(didx[vis], weights=dS[vis], minlength=R)
+            dbias_abs[h] += np.bincount(didx[vis], weights=np.abs(dS[vis]), minlength=R)
+    return dq, dk, dv, dbias, dbias_abs
