@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define RATTN_ABI_VERSION 5
+#define RATTN_ABI_VERSION 6
 
 enum rattn_status {
   RATTN_OK = 0,
@@ -192,6 +192,45 @@ int rattn_kv_sconv_write(const void* k_new, const void* v_new, const float* w_k,
                          const int* block_table, const int* ctx_lens, const int* cu_seqlens, int B,
                          int Hkv, int head_dim, int block_size, int num_blocks,
                          int max_blocks_per_seq, int max_new, void* stream);
+
+/*
+ * Device workspace, in bytes, that rattn_prefill_backward needs: one fp32 per query row
+ * (B * Lq * Hq of them), rounded up to 256 bytes.  Returns 0 for negative sizes.
+ */
+size_t rattn_prefill_backward_workspace_bytes(int B, int Lq, int Hq);
+
+/*
+ * Gradients of rattn_prefill (bf16, contiguous K/V) for an output gradient dout.
+ * vLLM recipes page "thinkingmachines/Inkling", Overview > Architectural highlights >
+ * Attention defines the forward pass (relative-position term on the pre-softmax logits of
+ * GQA, head size 128); the same page lists training and LoRA among the model's uses.  With
+ * s = q.k / sqrt(128) + r[h, min(p - j, R - 1)] over the visible keys (the visibility and
+ * positions of rattn_prefill), P = softmax(s) recomputed from lse, D = rowsum(dout * out):
+ *   dS = P * (dout V^T - D),  dq = dS K / sqrt(128),  dk = dS^T Q / sqrt(128),
+ *   dv = P^T dout,  dbias[h, d] = sum of dS over the pairs at clamped distance d,
+ * dk and dv summed over the query heads of each KV head.
+ *
+ *   q, out, dout  [B, Lq, Hq, 128]    bf16   device, read (out and lse: rattn_prefill's
+ *   k, v          [B, Lk, Hkv, 128]   bf16   device, read  results for these inputs)
+ *   bias          [Hq, R]             fp32   device, read
+ *   lse           [B, Lq, Hq]         fp32   device, read (natural log)
+ *   dq            [B, Lq, Hq, 128]    fp32   device, written
+ *   dk, dv        [B, Lk, Hkv, 128]   fp32   device, written (zeroed, then accumulated)
+ *   dbias         [Hq, R]             fp32   device, written (zeroed, then accumulated)
+ *   workspace     device scratch of at least rattn_prefill_backward_workspace_bytes(...)
+ *   window        <= 0 full causal, > 0 sliding window of that many keys
+ *
+ * The caller owns every buffer; the call enqueues its kernels on `stream` and returns.
+ * dk, dv and dbias are sums of fp32 atomic adds, so their last bits may differ from run
+ * to run; dq is deterministic.  Status: INVALID_ARG (null pointer, sizes, Lq > Lk,
+ * B or Hq > 65535), UNSUPPORTED (head_dim != 128), WORKSPACE (missing or too small),
+ * HIP (launch failure).
+ */
+int rattn_prefill_backward(const void* q, const void* k, const void* v, const float* bias,
+                           const void* out, const void* dout, const float* lse, float* dq,
+                           float* dk, float* dv, float* dbias, int B, int Lq, int Lk, int Hq,
+                           int Hkv, int head_dim, int R, int window, void* workspace,
+                           size_t workspace_bytes, void* stream);
 
 /*
  * Number of split workgroups rattn_decode_paged will use for these arguments.  The

@@ -25,9 +25,10 @@ LIB_PATH = os.path.join(_HERE, "librattn.so")
 
 RATTN_OK, RATTN_ERR_INVALID_ARG, RATTN_ERR_UNSUPPORTED, RATTN_ERR_WORKSPACE, RATTN_ERR_HIP = 0, 1, 2, 3, 4
 RATTN_BF16, RATTN_FP32 = 0, 1
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 EXPORTED = ("rattn_prefill_workspace_bytes", "rattn_prefill", "rattn_prefill_paged", "rattn_kv_sconv_write",
+            "rattn_prefill_backward_workspace_bytes", "rattn_prefill_backward",
             "rattn_decode_num_splits", "rattn_decode_workspace_bytes", "rattn_decode_paged", "rattn_last_error",
             "rattn_abi_version")
 
@@ -59,6 +60,10 @@ def load(path: Optional[str] = None):
     lib.rattn_prefill_paged.argtypes = [vp] * 9 + [i32] * 11 + [vp, sz, vp]
     lib.rattn_kv_sconv_write.restype = i32
     lib.rattn_kv_sconv_write.argtypes = [vp] * 11 + [i32] * 7 + [vp]
+    lib.rattn_prefill_backward_workspace_bytes.restype = sz
+    lib.rattn_prefill_backward_workspace_bytes.argtypes = [i32] * 3
+    lib.rattn_prefill_backward.restype = i32
+    lib.rattn_prefill_backward.argtypes = [vp] * 11 + [i32] * 8 + [vp, sz, vp]
     lib.rattn_decode_num_splits.restype = i32
     lib.rattn_decode_num_splits.argtypes = [i32] * 6
     lib.rattn_decode_workspace_bytes.restype = sz
@@ -177,6 +182,25 @@ def rattn_kv_sconv_write(k_new, v_new, w_k, w_v, k_cache, v_cache, k_state, v_st
                                        _stream(stream)))
 
 
+def rattn_prefill_backward_workspace_bytes(B: int, Lq: int, Hq: int) -> int:
+    return load().rattn_prefill_backward_workspace_bytes(B, Lq, Hq)
+
+
+def rattn_prefill_backward(q, k, v, bias, out, dout, lse, dq, dk, dv, dbias, window: int, workspace,
+                           stream=None) -> None:
+    """q/out/dout [B,Lq,Hq,128] bf16; k/v [B,Lk,Hkv,128] bf16; bias [Hq,R] fp32; lse [B,Lq,Hq]
+    fp32 (rattn_prefill's out and lse); dq like q, dk/dv like k, dbias like bias, all fp32;
+    workspace a device tensor of at least rattn_prefill_backward_workspace_bytes(B, Lq, Hq)
+    bytes."""
+    B, Lq, Hq, D = q.shape
+    Lk, Hkv = k.shape[1], k.shape[2]
+    R = bias.shape[1]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().rattn_prefill_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(out), _ptr(dout), _ptr(lse),
+                                         _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbias), B, Lq, Lk, Hq, Hkv, D, R,
+                                         int(window), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
 def rattn_decode_num_splits(B: int, n_q: int, Hq: int, Hkv: int, max_ctx_len: int, num_splits: int = 0) -> int:
     return load().rattn_decode_num_splits(B, n_q, Hq, Hkv, max_ctx_len, num_splits)
 
@@ -230,6 +254,20 @@ def prefill(q, k, v, bias, window: int = 0, want_lse: bool = True, kv_splits: in
         workspace = prefill_workspace(n, q.device) if n > 0 else None
     rattn_prefill(q, k, v, bias, out, lse, window, kv_splits, workspace, stream)
     return out, lse
+
+
+def prefill_backward(q, k, v, bias, out, lse, dout, window: int = 0, stream=None) -> Tuple:
+    """Allocate fp32 gradients and a workspace, call rattn_prefill_backward; returns
+    (dq, dk, dv, dbias)."""
+    import torch
+    dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    dk = torch.empty(k.shape, dtype=torch.float32, device=q.device)
+    dv = torch.empty(v.shape, dtype=torch.float32, device=q.device)
+    dbias = torch.empty(bias.shape, dtype=torch.float32, device=q.device)
+    n = rattn_prefill_backward_workspace_bytes(q.shape[0], q.shape[1], q.shape[2])
+    ws = torch.empty(n, dtype=torch.uint8, device=q.device)
+    rattn_prefill_backward(q, k, v, bias, out, dout, lse, dq, dk, dv, dbias, window, ws, stream)
+    return dq, dk, dv, dbias
 
 
 def prefill_paged(q, k_cache, v_cache, block_table, ctx_lens, bias, max_ctx_len: int, window: int = 0,

@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "librattn.so")
-SOURCES = ["abi.cpp", "prefill.hip", "prefill_bf16.hip", "decode.hip", "sconv.hip"]
+SOURCES = ["abi.cpp", "prefill.hip", "prefill_bf16.hip", "decode.hip", "sconv.hip", "backward.hip"]
 ARCH = "gfx950"
 
 

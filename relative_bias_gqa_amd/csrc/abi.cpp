@@ -482,6 +482,62 @@ int rattn_kv_sconv_write(const void* k_new, const void* v_new, const float* w_k,
   return ok();
 }
 
+size_t rattn_prefill_backward_workspace_bytes(int B, int Lq, int Hq) {
+  if (B < 0 || Lq < 0 || Hq < 0) return 0;
+  const size_t rows = (size_t)B * Lq * Hq;
+  return std::max<size_t>(256, (rows * sizeof(float) + 255) / 256 * 256);
+}
+
+int rattn_prefill_backward(const void* q, const void* k, const void* v, const float* bias, const void* out,
+                           const void* dout, const float* lse, float* dq, float* dk, float* dv, float* dbias, int B,
+                           int Lq, int Lk, int Hq, int Hkv, int head_dim, int R, int window, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  if (B < 0 || Lq < 0 || Lk < 0 || Hq < 0 || Hkv < 0)
+    return fail(RATTN_ERR_INVALID_ARG, "rattn_prefill_backward: negative size (B=%d Lq=%d Lk=%d Hq=%d Hkv=%d)", B,
+                Lq, Lk, Hq, Hkv);
+  if (head_dim != 128)
+    return fail(RATTN_ERR_UNSUPPORTED, "rattn_prefill_backward: head_dim %d (only 128)", head_dim);
+  if (!q || !k || !v || !bias || !out || !dout || !lse || !dq || !dk || !dv || !dbias)
+    return fail(RATTN_ERR_INVALID_ARG, "rattn_prefill_backward: null pointer argument");
+  if (Hkv < 1 || Hq < Hkv || Hq % Hkv != 0)
+    return fail(RATTN_ERR_INVALID_ARG, "rattn_prefill_backward: Hq=%d must be a positive multiple of Hkv=%d", Hq,
+                Hkv);
+  if (Lq > Lk) return fail(RATTN_ERR_INVALID_ARG, "rattn_prefill_backward: Lq=%d > Lk=%d", Lq, Lk);
+  if (Lk > kMaxPosition) return fail(RATTN_ERR_INVALID_ARG, "rattn_prefill_backward: Lk=%d too large", Lk);
+  if (R < 1) return fail(RATTN_ERR_INVALID_ARG, "rattn_prefill_backward: R=%d < 1", R);
+  if (B > 65535 || Hq > 65535)
+    return fail(RATTN_ERR_INVALID_ARG, "rattn_prefill_backward: B=%d or Hq=%d > 65535", B, Hq);
+  const size_t need = rattn_prefill_backward_workspace_bytes(B, Lq, Hq);
+  if (!workspace || workspace_bytes < need)
+    return fail(RATTN_ERR_WORKSPACE, "rattn_prefill_backward: workspace of %zu bytes, %zu needed",
+                workspace ? workspace_bytes : (size_t)0, need);
+  rattn::BackwardParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.bias = bias;
+  p.out = out;
+  p.dout = dout;
+  p.lse = lse;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.dbias = dbias;
+  p.D = (float*)workspace;
+  p.B = B;
+  p.Lq = Lq;
+  p.Lk = Lk;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.G = Hq / Hkv;
+  p.R = R;
+  p.window = window;
+  p.scale_log2 = kScaleLog2;
+  hipError_t e = rattn::launch_backward(p, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(RATTN_ERR_HIP, "rattn_prefill_backward: launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 size_t rattn_prefill_workspace_bytes(int B, int Lq, int Lk, int Hq, int Hkv, int window, int dtype,
                                      int kv_splits) {
   if (B < 1 || Lq < 1 || Lk < Lq || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || Lk > kMaxPosition ||

@@ -1,0 +1,291 @@
+// backward.hip -- gradients of the relative-bias GQA prefill (bf16 inputs), gfx950.
+//
+// The forward pass (vLLM recipes page "thinkingmachines/Inkling", Overview > Architectural
+// highlights > Attention: a learned relative-position term added to the pre-softmax logits
+// of GQA with head size 128; the page also lists training and LoRA among the model's uses)
+// is s = q.k / sqrt(128) + r[h, min(p - j, R - 1)] over the visible keys, P = softmax(s),
+// O = P V.  Its gradients for an output gradient dO, with D = rowsum(dO * O):
+//   dS = P * (dO V^T - D),  dQ = dS K / sqrt(128),  dK = dS^T Q / sqrt(128),  dV = P^T dO,
+//   dr[h, d] = sum of dS over the (query, key) pairs at clamped distance d,
+// dK and dV summed over the query heads of a KV head.  P is recomputed from the forward's
+// log-sum-exp, never stored.
+//
+// Three passes on the caller's stream, after a fill that zeroes dk, dv and dr:
+//   1. D per query row (fp32, from the bf16 out and dout);
+//   2. key-stationary: one wave per (32 keys, query head) walks the query tiles that see its
+//      keys; S = Q K^T and dP = dO V^T come out with one key per lane (the accumulator
+//      column), which is the register layout the A operand of dV += P^T dO and
+//      dK += dS^T Q needs, so P and dS feed the MFMAs straight from registers; dO and Q are
+//      read transposed from LDS for the B operand.  dK and dV of the wave's head are added
+//      into dk, dv at the end (fp32 atomics, one add per element per query head); dS is
+//      summed per distance in LDS (a 63-entry band per query tile) and the band added into
+//      dr;
+//   3. query-stationary: one wave per (32 queries, query head) walks the key tiles its
+//      queries see; S^T and dP^T come out with one query per lane, the B-operand layout of
+//      dQ^T += K^T dS^T, so dQ is accumulated in registers and stored once.
+// All products are v_mfma_f32_32x32x16_bf16 with fp32 accumulation; P and dS are rounded to
+// bf16 as MFMA operands.  Tiles sit in LDS with 272-byte rows (256 bytes of data and 16 of
+// padding) so that the row-wise operand reads of 32 consecutive rows spread over the banks.
+#include <algorithm>
+
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace rattn {
+namespace {
+
+constexpr int kRows = 32;                  // keys or queries per wave tile
+constexpr int kStride = 136;               // LDS row stride of a 128-wide bf16 tile (elements)
+constexpr int kTileElems = kRows * kStride;
+constexpr float kRsqrtD = 0.08838834764831845f;  // 1 / sqrt(128)
+
+// 32 rows of 128 bf16 from global memory (row r at src + r * row_stride) into an LDS tile;
+// rows at or past n_valid are zero.  One wave, 16 bytes per lane per pass.
+__device__ __forceinline__ void load_tile(uint16_t* tile, const uint16_t* src, size_t row_stride, int n_valid,
+                                          int lane) {
+#pragma unroll
+  for (int pass = 0; pass < 8; ++pass) {
+    const int idx = pass * 64 + lane;
+    const int row = idx >> 4, c = idx & 15;
+    u32x4_t x = zero_u32x4();
+    if (row < n_valid) x = *(const u32x4_t*)(src + row * row_stride + c * 8);
+    *(u32x4_t*)(tile + row * kStride + c * 8) = x;
+  }
+}
+
+// Operand of k-step ks read along rows: lane l gets row (l & 31), elements 16 ks + 8 (l >> 5)
+// .. + 7.  The A operand (rows of the product) and the B operand (columns) of
+// v_mfma_f32_32x32x16_bf16 both take this form when the tile is stored row by row.
+__device__ __forceinline__ u32x4_t row_operand(const uint16_t* tile, int ks, int lane) {
+  return *(const u32x4_t*)(tile + (lane & 31) * kStride + 16 * ks + 8 * (lane >> 5));
+}
+
+__global__ __launch_bounds__(256) void bwd_fill_zero_kernel(float* a, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) a[i] = 0.f;
+}
+
+// D[row] = sum_d dout[row, d] * out[row, d] for every (b, t, h) row, in fp32.
+__global__ __launch_bounds__(256) void bwd_rowdot_kernel(const uint16_t* out, const uint16_t* dout, float* D,
+                                                         size_t rows) {
+  const size_t row = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (row >= rows) return;
+  const u32x4_t* o = (const u32x4_t*)(out + row * kHeadDim);
+  const u32x4_t* g = (const u32x4_t*)(dout + row * kHeadDim);
+  float acc = 0.f;
+#pragma unroll 4
+  for (int c = 0; c < 16; ++c) {
+    const u32x4_t x = o[c], y = g[c];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc = fmaf(bf16_lo_to_f32(x[i]), bf16_lo_to_f32(y[i]), acc);
+      acc = fmaf(bf16_hi_to_f32(x[i]), bf16_hi_to_f32(y[i]), acc);
+    }
+  }
+  D[row] = acc;
+}
+
+// Key-stationary pass: dK, dV and dr.  Grid (key tiles, Hq, B), one wave each.
+__global__ __launch_bounds__(64) void bwd_dkdv_kernel(BackwardParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t kt[kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t vt[kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t qt[kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t gt[kTileElems];  // dO
+  __shared__ float lse_s[kRows];
+  __shared__ float d_s[kRows];
+  __shared__ float band[64];
+  const int lane = threadIdx.x;
+  const int col = lane & 31, hf = lane >> 5;
+  const int j0 = blockIdx.x * kRows;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int hk = h / p.G;
+  const int Lq = p.Lq, Lk = p.Lk, off = Lk - Lq;
+  const int Weff = p.window > 0 ? p.window : 0x40000000;
+  // queries that see a key of this tile: positions j0 .. j0 + 31 + Weff - 1
+  const int q_lo = max(0, j0 - off);
+  const int q_hi = (int)min((long long)Lq - 1, (long long)j0 + kRows - 1 + Weff - 1 - off);
+  const size_t kv_row = (size_t)p.Hkv * kHeadDim;
+  const size_t q_row = (size_t)p.Hq * kHeadDim;
+  const uint16_t* kg = (const uint16_t*)p.k + ((size_t)b * Lk + j0) * kv_row + (size_t)hk * kHeadDim;
+  const uint16_t* vg = (const uint16_t*)p.v + ((size_t)b * Lk + j0) * kv_row + (size_t)hk * kHeadDim;
+  load_tile(kt, kg, kv_row, min(kRows, Lk - j0), lane);
+  load_tile(vt, vg, kv_row, min(kRows, Lk - j0), lane);
+  band[lane] = 0.f;
+  const float* bias_h = p.bias + (size_t)h * p.R;
+  float* dbias_h = p.dbias + (size_t)h * p.R;
+  f32x16_t dk[4], dv[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) dk[db] = dv[db] = zero_f32x16();
+  const int j = j0 + col;  // this lane's key (accumulator column of S and dP)
+  for (int qi = q_lo / kRows; q_lo <= q_hi && qi <= q_hi / kRows; ++qi) {
+    const int q0 = qi * kRows;
+    const int nq = min(kRows, Lq - q0);
+    __syncthreads();  // the previous tile's reads of qt, gt, lse_s, d_s and the band are done
+    const size_t row0 = ((size_t)b * Lq + q0) * p.Hq + h;
+    load_tile(qt, (const uint16_t*)p.q + row0 * kHeadDim, q_row, nq, lane);
+    load_tile(gt, (const uint16_t*)p.dout + row0 * kHeadDim, q_row, nq, lane);
+    if (lane < kRows) {
+      lse_s[lane] = lane < nq ? p.lse[row0 + (size_t)lane * p.Hq] * kLog2e : 0.f;
+      d_s[lane] = lane < nq ? p.D[row0 + (size_t)lane * p.Hq] : 0.f;
+    }
+    __syncthreads();
+    // S = Q K^T and dP = dO V^T: rows are queries, the lane's column is key j
+    f32x16_t s = zero_f32x16(), dp = zero_f32x16();
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      s = mfma_32x32x16(row_operand(qt, ks, lane), row_operand(kt, ks, lane), s);
+      dp = mfma_32x32x16(row_operand(gt, ks, lane), row_operand(vt, ks, lane), dp);
+    }
+    // register r holds query 8 (r >> 2) + 4 hf + (r & 3) of the tile
+    float pr[16], ds[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int qq = 8 * (r >> 2) + 4 * hf + (r & 3);
+      const int dist = off + q0 + qq - j;
+      const bool vis = qq < nq && dist >= 0 && dist < Weff;
+      const float bv = vis ? bias_h[min(dist, p.R - 1)] : 0.f;
+      const float lg = fmaf(s[r], p.scale_log2, fmaf(bv, kLog2e, -lse_s[qq]));
+      pr[r] = vis ? fast_exp2(lg) : 0.f;
+      ds[r] = pr[r] * (dp[r] - d_s[qq]);
+      if (vis) atomicAdd(&band[qq - col + 31], ds[r]);
+    }
+    // dV += P^T dO and dK += dS^T Q: rows are keys (the lane's P and dS), columns dims
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
+      const u32x4_t ap = pack_p_operand(pr + 8 * qs);
+      const u32x4_t as = pack_p_operand(ds + 8 * qs);
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        dv[db] = mfma_32x32x16(ap, load_vt_operand(gt, kStride, 16 * qs, 32 * db, lane), dv[db]);
+        dk[db] = mfma_32x32x16(as, load_vt_operand(qt, kStride, 16 * qs, 32 * db, lane), dk[db]);
+      }
+    }
+    __syncthreads();
+    // band entry e holds the pairs at distance off + q0 - j0 + e - 31 (only visible ones, so
+    // a non-zero entry has a distance >= 0)
+    if (lane < 63) {
+      const float x = band[lane];
+      band[lane] = 0.f;
+      if (x != 0.f) unsafeAtomicAdd(dbias_h + min(off + q0 - j0 + lane - 31, p.R - 1), x);
+    }
+  }
+  // accumulator register 4 i + c of block db: key 8 i + 4 hf + c, dim 32 db + col
+  float* dkg = p.dk + ((size_t)b * Lk + j0) * kv_row + (size_t)hk * kHeadDim;
+  float* dvg = p.dv + ((size_t)b * Lk + j0) * kv_row + (size_t)hk * kHeadDim;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = 8 * (r >> 2) + 4 * hf + (r & 3);
+      if (j0 + key < Lk) {
+        const size_t o = (size_t)key * kv_row + 32 * db + col;
+        unsafeAtomicAdd(dkg + o, dk[db][r] * kRsqrtD);
+        unsafeAtomicAdd(dvg + o, dv[db][r]);
+      }
+    }
+}
+
+// Query-stationary pass: dQ.  Grid (query tiles, Hq, B), one wave each.
+__global__ __launch_bounds__(64) void bwd_dq_kernel(BackwardParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t qt[kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t gt[kTileElems];  // dO
+  __shared__ __attribute__((aligned(16))) uint16_t kt[kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t vt[kTileElems];
+  const int lane = threadIdx.x;
+  const int col = lane & 31, hf = lane >> 5;
+  const int q0 = blockIdx.x * kRows;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int hk = h / p.G;
+  const int Lq = p.Lq, Lk = p.Lk, off = Lk - Lq;
+  const int nq = min(kRows, Lq - q0);
+  const int Weff = p.window > 0 ? p.window : 0x40000000;
+  const size_t kv_row = (size_t)p.Hkv * kHeadDim;
+  const size_t q_row = (size_t)p.Hq * kHeadDim;
+  const size_t row0 = ((size_t)b * Lq + q0) * p.Hq + h;
+  load_tile(qt, (const uint16_t*)p.q + row0 * kHeadDim, q_row, nq, lane);
+  load_tile(gt, (const uint16_t*)p.dout + row0 * kHeadDim, q_row, nq, lane);
+  // this lane's query (accumulator column of S^T and dP^T)
+  const bool qvalid = col < nq;
+  const int pq = off + q0 + col;
+  const float lse2 = qvalid ? p.lse[row0 + (size_t)col * p.Hq] * kLog2e : 0.f;
+  const float dd = qvalid ? p.D[row0 + (size_t)col * p.Hq] : 0.f;
+  const float* bias_h = p.bias + (size_t)h * p.R;
+  // keys the tile's queries see: positions off + q0 - Weff + 1 .. off + q0 + 31
+  const int j_lo = max(0, off + q0 - Weff + 1);
+  const int j_hi = min(Lk - 1, off + q0 + nq - 1);
+  const uint16_t* kg = (const uint16_t*)p.k + (size_t)b * Lk * kv_row + (size_t)hk * kHeadDim;
+  const uint16_t* vg = (const uint16_t*)p.v + (size_t)b * Lk * kv_row + (size_t)hk * kHeadDim;
+  f32x16_t dq[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) dq[db] = zero_f32x16();
+  for (int kti = j_lo / kRows; j_lo <= j_hi && kti <= j_hi / kRows; ++kti) {
+    const int j0 = kti * kRows;
+    __syncthreads();  // the previous tile's reads of kt and vt are done
+    load_tile(kt, kg + (size_t)j0 * kv_row, kv_row, min(kRows, Lk - j0), lane);
+    load_tile(vt, vg + (size_t)j0 * kv_row, kv_row, min(kRows, Lk - j0), lane);
+    __syncthreads();
+    // S^T = K Q^T and dP^T = V dO^T: rows are keys, the lane's column is its query
+    f32x16_t st = zero_f32x16(), dpt = zero_f32x16();
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      st = mfma_32x32x16(row_operand(kt, ks, lane), row_operand(qt, ks, lane), st);
+      dpt = mfma_32x32x16(row_operand(vt, ks, lane), row_operand(gt, ks, lane), dpt);
+    }
+    // register r holds key j0 + 8 (r >> 2) + 4 hf + (r & 3)
+    float ds[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int dist = pq - (j0 + 8 * (r >> 2) + 4 * hf + (r & 3));
+      const bool vis = qvalid && dist >= 0 && dist < Weff;
+      const float bv = vis ? bias_h[min(dist, p.R - 1)] : 0.f;
+      const float lg = fmaf(st[r], p.scale_log2, fmaf(bv, kLog2e, -lse2));
+      const float pr = vis ? fast_exp2(lg) : 0.f;
+      ds[r] = pr * (dpt[r] - dd);
+    }
+    // dQ^T += K^T dS^T: rows are dims (K read transposed), the lane's column its query
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const u32x4_t bs = pack_p_operand(ds + 8 * ks);
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+        dq[db] = mfma_32x32x16(load_vt_operand(kt, kStride, 16 * ks, 32 * db, lane), bs, dq[db]);
+    }
+  }
+  if (!qvalid) return;
+  // accumulator register 4 i + c of block db: dim 32 db + 8 i + 4 hf + c of query q0 + col
+  float* dqg = p.dq + (row0 + (size_t)col * p.Hq) * kHeadDim;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f32x4_t x;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) x[c] = dq[db][4 * i + c] * kRsqrtD;
+      *(f32x4_t*)(dqg + 32 * db + 8 * i + 4 * hf) = x;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_backward(const BackwardParams& p, hipStream_t stream) {
+  const size_t n_kv = (size_t)p.B * p.Lk * p.Hkv * kHeadDim;
+  const size_t n_r = (size_t)p.Hq * p.R;
+  auto fill = [&](float* a, size_t n) {
+    if (n == 0) return;
+    const size_t blocks = std::min((n + 255) / 256, (size_t)4096);
+    hipLaunchKernelGGL(bwd_fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a, n);
+  };
+  fill(p.dk, n_kv);
+  fill(p.dv, n_kv);
+  fill(p.dbias, n_r);
+  if (p.B <= 0 || p.Lq <= 0 || p.Lk <= 0) return hipGetLastError();
+  const size_t rows = (size_t)p.B * p.Lq * p.Hq;
+  hipLaunchKernelGGL(bwd_rowdot_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream,
+                     (const uint16_t*)p.out, (const uint16_t*)p.dout, p.D, rows);
+  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)((p.Lk + kRows - 1) / kRows), (unsigned)p.Hq, (unsigned)p.B),
+                     dim3(64), 0, stream, p);
+  hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)((p.Lq + kRows - 1) / kRows), (unsigned)p.Hq, (unsigned)p.B),
+                     dim3(64), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace rattn

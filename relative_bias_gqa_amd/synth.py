@@ -137,6 +137,22 @@ def make_prefill(seed: int, B: int, Lq: int, Lk: int, Hq: int, Hkv: int, R: int,
     return PrefillCase(q, k, v, bias, window, dtype, name)
 
 
+@dataclass
+class BackwardCase:
+    fwd: PrefillCase          # q, k, v, r, window of the forward pass (bf16)
+    dout: np.ndarray          # [B, Lq, Hq, 128] uint16 (bf16 bits): gradient of the output
+    name: str = ""
+
+
+def make_backward(seed: int, B: int, Lq: int, Lk: int, Hq: int, Hkv: int, R: int, window: int,
+                  name: str = "") -> BackwardCase:
+    """Draw order: the prefill case of the same seed (Q, K, V, r), then dO N(0,1) from a
+    generator seeded with (seed, 1)."""
+    fwd = make_prefill(seed, B, Lq, Lk, Hq, Hkv, R, window, "bf16", name)
+    rng = np.random.default_rng([seed, 1])
+    return BackwardCase(fwd, _normal(rng, (B, Lq, Hq, HEAD_DIM), "bf16"), name)
+
+
 # ----------------------------------------------------------------------------
 # Paged decode
 # ----------------------------------------------------------------------------

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.rattn_abi_version() == rb.ABI_VERSION == 5
+    assert lib.rattn_abi_version() == rb.ABI_VERSION == 6
 
 
 def _prefill(lib, **kw):
@@ -246,3 +246,37 @@ def test_sconv_empty_is_noop(lib):
     assert _sconv(lib, B=0, kn=None) == rb.RATTN_OK
     assert _sconv(lib, max_new=0, kc=None) == rb.RATTN_OK
 
+
+
+def _bwd(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, r=FAKE, o=FAKE, do=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, dr=FAKE, B=1, Lq=64,
+             Lk=64, Hq=4, Hkv=2, D=128, R=16, W=0, ws=FAKE, wsb=1 << 20, stream=None)
+    a.update(kw)
+    return lib.rattn_prefill_backward(a["q"], a["k"], a["v"], a["r"], a["o"], a["do"], a["lse"], a["dq"], a["dk"],
+                                      a["dv"], a["dr"], a["B"], a["Lq"], a["Lk"], a["Hq"], a["Hkv"], a["D"], a["R"],
+                                      a["W"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(q=None), rb.RATTN_ERR_INVALID_ARG, "null"),
+    (dict(dr=None), rb.RATTN_ERR_INVALID_ARG, "null"),
+    (dict(lse=None), rb.RATTN_ERR_INVALID_ARG, "null"),
+    (dict(Hq=3), rb.RATTN_ERR_INVALID_ARG, "multiple"),
+    (dict(Lq=65), rb.RATTN_ERR_INVALID_ARG, "Lq="),
+    (dict(R=0), rb.RATTN_ERR_INVALID_ARG, "R="),
+    (dict(B=-1), rb.RATTN_ERR_INVALID_ARG, "negative"),
+    (dict(B=70000), rb.RATTN_ERR_INVALID_ARG, "65535"),
+    (dict(D=64), rb.RATTN_ERR_UNSUPPORTED, "head_dim"),
+    (dict(ws=None), rb.RATTN_ERR_WORKSPACE, "workspace"),
+    (dict(wsb=255), rb.RATTN_ERR_WORKSPACE, "workspace"),
+])
+def test_backward_validation(lib, kw, status, needle):
+    assert _bwd(lib, **kw) == status
+    assert needle in rb.rattn_last_error()
+
+
+def test_backward_workspace_formula():
+    assert rb.rattn_prefill_backward_workspace_bytes(1, 8192, 16) == 8192 * 16 * 4
+    assert rb.rattn_prefill_backward_workspace_bytes(1, 3, 1) == 256
+    assert rb.rattn_prefill_backward_workspace_bytes(0, 0, 0) == 256
+    assert rb.rattn_prefill_backward_workspace_bytes(-1, 1, 1) == 0

@@ -1,0 +1,78 @@
+"""Backward pass of the bf16 prefill (rattn_prefill_backward) against the fp64 oracle.
+
+The forward runs on the GPU (rattn_prefill) to give out and lse, as in training; the oracle
+recomputes everything from q, k, v, r and dO.  Tolerances (bf16 inputs, fp32 accumulation;
+the rounding of P and dS to bf16 for the MFMAs and of out to bf16 in D = rowsum(dO * out)
+each move a term by at most 2^-9 of its size):
+  dq, dk, dv: |gpu - ref|_2 <= 1e-2 |ref|_2 and max |gpu - ref| <= 3e-2 max |ref|;
+  dbias[h, d]: |gpu - ref| <= 1e-2 * (sum of |dS| behind the entry) + 1e-6 * max of those sums
+  + 1e-6 per pair behind the entry;
+  a reference that is exactly zero: max |gpu| <= 1e-4 (fp32 rounding of dP - D).
+Cases: ragged lengths (tails of 12 and 20 rows), a chunk after a prefix (Lq < Lk), a window
+with one KV head, one query head per KV head with window 1 (closed form: dq = dk = dbias = 0).
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import dev, host
+
+import relative_bias_gqa_amd as rb
+from relative_bias_gqa_amd import synth
+from oracle.backward import prefill_backward
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # name, seed, B, Lq, Lk, Hq, Hkv, R, window
+    ("full_ragged", 81, 2, 300, 300, 8, 2, 100, 0),
+    ("chunk_after_prefix", 82, 1, 200, 660, 16, 2, 1000, 0),
+    ("window_one_kv_head", 83, 2, 500, 500, 8, 1, 64, 129),
+    ("window_one", 84, 1, 100, 130, 4, 4, 9, 1),
+]
+
+
+def run_backward(case):
+    f = case.fwd
+    q, k, v, r = dev(f.q), dev(f.k), dev(f.v), dev(f.bias)
+    out, lse = rb.prefill(q, k, v, r, f.window)
+    dq, dk, dv, dbias = rb.prefill_backward(q, k, v, r, out, lse, dev(case.dout), f.window)
+    torch.cuda.synchronize()
+    return host(dq), host(dk), host(dv), host(dbias)
+
+
+def check(name, got, ref):
+    assert np.isfinite(got).all(), f"{name}: non-finite"
+    err = got - ref
+    nrm = np.linalg.norm(ref)
+    rel = np.linalg.norm(err) / max(nrm, 1e-30)
+    mx = np.abs(err).max() if err.size else 0.0
+    print(f"  {name}: normwise {rel:.2e}, max {mx:.2e} (max |ref| {np.abs(ref).max():.2e})", flush=True)
+    if nrm == 0:
+        # an exact zero that the kernel reaches as dS = P (dP - D) with P = 1 and dP, D two
+        # fp32 dot products of 128 terms of size ~1 taken in different orders
+        assert mx <= 1e-4, name
+        return
+    assert rel <= 1e-2, name
+    assert mx <= 3e-2 * np.abs(ref).max(), name
+
+
+@pytest.mark.parametrize("name,seed,B,Lq,Lk,Hq,Hkv,R,window", CASES, ids=[c[0] for c in CASES])
+def test_backward_matches_oracle(name, seed, B, Lq, Lk, Hq, Hkv, R, window):
+    print(f"case backward {name}", flush=True)
+    case = synth.make_backward(seed, B, Lq, Lk, Hq, Hkv, R, window, name)
+    dq, dk, dv, dr = run_backward(case)
+    f = case.fwd
+    rq, rk, rv, rr, rabs = prefill_backward(f.q, f.k, f.v, f.bias, case.dout, window)
+    check("dq", dq, rq)
+    check("dk", dk, rk)
+    check("dv", dv, rv)
+    derr = np.abs(dr - rr)
+    # pairs behind each entry: every dS carries the fp32 rounding of dP - D (up to ~1e-6)
+    pos = (Lk - Lq) + np.arange(Lq)[:, None]
+    dist = pos - np.arange(Lk)[None, :]
+    vis = (dist >= 0) & ((window <= 0) | (dist <= window - 1))
+    npairs = B * np.bincount(np.minimum(dist[vis], R - 1), minlength=R)
+    bound = 1e-2 * rabs + 1e-6 * max(rabs.max(), 1e-30) + 1e-6 * npairs[None, :]
+    print(f"  dbias: max err {derr.max():.2e}, worst err/bound {(derr / bound).max():.2f}", flush=True)
+    assert (derr <= bound).all()
