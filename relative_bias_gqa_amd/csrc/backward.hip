@@ -34,10 +34,20 @@
 namespace rattn {
 namespace {
 
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
 constexpr int kRows = 32;                  // keys or queries per wave tile
 constexpr int kStride = 136;               // LDS row stride of a 128-wide bf16 tile (elements)
 constexpr int kTileElems = kRows * kStride;
 constexpr float kRsqrtD = 0.08838834764831845f;  // 1 / sqrt(128)
+constexpr int kDiagStride = 34;            // floats per row of the diagonal table (conflict free)
+static_assert(63 * kDiagStride * 4 <= kTileElems * 2, "the diagonal table reuses a tile's space");
+
+// The 63 bias entries a 32 x 32 tile meets: entry e = r[h, clamp(dbase + e, 0, R - 1)] for the
+// pairs at distance dbase + e, dbase = (distance of query 0 to key 31).  Lanes 0..62 load one.
+__device__ __forceinline__ void stage_bias(float* band, const float* bias_h, int dbase, int R, int lane) {
+  if (lane < 63) band[lane] = bias_h[min(max(dbase + lane, 0), R - 1)];
+}
 
 // 32 rows of 128 bf16 from global memory (row r at src + r * row_stride) into an LDS tile;
 // rows at or past n_valid are zero.  One wave, 16 bytes per lane per pass.
@@ -92,7 +102,10 @@ __global__ __launch_bounds__(64) void bwd_dkdv_kernel(BackwardParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t gt[kTileElems];  // dO
   __shared__ float lse_s[kRows];
   __shared__ float d_s[kRows];
-  __shared__ float band[64];
+  __shared__ float bias_s[64];
+  // dS of the tile by diagonal, row e = qq - col + 31 (distance dbase + e), column col (key),
+  // written into the Q tile's space once the last MFMA that reads Q has its operands
+  float* diag = (float*)qt;
   const int lane = threadIdx.x;
   const int col = lane & 31, hf = lane >> 5;
   const int j0 = blockIdx.x * kRows;
@@ -109,7 +122,6 @@ __global__ __launch_bounds__(64) void bwd_dkdv_kernel(BackwardParams p) {
   const uint16_t* vg = (const uint16_t*)p.v + ((size_t)b * Lk + j0) * kv_row + (size_t)hk * kHeadDim;
   load_tile(kt, kg, kv_row, min(kRows, Lk - j0), lane);
   load_tile(vt, vg, kv_row, min(kRows, Lk - j0), lane);
-  band[lane] = 0.f;
   const float* bias_h = p.bias + (size_t)h * p.R;
   float* dbias_h = p.dbias + (size_t)h * p.R;
   f32x16_t dk[4], dv[4];
@@ -119,8 +131,10 @@ __global__ __launch_bounds__(64) void bwd_dkdv_kernel(BackwardParams p) {
   for (int qi = q_lo / kRows; q_lo <= q_hi && qi <= q_hi / kRows; ++qi) {
     const int q0 = qi * kRows;
     const int nq = min(kRows, Lq - q0);
-    __syncthreads();  // the previous tile's reads of qt, gt, lse_s, d_s and the band are done
+    __syncthreads();  // the previous tile's reads of qt, gt, lse_s, d_s, bias_s and diag are done
     const size_t row0 = ((size_t)b * Lq + q0) * p.Hq + h;
+    const int dbase = off + q0 - j0 - (kRows - 1);
+    stage_bias(bias_s, bias_h, dbase, p.R, lane);
     load_tile(qt, (const uint16_t*)p.q + row0 * kHeadDim, q_row, nq, lane);
     load_tile(gt, (const uint16_t*)p.dout + row0 * kHeadDim, q_row, nq, lane);
     if (lane < kRows) {
@@ -142,11 +156,9 @@ __global__ __launch_bounds__(64) void bwd_dkdv_kernel(BackwardParams p) {
       const int qq = 8 * (r >> 2) + 4 * hf + (r & 3);
       const int dist = off + q0 + qq - j;
       const bool vis = qq < nq && dist >= 0 && dist < Weff;
-      const float bv = vis ? bias_h[min(dist, p.R - 1)] : 0.f;
-      const float lg = fmaf(s[r], p.scale_log2, fmaf(bv, kLog2e, -lse_s[qq]));
+      const float lg = fmaf(s[r], p.scale_log2, fmaf(bias_s[qq - col + 31], kLog2e, -lse_s[qq]));
       pr[r] = vis ? fast_exp2(lg) : 0.f;
       ds[r] = pr[r] * (dp[r] - d_s[qq]);
-      if (vis) atomicAdd(&band[qq - col + 31], ds[r]);
     }
     // dV += P^T dO and dK += dS^T Q: rows are keys (the lane's P and dS), columns dims
 #pragma unroll
@@ -159,13 +171,25 @@ __global__ __launch_bounds__(64) void bwd_dkdv_kernel(BackwardParams p) {
         dk[db] = mfma_32x32x16(as, load_vt_operand(qt, kStride, 16 * qs, 32 * db, lane), dk[db]);
       }
     }
+    __syncthreads();  // every read of the Q tile is done: it becomes the diagonal table
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int qq = 8 * (r >> 2) + 4 * hf + (r & 3);
+      diag[(qq - col + 31) * kDiagStride + col] = ds[r];
+    }
     __syncthreads();
-    // band entry e holds the pairs at distance off + q0 - j0 + e - 31 (only visible ones, so
-    // a non-zero entry has a distance >= 0)
+    // row e holds the pairs at distance dbase + e in columns 31 - e .. 62 - e (the other
+    // cells hold Q data and are skipped; invisible pairs hold zero, so a non-zero sum has a
+    // distance >= 0)
     if (lane < 63) {
-      const float x = band[lane];
-      band[lane] = 0.f;
-      if (x != 0.f) unsafeAtomicAdd(dbias_h + min(off + q0 - j0 + lane - 31, p.R - 1), x);
+      float x = 0.f;
+#pragma unroll
+      for (int c = 0; c < kRows; c += 2) {
+        const f32x2_t y = *(const f32x2_t*)(diag + lane * kDiagStride + c);
+        const int qq0 = lane - 31 + c;  // query of column c
+        x += ((unsigned)qq0 < (unsigned)kRows ? y[0] : 0.f) + ((unsigned)(qq0 + 1) < (unsigned)kRows ? y[1] : 0.f);
+      }
+      if (x != 0.f) unsafeAtomicAdd(dbias_h + min(dbase + lane, p.R - 1), x);
     }
   }
   // accumulator register 4 i + c of block db: key 8 i + 4 hf + c, dim 32 db + col
@@ -186,10 +210,9 @@ __global__ __launch_bounds__(64) void bwd_dkdv_kernel(BackwardParams p) {
 
 // Query-stationary pass: dQ.  Grid (query tiles, Hq, B), one wave each.
 __global__ __launch_bounds__(64) void bwd_dq_kernel(BackwardParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t qt[kTileElems];
-  __shared__ __attribute__((aligned(16))) uint16_t gt[kTileElems];  // dO
   __shared__ __attribute__((aligned(16))) uint16_t kt[kTileElems];
   __shared__ __attribute__((aligned(16))) uint16_t vt[kTileElems];
+  __shared__ float bias_s[64];
   const int lane = threadIdx.x;
   const int col = lane & 31, hf = lane >> 5;
   const int q0 = blockIdx.x * kRows;
@@ -201,10 +224,19 @@ __global__ __launch_bounds__(64) void bwd_dq_kernel(BackwardParams p) {
   const size_t kv_row = (size_t)p.Hkv * kHeadDim;
   const size_t q_row = (size_t)p.Hq * kHeadDim;
   const size_t row0 = ((size_t)b * Lq + q0) * p.Hq + h;
-  load_tile(qt, (const uint16_t*)p.q + row0 * kHeadDim, q_row, nq, lane);
-  load_tile(gt, (const uint16_t*)p.dout + row0 * kHeadDim, q_row, nq, lane);
   // this lane's query (accumulator column of S^T and dP^T)
   const bool qvalid = col < nq;
+  // Q^T and dO^T operands (lane: its query, dims 16 ks + 8 hf ..), resident for the key loop
+  u32x4_t qr[8], gr[8];
+  {
+    const uint16_t* qs = (const uint16_t*)p.q + (row0 + (size_t)(qvalid ? col : 0) * p.Hq) * kHeadDim + 8 * hf;
+    const uint16_t* gs = (const uint16_t*)p.dout + (row0 + (size_t)(qvalid ? col : 0) * p.Hq) * kHeadDim + 8 * hf;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      qr[ks] = qvalid ? *(const u32x4_t*)(qs + 16 * ks) : zero_u32x4();
+      gr[ks] = qvalid ? *(const u32x4_t*)(gs + 16 * ks) : zero_u32x4();
+    }
+  }
   const int pq = off + q0 + col;
   const float lse2 = qvalid ? p.lse[row0 + (size_t)col * p.Hq] * kLog2e : 0.f;
   const float dd = qvalid ? p.D[row0 + (size_t)col * p.Hq] : 0.f;
@@ -219,25 +251,26 @@ __global__ __launch_bounds__(64) void bwd_dq_kernel(BackwardParams p) {
   for (int db = 0; db < 4; ++db) dq[db] = zero_f32x16();
   for (int kti = j_lo / kRows; j_lo <= j_hi && kti <= j_hi / kRows; ++kti) {
     const int j0 = kti * kRows;
-    __syncthreads();  // the previous tile's reads of kt and vt are done
+    __syncthreads();  // the previous tile's reads of kt, vt and bias_s are done
     load_tile(kt, kg + (size_t)j0 * kv_row, kv_row, min(kRows, Lk - j0), lane);
     load_tile(vt, vg + (size_t)j0 * kv_row, kv_row, min(kRows, Lk - j0), lane);
+    stage_bias(bias_s, bias_h, off + q0 - j0 - (kRows - 1), p.R, lane);
     __syncthreads();
     // S^T = K Q^T and dP^T = V dO^T: rows are keys, the lane's column is its query
     f32x16_t st = zero_f32x16(), dpt = zero_f32x16();
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      st = mfma_32x32x16(row_operand(kt, ks, lane), row_operand(qt, ks, lane), st);
-      dpt = mfma_32x32x16(row_operand(vt, ks, lane), row_operand(gt, ks, lane), dpt);
+      st = mfma_32x32x16(row_operand(kt, ks, lane), qr[ks], st);
+      dpt = mfma_32x32x16(row_operand(vt, ks, lane), gr[ks], dpt);
     }
     // register r holds key j0 + 8 (r >> 2) + 4 hf + (r & 3)
     float ds[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int dist = pq - (j0 + 8 * (r >> 2) + 4 * hf + (r & 3));
+      const int jj = 8 * (r >> 2) + 4 * hf + (r & 3);
+      const int dist = pq - (j0 + jj);
       const bool vis = qvalid && dist >= 0 && dist < Weff;
-      const float bv = vis ? bias_h[min(dist, p.R - 1)] : 0.f;
-      const float lg = fmaf(st[r], p.scale_log2, fmaf(bv, kLog2e, -lse2));
+      const float lg = fmaf(st[r], p.scale_log2, fmaf(bias_s[col - jj + 31], kLog2e, -lse2));
       const float pr = vis ? fast_exp2(lg) : 0.f;
       ds[r] = pr * (dpt[r] - dd);
     }
