@@ -38,7 +38,7 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 HEADLINE = "swa_prefill_8k"
 ALL_WORKLOADS = ["tiny_prefill_fp32", "swa_prefill_8k", "chunked_prefill_32k", "paged_decode_b64", "mtp_verify_1m",
-                 "paged_prefill_b4", "kv_sconv_32k"]
+                 "paged_prefill_b4", "kv_sconv_32k", "swa_prefill_8k_bwd"]
 HEAD_DIM = 128
 KERNEL_SOURCES = {
     "prefill": ["relative_bias_gqa_amd/csrc/prefill.hip", "relative_bias_gqa_amd/csrc/prefill_bf16.hip",
@@ -47,6 +47,8 @@ KERNEL_SOURCES = {
                "relative_bias_gqa_amd/csrc/launch.hpp"],
     "sconv": ["relative_bias_gqa_amd/csrc/sconv.hip", "relative_bias_gqa_amd/csrc/device_common.hpp",
               "relative_bias_gqa_amd/csrc/launch.hpp"],
+    "backward": ["relative_bias_gqa_amd/csrc/backward.hip", "relative_bias_gqa_amd/csrc/device_common.hpp",
+                 "relative_bias_gqa_amd/csrc/launch.hpp"],
 }
 
 
@@ -273,8 +275,53 @@ class SconvRun:
         del self.kn, self.vn, self.wk, self.wv, self.kc, self.vc, self.ks, self.vs, self.bt, self.ctx, self.cu
 
 
+class BackwardRun:
+    """Gradients of a bf16 prefill (dq, dk, dv, dr) for a given output gradient; the forward's
+    out and lse are computed once, outside the timed region."""
+    kind = "backward"
+
+    def __init__(self, name, torch, rb, synth, dev):
+        self.name = name
+        bc = synth.WORKLOAD_FNS[name]()
+        c = bc.fwd
+        self.case = c
+        self.q, self.k, self.v, self.bias, self.dout = dev(c.q), dev(c.k), dev(c.v), dev(c.bias), dev(bc.dout)
+        self.out, self.lse = rb.prefill(self.q, self.k, self.v, self.bias, c.window)
+        f32 = torch.float32
+        self.dq = torch.empty(self.q.shape, dtype=f32, device=self.q.device)
+        self.dk = torch.empty(self.k.shape, dtype=f32, device=self.q.device)
+        self.dv = torch.empty(self.v.shape, dtype=f32, device=self.q.device)
+        self.dbias = torch.empty(self.bias.shape, dtype=f32, device=self.q.device)
+        self.ws = torch.empty(rb.rattn_prefill_backward_workspace_bytes(c.B, c.Lq, c.Hq), dtype=torch.uint8,
+                              device=self.q.device)
+        self.rb = rb
+        # five products per visible (query, key) pair and head: QK^T again, dO V^T, P^T dO,
+        # dS^T Q, dS K (2 flop per multiply-add over the 128 dims)
+        self.work = prefill_flops(c.B, c.Lq, c.Lk, c.Hq, c.window) * 5 // 2
+        self.unit, self.peak, self.bound = "TFLOP/s", PEAK_BF16_TFLOPS, "mfma"
+        self.config = {"workload": name, "batch": c.B, "q_len": c.Lq, "kv_len": c.Lk, "q_heads": c.Hq,
+                       "kv_heads": c.Hkv, "head_dim": HEAD_DIM, "window": c.window, "bias_len": c.R,
+                       "dtype": "bf16", "grads": "fp32"}
+        self.dtype = "bf16"
+
+    def step(self, stream):
+        self.rb.rattn_prefill_backward(self.q, self.k, self.v, self.bias, self.out, self.dout, self.lse, self.dq,
+                                       self.dk, self.dv, self.dbias, self.case.window, self.ws, stream)
+
+    def rate(self, seconds):
+        return self.work / seconds / 1e12
+
+    def finite(self):
+        import torch
+        return all(bool(torch.isfinite(t).all()) for t in (self.dq, self.dk, self.dv, self.dbias))
+
+    def free(self):
+        del self.q, self.k, self.v, self.bias, self.dout, self.out, self.lse, self.dq, self.dk, self.dv
+        del self.dbias, self.ws
+
+
 RUN_CLASSES = {"paged_decode_b64": DecodeRun, "mtp_verify_1m": DecodeRun, "paged_prefill_b4": PagedPrefillRun,
-               "kv_sconv_32k": SconvRun}
+               "kv_sconv_32k": SconvRun, "swa_prefill_8k_bwd": BackwardRun}
 
 
 def settle_clock(run, torch, stream, ms: float) -> int:

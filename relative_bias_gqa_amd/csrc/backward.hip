@@ -12,17 +12,19 @@
 //
 // Three passes on the caller's stream, after a fill that zeroes dk, dv and dr:
 //   1. D per query row (fp32, from the bf16 out and dout);
-//   2. key-stationary: one wave per (32 keys, query head) walks the query tiles that see its
-//      keys; S = Q K^T and dP = dO V^T come out with one key per lane (the accumulator
-//      column), which is the register layout the A operand of dV += P^T dO and
-//      dK += dS^T Q needs, so P and dS feed the MFMAs straight from registers; dO and Q are
-//      read transposed from LDS for the B operand.  dK and dV of the wave's head are added
-//      into dk, dv at the end (fp32 atomics, one add per element per query head); dS is
-//      summed per distance in LDS (a 63-entry band per query tile) and the band added into
-//      dr;
-//   3. query-stationary: one wave per (32 queries, query head) walks the key tiles its
-//      queries see; S^T and dP^T come out with one query per lane, the B-operand layout of
-//      dQ^T += K^T dS^T, so dQ is accumulated in registers and stored once.
+//   2. key-stationary: one wave per (32 keys, query head), two heads of a KV head per
+//      workgroup sharing the K/V tiles, walks the query tiles that see its keys; S = Q K^T
+//      and dP = dO V^T come out with one key per lane (the accumulator column), which is
+//      the register layout the A operand of dV += P^T dO and dK += dS^T Q needs, so P and
+//      dS feed the MFMAs straight from registers; dO and Q are read transposed from LDS for
+//      the B operand.  dK and dV of the wave's head are added into dk, dv at the end (fp32
+//      atomics, one add per element per query head); dS is summed per distance through a
+//      skewed table in LDS (one row per diagonal of the 32 x 32 tile) and the 63 row sums
+//      added into dr;
+//   3. query-stationary: one wave per (32 queries, query head), paired the same way, walks
+//      the key tiles its queries see; S^T and dP^T come out with one query per lane, the
+//      B-operand layout of dQ^T += K^T dS^T, so dQ is accumulated in registers and stored
+//      once.
 // All products are v_mfma_f32_32x32x16_bf16 with fp32 accumulation; P and dS are rounded to
 // bf16 as MFMA operands.  Tiles sit in LDS with 272-byte rows (256 bytes of data and 16 of
 // padding) so that the row-wise operand reads of 32 consecutive rows spread over the banks.
@@ -94,23 +96,36 @@ __global__ __launch_bounds__(256) void bwd_rowdot_kernel(const uint16_t* out, co
   D[row] = acc;
 }
 
-// Key-stationary pass: dK, dV and dr.  Grid (key tiles, Hq, B), one wave each.
-__global__ __launch_bounds__(64) void bwd_dkdv_kernel(BackwardParams p) {
+// Key-stationary pass: dK, dV and dr.  Grid (key tiles, Hkv * ceil(G / 2), B); a workgroup is
+// two waves, each one query head of the same KV head, sharing the K and V tiles.  With an odd
+// G the second wave of the last pair has no head: it runs along (for the barriers) and
+// writes nothing.
+__global__ __launch_bounds__(2 * 64) void bwd_dkdv_kernel(BackwardParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t kt[kTileElems];
   __shared__ __attribute__((aligned(16))) uint16_t vt[kTileElems];
-  __shared__ __attribute__((aligned(16))) uint16_t qt[kTileElems];
-  __shared__ __attribute__((aligned(16))) uint16_t gt[kTileElems];  // dO
-  __shared__ float lse_s[kRows];
-  __shared__ float d_s[kRows];
-  __shared__ float bias_s[64];
+  __shared__ __attribute__((aligned(16))) uint16_t qt_w[2][kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t gt_w[2][kTileElems];  // dO
+  __shared__ float lse_w[2][kRows];
+  __shared__ float d_w[2][kRows];
+  __shared__ float bias_w[2][64];
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  uint16_t* qt = qt_w[wave];
+  uint16_t* gt = gt_w[wave];
+  float* lse_s = lse_w[wave];
+  float* d_s = d_w[wave];
+  float* bias_s = bias_w[wave];
   // dS of the tile by diagonal, row e = qq - col + 31 (distance dbase + e), column col (key),
-  // written into the Q tile's space once the last MFMA that reads Q has its operands
+  // written into this wave's Q tile space once the last MFMA that reads Q has its operands
   float* diag = (float*)qt;
-  const int lane = threadIdx.x;
   const int col = lane & 31, hf = lane >> 5;
   const int j0 = blockIdx.x * kRows;
-  const int h = blockIdx.y, b = blockIdx.z;
-  const int hk = h / p.G;
+  const int npair = (p.G + 1) / 2;
+  const int hk = blockIdx.y / npair;
+  const int hg = 2 * (blockIdx.y % npair) + wave;
+  const bool has_head = hg < p.G;
+  const int h = hk * p.G + (has_head ? hg : hg - 1);
+  const int b = blockIdx.z;
   const int Lq = p.Lq, Lk = p.Lk, off = Lk - Lq;
   const int Weff = p.window > 0 ? p.window : 0x40000000;
   // queries that see a key of this tile: positions j0 .. j0 + 31 + Weff - 1
@@ -120,8 +135,7 @@ __global__ __launch_bounds__(64) void bwd_dkdv_kernel(BackwardParams p) {
   const size_t q_row = (size_t)p.Hq * kHeadDim;
   const uint16_t* kg = (const uint16_t*)p.k + ((size_t)b * Lk + j0) * kv_row + (size_t)hk * kHeadDim;
   const uint16_t* vg = (const uint16_t*)p.v + ((size_t)b * Lk + j0) * kv_row + (size_t)hk * kHeadDim;
-  load_tile(kt, kg, kv_row, min(kRows, Lk - j0), lane);
-  load_tile(vt, vg, kv_row, min(kRows, Lk - j0), lane);
+  load_tile(wave == 0 ? kt : vt, wave == 0 ? kg : vg, kv_row, min(kRows, Lk - j0), lane);
   const float* bias_h = p.bias + (size_t)h * p.R;
   float* dbias_h = p.dbias + (size_t)h * p.R;
   f32x16_t dk[4], dv[4];
@@ -189,9 +203,10 @@ __global__ __launch_bounds__(64) void bwd_dkdv_kernel(BackwardParams p) {
         const int qq0 = lane - 31 + c;  // query of column c
         x += ((unsigned)qq0 < (unsigned)kRows ? y[0] : 0.f) + ((unsigned)(qq0 + 1) < (unsigned)kRows ? y[1] : 0.f);
       }
-      if (x != 0.f) unsafeAtomicAdd(dbias_h + min(dbase + lane, p.R - 1), x);
+      if (has_head && x != 0.f) unsafeAtomicAdd(dbias_h + min(dbase + lane, p.R - 1), x);
     }
   }
+  if (!has_head) return;
   // accumulator register 4 i + c of block db: key 8 i + 4 hf + c, dim 32 db + col
   float* dkg = p.dk + ((size_t)b * Lk + j0) * kv_row + (size_t)hk * kHeadDim;
   float* dvg = p.dv + ((size_t)b * Lk + j0) * kv_row + (size_t)hk * kHeadDim;
@@ -208,16 +223,24 @@ __global__ __launch_bounds__(64) void bwd_dkdv_kernel(BackwardParams p) {
     }
 }
 
-// Query-stationary pass: dQ.  Grid (query tiles, Hq, B), one wave each.
-__global__ __launch_bounds__(64) void bwd_dq_kernel(BackwardParams p) {
+// Query-stationary pass: dQ.  Grid (query tiles, Hkv * ceil(G / 2), B); a workgroup is two
+// waves, each one query head of the same KV head, sharing the K and V tiles (wave 0 loads
+// K, wave 1 V).  With an odd G the second wave of the last pair runs along and stores nothing.
+__global__ __launch_bounds__(2 * 64) void bwd_dq_kernel(BackwardParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t kt[kTileElems];
   __shared__ __attribute__((aligned(16))) uint16_t vt[kTileElems];
-  __shared__ float bias_s[64];
-  const int lane = threadIdx.x;
+  __shared__ float bias_w[2][64];
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  float* bias_s = bias_w[wave];
   const int col = lane & 31, hf = lane >> 5;
   const int q0 = blockIdx.x * kRows;
-  const int h = blockIdx.y, b = blockIdx.z;
-  const int hk = h / p.G;
+  const int npair = (p.G + 1) / 2;
+  const int hk = blockIdx.y / npair;
+  const int hg = 2 * (blockIdx.y % npair) + wave;
+  const bool has_head = hg < p.G;
+  const int h = hk * p.G + (has_head ? hg : hg - 1);
+  const int b = blockIdx.z;
   const int Lq = p.Lq, Lk = p.Lk, off = Lk - Lq;
   const int nq = min(kRows, Lq - q0);
   const int Weff = p.window > 0 ? p.window : 0x40000000;
@@ -252,8 +275,7 @@ __global__ __launch_bounds__(64) void bwd_dq_kernel(BackwardParams p) {
   for (int kti = j_lo / kRows; j_lo <= j_hi && kti <= j_hi / kRows; ++kti) {
     const int j0 = kti * kRows;
     __syncthreads();  // the previous tile's reads of kt, vt and bias_s are done
-    load_tile(kt, kg + (size_t)j0 * kv_row, kv_row, min(kRows, Lk - j0), lane);
-    load_tile(vt, vg + (size_t)j0 * kv_row, kv_row, min(kRows, Lk - j0), lane);
+    load_tile(wave == 0 ? kt : vt, (wave == 0 ? kg : vg) + (size_t)j0 * kv_row, kv_row, min(kRows, Lk - j0), lane);
     stage_bias(bias_s, bias_h, off + q0 - j0 - (kRows - 1), p.R, lane);
     __syncthreads();
     // S^T = K Q^T and dP^T = V dO^T: rows are keys, the lane's column is its query
@@ -283,7 +305,7 @@ __global__ __launch_bounds__(64) void bwd_dq_kernel(BackwardParams p) {
         dq[db] = mfma_32x32x16(load_vt_operand(kt, kStride, 16 * ks, 32 * db, lane), bs, dq[db]);
     }
   }
-  if (!qvalid) return;
+  if (!qvalid || !has_head) return;
   // accumulator register 4 i + c of block db: dim 32 db + 8 i + 4 hf + c of query q0 + col
   float* dqg = p.dq + (row0 + (size_t)col * p.Hq) * kHeadDim;
 #pragma unroll
@@ -314,10 +336,11 @@ hipError_t launch_backward(const BackwardParams& p, hipStream_t stream) {
   const size_t rows = (size_t)p.B * p.Lq * p.Hq;
   hipLaunchKernelGGL(bwd_rowdot_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream,
                      (const uint16_t*)p.out, (const uint16_t*)p.dout, p.D, rows);
-  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)((p.Lk + kRows - 1) / kRows), (unsigned)p.Hq, (unsigned)p.B),
-                     dim3(64), 0, stream, p);
-  hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)((p.Lq + kRows - 1) / kRows), (unsigned)p.Hq, (unsigned)p.B),
-                     dim3(64), 0, stream, p);
+  const unsigned pairs = (unsigned)(p.Hkv * ((p.G + 1) / 2));
+  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)((p.Lk + kRows - 1) / kRows), pairs, (unsigned)p.B), dim3(128),
+                     0, stream, p);
+  hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)((p.Lq + kRows - 1) / kRows), pairs, (unsigned)p.B), dim3(128), 0,
+                     stream, p);
   return hipGetLastError();
 }
 

@@ -296,6 +296,8 @@ WORKLOADS = {
                         "16/2 heads, bf16, full causal, R=8192",
     "kv_sconv_32k": "batch 4, 8192 new tokens each after prefixes of 0/8192/16384/24576 tokens, 2 KV heads, "
                     "bf16, window-4 short convolution into paged caches",
+    "swa_prefill_8k_bwd": "backward of swa_prefill_8k (batch 1, L=8192, 16/2 heads, window 4096, R=4096): dq, dk, dv, "
+                          "dr for a N(0,1) output gradient",
 }
 
 
@@ -332,6 +334,10 @@ def kv_sconv_32k(seed: int = 0) -> SconvCase:
     return make_sconv(seed, [8192, 16384, 24576, 32768], [8192] * 4, 2, "kv_sconv_32k")
 
 
+def swa_prefill_8k_bwd(seed: int = 0) -> BackwardCase:
+    return make_backward(seed, 1, 8192, 8192, 16, 2, 4096, 4096, "swa_prefill_8k_bwd")
+
+
 WORKLOAD_FNS = {
     "tiny_prefill_fp32": tiny_prefill_fp32,
     "swa_prefill_8k": swa_prefill_8k,
@@ -340,4 +346,5 @@ WORKLOAD_FNS = {
     "mtp_verify_1m": mtp_verify_1m,
     "paged_prefill_b4": paged_prefill_b4,
     "kv_sconv_32k": kv_sconv_32k,
+    "swa_prefill_8k_bwd": swa_prefill_8k_bwd,
 }

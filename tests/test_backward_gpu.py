@@ -9,7 +9,8 @@ each move a term by at most 2^-9 of its size):
   + 1e-6 per pair behind the entry;
   a reference that is exactly zero: max |gpu| <= 1e-4 (fp32 rounding of dP - D).
 Cases: ragged lengths (tails of 12 and 20 rows), a chunk after a prefix (Lq < Lk), a window
-with one KV head, one query head per KV head with window 1 (closed form: dq = dk = dbias = 0).
+with one KV head, one query head per KV head with window 1 (closed form: dq = dk = dbias = 0),
+three query heads per KV head (the kernels pair heads; the odd one out runs alone).
 """
 import numpy as np
 import pytest
@@ -29,6 +30,7 @@ CASES = [
     ("chunk_after_prefix", 82, 1, 200, 660, 16, 2, 1000, 0),
     ("window_one_kv_head", 83, 2, 500, 500, 8, 1, 64, 129),
     ("window_one", 84, 1, 100, 130, 4, 4, 9, 1),
+    ("three_heads_per_kv_head", 85, 1, 77, 333, 6, 2, 50, 100),
 ]
 
 
