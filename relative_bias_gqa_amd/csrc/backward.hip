@@ -72,6 +72,25 @@ __device__ __forceinline__ u32x4_t row_operand(const uint16_t* tile, int ks, int
   return *(const u32x4_t*)(tile + (lane & 31) * kStride + 16 * ks + 8 * (lane >> 5));
 }
 
+// Work item of this workgroup.  Workgroup i of a launch runs on XCD i mod 8 (each XCD has its
+// own L2), so consecutive work items (neighbouring tiles of one head pair, which read mostly
+// the same Q / dO or K / V tiles at the same time) are given to one XCD: XCD x takes a
+// contiguous range of the items, in launch order.  A bijection for any grid size.
+struct WorkItem {
+  int tile, pair, b;
+};
+__device__ __forceinline__ WorkItem xcd_work_item() {
+  const int n = gridDim.x * gridDim.y * gridDim.z;
+  const int L = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  const int per = n / 8, rem = n % 8, x = L % 8;
+  const int w = (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + L / 8;
+  WorkItem it;
+  it.tile = w % gridDim.x;
+  it.pair = (w / gridDim.x) % gridDim.y;
+  it.b = w / (gridDim.x * gridDim.y);
+  return it;
+}
+
 __global__ __launch_bounds__(256) void bwd_fill_zero_kernel(float* a, size_t n) {
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) a[i] = 0.f;
 }
@@ -119,13 +138,14 @@ __global__ __launch_bounds__(2 * 64) void bwd_dkdv_kernel(BackwardParams p) {
   // written into this wave's Q tile space once the last MFMA that reads Q has its operands
   float* diag = (float*)qt;
   const int col = lane & 31, hf = lane >> 5;
-  const int j0 = blockIdx.x * kRows;
+  const WorkItem it = xcd_work_item();
+  const int j0 = it.tile * kRows;
   const int npair = (p.G + 1) / 2;
-  const int hk = blockIdx.y / npair;
-  const int hg = 2 * (blockIdx.y % npair) + wave;
+  const int hk = it.pair / npair;
+  const int hg = 2 * (it.pair % npair) + wave;
   const bool has_head = hg < p.G;
   const int h = hk * p.G + (has_head ? hg : hg - 1);
-  const int b = blockIdx.z;
+  const int b = it.b;
   const int Lq = p.Lq, Lk = p.Lk, off = Lk - Lq;
   const int Weff = p.window > 0 ? p.window : 0x40000000;
   // queries that see a key of this tile: positions j0 .. j0 + 31 + Weff - 1
@@ -234,13 +254,14 @@ __global__ __launch_bounds__(2 * 64) void bwd_dq_kernel(BackwardParams p) {
   const int lane = threadIdx.x & 63;
   float* bias_s = bias_w[wave];
   const int col = lane & 31, hf = lane >> 5;
-  const int q0 = blockIdx.x * kRows;
+  const WorkItem it = xcd_work_item();
+  const int q0 = it.tile * kRows;
   const int npair = (p.G + 1) / 2;
-  const int hk = blockIdx.y / npair;
-  const int hg = 2 * (blockIdx.y % npair) + wave;
+  const int hk = it.pair / npair;
+  const int hg = 2 * (it.pair % npair) + wave;
   const bool has_head = hg < p.G;
   const int h = hk * p.G + (has_head ? hg : hg - 1);
-  const int b = blockIdx.z;
+  const int b = it.b;
   const int Lq = p.Lq, Lk = p.Lk, off = Lk - Lq;
   const int nq = min(kRows, Lq - q0);
   const int Weff = p.window > 0 ? p.window : 0x40000000;
