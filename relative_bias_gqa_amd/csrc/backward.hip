@@ -90,6 +90,14 @@ __device__ __forceinline__ WorkItem xcd_work_item() {
   it.b = w / (gridDim.x * gridDim.y);
   return it;
 }
+// The work item in launch order (consecutive tiles on consecutive XCDs).
+__device__ __forceinline__ WorkItem launch_order_work_item() {
+  WorkItem it;
+  it.tile = blockIdx.x;
+  it.pair = blockIdx.y;
+  it.b = blockIdx.z;
+  return it;
+}
 
 __global__ __launch_bounds__(256) void bwd_fill_zero_kernel(float* a, size_t n) {
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) a[i] = 0.f;
@@ -254,7 +262,9 @@ __global__ __launch_bounds__(2 * 64) void bwd_dq_kernel(BackwardParams p) {
   const int lane = threadIdx.x & 63;
   float* bias_s = bias_w[wave];
   const int col = lane & 31, hf = lane >> 5;
-  const WorkItem it = xcd_work_item();
+  // (the XCD-contiguous order measured 15 % slower here than launch order: every XCD then
+  // walks one head pair's tiles from light to heavy and the heaviest come last)
+  const WorkItem it = launch_order_work_item();
   const int q0 = it.tile * kRows;
   const int npair = (p.G + 1) / 2;
   const int hk = it.pair / npair;
