@@ -47,8 +47,8 @@ KERNEL_SOURCES = {
                "relative_bias_gqa_amd/csrc/launch.hpp"],
     "sconv": ["relative_bias_gqa_amd/csrc/sconv.hip", "relative_bias_gqa_amd/csrc/device_common.hpp",
               "relative_bias_gqa_amd/csrc/launch.hpp"],
-    "backward": ["relative_bias_gqa_amd/csrc/backward.hip", "relative_bias_gqa_amd/csrc/device_common.hpp",
-                 "relative_bias_gqa_amd/csrc/launch.hpp"],
+    "backward": ["relative_bias_gqa_amd/csrc/backward.hip", "relative_bias_gqa_amd/csrc/backward.hpp",
+                 "relative_bias_gqa_amd/csrc/device_common.hpp"],
 }
 
 

@@ -13,6 +13,7 @@
 #include <queue>
 #include <vector>
 
+#include "backward.hpp"
 #include "launch.hpp"
 #include "rattn.h"
 

@@ -30,8 +30,8 @@
 // padding) so that the row-wise operand reads of 32 consecutive rows spread over the banks.
 #include <algorithm>
 
+#include "backward.hpp"
 #include "device_common.hpp"
-#include "launch.hpp"
 
 namespace rattn {
 namespace {
