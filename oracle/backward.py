@@ -75,3 +75,31 @@ def prefill_backward(q, k, v, bias, dout, window: int = 0):
             dbias[h] += np.bincount(didx[vis], weights=dS[vis], minlength=R)
             dbias_abs[h] += np.bincount(didx[vis], weights=np.abs(dS[vis]), minlength=R)
     return dq, dk, dv, dbias, dbias_abs
+
+
+def prefill_backward_dq_rows(q, k, v, bias, dout, window: int, rows):
+    """dq for selected query rows [(b, t, h), ...] of a prefill, each from its own row of the
+    definition: the row's visible logits, P, dP = dO_t V^T, D = sum(P * dP), dS, dq = dS K /
+    sqrt(D).  Returns float64 [n, D].  Same inputs and reading as prefill_backward."""
+    Lq = np.asarray(q).shape[1]
+    Lk, Hkv = np.asarray(k).shape[1], np.asarray(k).shape[2]
+    Hq, R = np.asarray(q).shape[2], np.asarray(bias).shape[1]
+    G = Hq // Hkv
+    D = np.asarray(q).shape[3]
+    r = np.asarray(bias, dtype=np.float64)
+    out = []
+    for (b, t, h) in rows:
+        p = (Lk - Lq) + t
+        lo = max(0, p - window + 1) if window > 0 else 0
+        js = np.arange(lo, p + 1)
+        Kb = _f64(np.asarray(k)[b, lo:p + 1, h // G])
+        Vb = _f64(np.asarray(v)[b, lo:p + 1, h // G])
+        qi = _f64(np.asarray(q)[b, t, h])
+        gi = _f64(np.asarray(dout)[b, t, h])
+        s = Kb @ qi / np.sqrt(D) + r[h][np.minimum(p - js, R - 1)]
+        e = np.exp(s - s.max())
+        P = e / e.sum()
+        dP = Vb @ gi
+        dS = P * (dP - (P * dP).sum())
+        out.append(dS @ Kb / np.sqrt(D))
+    return np.stack(out) if out else np.zeros((0, D))

@@ -78,3 +78,39 @@ def test_backward_matches_oracle(name, seed, B, Lq, Lk, Hq, Hkv, R, window):
     bound = 1e-2 * rabs + 1e-6 * max(rabs.max(), 1e-30) + 1e-6 * npairs[None, :]
     print(f"  dbias: max err {derr.max():.2e}, worst err/bound {(derr / bound).max():.2f}", flush=True)
     assert (derr <= bound).all()
+
+
+def test_backward_full_size_sampled():
+    """The backward of the 8K-token window-4096 prefill (16/2 heads, R 4096) at full size, in the
+    launch configuration the benchmark times: 27 dq rows against the oracle row by row (same
+    bar as above), and two sums that hold at any size, bounded from the inputs alone:
+      sum_j dv[j] = sum_i sum_(h in group) dO[i, h] (every row of P sums to one): the sum of
+        8192 dv entries, each within ~2e-3 of its size (the cases above), is bounded by
+        2e-2 of the root-sum-square of the dO terms (a head left out would miss by ~90);
+      sum_d dr[h, d] = 0 (every row of dS sums to zero), a coarse check: D comes from the bf16
+        output (|out| <= max |V|), so |error| <= 2^-8 max|V| sum |dO| over the head."""
+    print("case backward full size swa_prefill_8k_bwd", flush=True)
+    from oracle.backward import prefill_backward_dq_rows
+    from oracle.sconv import bf16_to_f64
+    case = synth.swa_prefill_8k_bwd()
+    dq, dk, dv, dr = run_backward(case)
+    f = case.fwd
+    assert np.isfinite(dk).all() and np.isfinite(dv).all() and np.isfinite(dr).all()
+    rng = np.random.default_rng(5)
+    rows = [(0, int(t), int(h)) for t, h in zip(rng.integers(0, f.Lq, 24), rng.integers(0, f.Hq, 24))]
+    rows += [(0, 0, 0), (0, f.Lq - 1, f.Hq - 1), (0, f.window - 1, 7)]
+    ref = prefill_backward_dq_rows(f.q, f.k, f.v, f.bias, case.dout, f.window, rows)
+    check("dq rows", np.stack([dq[b, t, h] for (b, t, h) in rows]), ref)
+    do = bf16_to_f64(case.dout)  # [1, L, Hq, 128]
+    G = f.Hq // f.Hkv
+    grp = do.reshape(1, f.Lq, f.Hkv, G, 128)
+    expect = grp.sum(axis=(1, 3))
+    bound = 2e-2 * np.sqrt((grp ** 2).sum(axis=(1, 3))) + 1e-3
+    err = np.abs(dv.sum(axis=1) - expect)
+    print(f"  sum dv: max err {err.max():.3e}, worst err/bound {(err / bound).max():.3f}", flush=True)
+    assert (err <= bound).all()
+    vmax = np.abs(bf16_to_f64(f.v)).max()
+    rbound = 2.0 ** -8 * vmax * np.abs(do).sum(axis=(0, 1, 3)) + 1e-3
+    rerr = np.abs(dr.sum(axis=1))
+    print(f"  sum dr: max {rerr.max():.3e}, worst err/bound {(rerr / rbound).max():.3f}", flush=True)
+    assert (rerr <= rbound).all()

@@ -83,3 +83,14 @@ def test_backward_softmax_sums(window):
     a = prefill_backward(qb, k, v, r, do, window)[0]
     b = prefill_backward(oracle.sconv.bf16_to_f64(qb), k, v, r, do, window)[0]
     assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("window", [0, 4])
+def test_dq_rows_equal_full_call(window):
+    q, k, v, r, do = _case(9, 2, 10, 15, 4, 2, 6)
+    from oracle.backward import prefill_backward_dq_rows
+    dq = prefill_backward(q, k, v, r, do, window)[0]
+    rows = [(0, 0, 0), (1, 9, 3), (0, 5, 2), (1, 3, 1)]
+    got = prefill_backward_dq_rows(q, k, v, r, do, window, rows)
+    for n, (b, t, h) in enumerate(rows):
+        assert np.allclose(got[n], dq[b, t, h], rtol=1e-12, atol=1e-12)
