@@ -72,6 +72,10 @@ __device__ __forceinline__ u32x4_t row_operand(const uint16_t* tile, int ks, int
   return *(const u32x4_t*)(tile + (lane & 31) * kStride + 16 * ks + 8 * (lane >> 5));
 }
 
+// Keeps the compiler from moving memory accesses across this point.  Used between LDS
+// accesses of one wave, which the LDS performs in the wave's order.
+__device__ __forceinline__ void lds_order() { asm volatile("" ::: "memory"); }
+
 // Work item of this workgroup.  Workgroup i of a launch runs on XCD i mod 8 (each XCD has its
 // own L2), so consecutive work items (neighbouring tiles of one head pair, which read mostly
 // the same Q / dO or K / V tiles at the same time) are given to one XCD: XCD x takes a
@@ -173,7 +177,12 @@ __global__ __launch_bounds__(2 * 64) void bwd_dkdv_kernel(BackwardParams p) {
   for (int qi = q_lo / kRows; q_lo <= q_hi && qi <= q_hi / kRows; ++qi) {
     const int q0 = qi * kRows;
     const int nq = min(kRows, Lq - q0);
-    __syncthreads();  // the previous tile's reads of qt, gt, lse_s, d_s, bias_s and diag are done
+    // One barrier per query tile keeps the two waves together (and, on the first tile, makes
+    // the other wave's K or V tile visible).  Everything else in LDS here (Q, dO, lse, D, the
+    // bias band and the diagonal table) belongs to this wave alone, and the LDS serves one
+    // wave's requests in order, so between those only the compiler's order has to be kept
+    // (lds_order), e.g. the diagonal table's float stores after the Q tile's 16-bit reads.
+    __syncthreads();
     const size_t row0 = ((size_t)b * Lq + q0) * p.Hq + h;
     const int dbase = off + q0 - j0 - (kRows - 1);
     stage_bias(bias_s, bias_h, dbase, p.R, lane);
@@ -183,7 +192,7 @@ __global__ __launch_bounds__(2 * 64) void bwd_dkdv_kernel(BackwardParams p) {
       lse_s[lane] = lane < nq ? p.lse[row0 + (size_t)lane * p.Hq] * kLog2e : 0.f;
       d_s[lane] = lane < nq ? p.D[row0 + (size_t)lane * p.Hq] : 0.f;
     }
-    __syncthreads();
+    lds_order();
     // S = Q K^T and dP = dO V^T: rows are queries, the lane's column is key j
     f32x16_t s = zero_f32x16(), dp = zero_f32x16();
 #pragma unroll
@@ -213,13 +222,13 @@ __global__ __launch_bounds__(2 * 64) void bwd_dkdv_kernel(BackwardParams p) {
         dk[db] = mfma_32x32x16(as, load_vt_operand(qt, kStride, 16 * qs, 32 * db, lane), dk[db]);
       }
     }
-    __syncthreads();  // every read of the Q tile is done: it becomes the diagonal table
+    lds_order();  // the Q tile's reads above come first: it becomes the diagonal table
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int qq = 8 * (r >> 2) + 4 * hf + (r & 3);
       diag[(qq - col + 31) * kDiagStride + col] = ds[r];
     }
-    __syncthreads();
+    lds_order();
     // row e holds the pairs at distance dbase + e in columns 31 - e .. 62 - e (the other
     // cells hold Q data and are skipped; invisible pairs hold zero, so a non-zero sum has a
     // distance >= 0)
