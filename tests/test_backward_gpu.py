@@ -31,6 +31,7 @@ CASES = [
     ("window_one_kv_head", 83, 2, 500, 500, 8, 1, 64, 129),
     ("window_one", 84, 1, 100, 130, 4, 4, 9, 1),
     ("three_heads_per_kv_head", 85, 1, 77, 333, 6, 2, 50, 100),
+    ("sixteen_heads_per_kv_head", 86, 1, 150, 150, 32, 2, 40, 0),
 ]
 
 
@@ -114,3 +115,29 @@ def test_backward_full_size_sampled():
     rerr = np.abs(dr.sum(axis=1))
     print(f"  sum dr: max {rerr.max():.3e}, worst err/bound {(rerr / rbound).max():.3f}", flush=True)
     assert (rerr <= rbound).all()
+
+
+def test_backward_empty_chunk_zeroes_gradients():
+    """No queries (Lq = 0) over 300 keys: dk, dv and dbias are written as zeros (they start
+    as NaN here), dq has no elements."""
+    print("case backward empty chunk", flush=True)
+    Lk, Hq, Hkv, R = 300, 8, 2, 32
+    k = torch.randn(1, Lk, Hkv, 128, device="cuda").to(torch.bfloat16)
+    v = torch.randn(1, Lk, Hkv, 128, device="cuda").to(torch.bfloat16)
+    q = torch.empty(1, 0, Hq, 128, device="cuda", dtype=torch.bfloat16)
+    r = torch.randn(Hq, R, device="cuda")
+    lse = torch.empty(1, 0, Hq, device="cuda")
+    dq = torch.empty(1, 0, Hq, 128, device="cuda")
+    dk = torch.full((1, Lk, Hkv, 128), float("nan"), device="cuda")
+    dv = torch.full_like(dk, float("nan"))
+    dr = torch.full((Hq, R), float("nan"), device="cuda")
+    ws = torch.empty(rb.rattn_prefill_backward_workspace_bytes(1, 0, Hq), dtype=torch.uint8, device="cuda")
+    # zero-size tensors may have no storage: pass a live one-element pointer for q, out, dout, lse, dq
+    dummy = torch.zeros(1, device="cuda")
+    rc = rb.load().rattn_prefill_backward(q.data_ptr() or dummy.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                          r.data_ptr(), dummy.data_ptr(), dummy.data_ptr(), dummy.data_ptr(),
+                                          dummy.data_ptr(), dk.data_ptr(), dv.data_ptr(), dr.data_ptr(), 1, 0,
+                                          Lk, Hq, Hkv, 128, R, 0, ws.data_ptr(), ws.numel(), None)
+    torch.cuda.synchronize()
+    assert rc == rb.RATTN_OK, rb.rattn_last_error()
+    assert int((dk != 0).sum()) == 0 and int((dv != 0).sum()) == 0 and int((dr != 0).sum()) == 0
