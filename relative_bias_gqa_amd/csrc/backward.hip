@@ -18,13 +18,12 @@
 //      the register layout the A operand of dV += P^T dO and dK += dS^T Q needs, so P and
 //      dS feed the MFMAs straight from registers; dO and Q are read transposed from LDS for
 //      the B operand.  dK and dV of the wave's head are added into dk, dv at the end (fp32
-//      atomics, one add per element per query head); dS is summed per distance through a
-//      skewed table in LDS (one row per diagonal of the 32 x 32 tile) and the 63 row sums
-//      added into dr;
+//      atomics, one add per element per query head);
 //   3. query-stationary: one wave per (32 queries, query head), paired the same way, walks
 //      the key tiles its queries see; S^T and dP^T come out with one query per lane, the
 //      B-operand layout of dQ^T += K^T dS^T, so dQ is accumulated in registers and stored
-//      once.
+//      once; dS is also summed per distance through a skewed table in LDS (one row per
+//      diagonal of the 32 x 32 tile) and the 63 row sums added into dr.
 // All products are v_mfma_f32_32x32x16_bf16 with fp32 accumulation; P and dS are rounded to
 // bf16 as MFMA operands.  Tiles sit in LDS with 272-byte rows (256 bytes of data and 16 of
 // padding) so that the row-wise operand reads of 32 consecutive rows spread over the banks.
@@ -43,7 +42,6 @@ constexpr int kStride = 136;               // LDS row stride of a 128-wide bf16 
 constexpr int kTileElems = kRows * kStride;
 constexpr float kRsqrtD = 0.08838834764831845f;  // 1 / sqrt(128)
 constexpr int kDiagStride = 34;            // floats per row of the diagonal table (conflict free)
-static_assert(63 * kDiagStride * 4 <= kTileElems * 2, "the diagonal table reuses a tile's space");
 
 // The 63 bias entries a 32 x 32 tile meets: entry e = r[h, clamp(dbase + e, 0, R - 1)] for the
 // pairs at distance dbase + e, dbase = (distance of query 0 to key 31).  Lanes 0..62 load one.
@@ -127,7 +125,7 @@ __global__ __launch_bounds__(256) void bwd_rowdot_kernel(const uint16_t* out, co
   D[row] = acc;
 }
 
-// Key-stationary pass: dK, dV and dr.  Grid (key tiles, Hkv * ceil(G / 2), B); a workgroup is
+// Key-stationary pass: dK and dV.  Grid (key tiles, Hkv * ceil(G / 2), B); a workgroup is
 // two waves, each one query head of the same KV head, sharing the K and V tiles.  With an odd
 // G the second wave of the last pair has no head: it runs along (for the barriers) and
 // writes nothing.
@@ -146,9 +144,6 @@ __global__ __launch_bounds__(2 * 64) void bwd_dkdv_kernel(BackwardParams p) {
   float* lse_s = lse_w[wave];
   float* d_s = d_w[wave];
   float* bias_s = bias_w[wave];
-  // dS of the tile by diagonal, row e = qq - col + 31 (distance dbase + e), column col (key),
-  // written into this wave's Q tile space once the last MFMA that reads Q has its operands
-  float* diag = (float*)qt;
   const int col = lane & 31, hf = lane >> 5;
   const WorkItem it = xcd_work_item();
   const int j0 = it.tile * kRows;
@@ -169,7 +164,6 @@ __global__ __launch_bounds__(2 * 64) void bwd_dkdv_kernel(BackwardParams p) {
   const uint16_t* vg = (const uint16_t*)p.v + ((size_t)b * Lk + j0) * kv_row + (size_t)hk * kHeadDim;
   load_tile(wave == 0 ? kt : vt, wave == 0 ? kg : vg, kv_row, min(kRows, Lk - j0), lane);
   const float* bias_h = p.bias + (size_t)h * p.R;
-  float* dbias_h = p.dbias + (size_t)h * p.R;
   f32x16_t dk[4], dv[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) dk[db] = dv[db] = zero_f32x16();
@@ -178,10 +172,9 @@ __global__ __launch_bounds__(2 * 64) void bwd_dkdv_kernel(BackwardParams p) {
     const int q0 = qi * kRows;
     const int nq = min(kRows, Lq - q0);
     // One barrier per query tile keeps the two waves together (and, on the first tile, makes
-    // the other wave's K or V tile visible).  Everything else in LDS here (Q, dO, lse, D, the
-    // bias band and the diagonal table) belongs to this wave alone, and the LDS serves one
-    // wave's requests in order, so between those only the compiler's order has to be kept
-    // (lds_order), e.g. the diagonal table's float stores after the Q tile's 16-bit reads.
+    // the other wave's K or V tile visible).  Everything else in LDS here (Q, dO, lse, D and
+    // the bias band) belongs to this wave alone, and the LDS serves one wave's requests in
+    // order, so between those only the compiler's order has to be kept (lds_order).
     __syncthreads();
     const size_t row0 = ((size_t)b * Lq + q0) * p.Hq + h;
     const int dbase = off + q0 - j0 - (kRows - 1);
@@ -222,26 +215,6 @@ __global__ __launch_bounds__(2 * 64) void bwd_dkdv_kernel(BackwardParams p) {
         dk[db] = mfma_32x32x16(as, load_vt_operand(qt, kStride, 16 * qs, 32 * db, lane), dk[db]);
       }
     }
-    lds_order();  // the Q tile's reads above come first: it becomes the diagonal table
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int qq = 8 * (r >> 2) + 4 * hf + (r & 3);
-      diag[(qq - col + 31) * kDiagStride + col] = ds[r];
-    }
-    lds_order();
-    // row e holds the pairs at distance dbase + e in columns 31 - e .. 62 - e (the other
-    // cells hold Q data and are skipped; invisible pairs hold zero, so a non-zero sum has a
-    // distance >= 0)
-    if (lane < 63) {
-      float x = 0.f;
-#pragma unroll
-      for (int c = 0; c < kRows; c += 2) {
-        const f32x2_t y = *(const f32x2_t*)(diag + lane * kDiagStride + c);
-        const int qq0 = lane - 31 + c;  // query of column c
-        x += ((unsigned)qq0 < (unsigned)kRows ? y[0] : 0.f) + ((unsigned)(qq0 + 1) < (unsigned)kRows ? y[1] : 0.f);
-      }
-      if (has_head && x != 0.f) unsafeAtomicAdd(dbias_h + min(dbase + lane, p.R - 1), x);
-    }
   }
   if (!has_head) return;
   // accumulator register 4 i + c of block db: key 8 i + 4 hf + c, dim 32 db + col
@@ -260,16 +233,20 @@ __global__ __launch_bounds__(2 * 64) void bwd_dkdv_kernel(BackwardParams p) {
     }
 }
 
-// Query-stationary pass: dQ.  Grid (query tiles, Hkv * ceil(G / 2), B); a workgroup is two
+// Query-stationary pass: dQ and dr.  Grid (query tiles, Hkv * ceil(G / 2), B); a workgroup is two
 // waves, each one query head of the same KV head, sharing the K and V tiles (wave 0 loads
 // K, wave 1 V).  With an odd G the second wave of the last pair runs along and stores nothing.
 __global__ __launch_bounds__(2 * 64) void bwd_dq_kernel(BackwardParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t kt[kTileElems];
   __shared__ __attribute__((aligned(16))) uint16_t vt[kTileElems];
   __shared__ float bias_w[2][64];
+  // dS of the tile by diagonal: row e = col - jj + 31 (distance dbase + e), column col (the
+  // query); the cells of row e that no pair maps to (columns outside e - 31 .. e) are skipped
+  __shared__ __attribute__((aligned(16))) float diag_w[2][63 * kDiagStride];
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   float* bias_s = bias_w[wave];
+  float* diag = diag_w[wave];
   const int col = lane & 31, hf = lane >> 5;
   // (the XCD-contiguous order measured 15 % slower here than launch order: every XCD then
   // walks one head pair's tiles from light to heavy and the heaviest come last)
@@ -304,6 +281,7 @@ __global__ __launch_bounds__(2 * 64) void bwd_dq_kernel(BackwardParams p) {
   const float lse2 = qvalid ? p.lse[row0 + (size_t)col * p.Hq] * kLog2e : 0.f;
   const float dd = qvalid ? p.D[row0 + (size_t)col * p.Hq] : 0.f;
   const float* bias_h = p.bias + (size_t)h * p.R;
+  float* dbias_h = p.dbias + (size_t)h * p.R;
   // keys the tile's queries see: positions off + q0 - Weff + 1 .. off + q0 + 31
   const int j_lo = max(0, off + q0 - Weff + 1);
   const int j_hi = min(Lk - 1, off + q0 + nq - 1);
@@ -316,7 +294,8 @@ __global__ __launch_bounds__(2 * 64) void bwd_dq_kernel(BackwardParams p) {
     const int j0 = kti * kRows;
     __syncthreads();  // the previous tile's reads of kt, vt and bias_s are done
     load_tile(wave == 0 ? kt : vt, (wave == 0 ? kg : vg) + (size_t)j0 * kv_row, kv_row, min(kRows, Lk - j0), lane);
-    stage_bias(bias_s, bias_h, off + q0 - j0 - (kRows - 1), p.R, lane);
+    const int dbase = off + q0 - j0 - (kRows - 1);
+    stage_bias(bias_s, bias_h, dbase, p.R, lane);
     __syncthreads();
     // S^T = K Q^T and dP^T = V dO^T: rows are keys, the lane's column is its query
     f32x16_t st = zero_f32x16(), dpt = zero_f32x16();
@@ -335,6 +314,7 @@ __global__ __launch_bounds__(2 * 64) void bwd_dq_kernel(BackwardParams p) {
       const float lg = fmaf(st[r], p.scale_log2, fmaf(bias_s[col - jj + 31], kLog2e, -lse2));
       const float pr = vis ? fast_exp2(lg) : 0.f;
       ds[r] = pr * (dpt[r] - dd);
+      diag[(col - jj + 31) * kDiagStride + col] = ds[r];
     }
     // dQ^T += K^T dS^T: rows are dims (K read transposed), the lane's column its query
 #pragma unroll
@@ -344,6 +324,21 @@ __global__ __launch_bounds__(2 * 64) void bwd_dq_kernel(BackwardParams p) {
       for (int db = 0; db < 4; ++db)
         dq[db] = mfma_32x32x16(load_vt_operand(kt, kStride, 16 * ks, 32 * db, lane), bs, dq[db]);
     }
+    // dr: lane e < 63 sums row e of the table (the pairs at distance dbase + e; invisible pairs
+    // hold zero, so a non-zero sum has a distance >= 0).  The table is this wave's own and the
+    // LDS serves a wave's requests in order, so only the compiler's order is kept here.
+    lds_order();
+    if (lane < 63) {
+      float x = 0.f;
+#pragma unroll
+      for (int c = 0; c < kRows; c += 2) {
+        const f32x2_t y = *(const f32x2_t*)(diag + lane * kDiagStride + c);
+        const int jj0 = c - lane + 31;  // key of column c
+        x += ((unsigned)jj0 < (unsigned)kRows ? y[0] : 0.f) + ((unsigned)(jj0 + 1) < (unsigned)kRows ? y[1] : 0.f);
+      }
+      if (has_head && x != 0.f) unsafeAtomicAdd(dbias_h + min(dbase + lane, p.R - 1), x);
+    }
+    lds_order();  // the next tile's table stores come after these reads
   }
   if (!qvalid || !has_head) return;
   // accumulator register 4 i + c of block db: dim 32 db + 8 i + 4 hf + c of query q0 + col
