@@ -2,8 +2,8 @@
  * rattn.h -- relative-bias grouped-query attention for AMD Instinct MI355X (gfx950).
  *
  * The operation (vLLM recipes page "thinkingmachines/Inkling", Overview > Architectural
- * highlights > Attention): grouped-query attention with head size 128 in which RoPE is
- * replaced by a learned relative-position term added to the logits before the softmax.
+ * highlights > Attention): grouped-query attention with head size 128 without RoPE; the
+ * logits instead carry a trained bias that depends on the distance between query and key.
  * The term is a per-query-head table r indexed by the clamped distance, so for a query at
  * absolute position i and a key at position j:
  *
@@ -163,8 +163,8 @@ int rattn_prefill_paged(const void* q, const void* k_cache, const void* v_cache,
 /*
  * Short convolution of the new keys and values as they enter the paged caches (vLLM recipes
  * page "thinkingmachines/Inkling", Overview > Architectural highlights > Short convolution:
- * window-4 sconv modules on the attention keys and values; vLLM keeps their state as the KV
- * cache of a virtual sliding-window layer).  Read as the causal depthwise convolution over
+ * four-tap short convolutions over the token axis of the attention keys and values, among
+ * others, with their state kept in paged storage).  Read as the causal depthwise convolution over
  * tokens with four taps and a weight per tap and channel, no bias, no activation:
  *     y[p, c] = sum_{s=0..3} w[s, c] * x[p - s, c],   x[p] = 0 for p < 0.
  * Sequence b has n_b = cu_seqlens[b + 1] - cu_seqlens[b] new tokens at positions
@@ -202,8 +202,8 @@ size_t rattn_prefill_backward_workspace_bytes(int B, int Lq, int Hq);
 /*
  * Gradients of rattn_prefill (bf16, contiguous K/V) for an output gradient dout.
  * vLLM recipes page "thinkingmachines/Inkling", Overview > Architectural highlights >
- * Attention defines the forward pass (relative-position term on the pre-softmax logits of
- * GQA, head size 128); the same page lists training and LoRA among the model's uses.  With
+ * Attention defines the forward pass (GQA, head size 128, a distance-dependent bias on the
+ * logits); the same page lists training and LoRA among the model's uses.  With
  * s = q.k / sqrt(128) + r[h, min(p - j, R - 1)] over the visible keys (the visibility and
  * positions of rattn_prefill), P = softmax(s) recomputed from lse, D = rowsum(dout * out):
  *   dS = P * (dout V^T - D),  dq = dS K / sqrt(128),  dk = dS^T Q / sqrt(128),
@@ -236,7 +236,8 @@ int rattn_prefill_backward(const void* q, const void* k, const void* v, const fl
  * Number of split workgroups rattn_decode_paged will use for these arguments.  The
  * visible keys of the whole batch form one stream of 64-token units that is divided
  * evenly among them.  num_splits > 0 asks for exactly that many (fewer when the batch has
- * fewer units); 0 selects the default, one per compute unit of an MI355X (256).  Returns
+ * fewer units); 0 selects the default, one per compute unit of the current device (256 on
+ * an MI355X; 256 too when no device answers the query).  Returns
  * 0 for invalid sizes.  The choice changes only the summation order of the result.
  */
 int rattn_decode_num_splits(int B, int n_q, int Hq, int Hkv, int max_ctx_len, int num_splits);

@@ -4,8 +4,8 @@ TEST INFRASTRUCTURE, NOT PRODUCT CODE: only the test suite and the benchmark use
 shares nothing with the HIP library.
 
 The forward pass is the one of the vLLM recipes page "thinkingmachines/Inkling", Overview >
-Architectural highlights > Attention (a learned relative-position term added to the
-pre-softmax logits of GQA with head size 128), with the term read as r[h, min(i - j, R - 1)]:
+Architectural highlights > Attention (GQA, head size 128, no RoPE: a trained bias that
+depends on the query-key distance enters the logits before the softmax), with the term read as r[h, min(i - j, R - 1)]:
 
     s[i, j] = q_i . k_j / sqrt(D) + r[h, min(p_i - j, R - 1)]   over the visible keys j,
     P = softmax_j(s),  O = P V,

@@ -8,8 +8,8 @@
  * What it computes (the plain definition, nothing blocked, fused or reordered):
  *
  *   vLLM recipes page "thinkingmachines/Inkling", Overview > Architectural highlights >
- *   Attention: grouped-query attention with head size 128; RoPE is replaced by a learned
- *   relative-position term that is added to the logits before the softmax; 11 full
+ *   Attention: grouped-query attention with head size 128; instead of RoPE the logits
+ *   carry a trained bias that depends on the query-key distance; 11 full
  *   attention layers and 55 sliding-window layers.  The exact form of that term is fixed
  *   here as a per-query-head table r[h, d] indexed by the distance d = i - j and clamped
  *   at R-1:

@@ -2,8 +2,8 @@
  * rattn_oracle.h -- the CPU oracle's own interface (test infrastructure, not product).
  *
  * Relative-bias grouped-query attention, vLLM recipes page "thinkingmachines/Inkling",
- * Overview > Architectural highlights > Attention (a learned relative-position term added
- * to the pre-softmax logits, GQA, head size 128), with the term fixed as
+ * Overview > Architectural highlights > Attention (GQA, head size 128, a trained bias on the
+ * logits that depends on the query-key distance, in place of RoPE), with the term fixed as
  * r[h, min(i - j, R - 1)].  Computed in fp64 from the plain definition.
  */
 #ifndef RATTN_ORACLE_H

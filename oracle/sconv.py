@@ -4,9 +4,9 @@ TEST INFRASTRUCTURE, NOT PRODUCT CODE: only the test suite and the benchmark use
 shares nothing with the HIP library.
 
 What it computes (vLLM recipes page "thinkingmachines/Inkling", Overview > Architectural
-highlights > Short convolution: every layer applies window-4 sconv modules to the attention
-keys and values, and vLLM keeps the sconv state as the KV cache of a virtual sliding-window
-layer).  The pages give no formula; the reading taken is the plain causal depthwise
+highlights > Short convolution: each layer runs four-tap short convolutions over the token
+axis of, among others, the attention keys and values; their running state lives in paged
+storage that the engine handles like an attention cache).  The pages give no formula; the reading taken is the plain causal depthwise
 convolution over tokens with four taps and a weight per tap and channel, no bias, no
 activation:
 

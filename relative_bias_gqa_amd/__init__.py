@@ -8,8 +8,8 @@ kernels; there is no fallback.  If the library is missing or fails to load,
 every call raises.
 
 Operation (vLLM recipes page "thinkingmachines/Inkling", Overview >
-Architectural highlights > Attention): GQA with head size 128 and a learned
-relative-position term on the pre-softmax logits, fixed here as
+Architectural highlights > Attention): GQA with head size 128 whose logits
+carry a trained bias depending on the query-key distance, fixed here as
 ``logit[i,j] = q_i.k_j/sqrt(128) + r[h, min(i-j, R-1)]``; causal full or
 sliding-window; prefill over contiguous K/V and paged (block 128) decode with
 multi-query (MTP) verification.
@@ -231,14 +231,24 @@ def rattn_decode_paged(q, k_cache, v_cache, block_table, ctx_lens, windows, bias
 _prefill_ws = {}
 
 
-def prefill_workspace(nbytes: int, device):
-    """A zero-filled workspace of at least nbytes on `device`, kept and reused by later
-    calls (prefill calls leave it zero-filled).  Not for calls running concurrently."""
+def prefill_workspace(nbytes: int, device, stream=None):
+    """A zero-filled workspace of at least nbytes for calls on `stream` (default: the
+    current stream of `device`), kept and reused by later calls on that stream (prefill
+    calls leave it zero-filled).  One workspace per (device, stream): calls on one stream
+    run in order, so they never share it concurrently; calls on different streams get
+    different workspaces.  It is allocated on that stream, so growing it (the old one is
+    released to torch's allocator) stays ordered after the calls that used it."""
     import torch
-    key = str(torch.device(device))
+    device = torch.device(device)
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    handle = _stream(stream)
+    key = (str(device), handle)
     ws = _prefill_ws.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=device)
+        ctx = torch.cuda.stream(stream) if hasattr(stream, "cuda_stream") else torch.cuda.device(device)
+        with ctx:
+            ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=device)
         _prefill_ws[key] = ws
     return ws
 
@@ -251,7 +261,7 @@ def prefill(q, k, v, bias, window: int = 0, want_lse: bool = True, kv_splits: in
     if workspace is None:
         n = rattn_prefill_workspace_bytes(q.shape[0], q.shape[1], k.shape[1], q.shape[2], k.shape[2], window,
                                           _dtype_code(q), kv_splits)
-        workspace = prefill_workspace(n, q.device) if n > 0 else None
+        workspace = prefill_workspace(n, q.device, stream) if n > 0 else None
     rattn_prefill(q, k, v, bias, out, lse, window, kv_splits, workspace, stream)
     return out, lse
 
@@ -272,13 +282,13 @@ def prefill_backward(q, k, v, bias, out, lse, dout, window: int = 0, stream=None
 
 def prefill_paged(q, k_cache, v_cache, block_table, ctx_lens, bias, max_ctx_len: int, window: int = 0,
                   want_lse: bool = True, workspace="auto", stream=None, cu_seqlens_q=None, max_q_len: int = 0) -> Tuple:
-    """workspace "auto": the cached zero-filled prefill workspace of q's device (job queue);
-    None: one workgroup per job; else a tensor as for rattn_prefill_paged."""
+    """workspace "auto": the cached zero-filled prefill workspace of q's device and the call's
+    stream (job queue); None: one workgroup per job; else a tensor as for rattn_prefill_paged."""
     import torch
     out = torch.empty_like(q)
     lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device) if want_lse else None
     if isinstance(workspace, str):
-        workspace = prefill_workspace(PREFILL_PAGED_WORKSPACE_BYTES, q.device)
+        workspace = prefill_workspace(PREFILL_PAGED_WORKSPACE_BYTES, q.device, stream)
     rattn_prefill_paged(q, k_cache, v_cache, block_table, ctx_lens, bias, out, lse, max_ctx_len, window, workspace,
                         stream, cu_seqlens_q, max_q_len)
     return out, lse

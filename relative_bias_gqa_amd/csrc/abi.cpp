@@ -43,11 +43,25 @@ int largest_divisor_at_most(int n, int cap) {
 constexpr int kMaxPosition = (1 << 30) - 1;  // positions stay clear of the kernels' window sentinel
 constexpr float kScaleLog2 = 1.4426950408889634f * 0.08838834764831845f;  // log2(e) / sqrt(128)
 
+// compute units of the current device (queried once per device; 256, an MI355X's count,
+// when no device answers)
+int compute_units() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 // ---- paged-decode plan ---------------------------------------------------------------
 // Segment = (sequence, KV head, subgroup of gs query heads); rows = n_q * gs.  The unit
 // stream (64-token units of every segment) is divided among P workgroups; sequences are
 // processed in launches of at most `batch` sequences, each reusing the same workspace.
-constexpr int kAutoWorkgroups = 256;  // one per compute unit of an MI355X
+// The default P is one workgroup per compute unit of the current device.
 
 struct DecodePlan {
   int gs, n_hs, KH, rows, SL, P, batch, KS, NW;
@@ -80,7 +94,7 @@ bool plan_decode(int B, int n_q, int Hq, int Hkv, int max_ctx_len, int max_block
   const long long cap = 0x7fffffffLL / (max_units_per_seq * KH);
   if (cap < 1) return false;
   if (batch > cap) batch = cap;
-  const int P = num_splits > 0 ? num_splits : kAutoWorkgroups;
+  const int P = num_splits > 0 ? num_splits : compute_units();
   const long long rows = (long long)n_q * gs;
   // the two 32-key halves of a unit go to different waves, one wave per (32-row block, key
   // half): four waves up to two row blocks, eight (two per SIMD) up to four
@@ -160,8 +174,7 @@ constexpr size_t kCounterBytes = 256 * 1024;
 constexpr long long kMaxSplitJobs = kCounterBytes / sizeof(int);
 
 // With a queue, a launch has one workgroup per compute unit and each takes the next job
-// slot when it finishes one: the plan simulates that on the 256 compute units of an MI355X.
-constexpr int kDispatchUnits = 256;
+// slot when it finishes one: the plan simulates that on the compute units of the device.
 // fixed costs in key-tile times: a job's start (Q and the first tiles in flight) and
 // output; a piece's, including writing its partial and its share of the merge (measured
 // per job on sliding-window prefill on an MI355X: ~3 tile-times in the piece itself; the
@@ -171,9 +184,9 @@ constexpr double kWgOverhead = 1.5;
 constexpr double kPieceOverhead = 7.0;
 
 // finish time of the last job, jobs started in order on the least-loaded unit
-double simulate_dispatch(const std::vector<double>& jobs) {
+double simulate_dispatch(const std::vector<double>& jobs, int n_units) {
   std::priority_queue<double, std::vector<double>, std::greater<double>> units;
-  for (int i = 0; i < kDispatchUnits; ++i) units.push(0.0);
+  for (int i = 0; i < n_units; ++i) units.push(0.0);
   double end = 0.0;
   for (double j : jobs) {
     const double t = units.top() + j;
@@ -199,7 +212,7 @@ PrefillSplit split_layout(const rattn::PrefillParams& p, int n_split, int parts)
   return sp;
 }
 
-PrefillSplit plan_prefill_split_uncached(const rattn::PrefillParams& p, int dtype, int kv_splits) {
+PrefillSplit plan_prefill_split_uncached(const rattn::PrefillParams& p, int dtype, int kv_splits, int n_units) {
   if (dtype != RATTN_BF16) return PrefillSplit{};
   if (kv_splits == 1) return split_layout(p, 0, 1);
   const int nt = p.n_tok_tiles;
@@ -246,9 +259,9 @@ PrefillSplit plan_prefill_split_uncached(const rattn::PrefillParams& p, int dtyp
   };
   double total = 0.0;
   for (int t = 0; t < nt; ++t) total += (keys[t] + kWgOverhead) * per_tile;
-  double best = simulate_dispatch(jobs_of(0, 1));
+  double best = simulate_dispatch(jobs_of(0, 1), n_units);
   // a grid that already finishes within 5 % of an even spread is left alone
-  if (best <= 1.05 * total / kDispatchUnits) return split_layout(p, 0, 1);
+  if (best <= 1.05 * total / n_units) return split_layout(p, 0, 1);
   int best_split = 0, best_parts = 1;
   // candidates: the tiles with at least some number of key tiles (2 parts, and fractions
   // of the longest), and the heaviest n tiles for n a multiple of nt / 16 (the tiles of a
@@ -272,7 +285,7 @@ PrefillSplit plan_prefill_split_uncached(const rattn::PrefillParams& p, int dtyp
       n_split = std::min(n_split, max_split);
       while (n_split > 0 && keys[nt - n_split] < 2 * parts) --n_split;  // pieces of >= 2 key tiles
       if (n_split == 0) continue;
-      const double m = simulate_dispatch(jobs_of(n_split, parts));
+      const double m = simulate_dispatch(jobs_of(n_split, parts), n_units);
       const long long pieces = (long long)n_split * parts;
       if (best_split == 0 || m < 0.995 * best_m || (m <= 1.005 * best_m && pieces < best_pieces)) {
         best_m = m;
@@ -285,35 +298,23 @@ PrefillSplit plan_prefill_split_uncached(const rattn::PrefillParams& p, int dtyp
   PrefillSplit sp = split_layout(p, best_split, best_parts);
   sp.n_big = big_of(best_split, best_parts);
   return sp;
-  return split_layout(p, best_split, best_parts);
 }
 
-// compute units of the current device (queried once per device)
-int compute_units() {
-  static std::atomic<int> cached[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  int n = cached[dev].load(std::memory_order_relaxed);
-  if (n <= 0) {
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev].store(n, std::memory_order_relaxed);
-  }
-  return n;
-}
 
 // the plan of the last few shapes (calls repeat their shapes)
 PrefillSplit plan_prefill_split(const rattn::PrefillParams& p, int dtype, int kv_splits) {
   struct Entry {
-    int key[8];
+    int key[9];
     PrefillSplit plan;
   };
   thread_local Entry cache[8];
   thread_local int filled = 0, next = 0;
-  const int key[8] = {p.B, p.Lq, p.Lk, p.Hq, p.Hkv, p.window, dtype, kv_splits};
+  const int n_units = compute_units();
+  const int key[9] = {p.B, p.Lq, p.Lk, p.Hq, p.Hkv, p.window, dtype, kv_splits, n_units};
   for (int i = 0; i < filled; ++i)
-    if (std::equal(key, key + 8, cache[i].key)) return cache[i].plan;
-  const PrefillSplit sp = plan_prefill_split_uncached(p, dtype, kv_splits);
-  std::copy(key, key + 8, cache[next].key);
+    if (std::equal(key, key + 9, cache[i].key)) return cache[i].plan;
+  const PrefillSplit sp = plan_prefill_split_uncached(p, dtype, kv_splits, n_units);
+  std::copy(key, key + 9, cache[next].key);
   cache[next].plan = sp;
   next = (next + 1) % 8;
   filled = std::min(filled + 1, 8);

@@ -1,8 +1,8 @@
 // backward.hip -- gradients of the relative-bias GQA prefill (bf16 inputs), gfx950.
 //
 // The forward pass (vLLM recipes page "thinkingmachines/Inkling", Overview > Architectural
-// highlights > Attention: a learned relative-position term added to the pre-softmax logits
-// of GQA with head size 128; the page also lists training and LoRA among the model's uses)
+// highlights > Attention: GQA with head size 128, a trained distance-dependent bias on the
+// logits in place of RoPE; the page also lists training and LoRA among the model's uses)
 // is s = q.k / sqrt(128) + r[h, min(p - j, R - 1)] over the visible keys, P = softmax(s),
 // O = P V.  Its gradients for an output gradient dO, with D = rowsum(dO * O):
 //   dS = P * (dO V^T - D),  dQ = dS K / sqrt(128),  dK = dS^T Q / sqrt(128),  dV = P^T dO,
@@ -202,7 +202,8 @@ __global__ __launch_bounds__(2 * 64) void bwd_dkdv_kernel(BackwardParams p) {
       const bool vis = qq < nq && dist >= 0 && dist < Weff;
       const float lg = fmaf(s[r], p.scale_log2, fmaf(bias_s[qq - col + 31], kLog2e, -lse_s[qq]));
       pr[r] = vis ? fast_exp2(lg) : 0.f;
-      ds[r] = pr[r] * (dp[r] - d_s[qq]);
+      // select, not multiply: an invisible pair stays zero even if dP - D is not finite
+      ds[r] = vis ? pr[r] * (dp[r] - d_s[qq]) : 0.f;
     }
     // dV += P^T dO and dK += dS^T Q: rows are keys (the lane's P and dS), columns dims
 #pragma unroll
@@ -313,7 +314,7 @@ __global__ __launch_bounds__(2 * 64) void bwd_dq_kernel(BackwardParams p) {
       const bool vis = qvalid && dist >= 0 && dist < Weff;
       const float lg = fmaf(st[r], p.scale_log2, fmaf(bias_s[col - jj + 31], kLog2e, -lse2));
       const float pr = vis ? fast_exp2(lg) : 0.f;
-      ds[r] = pr * (dpt[r] - dd);
+      ds[r] = vis ? pr * (dpt[r] - dd) : 0.f;
       diag[(col - jj + 31) * kDiagStride + col] = ds[r];
     }
     // dQ^T += K^T dS^T: rows are dims (K read transposed), the lane's column its query
@@ -325,7 +326,7 @@ __global__ __launch_bounds__(2 * 64) void bwd_dq_kernel(BackwardParams p) {
         dq[db] = mfma_32x32x16(load_vt_operand(kt, kStride, 16 * ks, 32 * db, lane), bs, dq[db]);
     }
     // dr: lane e < 63 sums row e of the table (the pairs at distance dbase + e; invisible pairs
-    // hold zero, so a non-zero sum has a distance >= 0).  The table is this wave's own and the
+    // hold zero).  The table is this wave's own and the
     // LDS serves a wave's requests in order, so only the compiler's order is kept here.
     lds_order();
     if (lane < 63) {
@@ -336,7 +337,8 @@ __global__ __launch_bounds__(2 * 64) void bwd_dq_kernel(BackwardParams p) {
         const int jj0 = c - lane + 31;  // key of column c
         x += ((unsigned)jj0 < (unsigned)kRows ? y[0] : 0.f) + ((unsigned)(jj0 + 1) < (unsigned)kRows ? y[1] : 0.f);
       }
-      if (has_head && x != 0.f) unsafeAtomicAdd(dbias_h + min(dbase + lane, p.R - 1), x);
+      // rows of the table at negative distances hold only invisible pairs: never added
+      if (has_head && dbase + lane >= 0 && x != 0.f) unsafeAtomicAdd(dbias_h + min(dbase + lane, p.R - 1), x);
     }
     lds_order();  // the next tile's table stores come after these reads
   }

@@ -5,8 +5,8 @@
 //   out = softmax_j(q.k_j / sqrt(128) + r[h, min(p - j, R - 1)]) . V,  lse = log-sum-exp,
 // over keys 0 <= p - j (and p - j <= W - 1 for a sliding window).  This is the relative
 // attention of the vLLM recipes page "thinkingmachines/Inkling" (Overview >
-// Architectural highlights > Attention: a learned relative-position term added to the
-// pre-softmax logits of GQA with head size 128, full and sliding-window layers).  The
+// Architectural highlights > Attention: GQA with head size 128, a trained bias on the
+// logits that depends on the query-key distance, full and sliding-window layers).  The
 // page's Performance section names a "sheared-bias" attention kernel: the bias a query
 // tile meets against a key tile is one diagonal slice of r, which is what is staged here.
 //
@@ -23,8 +23,9 @@
 //     beyond R - 1), the causal / window mask only on edge tiles, an online softmax whose
 //     running maximum is only raised when it grows by more than kRescaleSlack (so the
 //     O rescale is rare), then O^T += V^T P^T with V read transposed from LDS.
-//   - bf16 inputs use two LDS stages (next tile's loads in flight while the current tile
-//     is computed); fp32 inputs keep hi/lo bf16 planes and use one stage.
+//   - the fp32 inputs are never rounded to bf16: K and V sit in LDS as hi/lo bf16 planes
+//     (hi = bf16(x), lo = bf16(x - hi)), Q as hi/lo registers, and each product takes the
+//     three terms hi.hi + hi.lo + lo.hi; one LDS stage, the next tile's loads in registers.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -41,27 +42,14 @@ constexpr int kBiasCopy = 100;       // floats per shifted copy (95 + 3 shift, p
 constexpr int kBiasWave = 4 * kBiasCopy;
 constexpr float kRescaleSlack = 8.0f;  // log2 units: P entries stay below 2^8
 
-template <bool F32>
-struct Cfg {
-  static constexpr int kStages = F32 ? 1 : 2;
-  static constexpr int kPlanes = F32 ? 2 : 1;  // bf16 hi (+ lo) planes
-  static constexpr int kKElems = kBK * kKStride;
-  static constexpr int kVElems = kBK * kVStride;
-};
+constexpr int kPlanes = 2;           // bf16 hi and lo planes of the fp32 K and V
+constexpr int kKElems = kBK * kKStride;
+constexpr int kVElems = kBK * kVStride;
 
-template <bool F32>
-struct TileRegs;
-
-template <>
-struct TileRegs<false> {  // 64 x 128 bf16 K and V: two 16-byte chunks each per thread
-  u32x4_t k[2], v[2];
-};
-template <>
-struct TileRegs<true> {  // 64 x 128 fp32 K and V: four 16-byte chunks each per thread
+struct TileRegs {  // 64 x 128 fp32 K and V: four 16-byte chunks each per thread
   f32x4_t k[4], v[4];
 };
 
-__device__ __forceinline__ u32x4_t ld16(const void* p) { return *(const u32x4_t*)p; }
 __device__ __forceinline__ f32x4_t ld16f(const void* p) { return *(const f32x4_t*)p; }
 
 // hi = bf16(x), lo = bf16(x - hi) for four floats, packed as 4 bf16 each.
@@ -74,12 +62,10 @@ __device__ __forceinline__ void split4(f32x4_t x, u32x2_t& hi, u32x2_t& lo) {
   lo[1] = pack_bf16x2(x[2] - bf16_lo_to_f32(h23), x[3] - bf16_hi_to_f32(h23));
 }
 
-template <bool F32>
 __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
-  using C = Cfg<F32>;
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[C::kStages][C::kPlanes][C::kKElems];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[C::kStages][C::kPlanes][C::kVElems];
-  __shared__ __attribute__((aligned(16))) float b_lds[C::kStages][kWaves][kBiasWave];
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[kPlanes][kKElems];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[kPlanes][kVElems];
+  __shared__ __attribute__((aligned(16))) float b_lds[kWaves][kBiasWave];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -116,8 +102,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
   const int wkmax = pw_last;
 
   // ---- Q^T operand, resident for the whole key loop -------------------------------
-  u32x4_t qh[8];
-  u32x4_t ql[F32 ? 8 : 1];
+  u32x4_t qh[8], ql[8];
   {
     const int tq = tw0 + col;
     const bool ok = wave_active && tq < p.Lq;
@@ -125,57 +110,37 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       const int d = 16 * ks + 8 * hf;
-      if constexpr (!F32) {
-        qh[ks] = ok ? ld16((const uint16_t*)p.q + qbase + d) : zero_u32x4();
+      f32x4_t x0, x1;
+      if (ok) {
+        x0 = ld16f((const float*)p.q + qbase + d);
+        x1 = ld16f((const float*)p.q + qbase + d + 4);
       } else {
-        f32x4_t x0, x1;
-        if (ok) {
-          x0 = ld16f((const float*)p.q + qbase + d);
-          x1 = ld16f((const float*)p.q + qbase + d + 4);
-        } else {
-          x0 = x1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        }
-        u32x2_t h0, l0, h1, l1;
-        split4(x0, h0, l0);
-        split4(x1, h1, l1);
-        qh[ks] = u32x4_t{h0[0], h0[1], h1[0], h1[1]};
-        ql[ks] = u32x4_t{l0[0], l0[1], l1[0], l1[1]};
+        x0 = x1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
       }
+      u32x2_t h0, l0, h1, l1;
+      split4(x0, h0, l0);
+      split4(x1, h1, l1);
+      qh[ks] = u32x4_t{h0[0], h0[1], h1[0], h1[1]};
+      ql[ks] = u32x4_t{l0[0], l0[1], l1[0], l1[1]};
     }
   }
 
   // ---- tile loads: global -> registers -> LDS -------------------------------------
-  TileRegs<F32> tr;
+  TileRegs tr;
   float breg[2];
   const size_t kv_seq = (size_t)b * p.Lk;
   auto issue_tile = [&](int kt) {
     const int j0 = kt * kBK;
-    if constexpr (!F32) {
-      const int r0 = tid >> 4, chunk = tid & 15;
+    const int r0 = tid >> 5, chunk = tid & 31;
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const int j = j0 + r0 + 32 * c;
-        if (j < p.Lk) {
-          const size_t a = ((kv_seq + j) * p.Hkv + hk) * kHeadDim + chunk * 8;
-          tr.k[c] = ld16((const uint16_t*)p.k + a);
-          tr.v[c] = ld16((const uint16_t*)p.v + a);
-        } else {
-          tr.k[c] = zero_u32x4();
-          tr.v[c] = zero_u32x4();
-        }
-      }
-    } else {
-      const int r0 = tid >> 5, chunk = tid & 31;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int j = j0 + r0 + 16 * c;
-        if (j < p.Lk) {
-          const size_t a = ((kv_seq + j) * p.Hkv + hk) * kHeadDim + chunk * 4;
-          tr.k[c] = ld16f((const float*)p.k + a);
-          tr.v[c] = ld16f((const float*)p.v + a);
-        } else {
-          tr.k[c] = tr.v[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        }
+    for (int c = 0; c < 4; ++c) {
+      const int j = j0 + r0 + 16 * c;
+      if (j < p.Lk) {
+        const size_t a = ((kv_seq + j) * p.Hkv + hk) * kHeadDim + chunk * 4;
+        tr.k[c] = ld16f((const float*)p.k + a);
+        tr.v[c] = ld16f((const float*)p.v + a);
+      } else {
+        tr.k[c] = tr.v[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       }
     }
     // bias slice for this wave: distances pw0 - j0 - 63 + c, c = 0..94, clamped to [0, R-1]
@@ -187,26 +152,17 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
       breg[c] = (idx < kBiasSlice) ? p.bias[(size_t)h * p.R + d] * kLog2e : 0.f;
     }
   };
-  auto store_tile = [&](int st) {
-    if constexpr (!F32) {
-      const int r0 = tid >> 4, chunk = tid & 15;
+  auto store_tile = [&]() {
+    const int r0 = tid >> 5, chunk = tid & 31;
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        *(u32x4_t*)&k_lds[st][0][(r0 + 32 * c) * kKStride + chunk * 8] = tr.k[c];
-        *(u32x4_t*)&v_lds[st][0][(r0 + 32 * c) * kVStride + chunk * 8] = tr.v[c];
-      }
-    } else {
-      const int r0 = tid >> 5, chunk = tid & 31;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        u32x2_t hi, lo;
-        split4(tr.k[c], hi, lo);
-        *(u32x2_t*)&k_lds[st][0][(r0 + 16 * c) * kKStride + chunk * 4] = hi;
-        *(u32x2_t*)&k_lds[st][1][(r0 + 16 * c) * kKStride + chunk * 4] = lo;
-        split4(tr.v[c], hi, lo);
-        *(u32x2_t*)&v_lds[st][0][(r0 + 16 * c) * kVStride + chunk * 4] = hi;
-        *(u32x2_t*)&v_lds[st][1][(r0 + 16 * c) * kVStride + chunk * 4] = lo;
-      }
+    for (int c = 0; c < 4; ++c) {
+      u32x2_t hi, lo;
+      split4(tr.k[c], hi, lo);
+      *(u32x2_t*)&k_lds[0][(r0 + 16 * c) * kKStride + chunk * 4] = hi;
+      *(u32x2_t*)&k_lds[1][(r0 + 16 * c) * kKStride + chunk * 4] = lo;
+      split4(tr.v[c], hi, lo);
+      *(u32x2_t*)&v_lds[0][(r0 + 16 * c) * kVStride + chunk * 4] = hi;
+      *(u32x2_t*)&v_lds[1][(r0 + 16 * c) * kVStride + chunk * 4] = lo;
     }
     // four copies shifted by 0..3 so every lane can fetch its four biases with one
     // aligned 16-byte read (copy s holds slice[c] at index c + s)
@@ -215,7 +171,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
       const int idx = lane + 64 * c;
       if (idx < kBiasSlice) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) b_lds[st][wave][s * kBiasCopy + idx + s] = breg[c];
+        for (int s = 0; s < 4; ++s) b_lds[wave][s * kBiasCopy + idx + s] = breg[c];
       }
     }
   };
@@ -230,7 +186,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
   const float bias_sat = p.bias[(size_t)h * p.R + (p.R - 1)] * kLog2e;
   const int bsel = (4 - (col & 3)) & 3;  // which shifted bias copy is aligned for this lane
 
-  auto compute_tile = [&](int kt, int st) {
+  auto compute_tile = [&](int kt) {
     const int j0 = kt * kBK;
     if (!wave_active || j0 > wkmax || j0 + kBK - 1 < wkmin) return;
     const bool need_mask = (j0 + kBK - 1 > pw0) || (j0 < pw_last - Weff + 1);
@@ -241,16 +197,15 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       s[kb] = zero_f32x16();
-      const uint16_t* krow = &k_lds[st][0][(32 * kb + col) * kKStride + 8 * hf];
+      const uint16_t* krow = &k_lds[0][(32 * kb + col) * kKStride + 8 * hf];
+      const uint16_t* krow_lo = &k_lds[1][(32 * kb + col) * kKStride + 8 * hf];
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
         const u32x4_t a = *(const u32x4_t*)(krow + 16 * ks);
+        const u32x4_t al = *(const u32x4_t*)(krow_lo + 16 * ks);
         s[kb] = mfma_32x32x16(a, qh[ks], s[kb]);
-        if constexpr (F32) {
-          const u32x4_t al = *(const u32x4_t*)(&k_lds[st][1][(32 * kb + col) * kKStride + 8 * hf] + 16 * ks);
-          s[kb] = mfma_32x32x16(a, ql[ks], s[kb]);
-          s[kb] = mfma_32x32x16(al, qh[ks], s[kb]);
-        }
+        s[kb] = mfma_32x32x16(a, ql[ks], s[kb]);
+        s[kb] = mfma_32x32x16(al, qh[ks], s[kb]);
       }
     }
 
@@ -266,7 +221,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
         } else {
           // element (col, key 32kb + 8q + 4hf + e) reads slice[col - 32kb - 8q - 4hf - e + 63]
           const int a = col - 32 * kb - 8 * q - 4 * hf + 60;
-          bv = *(const f32x4_t*)&b_lds[st][wave][bsel * kBiasCopy + a + bsel];
+          bv = *(const f32x4_t*)&b_lds[wave][bsel * kBiasCopy + a + bsel];
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) t[kb][4 * q + e] = s[kb][4 * q + e] * p.scale_log2 + bv[3 - e];
@@ -312,23 +267,20 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
     l_run += lsum;
 
     // O^T += V^T P^T
-    u32x4_t ph[2][2];
-    u32x4_t pl[2][2];
+    u32x4_t ph[2][2], pl[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         ph[kb][half] = pack_p_operand(&t[kb][8 * half]);
-        if constexpr (F32) {
-          float rest[8];
+        float rest[8];
 #pragma unroll
-          for (int e = 0; e < 8; e += 2) {
-            const uint32_t w = ph[kb][half][e >> 1];
-            rest[e] = t[kb][8 * half + e] - bf16_lo_to_f32(w);
-            rest[e + 1] = t[kb][8 * half + e + 1] - bf16_hi_to_f32(w);
-          }
-          pl[kb][half] = pack_p_operand(rest);
+        for (int e = 0; e < 8; e += 2) {
+          const uint32_t w = ph[kb][half][e >> 1];
+          rest[e] = t[kb][8 * half + e] - bf16_lo_to_f32(w);
+          rest[e + 1] = t[kb][8 * half + e + 1] - bf16_hi_to_f32(w);
         }
+        pl[kb][half] = pack_p_operand(rest);
       }
 #pragma unroll
     for (int db = 0; db < 4; ++db)
@@ -337,27 +289,24 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           const int kbase = 32 * kb + 16 * half;
-          const u32x4_t a = load_vt_operand(&v_lds[st][0][0], kVStride, kbase, 32 * db, lane);
+          const u32x4_t a = load_vt_operand(&v_lds[0][0], kVStride, kbase, 32 * db, lane);
+          const u32x4_t al = load_vt_operand(&v_lds[1][0], kVStride, kbase, 32 * db, lane);
           o[db] = mfma_32x32x16(a, ph[kb][half], o[db]);
-          if constexpr (F32) {
-            const u32x4_t al = load_vt_operand(&v_lds[st][1][0], kVStride, kbase, 32 * db, lane);
-            o[db] = mfma_32x32x16(al, ph[kb][half], o[db]);
-            o[db] = mfma_32x32x16(a, pl[kb][half], o[db]);
-          }
+          o[db] = mfma_32x32x16(al, ph[kb][half], o[db]);
+          o[db] = mfma_32x32x16(a, pl[kb][half], o[db]);
         }
   };
 
   // ---- key loop ----------------------------------------------------------------------
   issue_tile(kt_begin);
-  store_tile(0);
+  store_tile();
   __syncthreads();
   for (int kt = kt_begin; kt < kt_end; ++kt) {
-    const int st = (C::kStages == 2) ? ((kt - kt_begin) & 1) : 0;
     const bool has_next = kt + 1 < kt_end;
-    if (has_next) issue_tile(kt + 1);
-    compute_tile(kt, st);
-    if constexpr (C::kStages == 1) __syncthreads();
-    if (has_next) store_tile(C::kStages == 2 ? (st ^ 1) : 0);
+    if (has_next) issue_tile(kt + 1);  // into registers, while this tile is computed
+    compute_tile(kt);
+    __syncthreads();  // every wave is done with this tile's LDS
+    if (has_next) store_tile();
     __syncthreads();
   }
 
@@ -374,27 +323,20 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
       const int d = 32 * db + 8 * q + 4 * hf;
       const float x0 = o[db][4 * q + 0] * inv, x1 = o[db][4 * q + 1] * inv;
       const float x2 = o[db][4 * q + 2] * inv, x3 = o[db][4 * q + 3] * inv;
-      if constexpr (!F32) {
-        *(u32x2_t*)((uint16_t*)p.out + obase + d) = u32x2_t{pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
-      } else {
-        *(f32x4_t*)((float*)p.out + obase + d) = f32x4_t{x0, x1, x2, x3};
-      }
+      *(f32x4_t*)((float*)p.out + obase + d) = f32x4_t{x0, x1, x2, x3};
     }
   if (hf == 0 && p.lse != nullptr)
     p.lse[((size_t)b * p.Lq + tq) * p.Hq + h] = (m_run + __log2f(l_tot)) * kLn2;
 }
 
-template <bool F32>
-hipError_t launch(const PrefillParams& p, hipStream_t stream) {
+}  // namespace
+
+hipError_t launch_prefill_fp32(const PrefillParams& p, hipStream_t stream) {
   const long long grid = (long long)p.n_tok_tiles * p.B * p.Hkv * p.n_hg;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(prefill_kernel<F32>, dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL(prefill_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
-
-}  // namespace
-
-hipError_t launch_prefill_fp32(const PrefillParams& p, hipStream_t stream) { return launch<true>(p, stream); }
 
 }  // namespace rattn

@@ -4,8 +4,8 @@
 //   out = softmax_j(q.k_j / sqrt(128) + r[h, min(p - j, R - 1)]) . V,  lse = log-sum-exp,
 // over keys 0 <= p - j (and p - j <= W - 1 for a sliding window): the relative attention
 // of the vLLM recipes page "thinkingmachines/Inkling" (Overview > Architectural
-// highlights > Attention: a learned relative-position term added to the pre-softmax
-// logits of GQA with head size 128, full and sliding-window layers).  Its Performance
+// highlights > Attention: GQA with head size 128, a trained bias on the logits that
+// depends on the query-key distance, full and sliding-window layers).  Its Performance
 // section names a "sheared-bias" kernel: the bias a query tile meets against a key tile
 // is one diagonal band of r, which is what each wave stages per tile.
 //

@@ -1,8 +1,8 @@
 // sconv.hip -- the key/value short convolution written into the paged caches, gfx950.
 //
 // vLLM recipes page "thinkingmachines/Inkling", Overview > Architectural highlights > Short
-// convolution: every layer applies window-4 sconv modules to the attention keys and values,
-// and vLLM keeps the sconv state as the KV cache of a virtual sliding-window layer.  Read
+// convolution: each layer runs four-tap short convolutions over the token axis of, among
+// others, the attention keys and values, with their state kept in paged storage.  Read
 // here as the causal depthwise convolution over tokens with four taps and a weight per tap
 // and channel (no bias, no activation):
 //     y[p, c] = sum_{s=0..3} w[s, c] x[p - s, c],   x[p] = 0 for p < 0,

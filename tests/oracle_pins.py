@@ -12,8 +12,8 @@ AssertionError when the oracle disagrees with:
   * brute force over tiny inputs with pure-Python loops.
 The definition being pinned is the one on the vLLM recipes page
 "thinkingmachines/Inkling", Overview > Architectural highlights > Attention:
-a learned relative-position term added to the pre-softmax logits of GQA with
-head size 128, with the term fixed as r[h, min(i-j, R-1)].
+GQA with head size 128 whose logits carry a trained, distance-dependent bias
+in place of RoPE, with the term fixed as r[h, min(i-j, R-1)].
 
 tests/test_oracle.py runs every pin on the real oracle; tests/test_oracle_mutants.py
 runs them on deliberately broken copies and requires each copy to fail one.
