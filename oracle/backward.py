@@ -39,9 +39,11 @@ def prefill_backward(q, k, v, bias, dout, window: int = 0):
 
     q [B, Lq, Hq, D], k and v [B, Lk, Hkv, D], dout [B, Lq, Hq, D]: uint16 (bf16 bits),
     float32 or float64; bias [Hq, R].  Returns float64 arrays
-    (dq [B, Lq, Hq, D], dk [B, Lk, Hkv, D], dv [B, Lk, Hkv, D], dbias [Hq, R],
-    dbias_abs [Hq, R]); dbias_abs holds the sums of |dS| behind each dbias entry (for error
-    bounds: dbias entries are sums whose terms cancel)."""
+    (dq [B, Lq, Hq, D], dk [B, Lk, Hkv, D], dv [B, Lk, Hkv, D], dbias [Hq, R], absums) with
+    absums = (dq_abs, dk_abs, dv_abs, dbias_abs): the same sums with every term taken by
+    absolute value and dS replaced by dS_abs = P * (|dP - D| + D_abs), where D_abs =
+    rowsum(P * (|dO| |V|^T)) is the size of D's terms.  They bound an implementation's
+    rounding errors element by element (the gradients are sums whose terms cancel)."""
     Q, K, V, dO = _f64(q), _f64(k), _f64(v), _f64(dout)
     r = np.asarray(bias, dtype=np.float64)
     B, Lq, Hq, D = Q.shape
@@ -59,6 +61,9 @@ def prefill_backward(q, k, v, bias, dout, window: int = 0):
     dk = np.zeros_like(K)
     dv = np.zeros_like(V)
     dbias = np.zeros((Hq, R))
+    dq_abs = np.zeros_like(Q)
+    dk_abs = np.zeros_like(K)
+    dv_abs = np.zeros_like(V)
     dbias_abs = np.zeros((Hq, R))
     for b in range(B):
         for h in range(Hq):
@@ -68,13 +73,20 @@ def prefill_backward(q, k, v, bias, dout, window: int = 0):
             e = np.exp(s - s.max(axis=1, keepdims=True))
             P = e / e.sum(axis=1, keepdims=True)
             dP = dO[b, :, h] @ V[b, :, hk].T
-            dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+            Drow = (P * dP).sum(axis=1, keepdims=True)
+            dS = P * (dP - Drow)
             dq[b, :, h] = dS @ K[b, :, hk] * scale
             dk[b, :, hk] += dS.T @ Q[b, :, h] * scale
             dv[b, :, hk] += P.T @ dO[b, :, h]
             dbias[h] += np.bincount(didx[vis], weights=dS[vis], minlength=R)
-            dbias_abs[h] += np.bincount(didx[vis], weights=np.abs(dS[vis]), minlength=R)
-    return dq, dk, dv, dbias, dbias_abs
+            # magnitude sums
+            Dabs = (P * (np.abs(dO[b, :, h]) @ np.abs(V[b, :, hk]).T)).sum(axis=1, keepdims=True)
+            dSa = P * (np.abs(dP - Drow) + Dabs)
+            dq_abs[b, :, h] = dSa @ np.abs(K[b, :, hk]) * scale
+            dk_abs[b, :, hk] += dSa.T @ np.abs(Q[b, :, h]) * scale
+            dv_abs[b, :, hk] += P.T @ np.abs(dO[b, :, h])
+            dbias_abs[h] += np.bincount(didx[vis], weights=dSa[vis], minlength=R)
+    return dq, dk, dv, dbias, (dq_abs, dk_abs, dv_abs, dbias_abs)
 
 
 def prefill_backward_dq_rows(q, k, v, bias, dout, window: int, rows):

@@ -33,7 +33,7 @@
  * w_j = exp(s_j - m), Z = sum_j w_j, out = sum_j (w_j / Z) v_j, lse = m + log Z.
  * All arithmetic is double.  bf16 and fp32 inputs widen to double exactly.
  */
-#include "rattn_oracle.h"
+#include "rattn_oracle.h" /* include/rattn_oracle.h */
 
 #include <math.h>
 #include <stdint.h>
@@ -74,11 +74,13 @@ static size_t kv_offset(const int* block_table, int b, int j, int kvh, int Lk_ma
   }
 }
 
-int rattn_ref_cpu(const void* q, const void* k, const void* v, const int* block_table,
-                  const int* ctx_lens, const int* windows, const double* bias, double* out,
-                  double* lse, double* probs, int B, int n_q, int Lk_max, int Hq, int Hkv,
-                  int head_dim, int block_size, int R, int max_blocks_per_seq, int dtype,
-                  int num_threads) {
+/* bias_per_row = 0: bias is [Hq, R], the table of head h; 1: bias is [B, n_q, Hq, R], one
+   table per query row (the row (b, t, h) reads its own R entries) */
+static int ref_forward(const void* q, const void* k, const void* v, const int* block_table,
+                       const int* ctx_lens, const int* windows, const double* bias, int bias_per_row,
+                       double* out, double* lse, double* probs, int B, int n_q, int Lk_max, int Hq,
+                       int Hkv, int head_dim, int block_size, int R, int max_blocks_per_seq, int dtype,
+                       int num_threads) {
   long long rows, row;
   int b;
   int bad = 0;
@@ -125,7 +127,7 @@ int rattn_ref_cpu(const void* q, const void* k, const void* v, const int* block_
       const int lo = (W > 0 && p - W + 1 > 0) ? p - W + 1 : 0;
       const int hi = p;                                  /* causal: keys 0..p */
       const double scale = 1.0 / sqrt((double)head_dim);
-      const double* r = bias + (size_t)h * R;
+      const double* r = bias + (size_t)(bias_per_row ? row : h) * R;
       double m = -INFINITY, Z = 0.0;
       int j, e;
       const size_t orow = (size_t)row * head_dim;
@@ -173,4 +175,23 @@ int rattn_ref_cpu(const void* q, const void* k, const void* v, const int* block_
   return 0;
 }
 
-int rattn_oracle_version(void) { return 1; }
+int rattn_ref_cpu(const void* q, const void* k, const void* v, const int* block_table,
+                  const int* ctx_lens, const int* windows, const double* bias, double* out,
+                  double* lse, double* probs, int B, int n_q, int Lk_max, int Hq, int Hkv,
+                  int head_dim, int block_size, int R, int max_blocks_per_seq, int dtype,
+                  int num_threads) {
+  return ref_forward(q, k, v, block_table, ctx_lens, windows, bias, 0, out, lse, probs, B, n_q, Lk_max, Hq,
+                     Hkv, head_dim, block_size, R, max_blocks_per_seq, dtype, num_threads);
+}
+
+int rattn_ref_cpu_tokbias(const void* q, const void* k, const void* v, const int* block_table,
+                          const int* ctx_lens, const int* windows, const double* bias,
+                          double* out, double* lse, double* probs, int B, int n_q, int Lk_max,
+                          int Hq, int Hkv, int head_dim, int block_size, int R,
+                          int max_blocks_per_seq, int dtype, int num_threads) {
+  return ref_forward(q, k, v, block_table, ctx_lens, windows, bias, 1, out, lse, probs, B, n_q, Lk_max, Hq,
+                     Hkv, head_dim, block_size, R, max_blocks_per_seq, dtype, num_threads);
+}
+
+int rattn_oracle_version(void) { return 2; }
+

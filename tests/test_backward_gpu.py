@@ -1,16 +1,26 @@
-"""Backward pass of the bf16 prefill (rattn_prefill_backward) against the fp64 oracle.
+"""Backward pass of the bf16 prefill (rattn_prefill_backward) against the fp64 oracle, element
+by element.
 
-The forward runs on the GPU (rattn_prefill) to give out and lse, as in training; the oracle
-recomputes everything from q, k, v, r and dO.  Tolerances (bf16 inputs, fp32 accumulation;
-the rounding of P and dS to bf16 for the MFMAs and of out to bf16 in D = rowsum(dO * out)
-each move a term by at most 2^-9 of its size):
-  dq, dk, dv: |gpu - ref|_2 <= 1e-2 |ref|_2 and max |gpu - ref| <= 3e-2 max |ref|;
-  dbias[h, d]: |gpu - ref| <= 1e-2 * (sum of |dS| behind the entry) + 1e-6 * max of those sums
-  + 1e-6 per pair behind the entry;
-  a reference that is exactly zero: max |gpu| <= 1e-4 (fp32 rounding of dP - D).
+The forward runs on the GPU (rattn_prefill) to give out and lse, as in training; the C oracle
+(rattn_ref_cpu_backward) recomputes everything from q, k, v, r and dO in double and also
+returns, for every gradient entry, the sum of its terms' magnitudes (absum: dS replaced by
+dS_abs = P (|dP - D| + D_abs), D_abs = sum_j P_j sum_e |dO_e v_j,e|).
+
+Bound, per entry:  |gpu - oracle| <= 2^-6 * absum + 1e-7.
+Derivation (u = 2^-8, the unit roundoff of bf16):
+  - P and dS are rounded to bf16 as MFMA operands: relative error u per term;
+  - D comes from the bf16 output of the GPU forward, which is within u (P rounded to bf16 in
+    P.V) plus u (output rounding) of the exact O: |error of D| <= 2u D_abs, and every dS_j
+    carries P_j times that;
+  - P is recomputed from the fp32 logits and the forward's lse (error ~1e-5 relative, far
+    below u), the fp32 sums of <= 8192 terms add at most 8192 * 2^-24 = 2^-11 of absum;
+so each entry is within (2u + 2^-11) absum ~ 2^-7 absum; the bound takes twice that.  The
+1e-7 covers entries whose exact value and absum are both zero (keys no query sees: the GPU
+must write exact zeros there) and fp32 rounding at that scale.
 Cases: ragged lengths (tails of 12 and 20 rows), a chunk after a prefix (Lq < Lk), a window
 with one KV head, one query head per KV head with window 1 (closed form: dq = dk = dbias = 0),
-three query heads per KV head (the kernels pair heads; the odd one out runs alone).
+three query heads per KV head (the kernels pair heads; the odd one out runs alone), sixteen
+query heads per KV head, and the full 8K-token window-4096 workload the benchmark times.
 """
 import numpy as np
 import pytest
@@ -18,11 +28,14 @@ import torch
 
 from gpu_util import dev, host
 
+import oracle
 import relative_bias_gqa_amd as rb
 from relative_bias_gqa_amd import synth
-from oracle.backward import prefill_backward
 
 pytestmark = pytest.mark.gpu
+
+BOUND_REL = 2.0 ** -6
+BOUND_ABS = 1e-7
 
 CASES = [
     # name, seed, B, Lq, Lk, Hq, Hkv, R, window
@@ -32,6 +45,7 @@ CASES = [
     ("window_one", 84, 1, 100, 130, 4, 4, 9, 1),
     ("three_heads_per_kv_head", 85, 1, 77, 333, 6, 2, 50, 100),
     ("sixteen_heads_per_kv_head", 86, 1, 150, 150, 32, 2, 40, 0),
+    ("window_chunk_unseen_keys", 87, 1, 64, 400, 8, 2, 30, 50),
 ]
 
 
@@ -44,77 +58,78 @@ def run_backward(case):
     return host(dq), host(dk), host(dv), host(dbias)
 
 
-def check(name, got, ref):
+def check(name, got, ref, absum):
+    """Every entry within BOUND_REL * absum + BOUND_ABS of the oracle."""
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
     assert np.isfinite(got).all(), f"{name}: non-finite"
-    err = got - ref
+    err = np.abs(got - ref)
+    bound = BOUND_REL * absum + BOUND_ABS
+    ratio = err / bound
+    worst = np.unravel_index(np.argmax(ratio), ratio.shape) if ratio.size else ()
     nrm = np.linalg.norm(ref)
-    rel = np.linalg.norm(err) / max(nrm, 1e-30)
-    mx = np.abs(err).max() if err.size else 0.0
-    print(f"  {name}: normwise {rel:.2e}, max {mx:.2e} (max |ref| {np.abs(ref).max():.2e})", flush=True)
-    if nrm == 0:
-        # an exact zero that the kernel reaches as dS = P (dP - D) with P = 1 and dP, D two
-        # fp32 dot products of 128 terms of size ~1 taken in different orders
-        assert mx <= 1e-4, name
-        return
-    assert rel <= 1e-2, name
-    assert mx <= 3e-2 * np.abs(ref).max(), name
+    rel = np.linalg.norm(got - ref) / nrm if nrm > 0 else 0.0
+    print(f"  {name}: max err {err.max() if err.size else 0:.2e}, worst err/bound "
+          f"{ratio.max() if ratio.size else 0:.3f} at {worst}, normwise {rel:.2e}", flush=True)
+    assert (err <= bound).all(), f"{name}: {int((err > bound).sum())} entries beyond the bound"
+
+
+def compare_all(grads, case, num_threads=0):
+    f = case.fwd
+    refs, absums = oracle.ref_backward(f.q, f.k, f.v, f.bias, case.dout, f.window, num_threads=num_threads)
+    for name, g, ref, a in zip(("dq", "dk", "dv", "dbias"), grads, refs, absums):
+        check(name, g, ref, a)
 
 
 @pytest.mark.parametrize("name,seed,B,Lq,Lk,Hq,Hkv,R,window", CASES, ids=[c[0] for c in CASES])
 def test_backward_matches_oracle(name, seed, B, Lq, Lk, Hq, Hkv, R, window):
     print(f"case backward {name}", flush=True)
     case = synth.make_backward(seed, B, Lq, Lk, Hq, Hkv, R, window, name)
-    dq, dk, dv, dr = run_backward(case)
-    f = case.fwd
-    rq, rk, rv, rr, rabs = prefill_backward(f.q, f.k, f.v, f.bias, case.dout, window)
-    check("dq", dq, rq)
-    check("dk", dk, rk)
-    check("dv", dv, rv)
-    derr = np.abs(dr - rr)
-    # pairs behind each entry: every dS carries the fp32 rounding of dP - D (up to ~1e-6)
-    pos = (Lk - Lq) + np.arange(Lq)[:, None]
-    dist = pos - np.arange(Lk)[None, :]
-    vis = (dist >= 0) & ((window <= 0) | (dist <= window - 1))
-    npairs = B * np.bincount(np.minimum(dist[vis], R - 1), minlength=R)
-    bound = 1e-2 * rabs + 1e-6 * max(rabs.max(), 1e-30) + 1e-6 * npairs[None, :]
-    print(f"  dbias: max err {derr.max():.2e}, worst err/bound {(derr / bound).max():.2f}", flush=True)
-    assert (derr <= bound).all()
+    compare_all(run_backward(case), case)
 
 
-def test_backward_full_size_sampled():
-    """The backward of the 8K-token window-4096 prefill (16/2 heads, R 4096) at full size, in the
-    launch configuration the benchmark times: 27 dq rows against the oracle row by row (same
-    bar as above), and two sums that hold at any size, bounded from the inputs alone:
-      sum_j dv[j] = sum_i sum_(h in group) dO[i, h] (every row of P sums to one): the sum of
-        8192 dv entries, each within ~2e-3 of its size (the cases above), is bounded by
-        2e-2 of the root-sum-square of the dO terms (a head left out would miss by ~90);
-      sum_d dr[h, d] = 0 (every row of dS sums to zero), a coarse check: D comes from the bf16
-        output (|out| <= max |V|), so |error| <= 2^-8 max|V| sum |dO| over the head."""
+def test_backward_full_size():
+    """The backward of the 8K-token window-4096 prefill (16/2 heads, R 4096) at full size, in
+    the launch configuration the benchmark times: every entry of dq, dk, dv and dbias against
+    the oracle (about 30 s of host time on 16 threads)."""
     print("case backward full size swa_prefill_8k_bwd", flush=True)
-    from oracle.backward import prefill_backward_dq_rows
-    from oracle.sconv import bf16_to_f64
     case = synth.swa_prefill_8k_bwd()
-    dq, dk, dv, dr = run_backward(case)
+    grads = run_backward(case)
+    compare_all(grads, case)
+
+
+def test_backward_nan_gradient_row_stays_in_bounds():
+    """A non-finite output gradient must not make the kernels write outside their outputs.
+    One dO row is NaN; dbias sits inside a larger buffer whose guard entries on both sides
+    must come back unchanged.  Gradients that do not depend on that row stay finite: dq of
+    every other row, dbias of every other head, dk and dv of the other KV head."""
+    print("case backward NaN dout row, guarded dbias", flush=True)
+    B, Lq, Lk, Hq, Hkv, R, window = 1, 96, 96, 8, 2, 40, 0
+    case = synth.make_backward(88, B, Lq, Lk, Hq, Hkv, R, window, "nan_row")
     f = case.fwd
-    assert np.isfinite(dk).all() and np.isfinite(dv).all() and np.isfinite(dr).all()
-    rng = np.random.default_rng(5)
-    rows = [(0, int(t), int(h)) for t, h in zip(rng.integers(0, f.Lq, 24), rng.integers(0, f.Hq, 24))]
-    rows += [(0, 0, 0), (0, f.Lq - 1, f.Hq - 1), (0, f.window - 1, 7)]
-    ref = prefill_backward_dq_rows(f.q, f.k, f.v, f.bias, case.dout, f.window, rows)
-    check("dq rows", np.stack([dq[b, t, h] for (b, t, h) in rows]), ref)
-    do = bf16_to_f64(case.dout)  # [1, L, Hq, 128]
-    G = f.Hq // f.Hkv
-    grp = do.reshape(1, f.Lq, f.Hkv, G, 128)
-    expect = grp.sum(axis=(1, 3))
-    bound = 2e-2 * np.sqrt((grp ** 2).sum(axis=(1, 3))) + 1e-3
-    err = np.abs(dv.sum(axis=1) - expect)
-    print(f"  sum dv: max err {err.max():.3e}, worst err/bound {(err / bound).max():.3f}", flush=True)
-    assert (err <= bound).all()
-    vmax = np.abs(bf16_to_f64(f.v)).max()
-    rbound = 2.0 ** -8 * vmax * np.abs(do).sum(axis=(0, 1, 3)) + 1e-3
-    rerr = np.abs(dr.sum(axis=1))
-    print(f"  sum dr: max {rerr.max():.3e}, worst err/bound {(rerr / rbound).max():.3f}", flush=True)
-    assert (rerr <= rbound).all()
+    q, k, v, r = dev(f.q), dev(f.k), dev(f.v), dev(f.bias)
+    out, lse = rb.prefill(q, k, v, r, window)
+    dout = dev(case.dout)
+    t_nan, h_nan = 37, 3
+    dout[0, t_nan, h_nan, :] = float("nan")
+    guard = 4096
+    sentinel = 12345.0
+    buf = torch.full((guard + Hq * R + guard,), sentinel, dtype=torch.float32, device="cuda")
+    dbias = buf[guard:guard + Hq * R].view(Hq, R)
+    dq = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    dk = torch.empty(k.shape, dtype=torch.float32, device="cuda")
+    dv = torch.empty(v.shape, dtype=torch.float32, device="cuda")
+    ws = torch.empty(rb.rattn_prefill_backward_workspace_bytes(B, Lq, Hq), dtype=torch.uint8, device="cuda")
+    rb.rattn_prefill_backward(q, k, v, r, out, dout, lse, dq, dk, dv, dbias, window, ws)
+    torch.cuda.synchronize()
+    g = host(buf)
+    assert (g[:guard] == sentinel).all() and (g[guard + Hq * R:] == sentinel).all(), "write outside dbias"
+    dq_h, dbias_h, dk_h, dv_h = host(dq), host(dbias), host(dk), host(dv)
+    rows = np.ones((B, Lq, Hq), dtype=bool)
+    rows[0, t_nan, h_nan] = False
+    assert np.isfinite(dq_h[rows]).all()
+    assert np.isfinite(np.delete(dbias_h, h_nan, axis=0)).all()
+    other_kv = 1 - h_nan // (Hq // Hkv)
+    assert np.isfinite(dk_h[:, :, other_kv]).all() and np.isfinite(dv_h[:, :, other_kv]).all()
 
 
 def test_backward_empty_chunk_zeroes_gradients():
@@ -126,8 +141,6 @@ def test_backward_empty_chunk_zeroes_gradients():
     v = torch.randn(1, Lk, Hkv, 128, device="cuda").to(torch.bfloat16)
     q = torch.empty(1, 0, Hq, 128, device="cuda", dtype=torch.bfloat16)
     r = torch.randn(Hq, R, device="cuda")
-    lse = torch.empty(1, 0, Hq, device="cuda")
-    dq = torch.empty(1, 0, Hq, 128, device="cuda")
     dk = torch.full((1, Lk, Hkv, 128), float("nan"), device="cuda")
     dv = torch.full_like(dk, float("nan"))
     dr = torch.full((Hq, R), float("nan"), device="cuda")

@@ -1,4 +1,6 @@
-"""Pins of the backward oracle (oracle/backward.py) against things it does not compute itself.
+"""Pins of the two backward oracles -- oracle/backward.py (numpy, dense products per head) and
+rattn_ref_cpu_backward (oracle/rattn_oracle_bwd.c, plain loops one query row at a time) --
+against things they do not compute themselves.  Each pin runs on both.
 
 * Central finite differences of the forward oracle (the C implementation, itself pinned in
   test_oracle.py) of L = sum(dO * O), in float64, for entries of q, k, v and r: full causal
@@ -8,6 +10,9 @@
   dv[j] = sum over the heads of the group of dO at the same token.
 * Sums fixed by the softmax: every row of dS sums to zero, so sum_d dr[h, d] = 0; every row
   of P sums to one, so sum_j dv[j] = sum_i sum_(h in group) dO[i, h].
+* The magnitude sums (error-bound ingredients): never below the magnitude of the gradient
+  they go with (triangle inequality), equal to the gradient itself when every term is
+  non-negative in the dv sum (dO >= 0), and the same from both implementations.
 """
 import numpy as np
 import pytest
@@ -26,6 +31,18 @@ def _case(seed, B, Lq, Lk, Hq, Hkv, R, D=128):
     return q, k, v, r, do
 
 
+def _numpy_bwd(q, k, v, r, do, window):
+    dq, dk, dv, dr, absums = prefill_backward(q, k, v, r, do, window)
+    return (dq, dk, dv, dr), absums
+
+
+def _c_bwd(q, k, v, r, do, window):
+    return oracle.ref_backward(q, k, v, r, do, window)
+
+
+IMPLS = {"numpy": _numpy_bwd, "c": _c_bwd}
+
+
 def _loss(q, k, v, r, do, window):
     out, _, _ = oracle.ref_prefill(q, k, v, r, window)
     return float((out * do).sum())
@@ -39,10 +56,11 @@ FD_CASES = [
 ]
 
 
+@pytest.mark.parametrize("impl", sorted(IMPLS))
 @pytest.mark.parametrize("seed,B,Lq,Lk,Hq,Hkv,R,window", FD_CASES)
-def test_backward_matches_finite_differences(seed, B, Lq, Lk, Hq, Hkv, R, window):
+def test_backward_matches_finite_differences(impl, seed, B, Lq, Lk, Hq, Hkv, R, window):
     q, k, v, r, do = _case(seed, B, Lq, Lk, Hq, Hkv, R)
-    dq, dk, dv, dr, _ = prefill_backward(q, k, v, r, do, window)
+    (dq, dk, dv, dr), _ = IMPLS[impl](q, k, v, r, do, window)
     rng = np.random.default_rng(100 + seed)
     eps = 1e-5
     for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv), ("r", r, dr)):
@@ -62,27 +80,30 @@ def test_backward_matches_finite_differences(seed, B, Lq, Lk, Hq, Hkv, R, window
             assert abs(fd - gflat[idx]) <= 1e-6 * (1 + abs(fd)), (name, idx, fd, gflat[idx])
 
 
-def test_backward_window_one_closed_form():
+@pytest.mark.parametrize("impl", sorted(IMPLS))
+def test_backward_window_one_closed_form(impl):
     q, k, v, r, do = _case(7, 2, 8, 8, 4, 2, 5)
-    dq, dk, dv, dr, _ = prefill_backward(q, k, v, r, do, window=1)
+    (dq, dk, dv, dr), _ = IMPLS[impl](q, k, v, r, do, 1)
     assert np.abs(dq).max() == 0 and np.abs(dk).max() == 0 and np.abs(dr).max() == 0
     expect = do.reshape(2, 8, 2, 2, 128).sum(axis=3)  # heads 2 hk, 2 hk + 1 -> KV head hk
     assert np.allclose(dv, expect, rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("impl", sorted(IMPLS))
 @pytest.mark.parametrize("window", [0, 5])
-def test_backward_softmax_sums(window):
+def test_backward_softmax_sums(impl, window):
     q, k, v, r, do = _case(8, 2, 12, 20, 6, 2, 7)
-    dq, dk, dv, dr, dabs = prefill_backward(q, k, v, r, do, window)
-    assert np.all(np.abs(dr.sum(axis=1)) <= 1e-10 * (1 + dabs.sum(axis=1)))
+    (dq, dk, dv, dr), absums = IMPLS[impl](q, k, v, r, do, window)
+    assert np.all(np.abs(dr.sum(axis=1)) <= 1e-10 * (1 + absums[3].sum(axis=1)))
     expect = do.reshape(2, 12, 2, 3, 128).sum(axis=(1, 3))
     assert np.allclose(dv.sum(axis=1), expect, rtol=1e-12, atol=1e-10)
     # a bf16 input gives the same result as its exact float64 value
-    from oracle.sconv import f64_to_bf16
-    qb = f64_to_bf16(q)
-    a = prefill_backward(qb, k, v, r, do, window)[0]
-    b = prefill_backward(oracle.sconv.bf16_to_f64(qb), k, v, r, do, window)[0]
-    assert np.array_equal(a, b)
+    from oracle.sconv import bf16_to_f64, f64_to_bf16
+    qb, kb, vb, gb = (f64_to_bf16(x) for x in (q, k, v, do))
+    a = IMPLS[impl](qb, kb, vb, r, gb, window)[0]
+    b = IMPLS[impl](*(bf16_to_f64(x) for x in (qb, kb, vb)), r, bf16_to_f64(gb), window)[0]
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
 
 
 @pytest.mark.parametrize("window", [0, 4])
@@ -94,3 +115,43 @@ def test_dq_rows_equal_full_call(window):
     got = prefill_backward_dq_rows(q, k, v, r, do, window, rows)
     for n, (b, t, h) in enumerate(rows):
         assert np.allclose(got[n], dq[b, t, h], rtol=1e-12, atol=1e-12)
+
+
+ABS_CASES = [
+    # seed, B, Lq, Lk, Hq, Hkv, R, window
+    (11, 1, 20, 20, 4, 2, 8, 0),
+    (12, 2, 13, 30, 6, 2, 40, 7),
+    (13, 1, 9, 9, 3, 1, 3, 1),
+]
+
+
+@pytest.mark.parametrize("seed,B,Lq,Lk,Hq,Hkv,R,window", ABS_CASES)
+def test_backward_implementations_agree(seed, B, Lq, Lk, Hq, Hkv, R, window):
+    """The dense numpy form and the row-by-row C form compute the same gradients and
+    magnitude sums (summation orders differ: agreement to rounding)."""
+    q, k, v, r, do = _case(seed, B, Lq, Lk, Hq, Hkv, R)
+    ga, aa = _numpy_bwd(q, k, v, r, do, window)
+    gb, ab = _c_bwd(q, k, v, r, do, window)
+    for name, x, y, scale in zip(("dq", "dk", "dv", "dr"), ga, gb, aa):
+        assert np.all(np.abs(x - y) <= 1e-12 * (1 + scale)), name
+    for name, x, y in zip(("dq_abs", "dk_abs", "dv_abs", "dr_abs"), aa, ab):
+        assert np.allclose(x, y, rtol=1e-12, atol=1e-14), name
+
+
+@pytest.mark.parametrize("impl", sorted(IMPLS))
+@pytest.mark.parametrize("seed,B,Lq,Lk,Hq,Hkv,R,window", ABS_CASES)
+def test_backward_magnitude_sums(impl, seed, B, Lq, Lk, Hq, Hkv, R, window):
+    q, k, v, r, do = _case(seed, B, Lq, Lk, Hq, Hkv, R)
+    grads, absums = IMPLS[impl](q, k, v, r, do, window)
+    # triangle inequality: a sum is never larger than the sum of its terms' magnitudes
+    for name, g, a in zip(("dq", "dk", "dv", "dr"), grads, absums):
+        assert np.all(a >= np.abs(g) * (1 - 1e-12)), name
+    # with dO >= 0 every term of dv = P^T dO is non-negative: its magnitude sum is itself
+    grads, absums = IMPLS[impl](q, k, v, r, np.abs(do), window)
+    assert np.allclose(absums[2], grads[2], rtol=1e-12, atol=0)
+    # keys that no query sees get nothing
+    if Lk > Lq and window > 0:
+        first_seen = (Lk - Lq) - window + 1
+        if first_seen > 0:
+            for a in absums[1:3]:
+                assert np.all(a[:, :first_seen] == 0)

@@ -37,7 +37,7 @@ def test_pins_catch_mutant(tmp_path, name, old, new):
     assert src.count(old) == 1, f"mutation anchor not found exactly once: {old!r}"
     mut = tmp_path / "mutant.c"
     mut.write_text(src.replace(old, new))
-    hdr = os.path.join(os.path.dirname(SRC), "rattn_oracle.h")
+    hdr = os.path.join(os.path.dirname(os.path.dirname(SRC)), "include", "rattn_oracle.h")
     (tmp_path / "rattn_oracle.h").write_text(open(hdr).read())
     so = tmp_path / f"libmut_{name}.so"
     subprocess.run(["gcc", "-O1", "-std=c99", "-fPIC", "-shared", "-fopenmp", "-o", str(so), str(mut), "-lm"],

@@ -1,8 +1,9 @@
 """HIP path against the fp64 oracle, element by element, through the C ABI.
 
 Small cases span several tiles and end in ragged tails; the five named workloads run at
-full size (prefill checked on sampled rows the oracle computes one by one, decode in
-full).  Bar: O max abs <= 2e-2, O mean abs <= 2e-3, LSE max abs <= 1e-3."""
+full size and are compared in full: every output element and every lse entry (the 32K-key
+chunked prefill costs the oracle about 45 s of host time on 16 threads).
+Bar: O max abs <= 2e-2, O mean abs <= 2e-3 (over all elements), LSE max abs <= 1e-3."""
 import numpy as np
 import pytest
 
@@ -86,23 +87,16 @@ def test_tiny_prefill_fp32_workload():
     compare(out, lse, ref_o, ref_l, case.name)
 
 
-def _sample_rows(Lq, extra, seed):
-    rng = np.random.default_rng(seed)
-    base = {0, 1, 31, 32, 63, 64, 255, 256, Lq // 2, Lq - 65, Lq - 64, Lq - 33, Lq - 32, Lq - 2, Lq - 1}
-    base |= set(int(x) for x in extra if 0 <= x < Lq)
-    base |= set(int(x) for x in rng.integers(0, Lq, size=12))
-    return sorted(base)
-
-
 @pytest.mark.parametrize("workload", ["swa_prefill_8k", "chunked_prefill_32k"])
-def test_prefill_workload_sampled(workload):
+def test_prefill_workload_full(workload):
+    """The full-size workload in the launch configuration the benchmark times (the library's
+    key-range split plan and job queue), every element against the oracle."""
+    print(f"case {workload} (full output)", flush=True)
     case = synth.WORKLOAD_FNS[workload]()
     out, lse = run_prefill(case)
     assert np.isfinite(out).all() and np.isfinite(lse).all()
-    extra = [4094, 4095, 4096, 4097, 4127, 4128] if case.window else [8192 - 8193 + 4096]
-    rows = _sample_rows(case.Lq, extra, 7)
-    ref_o, ref_l = oracle.ref_prefill_rows(case.q, case.k, case.v, case.bias, case.window, [(0, t) for t in rows])
-    compare(out[0, rows], lse[0, rows], ref_o, ref_l, f"{workload} ({len(rows)} rows x {case.Hq} heads)")
+    ref_o, ref_l, _ = oracle.ref_prefill(case.q, case.k, case.v, case.bias, case.window)
+    compare(out, lse, ref_o, ref_l, f"{workload} (all {case.Lq} rows x {case.Hq} heads)")
 
 
 # ---------------------------------------------------------------------------------------
