@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define RATTN_ABI_VERSION 6
+#define RATTN_ABI_VERSION 7
 
 enum rattn_status {
   RATTN_OK = 0,
@@ -287,6 +287,34 @@ int rattn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
                        int Hkv, int head_dim, int block_size, int R, int num_blocks,
                        int max_blocks_per_seq, int max_ctx_len, int num_splits,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Allocation-free paged decode, for callers that cannot allocate device memory on the call
+ * path: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, computation and result as rattn_decode_paged (the same
+ * kernels and split plan: the output is bit-identical), minus the workspace: the split
+ * partials go to a static device array of rattn_decode_paged_noalloc_max_scratch_bytes()
+ * bytes (64 MiB) that the library holds on every device it runs on until the process ends.
+ * The call allocates and frees nothing (no hipMalloc, hipFree or allocating library
+ * routine); its first call on a device looks the array's address up on that device.
+ * The array holds only partial results that each call writes before it reads them, so
+ * nothing in it has to start at zero; it keeps the last call's contents.
+ * Every call on one device shares that device's array: calls that overlap on one device
+ * (on different streams, or from different threads without ordering) race and may return
+ * wrong results; calls on one stream are ordered and safe.
+ * Status: as rattn_decode_paged, and WORKSPACE when rattn_decode_workspace_bytes(...) for
+ * these sizes exceeds the static size (checked on the host before any launch; use
+ * rattn_decode_paged with a workspace, or fewer sequences per call); HIP if the array's
+ * address cannot be obtained.
+ */
+size_t rattn_decode_paged_noalloc_max_scratch_bytes(void);
+
+int rattn_decode_paged_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                               const int* block_table, const int* ctx_lens, const int* windows,
+                               const float* bias, void* out, float* lse, int B, int n_q, int Hq,
+                               int Hkv, int head_dim, int block_size, int R, int num_blocks,
+                               int max_blocks_per_seq, int max_ctx_len, int num_splits,
+                               void* stream);
 
 /* Message describing the last non-OK status returned on this thread ("" if none). */
 const char* rattn_last_error(void);

@@ -25,11 +25,12 @@ LIB_PATH = os.path.join(_HERE, "librattn.so")
 
 RATTN_OK, RATTN_ERR_INVALID_ARG, RATTN_ERR_UNSUPPORTED, RATTN_ERR_WORKSPACE, RATTN_ERR_HIP = 0, 1, 2, 3, 4
 RATTN_BF16, RATTN_FP32 = 0, 1
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 EXPORTED = ("rattn_prefill_workspace_bytes", "rattn_prefill", "rattn_prefill_paged", "rattn_kv_sconv_write",
             "rattn_prefill_backward_workspace_bytes", "rattn_prefill_backward",
-            "rattn_decode_num_splits", "rattn_decode_workspace_bytes", "rattn_decode_paged", "rattn_last_error",
+            "rattn_decode_num_splits", "rattn_decode_workspace_bytes", "rattn_decode_paged",
+            "rattn_decode_paged_noalloc_max_scratch_bytes", "rattn_decode_paged_noalloc", "rattn_last_error",
             "rattn_abi_version")
 
 _lib = None
@@ -70,6 +71,10 @@ def load(path: Optional[str] = None):
     lib.rattn_decode_workspace_bytes.argtypes = [i32] * 6
     lib.rattn_decode_paged.restype = i32
     lib.rattn_decode_paged.argtypes = [vp] * 9 + [i32] * 11 + [vp, sz, vp]
+    lib.rattn_decode_paged_noalloc_max_scratch_bytes.restype = sz
+    lib.rattn_decode_paged_noalloc_max_scratch_bytes.argtypes = []
+    lib.rattn_decode_paged_noalloc.restype = i32
+    lib.rattn_decode_paged_noalloc.argtypes = [vp] * 9 + [i32] * 11 + [vp]
     lib.rattn_last_error.restype = ctypes.c_char_p
     lib.rattn_last_error.argtypes = []
     lib.rattn_abi_version.restype = i32
@@ -225,6 +230,24 @@ def rattn_decode_paged(q, k_cache, v_cache, block_table, ctx_lens, windows, bias
                                      _ptr(windows), _ptr(bias), _ptr(out), _ptr(lse), B, n_q, Hq, Hkv, D, bs, R,
                                      num_blocks, mb, int(max_ctx_len), int(num_splits), _ptr(workspace), ws_bytes,
                                      _stream(stream)))
+
+
+def rattn_decode_paged_noalloc_max_scratch_bytes() -> int:
+    return load().rattn_decode_paged_noalloc_max_scratch_bytes()
+
+
+def rattn_decode_paged_noalloc(q, k_cache, v_cache, block_table, ctx_lens, windows, bias, out, lse,
+                               max_ctx_len: int, num_splits: int = 0, stream=None) -> None:
+    """rattn_decode_paged without a workspace: the split partials go to the library's static
+    per-device scratch (calls that overlap on one device race); same arguments otherwise."""
+    B, n_q, Hq, D = q.shape
+    num_blocks, bs, Hkv = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+    mb = block_table.shape[1]
+    R = bias.shape[1]
+    _check(load().rattn_decode_paged_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                                             _ptr(ctx_lens), _ptr(windows), _ptr(bias), _ptr(out), _ptr(lse), B,
+                                             n_q, Hq, Hkv, D, bs, R, num_blocks, mb, int(max_ctx_len),
+                                             int(num_splits), _stream(stream)))
 
 
 # ---- conveniences that allocate the outputs (torch device memory) and call the above ----

@@ -562,39 +562,53 @@ size_t rattn_decode_workspace_bytes(int B, int n_q, int Hq, int Hkv, int max_ctx
   return pl.total;
 }
 
-int rattn_decode_paged(const void* q, const void* k_cache, const void* v_cache, const int* block_table,
-                       const int* ctx_lens, const int* windows, const float* bias, void* out, float* lse,
-                       int B, int n_q, int Hq, int Hkv, int head_dim, int block_size, int R, int num_blocks,
-                       int max_blocks_per_seq, int max_ctx_len, int num_splits, void* workspace,
-                       size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The paged decode of both entry points.  from_scratch: the workspace is the device's static
+// scratch (looked up after validation), workspace / workspace_bytes are ignored.
+int decode_paged(const char* fn, const void* q, const void* k_cache, const void* v_cache, const int* block_table,
+                 const int* ctx_lens, const int* windows, const float* bias, void* out, float* lse, int B, int n_q,
+                 int Hq, int Hkv, int head_dim, int block_size, int R, int num_blocks, int max_blocks_per_seq,
+                 int max_ctx_len, int num_splits, void* workspace, size_t workspace_bytes, bool from_scratch,
+                 void* stream) {
   if (B < 0 || Hq < 0 || Hkv < 0 || num_blocks < 0 || max_blocks_per_seq < 0 || max_ctx_len < 0 || num_splits < 0)
-    return fail(RATTN_ERR_INVALID_ARG, "rattn_decode_paged: negative size");
-  if (head_dim != 128) return fail(RATTN_ERR_UNSUPPORTED, "rattn_decode_paged: head_dim %d (only 128)", head_dim);
-  if (block_size != 128)
-    return fail(RATTN_ERR_UNSUPPORTED, "rattn_decode_paged: block_size %d (only 128)", block_size);
-  if (n_q < 1) return fail(RATTN_ERR_INVALID_ARG, "rattn_decode_paged: n_q=%d < 1", n_q);
+    return fail(RATTN_ERR_INVALID_ARG, "%s: negative size", fn);
+  if (head_dim != 128) return fail(RATTN_ERR_UNSUPPORTED, "%s: head_dim %d (only 128)", fn, head_dim);
+  if (block_size != 128) return fail(RATTN_ERR_UNSUPPORTED, "%s: block_size %d (only 128)", fn, block_size);
+  if (n_q < 1) return fail(RATTN_ERR_INVALID_ARG, "%s: n_q=%d < 1", fn, n_q);
   if (n_q > rattn::kDecodeMaxRows)
-    return fail(RATTN_ERR_UNSUPPORTED, "rattn_decode_paged: n_q=%d > %d", n_q, rattn::kDecodeMaxRows);
+    return fail(RATTN_ERR_UNSUPPORTED, "%s: n_q=%d > %d", fn, n_q, rattn::kDecodeMaxRows);
   if (B == 0) return ok();
   if (!q || !k_cache || !v_cache || !block_table || !ctx_lens || !bias || !out)
-    return fail(RATTN_ERR_INVALID_ARG, "rattn_decode_paged: null pointer argument");
+    return fail(RATTN_ERR_INVALID_ARG, "%s: null pointer argument", fn);
   if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0)
-    return fail(RATTN_ERR_INVALID_ARG, "rattn_decode_paged: Hq=%d must be a positive multiple of Hkv=%d", Hq, Hkv);
-  if (R < 1) return fail(RATTN_ERR_INVALID_ARG, "rattn_decode_paged: R=%d < 1", R);
+    return fail(RATTN_ERR_INVALID_ARG, "%s: Hq=%d must be a positive multiple of Hkv=%d", fn, Hq, Hkv);
+  if (R < 1) return fail(RATTN_ERR_INVALID_ARG, "%s: R=%d < 1", fn, R);
   if (num_blocks < 1 || max_blocks_per_seq < 1)
-    return fail(RATTN_ERR_INVALID_ARG, "rattn_decode_paged: num_blocks=%d, max_blocks_per_seq=%d", num_blocks,
+    return fail(RATTN_ERR_INVALID_ARG, "%s: num_blocks=%d, max_blocks_per_seq=%d", fn, num_blocks,
                 max_blocks_per_seq);
-  if (max_ctx_len < n_q)
-    return fail(RATTN_ERR_INVALID_ARG, "rattn_decode_paged: max_ctx_len=%d < n_q=%d", max_ctx_len, n_q);
+  if (max_ctx_len < n_q) return fail(RATTN_ERR_INVALID_ARG, "%s: max_ctx_len=%d < n_q=%d", fn, max_ctx_len, n_q);
   if ((long long)max_ctx_len > 128LL * max_blocks_per_seq || max_ctx_len > kMaxPosition)
-    return fail(RATTN_ERR_INVALID_ARG, "rattn_decode_paged: max_ctx_len=%d exceeds the block table (%d blocks)",
-                max_ctx_len, max_blocks_per_seq);
+    return fail(RATTN_ERR_INVALID_ARG, "%s: max_ctx_len=%d exceeds the block table (%d blocks)", fn, max_ctx_len,
+                max_blocks_per_seq);
   DecodePlan pl;
   if (!plan_decode(B, n_q, Hq, Hkv, max_ctx_len, max_blocks_per_seq, num_splits, &pl))
-    return fail(RATTN_ERR_INVALID_ARG, "rattn_decode_paged: problem too large for one launch");
+    return fail(RATTN_ERR_INVALID_ARG, "%s: problem too large for one launch", fn);
+  if (from_scratch) {
+    if (pl.total > rattn::kDecodeScratchBytes)
+      return fail(RATTN_ERR_WORKSPACE,
+                  "%s: these sizes need %zu bytes of split scratch, more than the static %zu; use "
+                  "rattn_decode_paged with a workspace, or fewer sequences or splits per call",
+                  fn, pl.total, rattn::kDecodeScratchBytes);
+    const hipError_t e = rattn::decode_scratch(&workspace);
+    if (e != hipSuccess) return fail(RATTN_ERR_HIP, "%s: scratch address: %s", fn, hipGetErrorString(e));
+    workspace_bytes = rattn::kDecodeScratchBytes;
+  }
   if (!workspace || workspace_bytes < pl.total)
-    return fail(RATTN_ERR_WORKSPACE, "rattn_decode_paged: workspace %zu bytes at %p, need %zu", workspace_bytes,
-                workspace, pl.total);
+    return fail(RATTN_ERR_WORKSPACE, "%s: workspace %zu bytes at %p, need %zu", fn, workspace_bytes, workspace,
+                pl.total);
 
   rattn::DecodeParams p;
   p.k_cache = (const uint16_t*)k_cache;
@@ -628,9 +642,34 @@ int rattn_decode_paged(const void* q, const void* k_cache, const void* v_cache, 
     p.ctx_lens = ctx_lens + b0;
     p.windows = windows ? windows + b0 : nullptr;
     hipError_t e = rattn::launch_decode(p, (hipStream_t)stream);
-    if (e != hipSuccess) return fail(RATTN_ERR_HIP, "rattn_decode_paged: launch failed: %s", hipGetErrorString(e));
+    if (e != hipSuccess) return fail(RATTN_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   }
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int rattn_decode_paged(const void* q, const void* k_cache, const void* v_cache, const int* block_table,
+                       const int* ctx_lens, const int* windows, const float* bias, void* out, float* lse,
+                       int B, int n_q, int Hq, int Hkv, int head_dim, int block_size, int R, int num_blocks,
+                       int max_blocks_per_seq, int max_ctx_len, int num_splits, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  return decode_paged("rattn_decode_paged", q, k_cache, v_cache, block_table, ctx_lens, windows, bias, out, lse, B,
+                      n_q, Hq, Hkv, head_dim, block_size, R, num_blocks, max_blocks_per_seq, max_ctx_len, num_splits,
+                      workspace, workspace_bytes, false, stream);
+}
+
+size_t rattn_decode_paged_noalloc_max_scratch_bytes(void) { return rattn::kDecodeScratchBytes; }
+
+int rattn_decode_paged_noalloc(const void* q, const void* k_cache, const void* v_cache, const int* block_table,
+                               const int* ctx_lens, const int* windows, const float* bias, void* out, float* lse,
+                               int B, int n_q, int Hq, int Hkv, int head_dim, int block_size, int R, int num_blocks,
+                               int max_blocks_per_seq, int max_ctx_len, int num_splits, void* stream) {
+  return decode_paged("rattn_decode_paged_noalloc", q, k_cache, v_cache, block_table, ctx_lens, windows, bias, out,
+                      lse, B, n_q, Hq, Hkv, head_dim, block_size, R, num_blocks, max_blocks_per_seq, max_ctx_len,
+                      num_splits, nullptr, 0, true, stream);
 }
 
 }  // extern "C"

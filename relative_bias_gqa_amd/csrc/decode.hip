@@ -31,9 +31,37 @@
 #include "device_common.hpp"
 #include "launch.hpp"
 
+#include <atomic>
 #include <type_traits>
 
 namespace rattn {
+
+// Scratch of the allocation-free decode entry point: the split partials that the allocating
+// entry point keeps in its caller's workspace.  Each device the library runs on holds its
+// own copy for the life of the process; host code reaches it only through the address
+// hipGetSymbolAddress returns for the current device (decode_scratch), never by this name.
+__device__ __attribute__((aligned(256))) unsigned char scratch[kDecodeScratchBytes];
+
+hipError_t decode_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void*> addr[kMaxDevices];
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* a = addr[dev].load(std::memory_order_acquire);
+  if (a == nullptr) {
+    // once per device, with that device current (two threads may both ask: the runtime
+    // returns the same address to both)
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (a == nullptr) return hipErrorInvalidSymbol;
+    addr[dev].store(a, std::memory_order_release);
+  }
+  *ptr = a;
+  return hipSuccess;
+}
+
 namespace {
 
 constexpr int kThreads = 256;  // merge kernel: 4 waves

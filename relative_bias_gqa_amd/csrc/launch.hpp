@@ -100,6 +100,11 @@ struct DecodeParams {
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 
+// Static device scratch of the allocation-free decode (per device, kDecodeScratchBytes):
+// its address on the current device, looked up once per device.
+constexpr size_t kDecodeScratchBytes = (size_t)64 << 20;
+hipError_t decode_scratch(void** ptr);
+
 // Short convolution of new K/V tokens written into the paged caches.
 struct SconvParams {
   const uint16_t* k_new;   // [T, Hkv, 128] bf16, packed new tokens (rows cu[b] .. cu[b + 1] - 1)

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.rattn_abi_version() == rb.ABI_VERSION == 6
+    assert lib.rattn_abi_version() == rb.ABI_VERSION == 7
 
 
 def _prefill(lib, **kw):
@@ -109,6 +109,42 @@ def test_decode_validation(lib, kw, status, needle):
 
 def test_decode_empty_is_noop(lib):
     assert _decode(lib, B=0, q=None, kc=None) == rb.RATTN_OK
+
+
+def _decode_noalloc(lib, **kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, ctx=FAKE, win=None, bias=FAKE, out=FAKE, lse=None, B=2, n_q=1,
+             Hq=16, Hkv=2, D=128, bs=128, R=8, nb=4, mb=2, max_ctx=200, ns=0, stream=None)
+    a.update(kw)
+    return lib.rattn_decode_paged_noalloc(a["q"], a["kc"], a["vc"], a["bt"], a["ctx"], a["win"], a["bias"],
+                                          a["out"], a["lse"], a["B"], a["n_q"], a["Hq"], a["Hkv"], a["D"], a["bs"],
+                                          a["R"], a["nb"], a["mb"], a["max_ctx"], a["ns"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(q=None), rb.RATTN_ERR_INVALID_ARG, "null"),
+    (dict(Hq=15), rb.RATTN_ERR_INVALID_ARG, "multiple"),
+    (dict(n_q=0), rb.RATTN_ERR_INVALID_ARG, "n_q"),
+    (dict(D=96), rb.RATTN_ERR_UNSUPPORTED, "head_dim"),
+    (dict(max_ctx=257, mb=2), rb.RATTN_ERR_INVALID_ARG, "block table"),
+    # 2048 sequences of 9 queries over 64/8 heads need far more split scratch than the
+    # static array holds: rejected on the host, before any device call
+    (dict(B=2048, n_q=9, Hq=64, Hkv=8, max_ctx=4096, mb=32, nb=64), rb.RATTN_ERR_WORKSPACE, "static"),
+    (dict(ns=100000, B=64, n_q=9), rb.RATTN_ERR_WORKSPACE, "static"),
+])
+def test_decode_noalloc_validation(lib, kw, status, needle):
+    assert _decode_noalloc(lib, **kw) == status
+    assert needle in rb.rattn_last_error()
+
+
+def test_decode_noalloc_limit(lib):
+    """The static scratch is 64 MiB, and the limit check uses the same plan as the workspace
+    query: the batch-64 decode and the 1M-token verify fit, a plan one byte larger would not."""
+    limit = lib.rattn_decode_paged_noalloc_max_scratch_bytes()
+    assert limit == 64 << 20
+    assert rb.rattn_decode_workspace_bytes(64, 1, 16, 2, 131072, 0) <= limit
+    assert rb.rattn_decode_workspace_bytes(1, 9, 16, 2, 1 << 20, 0) <= limit
+    assert rb.rattn_decode_workspace_bytes(2048, 9, 64, 8, 4096, 0) > limit
+    assert _decode_noalloc(lib, B=0, q=None, kc=None) == rb.RATTN_OK
 
 
 def _prefill_paged(lib, **kw):
