@@ -1,18 +1,22 @@
 """Throughput of relative-bias GQA attention on one MI355X.
 
 One step is one call of the hot path on one batch of seeded synthetic input that is
-already resident in HBM.  The headline line is the sliding-window prefill (batch 1,
-8192 tokens, 16 query / 2 KV heads, d 128, window 4096, bias table 4096, bf16): attention
-TFLOP/s counted over the visible (query, key) pairs only.  The same JSON line carries the
-other workloads (fp32 tiny prefill, 32k chunked prefill, batch-64 paged decode, 1M-token
-9-query verify), each timed the same way: prefill in TFLOP/s against the bf16 MFMA peak,
-decode in KV GB/s (bytes the method must move) against the HBM peak.
+already resident in HBM.  The headline line is the full-attention chunked prefill, the
+largest single-GPU workload (batch 1, an 8192-token chunk at positions 24576..32767 over
+32768 keys, 16 query / 2 KV heads, d 128, bias table 8192, bf16): attention TFLOP/s counted
+over the visible (query, key) pairs only.  The same JSON line carries the other workloads
+(fp32 tiny prefill, 8K sliding-window prefill, batch-64 paged decode, 1M-token 9-query
+verify, paged prefill, K/V short convolution, backward, token-dependent bias), each timed the
+same way: prefill in TFLOP/s against the bf16 MFMA peak, decode in KV GB/s (bytes the method
+must move) against the HBM peak, and practical ceilings measured in the same process (a
+large bf16 GEMM through torch, a device copy and a read stream).
 
 Timing: the step repeated, untimed, for at least S ms of wall clock (the GPU raises its
 clock over its first tens of milliseconds under load; S 0 skips this), then W untimed
 warm-up steps, then exactly K steps between two hipEvents recorded on the stream the
 kernels are launched on, with a device synchronisation on both sides.
-The CPU oracle (fp64) is timed on a bounded sample of the headline workload.
+The CPU oracle (fp64) is timed on a bounded sample of the headline workload (every n-th
+query row, about 10-20 s of host time).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-ms S] [--workloads a,b,...]
                        [--no-cpu-baseline] [--only HEADLINE]
@@ -36,9 +40,9 @@ if ROOT not in sys.path:
 METRIC = "prefill attention TFLOP/s (% bf16 MFMA peak); decode KV GB/s (% HBM peak)"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
-HEADLINE = "swa_prefill_8k"
+HEADLINE = "chunked_prefill_32k"
 ALL_WORKLOADS = ["tiny_prefill_fp32", "swa_prefill_8k", "chunked_prefill_32k", "paged_decode_b64", "mtp_verify_1m",
-                 "paged_prefill_b4", "kv_sconv_32k", "swa_prefill_8k_bwd"]
+                 "paged_prefill_b4", "kv_sconv_32k", "swa_prefill_8k_bwd", "swa_prefill_8k_tokbias"]
 HEAD_DIM = 128
 KERNEL_SOURCES = {
     "prefill": ["relative_bias_gqa_amd/csrc/prefill.hip", "relative_bias_gqa_amd/csrc/prefill_bf16.hip",
@@ -320,8 +324,35 @@ class BackwardRun:
         del self.dbias, self.ws
 
 
+class TokBiasRun(PrefillRun):
+    """Prefill with a token-dependent table (bf16 [B, Lq, Hq, R], one per query row)."""
+
+    def __init__(self, name, torch, rb, synth, dev):
+        self.name = name
+        tc = synth.WORKLOAD_FNS[name]()
+        c = tc.fwd
+        self.case = c
+        self.q, self.k, self.v, self.bias = dev(c.q), dev(c.k), dev(c.v), dev(tc.bias_tok)
+        self.out = torch.empty_like(self.q)
+        self.lse = torch.empty(self.q.shape[:3], dtype=torch.float32, device=self.q.device)
+        self.rb = rb
+        self.work = prefill_flops(c.B, c.Lq, c.Lk, c.Hq, c.window)
+        self.unit, self.peak, self.bound = "TFLOP/s", PEAK_BF16_TFLOPS, "mfma"
+        nbytes = rb.rattn_prefill_workspace_bytes(c.B, c.Lq, c.Lk, c.Hq, c.Hkv, c.window, rb.RATTN_BF16)
+        self.ws = torch.zeros(nbytes, dtype=torch.uint8, device=self.q.device) if nbytes else None
+        self.config = {"workload": name, "batch": c.B, "q_len": c.Lq, "kv_len": c.Lk, "q_heads": c.Hq,
+                       "kv_heads": c.Hkv, "head_dim": HEAD_DIM, "window": c.window, "bias_len": tc.R,
+                       "bias": "token-dependent bf16 [B, Lq, Hq, R]", "dtype": "bf16",
+                       "kv_split_workspace_bytes": nbytes}
+        self.dtype = "bf16"
+
+    def step(self, stream):
+        self.rb.rattn_prefill_tokbias(self.q, self.k, self.v, self.bias, self.out, self.lse, self.case.window, 0,
+                                      self.ws, stream)
+
+
 RUN_CLASSES = {"paged_decode_b64": DecodeRun, "mtp_verify_1m": DecodeRun, "paged_prefill_b4": PagedPrefillRun,
-               "kv_sconv_32k": SconvRun, "swa_prefill_8k_bwd": BackwardRun}
+               "kv_sconv_32k": SconvRun, "swa_prefill_8k_bwd": BackwardRun, "swa_prefill_8k_tokbias": TokBiasRun}
 
 
 def settle_clock(run, torch, stream, ms: float) -> int:
@@ -364,6 +395,70 @@ def result_of(run, sec: float):
 # ---------------------------------------------------------------------------------------
 # CPU oracle baseline on a bounded sample of the headline workload
 # ---------------------------------------------------------------------------------------
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def practical_ceilings(torch):
+    """Context for the roofline, measured in this process: a large bf16 GEMM through torch
+    (hipBLASLt), a device-to-device copy (read + write) and a read stream (sum of a large
+    tensor), each timed with hipEvents after a warm-up."""
+    dev = "cuda:0"
+    res = {}
+    n = 8192
+    a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    reps = 20
+    for _ in range(reps):
+        torch.matmul(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) / 1e3 / reps
+    res["bf16_gemm_tflops"] = round(2.0 * n ** 3 / sec / 1e12, 1)
+    res["bf16_gemm_shape"] = f"{n}x{n}x{n}"
+    del a, b
+    nbytes = 2 << 30
+    src = torch.empty(nbytes // 4, device=dev, dtype=torch.float32).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0.record()
+    reps = 10
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    res["hbm_copy_gbs"] = round(2.0 * nbytes / (e0.elapsed_time(e1) / 1e3 / reps) / 1e9, 1)
+    out = torch.empty((), device=dev, dtype=torch.float32)
+    for _ in range(2):
+        torch.sum(src, out=out)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        torch.sum(src, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    res["hbm_read_gbs"] = round(nbytes / (e0.elapsed_time(e1) / 1e3 / reps) / 1e9, 1)
+    res["note"] = "practical ceilings for context (torch matmul bf16, device copy counted as read + write, " \
+                  "torch.sum over 2 GiB); the roofline peaks are the published ones"
+    del src, dst
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(case, stride: int):
     import oracle
     threads = max(1, min(16, len(os.sched_getaffinity(0))))
@@ -375,8 +470,9 @@ def cpu_baseline(case, stride: int):
                             num_threads=threads)
     sec = time.perf_counter() - t0
     return {"value": round(flops / sec / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "cpu": cpu_model(),
             "sample": f"{case.name}: every {stride}th query row ({len(rows)} of {case.Lq} rows x {case.Hq} heads, "
-                      f"{flops:.4e} algorithmic flop) in {sec:.2f} s, fp64"}
+                      f"{flops:.4e} algorithmic flop) in {sec:.2f} s, fp64 on {threads} threads"}
 
 
 def main(argv=None) -> int:
@@ -390,7 +486,8 @@ def main(argv=None) -> int:
                     help="comma-separated workloads to time besides the headline")
     ap.add_argument("--only-headline", action="store_true", help="time only the headline workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-stride", type=int, default=1, help="oracle sample: every n-th query row")
+    ap.add_argument("--cpu-stride", type=int, default=4, help="oracle sample: every n-th query row")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the GEMM / copy ceiling measurements")
     ap.add_argument("--only", default=None,
                     help="time just this workload and print its own result line (for profiler runs)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -490,6 +587,9 @@ def main(argv=None) -> int:
         line["cpu_baseline"] = cpu_baseline(hcase, args.cpu_stride)
     else:
         line["cpu_baseline"] = None
+    if not args.no_ceilings:
+        log("[bench] practical ceilings: bf16 GEMM, device copy, read stream")
+        line["practical_ceilings"] = practical_ceilings(torch)
     line["workloads"] = [results[n] for n in names if n != HEADLINE]
     print(json.dumps(line), flush=True)
     return 0

@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define RATTN_ABI_VERSION 7
+#define RATTN_ABI_VERSION 8
 
 enum rattn_status {
   RATTN_OK = 0,
@@ -110,6 +110,29 @@ int rattn_prefill(const void* q, const void* k, const void* v, const float* bias
                   float* lse, int B, int Lq, int Lk, int Hq, int Hkv, int head_dim, int R,
                   int window, int dtype, int kv_splits, void* workspace, size_t workspace_bytes,
                   void* stream);
+
+/*
+ * Prefill / chunked prefill with a token-dependent relative-bias table.  The recipes page
+ * "thinkingmachines/Inkling" keeps the "qkvr" linears in BF16 (Variants) and names a
+ * sheared-bias attention kernel for relative attention (Performance); read here as the
+ * projection producing, for every query token t, its own table r_t (bf16), so that
+ *     logit[t, j] = (q_t . k_j) / sqrt(128) + r_t[h, min(p - j, R - 1)]
+ * for the query at position p = Lk - Lq + t.  Everything else (positions, causal / window
+ * visibility, GQA mapping, outputs, workspace and split plan) is that of rattn_prefill with
+ * dtype RATTN_BF16.
+ *
+ *   bias_tok [B, Lq, Hq, R]  bf16  device, read; row (b, t, h) is r_t[h, :] of query t;
+ *            4-byte aligned; R >= 4.  Entries at distances that no visible key of the row
+ *            has (d > p, or d >= window) are never used and may hold anything (NaN
+ *            included); the clamp entry r_t[h, R - 1] is used when the row sees a key at
+ *            distance >= R - 1.
+ *
+ * Status: as rattn_prefill; INVALID_ARG also for a misaligned bias_tok, UNSUPPORTED for R < 4.
+ */
+int rattn_prefill_tokbias(const void* q, const void* k, const void* v, const void* bias_tok,
+                          void* out, float* lse, int B, int Lq, int Lk, int Hq, int Hkv,
+                          int head_dim, int R, int window, int kv_splits, void* workspace,
+                          size_t workspace_bytes, void* stream);
 
 /*
  * Chunked prefill against a paged KV cache (prefix caching: vLLM recipes page

@@ -71,17 +71,23 @@ int rattn_ref_cpu_tokbias(const void* q, const void* k, const void* v, const int
  * q, dout [B, Lq, Hq, head_dim], k, v [B, Lk, Hkv, head_dim] (dtype); bias [Hq, R] double;
  * dq [B, Lq, Hq, head_dim], dk, dv [B, Lk, Hkv, head_dim], dbias [Hq, R] double, written.
  *
+ * out: NULL, or a forward output [B, Lq, Hq, head_dim] (dtype): then D = sum_e dout_e out_e
+ * per row, the row sum a backward implementation takes from the forward's (rounded) output,
+ * in place of sum_j P_j dP_j.
+ *
  * Optional magnitude sums (NULL to skip), the same sums with every term replaced by its
- * absolute value and dS by dS_abs = P (|dP - D| + D_abs), D_abs = sum_j P_j sum_e |dout_e|
- * |v_j,e| (the size of D's terms): dq_abs, dk_abs, dv_abs (dv_abs = P^T |dout|),
- * dbias_abs.  They bound rounding errors of an implementation elementwise.
+ * absolute value and dS by dS_abs = P_j (|dP_j - D| + w (a_j + D_abs)), where
+ * a_j = sum_e |dout_e v_j,e| is the size of dP_j's terms, D_abs the size of D's terms
+ * (sum_j P_j a_j, or sum_e |dout_e out_e| with out) and w = abs_weight: dq_abs, dk_abs,
+ * dv_abs (dv_abs = P^T |dout|), dbias_abs.  They bound rounding errors of an
+ * implementation element by element.
  * Returns 0 on success, 1 on an invalid argument (nothing written).
  */
 int rattn_ref_cpu_backward(const void* q, const void* k, const void* v, const void* dout,
-                           const double* bias, double* dq, double* dk, double* dv,
+                           const void* out, const double* bias, double* dq, double* dk, double* dv,
                            double* dbias, double* dq_abs, double* dk_abs, double* dv_abs,
-                           double* dbias_abs, int B, int Lq, int Lk, int Hq, int Hkv,
-                           int head_dim, int R, int window, int dtype, int num_threads);
+                           double* dbias_abs, double abs_weight, int B, int Lq, int Lk, int Hq,
+                           int Hkv, int head_dim, int R, int window, int dtype, int num_threads);
 
 int rattn_oracle_version(void);
 

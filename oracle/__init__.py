@@ -51,7 +51,7 @@ def load_library(path: str):
         lib.rattn_ref_cpu_tokbias.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int] * 11
     if hasattr(lib, "rattn_ref_cpu_backward"):
         lib.rattn_ref_cpu_backward.restype = ctypes.c_int
-        lib.rattn_ref_cpu_backward.argtypes = [ctypes.c_void_p] * 13 + [ctypes.c_int] * 10
+        lib.rattn_ref_cpu_backward.argtypes = [ctypes.c_void_p] * 14 + [ctypes.c_double] + [ctypes.c_int] * 10
     return lib
 
 
@@ -210,25 +210,29 @@ def ref_prefill_tokbias_rows(q, k, v, bias_tok, window: int, rows: Sequence[Tupl
     return np.stack(outs), np.stack(lses)
 
 
-def ref_backward(q, k, v, bias, dout, window: int = 0, want_abs: bool = True, num_threads: int = 0, lib=None):
+def ref_backward(q, k, v, bias, dout, window: int = 0, want_abs: bool = True, num_threads: int = 0, lib=None,
+                 out=None, abs_weight: float = 1.0):
     """Gradients of a prefill (C oracle, one query row at a time in double).
 
     q, dout [B, Lq, Hq, D]; k, v [B, Lk, Hkv, D] (uint16 bf16 bits, float32 or float64, one
-    dtype); bias [Hq, R].  Returns (dq, dk, dv, dbias) and, with want_abs, the magnitude sums
-    (dq_abs, dk_abs, dv_abs, dbias_abs) as a second tuple (else None); all float64."""
+    dtype); bias [Hq, R]; out: None (D = sum_j P_j dP_j) or a forward output like q, same
+    dtype (D = rowsum(dout * out)).  Returns (dq, dk, dv, dbias) and, with want_abs, the
+    magnitude sums (dq_abs, dk_abs, dv_abs, dbias_abs) as a second tuple (else None), with
+    dS_abs = P (|dP - D| + abs_weight (a_j + D_abs)); all float64."""
     lib = lib if lib is not None else _load()
     dt = _dtype_of(q)
-    if any(_dtype_of(a) != dt for a in (k, v, dout)):
-        raise TypeError("q, k, v, dout must share a dtype")
+    if any(_dtype_of(a) != dt for a in (k, v, dout) + ((out,) if out is not None else ())):
+        raise TypeError("q, k, v, dout (and out) must share a dtype")
     q, k, v, dout = (np.ascontiguousarray(a) for a in (q, k, v, dout))
+    out = None if out is None else np.ascontiguousarray(out)
     B, Lq, Hq, D = q.shape
     Lk, Hkv = k.shape[1], k.shape[2]
     bias64 = _bias_f64(bias)
     R = bias64.shape[1]
     grads = [np.empty(q.shape), np.empty(k.shape), np.empty(k.shape), np.empty((Hq, R))]
     absums = [np.empty(q.shape), np.empty(k.shape), np.empty(k.shape), np.empty((Hq, R))] if want_abs else [None] * 4
-    rc = lib.rattn_ref_cpu_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(bias64),
-                                    *[_ptr(g) for g in grads], *[_ptr(a) for a in absums],
+    rc = lib.rattn_ref_cpu_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(out), _ptr(bias64),
+                                    *[_ptr(g) for g in grads], *[_ptr(a) for a in absums], float(abs_weight),
                                     B, Lq, Lk, Hq, Hkv, D, R, int(window), DTYPE_CODES[dt], int(num_threads))
     if rc != 0:
         raise ValueError("oracle rejected its arguments")

@@ -34,17 +34,22 @@ def _f64(a: np.ndarray) -> np.ndarray:
     return bf16_to_f64(a) if a.dtype == np.uint16 else a.astype(np.float64)
 
 
-def prefill_backward(q, k, v, bias, dout, window: int = 0):
+def prefill_backward(q, k, v, bias, dout, window: int = 0, out=None, abs_weight: float = 1.0):
     """Gradients of a prefill (every sequence has Lk keys; query t at Lk - Lq + t).
 
     q [B, Lq, Hq, D], k and v [B, Lk, Hkv, D], dout [B, Lq, Hq, D]: uint16 (bf16 bits),
     float32 or float64; bias [Hq, R].  Returns float64 arrays
     (dq [B, Lq, Hq, D], dk [B, Lk, Hkv, D], dv [B, Lk, Hkv, D], dbias [Hq, R], absums) with
     absums = (dq_abs, dk_abs, dv_abs, dbias_abs): the same sums with every term taken by
-    absolute value and dS replaced by dS_abs = P * (|dP - D| + D_abs), where D_abs =
-    rowsum(P * (|dO| |V|^T)) is the size of D's terms.  They bound an implementation's
-    rounding errors element by element (the gradients are sums whose terms cancel)."""
+    absolute value and dS replaced by dS_abs = P * (|dP - D| + w (A + D_abs)), where
+    A = |dO| |V|^T holds the sizes of dP's terms, D_abs = rowsum(P * A) the size of D's
+    terms and w = abs_weight.  They bound an implementation's rounding errors element by
+    element (the gradients are sums whose terms cancel).
+    out: None, or a forward output like q: then D = rowsum(dO * out) (the row sum a
+    backward implementation takes from the forward's rounded output), D_abs =
+    rowsum(|dO * out|)."""
     Q, K, V, dO = _f64(q), _f64(k), _f64(v), _f64(dout)
+    O = None if out is None else _f64(out)
     r = np.asarray(bias, dtype=np.float64)
     B, Lq, Hq, D = Q.shape
     Lk, Hkv = K.shape[1], K.shape[2]
@@ -73,15 +78,20 @@ def prefill_backward(q, k, v, bias, dout, window: int = 0):
             e = np.exp(s - s.max(axis=1, keepdims=True))
             P = e / e.sum(axis=1, keepdims=True)
             dP = dO[b, :, h] @ V[b, :, hk].T
-            Drow = (P * dP).sum(axis=1, keepdims=True)
+            A = np.abs(dO[b, :, h]) @ np.abs(V[b, :, hk]).T
+            if O is None:
+                Drow = (P * dP).sum(axis=1, keepdims=True)
+                Dabs = (P * A).sum(axis=1, keepdims=True)
+            else:
+                Drow = (dO[b, :, h] * O[b, :, h]).sum(axis=1, keepdims=True)
+                Dabs = np.abs(dO[b, :, h] * O[b, :, h]).sum(axis=1, keepdims=True)
             dS = P * (dP - Drow)
             dq[b, :, h] = dS @ K[b, :, hk] * scale
             dk[b, :, hk] += dS.T @ Q[b, :, h] * scale
             dv[b, :, hk] += P.T @ dO[b, :, h]
             dbias[h] += np.bincount(didx[vis], weights=dS[vis], minlength=R)
             # magnitude sums
-            Dabs = (P * (np.abs(dO[b, :, h]) @ np.abs(V[b, :, hk]).T)).sum(axis=1, keepdims=True)
-            dSa = P * (np.abs(dP - Drow) + Dabs)
+            dSa = P * (np.abs(dP - Drow) + abs_weight * (A + Dabs))
             dq_abs[b, :, h] = dSa @ np.abs(K[b, :, hk]) * scale
             dk_abs[b, :, hk] += dSa.T @ np.abs(Q[b, :, h]) * scale
             dv_abs[b, :, hk] += P.T @ np.abs(dO[b, :, h])

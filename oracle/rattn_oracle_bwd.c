@@ -51,14 +51,17 @@ static void widen(const void* src, size_t offset, int n, int dtype, double* dst)
  *     dbias[h, min(p - j, R - 1)] += dS_j,
  * one query row at a time, over its visible keys, in double.  Each query head accumulates
  * into its own dk, dv buffers (heads run in parallel); the heads of a KV head are summed
- * afterwards in head order.  The magnitude sums take every term by absolute value, with dS
- * replaced by P_j (|dP_j - D| + D_abs), D_abs = sum_j P_j sum_e |dout_e v_j,e|.
+ * afterwards in head order.  With a forward output `out` given, D is instead
+ * sum_e dout_e out_e, the row sum the backward kernels take from the forward's output.
+ * The magnitude sums take every term by absolute value, with dS replaced by
+ *     P_j (|dP_j - D| + w (a_j + D_abs)),   a_j = sum_e |dout_e v_j,e| (dP_j's terms),
+ * D_abs the size of D's terms (sum_j P_j a_j, or sum_e |dout_e out_e| with `out`).
  */
 int rattn_ref_cpu_backward(const void* q, const void* k, const void* v, const void* dout,
-                           const double* bias, double* dq, double* dk, double* dv,
+                           const void* out, const double* bias, double* dq, double* dk, double* dv,
                            double* dbias, double* dq_abs, double* dk_abs, double* dv_abs,
-                           double* dbias_abs, int B, int Lq, int Lk, int Hq, int Hkv,
-                           int head_dim, int R, int window, int dtype, int num_threads) {
+                           double* dbias_abs, double abs_weight, int B, int Lq, int Lk, int Hq,
+                           int Hkv, int head_dim, int R, int window, int dtype, int num_threads) {
   const int want_abs = dq_abs != NULL && dk_abs != NULL && dv_abs != NULL && dbias_abs != NULL;
   const size_t kv_elems = (size_t)B * Lk * Hkv * head_dim;
   const size_t head_kv = (size_t)B * Lk * head_dim; /* one query head's dk (or dv) buffer */
@@ -94,6 +97,7 @@ int rattn_ref_cpu_backward(const void* q, const void* k, const void* v, const vo
     const double scale = 1.0 / sqrt((double)head_dim);
     double* qrow = (double*)malloc(sizeof(double) * head_dim);
     double* grow = (double*)malloc(sizeof(double) * head_dim); /* dout row */
+    double* orow = (double*)malloc(sizeof(double) * head_dim); /* out row, when given */
     double* acc = (double*)malloc(sizeof(double) * head_dim);
     double* acca = (double*)malloc(sizeof(double) * head_dim);
     double* kb = (double*)malloc(sizeof(double) * ((size_t)Lk * head_dim + 1)); /* K of (b, kvh) */
@@ -131,6 +135,7 @@ int rattn_ref_cpu_backward(const void* q, const void* k, const void* v, const vo
           double m = -INFINITY, Z = 0.0, D = 0.0, Dabs = 0.0;
           widen(q, qoff, head_dim, dtype, qrow);
           widen(dout, qoff, head_dim, dtype, grow);
+          if (out != NULL) widen(out, qoff, head_dim, dtype, orow);
           /* logits and their maximum */
           for (j = lo; j <= p; ++j) {
             const double* kj = kb + (size_t)j * head_dim;
@@ -158,6 +163,13 @@ int rattn_ref_cpu_backward(const void* q, const void* k, const void* v, const vo
             D += s[j] * d1;
             Dabs += s[j] * d2;
           }
+          if (out != NULL) { /* D from the given forward output */
+            D = Dabs = 0.0;
+            for (e = 0; e < head_dim; ++e) {
+              D += grow[e] * orow[e];
+              Dabs += fabs(grow[e] * orow[e]);
+            }
+          }
           /* dS and the four gradients */
           for (e = 0; e < head_dim; ++e) acc[e] = acca[e] = 0.0;
           for (j = lo; j <= p; ++j) {
@@ -165,7 +177,7 @@ int rattn_ref_cpu_backward(const void* q, const void* k, const void* v, const vo
             const int dist = p - j;
             const int c = dist < R - 1 ? dist : R - 1;
             const double ds = s[j] * (dp[j] - D);
-            const double dsa = s[j] * (fabs(dp[j] - D) + Dabs);
+            const double dsa = s[j] * (fabs(dp[j] - D) + abs_weight * (av[j] + Dabs));
             double* dkj = dkq + ((size_t)b * Lk + j) * head_dim;
             double* dvj = dvq + ((size_t)b * Lk + j) * head_dim;
             for (e = 0; e < head_dim; ++e) {
@@ -194,6 +206,7 @@ int rattn_ref_cpu_backward(const void* q, const void* k, const void* v, const vo
     }
     free(qrow);
     free(grow);
+    free(orow);
     free(acc);
     free(acca);
     free(kb);

@@ -25,9 +25,9 @@ LIB_PATH = os.path.join(_HERE, "librattn.so")
 
 RATTN_OK, RATTN_ERR_INVALID_ARG, RATTN_ERR_UNSUPPORTED, RATTN_ERR_WORKSPACE, RATTN_ERR_HIP = 0, 1, 2, 3, 4
 RATTN_BF16, RATTN_FP32 = 0, 1
-ABI_VERSION = 7
+ABI_VERSION = 8
 
-EXPORTED = ("rattn_prefill_workspace_bytes", "rattn_prefill", "rattn_prefill_paged", "rattn_kv_sconv_write",
+EXPORTED = ("rattn_prefill_workspace_bytes", "rattn_prefill", "rattn_prefill_tokbias", "rattn_prefill_paged", "rattn_kv_sconv_write",
             "rattn_prefill_backward_workspace_bytes", "rattn_prefill_backward",
             "rattn_decode_num_splits", "rattn_decode_workspace_bytes", "rattn_decode_paged",
             "rattn_decode_paged_noalloc_max_scratch_bytes", "rattn_decode_paged_noalloc", "rattn_last_error",
@@ -57,6 +57,8 @@ def load(path: Optional[str] = None):
     lib.rattn_prefill_workspace_bytes.argtypes = [i32] * 8
     lib.rattn_prefill.restype = i32
     lib.rattn_prefill.argtypes = [vp] * 6 + [i32] * 10 + [vp, sz, vp]
+    lib.rattn_prefill_tokbias.restype = i32
+    lib.rattn_prefill_tokbias.argtypes = [vp] * 6 + [i32] * 9 + [vp, sz, vp]
     lib.rattn_prefill_paged.restype = i32
     lib.rattn_prefill_paged.argtypes = [vp] * 9 + [i32] * 11 + [vp, sz, vp]
     lib.rattn_kv_sconv_write.restype = i32
@@ -141,6 +143,21 @@ def rattn_prefill(q, k, v, bias, out, lse=None, window: int = 0, kv_splits: int 
     _check(load().rattn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(out), _ptr(lse),
                                 B, Lq, Lk, Hq, Hkv, D, R, int(window), _dtype_code(q), int(kv_splits),
                                 _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def rattn_prefill_tokbias(q, k, v, bias_tok, out, lse=None, window: int = 0, kv_splits: int = 0, workspace=None,
+                          stream=None) -> None:
+    """q [B,Lq,Hq,128], k/v [B,Lk,Hkv,128] bf16, bias_tok [B,Lq,Hq,R] bf16 (query t's own
+    table), out like q, lse [B,Lq,Hq] fp32 or None; workspace as for rattn_prefill."""
+    B, Lq, Hq, D = q.shape
+    Lk, Hkv = k.shape[1], k.shape[2]
+    R = bias_tok.shape[3]
+    if tuple(bias_tok.shape[:3]) != (B, Lq, Hq):
+        raise ValueError(f"bias_tok shape {tuple(bias_tok.shape)} does not match q {tuple(q.shape)}")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().rattn_prefill_tokbias(_ptr(q), _ptr(k), _ptr(v), _ptr(bias_tok), _ptr(out), _ptr(lse),
+                                        B, Lq, Lk, Hq, Hkv, D, R, int(window), int(kv_splits),
+                                        _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 PREFILL_PAGED_WORKSPACE_BYTES = 256
@@ -286,6 +303,19 @@ def prefill(q, k, v, bias, window: int = 0, want_lse: bool = True, kv_splits: in
                                           _dtype_code(q), kv_splits)
         workspace = prefill_workspace(n, q.device, stream) if n > 0 else None
     rattn_prefill(q, k, v, bias, out, lse, window, kv_splits, workspace, stream)
+    return out, lse
+
+
+def prefill_tokbias(q, k, v, bias_tok, window: int = 0, want_lse: bool = True, kv_splits: int = 0,
+                    workspace=None, stream=None) -> Tuple:
+    import torch
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if want_lse else None
+    if workspace is None:
+        n = rattn_prefill_workspace_bytes(q.shape[0], q.shape[1], k.shape[1], q.shape[2], k.shape[2], window,
+                                          RATTN_BF16, kv_splits)
+        workspace = prefill_workspace(n, q.device, stream) if n > 0 else None
+    rattn_prefill_tokbias(q, k, v, bias_tok, out, lse, window, kv_splits, workspace, stream)
     return out, lse
 
 

@@ -150,6 +150,7 @@ void prefill_shape(int B, int Lq, int Lk, int Hq, int Hkv, int window, rattn::Pr
   p->cu_q = nullptr;
   p->mbps = 0;
   p->num_blocks = 0;
+  p->bias_tok = nullptr;
 }
 
 // 64-key tiles walked by token tile `tile` (the same range as the kernel computes)
@@ -329,27 +330,40 @@ const char* rattn_last_error(void) { return g_err; }
 
 int rattn_abi_version(void) { return RATTN_ABI_VERSION; }
 
-int rattn_prefill(const void* q, const void* k, const void* v, const float* bias, void* out,
-                  float* lse, int B, int Lq, int Lk, int Hq, int Hkv, int head_dim, int R,
-                  int window, int dtype, int kv_splits, void* workspace, size_t workspace_bytes,
-                  void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Contiguous prefill with the per-head table (bias [Hq, R] fp32, bias_tok null) or the
+// token-dependent one (bias_tok [B, Lq, Hq, R] bf16, bias null).
+int prefill_contiguous(const char* fn, bool token, const void* q, const void* k, const void* v, const float* bias,
+                       const void* bias_tok, void* out, float* lse, int B, int Lq, int Lk, int Hq, int Hkv,
+                       int head_dim, int R, int window, int dtype, int kv_splits, void* workspace,
+                       size_t workspace_bytes, void* stream) {
   if (B < 0 || Lq < 0 || Lk < 0 || Hq < 0 || Hkv < 0)
-    return fail(RATTN_ERR_INVALID_ARG, "rattn_prefill: negative size (B=%d Lq=%d Lk=%d Hq=%d Hkv=%d)", B, Lq,
-                Lk, Hq, Hkv);
-  if (head_dim != 128) return fail(RATTN_ERR_UNSUPPORTED, "rattn_prefill: head_dim %d (only 128)", head_dim);
-  if (dtype != RATTN_BF16 && dtype != RATTN_FP32)
-    return fail(RATTN_ERR_UNSUPPORTED, "rattn_prefill: unknown dtype %d", dtype);
+    return fail(RATTN_ERR_INVALID_ARG, "%s: negative size (B=%d Lq=%d Lk=%d Hq=%d Hkv=%d)", fn, B, Lq, Lk, Hq,
+                Hkv);
+  if (head_dim != 128) return fail(RATTN_ERR_UNSUPPORTED, "%s: head_dim %d (only 128)", fn, head_dim);
+  if (dtype != RATTN_BF16 && dtype != RATTN_FP32) return fail(RATTN_ERR_UNSUPPORTED, "%s: unknown dtype %d", fn, dtype);
   if (kv_splits < 0 || kv_splits > rattn::kMaxPieces)
-    return fail(RATTN_ERR_INVALID_ARG, "rattn_prefill: kv_splits=%d outside 0..%d", kv_splits, rattn::kMaxPieces);
+    return fail(RATTN_ERR_INVALID_ARG, "%s: kv_splits=%d outside 0..%d", fn, kv_splits, rattn::kMaxPieces);
   if (B == 0 || Lq == 0) return ok();
-  if (!q || !k || !v || !bias || !out) return fail(RATTN_ERR_INVALID_ARG, "rattn_prefill: null pointer argument");
+  if (!q || !k || !v || !(token ? bias_tok : (const void*)bias) || !out)
+    return fail(RATTN_ERR_INVALID_ARG, "%s: null pointer argument", fn);
   if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0)
-    return fail(RATTN_ERR_INVALID_ARG, "rattn_prefill: Hq=%d must be a positive multiple of Hkv=%d", Hq, Hkv);
-  if (Lq > Lk) return fail(RATTN_ERR_INVALID_ARG, "rattn_prefill: Lq=%d > Lk=%d", Lq, Lk);
-  if (Lk > kMaxPosition) return fail(RATTN_ERR_INVALID_ARG, "rattn_prefill: Lk=%d too large", Lk);
-  if (R < 1) return fail(RATTN_ERR_INVALID_ARG, "rattn_prefill: R=%d < 1", R);
+    return fail(RATTN_ERR_INVALID_ARG, "%s: Hq=%d must be a positive multiple of Hkv=%d", fn, Hq, Hkv);
+  if (Lq > Lk) return fail(RATTN_ERR_INVALID_ARG, "%s: Lq=%d > Lk=%d", fn, Lq, Lk);
+  if (Lk > kMaxPosition) return fail(RATTN_ERR_INVALID_ARG, "%s: Lk=%d too large", fn, Lk);
+  if (R < 1) return fail(RATTN_ERR_INVALID_ARG, "%s: R=%d < 1", fn, R);
+  if (token) {
+    if (R < 4) return fail(RATTN_ERR_UNSUPPORTED, "%s: R=%d (the token-dependent table needs R >= 4)", fn, R);
+    if (((uintptr_t)bias_tok & 3) != 0)
+      return fail(RATTN_ERR_INVALID_ARG, "%s: bias_tok must be 4-byte aligned", fn);
+    if ((long long)B * Lq * Hq * (long long)R > 0x3fffffffffffLL)
+      return fail(RATTN_ERR_INVALID_ARG, "%s: token table too large", fn);
+  }
   if (workspace == nullptr && workspace_bytes != 0)
-    return fail(RATTN_ERR_INVALID_ARG, "rattn_prefill: workspace_bytes=%zu with a null workspace", workspace_bytes);
+    return fail(RATTN_ERR_INVALID_ARG, "%s: workspace_bytes=%zu with a null workspace", fn, workspace_bytes);
 
   rattn::PrefillParams p;
   p.q = q;
@@ -360,12 +374,12 @@ int rattn_prefill(const void* q, const void* k, const void* v, const float* bias
   p.lse = lse;
   p.R = R;
   prefill_shape(B, Lq, Lk, Hq, Hkv, window, &p);
+  p.bias_tok = (const uint16_t*)bias_tok;
   p.scale_log2 = kScaleLog2;
   // no workspace: one workgroup per job, never split
   const PrefillSplit sp = workspace == nullptr ? PrefillSplit{} : plan_prefill_split(p, dtype, kv_splits);
   if (sp.ws_bytes > workspace_bytes)
-    return fail(RATTN_ERR_WORKSPACE, "rattn_prefill: workspace of %zu bytes, %zu needed", workspace_bytes,
-                sp.ws_bytes);
+    return fail(RATTN_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, sp.ws_bytes);
   p.n_split = sp.n_split;
   p.n_big = sp.n_big;
   p.parts = sp.parts;
@@ -376,12 +390,32 @@ int rattn_prefill(const void* q, const void* k, const void* v, const float* bias
   p.ws_o = sp.n_split ? (float*)((char*)workspace + sp.o_off) : nullptr;
   const long long per_tile = (long long)B * Hkv * p.n_hg;
   const long long grid = ((long long)p.n_tok_tiles - p.n_split) * per_tile + (long long)p.n_split * per_tile * p.parts;
-  if (grid > 0x7fffffffLL) return fail(RATTN_ERR_INVALID_ARG, "rattn_prefill: problem too large for one launch");
+  if (grid > 0x7fffffffLL) return fail(RATTN_ERR_INVALID_ARG, "%s: problem too large for one launch", fn);
 
   hipError_t e = dtype == RATTN_BF16 ? rattn::launch_prefill_bf16(p, (hipStream_t)stream)
                                      : rattn::launch_prefill_fp32(p, (hipStream_t)stream);
-  if (e != hipSuccess) return fail(RATTN_ERR_HIP, "rattn_prefill: launch failed: %s", hipGetErrorString(e));
+  if (e != hipSuccess) return fail(RATTN_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int rattn_prefill(const void* q, const void* k, const void* v, const float* bias, void* out,
+                  float* lse, int B, int Lq, int Lk, int Hq, int Hkv, int head_dim, int R,
+                  int window, int dtype, int kv_splits, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  return prefill_contiguous("rattn_prefill", false, q, k, v, bias, nullptr, out, lse, B, Lq, Lk, Hq, Hkv, head_dim, R,
+                            window, dtype, kv_splits, workspace, workspace_bytes, stream);
+}
+
+int rattn_prefill_tokbias(const void* q, const void* k, const void* v, const void* bias_tok, void* out,
+                          float* lse, int B, int Lq, int Lk, int Hq, int Hkv, int head_dim, int R,
+                          int window, int kv_splits, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  return prefill_contiguous("rattn_prefill_tokbias", true, q, k, v, nullptr, bias_tok, out, lse, B, Lq, Lk, Hq, Hkv,
+                            head_dim, R, window, RATTN_BF16, kv_splits, workspace, workspace_bytes, stream);
 }
 
 int rattn_prefill_paged(const void* q, const void* k_cache, const void* v_cache, const int* block_table,

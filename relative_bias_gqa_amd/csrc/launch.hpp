@@ -41,6 +41,9 @@ struct PrefillParams {
   const int* cu_q;  // paged: [B + 1] packed query offsets (q, out, lse [total, Hq, ...]), or null: [B, Lq, ...]
   int mbps;
   int num_blocks;
+  // token-dependent table (contiguous bf16 path): bf16 [B, Lq, Hq, R], row (b, t, h) the table
+  // of query t, head h (bias unused); null for the per-head table bias [Hq, R]
+  const uint16_t* bias_tok;
 };
 
 constexpr int kMaxPieces = 8;

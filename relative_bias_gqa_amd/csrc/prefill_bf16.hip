@@ -23,6 +23,11 @@
 //   - each wave also loads its own diagonal slice of r for the tile (distances clamped to
 //     R - 1) into the stage and seeds its S accumulators with it, scaled by sqrt(128), so
 //     the MFMA adds q.k onto the bias;
+//   - TOK (a token-dependent table, every query row with its own r_t[h, :]): no slice is
+//     staged; a wave tile whose distances all clamp to R - 1 adds each row's r_t[h, R - 1]
+//     in the logit FMA; other tiles load each lane's 32 entries (8 runs of 4 consecutive
+//     distances) into registers at the start of the MFMA half-step, the rows' lines having
+//     been pulled into L2 two tiles earlier by one extra DMA per wave issued with K and V;
 //   - the two halves of the workgroup (one wave of each on every SIMD) run in ping-pong,
 //     half a tile apart: while one wave of a SIMD runs its MFMA half-step (O^T += V^T P^T
 //     of the previous tile, then S^T = sqrt(128) r + K Q^T on v_mfma_f32_32x32x16_bf16,
@@ -63,8 +68,12 @@ __device__ __attribute__((aligned(256))) const uint32_t kZeroRowP[64] = {0};
 // sequence by sequence, longest context first (each workgroup ranks the sequences by
 // ctx_lens in LDS, up to kMaxSortedSeqs of them), last token tile first: with the job
 // queue that is close to longest-first whatever the mix of context lengths.
-template <bool PAGED>
+template <bool PAGED, bool TOK>
 __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams p) {
+  static_assert(!(PAGED && TOK), "the token-dependent table is for contiguous K/V");
+  // DMA loads per wave and stage: 2 K + 2 V, and 2 bias-slice loads (static table) or one
+  // L2 warm-up load of the rows' table entries (token-dependent table)
+  constexpr int kLPS = TOK ? 5 : kLoadsPerStage;
   __shared__ __attribute__((aligned(1024))) unsigned char ring[kStages * kStageBytes];
   __shared__ int last_piece;
   __shared__ int next_slot;
@@ -166,6 +175,17 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
       for (int ks = 0; ks < 8; ++ks)
         qr[ks] = ok ? *(const u32x4_t*)((const uint16_t*)p.q + qbase + 16 * ks + 8 * hf) : zero_u32x4();
     }
+    // token-dependent table: this lane's row r_t[h, :] (bf16 [B, Lq, Hq, R]; a row past the
+    // chunk reads row 0 of the sequence, never stored) and its clamp entry r_t[h, R - 1]
+    const uint16_t* tok_row = nullptr;
+    float tok_sat = 0.f;
+    if constexpr (TOK) {
+      const int tq = tw0 + col;
+      const bool ok = wave_active && tq < qlen;
+      tok_row = p.bias_tok + ((qrow0 + (ok ? tq : 0)) * p.Hq + h) * (size_t)p.R;
+      tok_sat = __uint_as_float((uint32_t)tok_row[p.R - 1] << 16);
+      asm volatile("" : "+v"(tok_sat));
+    }
     // pin the waits for these loads here, before any LDS-bound load is in flight
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) asm volatile("" : "+v"(qr[ks]));
@@ -234,20 +254,29 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
           dma16(gv, vdst + i * 1024);
         }
       }
-      // this wave's bias slice, stored by decreasing distance:
-      // entry y = r[h, clamp(pw0 - j0 + 31 - y, 0, R - 1)]; half i holds y = 64 i + lane,
-      // distances lo + 63 - lane with lo = pw0 - j0 - 32 - 64 i
+      if constexpr (!TOK) {
+        // this wave's bias slice, stored by decreasing distance:
+        // entry y = r[h, clamp(pw0 - j0 + 31 - y, 0, R - 1)]; half i holds y = 64 i + lane,
+        // distances lo + 63 - lane with lo = pw0 - j0 - 32 - 64 i
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int lo = pw0 - j0 - 32 - 64 * i;
-        if (lo >= 0 && lo + 63 <= p.R - 1) {
-          dma4s(bias_row + lo, boff, bdst + i * 256);
-        } else if (lo >= p.R - 1) {
-          dma4s(bias_row + (p.R - 1), zoff, bdst + i * 256);
-        } else {
-          const int d = min(max(lo + 63 - lane, 0), p.R - 1);
-          dma4(bias_row + d, bdst + i * 256);
+        for (int i = 0; i < 2; ++i) {
+          const int lo = pw0 - j0 - 32 - 64 * i;
+          if (lo >= 0 && lo + 63 <= p.R - 1) {
+            dma4s(bias_row + lo, boff, bdst + i * 256);
+          } else if (lo >= p.R - 1) {
+            dma4s(bias_row + (p.R - 1), zoff, bdst + i * 256);
+          } else {
+            const int d = min(max(lo + 63 - lane, 0), p.R - 1);
+            dma4(bias_row + d, bdst + i * 256);
+          }
         }
+      } else {
+        // L2 warm-up of the table entries this tile's rows will load (distances pw0 + col -
+        // j0 - 63 .. + 0: 128 bytes per row, the two halves from lanes col and col + 32); the
+        // bytes land in this wave's unused slice area of the stage and are never read
+        // (d <= R - 2: the 4 aligned bytes around entry d stay inside the row)
+        const int d = min(max(pw0 + col - j0 - 63 + 32 * hf, 0), p.R - 2);
+        dma4((const void*)((uintptr_t)(tok_row + d) & ~(uintptr_t)3), bdst);
       }
     };
 
@@ -316,7 +345,34 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
     // S^T = sqrt(128) r + K Q^T for the tile in stage st on the seeded accumulators.  The
     // 32 MFMAs run as eight groups of four (P.V keys 16 G.., then S k-steps in pairs); each
     // group's operands are read from LDS two groups ahead.
-    auto mfma_half = [&](int st, int st_prev) {
+    // Token-dependent table: this wave's tile is SAT (every distance >= R - 1: the rows'
+    // clamp entries), INNER (every distance in 0 .. R - 1: lane runs straight from the rows)
+    // or MIXED (runs clamped into the row, entries chosen per element).  tb[4 kb + g]: the
+    // run of 4 consecutive distances for keys 32 kb + 8 g + 4 hf .. + 3.
+    u32x2_t tb[8];
+    auto tok_class = [&](int kt) {
+      const int j0 = kt * kBK;
+      const int dmin = pw0 - j0 - (kBK - 1), dmax = pw0 + 31 - j0;
+      return dmin >= p.R - 1 ? 0 : (dmin >= 0 && dmax <= p.R - 1 ? 1 : 2);
+    };
+    auto tok_load = [&](int kt) {
+      const int cls = tok_class(kt);
+      if (cls == 0) return;
+      const int d0 = pw0 + col - kt * kBK - 4 * hf;  // distance of the lane's first key
+      if (cls == 1) {
+        const uint16_t* base = tok_row + (d0 - 3);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) __builtin_memcpy(&tb[i], base - (32 * (i >> 2) + 8 * (i & 3)), 8);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int a = min(max(d0 - (32 * (i >> 2) + 8 * (i & 3)) - 3, 0), p.R - 4);
+          __builtin_memcpy(&tb[i], tok_row + a, 8);
+        }
+      }
+    };
+
+    auto mfma_half = [&](int st, int st_prev, int kt) {
       const uint32_t so = st * kStageBytes;
       const uint32_t kx = kx0 + so;
       const uint32_t vz = vz0 + st_prev * kStageBytes;
@@ -337,7 +393,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
         }
       };
       u32x4_t op[3][4];
-      seeds_begin(st);
+      if constexpr (!TOK) seeds_begin(st);
+      else tok_load(kt);
       __builtin_amdgcn_sched_barrier(0);
       load(0, op[0]);
       load(1, op[1]);
@@ -351,13 +408,82 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
           for (int db = 0; db < 4; ++db) o[db] = mfma_32x32x16(cur[db], pk[gi >> 1][gi & 1], o[db]);
           // the seeds (needed from group 4 on); the slice read went out before the operands
           // of groups 0 and 1, so it has arrived
-          if (gi == 1) seeds_end(st);
+          if (gi == 1) {
+            if constexpr (!TOK) {
+              seeds_end(st);
+            } else {
+              s[0] = zero_f32x16();
+              s[1] = zero_f32x16();
+            }
+          }
         } else {
           // alternate the two key blocks so that consecutive MFMAs are independent
 #pragma unroll
           for (int i = 0; i < 4; ++i) s[i & 1] = mfma_32x32x16(cur[i], qr[2 * (gi - 4) + (i >> 1)], s[i & 1]);
         }
         __builtin_amdgcn_sched_barrier(0);  // keep the reads two groups ahead
+      }
+      if constexpr (TOK) {
+        // the table runs have arrived before the next barrier (the loads are the wave's
+        // youngest compiler-visible ones; the group passing its barrier next issues more
+        // K/V loads, which the compiler's own wait would otherwise include)
+        if (tok_class(kt) != 0) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(tb[i]));
+        }
+      }
+    };
+
+    // Token-dependent table: logits of tile kt in log2 units relative to m_ref (bias, scale
+    // and reference in two FMAs), the causal / window mask applied after the bias, so a
+    // table entry at a distance no visible key has never reaches the result.
+    auto tok_logits = [&](int kt, float m_ref) {
+      const int j0 = kt * kBK;
+      const int cls = tok_class(kt);
+      const int dl = pw0 + col - j0 - 4 * hf;  // distance of the lane's first key
+      if (cls == 0) {
+        const float c = fmaf(tok_sat, kLog2e, -m_ref);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[kb][r] = fmaf(s[kb][r], p.scale_log2, c);
+      } else if (cls == 1) {
+        // run [d0 - 3, d0 - 2, d0 - 1, d0]: key k of the run (distance d0 - k) is element 3 - k
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const u32x2_t w = tb[4 * kb + (r >> 2)];
+            const int k = r & 3;
+            const uint32_t word = k < 2 ? w[1] : w[0];
+            const float bv = (k & 1) ? __uint_as_float(word << 16) : __uint_as_float(word & 0xffff0000u);
+            s[kb][r] = fmaf(bv, kLog2e, fmaf(s[kb][r], p.scale_log2, -m_ref));
+          }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int d0 = dl - 32 * kb - 8 * (r >> 2);
+            const int a = min(max(d0 - 3, 0), p.R - 4);
+            const int dist = d0 - (r & 3);
+            const int idx = min(max(dist - a, 0), 3);
+            const u32x2_t w = tb[4 * kb + (r >> 2)];
+            const uint32_t word = idx >= 2 ? w[1] : w[0];
+            float bv = (idx & 1) ? __uint_as_float(word & 0xffff0000u) : __uint_as_float(word << 16);
+            bv = dist >= p.R - 1 ? tok_sat : bv;
+            bv = dist < 0 ? 0.f : bv;
+            s[kb][r] = fmaf(bv, kLog2e, fmaf(s[kb][r], p.scale_log2, -m_ref));
+          }
+      }
+      if (j0 + kBK - 1 > pw0 || j0 < pw_last - Weff + 1) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int c = 32 * kb + 8 * (r >> 2) + (r & 3);
+            s[kb][r] = (uint32_t)(dl - c) < (uint32_t)Weff ? s[kb][r] : kNegInf;
+          }
       }
     };
 
@@ -368,7 +494,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
     // normaliser (the log-sum-exp needs that accuracy) and rounded to bf16 for P.V.
     auto softmax_half = [&](int kt) {
       const int j0 = kt * kBK;
-      if (j0 + kBK - 1 > pw0 || j0 < pw_last - Weff + 1) {
+      if (!TOK && (j0 + kBK - 1 > pw0 || j0 < pw_last - Weff + 1)) {
         // edge tile: mask the raw scores (in place; -inf stays -inf through the logit FMA).
         // Key 32 kb + 8 (r >> 2) + 4 hf + (r & 3) is at distance dl - c(kb, r) from this
         // lane's query; visible iff 0 <= distance < Weff (Weff is huge without a window).
@@ -384,10 +510,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
       const bool fresh = m_run == kNegInf;
       const float m_ref = fresh ? 0.f : m_run;
       const float raise_above = fresh ? kNegInf : kRescaleSlack;
+      if constexpr (!TOK) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][r] = fmaf(s[kb][r], p.scale_log2, -m_ref);
+          for (int r = 0; r < 16; ++r) s[kb][r] = fmaf(s[kb][r], p.scale_log2, -m_ref);
+      } else {
+        tok_logits(kt, m_ref);
+      }
       float ma = max3f(s[0][0], s[0][1], s[0][2]);
       float mb = max3f(s[1][0], s[1][1], s[1][2]);
 #pragma unroll
@@ -453,7 +583,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // before the first barrier
     }
     auto tile_barrier = [&](int j) {
-      if (j + 1 < n_tiles) vm_wait<kLoadsPerStage>();  // tile j; tile j + 1 may still be loading
+      if (j + 1 < n_tiles) vm_wait<kLPS>();  // tile j; tile j + 1 may still be loading
       else vm_wait<0>();
       wg_barrier_reads_in_flight();
       if (j + 2 < n_tiles) issue_tile(kt_begin + j + 2, (j + 2) % kStages);
@@ -461,7 +591,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillParams
     if (g1 && n_tiles > 0) tile_barrier(0);
     for (int t = 0; t < n_tiles; ++t) {
       if (!g1) tile_barrier(t);
-      mfma_half(t % kStages, (t + kStages - 1) % kStages);
+      mfma_half(t % kStages, (t + kStages - 1) % kStages, kt_begin + t);
       if (g1 && t + 1 < n_tiles) tile_barrier(t + 1);
       softmax_half(kt_begin + t);
     }
@@ -632,9 +762,11 @@ hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream) {
   // with a queue: one workgroup per compute unit, each running jobs until none is left
   if (p.queue != nullptr && grid > p.queue_workgroups) grid = p.queue_workgroups;
   if (p.block_table != nullptr)
-    hipLaunchKernelGGL(prefill_bf16_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((prefill_bf16_kernel<true, false>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+  else if (p.bias_tok != nullptr)
+    hipLaunchKernelGGL((prefill_bf16_kernel<false, true>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL(prefill_bf16_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((prefill_bf16_kernel<false, false>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -153,6 +153,29 @@ def make_backward(seed: int, B: int, Lq: int, Lk: int, Hq: int, Hkv: int, R: int
     return BackwardCase(fwd, _normal(rng, (B, Lq, Hq, HEAD_DIM), "bf16"), name)
 
 
+@dataclass
+class TokBiasCase:
+    """A prefill whose relative-bias table depends on the query token: row (b, t, h) has
+    its own table bias_tok[b, t, h, :] (a "qkvr" projection output, bf16)."""
+    fwd: PrefillCase          # q, k, v, window of the prefill (bf16); its static table is unused
+    bias_tok: np.ndarray      # [B, Lq, Hq, R] uint16 (bf16 bits)
+    name: str = ""
+
+    @property
+    def R(self): return self.bias_tok.shape[3]
+
+
+def make_prefill_tokbias(seed: int, B: int, Lq: int, Lk: int, Hq: int, Hkv: int, R: int, window: int,
+                         name: str = "") -> TokBiasCase:
+    """Draw order: the bf16 prefill case of the same seed (Q, K, V and a one-entry static
+    table), then the per-token tables from a generator seeded with (seed, 2): 0.5 * N(0,1)
+    rounded to bf16 (the N(0,1) draws rounded to bf16, then halved, which is exact)."""
+    fwd = make_prefill(seed, B, Lq, Lk, Hq, Hkv, 1, window, "bf16", name)
+    rng = np.random.default_rng([seed, 2])
+    tab = bf16_round(0.5 * to_float(_normal_bf16(rng, (B, Lq, Hq, R))))
+    return TokBiasCase(fwd, tab, name)
+
+
 # ----------------------------------------------------------------------------
 # Paged decode
 # ----------------------------------------------------------------------------
@@ -298,6 +321,8 @@ WORKLOADS = {
                     "bf16, window-4 short convolution into paged caches",
     "swa_prefill_8k_bwd": "backward of swa_prefill_8k (batch 1, L=8192, 16/2 heads, window 4096, R=4096): dq, dk, dv, "
                           "dr for a N(0,1) output gradient",
+    "swa_prefill_8k_tokbias": "batch 1, L=8192, 16/2 heads, bf16, window 4096, a token-dependent bf16 table of "
+                              "R=512 entries per query row and head (0.5*N(0,1))",
 }
 
 
@@ -338,6 +363,11 @@ def swa_prefill_8k_bwd(seed: int = 0) -> BackwardCase:
     return make_backward(seed, 1, 8192, 8192, 16, 2, 4096, 4096, "swa_prefill_8k_bwd")
 
 
+def swa_prefill_8k_tokbias(seed: int = 0) -> TokBiasCase:
+    """The 8K-token window-4096 prefill with a token-dependent table of 512 entries per row."""
+    return make_prefill_tokbias(seed, 1, 8192, 8192, 16, 2, 512, 4096, "swa_prefill_8k_tokbias")
+
+
 WORKLOAD_FNS = {
     "tiny_prefill_fp32": tiny_prefill_fp32,
     "swa_prefill_8k": swa_prefill_8k,
@@ -347,4 +377,5 @@ WORKLOAD_FNS = {
     "paged_prefill_b4": paged_prefill_b4,
     "kv_sconv_32k": kv_sconv_32k,
     "swa_prefill_8k_bwd": swa_prefill_8k_bwd,
+    "swa_prefill_8k_tokbias": swa_prefill_8k_tokbias,
 }

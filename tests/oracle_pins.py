@@ -9,7 +9,10 @@ AssertionError when the oracle disagrees with:
   * closed forms (window 1, position 0, R = 1, K = 0, constant V),
   * invariants (per-head bias shift, window >= L, chunk == full, paged ==
     contiguous, decode == last prefill rows, probabilities sum to 1),
-  * brute force over tiny inputs with pure-Python loops.
+  * brute force over tiny inputs with pure-Python loops,
+and the token-dependent variant (one table per query row) to the static one
+(equal rows), SDPA with a per-row float mask, closed forms, a per-row shift,
+row independence and brute force.
 The definition being pinned is the one on the vLLM recipes page
 "thinkingmachines/Inkling", Overview > Architectural highlights > Attention:
 GQA with head size 128 whose logits carry a trained, distance-dependent bias
@@ -361,9 +364,140 @@ def pin_brute_force(lib):
         np.testing.assert_allclose(lse, bl, rtol=0, atol=1e-12)
 
 
+# ----------------------------------------------------------------------------
+# token-dependent bias: every query row has its own table r_t[h, :]
+# (the "qkvr" linears of the recipes page's Variants section read as producing a
+# per-token table: logit = q.k/sqrt(D) + r_t[h, min(p - j, R - 1)])
+# ----------------------------------------------------------------------------
+def _prefill_tok(lib, q, k, v, rt, window=0, probs=False):
+    B = q.shape[0]
+    return oracle.ref_attention(q, k, v, rt, [k.shape[1]] * B, [window] * B, None, want_probs=probs, lib=lib,
+                                token_bias=True)
+
+
+def _rand_tok(seed, B, Lq, Hq, R, scale=0.5):
+    return scale * np.random.default_rng(seed).standard_normal((B, Lq, Hq, R))
+
+
+def pin_tokbias_equal_rows_is_static(lib):
+    """Every row given the static table r[h, :]: the same result as the static-table
+    oracle, bit for bit."""
+    for (B, Lq, Lk, Hq, Hkv, D, R, window) in [(2, 6, 11, 4, 2, 8, 5, 0), (1, 9, 9, 3, 1, 8, 20, 4)]:
+        q, k, v, r = _rand(40 + Lq, B, Lq, Lk, Hq, Hkv, D, R)
+        rt = np.broadcast_to(r[None, None], (B, Lq, Hq, R)).copy()
+        o1, l1, _ = _prefill(lib, q, k, v, r, window)
+        o2, l2, _ = _prefill_tok(lib, q, k, v, rt, window)
+        assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def pin_tokbias_row_shift(lib):
+    """Adding c[b, t, h] to every entry of row (b, t, h)'s table leaves out unchanged and
+    adds c[b, t, h] to that row's lse."""
+    B, Lq, Lk, Hq, Hkv, D, R = 2, 5, 9, 4, 2, 8, 6
+    q, k, v, _ = _rand(41, B, Lq, Lk, Hq, Hkv, D, R)
+    rt = _rand_tok(42, B, Lq, Hq, R)
+    c = np.random.default_rng(43).uniform(-3, 3, (B, Lq, Hq))
+    for window in (0, 3):
+        o1, l1, _ = _prefill_tok(lib, q, k, v, rt, window)
+        o2, l2, _ = _prefill_tok(lib, q, k, v, rt + c[..., None], window)
+        np.testing.assert_allclose(o2, o1, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(l2, l1 + c, rtol=0, atol=1e-12)
+
+
+def pin_tokbias_window_one(lib):
+    """W = 1: out_t = v_t and lse_t = q_t.k_t/sqrt(D) + r_t[h, 0]."""
+    B, L, Hq, Hkv, D, R = 2, 7, 4, 2, 8, 5
+    q, k, v, _ = _rand(44, B, L, L, Hq, Hkv, D, R)
+    rt = _rand_tok(45, B, L, Hq, R)
+    out, lse, _ = _prefill_tok(lib, q, k, v, rt, 1)
+    G = Hq // Hkv
+    for h in range(Hq):
+        np.testing.assert_allclose(out[:, :, h], v[:, :, h // G], rtol=0, atol=1e-12)
+        dots = np.einsum("bld,bld->bl", q[:, :, h], k[:, :, h // G])
+        np.testing.assert_allclose(lse[:, :, h], dots / math.sqrt(D) + rt[:, :, h, 0], rtol=0, atol=1e-12)
+
+
+def pin_tokbias_zero_keys(lib):
+    """K = 0: the weights of row (b, t, h) are the softmax of its own table's entries at the
+    clamped distances, whatever Q is."""
+    B, Lq, Lk, Hq, Hkv, D, R = 1, 6, 10, 2, 1, 8, 4
+    q, _, v, _ = _rand(46, B, Lq, Lk, Hq, Hkv, D, R)
+    k = np.zeros((B, Lk, Hkv, D))
+    rt = _rand_tok(47, B, Lq, Hq, R, 1.0)
+    _, lse, probs = _prefill_tok(lib, q, k, v, rt, 0, probs=True)
+    for t in range(Lq):
+        p = Lk - Lq + t
+        for h in range(Hq):
+            b = np.array([rt[0, t, h, min(p - j, R - 1)] for j in range(p + 1)])
+            w = np.exp(b - b.max())
+            np.testing.assert_allclose(probs[0, t, h, :p + 1], w / w.sum(), rtol=0, atol=1e-13)
+            assert abs(lse[0, t, h] - (b.max() + math.log(w.sum()))) < 1e-12
+
+
+def pin_tokbias_is_sdpa(lib):
+    """torch SDPA (float64) with the float mask m[b, h, t, j] = r_t[h, min(p - j, R - 1)] on
+    the visible pairs and -inf elsewhere, for a chunk after a prefix and a window."""
+    for (B, Lq, Lk, Hq, Hkv, D, R, window) in [(2, 5, 12, 4, 2, 8, 7, 0), (1, 8, 8, 6, 3, 8, 3, 4)]:
+        q, k, v, _ = _rand(48 + Lk, B, Lq, Lk, Hq, Hkv, D, R)
+        rt = _rand_tok(49 + Lk, B, Lq, Hq, R)
+        out, _, _ = _prefill_tok(lib, q, k, v, rt, window)
+        vis = _visibility(Lq, Lk, window)
+        dist = (Lk - Lq + np.arange(Lq))[:, None] - np.arange(Lk)[None, :]
+        idx = np.clip(dist, 0, R - 1)
+        mask = np.full((B, Hq, Lq, Lk), -np.inf)
+        for b in range(B):
+            for h in range(Hq):
+                for t in range(Lq):
+                    mask[b, h, t, vis[t]] = rt[b, t, h, idx[t, vis[t]]]
+        G = Hq // Hkv
+        ref = _sdpa(q, _expand_kv(k, G), _expand_kv(v, G), mask, 1.0 / math.sqrt(D))
+        np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+
+
+def pin_tokbias_brute_force(lib):
+    """Pure-Python loops, explicit exp, math.fsum, each row with its own table."""
+    B, Lq, Lk, Hq, Hkv, D, R, window = 1, 4, 7, 2, 1, 4, 3, 5
+    q, k, v, _ = _rand(50, B, Lq, Lk, Hq, Hkv, D, R, scale_bias=1.0)
+    rt = _rand_tok(51, B, Lq, Hq, R, 1.0)
+    out, lse, _ = _prefill_tok(lib, q, k, v, rt, window)
+    for t in range(Lq):
+        i = Lk - Lq + t
+        for h in range(Hq):
+            ws, js = [], []
+            for j in range(Lk):
+                d = i - j
+                if d < 0 or d >= window:
+                    continue
+                logit = math.fsum(float(q[0, t, h, e]) * float(k[0, j, 0, e]) for e in range(D)) / math.sqrt(D)
+                ws.append(math.exp(logit + float(rt[0, t, h, min(d, R - 1)])))
+                js.append(j)
+            Z = math.fsum(ws)
+            for e in range(D):
+                ref = math.fsum(w * float(v[0, j, 0, e]) for w, j in zip(ws, js)) / Z
+                assert abs(out[0, t, h, e] - ref) <= 1e-12
+            assert abs(lse[0, t, h] - math.log(Z)) <= 1e-12
+
+
+def pin_tokbias_rows_independent(lib):
+    """Changing the table of one row (b, t, h) changes that row's output only."""
+    B, Lq, Lk, Hq, Hkv, D, R = 2, 6, 9, 4, 2, 8, 5
+    q, k, v, _ = _rand(52, B, Lq, Lk, Hq, Hkv, D, R)
+    rt = _rand_tok(53, B, Lq, Hq, R)
+    o1, l1, _ = _prefill_tok(lib, q, k, v, rt, 0)
+    rt2 = rt.copy()
+    rt2[1, 3, 2, :] += np.linspace(-1, 2, R)
+    o2, l2, _ = _prefill_tok(lib, q, k, v, rt2, 0)
+    changed = np.abs(o2 - o1).max(axis=-1) > 0
+    expect = np.zeros((B, Lq, Hq), dtype=bool)
+    expect[1, 3, 2] = True
+    assert np.array_equal(changed, expect) and np.array_equal(l2 != l1, expect)
+
+
 ALL_PINS = [
     pin_zero_bias_is_sdpa, pin_alibi_is_sdpa, pin_golden_examples, pin_window_one, pin_position_zero,
     pin_R_one, pin_zero_keys, pin_constant_values, pin_bias_shift, pin_wide_window_is_full,
     pin_probs_sum_to_one, pin_chunk_equals_full, pin_paged_equals_contiguous, pin_input_widening,
     pin_brute_force,
+    pin_tokbias_equal_rows_is_static, pin_tokbias_row_shift, pin_tokbias_window_one, pin_tokbias_zero_keys,
+    pin_tokbias_is_sdpa, pin_tokbias_brute_force, pin_tokbias_rows_independent,
 ]

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.rattn_abi_version() == rb.ABI_VERSION == 7
+    assert lib.rattn_abi_version() == rb.ABI_VERSION == 8
 
 
 def _prefill(lib, **kw):
@@ -105,6 +105,36 @@ def _decode(lib, **kw):
 def test_decode_validation(lib, kw, status, needle):
     assert _decode(lib, **kw) == status
     assert needle in rb.rattn_last_error()
+
+
+def _prefill_tok(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, rt=FAKE, out=FAKE, lse=None, B=1, Lq=100, Lk=100, Hq=16, Hkv=2, D=128, R=64,
+             window=0, ks=0, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return lib.rattn_prefill_tokbias(a["q"], a["k"], a["v"], a["rt"], a["out"], a["lse"], a["B"], a["Lq"], a["Lk"],
+                                     a["Hq"], a["Hkv"], a["D"], a["R"], a["window"], a["ks"], a["ws"], a["wsb"],
+                                     a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(rt=None), rb.RATTN_ERR_INVALID_ARG, "null"),
+    (dict(q=None), rb.RATTN_ERR_INVALID_ARG, "null"),
+    (dict(R=3), rb.RATTN_ERR_UNSUPPORTED, "R >= 4"),
+    (dict(R=0), rb.RATTN_ERR_INVALID_ARG, "R="),
+    (dict(rt=ctypes.c_void_p(0x1002)), rb.RATTN_ERR_INVALID_ARG, "aligned"),
+    (dict(Lq=101), rb.RATTN_ERR_INVALID_ARG, "Lq="),
+    (dict(Hq=15), rb.RATTN_ERR_INVALID_ARG, "multiple"),
+    (dict(D=64), rb.RATTN_ERR_UNSUPPORTED, "head_dim"),
+    (dict(ks=9), rb.RATTN_ERR_INVALID_ARG, "kv_splits"),
+    (dict(ws=FAKE, wsb=16), rb.RATTN_ERR_WORKSPACE, "workspace"),
+])
+def test_prefill_tokbias_validation(lib, kw, status, needle):
+    assert _prefill_tok(lib, **kw) == status
+    assert needle in rb.rattn_last_error()
+
+
+def test_prefill_tokbias_empty_is_noop(lib):
+    assert _prefill_tok(lib, Lq=0, q=None, rt=None) == rb.RATTN_OK
 
 
 def test_decode_empty_is_noop(lib):

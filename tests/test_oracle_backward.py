@@ -155,3 +155,35 @@ def test_backward_magnitude_sums(impl, seed, B, Lq, Lk, Hq, Hkv, R, window):
         if first_seen > 0:
             for a in absums[1:3]:
                 assert np.all(a[:, :first_seen] == 0)
+
+
+@pytest.mark.parametrize("seed,B,Lq,Lk,Hq,Hkv,R,window", ABS_CASES)
+def test_backward_given_output(seed, B, Lq, Lk, Hq, Hkv, R, window):
+    """D from a given forward output: with the exact output (the forward oracle's, float64)
+    both implementations reproduce the exact gradients; with that output rounded to bf16 they
+    agree with each other (gradients and magnitude sums, any weight)."""
+    from oracle.sconv import f64_to_bf16
+    q, k, v, r, do = _case(seed, B, Lq, Lk, Hq, Hkv, R)
+    out, _, _ = oracle.ref_prefill(q, k, v, r, window)
+    exact, _ = _c_bwd(q, k, v, r, do, window)
+    for impl in ("numpy", "c"):
+        if impl == "numpy":
+            got = prefill_backward(q, k, v, r, do, window, out=out)[:4]
+        else:
+            got = oracle.ref_backward(q, k, v, r, do, window, out=out)[0]
+        for name, x, y in zip(("dq", "dk", "dv", "dr"), got, exact):
+            assert np.allclose(x, y, rtol=1e-10, atol=1e-12), (impl, name)
+    qb, kb, vb, gb, ob = (f64_to_bf16(x) for x in (q, k, v, do, out))
+    w = 2.0 ** -6
+    res_np = prefill_backward(qb, kb, vb, r, gb, window, out=ob, abs_weight=w)
+    g_np, a_np = res_np[:4], res_np[4]
+    g_c, a_c = oracle.ref_backward(qb, kb, vb, r, gb, window, out=ob, abs_weight=w)
+    for name, x, y, scale in zip(("dq", "dk", "dv", "dr"), g_np, g_c, a_np):
+        assert np.all(np.abs(x - y) <= 1e-12 * (1 + scale)), name
+    for name, x, y in zip(("dq_abs", "dk_abs", "dv_abs", "dr_abs"), a_np, a_c):
+        assert np.allclose(x, y, rtol=1e-12, atol=1e-14), name
+    # the D term of the magnitude sums scales with the weight
+    a_1 = oracle.ref_backward(qb, kb, vb, r, gb, window, out=ob, abs_weight=1.0)[1]
+    a_0 = oracle.ref_backward(qb, kb, vb, r, gb, window, out=ob, abs_weight=0.0)[1]
+    for x0, xw, x1 in zip(a_0, a_c, a_1):
+        assert np.allclose(xw, x0 + w * (x1 - x0), rtol=1e-12, atol=1e-12)

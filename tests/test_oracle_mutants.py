@@ -28,6 +28,12 @@ MUTANTS = [
     ("paged_slot_reversed", "(((size_t)phys * block_size + j % block_size)",
      "(((size_t)phys * block_size + (block_size - 1 - j % block_size))"),
     ("bf16_widened_wrong", "uint32_t u = (uint32_t)s[e] << 16;", "uint32_t u = (uint32_t)s[e] << 15;"),
+    # token-dependent bias: the row's own table
+    ("tokbias_head_table", "bias + (size_t)(bias_per_row ? row : h) * R", "bias + (size_t)(bias_per_row ? h : h) * R"),
+    ("tokbias_neighbour_row", "bias + (size_t)(bias_per_row ? row : h) * R",
+     "bias + (size_t)(bias_per_row ? (row + Hq) % rows : h) * R"),
+    ("tokbias_heads_reversed", "bias + (size_t)(bias_per_row ? row : h) * R",
+     "bias + (size_t)(bias_per_row ? row - h + (Hq - 1 - h) : h) * R"),
 ]
 
 
