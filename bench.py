@@ -296,7 +296,7 @@ class BackwardRun:
         self.dk = torch.empty(self.k.shape, dtype=f32, device=self.q.device)
         self.dv = torch.empty(self.v.shape, dtype=f32, device=self.q.device)
         self.dbias = torch.empty(self.bias.shape, dtype=f32, device=self.q.device)
-        self.ws = torch.empty(rb.rattn_prefill_backward_workspace_bytes(c.B, c.Lq, c.Hq), dtype=torch.uint8,
+        self.ws = torch.empty(rb.rattn_prefill_backward_workspace_bytes(c.B, c.Lq, c.Lk, c.Hq, c.Hkv), dtype=torch.uint8,
                               device=self.q.device)
         self.rb = rb
         # five products per visible (query, key) pair and head: QK^T again, dO V^T, P^T dO,

@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define RATTN_ABI_VERSION 8
+#define RATTN_ABI_VERSION 9
 
 enum rattn_status {
   RATTN_OK = 0,
@@ -217,10 +217,13 @@ int rattn_kv_sconv_write(const void* k_new, const void* v_new, const float* w_k,
                          int max_blocks_per_seq, int max_new, void* stream);
 
 /*
- * Device workspace, in bytes, that rattn_prefill_backward needs: one fp32 per query row
- * (B * Lq * Hq of them), rounded up to 256 bytes.  Returns 0 for negative sizes.
+ * Device workspace, in bytes, that rattn_prefill_backward needs: two fp32 per query row
+ * (rowsum(dout * out) and lse * log2(e), B * Lq * Hq rows), then, per pair of query heads of
+ * a KV head (ceil(G / 2) pairs, G = Hq / Hkv), a partial dK and a partial dV
+ * ([B, Lk, Hkv, 128] fp32 each), every part rounded up to 256 bytes.  Returns 0 for invalid
+ * sizes.
  */
-size_t rattn_prefill_backward_workspace_bytes(int B, int Lq, int Hq);
+size_t rattn_prefill_backward_workspace_bytes(int B, int Lq, int Lk, int Hq, int Hkv);
 
 /*
  * Gradients of rattn_prefill (bf16, contiguous K/V) for an output gradient dout.
@@ -244,10 +247,12 @@ size_t rattn_prefill_backward_workspace_bytes(int B, int Lq, int Hq);
  *   window        <= 0 full causal, > 0 sliding window of that many keys
  *
  * The caller owns every buffer; the call enqueues its kernels on `stream` and returns.
- * dk, dv and dbias are sums of fp32 atomic adds, so their last bits may differ from run
- * to run; dq is deterministic.  Status: INVALID_ARG (null pointer, sizes, Lq > Lk,
- * B or Hq > 65535), UNSUPPORTED (head_dim != 128), WORKSPACE (missing or too small),
- * HIP (launch failure).
+ * dq, dk and dv are deterministic (dk and dv: per-pair partials summed in pair order);
+ * dbias is a sum of fp32 atomic adds, so its last bits may differ from run to run.
+ * A non-finite dout or out row makes the gradients that depend on it non-finite; nothing
+ * is ever written outside dq, dk, dv, dbias and the workspace.  Status: INVALID_ARG (null
+ * pointer, sizes, Lq > Lk, B or Hq > 65535), UNSUPPORTED (head_dim != 128), WORKSPACE
+ * (missing or too small), HIP (launch failure).
  */
 int rattn_prefill_backward(const void* q, const void* k, const void* v, const float* bias,
                            const void* out, const void* dout, const float* lse, float* dq,

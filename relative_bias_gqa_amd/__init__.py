@@ -25,7 +25,7 @@ LIB_PATH = os.path.join(_HERE, "librattn.so")
 
 RATTN_OK, RATTN_ERR_INVALID_ARG, RATTN_ERR_UNSUPPORTED, RATTN_ERR_WORKSPACE, RATTN_ERR_HIP = 0, 1, 2, 3, 4
 RATTN_BF16, RATTN_FP32 = 0, 1
-ABI_VERSION = 8
+ABI_VERSION = 9
 
 EXPORTED = ("rattn_prefill_workspace_bytes", "rattn_prefill", "rattn_prefill_tokbias", "rattn_prefill_paged", "rattn_kv_sconv_write",
             "rattn_prefill_backward_workspace_bytes", "rattn_prefill_backward",
@@ -64,7 +64,7 @@ def load(path: Optional[str] = None):
     lib.rattn_kv_sconv_write.restype = i32
     lib.rattn_kv_sconv_write.argtypes = [vp] * 11 + [i32] * 7 + [vp]
     lib.rattn_prefill_backward_workspace_bytes.restype = sz
-    lib.rattn_prefill_backward_workspace_bytes.argtypes = [i32] * 3
+    lib.rattn_prefill_backward_workspace_bytes.argtypes = [i32] * 5
     lib.rattn_prefill_backward.restype = i32
     lib.rattn_prefill_backward.argtypes = [vp] * 11 + [i32] * 8 + [vp, sz, vp]
     lib.rattn_decode_num_splits.restype = i32
@@ -204,16 +204,16 @@ def rattn_kv_sconv_write(k_new, v_new, w_k, w_v, k_cache, v_cache, k_state, v_st
                                        _stream(stream)))
 
 
-def rattn_prefill_backward_workspace_bytes(B: int, Lq: int, Hq: int) -> int:
-    return load().rattn_prefill_backward_workspace_bytes(B, Lq, Hq)
+def rattn_prefill_backward_workspace_bytes(B: int, Lq: int, Lk: int, Hq: int, Hkv: int) -> int:
+    return load().rattn_prefill_backward_workspace_bytes(B, Lq, Lk, Hq, Hkv)
 
 
 def rattn_prefill_backward(q, k, v, bias, out, dout, lse, dq, dk, dv, dbias, window: int, workspace,
                            stream=None) -> None:
     """q/out/dout [B,Lq,Hq,128] bf16; k/v [B,Lk,Hkv,128] bf16; bias [Hq,R] fp32; lse [B,Lq,Hq]
     fp32 (rattn_prefill's out and lse); dq like q, dk/dv like k, dbias like bias, all fp32;
-    workspace a device tensor of at least rattn_prefill_backward_workspace_bytes(B, Lq, Hq)
-    bytes."""
+    workspace a device tensor of at least rattn_prefill_backward_workspace_bytes(B, Lq, Lk, Hq,
+    Hkv) bytes."""
     B, Lq, Hq, D = q.shape
     Lk, Hkv = k.shape[1], k.shape[2]
     R = bias.shape[1]
@@ -327,7 +327,7 @@ def prefill_backward(q, k, v, bias, out, lse, dout, window: int = 0, stream=None
     dk = torch.empty(k.shape, dtype=torch.float32, device=q.device)
     dv = torch.empty(v.shape, dtype=torch.float32, device=q.device)
     dbias = torch.empty(bias.shape, dtype=torch.float32, device=q.device)
-    n = rattn_prefill_backward_workspace_bytes(q.shape[0], q.shape[1], q.shape[2])
+    n = rattn_prefill_backward_workspace_bytes(q.shape[0], q.shape[1], k.shape[1], q.shape[2], k.shape[2])
     ws = torch.empty(n, dtype=torch.uint8, device=q.device)
     rattn_prefill_backward(q, k, v, bias, out, dout, lse, dq, dk, dv, dbias, window, ws, stream)
     return dq, dk, dv, dbias

@@ -518,10 +518,37 @@ int rattn_kv_sconv_write(const void* k_new, const void* v_new, const float* w_k,
   return ok();
 }
 
-size_t rattn_prefill_backward_workspace_bytes(int B, int Lq, int Hq) {
-  if (B < 0 || Lq < 0 || Hq < 0) return 0;
+}  // extern "C"
+
+namespace {
+
+// Backward workspace: D and lse * log2(e) per query row ([B, Hq, Lq] each), then the partial
+// dK and dV of each pair of query heads ([ceil(G / 2), B, Lk, Hkv, 128] each), 256-aligned.
+struct BackwardLayout {
+  size_t l2_off, pk_off, pv_off, total;
+  int n_pairs;
+};
+
+bool backward_layout(int B, int Lq, int Lk, int Hq, int Hkv, BackwardLayout* lay) {
+  if (B < 0 || Lq < 0 || Lk < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return false;
+  auto align = [](size_t x) { return (x + 255) / 256 * 256; };
   const size_t rows = (size_t)B * Lq * Hq;
-  return std::max<size_t>(256, (rows * sizeof(float) + 255) / 256 * 256);
+  const size_t plane = (size_t)B * Lk * Hkv * 128;
+  lay->n_pairs = (Hq / Hkv + 1) / 2;
+  lay->l2_off = align(rows * sizeof(float));
+  lay->pk_off = lay->l2_off + align(rows * sizeof(float));
+  lay->pv_off = lay->pk_off + align((size_t)lay->n_pairs * plane * sizeof(float));
+  lay->total = std::max<size_t>(256, lay->pv_off + align((size_t)lay->n_pairs * plane * sizeof(float)));
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t rattn_prefill_backward_workspace_bytes(int B, int Lq, int Lk, int Hq, int Hkv) {
+  BackwardLayout lay;
+  return backward_layout(B, Lq, Lk, Hq, Hkv, &lay) ? lay.total : 0;
 }
 
 int rattn_prefill_backward(const void* q, const void* k, const void* v, const float* bias, const void* out,
@@ -543,7 +570,9 @@ int rattn_prefill_backward(const void* q, const void* k, const void* v, const fl
   if (R < 1) return fail(RATTN_ERR_INVALID_ARG, "rattn_prefill_backward: R=%d < 1", R);
   if (B > 65535 || Hq > 65535)
     return fail(RATTN_ERR_INVALID_ARG, "rattn_prefill_backward: B=%d or Hq=%d > 65535", B, Hq);
-  const size_t need = rattn_prefill_backward_workspace_bytes(B, Lq, Hq);
+  BackwardLayout lay;
+  backward_layout(B, Lq, Lk, Hq, Hkv, &lay);
+  const size_t need = lay.total;
   if (!workspace || workspace_bytes < need)
     return fail(RATTN_ERR_WORKSPACE, "rattn_prefill_backward: workspace of %zu bytes, %zu needed",
                 workspace ? workspace_bytes : (size_t)0, need);
@@ -560,6 +589,10 @@ int rattn_prefill_backward(const void* q, const void* k, const void* v, const fl
   p.dv = dv;
   p.dbias = dbias;
   p.D = (float*)workspace;
+  p.L2 = (float*)((char*)workspace + lay.l2_off);
+  p.part_dk = (float*)((char*)workspace + lay.pk_off);
+  p.part_dv = (float*)((char*)workspace + lay.pv_off);
+  p.n_pairs = lay.n_pairs;
   p.B = B;
   p.Lq = Lq;
   p.Lk = Lk;

@@ -43,6 +43,9 @@ constexpr int kTileElems = kRows * kStride;
 constexpr float kRsqrtD = 0.08838834764831845f;  // 1 / sqrt(128)
 constexpr int kDiagStride = 34;            // floats per row of the diagonal table (conflict free)
 
+// 256 bytes of zeros: the source of every K/V row past Lk and query row past Lq.
+__device__ __attribute__((aligned(256))) const uint32_t kZeroRowB[64] = {0};
+
 // The 63 bias entries a 32 x 32 tile meets: entry e = r[h, clamp(dbase + e, 0, R - 1)] for the
 // pairs at distance dbase + e, dbase = (distance of query 0 to key 31).  Lanes 0..62 load one.
 __device__ __forceinline__ void stage_bias(float* band, const float* bias_h, int dbase, int R, int lane) {
@@ -105,9 +108,10 @@ __global__ __launch_bounds__(256) void bwd_fill_zero_kernel(float* a, size_t n) 
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) a[i] = 0.f;
 }
 
-// D[row] = sum_d dout[row, d] * out[row, d] for every (b, t, h) row, in fp32.
-__global__ __launch_bounds__(256) void bwd_rowdot_kernel(const uint16_t* out, const uint16_t* dout, float* D,
-                                                         size_t rows) {
+// D = sum_d dout[b, t, h, d] * out[b, t, h, d] and L2 = lse[b, t, h] * log2(e) for every row,
+// in fp32, stored head-major ([B, Hq, Lq]) so that a query tile of one head is contiguous.
+__global__ __launch_bounds__(256) void bwd_rowdot_kernel(const uint16_t* out, const uint16_t* dout, const float* lse,
+                                                         float* D, float* L2, int Lq, int Hq, size_t rows) {
   const size_t row = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (row >= rows) return;
   const u32x4_t* o = (const u32x4_t*)(out + row * kHeadDim);
@@ -122,88 +126,200 @@ __global__ __launch_bounds__(256) void bwd_rowdot_kernel(const uint16_t* out, co
       acc = fmaf(bf16_hi_to_f32(x[i]), bf16_hi_to_f32(y[i]), acc);
     }
   }
-  D[row] = acc;
+  const size_t h = row % Hq, t = (row / Hq) % Lq, b = row / ((size_t)Hq * Lq);
+  const size_t dst = (b * Hq + h) * Lq + t;
+  D[dst] = acc;
+  L2[dst] = lse[row] * kLog2e;
 }
 
-// Key-stationary pass: dK and dV.  Grid (key tiles, Hkv * ceil(G / 2), B); a workgroup is
-// two waves, each one query head of the same KV head, sharing the K and V tiles.  With an odd
-// G the second wave of the last pair has no head: it runs along (for the barriers) and
-// writes nothing.
-__global__ __launch_bounds__(2 * 64) void bwd_dkdv_kernel(BackwardParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t kt[kTileElems];
-  __shared__ __attribute__((aligned(16))) uint16_t vt[kTileElems];
-  __shared__ __attribute__((aligned(16))) uint16_t qt_w[2][kTileElems];
-  __shared__ __attribute__((aligned(16))) uint16_t gt_w[2][kTileElems];  // dO
-  __shared__ float lse_w[2][kRows];
-  __shared__ float d_w[2][kRows];
-  __shared__ float bias_w[2][64];
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-  uint16_t* qt = qt_w[wave];
-  uint16_t* gt = gt_w[wave];
-  float* lse_s = lse_w[wave];
-  float* d_s = d_w[wave];
-  float* bias_s = bias_w[wave];
+// ---- key-stationary pass (dK, dV) -----------------------------------------------------
+// A workgroup owns 128 keys (four 32-key blocks) of one KV head and one pair of its query
+// heads: 8 waves, wave w = key block w & 3 for head slot w >> 2.  K and V of the 128 keys sit
+// in LDS for the whole pass; the query tiles that see them stream through a two-stage LDS
+// ring, one step ahead, straight from global memory (global_load_lds_dwordx4): per step
+// the Q and dO tiles (32 queries) of both heads, their D and lse*log2(e), and each wave's
+// 63-entry bias slice.  Per step a wave computes S = Q K^T and dP = dO V^T with one key per
+// lane (the accumulator column), then P and dS, then dV += P^T dO and dK += dS^T Q (P and dS
+// as A operands straight from registers, dO and Q read transposed from LDS).  At the end the
+// two slots of a key block add up through LDS and slot 0 writes the pair's partial dK, dV;
+// a reduce kernel sums the pairs in pair order (no atomics: the result is deterministic).
+//
+// Tiles in LDS have 256-byte rows; 16-byte chunk c of row r is stored at chunk c ^ swz(r),
+// swz(r) = 4 (r & 3) + ((r >> 2) & 3): the sixteen rows a 16-lane group reads row-wise get
+// sixteen different chunks, and the four rows x four chunks of a transposed read
+// (ds_read_b64_tr_b16) land in sixteen different chunks as well.
+constexpr int kKvBlocks = 4;                // 32-key blocks per workgroup
+constexpr int kKvKeys = 32 * kKvBlocks;     // 128
+constexpr int kKvWaves = 2 * kKvBlocks;     // two head slots
+constexpr int kTileBytes = 32 * 256;        // 32 rows of 128 bf16
+constexpr int kRingQ = 0;                   // Q of slot 0, slot 1
+constexpr int kRingG = 2 * kTileBytes;      // dO of slot 0, slot 1
+constexpr int kRingD = 4 * kTileBytes;      // D: slot 0 (32 floats), slot 1
+constexpr int kRingL = kRingD + 256;        // lse * log2(e), likewise
+constexpr int kRingBias = kRingL + 256;     // 64 floats per wave
+constexpr int kRingStage = kRingBias + kKvWaves * 256;
+
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+__global__ __launch_bounds__(64 * kKvWaves, 1) void bwd_dkdv_kernel(BackwardParams p) {
+  __shared__ __attribute__((aligned(1024))) unsigned char kv_lds[2 * kKvKeys * 256];  // K, then V
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[2 * kRingStage];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kb = wave & 3, slot = wave >> 2;
   const int col = lane & 31, hf = lane >> 5;
-  const WorkItem it = xcd_work_item();
-  const int j0 = it.tile * kRows;
-  const int npair = (p.G + 1) / 2;
-  const int hk = it.pair / npair;
-  const int hg = 2 * (it.pair % npair) + wave;
-  const bool has_head = hg < p.G;
-  const int h = hk * p.G + (has_head ? hg : hg - 1);
-  const int b = it.b;
+  // launch order: consecutive workgroups take the head pairs and KV heads of one key block
+  // (they run on consecutive XCDs); workgroup i + 8 takes the next key block with the same
+  // heads, so an XCD's L2 serves neighbouring key blocks that read the same query tiles
+  const int per_block = p.n_pairs * p.Hkv * p.B;
+  const int blk = (int)blockIdx.x / per_block;
+  int rem = (int)blockIdx.x % per_block;
+  const int hp = rem % p.n_pairs;
+  rem /= p.n_pairs;
+  const int hk = rem % p.Hkv;
+  const int b = rem / p.Hkv;
+  const int J0 = blk * kKvKeys;
+  const int j0w = J0 + 32 * kb;
   const int Lq = p.Lq, Lk = p.Lk, off = Lk - Lq;
   const int Weff = p.window > 0 ? p.window : 0x40000000;
-  // queries that see a key of this tile: positions j0 .. j0 + 31 + Weff - 1
-  const int q_lo = max(0, j0 - off);
-  const int q_hi = (int)min((long long)Lq - 1, (long long)j0 + kRows - 1 + Weff - 1 - off);
-  const size_t kv_row = (size_t)p.Hkv * kHeadDim;
-  const size_t q_row = (size_t)p.Hq * kHeadDim;
-  const uint16_t* kg = (const uint16_t*)p.k + ((size_t)b * Lk + j0) * kv_row + (size_t)hk * kHeadDim;
-  const uint16_t* vg = (const uint16_t*)p.v + ((size_t)b * Lk + j0) * kv_row + (size_t)hk * kHeadDim;
-  load_tile(wave == 0 ? kt : vt, wave == 0 ? kg : vg, kv_row, min(kRows, Lk - j0), lane);
-  const float* bias_h = p.bias + (size_t)h * p.R;
+  const bool has_head = 2 * hp + slot < p.G;
+  const int h = hk * p.G + min(2 * hp + slot, p.G - 1);  // a wave without a head loads slot 0's
+  const int h_slot0 = hk * p.G + 2 * hp;
+  const int h_slot1 = hk * p.G + min(2 * hp + 1, p.G - 1);
+  // query tiles that see a key of the workgroup: positions J0 .. J0 + 127 + W - 1
+  const int q_lo = max(0, J0 - off);
+  const int q_hi = (int)min((long long)Lq - 1, (long long)J0 + kKvKeys - 1 + Weff - 1 - off);
+  const int t_lo = q_lo / 32;
+  const int n_steps = q_lo <= q_hi ? q_hi / 32 - t_lo + 1 : 0;
+  const size_t q_row = (size_t)p.Hq * 256;   // bytes between queries of a head
+  const size_t kv_row = (size_t)p.Hkv * 256;
+  const unsigned char* zero_bytes = (const unsigned char*)kZeroRowB;
+  const uint32_t kv_base = lds_addr(kv_lds);
+  const uint32_t ring_base = lds_addr(ring);
+
+  // ---- K and V of the workgroup's keys (keys past Lk: zero rows) --------------------
+  {
+    const unsigned char* kg = (const unsigned char*)p.k + (((size_t)b * Lk + J0) * p.Hkv + hk) * 256;
+    const unsigned char* vg = (const unsigned char*)p.v + (((size_t)b * Lk + J0) * p.Hkv + hk) * 256;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int g = 8 * wave + i;  // instruction g of 64: K rows 4 g .. (g < 32), else V
+      const int m = g & 31;
+      const int r = 4 * m + (lane >> 4);
+      const int c = (lane & 15) ^ swz(r);
+      const unsigned char* src = (g < 32 ? kg : vg) + (size_t)r * kv_row + 16 * c;
+      if (J0 + r >= Lk) src = zero_bytes + 16 * c;
+      dma16(src, kv_base + (g < 32 ? 0 : kKvKeys * 256) + m * 1024);
+    }
+  }
+
+  // ---- per-step loads ---------------------------------------------------------------
+  // Q / dO tiles: wave w issues rows 16 (w & 1) .. + 15 of tile T = w >> 1 (Q slot 0, Q slot
+  // 1, dO slot 0, dO slot 1), four rows per instruction; lane i of instruction n fetches
+  // logical chunk (i & 15) ^ swz(row) of row 16 (w & 1) + 4 n + i / 16.
+  const int T = wave >> 1;
+  uint32_t voff[4];
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const int r = 16 * (wave & 1) + 4 * n + (lane >> 4);
+    voff[n] = (uint32_t)r * (uint32_t)q_row + 16u * (uint32_t)((lane & 15) ^ swz(r));
+  }
+  const int hT = (T & 1) ? h_slot1 : h_slot0;
+  const unsigned char* tsrc_base = (const unsigned char*)(T < 2 ? p.q : p.dout) + (size_t)hT * 256;
+  auto issue_step = [&](int s, int st) {
+    const int q0 = (t_lo + s) * 32;
+    const uint32_t stage = ring_base + st * kRingStage;
+    const unsigned char* src = uniform_ptr(tsrc_base + ((size_t)b * Lq + q0) * q_row);
+    const uint32_t dst = stage + (T < 2 ? kRingQ : kRingG) + (T & 1) * kTileBytes + (wave & 1) * 4096;
+    if (q0 + 32 <= Lq) {
+#pragma unroll
+      for (int n = 0; n < 4; ++n) dma16s(src, voff[n], dst + n * 1024);
+    } else {
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const int r = 16 * (wave & 1) + 4 * n + (lane >> 4);
+        const unsigned char* a = src + voff[n];
+        if (q0 + r >= Lq) a = zero_bytes + 16 * ((lane & 15) ^ swz(r));
+        dma16(a, dst + n * 1024);
+      }
+    }
+    if (wave < 2) {
+      // D (wave 0) or lse * log2(e) (wave 1) of the tile's 32 queries, for both slots
+      const int t = min(q0 + col, Lq - 1);
+      const float* a = (wave == 0 ? p.D : p.L2) + ((size_t)b * p.Hq + (hf ? h_slot1 : h_slot0)) * Lq + t;
+      dma4(a, stage + (wave == 0 ? kRingD : kRingL));
+    }
+    // this wave's bias slice: entry e = r[h, clamp(dbase + e, 0, R - 1)], the distance of
+    // query e - 31 + jj of the tile to key jj of the block being dbase + e
+    const int dbase = off + q0 - j0w - 31;
+    dma4(p.bias + (size_t)h * p.R + min(max(dbase + lane, 0), p.R - 1), stage + kRingBias + wave * 256);
+  };
+
+  // ---- per-lane LDS operand addresses -----------------------------------------------
+  // row read (A and B operands): row (lane & 31), logical chunk 2 ks + hf, at
+  // rowA ^ (32 ks) from the tile base
+  const uint32_t rowA = (uint32_t)col * 256u + 16u * (uint32_t)(hf ^ swz(lane & 15));
+  // transposed read (B operand of dV and dK): rows 16 qs + 4 hf + (m >> 2) (+ 8), columns
+  // 32 db + 16 u + 4 (m & 3), at (tr1 or tr2) ^ (64 db) + 4096 qs from the tile base
+  uint32_t tr1, tr2;
+  {
+    const int m = lane & 15, u = (lane >> 4) & 1;
+    const int y = 2 * u + ((m & 3) >> 1);
+    const int r1 = 4 * hf + (m >> 2), r2 = r1 + 8;
+    tr1 = (uint32_t)(r1 * 256 + 16 * (y ^ swz(r1)) + 8 * (m & 1));
+    tr2 = (uint32_t)(r2 * 256 + 16 * (y ^ swz(r2)) + 8 * (m & 1));
+  }
+  const uint32_t k_rows = kv_base + 32u * 256u * kb;
+  const uint32_t v_rows = k_rows + kKvKeys * 256;
+
   f32x16_t dk[4], dv[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) dk[db] = dv[db] = zero_f32x16();
-  const int j = j0 + col;  // this lane's key (accumulator column of S and dP)
-  for (int qi = q_lo / kRows; q_lo <= q_hi && qi <= q_hi / kRows; ++qi) {
-    const int q0 = qi * kRows;
-    const int nq = min(kRows, Lq - q0);
-    // One barrier per query tile keeps the two waves together (and, on the first tile, makes
-    // the other wave's K or V tile visible).  Everything else in LDS here (Q, dO, lse, D and
-    // the bias band) belongs to this wave alone, and the LDS serves one wave's requests in
-    // order, so between those only the compiler's order has to be kept (lds_order).
-    __syncthreads();
-    const size_t row0 = ((size_t)b * Lq + q0) * p.Hq + h;
-    const int dbase = off + q0 - j0 - (kRows - 1);
-    stage_bias(bias_s, bias_h, dbase, p.R, lane);
-    load_tile(qt, (const uint16_t*)p.q + row0 * kHeadDim, q_row, nq, lane);
-    load_tile(gt, (const uint16_t*)p.dout + row0 * kHeadDim, q_row, nq, lane);
-    if (lane < kRows) {
-      lse_s[lane] = lane < nq ? p.lse[row0 + (size_t)lane * p.Hq] * kLog2e : 0.f;
-      d_s[lane] = lane < nq ? p.D[row0 + (size_t)lane * p.Hq] : 0.f;
-    }
-    lds_order();
-    // S = Q K^T and dP = dO V^T: rows are queries, the lane's column is key j
-    f32x16_t s = zero_f32x16(), dp = zero_f32x16();
+
+  auto compute_step = [&](int s, int st) {
+    const int q0 = (t_lo + s) * 32;
+    const int pq0 = off + q0;  // position of the tile's query 0
+    // does any query of the tile see a key of this wave's block?
+    if (!has_head || pq0 + 31 < j0w || pq0 - (Weff - 1) > j0w + 31) return;
+    const bool edge = pq0 < j0w + 31 || pq0 + 31 - j0w >= Weff || q0 + 32 > Lq;
+    const uint32_t stage = ring_base + st * kRingStage;
+    const uint32_t qt = stage + kRingQ + slot * kTileBytes;
+    const uint32_t gt = stage + kRingG + slot * kTileBytes;
+    // S = Q K^T and dP = dO V^T: rows are the tile's queries, the lane's column its key
+    f32x16_t sacc = zero_f32x16(), dpacc = zero_f32x16();
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      s = mfma_32x32x16(row_operand(qt, ks, lane), row_operand(kt, ks, lane), s);
-      dp = mfma_32x32x16(row_operand(gt, ks, lane), row_operand(vt, ks, lane), dp);
+      const uint32_t o = rowA ^ (32u * ks);
+      sacc = mfma_32x32x16(lds_ld16(qt + o), lds_ld16(k_rows + o), sacc);
+      dpacc = mfma_32x32x16(lds_ld16(gt + o), lds_ld16(v_rows + o), dpacc);
     }
-    // register r holds query 8 (r >> 2) + 4 hf + (r & 3) of the tile
+    // register r holds query qq = 8 (r >> 2) + 4 hf + (r & 3) of the tile
+    const lds_f32_t* bsl = (const lds_f32_t*)(size_t)(stage + kRingBias + wave * 256);
+    const uint32_t dl_addr = stage + kRingD + slot * 128 + 16 * hf;
+    const uint32_t ll_addr = stage + kRingL + slot * 128 + 16 * hf;
     float pr[16], ds[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int qq = 8 * (r >> 2) + 4 * hf + (r & 3);
-      const int dist = off + q0 + qq - j;
-      const bool vis = qq < nq && dist >= 0 && dist < Weff;
-      const float lg = fmaf(s[r], p.scale_log2, fmaf(bias_s[qq - col + 31], kLog2e, -lse_s[qq]));
-      pr[r] = vis ? fast_exp2(lg) : 0.f;
-      // select, not multiply: an invisible pair stays zero even if dP - D is not finite
-      ds[r] = vis ? pr[r] * (dp[r] - d_s[qq]) : 0.f;
+    for (int g = 0; g < 4; ++g) {
+      const f32x4_t dq4 = __builtin_bit_cast(f32x4_t, lds_ld16(dl_addr + 32 * g));
+      const f32x4_t lq4 = __builtin_bit_cast(f32x4_t, lds_ld16(ll_addr + 32 * g));
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) {
+        const int r = 4 * g + c4;
+        const int qq = 8 * g + 4 * hf + c4;
+        const float bias = bsl[qq - col + 31];
+        const float lg = fmaf(sacc[r], p.scale_log2, fmaf(bias, kLog2e, -lq4[c4]));
+        float pv = fast_exp2(lg);
+        float dv_ = pv * (dpacc[r] - dq4[c4]);
+        if (edge) {
+          const int dist = pq0 + qq - (j0w + col);
+          const bool vis = (uint32_t)dist < (uint32_t)Weff && q0 + qq < Lq;
+          pv = vis ? pv : 0.f;
+          dv_ = vis ? dv_ : 0.f;
+        }
+        pr[r] = pv;
+        ds[r] = dv_;
+      }
     }
     // dV += P^T dO and dK += dS^T Q: rows are keys (the lane's P and dS), columns dims
 #pragma unroll
@@ -212,26 +328,67 @@ __global__ __launch_bounds__(2 * 64) void bwd_dkdv_kernel(BackwardParams p) {
       const u32x4_t as = pack_p_operand(ds + 8 * qs);
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        dv[db] = mfma_32x32x16(ap, load_vt_operand(gt, kStride, 16 * qs, 32 * db, lane), dv[db]);
-        dk[db] = mfma_32x32x16(as, load_vt_operand(qt, kStride, 16 * qs, 32 * db, lane), dk[db]);
+        const uint32_t o1 = (tr1 ^ (64u * db)) + 4096u * qs, o2 = (tr2 ^ (64u * db)) + 4096u * qs;
+        const u32x2_t g1 = lds_tr8(gt + o1), g2 = lds_tr8(gt + o2);
+        dv[db] = mfma_32x32x16(ap, u32x4_t{g1[0], g1[1], g2[0], g2[1]}, dv[db]);
+        const u32x2_t x1 = lds_tr8(qt + o1), x2 = lds_tr8(qt + o2);
+        dk[db] = mfma_32x32x16(as, u32x4_t{x1[0], x1[1], x2[0], x2[1]}, dk[db]);
       }
     }
+  };
+
+  // ---- the query-tile loop: step s computed from stage s & 1 while step s + 1 loads ----
+  if (n_steps > 0) issue_step(0, 0);
+  for (int s = 0; s < n_steps; ++s) {
+    vm_wait<0>();  // this wave's loads of step s (and, on the first step, of K and V)
+    wg_barrier();  // every wave's loads of step s are in LDS; every wave is done with step s - 1
+    if (s + 1 < n_steps) issue_step(s + 1, (s + 1) & 1);
+    compute_step(s, s & 1);
   }
-  if (!has_head) return;
-  // accumulator register 4 i + c of block db: key 8 i + 4 hf + c, dim 32 db + col
-  float* dkg = p.dk + ((size_t)b * Lk + j0) * kv_row + (size_t)hk * kHeadDim;
-  float* dvg = p.dv + ((size_t)b * Lk + j0) * kv_row + (size_t)hk * kHeadDim;
+  vm_wait<0>();
+
+  // ---- slot 1 hands its sums to slot 0; slot 0 writes the pair's partial ---------------
+  // accumulator register 4 i + c of block db: key 8 i + 4 hf + c of the block, dim 32 db + col
+  float* red = (float*)ring;
+  const size_t part_row = ((size_t)hp * p.B + b) * Lk;
+  auto hand_over = [&](f32x16_t (&acc)[4], float* part) {
+    __syncthreads();  // every wave is done with the ring
+    if (slot == 1) {
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = 8 * (r >> 2) + 4 * hf + (r & 3);
-      if (j0 + key < Lk) {
-        const size_t o = (size_t)key * kv_row + 32 * db + col;
-        unsafeAtomicAdd(dkg + o, dk[db][r] * kRsqrtD);
-        unsafeAtomicAdd(dvg + o, dv[db][r]);
-      }
+        for (int r = 0; r < 16; ++r) red[((kb * 4 + db) * 16 + r) * 64 + lane] = acc[db][r];
     }
+    __syncthreads();
+    if (slot == 0) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = j0w + 8 * (r >> 2) + 4 * hf + (r & 3);
+          const float x = acc[db][r] + red[((kb * 4 + db) * 16 + r) * 64 + lane];
+          if (j < Lk) part[((part_row + j) * p.Hkv + hk) * kHeadDim + 32 * db + col] = x;
+        }
+    }
+  };
+  hand_over(dk, p.part_dk);
+  hand_over(dv, p.part_dv);
+}
+
+// dk = (sum over head pairs of the partial dK) / sqrt(128), dv = sum of the partial dV, in
+// pair order; four consecutive floats per thread.
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(const float* part_dk, const float* part_dv, float* dk,
+                                                         float* dv, size_t n4, size_t plane, int n_pairs) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  f32x4_t a = ((const f32x4_t*)part_dk)[i];
+  f32x4_t c = ((const f32x4_t*)part_dv)[i];
+  for (int pp = 1; pp < n_pairs; ++pp) {
+    a += ((const f32x4_t*)(part_dk + (size_t)pp * plane))[i];
+    c += ((const f32x4_t*)(part_dv + (size_t)pp * plane))[i];
+  }
+  ((f32x4_t*)dk)[i] = a * kRsqrtD;
+  ((f32x4_t*)dv)[i] = c;
 }
 
 // Query-stationary pass: dQ and dr.  Grid (query tiles, Hkv * ceil(G / 2), B); a workgroup is two
@@ -279,8 +436,9 @@ __global__ __launch_bounds__(2 * 64) void bwd_dq_kernel(BackwardParams p) {
     }
   }
   const int pq = off + q0 + col;
-  const float lse2 = qvalid ? p.lse[row0 + (size_t)col * p.Hq] * kLog2e : 0.f;
-  const float dd = qvalid ? p.D[row0 + (size_t)col * p.Hq] : 0.f;
+  const size_t drow = ((size_t)b * p.Hq + h) * Lq + q0 + col;  // D and lse * log2(e) are head-major
+  const float lse2 = qvalid ? p.L2[drow] : 0.f;
+  const float dd = qvalid ? p.D[drow] : 0.f;
   const float* bias_h = p.bias + (size_t)h * p.R;
   float* dbias_h = p.dbias + (size_t)h * p.R;
   // keys the tile's queries see: positions off + q0 - Weff + 1 .. off + q0 + 31
@@ -366,16 +524,23 @@ hipError_t launch_backward(const BackwardParams& p, hipStream_t stream) {
     const size_t blocks = std::min((n + 255) / 256, (size_t)4096);
     hipLaunchKernelGGL(bwd_fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a, n);
   };
-  fill(p.dk, n_kv);
-  fill(p.dv, n_kv);
   fill(p.dbias, n_r);
-  if (p.B <= 0 || p.Lq <= 0 || p.Lk <= 0) return hipGetLastError();
+  if (p.B <= 0 || p.Lq <= 0 || p.Lk <= 0) {
+    fill(p.dk, n_kv);
+    fill(p.dv, n_kv);
+    return hipGetLastError();
+  }
   const size_t rows = (size_t)p.B * p.Lq * p.Hq;
   hipLaunchKernelGGL(bwd_rowdot_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream,
-                     (const uint16_t*)p.out, (const uint16_t*)p.dout, p.D, rows);
+                     (const uint16_t*)p.out, (const uint16_t*)p.dout, p.lse, p.D, p.L2, p.Lq, p.Hq, rows);
+  const long long blocks = (p.Lk + kKvKeys - 1) / kKvKeys;
+  const long long grid = blocks * p.Hkv * p.n_pairs * p.B;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)grid), dim3(64 * kKvWaves), 0, stream, p);
+  const size_t n4 = n_kv / 4;
+  hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream,
+                     (const float*)p.part_dk, (const float*)p.part_dv, p.dk, p.dv, n4, n_kv, p.n_pairs);
   const unsigned pairs = (unsigned)(p.Hkv * ((p.G + 1) / 2));
-  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)((p.Lk + kRows - 1) / kRows), pairs, (unsigned)p.B), dim3(128),
-                     0, stream, p);
   hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)((p.Lq + kRows - 1) / kRows), pairs, (unsigned)p.B), dim3(128), 0,
                      stream, p);
   return hipGetLastError();

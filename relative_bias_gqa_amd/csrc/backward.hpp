@@ -18,7 +18,11 @@ struct BackwardParams {
   float* dk;          // [B, Lk, Hkv, 128]
   float* dv;          // [B, Lk, Hkv, 128]
   float* dbias;       // [Hq, R]
-  float* D;           // [B, Lq, Hq] workspace: rowsum(dout * out)
+  float* D;           // [B, Hq, Lq] workspace: rowsum(dout * out) (head-major)
+  float* L2;          // [B, Hq, Lq] workspace: lse * log2(e)
+  float* part_dk;     // [n_pairs, B, Lk, Hkv, 128] workspace: dK of each query-head pair (unscaled)
+  float* part_dv;     // [n_pairs, B, Lk, Hkv, 128] workspace: dV of each query-head pair
+  int n_pairs;        // ceil(G / 2)
   int B, Lq, Lk, Hq, Hkv, G, R, window;
   float scale_log2;   // log2(e) / sqrt(128)
 };

@@ -212,6 +212,15 @@ __device__ __forceinline__ void dma4s(const void* base, uint32_t off, uint32_t l
       : "memory");
 }
 
+// A pointer that is the same in every lane, made provably so (SGPR pair) for the scalar
+// base operand of dma16s / dma4s.
+__device__ __forceinline__ const unsigned char* uniform_ptr(const void* p) {
+  const uint64_t a = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return (const unsigned char*)(uintptr_t)(((uint64_t)hi << 32) | (uint64_t)lo);
+}
+
 // Wave-uniform 32-bit load through the scalar cache (lgkmcnt), so that it does not wait
 // behind the LDS-bound loads in flight.
 __device__ __forceinline__ int uniform_load_i32(const int* ptr) {

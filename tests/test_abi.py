@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.rattn_abi_version() == rb.ABI_VERSION == 8
+    assert lib.rattn_abi_version() == rb.ABI_VERSION == 9
 
 
 def _prefill(lib, **kw):
@@ -342,7 +342,12 @@ def test_backward_validation(lib, kw, status, needle):
 
 
 def test_backward_workspace_formula():
-    assert rb.rattn_prefill_backward_workspace_bytes(1, 8192, 16) == 8192 * 16 * 4
-    assert rb.rattn_prefill_backward_workspace_bytes(1, 3, 1) == 256
-    assert rb.rattn_prefill_backward_workspace_bytes(0, 0, 0) == 256
-    assert rb.rattn_prefill_backward_workspace_bytes(-1, 1, 1) == 0
+    # D and lse*log2(e) per row, then ceil(G/2) partial dK and dV planes [B, Lk, Hkv, 128] fp32
+    rows = 8192 * 16 * 4
+    plane = 8192 * 2 * 128 * 4
+    assert rb.rattn_prefill_backward_workspace_bytes(1, 8192, 8192, 16, 2) == 2 * rows + 2 * 4 * plane
+    # 3 rows: two 256-byte row parts; one pair: two planes of 5 keys x 128 x 4 B = 2560 -> 2560
+    assert rb.rattn_prefill_backward_workspace_bytes(1, 3, 5, 1, 1) == 256 + 256 + 2560 + 2560
+    assert rb.rattn_prefill_backward_workspace_bytes(0, 0, 0, 1, 1) == 256
+    assert rb.rattn_prefill_backward_workspace_bytes(-1, 1, 1, 1, 1) == 0
+    assert rb.rattn_prefill_backward_workspace_bytes(1, 1, 1, 3, 2) == 0  # Hq not a multiple of Hkv

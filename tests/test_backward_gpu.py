@@ -174,7 +174,7 @@ def test_backward_nan_gradient_row_stays_in_bounds():
     dq = torch.empty(q.shape, dtype=torch.float32, device="cuda")
     dk = torch.empty(k.shape, dtype=torch.float32, device="cuda")
     dv = torch.empty(v.shape, dtype=torch.float32, device="cuda")
-    ws = torch.empty(rb.rattn_prefill_backward_workspace_bytes(B, Lq, Hq), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(rb.rattn_prefill_backward_workspace_bytes(B, Lq, Lk, Hq, Hkv), dtype=torch.uint8, device="cuda")
     rb.rattn_prefill_backward(q, k, v, r, out, dout, lse, dq, dk, dv, dbias, window, ws)
     torch.cuda.synchronize()
     g = host(buf)
@@ -200,7 +200,7 @@ def test_backward_empty_chunk_zeroes_gradients():
     dk = torch.full((1, Lk, Hkv, 128), float("nan"), device="cuda")
     dv = torch.full_like(dk, float("nan"))
     dr = torch.full((Hq, R), float("nan"), device="cuda")
-    ws = torch.empty(rb.rattn_prefill_backward_workspace_bytes(1, 0, Hq), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(rb.rattn_prefill_backward_workspace_bytes(1, 0, Lk, Hq, Hkv), dtype=torch.uint8, device="cuda")
     # zero-size tensors may have no storage: pass a live one-element pointer for q, out, dout, lse, dq
     dummy = torch.zeros(1, device="cuda")
     rc = rb.load().rattn_prefill_backward(q.data_ptr() or dummy.data_ptr(), k.data_ptr(), v.data_ptr(),
