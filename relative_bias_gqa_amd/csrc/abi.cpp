@@ -593,6 +593,14 @@ int rattn_prefill_backward(const void* q, const void* k, const void* v, const fl
   p.part_dk = (float*)((char*)workspace + lay.pk_off);
   p.part_dv = (float*)((char*)workspace + lay.pv_off);
   p.n_pairs = lay.n_pairs;
+  {
+    rattn::PrefillParams shape;  // the forward's head / token grouping
+    prefill_shape(B, Lq, Lk, Hq, Hkv, window, &shape);
+    p.hpw = shape.hpw;
+    p.tsub = shape.tsub;
+    p.n_hg = shape.n_hg;
+    p.n_tok_tiles = shape.n_tok_tiles;
+  }
   p.B = B;
   p.Lq = Lq;
   p.Lk = Lk;

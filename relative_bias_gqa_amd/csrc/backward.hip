@@ -10,23 +10,22 @@
 // dK and dV summed over the query heads of a KV head.  P is recomputed from the forward's
 // log-sum-exp, never stored.
 //
-// Three passes on the caller's stream, after a fill that zeroes dk, dv and dr:
-//   1. D per query row (fp32, from the bf16 out and dout);
-//   2. key-stationary: one wave per (32 keys, query head), two heads of a KV head per
-//      workgroup sharing the K/V tiles, walks the query tiles that see its keys; S = Q K^T
-//      and dP = dO V^T come out with one key per lane (the accumulator column), which is
-//      the register layout the A operand of dV += P^T dO and dK += dS^T Q needs, so P and
-//      dS feed the MFMAs straight from registers; dO and Q are read transposed from LDS for
-//      the B operand.  dK and dV of the wave's head are added into dk, dv at the end (fp32
-//      atomics, one add per element per query head);
-//   3. query-stationary: one wave per (32 queries, query head), paired the same way, walks
-//      the key tiles its queries see; S^T and dP^T come out with one query per lane, the
-//      B-operand layout of dQ^T += K^T dS^T, so dQ is accumulated in registers and stored
-//      once; dS is also summed per distance through a skewed table in LDS (one row per
-//      diagonal of the 32 x 32 tile) and the 63 row sums added into dr.
+// Passes on the caller's stream:
+//   1. D = rowsum(dout * out) and lse * log2(e) per query row (fp32, head-major);
+//   2. key-stationary dK, dV: a workgroup owns 128 keys of a KV head and a pair of its query
+//      heads (8 waves = 4 blocks of 32 keys x 2 heads); K and V stay in LDS, the query
+//      tiles that see them stream in by direct-to-LDS DMA; S = Q K^T and dP = dO V^T come
+//      out with one key per lane, the A-operand layout of dV += P^T dO and dK += dS^T Q, so P
+//      and dS feed those MFMAs from registers (dO and Q read transposed from LDS); each pair
+//      writes a partial dK, dV and a reduce kernel sums the pairs in order (deterministic);
+//   3. query-stationary dQ and dr: the forward's decomposition (8 waves, one query head x 32
+//      queries each, Q^T and dO^T resident in registers), K and V streamed through an LDS
+//      ring; S^T and dP^T come out with one query per lane, the B-operand layout of
+//      dQ^T += K^T dS^T, so dQ stays in registers and is stored once; dS is also summed per
+//      distance through a skewed table in LDS and the 63 row sums added into dr (fp32
+//      atomics: dr's last bits may change from run to run).
 // All products are v_mfma_f32_32x32x16_bf16 with fp32 accumulation; P and dS are rounded to
-// bf16 as MFMA operands.  Tiles sit in LDS with 272-byte rows (256 bytes of data and 16 of
-// padding) so that the row-wise operand reads of 32 consecutive rows spread over the banks.
+// bf16 as MFMA operands.
 #include <algorithm>
 
 #include "backward.hpp"
@@ -37,72 +36,15 @@ namespace {
 
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kRows = 32;                  // keys or queries per wave tile
-constexpr int kStride = 136;               // LDS row stride of a 128-wide bf16 tile (elements)
-constexpr int kTileElems = kRows * kStride;
 constexpr float kRsqrtD = 0.08838834764831845f;  // 1 / sqrt(128)
 constexpr int kDiagStride = 34;            // floats per row of the diagonal table (conflict free)
 
 // 256 bytes of zeros: the source of every K/V row past Lk and query row past Lq.
 __device__ __attribute__((aligned(256))) const uint32_t kZeroRowB[64] = {0};
 
-// The 63 bias entries a 32 x 32 tile meets: entry e = r[h, clamp(dbase + e, 0, R - 1)] for the
-// pairs at distance dbase + e, dbase = (distance of query 0 to key 31).  Lanes 0..62 load one.
-__device__ __forceinline__ void stage_bias(float* band, const float* bias_h, int dbase, int R, int lane) {
-  if (lane < 63) band[lane] = bias_h[min(max(dbase + lane, 0), R - 1)];
-}
-
-// 32 rows of 128 bf16 from global memory (row r at src + r * row_stride) into an LDS tile;
-// rows at or past n_valid are zero.  One wave, 16 bytes per lane per pass.
-__device__ __forceinline__ void load_tile(uint16_t* tile, const uint16_t* src, size_t row_stride, int n_valid,
-                                          int lane) {
-#pragma unroll
-  for (int pass = 0; pass < 8; ++pass) {
-    const int idx = pass * 64 + lane;
-    const int row = idx >> 4, c = idx & 15;
-    u32x4_t x = zero_u32x4();
-    if (row < n_valid) x = *(const u32x4_t*)(src + row * row_stride + c * 8);
-    *(u32x4_t*)(tile + row * kStride + c * 8) = x;
-  }
-}
-
-// Operand of k-step ks read along rows: lane l gets row (l & 31), elements 16 ks + 8 (l >> 5)
-// .. + 7.  The A operand (rows of the product) and the B operand (columns) of
-// v_mfma_f32_32x32x16_bf16 both take this form when the tile is stored row by row.
-__device__ __forceinline__ u32x4_t row_operand(const uint16_t* tile, int ks, int lane) {
-  return *(const u32x4_t*)(tile + (lane & 31) * kStride + 16 * ks + 8 * (lane >> 5));
-}
-
 // Keeps the compiler from moving memory accesses across this point.  Used between LDS
 // accesses of one wave, which the LDS performs in the wave's order.
 __device__ __forceinline__ void lds_order() { asm volatile("" ::: "memory"); }
-
-// Work item of this workgroup.  Workgroup i of a launch runs on XCD i mod 8 (each XCD has its
-// own L2), so consecutive work items (neighbouring tiles of one head pair, which read mostly
-// the same Q / dO or K / V tiles at the same time) are given to one XCD: XCD x takes a
-// contiguous range of the items, in launch order.  A bijection for any grid size.
-struct WorkItem {
-  int tile, pair, b;
-};
-__device__ __forceinline__ WorkItem xcd_work_item() {
-  const int n = gridDim.x * gridDim.y * gridDim.z;
-  const int L = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
-  const int per = n / 8, rem = n % 8, x = L % 8;
-  const int w = (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + L / 8;
-  WorkItem it;
-  it.tile = w % gridDim.x;
-  it.pair = (w / gridDim.x) % gridDim.y;
-  it.b = w / (gridDim.x * gridDim.y);
-  return it;
-}
-// The work item in launch order (consecutive tiles on consecutive XCDs).
-__device__ __forceinline__ WorkItem launch_order_work_item() {
-  WorkItem it;
-  it.tile = blockIdx.x;
-  it.pair = blockIdx.y;
-  it.b = blockIdx.z;
-  return it;
-}
 
 __global__ __launch_bounds__(256) void bwd_fill_zero_kernel(float* a, size_t n) {
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) a[i] = 0.f;
@@ -391,116 +333,198 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(const float* part_dk, c
   ((f32x4_t*)dv)[i] = c;
 }
 
-// Query-stationary pass: dQ and dr.  Grid (query tiles, Hkv * ceil(G / 2), B); a workgroup is two
-// waves, each one query head of the same KV head, sharing the K and V tiles (wave 0 loads
-// K, wave 1 V).  With an odd G the second wave of the last pair runs along and stores nothing.
-__global__ __launch_bounds__(2 * 64) void bwd_dq_kernel(BackwardParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t kt[kTileElems];
-  __shared__ __attribute__((aligned(16))) uint16_t vt[kTileElems];
-  __shared__ float bias_w[2][64];
-  // dS of the tile by diagonal: row e = col - jj + 31 (distance dbase + e), column col (the
-  // query); the cells of row e that no pair maps to (columns outside e - 31 .. e) are skipped
-  __shared__ __attribute__((aligned(16))) float diag_w[2][63 * kDiagStride];
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-  float* bias_s = bias_w[wave];
-  float* diag = diag_w[wave];
+// ---- query-stationary pass (dQ, dr) -----------------------------------------------------
+// The forward's decomposition: a workgroup of 8 waves owns one KV head, hpw of its query heads
+// and 32 * tsub queries (hpw * tsub = 8); each wave owns one query head x 32 queries, its Q^T
+// and dO^T operands resident in registers, and walks the 32-key tiles its workgroup sees.
+// K, V and each wave's 63-entry bias slice of a tile are loaded straight into LDS
+// (global_load_lds) through a ring of three stages, two tiles ahead, and serve every wave
+// (GQA packing).  Per tile a wave computes S^T = K Q^T and dP^T = V dO^T with one query per
+// lane (the accumulator column), P and dS, dQ^T += K^T dS^T (K read transposed; dQ stays in
+// registers and is stored once), and sums dS along the tile's 63 diagonals through a skewed
+// table in LDS (row = diagonal, column = the lane's query, 34 floats per row) into dr, one
+// fp32 atomic per diagonal.  K rows are read both row-wise and transposed: the tile uses the
+// swizzle of the key-stationary pass.
+constexpr int kDqWaves = 8;
+constexpr int kDqStages = 3;
+constexpr int kDqKV = 32 * 256;                       // a K (or V) tile: 32 keys x 256 B
+constexpr int kDqBias = 2 * kDqKV;                    // bias slices: 64 floats per wave
+constexpr int kDqStage = kDqBias + kDqWaves * 256;
+constexpr int kDqLoads = 3;                           // DMA loads per wave and tile
+
+__global__ __launch_bounds__(64 * kDqWaves, 1) void bwd_dq_kernel(BackwardParams p) {
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[kDqStages * kDqStage];
+  // dS of a tile by diagonal: row e = col - jj + 31 (distance dbase + e), column col (the
+  // query).  The cells of row e that no pair maps to (columns outside e - 31 .. e) are the
+  // same in every tile and never written: zeroed once, they let a row sum take all 32 columns.
+  __shared__ __attribute__((aligned(16))) float diag_w[kDqWaves][63 * kDiagStride];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, hf = lane >> 5;
-  // (the XCD-contiguous order measured 15 % slower here than launch order: every XCD then
-  // walks one head pair's tiles from light to heavy and the heaviest come last)
-  const WorkItem it = launch_order_work_item();
-  const int q0 = it.tile * kRows;
-  const int npair = (p.G + 1) / 2;
-  const int hk = it.pair / npair;
-  const int hg = 2 * (it.pair % npair) + wave;
-  const bool has_head = hg < p.G;
-  const int h = hk * p.G + (has_head ? hg : hg - 1);
-  const int b = it.b;
+  float* diag = diag_w[wave];
+  for (int i = lane; i < 63 * kDiagStride; i += 64) diag[i] = 0.f;  // this wave's own table
+  // job: heaviest (last) token tiles first
+  const int per_tile = p.B * p.Hkv * p.n_hg;
+  const int tile = p.n_tok_tiles - 1 - (int)blockIdx.x / per_tile;
+  const int rem = (int)blockIdx.x % per_tile;
+  const int hg = rem % p.n_hg;
+  const int hk = (rem / p.n_hg) % p.Hkv;
+  const int b = rem / (p.n_hg * p.Hkv);
+  const int h = hk * p.G + hg * p.hpw + (wave % p.hpw);
   const int Lq = p.Lq, Lk = p.Lk, off = Lk - Lq;
-  const int nq = min(kRows, Lq - q0);
+  const int T0 = tile * 32 * p.tsub;
+  const int T1 = min(Lq, T0 + 32 * p.tsub);
+  const int q0 = T0 + (wave / p.hpw) * 32;  // this wave's first query
+  const int nq = min(32, Lq - q0);         // its queries (may be <= 0)
   const int Weff = p.window > 0 ? p.window : 0x40000000;
-  const size_t kv_row = (size_t)p.Hkv * kHeadDim;
+  const bool qvalid = col < nq;
   const size_t q_row = (size_t)p.Hq * kHeadDim;
   const size_t row0 = ((size_t)b * Lq + q0) * p.Hq + h;
-  // this lane's query (accumulator column of S^T and dP^T)
-  const bool qvalid = col < nq;
   // Q^T and dO^T operands (lane: its query, dims 16 ks + 8 hf ..), resident for the key loop
   u32x4_t qr[8], gr[8];
   {
-    const uint16_t* qs = (const uint16_t*)p.q + (row0 + (size_t)(qvalid ? col : 0) * p.Hq) * kHeadDim + 8 * hf;
-    const uint16_t* gs = (const uint16_t*)p.dout + (row0 + (size_t)(qvalid ? col : 0) * p.Hq) * kHeadDim + 8 * hf;
+    const size_t rq = row0 + (size_t)(qvalid ? col : 0) * p.Hq;
+    const uint16_t* qs = (const uint16_t*)p.q + rq * kHeadDim + 8 * hf;
+    const uint16_t* gs = (const uint16_t*)p.dout + rq * kHeadDim + 8 * hf;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       qr[ks] = qvalid ? *(const u32x4_t*)(qs + 16 * ks) : zero_u32x4();
       gr[ks] = qvalid ? *(const u32x4_t*)(gs + 16 * ks) : zero_u32x4();
     }
   }
-  const int pq = off + q0 + col;
-  const size_t drow = ((size_t)b * p.Hq + h) * Lq + q0 + col;  // D and lse * log2(e) are head-major
-  const float lse2 = qvalid ? p.L2[drow] : 0.f;
-  const float dd = qvalid ? p.D[drow] : 0.f;
-  const float* bias_h = p.bias + (size_t)h * p.R;
+  const size_t drow = ((size_t)b * p.Hq + h) * Lq + q0 + col;  // D and lse * log2(e): head-major
+  float lse2 = qvalid ? p.L2[drow] : 0.f;
+  float dd = qvalid ? p.D[drow] : 0.f;
+  // pin the waits for these loads here, before any LDS-bound load is in flight
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) asm volatile("" : "+v"(qr[ks]), "+v"(gr[ks]));
+  asm volatile("" : "+v"(lse2), "+v"(dd));
+  const int pq = off + q0 + col;  // this lane's query position
   float* dbias_h = p.dbias + (size_t)h * p.R;
-  // keys the tile's queries see: positions off + q0 - Weff + 1 .. off + q0 + 31
-  const int j_lo = max(0, off + q0 - Weff + 1);
-  const int j_hi = min(Lk - 1, off + q0 + nq - 1);
-  const uint16_t* kg = (const uint16_t*)p.k + (size_t)b * Lk * kv_row + (size_t)hk * kHeadDim;
-  const uint16_t* vg = (const uint16_t*)p.v + (size_t)b * Lk * kv_row + (size_t)hk * kHeadDim;
+  // key tiles of the workgroup, and of this wave
+  const int kt_begin = max(0, off + T0 - Weff + 1) / 32;
+  const int n_tiles = T0 < T1 ? (off + T1 - 1) / 32 + 1 - kt_begin : 0;
+  const int wj_lo = max(0, off + q0 - Weff + 1), wj_hi = off + q0 + max(nq, 1) - 1;
+
+  // ---- tile loads: waves 0-3 issue K, waves 4-7 V, two instructions of 4 keys each ----
+  const size_t kv_row = (size_t)p.Hkv * 256;  // bytes between keys
+  const unsigned char* kvg = (const unsigned char*)(wave < 4 ? p.k : p.v) + ((size_t)b * Lk * p.Hkv + hk) * 256;
+  const unsigned char* zero_bytes = (const unsigned char*)kZeroRowB;
+  const uint32_t ring_base = lds_addr(ring);
+  uint32_t koff[2];
+  int krow[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = 4 * (2 * (wave & 3) + i) + (lane >> 4);
+    krow[i] = r;
+    koff[i] = (uint32_t)r * (uint32_t)kv_row + 16u * (uint32_t)((lane & 15) ^ swz(r));
+  }
+  auto issue_tile = [&](int kt, int st) {
+    const int j0 = kt * 32;
+    const uint32_t stage = ring_base + st * kDqStage;
+    const uint32_t dst = stage + (wave < 4 ? 0 : kDqKV) + (wave & 3) * 2048;
+    const unsigned char* base = uniform_ptr(kvg + (size_t)j0 * kv_row);
+    if (j0 + 32 <= Lk) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) dma16s(base, koff[i], dst + i * 1024);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const unsigned char* a = base + koff[i];
+        if (j0 + krow[i] >= Lk) a = zero_bytes + 16 * ((lane & 15) ^ swz(krow[i]));
+        dma16(a, dst + i * 1024);
+      }
+    }
+    // this wave's bias slice: entry e = r[h, clamp(dbase + e, 0, R - 1)]
+    const int dbase = off + q0 - j0 - 31;
+    dma4(p.bias + (size_t)h * p.R + min(max(dbase + lane, 0), p.R - 1), stage + kDqBias + wave * 256);
+  };
+
+  // ---- per-lane LDS operand addresses (tile-relative, as in the key-stationary pass) ----
+  const uint32_t rowA = (uint32_t)col * 256u + 16u * (uint32_t)(hf ^ swz(lane & 15));
+  uint32_t tr1, tr2;
+  {
+    const int m = lane & 15, u = (lane >> 4) & 1;
+    const int y = 2 * u + ((m & 3) >> 1);
+    const int r1 = 4 * hf + (m >> 2), r2 = r1 + 8;
+    tr1 = (uint32_t)(r1 * 256 + 16 * (y ^ swz(r1)) + 8 * (m & 1));
+    tr2 = (uint32_t)(r2 * 256 + 16 * (y ^ swz(r2)) + 8 * (m & 1));
+  }
+
   f32x16_t dq[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) dq[db] = zero_f32x16();
-  for (int kti = j_lo / kRows; j_lo <= j_hi && kti <= j_hi / kRows; ++kti) {
-    const int j0 = kti * kRows;
-    __syncthreads();  // the previous tile's reads of kt, vt and bias_s are done
-    load_tile(wave == 0 ? kt : vt, (wave == 0 ? kg : vg) + (size_t)j0 * kv_row, kv_row, min(kRows, Lk - j0), lane);
-    const int dbase = off + q0 - j0 - (kRows - 1);
-    stage_bias(bias_s, bias_h, dbase, p.R, lane);
-    __syncthreads();
+
+  auto compute_tile = [&](int kt, int st) {
+    const int j0 = kt * 32;
+    if (!(nq > 0) || j0 > wj_hi || j0 + 31 < wj_lo) return;
+    const bool edge = j0 + 31 > off + q0 || j0 < off + q0 + nq - 1 - Weff + 1 || nq < 32;
+    const uint32_t stage = ring_base + st * kDqStage;
+    const uint32_t kt_lds = stage, vt_lds = stage + kDqKV;
     // S^T = K Q^T and dP^T = V dO^T: rows are keys, the lane's column is its query
-    f32x16_t st = zero_f32x16(), dpt = zero_f32x16();
+    f32x16_t st_acc = zero_f32x16(), dpt = zero_f32x16();
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      st = mfma_32x32x16(row_operand(kt, ks, lane), qr[ks], st);
-      dpt = mfma_32x32x16(row_operand(vt, ks, lane), gr[ks], dpt);
+      const uint32_t o = rowA ^ (32u * ks);
+      st_acc = mfma_32x32x16(lds_ld16(kt_lds + o), qr[ks], st_acc);
+      dpt = mfma_32x32x16(lds_ld16(vt_lds + o), gr[ks], dpt);
     }
-    // register r holds key j0 + 8 (r >> 2) + 4 hf + (r & 3)
+    // register r holds key j0 + jj, jj = 8 (r >> 2) + 4 hf + (r & 3)
+    const lds_f32_t* bsl = (const lds_f32_t*)(size_t)(stage + kDqBias + wave * 256);
     float ds[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int jj = 8 * (r >> 2) + 4 * hf + (r & 3);
-      const int dist = pq - (j0 + jj);
-      const bool vis = qvalid && dist >= 0 && dist < Weff;
-      const float lg = fmaf(st[r], p.scale_log2, fmaf(bias_s[col - jj + 31], kLog2e, -lse2));
-      const float pr = vis ? fast_exp2(lg) : 0.f;
-      ds[r] = vis ? pr * (dpt[r] - dd) : 0.f;
-      diag[(col - jj + 31) * kDiagStride + col] = ds[r];
+      const float lg = fmaf(st_acc[r], p.scale_log2, fmaf(bsl[col - jj + 31], kLog2e, -lse2));
+      float x = fast_exp2(lg) * (dpt[r] - dd);
+      if (edge) {
+        const int dist = pq - (j0 + jj);
+        const bool vis = qvalid && (uint32_t)dist < (uint32_t)Weff;
+        x = vis ? x : 0.f;
+      }
+      ds[r] = x;
+      diag[(col - jj + 31) * kDiagStride + col] = x;
     }
     // dQ^T += K^T dS^T: rows are dims (K read transposed), the lane's column its query
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const u32x4_t bs = pack_p_operand(ds + 8 * ks);
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
-        dq[db] = mfma_32x32x16(load_vt_operand(kt, kStride, 16 * ks, 32 * db, lane), bs, dq[db]);
+      for (int db = 0; db < 4; ++db) {
+        const uint32_t o1 = (tr1 ^ (64u * db)) + 4096u * ks, o2 = (tr2 ^ (64u * db)) + 4096u * ks;
+        const u32x2_t a1 = lds_tr8(kt_lds + o1), a2 = lds_tr8(kt_lds + o2);
+        dq[db] = mfma_32x32x16(u32x4_t{a1[0], a1[1], a2[0], a2[1]}, bs, dq[db]);
+      }
     }
     // dr: lane e < 63 sums row e of the table (the pairs at distance dbase + e; invisible pairs
-    // hold zero).  The table is this wave's own and the
-    // LDS serves a wave's requests in order, so only the compiler's order is kept here.
+    // hold zero).  The table is this wave's own and the LDS serves a wave's requests in
+    // order, so only the compiler's order is kept here.
     lds_order();
+    const int dbase = off + q0 - j0 - 31;
     if (lane < 63) {
-      float x = 0.f;
+      f32x2_t acc = {0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < kRows; c += 2) {
-        const f32x2_t y = *(const f32x2_t*)(diag + lane * kDiagStride + c);
-        const int jj0 = c - lane + 31;  // key of column c
-        x += ((unsigned)jj0 < (unsigned)kRows ? y[0] : 0.f) + ((unsigned)(jj0 + 1) < (unsigned)kRows ? y[1] : 0.f);
-      }
+      for (int c = 0; c < 32; c += 2) acc += *(const f32x2_t*)(diag + lane * kDiagStride + c);
+      const float x = acc[0] + acc[1];
       // rows of the table at negative distances hold only invisible pairs: never added
-      if (has_head && dbase + lane >= 0 && x != 0.f) unsafeAtomicAdd(dbias_h + min(dbase + lane, p.R - 1), x);
+      if (dbase + lane >= 0 && x != 0.f) unsafeAtomicAdd(dbias_h + min(dbase + lane, p.R - 1), x);
     }
     lds_order();  // the next tile's table stores come after these reads
+  };
+
+  // ---- key loop: tile t computed from stage t % 3 while tiles t + 1, t + 2 load ----------
+  const int prologue = min(2, n_tiles);
+  for (int i = 0; i < prologue; ++i) issue_tile(kt_begin + i, i);
+  for (int t = 0; t < n_tiles; ++t) {
+    // tile t's loads are done; tile t + 1's (and at most one dr atomic) may be in flight
+    if (t + 1 < n_tiles) vm_wait<kDqLoads>();
+    else vm_wait<0>();
+    wg_barrier();  // tile t is in LDS for every wave; every wave is done with tile t - 1
+    if (t + 2 < n_tiles) issue_tile(kt_begin + t + 2, (t + 2) % kDqStages);
+    compute_tile(kt_begin + t, t % kDqStages);
   }
-  if (!qvalid || !has_head) return;
+  if (!qvalid) return;
   // accumulator register 4 i + c of block db: dim 32 db + 8 i + 4 hf + c of query q0 + col
   float* dqg = p.dq + (row0 + (size_t)col * p.Hq) * kHeadDim;
 #pragma unroll
@@ -540,9 +564,9 @@ hipError_t launch_backward(const BackwardParams& p, hipStream_t stream) {
   const size_t n4 = n_kv / 4;
   hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream,
                      (const float*)p.part_dk, (const float*)p.part_dv, p.dk, p.dv, n4, n_kv, p.n_pairs);
-  const unsigned pairs = (unsigned)(p.Hkv * ((p.G + 1) / 2));
-  hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)((p.Lq + kRows - 1) / kRows), pairs, (unsigned)p.B), dim3(128), 0,
-                     stream, p);
+  const long long dq_grid = (long long)p.n_tok_tiles * p.B * p.Hkv * p.n_hg;
+  if (dq_grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)dq_grid), dim3(64 * kDqWaves), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -23,6 +23,9 @@ struct BackwardParams {
   float* part_dk;     // [n_pairs, B, Lk, Hkv, 128] workspace: dK of each query-head pair (unscaled)
   float* part_dv;     // [n_pairs, B, Lk, Hkv, 128] workspace: dV of each query-head pair
   int n_pairs;        // ceil(G / 2)
+  // query-stationary pass: a workgroup takes hpw query heads x 32 * tsub queries (hpw * tsub
+  // = 8 waves), n_hg = G / hpw head groups per KV head, n_tok_tiles token tiles
+  int hpw, tsub, n_hg, n_tok_tiles;
   int B, Lq, Lk, Hq, Hkv, G, R, window;
   float scale_log2;   // log2(e) / sqrt(128)
 };
