@@ -249,8 +249,10 @@ size_t rattn_prefill_backward_workspace_bytes(int B, int Lq, int Lk, int Hq, int
  * The caller owns every buffer; the call enqueues its kernels on `stream` and returns.
  * dq, dk and dv are deterministic (dk and dv: per-pair partials summed in pair order);
  * dbias is a sum of fp32 atomic adds, so its last bits may differ from run to run.
- * A non-finite dout or out row makes the gradients that depend on it non-finite; nothing
- * is ever written outside dq, dk, dv, dbias and the workspace.  Status: INVALID_ARG (null
+ * A non-finite dout or out row makes the gradients that depend on it non-finite, and may do
+ * so for dk, dv and dbias entries of the same query head's 32 x 32 (query, key) tiles that it
+ * does not reach (a product with a zero probability is still non-finite); nothing is ever
+ * written outside dq, dk, dv, dbias and the workspace.  Status: INVALID_ARG (null
  * pointer, sizes, Lq > Lk, B or Hq > 65535), UNSUPPORTED (head_dim != 128), WORKSPACE
  * (missing or too small), HIP (launch failure).
  */

@@ -41,6 +41,11 @@ constexpr int kDiagStride = 34;            // floats per row of the diagonal tab
 
 // 256 bytes of zeros: the source of every K/V row past Lk and query row past Lq.
 __device__ __attribute__((aligned(256))) const uint32_t kZeroRowB[64] = {0};
+// The masks live in the data: a bias-slice entry at a distance no visible pair has
+// (negative, or >= the window) is loaded as -inf, and lse * log2(e) of a query row past Lq as
+// +inf, so exp2 gives P = 0 (hence dS = 0) for every invisible pair with no select.
+__device__ const float kNegInfF = -__builtin_inff();
+__device__ const float kPosInfF = __builtin_inff();
 
 // Keeps the compiler from moving memory accesses across this point.  Used between LDS
 // accesses of one wave, which the LDS performs in the wave's order.
@@ -187,15 +192,19 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void bwd_dkdv_kernel(BackwardPara
       }
     }
     if (wave < 2) {
-      // D (wave 0) or lse * log2(e) (wave 1) of the tile's 32 queries, for both slots
-      const int t = min(q0 + col, Lq - 1);
+      // D (wave 0) or lse * log2(e) (wave 1) of the tile's 32 queries, for both slots; rows
+      // past Lq: D = 0, lse * log2(e) = +inf
+      const int t = q0 + col;
       const float* a = (wave == 0 ? p.D : p.L2) + ((size_t)b * p.Hq + (hf ? h_slot1 : h_slot0)) * Lq + t;
+      if (t >= Lq) a = wave == 0 ? (const float*)kZeroRowB : &kPosInfF;
       dma4(a, stage + (wave == 0 ? kRingD : kRingL));
     }
-    // this wave's bias slice: entry e = r[h, clamp(dbase + e, 0, R - 1)], the distance of
-    // query e - 31 + jj of the tile to key jj of the block being dbase + e
-    const int dbase = off + q0 - j0w - 31;
-    dma4(p.bias + (size_t)h * p.R + min(max(dbase + lane, 0), p.R - 1), stage + kRingBias + wave * 256);
+    // this wave's bias slice: entry e = r[h, min(d, R - 1)] at distance d = dbase + e, the
+    // distance of query e - 31 + jj of the tile to key jj of the block; -inf where no visible
+    // pair has distance d
+    const int d = off + q0 - j0w - 31 + lane;
+    dma4((uint32_t)d < (uint32_t)Weff ? p.bias + (size_t)h * p.R + min(d, p.R - 1) : &kNegInfF,
+         stage + kRingBias + wave * 256);
   };
 
   // ---- per-lane LDS operand addresses -----------------------------------------------
@@ -224,55 +233,63 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void bwd_dkdv_kernel(BackwardPara
     const int pq0 = off + q0;  // position of the tile's query 0
     // does any query of the tile see a key of this wave's block?
     if (!has_head || pq0 + 31 < j0w || pq0 - (Weff - 1) > j0w + 31) return;
-    const bool edge = pq0 < j0w + 31 || pq0 + 31 - j0w >= Weff || q0 + 32 > Lq;
     const uint32_t stage = ring_base + st * kRingStage;
     const uint32_t qt = stage + kRingQ + slot * kTileBytes;
     const uint32_t gt = stage + kRingG + slot * kTileBytes;
-    // S = Q K^T and dP = dO V^T: rows are the tile's queries, the lane's column its key
+    // register r of an accumulator holds query qq = 8 (r >> 2) + 4 hf + (r & 3) of the tile;
+    // its bias entry is slice entry qq - col + 31.  These reads go out first, their latency
+    // hidden behind the products.
+    const uint32_t bsl = stage + kRingBias + wave * 256 + 4u * (uint32_t)(4 * hf - col + 31);
+    float bv[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) bv[r] = lds_ldf(bsl + 4u * (8 * (r >> 2) + (r & 3)));
+    // S = Q K^T, then dP = dO V^T: rows are the tile's queries, the lane's column its key
     f32x16_t sacc = zero_f32x16(), dpacc = zero_f32x16();
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       const uint32_t o = rowA ^ (32u * ks);
       sacc = mfma_32x32x16(lds_ld16(qt + o), lds_ld16(k_rows + o), sacc);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const uint32_t o = rowA ^ (32u * ks);
       dpacc = mfma_32x32x16(lds_ld16(gt + o), lds_ld16(v_rows + o), dpacc);
     }
-    // register r holds query qq = 8 (r >> 2) + 4 hf + (r & 3) of the tile
-    const lds_f32_t* bsl = (const lds_f32_t*)(size_t)(stage + kRingBias + wave * 256);
     const uint32_t dl_addr = stage + kRingD + slot * 128 + 16 * hf;
     const uint32_t ll_addr = stage + kRingL + slot * 128 + 16 * hf;
     float pr[16], ds[16];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const f32x4_t dq4 = __builtin_bit_cast(f32x4_t, lds_ld16(dl_addr + 32 * g));
       const f32x4_t lq4 = __builtin_bit_cast(f32x4_t, lds_ld16(ll_addr + 32 * g));
 #pragma unroll
       for (int c4 = 0; c4 < 4; ++c4) {
         const int r = 4 * g + c4;
-        const int qq = 8 * g + 4 * hf + c4;
-        const float bias = bsl[qq - col + 31];
-        const float lg = fmaf(sacc[r], p.scale_log2, fmaf(bias, kLog2e, -lq4[c4]));
-        float pv = fast_exp2(lg);
-        float dv_ = pv * (dpacc[r] - dq4[c4]);
-        if (edge) {
-          const int dist = pq0 + qq - (j0w + col);
-          const bool vis = (uint32_t)dist < (uint32_t)Weff && q0 + qq < Lq;
-          pv = vis ? pv : 0.f;
-          dv_ = vis ? dv_ : 0.f;
-        }
-        pr[r] = pv;
-        ds[r] = dv_;
+        pr[r] = fast_exp2(fmaf(sacc[r], p.scale_log2, fmaf(bv[r], kLog2e, -lq4[c4])));
       }
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4_t dq4 = __builtin_bit_cast(f32x4_t, lds_ld16(dl_addr + 32 * g));
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) ds[4 * g + c4] = pr[4 * g + c4] * (dpacc[4 * g + c4] - dq4[c4]);
     }
     // dV += P^T dO and dK += dS^T Q: rows are keys (the lane's P and dS), columns dims
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs) {
       const u32x4_t ap = pack_p_operand(pr + 8 * qs);
-      const u32x4_t as = pack_p_operand(ds + 8 * qs);
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         const uint32_t o1 = (tr1 ^ (64u * db)) + 4096u * qs, o2 = (tr2 ^ (64u * db)) + 4096u * qs;
         const u32x2_t g1 = lds_tr8(gt + o1), g2 = lds_tr8(gt + o2);
         dv[db] = mfma_32x32x16(ap, u32x4_t{g1[0], g1[1], g2[0], g2[1]}, dv[db]);
+      }
+    }
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
+      const u32x4_t as = pack_p_operand(ds + 8 * qs);
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const uint32_t o1 = (tr1 ^ (64u * db)) + 4096u * qs, o2 = (tr2 ^ (64u * db)) + 4096u * qs;
         const u32x2_t x1 = lds_tr8(qt + o1), x2 = lds_tr8(qt + o2);
         dk[db] = mfma_32x32x16(as, u32x4_t{x1[0], x1[1], x2[0], x2[1]}, dk[db]);
       }
@@ -394,7 +411,8 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void bwd_dq_kernel(BackwardParams
     }
   }
   const size_t drow = ((size_t)b * p.Hq + h) * Lq + q0 + col;  // D and lse * log2(e): head-major
-  float lse2 = qvalid ? p.L2[drow] : 0.f;
+  // a lane past Lq: lse * log2(e) = +inf makes its P (hence dS) zero
+  float lse2 = qvalid ? p.L2[drow] : __builtin_inff();
   float dd = qvalid ? p.D[drow] : 0.f;
   // pin the waits for these loads here, before any LDS-bound load is in flight
 #pragma unroll
@@ -436,9 +454,11 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void bwd_dq_kernel(BackwardParams
         dma16(a, dst + i * 1024);
       }
     }
-    // this wave's bias slice: entry e = r[h, clamp(dbase + e, 0, R - 1)]
-    const int dbase = off + q0 - j0 - 31;
-    dma4(p.bias + (size_t)h * p.R + min(max(dbase + lane, 0), p.R - 1), stage + kDqBias + wave * 256);
+    // this wave's bias slice: entry e = r[h, min(d, R - 1)] at distance d = dbase + e; -inf
+    // where no visible pair has distance d
+    const int d = off + q0 - j0 - 31 + lane;
+    dma4((uint32_t)d < (uint32_t)Weff ? p.bias + (size_t)h * p.R + min(d, p.R - 1) : &kNegInfF,
+         stage + kDqBias + wave * 256);
   };
 
   // ---- per-lane LDS operand addresses (tile-relative, as in the key-stationary pass) ----
@@ -459,33 +479,29 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void bwd_dq_kernel(BackwardParams
   auto compute_tile = [&](int kt, int st) {
     const int j0 = kt * 32;
     if (!(nq > 0) || j0 > wj_hi || j0 + 31 < wj_lo) return;
-    const bool edge = j0 + 31 > off + q0 || j0 < off + q0 + nq - 1 - Weff + 1 || nq < 32;
     const uint32_t stage = ring_base + st * kDqStage;
     const uint32_t kt_lds = stage, vt_lds = stage + kDqKV;
-    // S^T = K Q^T and dP^T = V dO^T: rows are keys, the lane's column is its query
+    // register r of an accumulator holds key j0 + jj, jj = 8 (r >> 2) + 4 hf + (r & 3); its
+    // bias entry is slice entry col - jj + 31.  These reads go out first, their latency hidden
+    // behind the products.
+    const uint32_t bsl = stage + kDqBias + wave * 256 + 4u * (uint32_t)(col - 4 * hf + 31);
+    float bv[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) bv[r] = lds_ldf(bsl - 4u * (8 * (r >> 2) + (r & 3)));
+    // S^T = K Q^T, then dP^T = V dO^T: rows are keys, the lane's column is its query
     f32x16_t st_acc = zero_f32x16(), dpt = zero_f32x16();
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const uint32_t o = rowA ^ (32u * ks);
-      st_acc = mfma_32x32x16(lds_ld16(kt_lds + o), qr[ks], st_acc);
-      dpt = mfma_32x32x16(lds_ld16(vt_lds + o), gr[ks], dpt);
-    }
-    // register r holds key j0 + jj, jj = 8 (r >> 2) + 4 hf + (r & 3)
-    const lds_f32_t* bsl = (const lds_f32_t*)(size_t)(stage + kDqBias + wave * 256);
+    for (int ks = 0; ks < 8; ++ks)
+      st_acc = mfma_32x32x16(lds_ld16(kt_lds + (rowA ^ (32u * ks))), qr[ks], st_acc);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+      dpt = mfma_32x32x16(lds_ld16(vt_lds + (rowA ^ (32u * ks))), gr[ks], dpt);
     float ds[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int jj = 8 * (r >> 2) + 4 * hf + (r & 3);
-      const float lg = fmaf(st_acc[r], p.scale_log2, fmaf(bsl[col - jj + 31], kLog2e, -lse2));
-      float x = fast_exp2(lg) * (dpt[r] - dd);
-      if (edge) {
-        const int dist = pq - (j0 + jj);
-        const bool vis = qvalid && (uint32_t)dist < (uint32_t)Weff;
-        x = vis ? x : 0.f;
-      }
-      ds[r] = x;
-      diag[(col - jj + 31) * kDiagStride + col] = x;
-    }
+    for (int r = 0; r < 16; ++r)
+      ds[r] = fast_exp2(fmaf(st_acc[r], p.scale_log2, fmaf(bv[r], kLog2e, -lse2))) * (dpt[r] - dd);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) diag[(col - (8 * (r >> 2) + 4 * hf + (r & 3)) + 31) * kDiagStride + col] = ds[r];
     // dQ^T += K^T dS^T: rows are dims (K read transposed), the lane's column its query
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
