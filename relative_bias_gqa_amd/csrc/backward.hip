@@ -108,6 +108,37 @@ constexpr int kRingStage = kRingBias + kKvWaves * 256;
 
 __device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
+// a ^ k computed where it is used (k a constant).  Left to itself the compiler computes such
+// loop-invariant lane addresses once, keeps them in registers the kernel does not have, and
+// reloads them from scratch inside the loop, whose wait also waits for the DMA in flight.
+__device__ __forceinline__ uint32_t xor_at(uint32_t a, uint32_t k) {
+  uint32_t r;
+  asm volatile("v_xor_b32_e32 %0, %1, %2" : "=v"(r) : "i"(k), "v"(a));
+  return r;
+}
+
+// A wave-uniform value held in a scalar register at this point, so that the vector
+// instruction using it reads it there rather than from a hoisted (and spilled) vector copy.
+__device__ __forceinline__ uint32_t sgpr_at(uint32_t x) {
+  x = __builtin_amdgcn_readfirstlane(x);
+  asm volatile("" : "+s"(x));
+  return x;
+}
+
+// The lane's index, read where it is used (a value the compiler cannot keep across a loop).
+__device__ __forceinline__ uint32_t lane_now() {
+  uint32_t l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
+// Direct-to-LDS load of bias-slice entries: lane i stores at LDS byte lds + 4 i the entry at
+// table offset idx (bytes, from `table`) when ok, else -inf.  Both loads take a scalar base.
+__device__ __forceinline__ void dma4_bias_or_neginf(const float* table, uint32_t idx_bytes, bool ok, uint32_t lds) {
+  if (ok) dma4s(table, idx_bytes, lds);
+  else dma4s(&kNegInfF, 0u, lds);
+}
+
 __global__ __launch_bounds__(64 * kKvWaves, 1) void bwd_dkdv_kernel(BackwardParams p) {
   __shared__ __attribute__((aligned(1024))) unsigned char kv_lds[2 * kKvKeys * 256];  // K, then V
   __shared__ __attribute__((aligned(1024))) unsigned char ring[2 * kRingStage];
@@ -137,8 +168,9 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void bwd_dkdv_kernel(BackwardPara
   // query tiles that see a key of the workgroup: positions J0 .. J0 + 127 + W - 1
   const int q_lo = max(0, J0 - off);
   const int q_hi = (int)min((long long)Lq - 1, (long long)J0 + kKvKeys - 1 + Weff - 1 - off);
-  const int t_lo = q_lo / 32;
-  const int n_steps = q_lo <= q_hi ? q_hi / 32 - t_lo + 1 : 0;
+  // (wave-uniform; held in scalar registers)
+  const int t_lo = __builtin_amdgcn_readfirstlane(q_lo / 32);
+  const int n_steps = __builtin_amdgcn_readfirstlane(q_lo <= q_hi ? q_hi / 32 - q_lo / 32 + 1 : 0);
   const size_t q_row = (size_t)p.Hq * 256;   // bytes between queries of a head
   const size_t kv_row = (size_t)p.Hkv * 256;
   const unsigned char* zero_bytes = (const unsigned char*)kZeroRowB;
@@ -165,28 +197,34 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void bwd_dkdv_kernel(BackwardPara
   // Q / dO tiles: wave w issues rows 16 (w & 1) .. + 15 of tile T = w >> 1 (Q slot 0, Q slot
   // 1, dO slot 0, dO slot 1), four rows per instruction; lane i of instruction n fetches
   // logical chunk (i & 15) ^ swz(row) of row 16 (w & 1) + 4 n + i / 16.
+  // Row 16 (w & 1) + 4 n + i / 16 has swizzle 4 (i / 16) + n, so instruction n's lane offset
+  // is voff0 ^ 16 n plus the uniform 4 n rows.
   const int T = wave >> 1;
-  uint32_t voff[4];
-#pragma unroll
-  for (int n = 0; n < 4; ++n) {
-    const int r = 16 * (wave & 1) + 4 * n + (lane >> 4);
-    voff[n] = (uint32_t)r * (uint32_t)q_row + 16u * (uint32_t)((lane & 15) ^ swz(r));
-  }
+  const uint32_t voff0 = (uint32_t)(16 * (wave & 1) + (lane >> 4)) * (uint32_t)q_row +
+                         16u * (uint32_t)((lane & 15) ^ ((lane >> 4) << 2));
   const int hT = (T & 1) ? h_slot1 : h_slot0;
-  const unsigned char* tsrc_base = (const unsigned char*)(T < 2 ? p.q : p.dout) + (size_t)hT * 256;
+  // this wave's tile rows of step 0; step s adds s * 32 rows (kept scalar)
+  const unsigned char* tsrc0 = (const unsigned char*)uniform_ptr(
+      (const unsigned char*)(T < 2 ? p.q : p.dout) + (size_t)hT * 256 + ((size_t)b * Lq + t_lo * 32) * q_row);
+  const size_t step_bytes = 32 * q_row;
+  // D / lse * log2(e) rows of slot 0's head (waves 0, 1); lanes 32-63 read slot 1's head,
+  // Lq rows further when it is another head
+  const float* drow0 = (const float*)uniform_ptr((wave == 0 ? p.D : p.L2) + ((size_t)b * p.Hq + h_slot0) * Lq);
+  const uint32_t d_half = __builtin_amdgcn_readfirstlane(h_slot1 != h_slot0 ? (uint32_t)Lq : 0u);
+  const float* bias_h = (const float*)uniform_ptr(p.bias + (size_t)h * p.R);
   auto issue_step = [&](int s, int st) {
     const int q0 = (t_lo + s) * 32;
     const uint32_t stage = ring_base + st * kRingStage;
-    const unsigned char* src = uniform_ptr(tsrc_base + ((size_t)b * Lq + q0) * q_row);
+    const unsigned char* src = tsrc0 + (size_t)s * step_bytes;
     const uint32_t dst = stage + (T < 2 ? kRingQ : kRingG) + (T & 1) * kTileBytes + (wave & 1) * 4096;
     if (q0 + 32 <= Lq) {
 #pragma unroll
-      for (int n = 0; n < 4; ++n) dma16s(src, voff[n], dst + n * 1024);
+      for (int n = 0; n < 4; ++n) dma16s(src + (size_t)(4 * n) * q_row, xor_at(voff0, 16u * n), dst + n * 1024);
     } else {
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
         const int r = 16 * (wave & 1) + 4 * n + (lane >> 4);
-        const unsigned char* a = src + voff[n];
+        const unsigned char* a = src + (size_t)(4 * n) * q_row + (voff0 ^ (16u * n));
         if (q0 + r >= Lq) a = zero_bytes + 16 * ((lane & 15) ^ swz(r));
         dma16(a, dst + n * 1024);
       }
@@ -194,17 +232,23 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void bwd_dkdv_kernel(BackwardPara
     if (wave < 2) {
       // D (wave 0) or lse * log2(e) (wave 1) of the tile's 32 queries, for both slots; rows
       // past Lq: D = 0, lse * log2(e) = +inf
-      const int t = q0 + col;
-      const float* a = (wave == 0 ? p.D : p.L2) + ((size_t)b * p.Hq + (hf ? h_slot1 : h_slot0)) * Lq + t;
-      if (t >= Lq) a = wave == 0 ? (const float*)kZeroRowB : &kPosInfF;
-      dma4(a, stage + (wave == 0 ? kRingD : kRingL));
+      const uint32_t l = lane_now();
+      const uint32_t d_lane = 4u * ((l & 31) + (l >> 5) * sgpr_at(d_half));
+      if (q0 + 32 <= Lq) {
+        dma4s(uniform_ptr(drow0 + q0), d_lane, stage + (wave == 0 ? kRingD : kRingL));
+      } else {
+        const int t = q0 + (int)(l & 31);
+        const float* a = (const float*)((const unsigned char*)(drow0 + q0) + d_lane);
+        if (t >= Lq) a = wave == 0 ? (const float*)kZeroRowB : &kPosInfF;
+        dma4(a, stage + (wave == 0 ? kRingD : kRingL));
+      }
     }
     // this wave's bias slice: entry e = r[h, min(d, R - 1)] at distance d = dbase + e, the
     // distance of query e - 31 + jj of the tile to key jj of the block; -inf where no visible
     // pair has distance d
-    const int d = off + q0 - j0w - 31 + lane;
-    dma4((uint32_t)d < (uint32_t)Weff ? p.bias + (size_t)h * p.R + min(d, p.R - 1) : &kNegInfF,
-         stage + kRingBias + wave * 256);
+    const int d = off + q0 - j0w - 31 + (int)lane_now();
+    dma4_bias_or_neginf(bias_h, 4u * (uint32_t)min(d, (int)sgpr_at(p.R - 1)), (uint32_t)d < sgpr_at(Weff),
+                        stage + kRingBias + wave * 256);
   };
 
   // ---- per-lane LDS operand addresses -----------------------------------------------
@@ -221,8 +265,7 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void bwd_dkdv_kernel(BackwardPara
     tr1 = (uint32_t)(r1 * 256 + 16 * (y ^ swz(r1)) + 8 * (m & 1));
     tr2 = (uint32_t)(r2 * 256 + 16 * (y ^ swz(r2)) + 8 * (m & 1));
   }
-  const uint32_t k_rows = kv_base + 32u * 256u * kb;
-  const uint32_t v_rows = k_rows + kKvKeys * 256;
+  const uint32_t ka = kv_base + 32u * 256u * kb + rowA;  // this wave's K rows; V 32 KB further
 
   f32x16_t dk[4], dv[4];
 #pragma unroll
@@ -236,62 +279,69 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void bwd_dkdv_kernel(BackwardPara
     const uint32_t stage = ring_base + st * kRingStage;
     const uint32_t qt = stage + kRingQ + slot * kTileBytes;
     const uint32_t gt = stage + kRingG + slot * kTileBytes;
-    // register r of an accumulator holds query qq = 8 (r >> 2) + 4 hf + (r & 3) of the tile;
-    // its bias entry is slice entry qq - col + 31.  These reads go out first, their latency
-    // hidden behind the products.
-    const uint32_t bsl = stage + kRingBias + wave * 256 + 4u * (uint32_t)(4 * hf - col + 31);
-    float bv[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) bv[r] = lds_ldf(bsl + 4u * (8 * (r >> 2) + (r & 3)));
-    // S = Q K^T, then dP = dO V^T: rows are the tile's queries, the lane's column its key
+    // Four phases, each kept together by a scheduling barrier so that no phase's operand
+    // loads are hoisted into an earlier one (the wave has no registers to spare), while each
+    // phase's vector work overlaps its own products:
+    //   1. S = Q K^T;  2. dP = dO V^T, with P from S;  3. dV += P^T dO, with dS from dP;
+    //   4. dK += dS^T Q.
+    // S and dP have the tile's queries as rows and the lane's key as column: register r holds
+    // query qq = 8 (r >> 2) + 4 hf + (r & 3), whose bias entry is slice entry qq - col + 31.
+    // Tile and block bases are multiples of 256 bytes, so (base + lane offset) ^ (32 ks) is the
+    // swizzled address of chunk 2 ks + hf; dO sits 16 KB after Q, V 32 KB after K.
+    const uint32_t qa = qt + rowA;
     f32x16_t sacc = zero_f32x16(), dpacc = zero_f32x16();
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const uint32_t o = rowA ^ (32u * ks);
-      sacc = mfma_32x32x16(lds_ld16(qt + o), lds_ld16(k_rows + o), sacc);
-    }
+    for (int ks = 0; ks < 8; ++ks)
+      sacc = mfma_32x32x16(lds_ld16(qa ^ (32u * ks)), lds_ld16(xor_at(ka, 32u * ks)), sacc);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const uint32_t o = rowA ^ (32u * ks);
-      dpacc = mfma_32x32x16(lds_ld16(gt + o), lds_ld16(v_rows + o), dpacc);
-    }
-    const uint32_t dl_addr = stage + kRingD + slot * 128 + 16 * hf;
+    for (int ks = 0; ks < 8; ++ks)
+      dpacc = mfma_32x32x16(lds_ld16((qa ^ (32u * ks)) + 2 * kTileBytes),
+                            lds_ld16(xor_at(ka, 32u * ks) + kKvKeys * 256), dpacc);
+    const uint32_t bsl = stage + kRingBias + wave * 256 + 4u * (uint32_t)(4 * hf - col + 31);
     const uint32_t ll_addr = stage + kRingL + slot * 128 + 16 * hf;
-    float pr[16], ds[16];
+    float pr[16];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const f32x4_t lq4 = __builtin_bit_cast(f32x4_t, lds_ld16(ll_addr + 32 * g));
 #pragma unroll
       for (int c4 = 0; c4 < 4; ++c4) {
-        const int r = 4 * g + c4;
-        pr[r] = fast_exp2(fmaf(sacc[r], p.scale_log2, fmaf(bv[r], kLog2e, -lq4[c4])));
+        const float bias = lds_ldf(bsl + 4u * (8 * g + c4));
+        pr[4 * g + c4] = fast_exp2(fmaf(sacc[4 * g + c4], p.scale_log2, fmaf(bias, kLog2e, -lq4[c4])));
       }
     }
+    const u32x4_t ap0 = pack_p_operand(pr), ap1 = pack_p_operand(pr + 8);
+    __builtin_amdgcn_sched_barrier(0);
+    // dV += P^T dO (rows: keys, the lane's P; columns: dims, dO read transposed)
+    const uint32_t t1 = qt + tr1, t2 = qt + tr2;
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const uint32_t o1 = (t1 ^ (64u * db)) + 4096u * qs + 2 * kTileBytes;
+        const uint32_t o2 = (t2 ^ (64u * db)) + 4096u * qs + 2 * kTileBytes;
+        const u32x2_t g1 = lds_tr8(o1), g2 = lds_tr8(o2);
+        dv[db] = mfma_32x32x16(qs ? ap1 : ap0, u32x4_t{g1[0], g1[1], g2[0], g2[1]}, dv[db]);
+      }
+    }
+    const uint32_t dl_addr = stage + kRingD + slot * 128 + 16 * hf;
+    float ds[16];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const f32x4_t dq4 = __builtin_bit_cast(f32x4_t, lds_ld16(dl_addr + 32 * g));
 #pragma unroll
       for (int c4 = 0; c4 < 4; ++c4) ds[4 * g + c4] = pr[4 * g + c4] * (dpacc[4 * g + c4] - dq4[c4]);
     }
-    // dV += P^T dO and dK += dS^T Q: rows are keys (the lane's P and dS), columns dims
+    const u32x4_t as0 = pack_p_operand(ds), as1 = pack_p_operand(ds + 8);
+    __builtin_amdgcn_sched_barrier(0);
+    // dK += dS^T Q (Q read transposed)
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs) {
-      const u32x4_t ap = pack_p_operand(pr + 8 * qs);
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const uint32_t o1 = (tr1 ^ (64u * db)) + 4096u * qs, o2 = (tr2 ^ (64u * db)) + 4096u * qs;
-        const u32x2_t g1 = lds_tr8(gt + o1), g2 = lds_tr8(gt + o2);
-        dv[db] = mfma_32x32x16(ap, u32x4_t{g1[0], g1[1], g2[0], g2[1]}, dv[db]);
-      }
-    }
-#pragma unroll
-    for (int qs = 0; qs < 2; ++qs) {
-      const u32x4_t as = pack_p_operand(ds + 8 * qs);
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const uint32_t o1 = (tr1 ^ (64u * db)) + 4096u * qs, o2 = (tr2 ^ (64u * db)) + 4096u * qs;
-        const u32x2_t x1 = lds_tr8(qt + o1), x2 = lds_tr8(qt + o2);
-        dk[db] = mfma_32x32x16(as, u32x4_t{x1[0], x1[1], x2[0], x2[1]}, dk[db]);
+        const uint32_t o1 = (t1 ^ (64u * db)) + 4096u * qs, o2 = (t2 ^ (64u * db)) + 4096u * qs;
+        const u32x2_t x1 = lds_tr8(o1), x2 = lds_tr8(o2);
+        dk[db] = mfma_32x32x16(qs ? as1 : as0, u32x4_t{x1[0], x1[1], x2[0], x2[1]}, dk[db]);
       }
     }
   };
@@ -480,7 +530,7 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void bwd_dq_kernel(BackwardParams
     const int j0 = kt * 32;
     if (!(nq > 0) || j0 > wj_hi || j0 + 31 < wj_lo) return;
     const uint32_t stage = ring_base + st * kDqStage;
-    const uint32_t kt_lds = stage, vt_lds = stage + kDqKV;
+    const uint32_t kt_lds = stage;
     // register r of an accumulator holds key j0 + jj, jj = 8 (r >> 2) + 4 hf + (r & 3); its
     // bias entry is slice entry col - jj + 31.  These reads go out first, their latency hidden
     // behind the products.
@@ -488,14 +538,15 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void bwd_dq_kernel(BackwardParams
     float bv[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) bv[r] = lds_ldf(bsl - 4u * (8 * (r >> 2) + (r & 3)));
-    // S^T = K Q^T, then dP^T = V dO^T: rows are keys, the lane's column is its query
+    // S^T = K Q^T, then dP^T = V dO^T: rows are keys, the lane's column is its query.  The
+    // stage base is a multiple of 256 bytes, so (base + lane offset) ^ (32 ks) is the swizzled
+    // address of chunk 2 ks + hf; V sits 8 KB after K.
+    const uint32_t ka = kt_lds + rowA;
     f32x16_t st_acc = zero_f32x16(), dpt = zero_f32x16();
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-      st_acc = mfma_32x32x16(lds_ld16(kt_lds + (rowA ^ (32u * ks))), qr[ks], st_acc);
+    for (int ks = 0; ks < 8; ++ks) st_acc = mfma_32x32x16(lds_ld16(ka ^ (32u * ks)), qr[ks], st_acc);
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-      dpt = mfma_32x32x16(lds_ld16(vt_lds + (rowA ^ (32u * ks))), gr[ks], dpt);
+    for (int ks = 0; ks < 8; ++ks) dpt = mfma_32x32x16(lds_ld16((ka ^ (32u * ks)) + kDqKV), gr[ks], dpt);
     float ds[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r)
@@ -503,13 +554,14 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void bwd_dq_kernel(BackwardParams
 #pragma unroll
     for (int r = 0; r < 16; ++r) diag[(col - (8 * (r >> 2) + 4 * hf + (r & 3)) + 31) * kDiagStride + col] = ds[r];
     // dQ^T += K^T dS^T: rows are dims (K read transposed), the lane's column its query
+    const uint32_t t1 = kt_lds + tr1, t2 = kt_lds + tr2;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const u32x4_t bs = pack_p_operand(ds + 8 * ks);
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const uint32_t o1 = (tr1 ^ (64u * db)) + 4096u * ks, o2 = (tr2 ^ (64u * db)) + 4096u * ks;
-        const u32x2_t a1 = lds_tr8(kt_lds + o1), a2 = lds_tr8(kt_lds + o2);
+        const uint32_t o1 = (t1 ^ (64u * db)) + 4096u * ks, o2 = (t2 ^ (64u * db)) + 4096u * ks;
+        const u32x2_t a1 = lds_tr8(o1), a2 = lds_tr8(o2);
         dq[db] = mfma_32x32x16(u32x4_t{a1[0], a1[1], a2[0], a2[1]}, bs, dq[db]);
       }
     }
