@@ -523,9 +523,11 @@ int rattn_kv_sconv_write(const void* k_new, const void* v_new, const float* w_k,
 namespace {
 
 // Backward workspace: D and lse * log2(e) per query row ([B, Hq, Lq] each), then the partial
-// dK and dV of each pair of query heads ([ceil(G / 2), B, Lk, Hkv, 128] each), 256-aligned.
+// dK and dV of each pair of query heads for each of the (at most) two query-step chunks of a
+// key block ([2, ceil(G / 2), B, Lk, Hkv, 128] each), then the second key-tile chunk's dq
+// ([B, Lq, Hq, 128]); each part 256-aligned.
 struct BackwardLayout {
-  size_t l2_off, pk_off, pv_off, total;
+  size_t l2_off, pk_off, pv_off, dqp_off, total;
   int n_pairs;
 };
 
@@ -537,9 +539,77 @@ bool backward_layout(int B, int Lq, int Lk, int Hq, int Hkv, BackwardLayout* lay
   lay->n_pairs = (Hq / Hkv + 1) / 2;
   lay->l2_off = align(rows * sizeof(float));
   lay->pk_off = lay->l2_off + align(rows * sizeof(float));
-  lay->pv_off = lay->pk_off + align((size_t)lay->n_pairs * plane * sizeof(float));
-  lay->total = std::max<size_t>(256, lay->pv_off + align((size_t)lay->n_pairs * plane * sizeof(float)));
+  lay->pv_off = lay->pk_off + align(2 * (size_t)lay->n_pairs * plane * sizeof(float));
+  lay->dqp_off = lay->pv_off + align(2 * (size_t)lay->n_pairs * plane * sizeof(float));
+  lay->total = std::max<size_t>(256, lay->dqp_off + align(rows * 128 * sizeof(float)));
   return true;
+}
+
+// Query steps (32-query tiles) that see key block blk of the key-stationary pass, key tiles
+// (32 keys) that token tile t of the query-stationary pass walks; the kernels' counts.
+long long bwd_kv_block_steps(int Lq, int Lk, int window, int blk) {
+  const long long off = (long long)Lk - Lq, weff = window > 0 ? window : 0x40000000LL;
+  const long long J0 = 128LL * blk, q_lo = std::max(0LL, J0 - off);
+  const long long q_hi = std::min((long long)Lq - 1, J0 + 127 + weff - 1 - off);
+  return q_lo <= q_hi ? q_hi / 32 - q_lo / 32 + 1 : 0;
+}
+
+// Makespan of a launch whose units (in launch order) take w[i] (in steps), for the way the
+// hardware hands out workgroups: workgroup i to XCD i % 8, within it to shader engine
+// (i / 8) % 4, and to whichever compute unit of that engine frees up first.  A model used
+// only to choose between plans.
+double dispatch_makespan(const std::vector<double>& w, int cus) {
+  const int per_pool = std::max(1, cus / 32);
+  std::vector<std::priority_queue<double, std::vector<double>, std::greater<double>>> pools(32);
+  for (auto& q : pools)
+    for (int c = 0; c < per_pool; ++c) q.push(0.0);
+  double end = 0.0;
+  for (size_t i = 0; i < w.size(); ++i) {
+    auto& q = pools[(i % 8) * 4 + (i / 8) % 4];
+    const double t = q.top() + w[i];
+    q.pop();
+    q.push(t);
+    end = std::max(end, t);
+  }
+  return end;
+}
+
+struct ChunkPlan {
+  int chunks, chunk;
+};
+
+// Segments with the given walks (in launch order), each repeated `inner` times (head groups,
+// KV heads, sequences), cut into one or two chunks, chunk-major: the plan that finishes first.
+ChunkPlan plan_chunks(const std::vector<long long>& walk, long long inner) {
+  long long most = 1;
+  for (long long x : walk) most = std::max(most, x);
+  ChunkPlan best{1, (int)std::min<long long>(most, 0x7fffffff)};
+  if (walk.empty() || inner <= 0 || (double)walk.size() * inner > 4e6) return best;
+  const double overhead = 3.0;  // steps a unit spends on loads before its first step
+  double best_t = 0.0;
+  for (int chunks = 1; chunks <= 2; ++chunks) {
+    const long long chunk = (most + chunks - 1) / chunks;
+    std::vector<double> w;
+    w.reserve(walk.size() * chunks * inner);
+    for (int c = 0; c < chunks; ++c)
+      for (long long x : walk) {
+        const long long steps = std::max(0LL, std::min(chunk, x - c * chunk));
+        const double t = steps > 0 ? (double)steps + overhead : (c == 0 ? overhead : 0.1);
+        for (long long g = 0; g < inner; ++g) w.push_back(t);
+      }
+    const double t = dispatch_makespan(w, compute_units());
+    if (chunks == 1 || t < best_t) {
+      best_t = t;
+      best = ChunkPlan{chunks, (int)chunk};
+    }
+  }
+  return best;
+}
+
+long long bwd_dq_tile_keys(int Lq, int Lk, int window, int tsub, int t) {
+  const long long off = (long long)Lk - Lq, weff = window > 0 ? window : 0x40000000LL;
+  const long long T0 = 32LL * tsub * t, T1 = std::min<long long>(Lq, T0 + 32LL * tsub);
+  return (off + T1 - 1) / 32 + 1 - std::max(0LL, off + T0 - weff + 1) / 32;
 }
 
 }  // namespace
@@ -592,6 +662,7 @@ int rattn_prefill_backward(const void* q, const void* k, const void* v, const fl
   p.L2 = (float*)((char*)workspace + lay.l2_off);
   p.part_dk = (float*)((char*)workspace + lay.pk_off);
   p.part_dv = (float*)((char*)workspace + lay.pv_off);
+  p.dq_part = (float*)((char*)workspace + lay.dqp_off);
   p.n_pairs = lay.n_pairs;
   {
     rattn::PrefillParams shape;  // the forward's head / token grouping
@@ -600,6 +671,20 @@ int rattn_prefill_backward(const void* q, const void* k, const void* v, const fl
     p.tsub = shape.tsub;
     p.n_hg = shape.n_hg;
     p.n_tok_tiles = shape.n_tok_tiles;
+  }
+  {
+    // walk of every key block / token tile, then one or two chunks each, whichever plan the
+    // dispatch model finishes sooner
+    const int n_blk = (Lk + 127) / 128;
+    std::vector<long long> kw(n_blk), qw(p.n_tok_tiles);
+    for (int blk = 0; blk < n_blk; ++blk) kw[blk] = bwd_kv_block_steps(Lq, Lk, window, blk);
+    for (int t = 0; t < p.n_tok_tiles; ++t) qw[p.n_tok_tiles - 1 - t] = bwd_dq_tile_keys(Lq, Lk, window, p.tsub, t);
+    const ChunkPlan kv = plan_chunks(kw, (long long)B * Hkv * lay.n_pairs);
+    const ChunkPlan qp = plan_chunks(qw, (long long)B * Hkv * p.n_hg);
+    p.kv_chunks = kv.chunks;
+    p.kv_chunk = kv.chunk;
+    p.q_chunks = qp.chunks;
+    p.q_chunk = qp.chunk;
   }
   p.B = B;
   p.Lq = Lq;

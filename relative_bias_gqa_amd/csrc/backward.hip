@@ -125,6 +125,16 @@ __device__ __forceinline__ uint32_t sgpr_at(uint32_t x) {
   return x;
 }
 
+// Query steps (32-query tiles) that see key block blk of the key-stationary pass.
+__device__ __forceinline__ int kv_block_steps(const BackwardParams& p, int blk) {
+  const int off = p.Lk - p.Lq;
+  const int Weff = p.window > 0 ? p.window : 0x40000000;
+  const int J0 = blk * kKvKeys;
+  const int q_lo = max(0, J0 - off);
+  const int q_hi = (int)min((long long)p.Lq - 1, (long long)J0 + kKvKeys - 1 + Weff - 1 - off);
+  return q_lo <= q_hi ? q_hi / 32 - q_lo / 32 + 1 : 0;
+}
+
 // The lane's index, read where it is used (a value the compiler cannot keep across a loop).
 __device__ __forceinline__ uint32_t lane_now() {
   uint32_t l;
@@ -147,16 +157,21 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void bwd_dkdv_kernel(BackwardPara
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kb = wave & 3, slot = wave >> 2;
   const int col = lane & 31, hf = lane >> 5;
-  // launch order: consecutive workgroups take the head pairs and KV heads of one key block
-  // (they run on consecutive XCDs); workgroup i + 8 takes the next key block with the same
-  // heads, so an XCD's L2 serves neighbouring key blocks that read the same query tiles
+  // One workgroup per unit: a key block's query steps, for one head pair and KV head, cut
+  // into kv_chunks (1 or 2) chunks of kv_chunk steps.  Launch order: chunk, then key block,
+  // then the head pairs and KV heads.  Workgroup i runs on XCD i % 8 and, within it, on a
+  // shader engine fixed by its position, only the compute unit being picked as one frees up;
+  // this order gives every shader engine the same mix of units, heaviest first (later blocks
+  // see fewer queries, second chunks are lighter); the host picks the number of chunks.
   const int per_block = p.n_pairs * p.Hkv * p.B;
-  const int blk = (int)blockIdx.x / per_block;
-  int rem = (int)blockIdx.x % per_block;
-  const int hp = rem % p.n_pairs;
-  rem /= p.n_pairs;
-  const int hk = rem % p.Hkv;
-  const int b = rem / p.Hkv;
+  const int n_blk = (p.Lk + kKvKeys - 1) / kKvKeys;
+  auto unit = [&](const int u) {
+  const int chunk = __builtin_amdgcn_readfirstlane(u / (n_blk * per_block));
+  const int blk = __builtin_amdgcn_readfirstlane((u / per_block) % n_blk);
+  const int rem = u % per_block;
+  const int hp = __builtin_amdgcn_readfirstlane(rem % p.n_pairs);
+  const int hk = __builtin_amdgcn_readfirstlane((rem / p.n_pairs) % p.Hkv);
+  const int b = __builtin_amdgcn_readfirstlane(rem / (p.n_pairs * p.Hkv));
   const int J0 = blk * kKvKeys;
   const int j0w = J0 + 32 * kb;
   const int Lq = p.Lq, Lk = p.Lk, off = Lk - Lq;
@@ -168,9 +183,11 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void bwd_dkdv_kernel(BackwardPara
   // query tiles that see a key of the workgroup: positions J0 .. J0 + 127 + W - 1
   const int q_lo = max(0, J0 - off);
   const int q_hi = (int)min((long long)Lq - 1, (long long)J0 + kKvKeys - 1 + Weff - 1 - off);
-  // (wave-uniform; held in scalar registers)
-  const int t_lo = __builtin_amdgcn_readfirstlane(q_lo / 32);
-  const int n_steps = __builtin_amdgcn_readfirstlane(q_lo <= q_hi ? q_hi / 32 - q_lo / 32 + 1 : 0);
+  // this chunk's query tiles: t_lo .. t_lo + n_steps - 1 (wave-uniform; scalar registers)
+  const int all_steps = q_lo <= q_hi ? q_hi / 32 - q_lo / 32 + 1 : 0;
+  if (chunk == 1 && all_steps <= p.kv_chunk) return;  // the block has one chunk
+  const int t_lo = __builtin_amdgcn_readfirstlane(q_lo / 32 + chunk * p.kv_chunk);
+  const int n_steps = __builtin_amdgcn_readfirstlane(min(all_steps - chunk * p.kv_chunk, p.kv_chunk));
   const size_t q_row = (size_t)p.Hq * 256;   // bytes between queries of a head
   const size_t kv_row = (size_t)p.Hkv * 256;
   const unsigned char* zero_bytes = (const unsigned char*)kZeroRowB;
@@ -359,7 +376,7 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void bwd_dkdv_kernel(BackwardPara
   // ---- slot 1 hands its sums to slot 0; slot 0 writes the pair's partial ---------------
   // accumulator register 4 i + c of block db: key 8 i + 4 hf + c of the block, dim 32 db + col
   float* red = (float*)ring;
-  const size_t part_row = ((size_t)hp * p.B + b) * Lk;
+  const size_t part_row = (((size_t)chunk * p.n_pairs + hp) * p.B + b) * Lk;
   auto hand_over = [&](f32x16_t (&acc)[4], float* part) {
     __syncthreads();  // every wave is done with the ring
     if (slot == 1) {
@@ -382,22 +399,30 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void bwd_dkdv_kernel(BackwardPara
   };
   hand_over(dk, p.part_dk);
   hand_over(dv, p.part_dv);
+  };
+  unit((int)blockIdx.x);
 }
 
 // dk = (sum over head pairs of the partial dK) / sqrt(128), dv = sum of the partial dV, in
-// pair order; four consecutive floats per thread.
-__global__ __launch_bounds__(256) void bwd_reduce_kernel(const float* part_dk, const float* part_dv, float* dk,
-                                                         float* dv, size_t n4, size_t plane, int n_pairs) {
+// pair order, a pair's second chunk (blocks walked in two) right after its first; four
+// consecutive floats per thread.
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(BackwardParams p, size_t n4) {
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n4) return;
-  f32x4_t a = ((const f32x4_t*)part_dk)[i];
-  f32x4_t c = ((const f32x4_t*)part_dv)[i];
-  for (int pp = 1; pp < n_pairs; ++pp) {
-    a += ((const f32x4_t*)(part_dk + (size_t)pp * plane))[i];
-    c += ((const f32x4_t*)(part_dv + (size_t)pp * plane))[i];
+  const size_t plane = (size_t)p.B * p.Lk * p.Hkv * kHeadDim;
+  const int j = (int)((i / ((size_t)p.Hkv * 32)) % (size_t)p.Lk);
+  const bool two = kv_block_steps(p, j / kKvKeys) > p.kv_chunk;
+  f32x4_t a = {0.f, 0.f, 0.f, 0.f}, c = {0.f, 0.f, 0.f, 0.f};
+  for (int hp = 0; hp < p.n_pairs; ++hp) {
+    a += ((const f32x4_t*)(p.part_dk + (size_t)hp * plane))[i];
+    c += ((const f32x4_t*)(p.part_dv + (size_t)hp * plane))[i];
+    if (two) {
+      a += ((const f32x4_t*)(p.part_dk + (size_t)(p.n_pairs + hp) * plane))[i];
+      c += ((const f32x4_t*)(p.part_dv + (size_t)(p.n_pairs + hp) * plane))[i];
+    }
   }
-  ((f32x4_t*)dk)[i] = a * kRsqrtD;
-  ((f32x4_t*)dv)[i] = c;
+  ((f32x4_t*)p.dk)[i] = a * kRsqrtD;
+  ((f32x4_t*)p.dv)[i] = c;
 }
 
 // ---- query-stationary pass (dQ, dr) -----------------------------------------------------
@@ -419,6 +444,14 @@ constexpr int kDqBias = 2 * kDqKV;                    // bias slices: 64 floats 
 constexpr int kDqStage = kDqBias + kDqWaves * 256;
 constexpr int kDqLoads = 3;                           // DMA loads per wave and tile
 
+// Key tiles that token tile t of the query-stationary pass walks.
+__device__ __forceinline__ int dq_tile_keys(const BackwardParams& p, int t) {
+  const int off = p.Lk - p.Lq;
+  const int Weff = p.window > 0 ? p.window : 0x40000000;
+  const int T0 = t * 32 * p.tsub, T1 = min(p.Lq, T0 + 32 * p.tsub);
+  return (off + T1 - 1) / 32 + 1 - max(0, off + T0 - Weff + 1) / 32;
+}
+
 __global__ __launch_bounds__(64 * kDqWaves, 1) void bwd_dq_kernel(BackwardParams p) {
   __shared__ __attribute__((aligned(1024))) unsigned char ring[kDqStages * kDqStage];
   // dS of a tile by diagonal: row e = col - jj + 31 (distance dbase + e), column col (the
@@ -431,10 +464,15 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void bwd_dq_kernel(BackwardParams
   const int col = lane & 31, hf = lane >> 5;
   float* diag = diag_w[wave];
   for (int i = lane; i < 63 * kDiagStride; i += 64) diag[i] = 0.f;  // this wave's own table
-  // job: heaviest (last) token tiles first
+  // One workgroup per unit: a token tile's key tiles, for one head group and KV head, cut into
+  // q_chunks (1 or 2) chunks of q_chunk; chunk 0 writes dq, chunk 1 a partial that the fix-up
+  // kernel adds.  Launch order: chunk, then token tile (heaviest, last, first), then the head
+  // groups and KV heads (see the key-stationary pass for why).
   const int per_tile = p.B * p.Hkv * p.n_hg;
-  const int tile = p.n_tok_tiles - 1 - (int)blockIdx.x / per_tile;
-  const int rem = (int)blockIdx.x % per_tile;
+  auto unit = [&](const int u) {
+  const int chunk = __builtin_amdgcn_readfirstlane(u / (p.n_tok_tiles * per_tile));
+  const int tile = __builtin_amdgcn_readfirstlane(p.n_tok_tiles - 1 - (u / per_tile) % p.n_tok_tiles);
+  const int rem = __builtin_amdgcn_readfirstlane(u % per_tile);
   const int hg = rem % p.n_hg;
   const int hk = (rem / p.n_hg) % p.Hkv;
   const int b = rem / (p.n_hg * p.Hkv);
@@ -470,9 +508,11 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void bwd_dq_kernel(BackwardParams
   asm volatile("" : "+v"(lse2), "+v"(dd));
   const int pq = off + q0 + col;  // this lane's query position
   float* dbias_h = p.dbias + (size_t)h * p.R;
-  // key tiles of the workgroup, and of this wave
-  const int kt_begin = max(0, off + T0 - Weff + 1) / 32;
-  const int n_tiles = T0 < T1 ? (off + T1 - 1) / 32 + 1 - kt_begin : 0;
+  // key tiles of the workgroup's chunk, and of this wave
+  const int all_tiles = (off + T1 - 1) / 32 + 1 - max(0, off + T0 - Weff + 1) / 32;
+  if (chunk == 1 && all_tiles <= p.q_chunk) return;  // the tile has one chunk
+  const int kt_begin = __builtin_amdgcn_readfirstlane(max(0, off + T0 - Weff + 1) / 32 + chunk * p.q_chunk);
+  const int n_tiles = __builtin_amdgcn_readfirstlane(min(all_tiles - chunk * p.q_chunk, p.q_chunk));
   const int wj_lo = max(0, off + q0 - Weff + 1), wj_hi = off + q0 + max(nq, 1) - 1;
 
   // ---- tile loads: waves 0-3 issue K, waves 4-7 V, two instructions of 4 keys each ----
@@ -594,7 +634,7 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void bwd_dq_kernel(BackwardParams
   }
   if (!qvalid) return;
   // accumulator register 4 i + c of block db: dim 32 db + 8 i + 4 hf + c of query q0 + col
-  float* dqg = p.dq + (row0 + (size_t)col * p.Hq) * kHeadDim;
+  float* dqg = (chunk ? p.dq_part : p.dq) + (row0 + (size_t)col * p.Hq) * kHeadDim;
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -604,6 +644,18 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void bwd_dq_kernel(BackwardParams
       for (int c = 0; c < 4; ++c) x[c] = dq[db][4 * i + c] * kRsqrtD;
       *(f32x4_t*)(dqg + 32 * db + 8 * i + 4 * hf) = x;
     }
+  };
+  unit((int)blockIdx.x);
+}
+
+// dq += the second chunk's partial, for the token tiles whose key tiles two workgroups shared;
+// four consecutive floats per thread.
+__global__ __launch_bounds__(256) void bwd_dq_fixup_kernel(BackwardParams p, size_t n4) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  const int q = (int)((i / ((size_t)p.Hq * 32)) % (size_t)p.Lq);
+  if (dq_tile_keys(p, q / (32 * p.tsub)) <= p.q_chunk) return;
+  ((f32x4_t*)p.dq)[i] += ((const f32x4_t*)p.dq_part)[i];
 }
 
 }  // namespace
@@ -625,16 +677,17 @@ hipError_t launch_backward(const BackwardParams& p, hipStream_t stream) {
   const size_t rows = (size_t)p.B * p.Lq * p.Hq;
   hipLaunchKernelGGL(bwd_rowdot_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream,
                      (const uint16_t*)p.out, (const uint16_t*)p.dout, p.lse, p.D, p.L2, p.Lq, p.Hq, rows);
-  const long long blocks = (p.Lk + kKvKeys - 1) / kKvKeys;
-  const long long grid = blocks * p.Hkv * p.n_pairs * p.B;
-  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)grid), dim3(64 * kKvWaves), 0, stream, p);
+  const long long kv_units = (long long)((p.Lk + kKvKeys - 1) / kKvKeys) * p.kv_chunks * p.Hkv * p.n_pairs * p.B;
+  const long long q_units = (long long)p.n_tok_tiles * p.q_chunks * p.B * p.Hkv * p.n_hg;
+  if (kv_units > 0x7fffffffLL || q_units > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)kv_units), dim3(64 * kKvWaves), 0, stream, p);
   const size_t n4 = n_kv / 4;
-  hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream,
-                     (const float*)p.part_dk, (const float*)p.part_dv, p.dk, p.dv, n4, n_kv, p.n_pairs);
-  const long long dq_grid = (long long)p.n_tok_tiles * p.B * p.Hkv * p.n_hg;
-  if (dq_grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)dq_grid), dim3(64 * kDqWaves), 0, stream, p);
+  hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream, p, n4);
+  hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)q_units), dim3(64 * kDqWaves), 0, stream, p);
+  if (p.q_chunks > 1) {
+    const size_t nq4 = (size_t)p.B * p.Lq * p.Hq * kHeadDim / 4;
+    hipLaunchKernelGGL(bwd_dq_fixup_kernel, dim3((unsigned)((nq4 + 255) / 256)), dim3(256), 0, stream, p, nq4);
+  }
   return hipGetLastError();
 }
 

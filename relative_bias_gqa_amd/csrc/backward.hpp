@@ -20,9 +20,17 @@ struct BackwardParams {
   float* dbias;       // [Hq, R]
   float* D;           // [B, Hq, Lq] workspace: rowsum(dout * out) (head-major)
   float* L2;          // [B, Hq, Lq] workspace: lse * log2(e)
-  float* part_dk;     // [n_pairs, B, Lk, Hkv, 128] workspace: dK of each query-head pair (unscaled)
-  float* part_dv;     // [n_pairs, B, Lk, Hkv, 128] workspace: dV of each query-head pair
+  // key-stationary pass: a key block's query steps in kv_chunks chunks of kv_chunk;
+  // partials [chunk][pair] (chunk-1 planes are written and read only for two-chunk blocks)
+  float* part_dk;     // [2, n_pairs, B, Lk, Hkv, 128] workspace: dK of each pair (unscaled)
+  float* part_dv;     // [2, n_pairs, B, Lk, Hkv, 128] workspace: dV of each pair
   int n_pairs;        // ceil(G / 2)
+  int kv_chunk;       // steps per chunk (a block's steps when kv_chunks == 1)
+  // query-stationary pass: a token tile's key tiles in q_chunks chunks of q_chunk; the
+  // second chunk's dq goes to dq_part (rows of two-chunk tiles only), added by a fix-up
+  float* dq_part;     // [B, Lq, Hq, 128] workspace
+  int q_chunk;        // key tiles per chunk (a tile's when q_chunks == 1)
+  int kv_chunks, q_chunks;  // chunks per key block / token tile: 1 or 2 (host's plan)
   // query-stationary pass: a workgroup takes hpw query heads x 32 * tsub queries (hpw * tsub
   // = 8 waves), n_hg = G / hpw head groups per KV head, n_tok_tiles token tiles
   int hpw, tsub, n_hg, n_tok_tiles;
