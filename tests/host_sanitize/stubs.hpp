@@ -1,0 +1,25 @@
+// Launch records of the host stubs (tests/host_sanitize/stubs.cpp).
+#pragma once
+
+#include <functional>
+
+#include "backward.hpp"
+#include "launch.hpp"
+
+namespace stub {
+
+struct Record {
+  int compute_units = 256;
+  rattn::PrefillParams prefill{};
+  rattn::DecodeParams decode{};
+  rattn::SconvParams sconv{};
+  rattn::BackwardParams backward{};
+  int prefill_bf16_calls = 0, prefill_fp32_calls = 0, decode_calls = 0, sconv_calls = 0, backward_calls = 0;
+  // called on every decode launch (a call may launch several batches); false fails the launch
+  std::function<bool(const rattn::DecodeParams&)> on_decode = [](const rattn::DecodeParams&) { return true; };
+};
+
+extern Record rec;
+const void* scratch_base();
+
+}  // namespace stub
