@@ -106,7 +106,7 @@ constexpr int kRingL = kRingD + 256;        // lse * log2(e), likewise
 constexpr int kRingBias = kRingL + 256;     // 64 floats per wave
 constexpr int kRingStage = kRingBias + kKvWaves * 256;
 
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ int swz(int r) { return lds_swz(r); }
 
 // a ^ k computed where it is used (k a constant).  Left to itself the compiler computes such
 // loop-invariant lane addresses once, keeps them in registers the kernel does not have, and
@@ -133,6 +133,14 @@ __device__ __forceinline__ int kv_block_steps(const BackwardParams& p, int blk) 
   const int q_lo = max(0, J0 - off);
   const int q_hi = (int)min((long long)p.Lq - 1, (long long)J0 + kKvKeys - 1 + Weff - 1 - off);
   return q_lo <= q_hi ? q_hi / 32 - q_lo / 32 + 1 : 0;
+}
+
+// base + off computed here, as one value: the compiler would otherwise fold a per-tile scalar
+// base into every per-lane address separately (two vector operations per address).
+__device__ __forceinline__ uint32_t base_at(uint32_t base, uint32_t off) {
+  uint32_t r;
+  asm volatile("v_add_u32_e32 %0, %1, %2" : "=v"(r) : "s"(__builtin_amdgcn_readfirstlane(base)), "v"(off));
+  return r;
 }
 
 // The lane's index, read where it is used (a value the compiler cannot keep across a loop).
@@ -569,19 +577,21 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void bwd_dq_kernel(BackwardParams
   auto compute_tile = [&](int kt, int st) {
     const int j0 = kt * 32;
     if (!(nq > 0) || j0 > wj_hi || j0 + 31 < wj_lo) return;
-    const uint32_t stage = ring_base + st * kDqStage;
+    const uint32_t stage = ring_base + st * kDqStage;  // (wave-uniform)
     const uint32_t kt_lds = stage;
     // register r of an accumulator holds key j0 + jj, jj = 8 (r >> 2) + 4 hf + (r & 3); its
     // bias entry is slice entry col - jj + 31.  These reads go out first, their latency hidden
     // behind the products.
-    const uint32_t bsl = stage + kDqBias + wave * 256 + 4u * (uint32_t)(col - 4 * hf + 31);
+    // (x_r = 8 (r >> 2) + (r & 3) <= 27: the lane's base is entry col - 4 hf + 4, the entry of
+    // x_r = 27, so every register's offset is a non-negative constant the read instruction holds)
+    const uint32_t bsl = base_at(stage + kDqBias + wave * 256, 4u * (uint32_t)(col - 4 * hf + 4));
     float bv[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) bv[r] = lds_ldf(bsl - 4u * (8 * (r >> 2) + (r & 3)));
+    for (int r = 0; r < 16; ++r) bv[r] = lds_ldf(bsl + 4u * (27 - (8 * (r >> 2) + (r & 3))));
     // S^T = K Q^T, then dP^T = V dO^T: rows are keys, the lane's column is its query.  The
     // stage base is a multiple of 256 bytes, so (base + lane offset) ^ (32 ks) is the swizzled
     // address of chunk 2 ks + hf; V sits 8 KB after K.
-    const uint32_t ka = kt_lds + rowA;
+    const uint32_t ka = base_at(kt_lds, rowA);
     f32x16_t st_acc = zero_f32x16(), dpt = zero_f32x16();
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) st_acc = mfma_32x32x16(lds_ld16(ka ^ (32u * ks)), qr[ks], st_acc);
@@ -591,10 +601,12 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void bwd_dq_kernel(BackwardParams
 #pragma unroll
     for (int r = 0; r < 16; ++r)
       ds[r] = fast_exp2(fmaf(st_acc[r], p.scale_log2, fmaf(bv[r], kLog2e, -lse2))) * (dpt[r] - dd);
+    // table cell (row col - jj + 31, column col): from the cell of x_r = 27, 34 (27 - x_r) further
+    float* const dcell = diag + (col - 4 * hf + 4) * kDiagStride + col;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) diag[(col - (8 * (r >> 2) + 4 * hf + (r & 3)) + 31) * kDiagStride + col] = ds[r];
+    for (int r = 0; r < 16; ++r) dcell[kDiagStride * (27 - (8 * (r >> 2) + (r & 3)))] = ds[r];
     // dQ^T += K^T dS^T: rows are dims (K read transposed), the lane's column its query
-    const uint32_t t1 = kt_lds + tr1, t2 = kt_lds + tr2;
+    const uint32_t t1 = base_at(kt_lds, tr1), t2 = base_at(kt_lds, tr2);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const u32x4_t bs = pack_p_operand(ds + 8 * ks);

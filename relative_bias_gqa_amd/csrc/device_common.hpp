@@ -122,6 +122,14 @@ typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
 typedef __attribute__((address_space(3))) float lds_f32_t;
 __device__ __forceinline__ u32x4_t lds_ld16(uint32_t a) { return *(const lds_u32x4_t*)(size_t)a; }
 __device__ __forceinline__ float lds_ldf(uint32_t a) { return *(const lds_f32_t*)(size_t)a; }
+// 16-byte-chunk swizzle of LDS tiles with 256-byte rows: chunk c of row r is stored at chunk
+// c ^ lds_swz(r), lds_swz(r) = 4 (r & 3) + ((r >> 2) & 3).  Sixteen consecutive rows read at one
+// logical chunk (a row-wise MFMA operand, 16 lanes x 16 B) hit sixteen different chunks, and
+// the rows x columns a transposed read (ds_read_b64_tr_b16) gathers in each half-wave hit all
+// 64 banks.  Rows r and r + 8 differ by chunk bit 1 (byte address bit 5).  (The forward
+// kernels keep their own V layout: this one measured no faster there.)
+__device__ __forceinline__ int lds_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
 __device__ __forceinline__ u32x2_t lds_tr8(uint32_t a) {
   return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(size_t)a));
 }
