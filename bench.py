@@ -444,11 +444,11 @@ def practical_ceilings(torch):
     res["hbm_copy_gbs"] = round(2.0 * nbytes / (e0.elapsed_time(e1) / 1e3 / reps) / 1e9, 1)
     out = torch.empty((), device=dev, dtype=torch.float32)
     for _ in range(2):
-        torch.sum(src, out=out)
+        torch.sum(src, dim=0, out=out)
     torch.cuda.synchronize()
     e0.record()
     for _ in range(reps):
-        torch.sum(src, out=out)
+        torch.sum(src, dim=0, out=out)
     e1.record()
     torch.cuda.synchronize()
     res["hbm_read_gbs"] = round(nbytes / (e0.elapsed_time(e1) / 1e3 / reps) / 1e9, 1)
@@ -589,7 +589,10 @@ def main(argv=None) -> int:
         line["cpu_baseline"] = None
     if not args.no_ceilings:
         log("[bench] practical ceilings: bf16 GEMM, device copy, read stream")
-        line["practical_ceilings"] = practical_ceilings(torch)
+        try:
+            line["practical_ceilings"] = practical_ceilings(torch)
+        except Exception as exc:  # context only: never let it cost the measurement
+            line["practical_ceilings"] = {"error": f"{type(exc).__name__}: {exc}"}
     line["workloads"] = [results[n] for n in names if n != HEADLINE]
     print(json.dumps(line), flush=True)
     return 0
