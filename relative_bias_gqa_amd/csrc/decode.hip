@@ -94,38 +94,6 @@ __device__ __forceinline__ SeqInfo seq_info(const DecodeParams& p, int b) {
   return s;
 }
 
-// Exclusive prefix of visible units over the sequences, pre[0..B], computed by the whole
-// workgroup (NT threads) into LDS.  Returns pre[B].
-template <int NT>
-__device__ int batch_prefix(const DecodeParams& p, int* pre, int* scratch) {
-  const int tid = threadIdx.x;
-  const int per = (p.B + NT - 1) / NT;
-  int local = 0;
-  for (int i = 0; i < per; ++i) {
-    const int b = tid * per + i;
-    if (b < p.B) local += seq_info(p, b).nch;
-  }
-  scratch[tid] = local;
-  __syncthreads();
-  for (int off = 1; off < NT; off <<= 1) {
-    const int v = tid >= off ? scratch[tid - off] : 0;
-    __syncthreads();
-    scratch[tid] += v;
-    __syncthreads();
-  }
-  int run = scratch[tid] - local;
-  for (int i = 0; i < per; ++i) {
-    const int b = tid * per + i;
-    if (b < p.B) {
-      pre[b] = run;
-      run += seq_info(p, b).nch;
-    }
-  }
-  if (tid == NT - 1) pre[p.B] = scratch[tid];
-  __syncthreads();
-  return pre[p.B];
-}
-
 // Position in the unit stream: sequence, segment within the sequence, absolute chunk.
 struct Cursor {
   int b, kh, c;
@@ -162,6 +130,120 @@ __device__ __forceinline__ void cursor_next(const DecodeParams& p, Cursor& c) {
   }
 }
 
+// ---- division of the unit stream among the workgroups ----------------------------------
+// Units do not cost the same: a unit whose keys are all at distance >= R - 1 from every
+// query of its sequence adds the single clamp entry r[h, R - 1], any other one stages a
+// slice of r per head and adds it element by element, about 1.2 times the time.  With C(k)
+// the cost of the units before unit k and C their total, unit k goes to workgroup
+// floor(C(k) P / C): each workgroup gets a contiguous run of units of equal cost.
+constexpr int kCostSat = 5;
+constexpr int kCostUnsat = 6;
+
+// leading units of the visible range whose keys are all at distance >= R - 1
+__device__ __forceinline__ int seq_nsat(const DecodeParams& p, const SeqInfo& s) {
+  // unit c (keys 64 c .. 64 c + 63) qualifies iff (ctx - n_q) - (64 c + 63) >= R - 1
+  const long long lim = (long long)s.ctx - p.n_q - p.R - (kUnit - 2);
+  if (lim < 0) return 0;
+  return (int)min(max(lim / kUnit + 1 - s.clo, 0LL), (long long)s.nch);
+}
+
+// cost of one segment (one KV head's share) of a sequence
+__device__ __forceinline__ long long seg_cost(int nch, int nsat) {
+  return (long long)nsat * kCostSat + (long long)(nch - nsat) * kCostUnsat;
+}
+
+// Workgroups that take part: at most one per cost kCostUnsat, so that every workgroup's
+// cost range (C / P wide) holds the start of some unit and no workgroup is left empty.
+__device__ __forceinline__ int split_count(const DecodeParams& p, long long ctot) {
+  return (int)max(1LL, min((long long)p.P, ctot / kCostUnsat));
+}
+
+struct SplitRange {
+  int P;        // workgroups that take part
+  int n_units;  // this workgroup's units
+  Cursor c0;    // its first unit
+};
+
+// This workgroup's share of the unit stream, computed by the whole workgroup (NT threads)
+// with `lds` as scratch (at least 16 NT + 12 (B + 1) bytes, not yet in use by any load).
+template <int NT>
+__device__ SplitRange split_range(const DecodeParams& p, unsigned char* lds) {
+  long long* scan_u = (long long*)lds;
+  long long* scan_c = scan_u + NT;
+  long long* pre_c = scan_c + NT;          // [B + 1]: cost of the sequences before b (all segments)
+  int* pre_u = (int*)(pre_c + p.B + 1);    // [B + 1]: units per segment of the sequences before b
+  const int tid = threadIdx.x;
+  const int per = (p.B + NT - 1) / NT;
+  long long lu = 0, lc = 0;
+  for (int i = 0; i < per; ++i) {
+    const int b = tid * per + i;
+    if (b < p.B) {
+      const SeqInfo si = seq_info(p, b);
+      lu += si.nch;
+      lc += seg_cost(si.nch, seq_nsat(p, si));
+    }
+  }
+  scan_u[tid] = lu;
+  scan_c[tid] = lc;
+  __syncthreads();
+  for (int off = 1; off < NT; off <<= 1) {
+    const long long vu = tid >= off ? scan_u[tid - off] : 0;
+    const long long vc = tid >= off ? scan_c[tid - off] : 0;
+    __syncthreads();
+    scan_u[tid] += vu;
+    scan_c[tid] += vc;
+    __syncthreads();
+  }
+  long long ru = scan_u[tid] - lu, rc = scan_c[tid] - lc;
+  for (int i = 0; i < per; ++i) {
+    const int b = tid * per + i;
+    if (b < p.B) {
+      const SeqInfo si = seq_info(p, b);
+      pre_u[b] = (int)ru;
+      pre_c[b] = rc * p.KH;
+      ru += si.nch;
+      rc += seg_cost(si.nch, seq_nsat(p, si));
+    }
+  }
+  if (tid == NT - 1) {
+    pre_u[p.B] = (int)scan_u[tid];
+    pre_c[p.B] = scan_c[tid] * p.KH;
+  }
+  __syncthreads();
+  const long long ctot = pre_c[p.B];
+  const int units = pre_u[p.B] * p.KH;
+  SplitRange sr;
+  sr.P = split_count(p, ctot);
+  sr.n_units = 0;
+  const int w = blockIdx.x;
+  // index of the first unit whose cost prefix is >= T (units if there is none)
+  auto first_unit = [&](long long T) {
+    if (T >= ctot) return units;
+    int lo = 0, hi = p.B - 1;  // last b with pre_c[b] <= T
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (pre_c[mid] <= T) lo = mid;
+      else hi = mid - 1;
+    }
+    const SeqInfo si = seq_info(p, lo);
+    const int nsat = seq_nsat(p, si);
+    const long long sc = seg_cost(si.nch, nsat);
+    const long long r = T - pre_c[lo];
+    const int kh = (int)(r / sc);
+    const long long r2 = r - kh * sc, sat_cost = (long long)nsat * kCostSat;
+    const int k = r2 <= sat_cost ? (int)((r2 + kCostSat - 1) / kCostSat)
+                                 : nsat + (int)((r2 - sat_cost + kCostUnsat - 1) / kCostUnsat);
+    return pre_u[lo] * p.KH + kh * si.nch + k;
+  };
+  if (w < sr.P) {
+    const int u0 = first_unit(((long long)w * ctot + sr.P - 1) / sr.P);
+    sr.n_units = first_unit(((long long)(w + 1) * ctot + sr.P - 1) / sr.P) - u0;
+    sr.c0 = cursor_at(p, pre_u, u0);
+  }
+  __syncthreads();  // every wave is done with the scratch before any load reaches it
+  return sr;
+}
+
 // NW: waves per workgroup (4, or 8 = two per SIMD, so that one wave's softmax overlaps
 // its partner's MFMAs).  Every computing wave owns one 32-row block and one 32-key half of
 // each unit (KS = 2 waves share a unit's keys, KB = 1 key block per wave).  NL: waves that
@@ -180,8 +262,7 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_split_kernel(DecodeParams p
   static_assert(NL >= 1 && NL <= NW && NI >= 1 && NI * 4 * NL == kUnit, "load split");
   static_assert(2 * kLoadsPerStage < 64, "vmcnt range");
   __shared__ __attribute__((aligned(1024))) unsigned char ring[kStages * kStageBytes];
-  __shared__ int pre[kDecodeMaxBatch + 1];
-  __shared__ int scratch[NT];
+  static_assert(16 * NT + 12 * (kDecodeMaxBatch + 1) <= kStages * kStageBytes, "split scratch");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -191,12 +272,10 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_split_kernel(DecodeParams p
   const int li = wave - (NW - NL);  // index among the loading waves, < 0 for the others
   const bool loader = li >= 0;
 
-  const int units = batch_prefix<NT>(p, pre, scratch) * p.KH;
-  const int P = min(p.P, units);
+  const SplitRange sr = split_range<NT>(p, ring);
   const int w = blockIdx.x;
-  if (w >= P) return;  // uniform
-  const int u0 = (int)((long long)w * units / P);
-  const int n_units = (int)((long long)(w + 1) * units / P) - u0;
+  if (w >= sr.P) return;  // uniform
+  const int n_units = sr.n_units;
 
   // ---- loads of one unit into a stage -------------------------------------------------
   // K/V: loading wave li issues tokens TPW li .. TPW li + TPW - 1 of the 64-token unit,
@@ -489,7 +568,7 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_split_kernel(DecodeParams p
   };
 
   // ---- main loop: unit t computed from stage t % 4 while units t+1..t+3 load ------------
-  Cursor cc = cursor_at(p, pre, u0);
+  Cursor cc = sr.c0;
   Cursor ic = cc;
   begin_segment(cc);  // before any LDS load is in flight
   const int prologue = min(kStages - 1, n_units);
@@ -540,7 +619,7 @@ constexpr int kMergeLse = 2048;  // log2-sum-exps of a segment kept in LDS for t
 __global__ __launch_bounds__(kThreads) void decode_merge_kernel(DecodeParams p) {
   __shared__ float lse_s[kMergeLse];
   __shared__ float red[2][kThreads / 64];
-  __shared__ int ired[2][kThreads / 64];
+  __shared__ long long cred[2][kThreads / 64];
   __shared__ f32x4_t acc_lds[8][32];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -549,12 +628,13 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(DecodeParams p) 
   const int b = seg / p.KH;
   const int kh = seg - b * p.KH;
 
-  // units before sequence b, and in total
-  int before = 0, total = 0;
+  // cost of the sequences before b, and in total
+  long long before = 0, total = 0;
   for (int bb = tid; bb < p.B; bb += kThreads) {
-    const int n = seq_info(p, bb).nch;
-    total += n;
-    if (bb < b) before += n;
+    const SeqInfo si = seq_info(p, bb);
+    const long long c = seg_cost(si.nch, seq_nsat(p, si));
+    total += c;
+    if (bb < b) before += c;
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
@@ -562,25 +642,27 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(DecodeParams p) 
     total += __shfl_xor(total, off);
   }
   if (lane == 0) {
-    ired[0][wave] = before;
-    ired[1][wave] = total;
+    cred[0][wave] = before;
+    cred[1][wave] = total;
   }
   __syncthreads();
   before = 0;
   total = 0;
 #pragma unroll
   for (int w = 0; w < kThreads / 64; ++w) {
-    before += ired[0][w];
-    total += ired[1][w];
+    before += cred[0][w];
+    total += cred[1][w];
   }
-  const long long units = (long long)total * p.KH;
-  const long long P = min((long long)p.P, units);
-  const int nch = seq_info(p, b).nch;
-  const long long us = (long long)before * p.KH + (long long)kh * nch;
-  const long long ue = us + nch;
-  // workgroup w covers units [w units / P, (w + 1) units / P)
-  const int w_first = (int)(((us + 1) * P + units - 1) / units) - 1;
-  const int w_last = (int)((ue * P + units - 1) / units) - 1;
+  const long long ctot = total * p.KH;
+  const long long P = split_count(p, ctot);
+  // the workgroups that hold this segment's first and last units
+  const SeqInfo sb = seq_info(p, b);
+  const int nsat = seq_nsat(p, sb);
+  const long long sc = seg_cost(sb.nch, nsat);
+  const long long c_first = before * p.KH + kh * sc;
+  const long long c_last = c_first + sc - (nsat == sb.nch ? kCostSat : kCostUnsat);
+  const int w_first = (int)(c_first * P / ctot);
+  const int w_last = (int)(c_last * P / ctot);
   // piece i = (workgroup w_first + i / KS, key half i % KS)
   const int n_pieces = (w_last - w_first + 1) * p.KS;
   auto slot_row = [&](int i) {
