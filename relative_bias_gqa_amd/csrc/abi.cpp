@@ -101,7 +101,7 @@ bool plan_decode(int B, int n_q, int Hq, int Hkv, int max_ctx_len, int max_block
   const int KS = 2;
   const int NW = rows <= 64 ? 4 : 8;
   const long long slots = (P + batch * KH) * KS;
-  if (batch * KH * rows > 0x7fffffffLL) return false;
+  if (batch * KH * rows * rattn::kDecodeMergeSlices > 0x7fffffffLL) return false;
   pl->gs = gs;
   pl->n_hs = n_hs;
   pl->KH = (int)KH;

@@ -165,14 +165,15 @@ struct SplitRange {
 };
 
 // This workgroup's share of the unit stream, computed by the whole workgroup (NT threads)
-// with `lds` as scratch (at least 16 NT + 12 (B + 1) bytes, not yet in use by any load).
+// with `lds` as scratch (at least NT / 4 + 12 (B + 1) bytes, not yet in use by any load).
 template <int NT>
 __device__ SplitRange split_range(const DecodeParams& p, unsigned char* lds) {
-  long long* scan_u = (long long*)lds;
-  long long* scan_c = scan_u + NT;
-  long long* pre_c = scan_c + NT;          // [B + 1]: cost of the sequences before b (all segments)
+  long long* wave_u = (long long*)lds;     // [NT / 64]: units of each wave's sequences
+  long long* wave_c = wave_u + NT / 64;    // [NT / 64]: their cost
+  long long* pre_c = wave_c + NT / 64;     // [B + 1]: cost of the sequences before b (all segments)
   int* pre_u = (int*)(pre_c + p.B + 1);    // [B + 1]: units per segment of the sequences before b
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int per = (p.B + NT - 1) / NT;
   long long lu = 0, lc = 0;
   for (int i = 0; i < per; ++i) {
@@ -183,18 +184,26 @@ __device__ SplitRange split_range(const DecodeParams& p, unsigned char* lds) {
       lc += seg_cost(si.nch, seq_nsat(p, si));
     }
   }
-  scan_u[tid] = lu;
-  scan_c[tid] = lc;
-  __syncthreads();
-  for (int off = 1; off < NT; off <<= 1) {
-    const long long vu = tid >= off ? scan_u[tid - off] : 0;
-    const long long vc = tid >= off ? scan_c[tid - off] : 0;
-    __syncthreads();
-    scan_u[tid] += vu;
-    scan_c[tid] += vc;
-    __syncthreads();
+  // inclusive scan within the wave, then the totals of the waves before this one
+  long long su = lu, sc = lc;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const long long tu = __shfl_up(su, off), tc = __shfl_up(sc, off);
+    if (lane >= off) {
+      su += tu;
+      sc += tc;
+    }
   }
-  long long ru = scan_u[tid] - lu, rc = scan_c[tid] - lc;
+  if (lane == 63) {
+    wave_u[wave] = su;
+    wave_c[wave] = sc;
+  }
+  __syncthreads();
+  for (int v = 0; v < wave; ++v) {
+    su += wave_u[v];
+    sc += wave_c[v];
+  }
+  long long ru = su - lu, rc = sc - lc;
   for (int i = 0; i < per; ++i) {
     const int b = tid * per + i;
     if (b < p.B) {
@@ -206,8 +215,8 @@ __device__ SplitRange split_range(const DecodeParams& p, unsigned char* lds) {
     }
   }
   if (tid == NT - 1) {
-    pre_u[p.B] = (int)scan_u[tid];
-    pre_c[p.B] = scan_c[tid] * p.KH;
+    pre_u[p.B] = (int)su;
+    pre_c[p.B] = sc * p.KH;
   }
   __syncthreads();
   const long long ctot = pre_c[p.B];
@@ -262,7 +271,7 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_split_kernel(DecodeParams p
   static_assert(NL >= 1 && NL <= NW && NI >= 1 && NI * 4 * NL == kUnit, "load split");
   static_assert(2 * kLoadsPerStage < 64, "vmcnt range");
   __shared__ __attribute__((aligned(1024))) unsigned char ring[kStages * kStageBytes];
-  static_assert(16 * NT + 12 * (kDecodeMaxBatch + 1) <= kStages * kStageBytes, "split scratch");
+  static_assert(NT / 4 + 12 * (kDecodeMaxBatch + 1) <= kStages * kStageBytes, "split scratch");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -603,28 +612,27 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_split_kernel(DecodeParams p
   flush_segment(seg);
 }
 
-// (max, sum of 2^(x - max)) pairs: the combination of two partial log2-sum-exps.
-__device__ __forceinline__ void lse_combine(float& m, float& z, float m2, float z2) {
-  const float mm = fmaxf(m, m2);
-  if (mm == kNegInf) return;  // both empty
-  z = (m == kNegInf ? 0.f : z * fast_exp2(m - mm)) + (m2 == kNegInf ? 0.f : z2 * fast_exp2(m2 - mm));
-  m = mm;
-}
+// Merge: one workgroup per (segment, row, slice of the 128 outputs; SLICES = 4 when a
+// segment has many pieces, else 1).  Its threads form groups of 32 / SLICES (one float4
+// each of the slice); group g takes pieces g, g + groups, ..., eight at a time with all
+// eight pieces' loads in flight, and keeps a running maximum, sum and weighted output (one
+// pass: a piece's weight is 2^(lse - max) against the running max).  The groups' partial
+// results are then combined through LDS in group order.
+constexpr int kMergeBatch = 8;  // pieces per group and round
 
-constexpr int kMergeLse = 2048;  // log2-sum-exps of a segment kept in LDS for the second pass
-
-// One workgroup per (segment, row): merge the pieces of the segment.  One pass over the
-// pieces' log2-sum-exps (an online maximum and sum, combined across lanes and waves), then
-// one over their outputs with eight pieces' loads in flight per thread.
+template <int SLICES>
 __global__ __launch_bounds__(kThreads) void decode_merge_kernel(DecodeParams p) {
-  __shared__ float lse_s[kMergeLse];
-  __shared__ float red[2][kThreads / 64];
+  constexpr int kMergeLanes = kHeadDim / SLICES / 4;  // float4 lanes per piece
+  constexpr int kMergeGroups = kThreads / kMergeLanes;
   __shared__ long long cred[2][kThreads / 64];
-  __shared__ f32x4_t acc_lds[8][32];
+  __shared__ float gm[kMergeGroups], gz[kMergeGroups];
+  __shared__ f32x4_t gacc[kMergeGroups][kMergeLanes];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int seg = blockIdx.x / p.rows;
-  const int r_row = blockIdx.x - seg * p.rows;
+  const int slice = blockIdx.x % SLICES;
+  const int sr = blockIdx.x / SLICES;
+  const int seg = sr / p.rows;
+  const int r_row = sr - seg * p.rows;
   const int b = seg / p.KH;
   const int kh = seg - b * p.KH;
 
@@ -669,69 +677,82 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(DecodeParams p) 
     return ((size_t)(w_first + i / p.KS + seg) * p.KS + (i % p.KS)) * p.rows + r_row;
   };
 
+  const int d4 = tid % kMergeLanes, grp = tid / kMergeLanes;
+  const int col = slice * (kHeadDim / SLICES) + 4 * d4;
   float m = kNegInf, z = 0.f;
-  for (int i = tid; i < n_pieces; i += kThreads) {
-    const float l = p.ws_lse[slot_row(i)];
-    if (i < kMergeLse) lse_s[i] = l;
-    lse_combine(m, z, l, 1.f);
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const float m2 = __shfl_xor(m, off), z2 = __shfl_xor(z, off);
-    lse_combine(m, z, m2, z2);
-  }
-  if (lane == 0) {
-    red[0][wave] = m;
-    red[1][wave] = z;
-  }
-  __syncthreads();
-  float M = red[0][0], Z = red[1][0];
-#pragma unroll
-  for (int w = 1; w < kThreads / 64; ++w) lse_combine(M, Z, red[0][w], red[1][w]);
-  auto lse_of = [&](int i) { return i < kMergeLse ? lse_s[i] : p.ws_lse[slot_row(i)]; };
-
-  const int d4 = tid & 31, grp = tid >> 5;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  int i = grp;
-  for (; i + 8 * 7 < n_pieces; i += 64) {
-    f32x4_t x[8];
-    float wt[8];
+  for (int i0 = grp; i0 < n_pieces; i0 += kMergeGroups * kMergeBatch) {
+    float l[kMergeBatch];
+    f32x4_t x[kMergeBatch];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const size_t sr = slot_row(i + 8 * u);
-      x[u] = *(const f32x4_t*)(p.ws_o + sr * kHeadDim + 4 * d4);
-      wt[u] = fast_exp2(lse_of(i + 8 * u) - M);
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const int i = i0 + kMergeGroups * u;
+      l[u] = kNegInf;
+      x[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      if (i < n_pieces) {
+        const size_t sr_i = slot_row(i);
+        l[u] = p.ws_lse[sr_i];
+        x[u] = *(const f32x4_t*)(p.ws_o + sr_i * kHeadDim + col);
+      }
     }
+    float mb = m;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) acc += wt[u] * x[u];
+    for (int u = 0; u < kMergeBatch; ++u) mb = fmaxf(mb, l[u]);
+    if (mb != kNegInf) {
+      const float scale = fast_exp2(m - mb);  // 0 while m is still -inf
+      acc *= scale;
+      z *= scale;
+#pragma unroll
+      for (int u = 0; u < kMergeBatch; ++u) {
+        const float wt = fast_exp2(l[u] - mb);  // 0 for an empty piece (lse -inf)
+        acc += wt * x[u];
+        z += wt;
+      }
+      m = mb;
+    }
   }
-  for (; i < n_pieces; i += 8) {
-    const size_t sr = slot_row(i);
-    acc += fast_exp2(lse_of(i) - M) * *(const f32x4_t*)(p.ws_o + sr * kHeadDim + 4 * d4);
+  if (d4 == 0) {
+    gm[grp] = m;
+    gz[grp] = z;
   }
-  acc_lds[grp][d4] = acc;
+  gacc[grp][d4] = acc;
   __syncthreads();
-  const int kvh = kh / p.n_hs;
-  const int hs = kh - kvh * p.n_hs;
-  const int tq = r_row / p.gs;
-  const int h = kvh * p.G + hs * p.gs + (r_row - tq * p.gs);
-  const size_t out_row = ((size_t)b * p.n_q + tq) * p.Hq + h;
-  if (grp == 0) {
-    f32x4_t tot = acc_lds[0][d4];
+  if (tid < kMergeLanes) {
+    float M = kNegInf;
 #pragma unroll
-    for (int g = 1; g < 8; ++g) tot += acc_lds[g][d4];
-    const float inv = 1.f / Z;
-    *(u32x2_t*)(p.out + out_row * kHeadDim + 4 * d4) =
+    for (int g = 0; g < kMergeGroups; ++g) M = fmaxf(M, gm[g]);
+    float Z = 0.f;
+    f32x4_t tot = {0.f, 0.f, 0.f, 0.f};
+    if (M != kNegInf) {
+#pragma unroll
+      for (int g = 0; g < kMergeGroups; ++g) {
+        const float wt = fast_exp2(gm[g] - M);
+        Z += wt * gz[g];
+        tot += wt * gacc[g][tid];
+      }
+    }
+    const float inv = Z > 0.f ? 1.f / Z : 0.f;
+    const int kvh = kh / p.n_hs;
+    const int hs = kh - kvh * p.n_hs;
+    const int tq = r_row / p.gs;
+    const int h = kvh * p.G + hs * p.gs + (r_row - tq * p.gs);
+    const size_t out_row = ((size_t)b * p.n_q + tq) * p.Hq + h;
+    *(u32x2_t*)(p.out + out_row * kHeadDim + slice * (kHeadDim / SLICES) + 4 * tid) =
         u32x2_t{pack_bf16x2(tot[0] * inv, tot[1] * inv), pack_bf16x2(tot[2] * inv, tot[3] * inv)};
+    if (tid == 0 && slice == 0 && p.lse != nullptr) p.lse[out_row] = Z > 0.f ? (M + __log2f(Z)) * kLn2 : kNegInf;
   }
-  if (tid == 0 && p.lse != nullptr) p.lse[out_row] = (M + __log2f(Z)) * kLn2;
 }
 
 }  // namespace
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
-  const long long grid2 = (long long)p.B * p.KH * p.rows;
   if (p.B <= 0) return hipSuccess;
+  if (p.KH < 1) return hipErrorInvalidConfiguration;
+  // merge slices: 4 when a segment averages 64 or more pieces (KS per workgroup that
+  // touches it), so that a row's pieces are read by four workgroups at once
+  const long long segs = (long long)p.B * p.KH;
+  const int slices = (long long)p.KS * (p.P / segs + 2) >= 64 ? kDecodeMergeSlices : 1;
+  const long long grid2 = segs * p.rows * slices;
   if (grid2 > 0x7fffffffLL || p.P < 1) return hipErrorInvalidConfiguration;
   if ((p.NW != 4 && p.NW != 8) || p.KS != 2) return hipErrorInvalidConfiguration;
   // every computing role (32-row block, key half) needs a wave of its own; the waves left
@@ -766,7 +787,8 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
 #undef RATTN_SPLIT
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_merge_kernel, dim3((unsigned)grid2), dim3(kThreads), 0, stream, p);
+  if (slices == 1) hipLaunchKernelGGL(decode_merge_kernel<1>, dim3((unsigned)grid2), dim3(kThreads), 0, stream, p);
+  else hipLaunchKernelGGL(decode_merge_kernel<kDecodeMergeSlices>, dim3((unsigned)grid2), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -131,5 +131,6 @@ constexpr int kDecodeMaxRows = 128;       // n_q * gs (four blocks of 32 rows)
 constexpr int kDecodeBiasFloats = 1024;   // gs * (63 + n_q) per unit
 constexpr int kDecodeMaxBatch = 2048;     // sequences per launch (prefix table in LDS)
 constexpr int kDecodeUnit = 64;           // tokens per unit
+constexpr int kDecodeMergeSlices = 4;     // merge workgroups per (segment, row), 32 outputs each
 
 }  // namespace rattn
