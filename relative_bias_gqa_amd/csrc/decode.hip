@@ -371,6 +371,11 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_split_kernel(DecodeParams p
   const int ks_w = wave / n_rb;
   const bool wave_active = rb < n_rb && ks_w < KS;
   const int kb_lo = ks_w;
+  // The loading waves issue first whenever they are ready: with more computing waves than
+  // SIMDs a loading wave shares its SIMD with a computing one, and at equal priority its
+  // load issue after each barrier queues behind that wave's MFMA and softmax instructions
+  // (1M-token MTP verify: 3.5 % shorter split kernel).
+  if (loader) __builtin_amdgcn_s_setprio(3);
   // LDS operand bases (stage 0).  K rows are 256 B with 16-byte chunk c of key j at chunk
   // c ^ (j & 15): the A operand of k-step k8 (key 32 kb + col, chunk 2 k8 + hf) sits at
   // kx0 ^ (32 k8).  V rows have chunk c of key j at c ^ (2 (j & 7)): the transposed read
