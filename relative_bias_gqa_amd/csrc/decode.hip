@@ -83,15 +83,24 @@ struct SeqInfo {
   int nch;     // units of the visible range
 };
 
-__device__ __forceinline__ SeqInfo seq_info(const DecodeParams& p, int b) {
+__device__ __forceinline__ SeqInfo seq_info_of(const DecodeParams& p, int ctx_len, int W) {
   SeqInfo s;
-  s.ctx = min(max(p.ctx_lens[b], 1), p.mbps * 128);
-  const int W = p.windows ? p.windows[b] : 0;
+  s.ctx = min(max(ctx_len, 1), p.mbps * 128);
   s.weff = W > 0 ? W : 0x40000000;
   s.vis_lo = W > 0 ? max(0, s.ctx - p.n_q - W + 1) : 0;
   s.clo = s.vis_lo / kUnit;
   s.nch = (s.ctx - 1) / kUnit + 1 - s.clo;
   return s;
+}
+
+__device__ __forceinline__ SeqInfo seq_info(const DecodeParams& p, int b) {
+  return seq_info_of(p, p.ctx_lens[b], p.windows ? p.windows[b] : 0);
+}
+
+// The same for a sequence index that every lane of the wave holds: read through the scalar
+// cache, so that a loading wave's read does not wait behind its global -> LDS loads.
+__device__ __forceinline__ SeqInfo seq_info_u(const DecodeParams& p, int b) {
+  return seq_info_of(p, uniform_load_i32(p.ctx_lens + b), p.windows ? uniform_load_i32(p.windows + b) : 0);
 }
 
 // Position in the unit stream: sequence, segment within the sequence, absolute chunk.
@@ -110,7 +119,7 @@ __device__ __forceinline__ Cursor cursor_at(const DecodeParams& p, const int* pr
   }
   Cursor c;
   c.b = lo;
-  c.si = seq_info(p, lo);
+  c.si = seq_info_u(p, lo);
   const int r = u - pre[lo] * p.KH;
   c.kh = r / c.si.nch;
   c.c = c.si.clo + (r - c.kh * c.si.nch);
@@ -123,7 +132,7 @@ __device__ __forceinline__ void cursor_next(const DecodeParams& p, Cursor& c) {
       c.kh = 0;
       if (c.b + 1 < p.B) {
         ++c.b;
-        c.si = seq_info(p, c.b);
+        c.si = seq_info_u(p, c.b);
       }
     }
     c.c = c.si.clo;
@@ -234,7 +243,7 @@ __device__ SplitRange split_range(const DecodeParams& p, unsigned char* lds) {
       if (pre_c[mid] <= T) lo = mid;
       else hi = mid - 1;
     }
-    const SeqInfo si = seq_info(p, lo);
+    const SeqInfo si = seq_info_u(p, lo);
     const int nsat = seq_nsat(p, si);
     const long long sc = seg_cost(si.nch, nsat);
     const long long r = T - pre_c[lo];
@@ -669,7 +678,7 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(DecodeParams p) 
   const long long ctot = total * p.KH;
   const long long P = split_count(p, ctot);
   // the workgroups that hold this segment's first and last units
-  const SeqInfo sb = seq_info(p, b);
+  const SeqInfo sb = seq_info_u(p, b);
   const int nsat = seq_nsat(p, sb);
   const long long sc = seg_cost(sb.nch, nsat);
   const long long c_first = before * p.KH + kh * sc;
