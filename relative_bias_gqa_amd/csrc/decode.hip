@@ -12,13 +12,15 @@
 // Work decomposition: a segment is (sequence, KV head, query-head subgroup); its rows are
 // the n_q tokens x gs query heads that share the KV head (GQA packing: each K/V byte is
 // read from HBM once for all of them).  A segment's visible keys are cut into 64-token
-// units; the units of all segments, in order, form one stream that is divided evenly
-// among P workgroups (one per CU), so every CU moves the same number of bytes whatever
-// the context lengths.  A workgroup walks its units in order and writes one normalised
-// partial output and log2-sum-exp per segment it touches (slot = workgroup + segment);
-// the merge kernel combines the pieces of each segment.
+// units; the units of all segments, in order, form one stream that is divided among P
+// workgroups (one per CU) in contiguous runs of equal cost, a unit that needs per-key bias
+// entries weighing 6 against 5 for one whose keys all take the clamp entry, so every CU
+// finishes at about the same time whatever the context lengths.  A workgroup walks its run
+// in order and writes one normalised partial output and log2-sum-exp per segment it touches
+// (slot = workgroup + segment); the merge kernel combines the pieces of each segment.
 //
-// Split kernel pipeline (4 waves): K and V rows of a unit are gathered through the block
+// Split kernel pipeline (4 waves, or 8 when a segment has more than two 32-row blocks, the
+// loading waves at raised priority): K and V rows of a unit are gathered through the block
 // table straight into LDS (global_load_lds_dwordx4, no register staging) into a ring of
 // four stages, three units ahead of the one being computed, so about 96 KB per CU are
 // always in flight.  Slots outside a sequence's visible range are loaded from a zero row
