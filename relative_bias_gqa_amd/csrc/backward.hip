@@ -57,26 +57,49 @@ __global__ __launch_bounds__(256) void bwd_fill_zero_kernel(float* a, size_t n) 
 
 // D = sum_d dout[b, t, h, d] * out[b, t, h, d] and L2 = lse[b, t, h] * log2(e) for every row,
 // in fp32, stored head-major ([B, Hq, Lq]) so that a query tile of one head is contiguous.
+// A workgroup takes one (batch, head) pair and kRowdotRows consecutive query positions, so its
+// D and L2 stores fill whole cache lines from one XCD.  Sixteen lanes share a row, each reading
+// one 16-byte chunk of dout and of out; the sixteen partial sums are then added across those
+// lanes.
+constexpr int kRowdotPasses = 2;
+constexpr int kRowdotRows = 16 * kRowdotPasses;  // query positions per workgroup: one 128 B line of D
+
 __global__ __launch_bounds__(256) void bwd_rowdot_kernel(const uint16_t* out, const uint16_t* dout, const float* lse,
-                                                         float* D, float* L2, int Lq, int Hq, size_t rows) {
-  const size_t row = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (row >= rows) return;
-  const u32x4_t* o = (const u32x4_t*)(out + row * kHeadDim);
-  const u32x4_t* g = (const u32x4_t*)(dout + row * kHeadDim);
-  float acc = 0.f;
-#pragma unroll 4
-  for (int c = 0; c < 16; ++c) {
-    const u32x4_t x = o[c], y = g[c];
+                                                         float* D, float* L2, int Lq, int Hq, int n_tb) {
+  const int c = threadIdx.x & 15;
+  const int tb = blockIdx.x % n_tb;
+  const size_t bh = blockIdx.x / n_tb;
+  const size_t b = bh / Hq, h = bh % Hq;
+  const int t0 = tb * kRowdotRows + (threadIdx.x >> 4);
+  u32x4_t x[kRowdotPasses], y[kRowdotPasses];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc = fmaf(bf16_lo_to_f32(x[i]), bf16_lo_to_f32(y[i]), acc);
-      acc = fmaf(bf16_hi_to_f32(x[i]), bf16_hi_to_f32(y[i]), acc);
+  for (int j = 0; j < kRowdotPasses; ++j) {
+    const int t = t0 + 16 * j;
+    x[j] = u32x4_t{0, 0, 0, 0};
+    y[j] = u32x4_t{0, 0, 0, 0};
+    if (t < Lq) {
+      const size_t row = (b * Lq + t) * Hq + h;
+      x[j] = ((const u32x4_t*)(out + row * kHeadDim))[c];
+      y[j] = ((const u32x4_t*)(dout + row * kHeadDim))[c];
     }
   }
-  const size_t h = row % Hq, t = (row / Hq) % Lq, b = row / ((size_t)Hq * Lq);
-  const size_t dst = (b * Hq + h) * Lq + t;
-  D[dst] = acc;
-  L2[dst] = lse[row] * kLog2e;
+#pragma unroll
+  for (int j = 0; j < kRowdotPasses; ++j) {
+    const int t = t0 + 16 * j;
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc = fmaf(bf16_lo_to_f32(x[j][i]), bf16_lo_to_f32(y[j][i]), acc);
+      acc = fmaf(bf16_hi_to_f32(x[j][i]), bf16_hi_to_f32(y[j][i]), acc);
+    }
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 16);
+    if (t < Lq && c == 0) {
+      const size_t dst = bh * Lq + t;
+      D[dst] = acc;
+      L2[dst] = lse[(b * Lq + t) * Hq + h] * kLog2e;
+    }
+  }
 }
 
 // ---- key-stationary pass (dK, dV) -----------------------------------------------------
@@ -686,9 +709,11 @@ hipError_t launch_backward(const BackwardParams& p, hipStream_t stream) {
     fill(p.dv, n_kv);
     return hipGetLastError();
   }
-  const size_t rows = (size_t)p.B * p.Lq * p.Hq;
-  hipLaunchKernelGGL(bwd_rowdot_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream,
-                     (const uint16_t*)p.out, (const uint16_t*)p.dout, p.lse, p.D, p.L2, p.Lq, p.Hq, rows);
+  const int n_tb = (p.Lq + kRowdotRows - 1) / kRowdotRows;
+  const size_t rowdot_blocks = (size_t)p.B * p.Hq * n_tb;
+  if (rowdot_blocks > 0x7fffffffULL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(bwd_rowdot_kernel, dim3((unsigned)rowdot_blocks), dim3(256), 0, stream,
+                     (const uint16_t*)p.out, (const uint16_t*)p.dout, p.lse, p.D, p.L2, p.Lq, p.Hq, n_tb);
   const long long kv_units = (long long)((p.Lk + kKvKeys - 1) / kKvKeys) * p.kv_chunks * p.Hkv * p.n_pairs * p.B;
   const long long q_units = (long long)p.n_tok_tiles * p.q_chunks * p.B * p.Hkv * p.n_hg;
   if (kv_units > 0x7fffffffLL || q_units > 0x7fffffffLL) return hipErrorInvalidConfiguration;
