@@ -596,6 +596,9 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void bwd_dq_kernel(BackwardParams
   f32x16_t dq[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) dq[db] = zero_f32x16();
+  // dr sums carried from one key tile to the next (lanes 32..62), at distance carry_base + lane
+  float carry = 0.f;
+  int carry_base = 0;
 
   auto compute_tile = [&](int kt, int st) {
     const int j0 = kt * 32;
@@ -645,15 +648,24 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void bwd_dq_kernel(BackwardParams
     // order, so only the compiler's order is kept here.
     lds_order();
     const int dbase = off + q0 - j0 - 31;
+    float x = 0.f;
     if (lane < 63) {
       f32x2_t acc = {0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < 32; c += 2) acc += *(const f32x2_t*)(diag + lane * kDiagStride + c);
-      const float x = acc[0] + acc[1];
-      // rows of the table at negative distances hold only invisible pairs: never added
-      if (dbase + lane >= 0 && x != 0.f) unsafeAtomicAdd(dbias_h + min(dbase + lane, p.R - 1), x);
+      x = acc[0] + acc[1];
     }
     lds_order();  // the next tile's table stores come after these reads
+    // Key tiles advance by 32, so the diagonals of rows e <= 30 (tile distance c = e - 31 < 0)
+    // continue as rows e + 32 of the next tile: lanes 0..30 hand their sums to lanes 32..62,
+    // and only rows 31..62, which no later tile reaches, are added to dr.
+    const float tot = x + carry;
+    // rows of the table at negative distances hold only invisible pairs: never added
+    if (lane >= 31 && lane < 63 && dbase + lane >= 0 && tot != 0.f)
+      unsafeAtomicAdd(dbias_h + min(dbase + lane, p.R - 1), tot);
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    carry = lane >= 32 && lane < 63 ? __uint_as_float(sw[0]) : 0.f;  // lane l >= 32: row l - 32's sum
+    carry_base = dbase - 32;                                           // lane l: distance carry_base + l
   };
 
   // ---- key loop: tile t computed from stage t % 3 while tiles t + 1, t + 2 load ----------
@@ -667,6 +679,10 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void bwd_dq_kernel(BackwardParams
     if (t + 2 < n_tiles) issue_tile(kt_begin + t + 2, (t + 2) % kDqStages);
     compute_tile(kt_begin + t, t % kDqStages);
   }
+  // the last computed tile's carried rows (the visible key tiles of a wave are contiguous, so
+  // no tile it skipped lies between two it computed)
+  if (lane >= 32 && lane < 63 && carry_base + lane >= 0 && carry != 0.f)
+    unsafeAtomicAdd(dbias_h + min(carry_base + lane, p.R - 1), carry);
   if (!qvalid) return;
   // accumulator register 4 i + c of block db: dim 32 db + 8 i + 4 hf + c of query q0 + col
   float* dqg = (chunk ? p.dq_part : p.dq) + (row0 + (size_t)col * p.Hq) * kHeadDim;
