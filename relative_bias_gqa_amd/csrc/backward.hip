@@ -631,6 +631,19 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void bwd_dq_kernel(BackwardParams
     float* const dcell = diag + (col - 4 * hf + 4) * kDiagStride + col;
 #pragma unroll
     for (int r = 0; r < 16; ++r) dcell[kDiagStride * (27 - (8 * (r >> 2) + (r & 3)))] = ds[r];
+    // dr: lane e < 63 sums row e of the table (the pairs at distance dbase + e; invisible pairs
+    // hold zero), with its reads free to overlap the dQ products below.  The table is this
+    // wave's own and the LDS serves a wave's requests in order, so only the compiler's order
+    // is kept here.
+    lds_order();
+    float x;
+    {
+      const float* row = diag + min(lane, 62) * kDiagStride;
+      f32x2_t acc = {0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < 32; c += 2) acc += *(const f32x2_t*)(row + c);
+      x = lane < 63 ? acc[0] + acc[1] : 0.f;
+    }
     // dQ^T += K^T dS^T: rows are dims (K read transposed), the lane's column its query
     const uint32_t t1 = base_at(kt_lds, tr1), t2 = base_at(kt_lds, tr2);
 #pragma unroll
@@ -643,19 +656,8 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void bwd_dq_kernel(BackwardParams
         dq[db] = mfma_32x32x16(u32x4_t{a1[0], a1[1], a2[0], a2[1]}, bs, dq[db]);
       }
     }
-    // dr: lane e < 63 sums row e of the table (the pairs at distance dbase + e; invisible pairs
-    // hold zero).  The table is this wave's own and the LDS serves a wave's requests in
-    // order, so only the compiler's order is kept here.
-    lds_order();
+    lds_order();  // the next tile's table stores come after the row reads
     const int dbase = off + q0 - j0 - 31;
-    float x = 0.f;
-    if (lane < 63) {
-      f32x2_t acc = {0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < 32; c += 2) acc += *(const f32x2_t*)(diag + lane * kDiagStride + c);
-      x = acc[0] + acc[1];
-    }
-    lds_order();  // the next tile's table stores come after these reads
     // Key tiles advance by 32, so the diagonals of rows e <= 30 (tile distance c = e - 31 < 0)
     // continue as rows e + 32 of the next tile: lanes 0..30 hand their sums to lanes 32..62,
     // and only rows 31..62, which no later tile reaches, are added to dr.
