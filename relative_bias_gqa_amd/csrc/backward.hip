@@ -617,12 +617,22 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void bwd_dq_kernel(BackwardParams
     // S^T = K Q^T, then dP^T = V dO^T: rows are keys, the lane's column is its query.  The
     // stage base is a multiple of 256 bytes, so (base + lane offset) ^ (32 ks) is the swizzled
     // address of chunk 2 ks + hf; V sits 8 KB after K.
+    // The eight K operands are read ahead of the products (the compiler barrier keeps them
+    // there), and each register takes its V operand once its product has issued; left to
+    // itself the scheduler fed every product through one register, a full LDS latency each.
     const uint32_t ka = base_at(kt_lds, rowA);
     f32x16_t st_acc = zero_f32x16(), dpt = zero_f32x16();
+    u32x4_t op[8];
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) st_acc = mfma_32x32x16(lds_ld16(ka ^ (32u * ks)), qr[ks], st_acc);
+    for (int ks = 0; ks < 8; ++ks) op[ks] = lds_ld16(ka ^ (32u * ks));
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) dpt = mfma_32x32x16(lds_ld16((ka ^ (32u * ks)) + kDqKV), gr[ks], dpt);
+    for (int ks = 0; ks < 8; ++ks) st_acc = mfma_32x32x16(op[ks], qr[ks], st_acc);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) op[ks] = lds_ld16((ka ^ (32u * ks)) + kDqKV);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) dpt = mfma_32x32x16(op[ks], gr[ks], dpt);
     float ds[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r)
