@@ -527,7 +527,7 @@ namespace {
 // key block ([2, ceil(G / 2), B, Lk, Hkv, 128] each), then the second key-tile chunk's dq
 // ([B, Lq, Hq, 128]); each part 256-aligned.
 struct BackwardLayout {
-  size_t l2_off, pk_off, pv_off, dqp_off, total;
+  size_t l2_off, pk_off, pv_off, dqp_off, bias_off, total;
   int n_pairs;
 };
 
@@ -541,7 +541,8 @@ bool backward_layout(int B, int Lq, int Lk, int Hq, int Hkv, BackwardLayout* lay
   lay->pk_off = lay->l2_off + align(rows * sizeof(float));
   lay->pv_off = lay->pk_off + align(2 * (size_t)lay->n_pairs * plane * sizeof(float));
   lay->dqp_off = lay->pv_off + align(2 * (size_t)lay->n_pairs * plane * sizeof(float));
-  lay->total = std::max<size_t>(256, lay->dqp_off + align(rows * 128 * sizeof(float)));
+  lay->bias_off = lay->dqp_off + align(rows * 128 * sizeof(float));
+  lay->total = std::max<size_t>(256, lay->bias_off + align((size_t)Hq * Lk * sizeof(float)));
   return true;
 }
 
@@ -663,6 +664,8 @@ int rattn_prefill_backward(const void* q, const void* k, const void* v, const fl
   p.part_dk = (float*)((char*)workspace + lay.pk_off);
   p.part_dv = (float*)((char*)workspace + lay.pv_off);
   p.dq_part = (float*)((char*)workspace + lay.dqp_off);
+  p.bias_s = (float*)((char*)workspace + lay.bias_off);
+  p.Rs = std::min(R, Lk);
   p.n_pairs = lay.n_pairs;
   {
     rattn::PrefillParams shape;  // the forward's head / token grouping

@@ -37,6 +37,7 @@ namespace {
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr float kRsqrtD = 0.08838834764831845f;  // 1 / sqrt(128)
+constexpr float kSqrtD = 11.313708498984761f;     // sqrt(128)
 constexpr int kDiagStride = 34;            // floats per row of the diagonal table (conflict free)
 
 // 256 bytes of zeros: the source of every K/V row past Lk and query row past Lq.
@@ -53,6 +54,18 @@ __device__ __forceinline__ void lds_order() { asm volatile("" ::: "memory"); }
 
 __global__ __launch_bounds__(256) void bwd_fill_zero_kernel(float* a, size_t n) {
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) a[i] = 0.f;
+}
+
+// dbias = 0, and bias_s[h, i] = sqrt(128) * bias[h, i] for i < Rs: the table in score units
+// that seeds the S accumulators of both passes (the forward pass seeds its own the same way).
+__global__ __launch_bounds__(256) void bwd_prep_kernel(float* dbias, const float* bias, float* bias_s, int R, int Rs,
+                                                       size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+    dbias[i] = 0.f;
+    const size_t h = i / R;
+    const int j = (int)(i - h * R);
+    if (j < Rs) bias_s[h * Rs + j] = bias[i] * kSqrtD;
+  }
 }
 
 // D = sum_d dout[b, t, h, d] * out[b, t, h, d] and L2 = lse[b, t, h] * log2(e) for every row,
@@ -259,7 +272,7 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void bwd_dkdv_kernel(BackwardPara
   // Lq rows further when it is another head
   const float* drow0 = (const float*)uniform_ptr((wave == 0 ? p.D : p.L2) + ((size_t)b * p.Hq + h_slot0) * Lq);
   const uint32_t d_half = __builtin_amdgcn_readfirstlane(h_slot1 != h_slot0 ? (uint32_t)Lq : 0u);
-  const float* bias_h = (const float*)uniform_ptr(p.bias + (size_t)h * p.R);
+  const float* bias_h = (const float*)uniform_ptr(p.bias_s + (size_t)h * p.Rs);
   auto issue_step = [&](int s, int st) {
     const int q0 = (t_lo + s) * 32;
     const uint32_t stage = ring_base + st * kRingStage;
@@ -291,11 +304,12 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void bwd_dkdv_kernel(BackwardPara
         dma4(a, stage + (wave == 0 ? kRingD : kRingL));
       }
     }
-    // this wave's bias slice: entry e = r[h, min(d, R - 1)] at distance d = dbase + e, the
-    // distance of query e - 31 + jj of the tile to key jj of the block; -inf where no visible
-    // pair has distance d
+    // this wave's bias slice in score units: entry e = sqrt(128) r[h, min(d, R - 1)] at
+    // distance d = dbase + e, the distance of query e - 31 + jj of the tile to key jj of the
+    // block; -inf where no visible pair has distance d (entries past the table's Rs hold no
+    // pair's distance: clamped into it)
     const int d = off + q0 - j0w - 31 + (int)lane_now();
-    dma4_bias_or_neginf(bias_h, 4u * (uint32_t)min(d, (int)sgpr_at(p.R - 1)), (uint32_t)d < sgpr_at(Weff),
+    dma4_bias_or_neginf(bias_h, 4u * (uint32_t)min(d, (int)sgpr_at(p.Rs - 1)), (uint32_t)d < sgpr_at(Weff),
                         stage + kRingBias + wave * 256);
   };
 
@@ -336,8 +350,13 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void bwd_dkdv_kernel(BackwardPara
     // query qq = 8 (r >> 2) + 4 hf + (r & 3), whose bias entry is slice entry qq - col + 31.
     // Tile and block bases are multiples of 256 bytes, so (base + lane offset) ^ (32 ks) is the
     // swizzled address of chunk 2 ks + hf; dO sits 16 KB after Q, V 32 KB after K.
+    // S starts from the bias in score units (register r: slice entry qq - col + 31, ascending
+    // in r, so consecutive registers load in pairs straight into the accumulator).
     const uint32_t qa = qt + rowA;
-    f32x16_t sacc = zero_f32x16(), dpacc = zero_f32x16();
+    const uint32_t bsl = stage + kRingBias + wave * 256 + 4u * (uint32_t)(4 * hf - col + 31);
+    f32x16_t sacc, dpacc = zero_f32x16();
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sacc[r] = lds_ldf(bsl + 4u * (8 * (r >> 2) + (r & 3)));
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
       sacc = mfma_32x32x16(lds_ld16(qa ^ (32u * ks)), lds_ld16(xor_at(ka, 32u * ks)), sacc);
@@ -346,17 +365,13 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void bwd_dkdv_kernel(BackwardPara
     for (int ks = 0; ks < 8; ++ks)
       dpacc = mfma_32x32x16(lds_ld16((qa ^ (32u * ks)) + 2 * kTileBytes),
                             lds_ld16(xor_at(ka, 32u * ks) + kKvKeys * 256), dpacc);
-    const uint32_t bsl = stage + kRingBias + wave * 256 + 4u * (uint32_t)(4 * hf - col + 31);
     const uint32_t ll_addr = stage + kRingL + slot * 128 + 16 * hf;
     float pr[16];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const f32x4_t lq4 = __builtin_bit_cast(f32x4_t, lds_ld16(ll_addr + 32 * g));
 #pragma unroll
-      for (int c4 = 0; c4 < 4; ++c4) {
-        const float bias = lds_ldf(bsl + 4u * (8 * g + c4));
-        pr[4 * g + c4] = fast_exp2(fmaf(sacc[4 * g + c4], p.scale_log2, fmaf(bias, kLog2e, -lq4[c4])));
-      }
+      for (int c4 = 0; c4 < 4; ++c4) pr[4 * g + c4] = fast_exp2(fmaf(sacc[4 * g + c4], p.scale_log2, -lq4[c4]));
     }
     const u32x4_t ap0 = pack_p_operand(pr), ap1 = pack_p_operand(pr + 8);
     __builtin_amdgcn_sched_barrier(0);
@@ -575,10 +590,11 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void bwd_dq_kernel(BackwardParams
         dma16(a, dst + i * 1024);
       }
     }
-    // this wave's bias slice: entry e = r[h, min(d, R - 1)] at distance d = dbase + e; -inf
-    // where no visible pair has distance d
-    const int d = off + q0 - j0 - 31 + lane;
-    dma4((uint32_t)d < (uint32_t)Weff ? p.bias + (size_t)h * p.R + min(d, p.R - 1) : &kNegInfF,
+    // this wave's bias slice in score units, reversed: position 63 - e holds entry
+    // e = sqrt(128) r[h, min(d, R - 1)] at distance d = dbase + e; -inf where no visible pair has
+    // distance d (entries past the table's Rs hold no pair's distance: clamped into it)
+    const int d = off + q0 - j0 - 31 + (63 - lane);
+    dma4((uint32_t)d < (uint32_t)Weff ? p.bias_s + (size_t)h * p.Rs + min(d, p.Rs - 1) : &kNegInfF,
          stage + kDqBias + wave * 256);
   };
 
@@ -605,38 +621,38 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void bwd_dq_kernel(BackwardParams
     if (!(nq > 0) || j0 > wj_hi || j0 + 31 < wj_lo) return;
     const uint32_t stage = ring_base + st * kDqStage;  // (wave-uniform)
     const uint32_t kt_lds = stage;
-    // register r of an accumulator holds key j0 + jj, jj = 8 (r >> 2) + 4 hf + (r & 3); its
-    // bias entry is slice entry col - jj + 31.  These reads go out first, their latency hidden
-    // behind the products.
-    // (x_r = 8 (r >> 2) + (r & 3) <= 27: the lane's base is entry col - 4 hf + 4, the entry of
-    // x_r = 27, so every register's offset is a non-negative constant the read instruction holds)
-    const uint32_t bsl = base_at(stage + kDqBias + wave * 256, 4u * (uint32_t)(col - 4 * hf + 4));
-    float bv[16];
+    // S^T starts from the bias in score units.  Register r of an accumulator holds key j0 + jj,
+    // jj = 8 (r >> 2) + 4 hf + (r & 3); its seed is slice entry col - jj + 31, at position
+    // 32 - col + jj = (32 - col + 4 hf) + x_r, x_r = 8 (r >> 2) + (r & 3): ascending in r, so
+    // consecutive registers load in pairs straight into the accumulator.  The seeds go out
+    // first; dP^T runs before S^T, so that their latency is spent on its products.
+    const uint32_t bsl = base_at(stage + kDqBias + wave * 256, 4u * (uint32_t)(32 - col + 4 * hf));
+    f32x16_t st_acc;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) bv[r] = lds_ldf(bsl + 4u * (27 - (8 * (r >> 2) + (r & 3))));
-    // S^T = K Q^T, then dP^T = V dO^T: rows are keys, the lane's column is its query.  The
+    for (int r = 0; r < 16; ++r) st_acc[r] = lds_ldf(bsl + 4u * (8 * (r >> 2) + (r & 3)));
+    // dP^T = V dO^T, then S^T = K Q^T: rows are keys, the lane's column is its query.  The
     // stage base is a multiple of 256 bytes, so (base + lane offset) ^ (32 ks) is the swizzled
-    // address of chunk 2 ks + hf; V sits 8 KB after K.
-    // The eight K operands are read ahead of the products (the compiler barrier keeps them
-    // there), and each register takes its V operand once its product has issued; left to
-    // itself the scheduler fed every product through one register, a full LDS latency each.
+    // address of chunk 2 ks + hf; V sits 8 KB after K.  The eight V operands are read ahead of
+    // their products and each register takes its K operand once its product has issued
+    // (scheduling barriers hold this order; left to itself the scheduler fed every product
+    // through one register, a full LDS latency each).
     const uint32_t ka = base_at(kt_lds, rowA);
-    f32x16_t st_acc = zero_f32x16(), dpt = zero_f32x16();
+    f32x16_t dpt = zero_f32x16();
     u32x4_t op[8];
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) op[ks] = lds_ld16(ka ^ (32u * ks));
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) st_acc = mfma_32x32x16(op[ks], qr[ks], st_acc);
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) op[ks] = lds_ld16((ka ^ (32u * ks)) + kDqKV);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) dpt = mfma_32x32x16(op[ks], gr[ks], dpt);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) op[ks] = lds_ld16(ka ^ (32u * ks));
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) st_acc = mfma_32x32x16(op[ks], qr[ks], st_acc);
     float ds[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r)
-      ds[r] = fast_exp2(fmaf(st_acc[r], p.scale_log2, fmaf(bv[r], kLog2e, -lse2))) * (dpt[r] - dd);
+      ds[r] = fast_exp2(fmaf(st_acc[r], p.scale_log2, -lse2)) * (dpt[r] - dd);
     // table cell (row col - jj + 31, column col): from the cell of x_r = 27, 34 (27 - x_r) further
     float* const dcell = diag + (col - 4 * hf + 4) * kDiagStride + col;
 #pragma unroll
@@ -731,7 +747,11 @@ hipError_t launch_backward(const BackwardParams& p, hipStream_t stream) {
     const size_t blocks = std::min((n + 255) / 256, (size_t)4096);
     hipLaunchKernelGGL(bwd_fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a, n);
   };
-  fill(p.dbias, n_r);
+  if (n_r > 0) {
+    const size_t blocks = std::min((n_r + 255) / 256, (size_t)4096);
+    hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p.dbias, p.bias, p.bias_s, p.R,
+                       p.Rs, n_r);
+  }
   if (p.B <= 0 || p.Lq <= 0 || p.Lk <= 0) {
     fill(p.dk, n_kv);
     fill(p.dv, n_kv);

@@ -29,6 +29,10 @@ struct BackwardParams {
   // query-stationary pass: a token tile's key tiles in q_chunks chunks of q_chunk; the
   // second chunk's dq goes to dq_part (rows of two-chunk tiles only), added by a fix-up
   float* dq_part;     // [B, Lq, Hq, 128] workspace
+  // sqrt(128) * bias[h, i] for i < Rs = min(R, Lk) (the entries any visible pair can reach):
+  // the seed of every S accumulator, as in the forward pass
+  float* bias_s;      // [Hq, Rs] workspace
+  int Rs;
   int q_chunk;        // key tiles per chunk (a tile's when q_chunks == 1)
   int kv_chunks, q_chunks;  // chunks per key block / token tile: 1 or 2 (host's plan)
   // query-stationary pass: a workgroup takes hpw query heads x 32 * tsub queries (hpw * tsub
