@@ -220,10 +220,11 @@ int rattn_kv_sconv_write(const void* k_new, const void* v_new, const float* w_k,
  * Device workspace, in bytes, that rattn_prefill_backward needs: two fp32 per query row
  * (rowsum(dout * out) and lse * log2(e), B * Lq * Hq rows), then, for each of two chunks of
  * a key block's queries and each pair of query heads of a KV head (ceil(G / 2) pairs,
- * G = Hq / Hkv), a partial dK and a partial dV ([B, Lk, Hkv, 128] fp32 each), then a
- * partial dq ([B, Lq, Hq, 128] fp32), then the bias table scaled to score units (Hq * Lk fp32:
- * at most Lk entries per head are reachable), every part rounded up to 256 bytes.  Returns 0
- * for invalid sizes.
+ * G = Hq / Hkv), a partial dK and a partial dV ([B, Lk, Hkv, 128] fp32 each), then two
+ * partial dq per query row and head for token tiles cut in two (2 * B * Hq * (Lq rounded up
+ * to 256) * 128 fp32), then the bias table scaled to score units (Hq * Lk fp32:
+ * at most Lk entries per head are reachable), then B * Hq * ceil(Lq / 32) int counters, every
+ * part rounded up to 256 bytes.  Returns 0 for invalid sizes.
  */
 size_t rattn_prefill_backward_workspace_bytes(int B, int Lq, int Lk, int Hq, int Hkv);
 

@@ -527,7 +527,7 @@ namespace {
 // key block ([2, ceil(G / 2), B, Lk, Hkv, 128] each), then the second key-tile chunk's dq
 // ([B, Lq, Hq, 128]); each part 256-aligned.
 struct BackwardLayout {
-  size_t l2_off, pk_off, pv_off, dqp_off, bias_off, total;
+  size_t l2_off, pk_off, pv_off, dqp_off, bias_off, cnt_off, total;
   int n_pairs;
 };
 
@@ -541,8 +541,13 @@ bool backward_layout(int B, int Lq, int Lk, int Hq, int Hkv, BackwardLayout* lay
   lay->pk_off = lay->l2_off + align(rows * sizeof(float));
   lay->pv_off = lay->pk_off + align(2 * (size_t)lay->n_pairs * plane * sizeof(float));
   lay->dqp_off = lay->pv_off + align(2 * (size_t)lay->n_pairs * plane * sizeof(float));
-  lay->bias_off = lay->dqp_off + align(rows * 128 * sizeof(float));
-  lay->total = std::max<size_t>(256, lay->bias_off + align((size_t)Hq * Lk * sizeof(float)));
+  // the dq pass's split partials: two slots per unit (256 query x head rows of 128 fp32 each);
+  // the units of a chunk cover B * Hq * (Lq rounded up to 256) rows at most
+  const size_t unit_rows = (size_t)B * Hq * (((size_t)Lq + 255) / 256 * 256);
+  lay->bias_off = lay->dqp_off + align(2 * unit_rows * 128 * sizeof(float));
+  lay->cnt_off = lay->bias_off + align((size_t)Hq * Lk * sizeof(float));
+  // counters of the dq pass's split token tiles: at most one per 32 queries and query head
+  lay->total = std::max<size_t>(256, lay->cnt_off + align((size_t)B * Hq * ((Lq + 31) / 32) * sizeof(int)));
   return true;
 }
 
@@ -665,6 +670,7 @@ int rattn_prefill_backward(const void* q, const void* k, const void* v, const fl
   p.part_dv = (float*)((char*)workspace + lay.pv_off);
   p.dq_part = (float*)((char*)workspace + lay.dqp_off);
   p.bias_s = (float*)((char*)workspace + lay.bias_off);
+  p.dq_cnt = (int*)((char*)workspace + lay.cnt_off);
   p.Rs = std::min(R, Lk);
   p.n_pairs = lay.n_pairs;
   {

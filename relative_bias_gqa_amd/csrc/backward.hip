@@ -57,15 +57,18 @@ __global__ __launch_bounds__(256) void bwd_fill_zero_kernel(float* a, size_t n) 
 }
 
 // dbias = 0, and bias_s[h, i] = sqrt(128) * bias[h, i] for i < Rs: the table in score units
-// that seeds the S accumulators of both passes (the forward pass seeds its own the same way).
+// that seeds the S accumulators of both passes (the forward pass seeds its own the same way);
+// the dq pass's n_cnt split counters = 0.
 __global__ __launch_bounds__(256) void bwd_prep_kernel(float* dbias, const float* bias, float* bias_s, int R, int Rs,
-                                                       size_t n) {
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+                                                       size_t n, int* cnt, size_t n_cnt) {
+  const size_t stride = (size_t)gridDim.x * 256;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) {
     dbias[i] = 0.f;
     const size_t h = i / R;
     const int j = (int)(i - h * R);
     if (j < Rs) bias_s[h * Rs + j] = bias[i] * kSqrtD;
   }
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n_cnt; i += stride) cnt[i] = 0;
 }
 
 // D = sum_d dout[b, t, h, d] * out[b, t, h, d] and L2 = lse[b, t, h] * log2(e) for every row,
@@ -490,16 +493,9 @@ constexpr int kDqBias = 2 * kDqKV;                    // bias slices: 64 floats 
 constexpr int kDqStage = kDqBias + kDqWaves * 256;
 constexpr int kDqLoads = 3;                           // DMA loads per wave and tile
 
-// Key tiles that token tile t of the query-stationary pass walks.
-__device__ __forceinline__ int dq_tile_keys(const BackwardParams& p, int t) {
-  const int off = p.Lk - p.Lq;
-  const int Weff = p.window > 0 ? p.window : 0x40000000;
-  const int T0 = t * 32 * p.tsub, T1 = min(p.Lq, T0 + 32 * p.tsub);
-  return (off + T1 - 1) / 32 + 1 - max(0, off + T0 - Weff + 1) / 32;
-}
-
 __global__ __launch_bounds__(64 * kDqWaves, 1) void bwd_dq_kernel(BackwardParams p) {
   __shared__ __attribute__((aligned(1024))) unsigned char ring[kDqStages * kDqStage];
+  __shared__ int merges;  // this workgroup finished second of a split token tile
   // dS of a tile by diagonal: row e = col - jj + 31 (distance dbase + e), column col (the
   // query).  The cells of row e that no pair maps to (columns outside e - 31 .. e) are the
   // same in every tile and never written: zeroed once, they let a row sum take all 32 columns.
@@ -711,30 +707,57 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void bwd_dq_kernel(BackwardParams
   // no tile it skipped lies between two it computed)
   if (lane >= 32 && lane < 63 && carry_base + lane >= 0 && carry != 0.f)
     unsafeAtomicAdd(dbias_h + min(carry_base + lane, p.R - 1), carry);
-  if (!qvalid) return;
   // accumulator register 4 i + c of block db: dim 32 db + 8 i + 4 hf + c of query q0 + col
-  float* dqg = (chunk ? p.dq_part : p.dq) + (row0 + (size_t)col * p.Hq) * kHeadDim;
+  const size_t qoff = (row0 + (size_t)col * p.Hq) * kHeadDim + 4 * hf;
+  if (all_tiles <= p.q_chunk) {  // one chunk: this workgroup's dq is the result
+    if (!qvalid) return;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f32x4_t x;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) x[c] = dq[db][4 * i + c] * kRsqrtD;
+        *(f32x4_t*)(p.dq + qoff + 32 * db + 8 * i) = x;
+      }
+    return;
+  }
+  // Two chunks: each writes its partial into its own slot of the workspace with device-coherent
+  // stores (relaxed agent-scope atomic stores carry the sc1 bit on this target and go to the
+  // coherence point, past this XCD's L2), waits for them and counts; the one that counts
+  // second reads the other's slot the same way and writes dq = part 0 + part 1, the same sum
+  // whichever chunk that is.  Slot layout: element e = 16 db + 4 i + c of lane l of wave w at
+  // (64 w + e) * 64 + l, so each access of a wave covers 256 consecutive bytes.
+  const size_t unit_c = (size_t)(u % (p.n_tok_tiles * per_tile));  // the unit within its chunk
+  float* const slot = p.dq_part + (unit_c * 2 + chunk) * (kDqWaves * 64 * 64) + wave * 64 * 64 + lane;
+#pragma unroll
+  for (int e = 0; e < 64; ++e)
+    __hip_atomic_store(slot + 64 * e, dq[e >> 4][e & 15] * kRsqrtD, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's partial has landed
+  __syncthreads();
+  if (tid == 0) {
+    const int old = __hip_atomic_fetch_add(p.dq_cnt + unit_c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    merges = old == 1;
+  }
+  __syncthreads();
+  if (!merges || !qvalid) return;
+  const float* const other = slot + (chunk ? -1 : 1) * (kDqWaves * 64 * 64);
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       f32x4_t x;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) x[c] = dq[db][4 * i + c] * kRsqrtD;
-      *(f32x4_t*)(dqg + 32 * db + 8 * i + 4 * hf) = x;
+      for (int c = 0; c < 4; ++c) {
+        const float mine = dq[db][4 * i + c] * kRsqrtD;
+        const float theirs =
+            __hip_atomic_load(other + 64 * (16 * db + 4 * i + c), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        x[c] = chunk ? theirs + mine : mine + theirs;
+      }
+      *(f32x4_t*)(p.dq + qoff + 32 * db + 8 * i) = x;
     }
   };
   unit((int)blockIdx.x);
-}
-
-// dq += the second chunk's partial, for the token tiles whose key tiles two workgroups shared;
-// four consecutive floats per thread.
-__global__ __launch_bounds__(256) void bwd_dq_fixup_kernel(BackwardParams p, size_t n4) {
-  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n4) return;
-  const int q = (int)((i / ((size_t)p.Hq * 32)) % (size_t)p.Lq);
-  if (dq_tile_keys(p, q / (32 * p.tsub)) <= p.q_chunk) return;
-  ((f32x4_t*)p.dq)[i] += ((const f32x4_t*)p.dq_part)[i];
 }
 
 }  // namespace
@@ -747,10 +770,11 @@ hipError_t launch_backward(const BackwardParams& p, hipStream_t stream) {
     const size_t blocks = std::min((n + 255) / 256, (size_t)4096);
     hipLaunchKernelGGL(bwd_fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a, n);
   };
-  if (n_r > 0) {
-    const size_t blocks = std::min((n_r + 255) / 256, (size_t)4096);
+  const size_t n_cnt = (size_t)std::max(p.n_tok_tiles, 0) * std::max(p.B, 0) * p.Hkv * p.n_hg;
+  if (n_r > 0 || n_cnt > 0) {
+    const size_t blocks = std::max<size_t>(1, std::min((std::max(n_r, n_cnt) + 255) / 256, (size_t)4096));
     hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p.dbias, p.bias, p.bias_s, p.R,
-                       p.Rs, n_r);
+                       p.Rs, n_r, p.dq_cnt, n_cnt);
   }
   if (p.B <= 0 || p.Lq <= 0 || p.Lk <= 0) {
     fill(p.dk, n_kv);
@@ -769,10 +793,6 @@ hipError_t launch_backward(const BackwardParams& p, hipStream_t stream) {
   const size_t n4 = n_kv / 4;
   hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream, p, n4);
   hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)q_units), dim3(64 * kDqWaves), 0, stream, p);
-  if (p.q_chunks > 1) {
-    const size_t nq4 = (size_t)p.B * p.Lq * p.Hq * kHeadDim / 4;
-    hipLaunchKernelGGL(bwd_dq_fixup_kernel, dim3((unsigned)((nq4 + 255) / 256)), dim3(256), 0, stream, p, nq4);
-  }
   return hipGetLastError();
 }
 

@@ -26,9 +26,11 @@ struct BackwardParams {
   float* part_dv;     // [2, n_pairs, B, Lk, Hkv, 128] workspace: dV of each pair
   int n_pairs;        // ceil(G / 2)
   int kv_chunk;       // steps per chunk (a block's steps when kv_chunks == 1)
-  // query-stationary pass: a token tile's key tiles in q_chunks chunks of q_chunk; the
-  // second chunk's dq goes to dq_part (rows of two-chunk tiles only), added by a fix-up
-  float* dq_part;     // [B, Lq, Hq, 128] workspace
+  // query-stationary pass: a token tile's key tiles in q_chunks chunks of q_chunk; for a
+  // two-chunk tile each chunk's dq goes to its slot of dq_part, and whichever chunk finishes
+  // second adds the other's partial (dq_cnt: one counter per tile and head group)
+  float* dq_part;     // [units, 2, 8 waves, 64, 64] workspace
+  int* dq_cnt;        // [n_tok_tiles * B * Hkv * n_hg] workspace, zeroed by bwd_prep_kernel
   // sqrt(128) * bias[h, i] for i < Rs = min(R, Lk) (the entries any visible pair can reach):
   // the seed of every S accumulator, as in the forward pass
   float* bias_s;      // [Hq, Rs] workspace

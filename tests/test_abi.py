@@ -343,16 +343,19 @@ def test_backward_validation(lib, kw, status, needle):
 
 def test_backward_workspace_formula():
     # D and lse*log2(e) per row; partial dK and dV for 2 chunks x ceil(G/2) pairs, each plane
-    # [B, Lk, Hkv, 128] fp32; the second chunk's dq [B, Lq, Hq, 128] fp32; the scaled bias
-    # table, Hq x Lk fp32
+    # [B, Lk, Hkv, 128] fp32; two partial dq slots per query row and head (Lq rounded up to
+    # 256), 128 fp32 each; the scaled bias table, Hq x Lk fp32; split counters,
+    # B x Hq x ceil(Lq / 32) int
     rows = 8192 * 16 * 4
     plane = 8192 * 2 * 128 * 4
     table = 16 * 8192 * 4
+    counters = 16 * 256 * 4
     assert (rb.rattn_prefill_backward_workspace_bytes(1, 8192, 8192, 16, 2)
-            == 2 * rows + 2 * 2 * 4 * plane + 128 * rows + table)
+            == 2 * rows + 2 * 2 * 4 * plane + 2 * 128 * rows + table + counters)
     # 3 rows: two 256-byte row parts; one pair: 2 chunks x 5 keys x 128 x 4 B = 5120 for dK and
-    # for dV; dq part 3 x 128 x 4 = 1536; table 1 x 5 x 4 = 20 -> 256
-    assert rb.rattn_prefill_backward_workspace_bytes(1, 3, 5, 1, 1) == 256 + 256 + 5120 + 5120 + 1536 + 256
+    # for dV; dq slots 2 x 256 x 128 x 4; table 1 x 5 x 4 = 20 -> 256; one counter -> 256
+    assert (rb.rattn_prefill_backward_workspace_bytes(1, 3, 5, 1, 1)
+            == 256 + 256 + 5120 + 5120 + 2 * 256 * 512 + 256 + 256)
     assert rb.rattn_prefill_backward_workspace_bytes(0, 0, 0, 1, 1) == 256
     assert rb.rattn_prefill_backward_workspace_bytes(-1, 1, 1, 1, 1) == 0
     assert rb.rattn_prefill_backward_workspace_bytes(1, 1, 1, 3, 2) == 0  # Hq not a multiple of Hkv
