@@ -378,18 +378,25 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void bwd_dkdv_kernel(BackwardPara
     }
     const u32x4_t ap0 = pack_p_operand(pr), ap1 = pack_p_operand(pr + 8);
     __builtin_amdgcn_sched_barrier(0);
-    // dV += P^T dO (rows: keys, the lane's P; columns: dims, dO read transposed)
+    // dV += P^T dO (rows: keys, the lane's P; columns: dims, dO read transposed).  All sixteen
+    // transposed reads of a phase go out before its products (S and dP, dead by now, leave the
+    // registers), instead of one product ahead.
     const uint32_t t1 = qt + tr1, t2 = qt + tr2;
+    u32x4_t top[8];
 #pragma unroll
-    for (int qs = 0; qs < 2; ++qs) {
+    for (int qs = 0; qs < 2; ++qs)
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         const uint32_t o1 = (t1 ^ (64u * db)) + 4096u * qs + 2 * kTileBytes;
         const uint32_t o2 = (t2 ^ (64u * db)) + 4096u * qs + 2 * kTileBytes;
         const u32x2_t g1 = lds_tr8(o1), g2 = lds_tr8(o2);
-        dv[db] = mfma_32x32x16(qs ? ap1 : ap0, u32x4_t{g1[0], g1[1], g2[0], g2[1]}, dv[db]);
+        top[4 * qs + db] = u32x4_t{g1[0], g1[1], g2[0], g2[1]};
       }
-    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) dv[db] = mfma_32x32x16(qs ? ap1 : ap0, top[4 * qs + db], dv[db]);
     const uint32_t dl_addr = stage + kRingD + slot * 128 + 16 * hf;
     float ds[16];
 #pragma unroll
@@ -402,14 +409,18 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void bwd_dkdv_kernel(BackwardPara
     __builtin_amdgcn_sched_barrier(0);
     // dK += dS^T Q (Q read transposed)
 #pragma unroll
-    for (int qs = 0; qs < 2; ++qs) {
+    for (int qs = 0; qs < 2; ++qs)
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         const uint32_t o1 = (t1 ^ (64u * db)) + 4096u * qs, o2 = (t2 ^ (64u * db)) + 4096u * qs;
         const u32x2_t x1 = lds_tr8(o1), x2 = lds_tr8(o2);
-        dk[db] = mfma_32x32x16(qs ? as1 : as0, u32x4_t{x1[0], x1[1], x2[0], x2[1]}, dk[db]);
+        top[4 * qs + db] = u32x4_t{x1[0], x1[1], x2[0], x2[1]};
       }
-    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) dk[db] = mfma_32x32x16(qs ? as1 : as0, top[4 * qs + db], dk[db]);
   };
 
   // ---- the query-tile loop: step s computed from stage s & 1 while step s + 1 loads ----
