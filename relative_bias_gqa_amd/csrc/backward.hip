@@ -58,17 +58,20 @@ __global__ __launch_bounds__(256) void bwd_fill_zero_kernel(float* a, size_t n) 
 
 // dbias = 0, and bias_s[h, i] = sqrt(128) * bias[h, i] for i < Rs: the table in score units
 // that seeds the S accumulators of both passes (the forward pass seeds its own the same way);
-// the dq pass's n_cnt split counters = 0.
-__global__ __launch_bounds__(256) void bwd_prep_kernel(float* dbias, const float* bias, float* bias_s, int R, int Rs,
-                                                       size_t n, int* cnt, size_t n_cnt) {
-  const size_t stride = (size_t)gridDim.x * 256;
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) {
-    dbias[i] = 0.f;
-    const size_t h = i / R;
-    const int j = (int)(i - h * R);
-    if (j < Rs) bias_s[h * Rs + j] = bias[i] * kSqrtD;
+// the dq pass's n_cnt split counters = 0.  Elements i0, i0 + stride, ... of each.
+__device__ __forceinline__ void prep_work(const BackwardParams& p, size_t n_r, size_t n_cnt, size_t i0, size_t stride) {
+  for (size_t i = i0; i < n_r; i += stride) {
+    p.dbias[i] = 0.f;
+    const size_t h = i / p.R;
+    const int j = (int)(i - h * p.R);
+    if (j < p.Rs) p.bias_s[h * p.Rs + j] = p.bias[i] * kSqrtD;
   }
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n_cnt; i += stride) cnt[i] = 0;
+  for (size_t i = i0; i < n_cnt; i += stride) p.dq_cnt[i] = 0;
+}
+
+// The same work alone (when there is no query row to run bwd_rowdot_kernel for).
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BackwardParams p, size_t n_r, size_t n_cnt) {
+  prep_work(p, n_r, n_cnt, (size_t)blockIdx.x * 256 + threadIdx.x, (size_t)gridDim.x * 256);
 }
 
 // D = sum_d dout[b, t, h, d] * out[b, t, h, d] and L2 = lse[b, t, h] * log2(e) for every row,
@@ -80,8 +83,14 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(float* dbias, const float
 constexpr int kRowdotPasses = 2;
 constexpr int kRowdotRows = 16 * kRowdotPasses;  // query positions per workgroup: one 128 B line of D
 
-__global__ __launch_bounds__(256) void bwd_rowdot_kernel(const uint16_t* out, const uint16_t* dout, const float* lse,
-                                                         float* D, float* L2, int Lq, int Hq, int n_tb) {
+// The launch also does prep_work over its whole grid (one launch fewer).
+__global__ __launch_bounds__(256) void bwd_rowdot_kernel(BackwardParams p, int n_tb, size_t n_r, size_t n_cnt) {
+  const uint16_t* const out = (const uint16_t*)p.out;
+  const uint16_t* const dout = (const uint16_t*)p.dout;
+  const float* const lse = p.lse;
+  float* const D = p.D;
+  float* const L2 = p.L2;
+  const int Lq = p.Lq, Hq = p.Hq;
   const int c = threadIdx.x & 15;
   const int tb = blockIdx.x % n_tb;
   const size_t bh = blockIdx.x / n_tb;
@@ -116,6 +125,7 @@ __global__ __launch_bounds__(256) void bwd_rowdot_kernel(const uint16_t* out, co
       L2[dst] = lse[(b * Lq + t) * Hq + h] * kLog2e;
     }
   }
+  prep_work(p, n_r, n_cnt, (size_t)blockIdx.x * 256 + threadIdx.x, (size_t)gridDim.x * 256);
 }
 
 // ---- key-stationary pass (dK, dV) -----------------------------------------------------
@@ -782,12 +792,11 @@ hipError_t launch_backward(const BackwardParams& p, hipStream_t stream) {
     hipLaunchKernelGGL(bwd_fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a, n);
   };
   const size_t n_cnt = (size_t)std::max(p.n_tok_tiles, 0) * std::max(p.B, 0) * p.Hkv * p.n_hg;
-  if (n_r > 0 || n_cnt > 0) {
-    const size_t blocks = std::max<size_t>(1, std::min((std::max(n_r, n_cnt) + 255) / 256, (size_t)4096));
-    hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p.dbias, p.bias, p.bias_s, p.R,
-                       p.Rs, n_r, p.dq_cnt, n_cnt);
-  }
   if (p.B <= 0 || p.Lq <= 0 || p.Lk <= 0) {
+    if (n_r > 0 || n_cnt > 0) {
+      const size_t blocks = std::max<size_t>(1, std::min((std::max(n_r, n_cnt) + 255) / 256, (size_t)4096));
+      hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p, n_r, n_cnt);
+    }
     fill(p.dk, n_kv);
     fill(p.dv, n_kv);
     return hipGetLastError();
@@ -795,8 +804,7 @@ hipError_t launch_backward(const BackwardParams& p, hipStream_t stream) {
   const int n_tb = (p.Lq + kRowdotRows - 1) / kRowdotRows;
   const size_t rowdot_blocks = (size_t)p.B * p.Hq * n_tb;
   if (rowdot_blocks > 0x7fffffffULL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(bwd_rowdot_kernel, dim3((unsigned)rowdot_blocks), dim3(256), 0, stream,
-                     (const uint16_t*)p.out, (const uint16_t*)p.dout, p.lse, p.D, p.L2, p.Lq, p.Hq, n_tb);
+  hipLaunchKernelGGL(bwd_rowdot_kernel, dim3((unsigned)rowdot_blocks), dim3(256), 0, stream, p, n_tb, n_r, n_cnt);
   const long long kv_units = (long long)((p.Lk + kKvKeys - 1) / kKvKeys) * p.kv_chunks * p.Hkv * p.n_pairs * p.B;
   const long long q_units = (long long)p.n_tok_tiles * p.q_chunks * p.B * p.Hkv * p.n_hg;
   if (kv_units > 0x7fffffffLL || q_units > 0x7fffffffLL) return hipErrorInvalidConfiguration;
