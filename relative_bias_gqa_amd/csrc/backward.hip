@@ -475,10 +475,8 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void bwd_dkdv_kernel(BackwardPara
 
 // dk = (sum over head pairs of the partial dK) / sqrt(128), dv = sum of the partial dV, in
 // pair order, a pair's second chunk (blocks walked in two) right after its first; four
-// consecutive floats per thread.
-__global__ __launch_bounds__(256) void bwd_reduce_kernel(BackwardParams p, size_t n4) {
-  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n4) return;
+// consecutive floats per call (run by the tail workgroups of the dq grid).
+__device__ __forceinline__ void reduce_element(const BackwardParams& p, size_t i) {
   const size_t plane = (size_t)p.B * p.Lk * p.Hkv * kHeadDim;
   const int j = (int)((i / ((size_t)p.Hkv * 32)) % (size_t)p.Lk);
   const bool two = kv_block_steps(p, j / kKvKeys) > p.kv_chunk;
@@ -512,11 +510,23 @@ constexpr int kDqStages = 3;
 constexpr int kDqKV = 32 * 256;                       // a K (or V) tile: 32 keys x 256 B
 constexpr int kDqBias = 2 * kDqKV;                    // bias slices: 64 floats per wave
 constexpr int kDqStage = kDqBias + kDqWaves * 256;
-constexpr int kDqLoads = 3;                           // DMA loads per wave and tile
+constexpr int kDqLoads = 3;
+// workgroups appended to the dq grid that sum the dK/dV partials (1024, 2048 and 4096 ran
+// the same; 256 left part of the tail idle)
+constexpr int kDqReduceWorkgroups = 1024;                           // DMA loads per wave and tile
 
-__global__ __launch_bounds__(64 * kDqWaves, 1) void bwd_dq_kernel(BackwardParams p) {
+__global__ __launch_bounds__(64 * kDqWaves, 1) void bwd_dq_kernel(BackwardParams p, int q_units, int n_red, size_t n4) {
   __shared__ __attribute__((aligned(1024))) unsigned char ring[kDqStages * kDqStage];
   __shared__ int merges;  // this workgroup finished second of a split token tile
+  // The grid's last n_red workgroups sum the dK/dV partials (the dK/dV pass has finished):
+  // dispatched after every dq unit, they run on compute units that the dq units' tail leaves
+  // idle.
+  if ((int)blockIdx.x >= q_units) {
+    const size_t stride = (size_t)n_red * 64 * kDqWaves;
+    for (size_t i = (size_t)(blockIdx.x - q_units) * 64 * kDqWaves + threadIdx.x; i < n4; i += stride)
+      reduce_element(p, i);
+    return;
+  }
   // dS of a tile by diagonal: row e = col - jj + 31 (distance dbase + e), column col (the
   // query).  The cells of row e that no pair maps to (columns outside e - 31 .. e) are the
   // same in every tile and never written: zeroed once, they let a row sum take all 32 columns.
@@ -807,11 +817,12 @@ hipError_t launch_backward(const BackwardParams& p, hipStream_t stream) {
   hipLaunchKernelGGL(bwd_rowdot_kernel, dim3((unsigned)rowdot_blocks), dim3(256), 0, stream, p, n_tb, n_r, n_cnt);
   const long long kv_units = (long long)((p.Lk + kKvKeys - 1) / kKvKeys) * p.kv_chunks * p.Hkv * p.n_pairs * p.B;
   const long long q_units = (long long)p.n_tok_tiles * p.q_chunks * p.B * p.Hkv * p.n_hg;
-  if (kv_units > 0x7fffffffLL || q_units > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  if (kv_units > 0x7fffffffLL || q_units + kDqReduceWorkgroups > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)kv_units), dim3(64 * kKvWaves), 0, stream, p);
   const size_t n4 = n_kv / 4;
-  hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream, p, n4);
-  hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)q_units), dim3(64 * kDqWaves), 0, stream, p);
+  const int n_red = (int)std::min<size_t>((n4 + 64 * kDqWaves - 1) / (64 * kDqWaves), (size_t)kDqReduceWorkgroups);
+  hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)(q_units + n_red)), dim3(64 * kDqWaves), 0, stream, p,
+                     (int)q_units, n_red, n4);
   return hipGetLastError();
 }
 
