@@ -210,3 +210,40 @@ def test_backward_empty_chunk_zeroes_gradients():
     torch.cuda.synchronize()
     assert rc == rb.RATTN_OK, rb.rattn_last_error()
     assert int((dk != 0).sum()) == 0 and int((dv != 0).sum()) == 0 and int((dr != 0).sum()) == 0
+
+
+def test_backward_deterministic_with_reused_workspace():
+    """dq, dk and dv are sums in a fixed order whichever workgroup of a token tile or key block
+    cut in two finishes last.  The 8K-token window-4096 workload (whose tiles and key blocks
+    are cut in two) runs once on a fresh zeroed workspace and three times on one workspace
+    whose bytes start as 0xFF (split counters -1, partial slots NaN: every call must reset
+    what it counts on); every call gives the first one's dq, dk and dv bit for bit, and dbias
+    (fp32 atomic adds in any order) within rounding of it."""
+    print("case backward determinism, reused poisoned workspace, swa_prefill_8k_bwd", flush=True)
+    case = synth.swa_prefill_8k_bwd()
+    f = case.fwd
+    q, k, v, r = dev(f.q), dev(f.k), dev(f.v), dev(f.bias)
+    out, lse = rb.prefill(q, k, v, r, f.window)
+    dout = dev(case.dout)
+    B, Lq, Hq = q.shape[0], q.shape[1], q.shape[2]
+    Lk, Hkv = k.shape[1], k.shape[2]
+    n = rb.rattn_prefill_backward_workspace_bytes(B, Lq, Lk, Hq, Hkv)
+
+    def call(ws):
+        dq = torch.full(q.shape, float("nan"), dtype=torch.float32, device="cuda")
+        dk = torch.full(k.shape, float("nan"), dtype=torch.float32, device="cuda")
+        dv = torch.full(v.shape, float("nan"), dtype=torch.float32, device="cuda")
+        dbias = torch.full(r.shape, float("nan"), dtype=torch.float32, device="cuda")
+        rb.rattn_prefill_backward(q, k, v, r, out, dout, lse, dq, dk, dv, dbias, f.window, ws)
+        torch.cuda.synchronize()
+        return host(dq), host(dk), host(dv), host(dbias)
+
+    first = call(torch.zeros(n, dtype=torch.uint8, device="cuda"))
+    for name, g in zip(("dq", "dk", "dv", "dbias"), first):
+        assert np.isfinite(g).all(), f"{name}: non-finite on a fresh workspace"
+    ws = torch.full((n,), 0xFF, dtype=torch.uint8, device="cuda")
+    for i in range(3):
+        got = call(ws)
+        for name, a, b in zip(("dq", "dk", "dv"), first, got):
+            assert np.array_equal(a, b), f"call {i + 1}: {name} differs from the first call"
+        assert np.allclose(got[3], first[3], rtol=1e-5, atol=1e-6), f"call {i + 1}: dbias beyond rounding"
