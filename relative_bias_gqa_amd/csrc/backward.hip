@@ -10,20 +10,24 @@
 // dK and dV summed over the query heads of a KV head.  P is recomputed from the forward's
 // log-sum-exp, never stored.
 //
-// Passes on the caller's stream:
-//   1. D = rowsum(dout * out) and lse * log2(e) per query row (fp32, head-major);
+// Three launches on the caller's stream:
+//   1. D = rowsum(dout * out) and lse * log2(e) per query row (fp32, head-major), plus the
+//      preparation: dr zeroed, the bias table scaled to score units (sqrt(128) r, the seed of
+//      every S accumulator, as in the forward pass), the split counters zeroed;
 //   2. key-stationary dK, dV: a workgroup owns 128 keys of a KV head and a pair of its query
 //      heads (8 waves = 4 blocks of 32 keys x 2 heads); K and V stay in LDS, the query
 //      tiles that see them stream in by direct-to-LDS DMA; S = Q K^T and dP = dO V^T come
 //      out with one key per lane, the A-operand layout of dV += P^T dO and dK += dS^T Q, so P
 //      and dS feed those MFMAs from registers (dO and Q read transposed from LDS); each pair
-//      writes a partial dK, dV and a reduce kernel sums the pairs in order (deterministic);
+//      writes a partial dK, dV, summed in pair order by the last workgroups of launch 3
+//      (deterministic);
 //   3. query-stationary dQ and dr: the forward's decomposition (8 waves, one query head x 32
 //      queries each, Q^T and dO^T resident in registers), K and V streamed through an LDS
 //      ring; S^T and dP^T come out with one query per lane, the B-operand layout of
-//      dQ^T += K^T dS^T, so dQ stays in registers and is stored once; dS is also summed per
-//      distance through a skewed table in LDS and the 63 row sums added into dr (fp32
-//      atomics: dr's last bits may change from run to run).
+//      dQ^T += K^T dS^T, so dQ stays in registers and is stored once (a token tile whose key
+//      tiles two workgroups share is merged by the one that finishes second); dS is also
+//      summed per distance through a skewed table in LDS and added into dr (fp32 atomics:
+//      dr's last bits may change from run to run).
 // All products are v_mfma_f32_32x32x16_bf16 with fp32 accumulation; P and dS are rounded to
 // bf16 as MFMA operands.
 #include <algorithm>
@@ -134,11 +138,11 @@ __global__ __launch_bounds__(256) void bwd_rowdot_kernel(BackwardParams p, int n
 // in LDS for the whole pass; the query tiles that see them stream through a two-stage LDS
 // ring, one step ahead, straight from global memory (global_load_lds_dwordx4): per step
 // the Q and dO tiles (32 queries) of both heads, their D and lse*log2(e), and each wave's
-// 63-entry bias slice.  Per step a wave computes S = Q K^T and dP = dO V^T with one key per
+// 63-entry slice of the bias table in score units (the seeds of its S).  Per step a wave computes S = Q K^T and dP = dO V^T with one key per
 // lane (the accumulator column), then P and dS, then dV += P^T dO and dK += dS^T Q (P and dS
 // as A operands straight from registers, dO and Q read transposed from LDS).  At the end the
 // two slots of a key block add up through LDS and slot 0 writes the pair's partial dK, dV;
-// a reduce kernel sums the pairs in pair order (no atomics: the result is deterministic).
+// the pairs are summed in pair order afterwards (no atomics: the result is deterministic).
 //
 // Tiles in LDS have 256-byte rows; 16-byte chunk c of row r is stored at chunk c ^ swz(r),
 // swz(r) = 4 (r & 3) + ((r >> 2) & 3): the sixteen rows a 16-lane group reads row-wise get
@@ -497,14 +501,15 @@ __device__ __forceinline__ void reduce_element(const BackwardParams& p, size_t i
 // The forward's decomposition: a workgroup of 8 waves owns one KV head, hpw of its query heads
 // and 32 * tsub queries (hpw * tsub = 8); each wave owns one query head x 32 queries, its Q^T
 // and dO^T operands resident in registers, and walks the 32-key tiles its workgroup sees.
-// K, V and each wave's 63-entry bias slice of a tile are loaded straight into LDS
-// (global_load_lds) through a ring of three stages, two tiles ahead, and serve every wave
-// (GQA packing).  Per tile a wave computes S^T = K Q^T and dP^T = V dO^T with one query per
-// lane (the accumulator column), P and dS, dQ^T += K^T dS^T (K read transposed; dQ stays in
-// registers and is stored once), and sums dS along the tile's 63 diagonals through a skewed
-// table in LDS (row = diagonal, column = the lane's query, 34 floats per row) into dr, one
-// fp32 atomic per diagonal.  K rows are read both row-wise and transposed: the tile uses the
-// swizzle of the key-stationary pass.
+// K, V and each wave's 64-entry slice of the bias table in score units are loaded straight
+// into LDS (global_load_lds) through a ring of three stages, two tiles ahead, and serve every
+// wave (GQA packing).  Per tile a wave computes dP^T = V dO^T and S^T = K Q^T (seeded with the
+// bias) with one query per lane (the accumulator column), P and dS, dQ^T += K^T dS^T (K read
+// transposed; dQ stays in registers and is stored once), and sums dS along the tile's 63
+// diagonals through a skewed table in LDS (row = diagonal, column = the lane's query, 34 floats
+// per row) into dr: a diagonal that continues into the next key tile carries its sum there,
+// and each finished diagonal is one fp32 atomic add.  K rows are read both row-wise and
+// transposed: the tile uses the swizzle of the key-stationary pass.
 constexpr int kDqWaves = 8;
 constexpr int kDqStages = 3;
 constexpr int kDqKV = 32 * 256;                       // a K (or V) tile: 32 keys x 256 B
@@ -538,9 +543,9 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void bwd_dq_kernel(BackwardParams
   float* diag = diag_w[wave];
   for (int i = lane; i < 63 * kDiagStride; i += 64) diag[i] = 0.f;  // this wave's own table
   // One workgroup per unit: a token tile's key tiles, for one head group and KV head, cut into
-  // q_chunks (1 or 2) chunks of q_chunk; chunk 0 writes dq, chunk 1 a partial that the fix-up
-  // kernel adds.  Launch order: chunk, then token tile (heaviest, last, first), then the head
-  // groups and KV heads (see the key-stationary pass for why).
+  // q_chunks (1 or 2) chunks of q_chunk; a tile cut in two is merged by whichever of its chunks
+  // finishes second (at the end of the unit).  Launch order: chunk, then token tile (heaviest,
+  // last, first), then the head groups and KV heads (see the key-stationary pass for why).
   const int per_tile = p.B * p.Hkv * p.n_hg;
   auto unit = [&](const int u) {
   const int chunk = __builtin_amdgcn_readfirstlane(u / (p.n_tok_tiles * per_tile));
