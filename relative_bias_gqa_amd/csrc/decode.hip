@@ -13,9 +13,10 @@
 // the n_q tokens x gs query heads that share the KV head (GQA packing: each K/V byte is
 // read from HBM once for all of them).  A segment's visible keys are cut into 64-token
 // units; the units of all segments, in order, form one stream that is divided among P
-// workgroups (one per CU) in contiguous runs of equal cost, a unit that needs per-key bias
-// entries weighing 6 against 5 for one whose keys all take the clamp entry, so every CU
-// finishes at about the same time whatever the context lengths.  A workgroup walks its run
+// workgroups (one per CU) in contiguous runs, each of its workgroup's share of the cost (a
+// unit that needs per-key bias entries weighing 6 against 5 for one whose keys all take the
+// clamp entry; with four waves, a share of 9 parts on an odd XCD against 10 on an even one),
+// so every CU finishes at about the same time whatever the context lengths.  A workgroup walks its run
 // in order and writes one normalised partial output and log2-sum-exp per segment it touches
 // (slot = workgroup + segment); the merge kernel combines the pieces of each segment.
 //
@@ -145,8 +146,8 @@ __device__ __forceinline__ void cursor_next(const DecodeParams& p, Cursor& c) {
 // Units do not cost the same: a unit whose keys are all at distance >= R - 1 from every
 // query of its sequence adds the single clamp entry r[h, R - 1], any other one stages a
 // slice of r per head and adds it element by element, about 1.2 times the time.  With C(k)
-// the cost of the units before unit k and C their total, unit k goes to workgroup
-// floor(C(k) P / C): each workgroup gets a contiguous run of units of equal cost.
+// the cost of the units before unit k and C their total, each workgroup gets a contiguous run
+// of units whose cost is its share of C (shares below).
 constexpr int kCostSat = 5;
 constexpr int kCostUnsat = 6;
 
@@ -163,10 +164,39 @@ __device__ __forceinline__ long long seg_cost(int nch, int nsat) {
   return (long long)nsat * kCostSat + (long long)(nch - nsat) * kCostUnsat;
 }
 
-// Workgroups that take part: at most one per cost kCostUnsat, so that every workgroup's
-// cost range (C / P wide) holds the start of some unit and no workgroup is left empty.
+// Shares by XCD.  Workgroup w runs on XCD w % 8.  With four waves (segments of up to 64 rows:
+// the kernel waits on its K/V loads) workgroups on odd XCDs took ~10 % longer for the same
+// units (per-workgroup timelines), so there a share is 10 parts on an even XCD and 9 on an
+// odd one; with eight waves (more rows: compute and loads overlap) the XCDs ran alike and
+// every share is one part.  K(w) = the parts of the workgroups before w.
+struct Caps {
+  int even, odd;
+};
+__device__ __forceinline__ Caps share_caps(const DecodeParams& p) { return p.NW == 4 ? Caps{10, 9} : Caps{1, 1}; }
+__device__ __forceinline__ long long cap_prefix(long long w, Caps c) {
+  const int j = (int)(w & 7);
+  return (w >> 3) * (4LL * (c.even + c.odd)) + (long long)((j + 1) >> 1) * c.even + (long long)(j >> 1) * c.odd;
+}
+// the last workgroup w with cap_prefix(w) <= x
+__device__ __forceinline__ long long cap_owner(long long x, Caps c) {
+  const long long c8 = 4LL * (c.even + c.odd);
+  const long long a = x / c8;
+  const long long r = x - a * c8;
+  int j = 0;
+#pragma unroll
+  for (int i = 1; i < 8; ++i) j += (long long)((i + 1) >> 1) * c.even + (long long)(i >> 1) * c.odd <= r ? 1 : 0;
+  return 8 * a + j;
+}
+
+// Workgroups that take part: few enough that every workgroup's cost range (at least
+// C min(part) / (P max(part)) wide) holds the start of some unit, so that no workgroup is left
+// empty: at most one per cost kCostUnsat (scaled by the largest to the smallest share, plus
+// one for rounding, when they differ).
 __device__ __forceinline__ int split_count(const DecodeParams& p, long long ctot) {
-  return (int)max(1LL, min((long long)p.P, ctot / kCostUnsat));
+  const Caps c = share_caps(p);
+  const int lo = min(c.even, c.odd), hi = max(c.even, c.odd);
+  const long long per = lo == hi ? kCostUnsat : (kCostUnsat * hi + lo - 1) / lo + 1;
+  return (int)max(1LL, min((long long)p.P, ctot / per));
 }
 
 struct SplitRange {
@@ -256,8 +286,10 @@ __device__ SplitRange split_range(const DecodeParams& p, unsigned char* lds) {
     return pre_u[lo] * p.KH + kh * si.nch + k;
   };
   if (w < sr.P) {
-    const int u0 = first_unit(((long long)w * ctot + sr.P - 1) / sr.P);
-    sr.n_units = first_unit(((long long)(w + 1) * ctot + sr.P - 1) / sr.P) - u0;
+    const Caps caps = share_caps(p);
+    const long long ktot = cap_prefix(sr.P, caps);
+    const int u0 = first_unit((cap_prefix(w, caps) * ctot + ktot - 1) / ktot);
+    sr.n_units = first_unit((cap_prefix(w + 1, caps) * ctot + ktot - 1) / ktot) - u0;
     sr.c0 = cursor_at(p, pre_u, u0);
   }
   __syncthreads();  // every wave is done with the scratch before any load reaches it
@@ -685,8 +717,10 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(DecodeParams p) 
   const long long sc = seg_cost(sb.nch, nsat);
   const long long c_first = before * p.KH + kh * sc;
   const long long c_last = c_first + sc - (nsat == sb.nch ? kCostSat : kCostUnsat);
-  const int w_first = (int)(c_first * P / ctot);
-  const int w_last = (int)(c_last * P / ctot);
+  const Caps caps = share_caps(p);
+  const long long ktot = cap_prefix(P, caps);
+  const int w_first = (int)min(cap_owner(c_first * ktot / ctot, caps), P - 1);
+  const int w_last = (int)min(cap_owner(c_last * ktot / ctot, caps), P - 1);
   // piece i = (workgroup w_first + i / KS, key half i % KS)
   const int n_pieces = (w_last - w_first + 1) * p.KS;
   auto slot_row = [&](int i) {
