@@ -182,7 +182,15 @@ static void backward_cases() {
     CHECK(inside(p.D, rows * 4, ws, need) && inside(p.L2, rows * 4, ws, need));
     CHECK(inside(p.part_dk, 2 * p.n_pairs * plane * 4, ws, need));
     CHECK(inside(p.part_dv, 2 * p.n_pairs * plane * 4, ws, need));
-    CHECK(inside(p.dq_part, rows * 128 * 4, ws, need));
+    // the dq pass's units (a token tile x head group x KV head x sequence): two partial slots of
+    // 8 waves x 64 x 64 fp32 each, and one split counter each
+    const size_t units = (size_t)p.n_tok_tiles * c.B * c.Hkv * p.n_hg;
+    CHECK(p.hpw * p.tsub == 8 && p.n_hg * p.hpw == c.Hq / c.Hkv);
+    CHECK(inside(p.dq_part, units * 2 * 8 * 64 * 64 * 4, ws, need));
+    CHECK(inside(p.dq_cnt, units * 4, ws, need));
+    // the bias table in score units: Rs = min(R, Lk) entries per head
+    CHECK(p.Rs == (c.R < c.Lk ? c.R : c.Lk));
+    CHECK(inside(p.bias_s, (size_t)c.Hq * p.Rs * 4, ws, need));
     CHECK((p.kv_chunks == 1 || p.kv_chunks == 2) && (p.q_chunks == 1 || p.q_chunks == 2));
     long long most = 1;
     for (int blk = 0; blk < (c.Lk + 127) / 128; ++blk) {
