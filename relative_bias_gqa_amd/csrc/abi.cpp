@@ -584,32 +584,73 @@ struct ChunkPlan {
   int chunks, chunk;
 };
 
-// Segments with the given walks (in launch order), each repeated `inner` times (head groups,
-// KV heads, sequences), cut into one or two chunks, chunk-major: the plan that finishes first.
-ChunkPlan plan_chunks(const std::vector<long long>& walk, long long inner) {
+// Units of segments with the given walks (in launch order), each repeated `inner` times (head
+// groups, KV heads, sequences), cut into `chunks` chunks, chunk-major: a unit weighs its steps
+// plus the steps it spends on loads before its first one, times `cost`.
+std::vector<double> chunk_units(const std::vector<long long>& walk, long long inner, int chunks, double cost) {
   long long most = 1;
   for (long long x : walk) most = std::max(most, x);
-  ChunkPlan best{1, (int)std::min<long long>(most, 0x7fffffff)};
-  if (walk.empty() || inner <= 0 || (double)walk.size() * inner > 4e6) return best;
-  const double overhead = 3.0;  // steps a unit spends on loads before its first step
+  const long long chunk = (most + chunks - 1) / chunks;
+  const double overhead = 3.0;
+  std::vector<double> w;
+  w.reserve(walk.size() * chunks * inner);
+  for (int c = 0; c < chunks; ++c)
+    for (long long x : walk) {
+      const long long steps = std::max(0LL, std::min(chunk, x - c * chunk));
+      const double t = steps > 0 ? (double)steps + overhead : (c == 0 ? overhead : 0.1);
+      for (long long g = 0; g < inner; ++g) w.push_back(t * cost);
+    }
+  return w;
+}
+
+ChunkPlan chunk_plan(const std::vector<long long>& walk, int chunks) {
+  long long most = 1;
+  for (long long x : walk) most = std::max(most, x);
+  return ChunkPlan{chunks, (int)std::min<long long>((most + chunks - 1) / chunks, 0x7fffffff)};
+}
+
+// One or two chunks per segment, whichever plan the dispatch model finishes sooner.
+ChunkPlan plan_chunks(const std::vector<long long>& walk, long long inner) {
+  if (walk.empty() || inner <= 0 || (double)walk.size() * inner > 4e6) return chunk_plan(walk, 1);
+  int best = 1;
   double best_t = 0.0;
   for (int chunks = 1; chunks <= 2; ++chunks) {
-    const long long chunk = (most + chunks - 1) / chunks;
-    std::vector<double> w;
-    w.reserve(walk.size() * chunks * inner);
-    for (int c = 0; c < chunks; ++c)
-      for (long long x : walk) {
-        const long long steps = std::max(0LL, std::min(chunk, x - c * chunk));
-        const double t = steps > 0 ? (double)steps + overhead : (c == 0 ? overhead : 0.1);
-        for (long long g = 0; g < inner; ++g) w.push_back(t);
-      }
-    const double t = dispatch_makespan(w, compute_units());
+    const double t = dispatch_makespan(chunk_units(walk, inner, chunks, 1.0), compute_units());
     if (chunks == 1 || t < best_t) {
       best_t = t;
-      best = ChunkPlan{chunks, (int)chunk};
+      best = chunks;
     }
   }
-  return best;
+  return chunk_plan(walk, best);
+}
+
+// The same choice for two launches that run side by side (the backward's key-stationary units
+// `a` and query-stationary units `b`), their workgroups handed out alternately; a step of `a`
+// costs `cost_a` steps of `b`.
+void plan_chunks_joint(const std::vector<long long>& wa, long long inner_a, double cost_a,
+                       const std::vector<long long>& wb, long long inner_b, ChunkPlan* pa, ChunkPlan* pb) {
+  *pa = chunk_plan(wa, 1);
+  *pb = chunk_plan(wb, 1);
+  if (wa.empty() || wb.empty() || inner_a <= 0 || inner_b <= 0 ||
+      (double)wa.size() * inner_a + (double)wb.size() * inner_b > 4e6)
+    return;
+  double best_t = 0.0;
+  for (int ca = 1; ca <= 2; ++ca)
+    for (int cb = 1; cb <= 2; ++cb) {
+      const std::vector<double> a = chunk_units(wa, inner_a, ca, cost_a), b = chunk_units(wb, inner_b, cb, 1.0);
+      std::vector<double> w;
+      w.reserve(a.size() + b.size());
+      for (size_t i = 0; i < std::max(a.size(), b.size()); ++i) {
+        if (i < a.size()) w.push_back(a[i]);
+        if (i < b.size()) w.push_back(b[i]);
+      }
+      const double t = dispatch_makespan(w, compute_units());
+      if ((ca == 1 && cb == 1) || t < best_t) {
+        best_t = t;
+        *pa = chunk_plan(wa, ca);
+        *pb = chunk_plan(wb, cb);
+      }
+    }
 }
 
 long long bwd_dq_tile_keys(int Lq, int Lk, int window, int tsub, int t) {
@@ -681,15 +722,26 @@ int rattn_prefill_backward(const void* q, const void* k, const void* v, const fl
     p.n_hg = shape.n_hg;
     p.n_tok_tiles = shape.n_tok_tiles;
   }
+  hipStream_t side = nullptr;
+  hipError_t e = rattn::backward_side_stream((hipStream_t)stream, &side);
+  if (e != hipSuccess)
+    return fail(RATTN_ERR_HIP, "rattn_prefill_backward: second stream: %s", hipGetErrorString(e));
   {
     // walk of every key block / token tile, then one or two chunks each, whichever plan the
-    // dispatch model finishes sooner
+    // dispatch model finishes sooner: for the two passes together when they run side by side
+    // (a key-stationary step and a query-stationary one both cover 8192 query-key pairs; the
+    // first takes about 1.1 times as long), else for each alone
     const int n_blk = (Lk + 127) / 128;
     std::vector<long long> kw(n_blk), qw(p.n_tok_tiles);
     for (int blk = 0; blk < n_blk; ++blk) kw[blk] = bwd_kv_block_steps(Lq, Lk, window, blk);
     for (int t = 0; t < p.n_tok_tiles; ++t) qw[p.n_tok_tiles - 1 - t] = bwd_dq_tile_keys(Lq, Lk, window, p.tsub, t);
-    const ChunkPlan kv = plan_chunks(kw, (long long)B * Hkv * lay.n_pairs);
-    const ChunkPlan qp = plan_chunks(qw, (long long)B * Hkv * p.n_hg);
+    ChunkPlan kv, qp;
+    if (side != nullptr) {
+      plan_chunks_joint(kw, (long long)B * Hkv * lay.n_pairs, 1.1, qw, (long long)B * Hkv * p.n_hg, &kv, &qp);
+    } else {
+      kv = plan_chunks(kw, (long long)B * Hkv * lay.n_pairs);
+      qp = plan_chunks(qw, (long long)B * Hkv * p.n_hg);
+    }
     p.kv_chunks = kv.chunks;
     p.kv_chunk = kv.chunk;
     p.q_chunks = qp.chunks;
@@ -704,7 +756,7 @@ int rattn_prefill_backward(const void* q, const void* k, const void* v, const fl
   p.R = R;
   p.window = window;
   p.scale_log2 = kScaleLog2;
-  hipError_t e = rattn::launch_backward(p, (hipStream_t)stream);
+  e = rattn::launch_backward(p, (hipStream_t)stream, side);
   if (e != hipSuccess) return fail(RATTN_ERR_HIP, "rattn_prefill_backward: launch failed: %s", hipGetErrorString(e));
   return ok();
 }

@@ -31,6 +31,7 @@
 // All products are v_mfma_f32_32x32x16_bf16 with fp32 accumulation; P and dS are rounded to
 // bf16 as MFMA operands.
 #include <algorithm>
+#include <mutex>
 
 #include "backward.hpp"
 #include "device_common.hpp"
@@ -497,6 +498,11 @@ __device__ __forceinline__ void reduce_element(const BackwardParams& p, size_t i
   ((f32x4_t*)p.dv)[i] = c;
 }
 
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(BackwardParams p, size_t n4) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n4) reduce_element(p, i);
+}
+
 // ---- query-stationary pass (dQ, dr) -----------------------------------------------------
 // The forward's decomposition: a workgroup of 8 waves owns one KV head, hpw of its query heads
 // and 32 * tsub queries (hpw * tsub = 8); each wave owns one query head x 32 queries, its Q^T
@@ -798,7 +804,32 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void bwd_dq_kernel(BackwardParams
 
 }  // namespace
 
-hipError_t launch_backward(const BackwardParams& p, hipStream_t stream) {
+hipError_t backward_side_stream(hipStream_t stream, hipStream_t* side) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static hipStream_t streams[kMaxDevices] = {};
+  *side = nullptr;
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  hipError_t e = hipStreamIsCapturing(stream, &st);
+  if (e != hipSuccess) return e;
+  if (st != hipStreamCaptureStatusNone) return hipSuccess;
+  int dev = -1;
+  e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipSuccess;
+  std::lock_guard<std::mutex> lock(mu);
+  if (streams[dev] == nullptr) {
+    e = hipStreamCreateWithFlags(&streams[dev], hipStreamNonBlocking);
+    if (e != hipSuccess) {
+      streams[dev] = nullptr;
+      return e;
+    }
+  }
+  *side = streams[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_backward(const BackwardParams& p, hipStream_t stream, hipStream_t side) {
   const size_t n_kv = (size_t)p.B * p.Lk * p.Hkv * kHeadDim;
   const size_t n_r = (size_t)p.Hq * p.R;
   auto fill = [&](float* a, size_t n) {
@@ -823,11 +854,37 @@ hipError_t launch_backward(const BackwardParams& p, hipStream_t stream) {
   const long long kv_units = (long long)((p.Lk + kKvKeys - 1) / kKvKeys) * p.kv_chunks * p.Hkv * p.n_pairs * p.B;
   const long long q_units = (long long)p.n_tok_tiles * p.q_chunks * p.B * p.Hkv * p.n_hg;
   if (kv_units > 0x7fffffffLL || q_units + kDqReduceWorkgroups > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)kv_units), dim3(64 * kKvWaves), 0, stream, p);
   const size_t n4 = n_kv / 4;
-  const int n_red = (int)std::min<size_t>((n4 + 64 * kDqWaves - 1) / (64 * kDqWaves), (size_t)kDqReduceWorkgroups);
-  hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)(q_units + n_red)), dim3(64 * kDqWaves), 0, stream, p,
-                     (int)q_units, n_red, n4);
+  if ((n4 + 255) / 256 > 0x7fffffffULL) return hipErrorInvalidConfiguration;
+  if (side == nullptr) {
+    // one stream: the dK/dV sums run in the dq grid's last workgroups, after the dK/dV pass
+    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)kv_units), dim3(64 * kKvWaves), 0, stream, p);
+    const int n_red = (int)std::min<size_t>((n4 + 64 * kDqWaves - 1) / (64 * kDqWaves), (size_t)kDqReduceWorkgroups);
+    hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)(q_units + n_red)), dim3(64 * kDqWaves), 0, stream, p,
+                       (int)q_units, n_red, n4);
+    return hipGetLastError();
+  }
+  // the two passes side by side (fork after the rowdot launch, join before the sums)
+  hipEvent_t fork = nullptr, join = nullptr;
+  hipError_t e = hipEventCreateWithFlags(&fork, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&join, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventRecord(fork, stream);
+  if (e == hipSuccess) e = hipStreamWaitEvent(side, fork, 0);
+  if (e == hipSuccess) {
+    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)kv_units), dim3(64 * kKvWaves), 0, side, p);
+    e = hipEventRecord(join, side);
+  }
+  if (e == hipSuccess) {
+    hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)q_units), dim3(64 * kDqWaves), 0, stream, p, (int)q_units, 0,
+                       n4);
+    e = hipStreamWaitEvent(stream, join, 0);
+  }
+  if (e == hipSuccess)
+    hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream, p, n4);
+  // (destroying a recorded event releases it once the device has passed it)
+  if (fork) (void)hipEventDestroy(fork);
+  if (join) (void)hipEventDestroy(join);
+  if (e != hipSuccess) return e;
   return hipGetLastError();
 }
 

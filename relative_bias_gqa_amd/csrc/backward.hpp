@@ -44,6 +44,18 @@ struct BackwardParams {
   float scale_log2;   // log2(e) / sqrt(128)
 };
 
-hipError_t launch_backward(const BackwardParams& p, hipStream_t stream);
+// The stream on which the key-stationary pass runs beside the query-stationary one (neither
+// reads the other's results, so each fills the compute units the other's tail leaves idle):
+// one per device, created on first use with the device current, at the default priority, kept
+// for the life of the process.  nullptr while `stream` is being captured (everything then runs
+// on `stream`) or for a device index beyond the table.
+hipError_t backward_side_stream(hipStream_t stream, hipStream_t* side);
+
+// All launches of the backward pass.  With `side` null they run in order on `stream` and the
+// dK/dV sums run in the dq grid's last workgroups; otherwise the dK/dV pass runs on `side`
+// (after an event recorded on `stream` behind the row pass) and `stream` waits for it (a
+// second event) before a kernel of its own sums dK/dV, so whatever the caller enqueues on
+// `stream` next comes after every launch.
+hipError_t launch_backward(const BackwardParams& p, hipStream_t stream, hipStream_t side);
 
 }  // namespace rattn

@@ -212,21 +212,31 @@ def test_backward_empty_chunk_zeroes_gradients():
     assert int((dk != 0).sum()) == 0 and int((dv != 0).sum()) == 0 and int((dr != 0).sum()) == 0
 
 
-def test_backward_deterministic_with_reused_workspace():
-    """dq, dk and dv are sums in a fixed order whichever workgroup of a token tile or key block
-    cut in two finishes last.  The 8K-token window-4096 workload (whose tiles and key blocks
-    are cut in two) runs once on a fresh zeroed workspace and three times on one workspace
-    whose bytes start as 0xFF (split counters -1, partial slots NaN: every call must reset
-    what it counts on); every call gives the first one's dq, dk and dv bit for bit, and dbias
-    (fp32 atomic adds in any order) within rounding of it."""
-    print("case backward determinism, reused poisoned workspace, swa_prefill_8k_bwd", flush=True)
-    case = synth.swa_prefill_8k_bwd()
+DETERMINISM_SHAPES = [
+    # name, seed, B, Lq, Lk, Hq, Hkv, R, window
+    ("swa_prefill_8k_bwd", None, 1, 8192, 8192, 16, 2, 4096, 4096),
+    ("causal_2k", 89, 1, 2048, 2048, 16, 2, 2048, 0),
+]
+
+
+@pytest.mark.parametrize("name,seed,B,Lq,Lk,Hq,Hkv,R,window", DETERMINISM_SHAPES,
+                         ids=[c[0] for c in DETERMINISM_SHAPES])
+def test_backward_deterministic_with_reused_workspace(name, seed, B, Lq, Lk, Hq, Hkv, R, window):
+    """dq, dk and dv are sums in a fixed order, whichever workgroup of a token tile or key block
+    cut in two finishes last and however the two passes, which run side by side, interleave.
+    The 8K-token window-4096 workload (128 full-length units per pass: one chunk each) and a
+    causal 2048-token prefill (few units: its tiles and key blocks are cut in two) each run
+    once on a fresh zeroed workspace and three times on one workspace whose bytes start as
+    0xFF (split counters -1, partial slots NaN: every call must reset what it counts on); every
+    call gives the first one's dq, dk and dv bit for bit, and dbias (fp32 atomic adds in any
+    order) within rounding of it."""
+    print(f"case backward determinism, reused poisoned workspace, {name}", flush=True)
+    case = synth.swa_prefill_8k_bwd() if seed is None else synth.make_backward(seed, B, Lq, Lk, Hq, Hkv, R, window,
+                                                                               name)
     f = case.fwd
     q, k, v, r = dev(f.q), dev(f.k), dev(f.v), dev(f.bias)
     out, lse = rb.prefill(q, k, v, r, f.window)
     dout = dev(case.dout)
-    B, Lq, Hq = q.shape[0], q.shape[1], q.shape[2]
-    Lk, Hkv = k.shape[1], k.shape[2]
     n = rb.rattn_prefill_backward_workspace_bytes(B, Lq, Lk, Hq, Hkv)
 
     def call(ws):
@@ -239,11 +249,61 @@ def test_backward_deterministic_with_reused_workspace():
         return host(dq), host(dk), host(dv), host(dbias)
 
     first = call(torch.zeros(n, dtype=torch.uint8, device="cuda"))
-    for name, g in zip(("dq", "dk", "dv", "dbias"), first):
-        assert np.isfinite(g).all(), f"{name}: non-finite on a fresh workspace"
+    for gname, g in zip(("dq", "dk", "dv", "dbias"), first):
+        assert np.isfinite(g).all(), f"{gname}: non-finite on a fresh workspace"
     ws = torch.full((n,), 0xFF, dtype=torch.uint8, device="cuda")
     for i in range(3):
         got = call(ws)
-        for name, a, b in zip(("dq", "dk", "dv"), first, got):
-            assert np.array_equal(a, b), f"call {i + 1}: {name} differs from the first call"
+        for gname, a, b in zip(("dq", "dk", "dv"), first, got):
+            assert np.array_equal(a, b), f"call {i + 1}: {gname} differs from the first call"
         assert np.allclose(got[3], first[3], rtol=1e-5, atol=1e-6), f"call {i + 1}: dbias beyond rounding"
+
+
+def test_backward_graph_capture_one_stream():
+    """Captured in a graph, the backward runs every launch on the capturing stream (no second
+    stream: its tiles and key blocks are planned for one pass at a time, the dK/dV sums run
+    in the dq grid's tail).  A causal 1024-token prefill (16/2 heads, R 300) is captured
+    once and replayed three times, each replay after an eager call (the two passes side by
+    side) into other buffers and a synchronisation; every replay and every eager call is
+    within the bound of the oracle, and the replays give the same dq, dk and dv bit for bit."""
+    print("case backward graph capture (one stream), causal 1024", flush=True)
+    B, Lq, Lk, Hq, Hkv, R, window = 1, 1024, 1024, 16, 2, 300, 0
+    case = synth.make_backward(90, B, Lq, Lk, Hq, Hkv, R, window, "graph_causal_1k")
+    f = case.fwd
+    q, k, v, r = dev(f.q), dev(f.k), dev(f.v), dev(f.bias)
+    out, lse = rb.prefill(q, k, v, r, window)
+    dout = dev(case.dout)
+    refs, absums = oracle.ref_backward(f.q, f.k, f.v, f.bias, case.dout, window)
+
+    def buffers():
+        return (torch.empty(q.shape, dtype=torch.float32, device="cuda"),
+                torch.empty(k.shape, dtype=torch.float32, device="cuda"),
+                torch.empty(v.shape, dtype=torch.float32, device="cuda"),
+                torch.empty(r.shape, dtype=torch.float32, device="cuda"))
+
+    n = rb.rattn_prefill_backward_workspace_bytes(B, Lq, Lk, Hq, Hkv)
+    ws_g = torch.full((n,), 0xFF, dtype=torch.uint8, device="cuda")
+    ws_e = torch.empty(n, dtype=torch.uint8, device="cuda")
+    g_out, e_out = buffers(), buffers()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        rb.rattn_prefill_backward(q, k, v, r, out, dout, lse, *g_out, window, ws_g)
+    torch.cuda.synchronize()
+    first = None
+    for i in range(3):
+        for t in e_out + g_out:
+            t.fill_(float("nan"))
+        rb.rattn_prefill_backward(q, k, v, r, out, dout, lse, *e_out, window, ws_e)
+        torch.cuda.synchronize()
+        for gname, g, ref, a in zip(("dq", "dk", "dv", "dbias"), e_out, refs, absums):
+            check(f"eager {i} {gname}", host(g), ref, a)
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [host(t) for t in g_out]
+        for gname, g, ref, a in zip(("dq", "dk", "dv", "dbias"), got, refs, absums):
+            check(f"replay {i} {gname}", g, ref, a)
+        if first is None:
+            first = got
+        for gname, a, b in zip(("dq", "dk", "dv"), first, got):
+            assert np.array_equal(a, b), f"replay {i}: {gname} differs from the first replay"
