@@ -609,24 +609,9 @@ ChunkPlan chunk_plan(const std::vector<long long>& walk, int chunks) {
   return ChunkPlan{chunks, (int)std::min<long long>((most + chunks - 1) / chunks, 0x7fffffff)};
 }
 
-// One or two chunks per segment, whichever plan the dispatch model finishes sooner.
-ChunkPlan plan_chunks(const std::vector<long long>& walk, long long inner) {
-  if (walk.empty() || inner <= 0 || (double)walk.size() * inner > 4e6) return chunk_plan(walk, 1);
-  int best = 1;
-  double best_t = 0.0;
-  for (int chunks = 1; chunks <= 2; ++chunks) {
-    const double t = dispatch_makespan(chunk_units(walk, inner, chunks, 1.0), compute_units());
-    if (chunks == 1 || t < best_t) {
-      best_t = t;
-      best = chunks;
-    }
-  }
-  return chunk_plan(walk, best);
-}
-
-// The same choice for two launches that run side by side (the backward's key-stationary units
-// `a` and query-stationary units `b`), their workgroups handed out alternately; a step of `a`
-// costs `cost_a` steps of `b`.
+// One or two chunks per segment of each of the two passes of one grid (the key-stationary
+// units `a` first, then the query-stationary ones `b`; a step of `a` costs `cost_a` steps of
+// `b`): the plan that the dispatch model finishes first.
 void plan_chunks_joint(const std::vector<long long>& wa, long long inner_a, double cost_a,
                        const std::vector<long long>& wb, long long inner_b, ChunkPlan* pa, ChunkPlan* pb) {
   *pa = chunk_plan(wa, 1);
@@ -637,13 +622,9 @@ void plan_chunks_joint(const std::vector<long long>& wa, long long inner_a, doub
   double best_t = 0.0;
   for (int ca = 1; ca <= 2; ++ca)
     for (int cb = 1; cb <= 2; ++cb) {
-      const std::vector<double> a = chunk_units(wa, inner_a, ca, cost_a), b = chunk_units(wb, inner_b, cb, 1.0);
-      std::vector<double> w;
-      w.reserve(a.size() + b.size());
-      for (size_t i = 0; i < std::max(a.size(), b.size()); ++i) {
-        if (i < a.size()) w.push_back(a[i]);
-        if (i < b.size()) w.push_back(b[i]);
-      }
+      std::vector<double> w = chunk_units(wa, inner_a, ca, cost_a);
+      const std::vector<double> b = chunk_units(wb, inner_b, cb, 1.0);
+      w.insert(w.end(), b.begin(), b.end());
       const double t = dispatch_makespan(w, compute_units());
       if ((ca == 1 && cb == 1) || t < best_t) {
         best_t = t;
@@ -722,26 +703,17 @@ int rattn_prefill_backward(const void* q, const void* k, const void* v, const fl
     p.n_hg = shape.n_hg;
     p.n_tok_tiles = shape.n_tok_tiles;
   }
-  hipStream_t side = nullptr;
-  hipError_t e = rattn::backward_side_stream((hipStream_t)stream, &side);
-  if (e != hipSuccess)
-    return fail(RATTN_ERR_HIP, "rattn_prefill_backward: second stream: %s", hipGetErrorString(e));
   {
     // walk of every key block / token tile, then one or two chunks each, whichever plan the
-    // dispatch model finishes sooner: for the two passes together when they run side by side
-    // (a key-stationary step and a query-stationary one both cover 8192 query-key pairs; the
-    // first takes about 1.1 times as long), else for each alone
+    // dispatch model finishes sooner for the two passes' grid (a key-stationary step and a
+    // query-stationary one both cover 8192 query-key pairs; the first takes about 1.1 times
+    // as long)
     const int n_blk = (Lk + 127) / 128;
     std::vector<long long> kw(n_blk), qw(p.n_tok_tiles);
     for (int blk = 0; blk < n_blk; ++blk) kw[blk] = bwd_kv_block_steps(Lq, Lk, window, blk);
     for (int t = 0; t < p.n_tok_tiles; ++t) qw[p.n_tok_tiles - 1 - t] = bwd_dq_tile_keys(Lq, Lk, window, p.tsub, t);
     ChunkPlan kv, qp;
-    if (side != nullptr) {
-      plan_chunks_joint(kw, (long long)B * Hkv * lay.n_pairs, 1.1, qw, (long long)B * Hkv * p.n_hg, &kv, &qp);
-    } else {
-      kv = plan_chunks(kw, (long long)B * Hkv * lay.n_pairs);
-      qp = plan_chunks(qw, (long long)B * Hkv * p.n_hg);
-    }
+    plan_chunks_joint(kw, (long long)B * Hkv * lay.n_pairs, 1.1, qw, (long long)B * Hkv * p.n_hg, &kv, &qp);
     p.kv_chunks = kv.chunks;
     p.kv_chunk = kv.chunk;
     p.q_chunks = qp.chunks;
@@ -756,7 +728,7 @@ int rattn_prefill_backward(const void* q, const void* k, const void* v, const fl
   p.R = R;
   p.window = window;
   p.scale_log2 = kScaleLog2;
-  e = rattn::launch_backward(p, (hipStream_t)stream, side);
+  const hipError_t e = rattn::launch_backward(p, (hipStream_t)stream);
   if (e != hipSuccess) return fail(RATTN_ERR_HIP, "rattn_prefill_backward: launch failed: %s", hipGetErrorString(e));
   return ok();
 }

@@ -14,24 +14,25 @@
 //   1. D = rowsum(dout * out) and lse * log2(e) per query row (fp32, head-major), plus the
 //      preparation: dr zeroed, the bias table scaled to score units (sqrt(128) r, the seed of
 //      every S accumulator, as in the forward pass), the split counters zeroed;
-//   2. key-stationary dK, dV: a workgroup owns 128 keys of a KV head and a pair of its query
-//      heads (8 waves = 4 blocks of 32 keys x 2 heads); K and V stay in LDS, the query
-//      tiles that see them stream in by direct-to-LDS DMA; S = Q K^T and dP = dO V^T come
-//      out with one key per lane, the A-operand layout of dV += P^T dO and dK += dS^T Q, so P
-//      and dS feed those MFMAs from registers (dO and Q read transposed from LDS); each pair
-//      writes a partial dK, dV, summed in pair order by the last workgroups of launch 3
-//      (deterministic);
-//   3. query-stationary dQ and dr: the forward's decomposition (8 waves, one query head x 32
-//      queries each, Q^T and dO^T resident in registers), K and V streamed through an LDS
-//      ring; S^T and dP^T come out with one query per lane, the B-operand layout of
-//      dQ^T += K^T dS^T, so dQ stays in registers and is stored once (a token tile whose key
-//      tiles two workgroups share is merged by the one that finishes second); dS is also
-//      summed per distance through a skewed table in LDS and added into dr (fp32 atomics:
-//      dr's last bits may change from run to run).
+//   2. both passes in one grid (neither reads the other's results, so each fills the compute
+//      units the other leaves idle; the key-stationary units, the longer ones, come first):
+//      - key-stationary dK, dV: a workgroup owns 128 keys of a KV head and a pair of its
+//        query heads (8 waves = 4 blocks of 32 keys x 2 heads); K and V stay in LDS, the query
+//        tiles that see them stream in by direct-to-LDS DMA; S = Q K^T and dP = dO V^T come
+//        out with one key per lane, the A-operand layout of dV += P^T dO and dK += dS^T Q, so
+//        P and dS feed those MFMAs from registers (dO and Q read transposed from LDS); each
+//        pair writes a partial dK, dV;
+//      - query-stationary dQ and dr: the forward's decomposition (8 waves, one query head x
+//        32 queries each, Q^T and dO^T resident in registers), K and V streamed through an LDS
+//        ring; S^T and dP^T come out with one query per lane, the B-operand layout of
+//        dQ^T += K^T dS^T, so dQ stays in registers and is stored once (a token tile whose key
+//        tiles two workgroups share is merged by the one that finishes second); dS is also
+//        summed per distance through a skewed table in LDS and added into dr (fp32 atomics:
+//        dr's last bits may change from run to run);
+//   3. dK, dV = the pairs' partials summed in pair order (deterministic).
 // All products are v_mfma_f32_32x32x16_bf16 with fp32 accumulation; P and dS are rounded to
 // bf16 as MFMA operands.
 #include <algorithm>
-#include <mutex>
 
 #include "backward.hpp"
 #include "device_common.hpp"
@@ -211,9 +212,10 @@ __device__ __forceinline__ void dma4_bias_or_neginf(const float* table, uint32_t
   else dma4s(&kNegInfF, 0u, lds);
 }
 
-__global__ __launch_bounds__(64 * kKvWaves, 1) void bwd_dkdv_kernel(BackwardParams p) {
-  __shared__ __attribute__((aligned(1024))) unsigned char kv_lds[2 * kKvKeys * 256];  // K, then V
-  __shared__ __attribute__((aligned(1024))) unsigned char ring[2 * kRingStage];
+// Unit u0 of the key-stationary pass (workgroup u0 of the grid); kv_lds holds K then V of its
+// 128 keys (64 KB), ring the two stages of query tiles.
+__device__ __forceinline__ void dkdv_work(const BackwardParams& p, const int u0, unsigned char* kv_lds,
+                                          unsigned char* ring) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -475,7 +477,7 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void bwd_dkdv_kernel(BackwardPara
   hand_over(dk, p.part_dk);
   hand_over(dv, p.part_dv);
   };
-  unit((int)blockIdx.x);
+  unit(u0);
 }
 
 // dk = (sum over head pairs of the partial dK) / sqrt(128), dv = sum of the partial dV, in
@@ -522,30 +524,22 @@ constexpr int kDqKV = 32 * 256;                       // a K (or V) tile: 32 key
 constexpr int kDqBias = 2 * kDqKV;                    // bias slices: 64 floats per wave
 constexpr int kDqStage = kDqBias + kDqWaves * 256;
 constexpr int kDqLoads = 3;
-// workgroups appended to the dq grid that sum the dK/dV partials (1024, 2048 and 4096 ran
-// the same; 256 left part of the tail idle)
-constexpr int kDqReduceWorkgroups = 1024;                           // DMA loads per wave and tile
 
-__global__ __launch_bounds__(64 * kDqWaves, 1) void bwd_dq_kernel(BackwardParams p, int q_units, int n_red, size_t n4) {
-  __shared__ __attribute__((aligned(1024))) unsigned char ring[kDqStages * kDqStage];
-  __shared__ int merges;  // this workgroup finished second of a split token tile
-  // The grid's last n_red workgroups sum the dK/dV partials (the dK/dV pass has finished):
-  // dispatched after every dq unit, they run on compute units that the dq units' tail leaves
-  // idle.
-  if ((int)blockIdx.x >= q_units) {
-    const size_t stride = (size_t)n_red * 64 * kDqWaves;
-    for (size_t i = (size_t)(blockIdx.x - q_units) * 64 * kDqWaves + threadIdx.x; i < n4; i += stride)
-      reduce_element(p, i);
-    return;
-  }
-  // dS of a tile by diagonal: row e = col - jj + 31 (distance dbase + e), column col (the
-  // query).  The cells of row e that no pair maps to (columns outside e - 31 .. e) are the
-  // same in every tile and never written: zeroed once, they let a row sum take all 32 columns.
-  __shared__ __attribute__((aligned(16))) float diag_w[kDqWaves][63 * kDiagStride];
+constexpr int kDqRing = kDqStages * kDqStage;
+constexpr int kDqDiag = kDqWaves * 63 * kDiagStride * 4;
+
+// Unit u0 of the query-stationary pass (workgroup kv_units + u0 of the grid); ring holds the
+// three stages of K/V tiles and bias slices, diag_w a distance table per wave, merges the flag
+// of a workgroup that finishes a split token tile second.
+__device__ __forceinline__ void dq_work(const BackwardParams& p, const int u0, unsigned char* ring,
+                                        float (*diag_w)[63 * kDiagStride], int& merges) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, hf = lane >> 5;
+  // dS of a tile by diagonal: row e = col - jj + 31 (distance dbase + e), column col (the
+  // query).  The cells of row e that no pair maps to (columns outside e - 31 .. e) are the
+  // same in every tile and never written: zeroed once, they let a row sum take all 32 columns.
   float* diag = diag_w[wave];
   for (int i = lane; i < 63 * kDiagStride; i += 64) diag[i] = 0.f;  // this wave's own table
   // One workgroup per unit: a token tile's key tiles, for one head group and KV head, cut into
@@ -799,37 +793,31 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void bwd_dq_kernel(BackwardParams
       *(f32x4_t*)(p.dq + qoff + 32 * db + 8 * i) = x;
     }
   };
-  unit((int)blockIdx.x);
+  unit(u0);
+}
+
+constexpr int kKvLds = 2 * kKvKeys * 256 + 2 * kRingStage;
+constexpr int kDqLds = kDqRing + kDqDiag + 16;
+constexpr int kPassLds = kKvLds > kDqLds ? kKvLds : kDqLds;
+static_assert(64 * kKvWaves == 64 * kDqWaves, "one workgroup size for both passes");
+
+// One workgroup per unit of either pass: the kv_units key-stationary units first (they take
+// about 1.1 times as long per step), then the query-stationary ones, each in its own launch
+// order.  LDS holds one pass's buffers at a time: K, V and the query ring, or the K/V ring,
+// the distance tables and the split flag.
+__global__ __launch_bounds__(64 * kDqWaves, 1) void bwd_passes_kernel(BackwardParams p, int kv_units) {
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[kPassLds];
+  const int i = blockIdx.x;
+  if (i < kv_units) {
+    dkdv_work(p, i, lds, lds + kKvKeys * 512);
+  } else {
+    dq_work(p, i - kv_units, lds, (float(*)[63 * kDiagStride])(lds + kDqRing), *(int*)(lds + kDqRing + kDqDiag));
+  }
 }
 
 }  // namespace
 
-hipError_t backward_side_stream(hipStream_t stream, hipStream_t* side) {
-  constexpr int kMaxDevices = 64;
-  static std::mutex mu;
-  static hipStream_t streams[kMaxDevices] = {};
-  *side = nullptr;
-  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
-  hipError_t e = hipStreamIsCapturing(stream, &st);
-  if (e != hipSuccess) return e;
-  if (st != hipStreamCaptureStatusNone) return hipSuccess;
-  int dev = -1;
-  e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= kMaxDevices) return hipSuccess;
-  std::lock_guard<std::mutex> lock(mu);
-  if (streams[dev] == nullptr) {
-    e = hipStreamCreateWithFlags(&streams[dev], hipStreamNonBlocking);
-    if (e != hipSuccess) {
-      streams[dev] = nullptr;
-      return e;
-    }
-  }
-  *side = streams[dev];
-  return hipSuccess;
-}
-
-hipError_t launch_backward(const BackwardParams& p, hipStream_t stream, hipStream_t side) {
+hipError_t launch_backward(const BackwardParams& p, hipStream_t stream) {
   const size_t n_kv = (size_t)p.B * p.Lk * p.Hkv * kHeadDim;
   const size_t n_r = (size_t)p.Hq * p.R;
   auto fill = [&](float* a, size_t n) {
@@ -853,38 +841,11 @@ hipError_t launch_backward(const BackwardParams& p, hipStream_t stream, hipStrea
   hipLaunchKernelGGL(bwd_rowdot_kernel, dim3((unsigned)rowdot_blocks), dim3(256), 0, stream, p, n_tb, n_r, n_cnt);
   const long long kv_units = (long long)((p.Lk + kKvKeys - 1) / kKvKeys) * p.kv_chunks * p.Hkv * p.n_pairs * p.B;
   const long long q_units = (long long)p.n_tok_tiles * p.q_chunks * p.B * p.Hkv * p.n_hg;
-  if (kv_units > 0x7fffffffLL || q_units + kDqReduceWorkgroups > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const size_t n4 = n_kv / 4;
-  if ((n4 + 255) / 256 > 0x7fffffffULL) return hipErrorInvalidConfiguration;
-  if (side == nullptr) {
-    // one stream: the dK/dV sums run in the dq grid's last workgroups, after the dK/dV pass
-    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)kv_units), dim3(64 * kKvWaves), 0, stream, p);
-    const int n_red = (int)std::min<size_t>((n4 + 64 * kDqWaves - 1) / (64 * kDqWaves), (size_t)kDqReduceWorkgroups);
-    hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)(q_units + n_red)), dim3(64 * kDqWaves), 0, stream, p,
-                       (int)q_units, n_red, n4);
-    return hipGetLastError();
-  }
-  // the two passes side by side (fork after the rowdot launch, join before the sums)
-  hipEvent_t fork = nullptr, join = nullptr;
-  hipError_t e = hipEventCreateWithFlags(&fork, hipEventDisableTiming);
-  if (e == hipSuccess) e = hipEventCreateWithFlags(&join, hipEventDisableTiming);
-  if (e == hipSuccess) e = hipEventRecord(fork, stream);
-  if (e == hipSuccess) e = hipStreamWaitEvent(side, fork, 0);
-  if (e == hipSuccess) {
-    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)kv_units), dim3(64 * kKvWaves), 0, side, p);
-    e = hipEventRecord(join, side);
-  }
-  if (e == hipSuccess) {
-    hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)q_units), dim3(64 * kDqWaves), 0, stream, p, (int)q_units, 0,
-                       n4);
-    e = hipStreamWaitEvent(stream, join, 0);
-  }
-  if (e == hipSuccess)
-    hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream, p, n4);
-  // (destroying a recorded event releases it once the device has passed it)
-  if (fork) (void)hipEventDestroy(fork);
-  if (join) (void)hipEventDestroy(join);
-  if (e != hipSuccess) return e;
+  if (kv_units + q_units > 0x7fffffffLL || (n4 + 255) / 256 > 0x7fffffffULL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(bwd_passes_kernel, dim3((unsigned)(kv_units + q_units)), dim3(64 * kDqWaves), 0, stream, p,
+                     (int)kv_units);
+  hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream, p, n4);
   return hipGetLastError();
 }
 

@@ -30,7 +30,7 @@ struct BackwardParams {
   // two-chunk tile each chunk's dq goes to its slot of dq_part, and whichever chunk finishes
   // second adds the other's partial (dq_cnt: one counter per tile and head group)
   float* dq_part;     // [units, 2, 8 waves, 64, 64] workspace
-  int* dq_cnt;        // [n_tok_tiles * B * Hkv * n_hg] workspace, zeroed by bwd_prep_kernel
+  int* dq_cnt;        // [n_tok_tiles * B * Hkv * n_hg] workspace, zeroed by the row pass
   // sqrt(128) * bias[h, i] for i < Rs = min(R, Lk) (the entries any visible pair can reach):
   // the seed of every S accumulator, as in the forward pass
   float* bias_s;      // [Hq, Rs] workspace
@@ -44,18 +44,7 @@ struct BackwardParams {
   float scale_log2;   // log2(e) / sqrt(128)
 };
 
-// The stream on which the key-stationary pass runs beside the query-stationary one (neither
-// reads the other's results, so each fills the compute units the other's tail leaves idle):
-// one per device, created on first use with the device current, at the default priority, kept
-// for the life of the process.  nullptr while `stream` is being captured (everything then runs
-// on `stream`) or for a device index beyond the table.
-hipError_t backward_side_stream(hipStream_t stream, hipStream_t* side);
-
-// All launches of the backward pass.  With `side` null they run in order on `stream` and the
-// dK/dV sums run in the dq grid's last workgroups; otherwise the dK/dV pass runs on `side`
-// (after an event recorded on `stream` behind the row pass) and `stream` waits for it (a
-// second event) before a kernel of its own sums dK/dV, so whatever the caller enqueues on
-// `stream` next comes after every launch.
-hipError_t launch_backward(const BackwardParams& p, hipStream_t stream, hipStream_t side);
+// All launches of the backward pass, in order on `stream`.
+hipError_t launch_backward(const BackwardParams& p, hipStream_t stream);
 
 }  // namespace rattn

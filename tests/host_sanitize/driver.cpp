@@ -161,8 +161,7 @@ static long long kv_steps(int Lq, int Lk, int window, int blk) {
   return lo <= hi ? hi / 32 - lo / 32 + 1 : 0;
 }
 
-static void backward_cases(bool side_stream) {
-  stub::rec.side_stream = side_stream;
+static void backward_cases() {
   struct Case { int B, Lq, Lk, Hq, Hkv, R, window; };
   const Case cases[] = {{1, 8192, 8192, 16, 2, 4096, 4096}, {2, 300, 300, 8, 2, 40, 0}, {1, 150, 700, 8, 2, 77, 120},
                         {1, 96, 96, 48, 3, 64, 0},          {1, 1, 5, 1, 1, 3, 1},     {1, 0, 300, 8, 2, 32, 0},
@@ -177,7 +176,6 @@ static void backward_cases(bool side_stream) {
                                     c.Hq, c.Hkv, 128, c.R, c.window, ws, need, nullptr);
     CHECK(st == RATTN_OK);
     CHECK(stub::rec.backward_calls == before + 1);
-    CHECK((stub::rec.backward_side != nullptr) == side_stream);
     const rattn::BackwardParams& p = stub::rec.backward;
     const size_t rows = (size_t)c.B * c.Lq * c.Hq, plane = (size_t)c.B * c.Lk * c.Hkv * 128;
     CHECK(p.n_pairs == (c.Hq / c.Hkv + 1) / 2);
@@ -277,8 +275,7 @@ int main() {
     paged_prefill_cases();
     decode_cases();
     sconv_cases();
-    backward_cases(true);
-    backward_cases(false);
+    backward_cases();
   }
   oracle_cases();
   // every stubbed launch was reached

@@ -2,7 +2,6 @@
 // (relative_bias_gqa_amd/csrc/abi.cpp) makes, so that the layer can be built with g++ under
 // AddressSanitizer and UndefinedBehaviorSanitizer and driven on a machine without a GPU.
 // Each launch records its parameters for the driver to check; no kernel runs.
-#include <cstdint>
 #include <hip/hip_runtime.h>
 
 #include <cstring>
@@ -55,15 +54,8 @@ hipError_t launch_sconv_write(const SconvParams& p, hipStream_t) {
   return hipSuccess;
 }
 
-// a stand-in second stream (never dereferenced), or none as under graph capture
-hipError_t backward_side_stream(hipStream_t, hipStream_t* side) {
-  *side = stub::rec.side_stream ? reinterpret_cast<hipStream_t>(static_cast<uintptr_t>(0x5eed)) : nullptr;
-  return hipSuccess;
-}
-
-hipError_t launch_backward(const BackwardParams& p, hipStream_t, hipStream_t side) {
+hipError_t launch_backward(const BackwardParams& p, hipStream_t) {
   stub::rec.backward = p;
-  stub::rec.backward_side = side;
   ++stub::rec.backward_calls;
   return hipSuccess;
 }

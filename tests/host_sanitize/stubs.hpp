@@ -15,9 +15,6 @@ struct Record {
   rattn::SconvParams sconv{};
   rattn::BackwardParams backward{};
   int prefill_bf16_calls = 0, prefill_fp32_calls = 0, decode_calls = 0, sconv_calls = 0, backward_calls = 0;
-  // whether backward_side_stream hands out a second stream (false: as under graph capture)
-  bool side_stream = true;
-  hipStream_t backward_side = nullptr;
   // called on every decode launch (a call may launch several batches); false fails the launch
   std::function<bool(const rattn::DecodeParams&)> on_decode = [](const rattn::DecodeParams&) { return true; };
 };
