@@ -244,7 +244,7 @@ size_t rattn_prefill_backward_workspace_bytes(int B, int Lq, int Lk, int Hq, int
  *   bias          [Hq, R]             fp32   device, read
  *   lse           [B, Lq, Hq]         fp32   device, read (natural log)
  *   dq            [B, Lq, Hq, 128]    fp32   device, written
- *   dk, dv        [B, Lk, Hkv, 128]   fp32   device, written (zeroed, then accumulated)
+ *   dk, dv        [B, Lk, Hkv, 128]   fp32   device, written (every entry, once)
  *   dbias         [Hq, R]             fp32   device, written (zeroed, then accumulated)
  *   workspace     device scratch of at least rattn_prefill_backward_workspace_bytes(...)
  *   window        <= 0 full causal, > 0 sliding window of that many keys
