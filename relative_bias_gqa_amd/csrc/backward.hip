@@ -482,8 +482,10 @@ __device__ __forceinline__ void dkdv_work(const BackwardParams& p, const int u0,
 
 // dk = (sum over head pairs of the partial dK) / sqrt(128), dv = sum of the partial dV, in
 // pair order, a pair's second chunk (blocks walked in two) right after its first; four
-// consecutive floats per call (run by the tail workgroups of the dq grid).
-__device__ __forceinline__ void reduce_element(const BackwardParams& p, size_t i) {
+// consecutive floats per thread.
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(BackwardParams p, size_t n4) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
   const size_t plane = (size_t)p.B * p.Lk * p.Hkv * kHeadDim;
   const int j = (int)((i / ((size_t)p.Hkv * 32)) % (size_t)p.Lk);
   const bool two = kv_block_steps(p, j / kKvKeys) > p.kv_chunk;
@@ -498,11 +500,6 @@ __device__ __forceinline__ void reduce_element(const BackwardParams& p, size_t i
   }
   ((f32x4_t*)p.dk)[i] = a * kRsqrtD;
   ((f32x4_t*)p.dv)[i] = c;
-}
-
-__global__ __launch_bounds__(256) void bwd_reduce_kernel(BackwardParams p, size_t n4) {
-  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < n4) reduce_element(p, i);
 }
 
 // ---- query-stationary pass (dQ, dr) -----------------------------------------------------
