@@ -165,7 +165,7 @@ static void backward_cases() {
   struct Case { int B, Lq, Lk, Hq, Hkv, R, window; };
   const Case cases[] = {{1, 8192, 8192, 16, 2, 4096, 4096}, {2, 300, 300, 8, 2, 40, 0}, {1, 150, 700, 8, 2, 77, 120},
                         {1, 96, 96, 48, 3, 64, 0},          {1, 1, 5, 1, 1, 3, 1},     {1, 0, 300, 8, 2, 32, 0},
-                        {1, 2048, 32768, 16, 2, 512, 0}};
+                        {1, 2048, 32768, 16, 2, 512, 0}, {1, 1024, 1024, 16, 2, 300, 0}};
   for (const Case& c : cases) {
     const size_t need = rattn_prefill_backward_workspace_bytes(c.B, c.Lq, c.Lk, c.Hq, c.Hkv);
     CHECK(need >= 256);
@@ -192,6 +192,14 @@ static void backward_cases() {
     CHECK(p.Rs == (c.R < c.Lk ? c.R : c.Lk));
     CHECK(inside(p.bias_s, (size_t)c.Hq * p.Rs * 4, ws, need));
     CHECK((p.kv_chunks == 1 || p.kv_chunks == 2) && (p.q_chunks == 1 || p.q_chunks == 2));
+    // the plans on 256 compute units: the 8K-token window-4096 workload uncut (its 512 + 512
+    // units fill the grid; measured 0.847 ms against 0.880 with both passes cut in two), and a
+    // causal 1024-token prefill, whose 64 + 64 units would leave most compute units idle, with
+    // both passes cut in two
+    if (stub::rec.compute_units == 256 && c.Lq == 8192 && c.Lk == 8192 && c.window == 4096)
+      CHECK(p.kv_chunks == 1 && p.q_chunks == 1);
+    if (stub::rec.compute_units == 256 && c.Lq == 1024 && c.Lk == 1024 && c.window == 0)
+      CHECK(p.kv_chunks == 2 && p.q_chunks == 2);
     long long most = 1;
     for (int blk = 0; blk < (c.Lk + 127) / 128; ++blk) {
       const long long s = kv_steps(c.Lq, c.Lk, c.window, blk);
@@ -269,8 +277,10 @@ static void oracle_cases() {
 
 int main() {
   CHECK(rattn_abi_version() == RATTN_ABI_VERSION);
+  int device = 0;
   for (int cus : {256, 304, 80}) {
     stub::rec.compute_units = cus;
+    stub::rec.device = device++;
     prefill_cases();
     paged_prefill_cases();
     decode_cases();

@@ -15,7 +15,7 @@ Record rec;
 }
 
 extern "C" hipError_t hipGetDevice(int* device) {
-  *device = 0;
+  *device = stub::rec.device;
   return hipSuccess;
 }
 

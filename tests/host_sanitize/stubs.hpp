@@ -10,6 +10,9 @@ namespace stub {
 
 struct Record {
   int compute_units = 256;
+  // the current device's index: the library caches the compute-unit count per device, so each
+  // count the driver tries is reported for a device of its own
+  int device = 0;
   rattn::PrefillParams prefill{};
   rattn::DecodeParams decode{};
   rattn::SconvParams sconv{};
